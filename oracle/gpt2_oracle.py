@@ -1,0 +1,408 @@
+"""Plain CPU oracle for one GPT-2 training step (forward, backward, clip, AdamW).
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import, call or
+execute this module: only the test suite, the package's smoke check and the
+CPU-baseline leg of the benchmark use it.  It shares no code with the HIP
+library: it has its own parameter layout, its own maths, and it imports
+nothing from this repository.
+
+Every function is the textbook definition written out in numpy, in the dtype
+of its inputs (float32 for parity, float64 for gradient checks).  Sources, by
+page title and section:
+
+* "GPT-2 from Scratch" (lumen chapter): "The config", "Embeddings",
+  "CausalSelfAttention", "The MLP and GPT-2's GELU", "The Block: pre-LN and
+  residuals", "The full model", "Weight tying", "Initialization",
+  "AdamW, and weight decay on matrices only", "Warmup and cosine decay",
+  "Gradient clipping", "How to scale up" (accumulation).
+* "Let's reproduce GPT-2 (124M)" (synopsis): weight tying, residual init
+  scaling, padded vocabulary, GPT-3 optimizer settings, loss/k accumulation.
+* "Pretraining and fine-tuning nanoGPT-124M from scratch": padded vocab
+  50,304, loss masking with target -1.
+
+Readings where the pages are silent or garbled (each is listed with its reason
+in the design notes):
+  R1  GELU is the tanh form 0.5 x (1 + tanh(sqrt(2/pi) (x + 0.044715 x^3)))
+      of Hendrycks & Gimpel; the page's formula did not survive extraction.
+  R2  LayerNorm uses the biased variance over C and eps = 1e-5 inside the
+      square root.
+  R3  The loss is the mean over positions whose target is not -1; with no
+      valid position the loss is 0 and the gradient is 0.
+  R4  Padded vocabulary columns take part in the softmax like real ones.
+  R5  Clip coefficient min(1, max_norm / (norm + 1e-6)); the pre-clip norm is
+      what is reported.
+  R6  AdamW: decoupled decay p <- p (1 - lr wd) on tensors with dim >= 2,
+      then the moment updates, bias correction with t starting at 1, eps added
+      to sqrt(v_hat).
+The backward pass is the chain rule of the forward pass; it is pinned by
+central differences and by torch autograd in the CPU tests.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass
+
+import numpy as np
+
+
+# ----------------------------------------------------------------------------
+# configuration and parameter layout
+# ("GPT-2 from Scratch", "The config" / "The full model")
+# ----------------------------------------------------------------------------
+
+@dataclass(frozen=True)
+class Config:
+    n_layer: int
+    n_head: int
+    n_embd: int
+    vocab_size: int
+    padded_vocab_size: int
+    block_size: int
+
+
+def param_specs(cfg: Config):
+    """Canonical tensor order and shapes: wte, wpe, per block (ln_1, c_attn,
+    c_proj, ln_2, c_fc, mlp c_proj), ln_f.  Weights are (out, in) as for a
+    torch Linear; wte doubles as the lm_head weight (weight tying)."""
+    C, Vp = cfg.n_embd, cfg.padded_vocab_size
+    specs = [("wte", (Vp, C)), ("wpe", (cfg.block_size, C))]
+    for l in range(cfg.n_layer):
+        p = f"h.{l}."
+        specs += [
+            (p + "ln_1.weight", (C,)), (p + "ln_1.bias", (C,)),
+            (p + "attn.c_attn.weight", (3 * C, C)), (p + "attn.c_attn.bias", (3 * C,)),
+            (p + "attn.c_proj.weight", (C, C)), (p + "attn.c_proj.bias", (C,)),
+            (p + "ln_2.weight", (C,)), (p + "ln_2.bias", (C,)),
+            (p + "mlp.c_fc.weight", (4 * C, C)), (p + "mlp.c_fc.bias", (4 * C,)),
+            (p + "mlp.c_proj.weight", (C, 4 * C)), (p + "mlp.c_proj.bias", (C,)),
+        ]
+    specs += [("ln_f.weight", (C,)), ("ln_f.bias", (C,))]
+    return specs
+
+
+def num_params(cfg: Config) -> int:
+    return sum(int(np.prod(s)) for _, s in param_specs(cfg))
+
+
+def unflatten(flat: np.ndarray, cfg: Config) -> dict:
+    """Views of the flat vector, one per named tensor (no copies)."""
+    out, off = {}, 0
+    for name, shape in param_specs(cfg):
+        n = int(np.prod(shape))
+        out[name] = flat[off:off + n].reshape(shape)
+        off += n
+    assert off == flat.size, (off, flat.size)
+    return out
+
+
+def decay_mask(cfg: Config, dtype=np.float32) -> np.ndarray:
+    """1 on tensors with dim >= 2 (matrices and embeddings), 0 on biases and
+    LayerNorm parameters ("AdamW, and weight decay on matrices only")."""
+    parts = [np.full(int(np.prod(s)), 1.0 if len(s) >= 2 else 0.0, dtype=dtype)
+             for _, s in param_specs(cfg)]
+    return np.concatenate(parts)
+
+
+# ----------------------------------------------------------------------------
+# elementwise pieces
+# ----------------------------------------------------------------------------
+
+def layernorm_fwd(x, w, b, eps=1e-5):
+    """y = (x - mean) / sqrt(var + eps) * w + b over the last axis (R2)."""
+    mu = x.mean(axis=-1, keepdims=True)
+    xc = x - mu
+    var = (xc * xc).mean(axis=-1, keepdims=True)
+    rstd = 1.0 / np.sqrt(var + eps)
+    xhat = xc * rstd
+    return xhat * w + b, xhat, rstd
+
+
+def layernorm_bwd(dy, xhat, rstd, w):
+    """Chain rule of layernorm_fwd: returns dx, dw, db."""
+    C = xhat.shape[-1]
+    dxhat = dy * w
+    mean_d = dxhat.sum(axis=-1, keepdims=True) / C
+    mean_dx = (dxhat * xhat).sum(axis=-1, keepdims=True) / C
+    dx = rstd * (dxhat - mean_d - xhat * mean_dx)
+    red = tuple(range(dy.ndim - 1))
+    return dx, (dy * xhat).sum(axis=red), dy.sum(axis=red)
+
+
+_GELU_A = math.sqrt(2.0 / math.pi)
+_GELU_C = 0.044715
+
+
+def gelu_tanh(x):
+    """R1: the tanh approximation of GELU ("The MLP and GPT-2's GELU")."""
+    return 0.5 * x * (1.0 + np.tanh(_GELU_A * (x + _GELU_C * x ** 3)))
+
+
+def gelu_tanh_grad(x):
+    """d/dx of gelu_tanh."""
+    th = np.tanh(_GELU_A * (x + _GELU_C * x ** 3))
+    return 0.5 * (1.0 + th) + 0.5 * x * (1.0 - th * th) * _GELU_A * (1.0 + 3.0 * _GELU_C * x * x)
+
+
+def softmax_rows(s):
+    m = s.max(axis=-1, keepdims=True)
+    e = np.exp(s - m)
+    return e / e.sum(axis=-1, keepdims=True)
+
+
+# ----------------------------------------------------------------------------
+# causal self-attention ("CausalSelfAttention")
+# ----------------------------------------------------------------------------
+
+def causal_attention_fwd(q, k, v):
+    """q, k, v: (B, H, T, hd).  S = q k^T / sqrt(hd), entries j > i set to
+    -inf, P = row softmax, O = P v.  Also returns the row log-sum-exp of the
+    masked, scaled scores so that the backward pass can rebuild P."""
+    B, H, T, hd = q.shape
+    scale = 1.0 / math.sqrt(hd)
+    mask = np.triu(np.ones((T, T), dtype=bool), k=1)
+    O = np.empty_like(q)
+    lse = np.empty((B, H, T), dtype=q.dtype)
+    for b in range(B):                         # one batch row at a time bounds memory
+        s = np.matmul(q[b], np.swapaxes(k[b], -1, -2)) * q.dtype.type(scale)
+        s[:, mask] = -np.inf
+        m = s.max(axis=-1, keepdims=True)
+        e = np.exp(s - m)
+        z = e.sum(axis=-1, keepdims=True)
+        O[b] = np.matmul(e / z, v[b])
+        lse[b] = (m + np.log(z))[..., 0]
+    return O, lse
+
+
+def attention_probs(q, k):
+    """The full P (B, H, T, T) for small inputs (used by the invariant tests)."""
+    hd = q.shape[-1]
+    T = q.shape[-2]
+    s = np.matmul(q, np.swapaxes(k, -1, -2)) * q.dtype.type(1.0 / math.sqrt(hd))
+    s[..., np.triu(np.ones((T, T), dtype=bool), k=1)] = -np.inf
+    return softmax_rows(s)
+
+
+def causal_attention_bwd(dO, q, k, v, lse):
+    """Gradients of O = softmax(mask(q k^T/sqrt(hd))) v with P rebuilt from
+    the saved log-sum-exp: dV = P^T dO, dP = dO V^T, dS = P (dP - rowsum(dP P)),
+    dQ = dS K / sqrt(hd), dK = dS^T Q / sqrt(hd)."""
+    B, H, T, hd = q.shape
+    scale = q.dtype.type(1.0 / math.sqrt(hd))
+    mask = np.triu(np.ones((T, T), dtype=bool), k=1)
+    dq, dk, dv = np.empty_like(q), np.empty_like(k), np.empty_like(v)
+    for b in range(B):
+        s = np.matmul(q[b], np.swapaxes(k[b], -1, -2)) * scale
+        s[:, mask] = -np.inf
+        P = np.exp(s - lse[b][..., None])
+        dv[b] = np.matmul(np.swapaxes(P, -1, -2), dO[b])
+        dP = np.matmul(dO[b], np.swapaxes(v[b], -1, -2))
+        D = (dP * P).sum(axis=-1, keepdims=True)
+        dS = P * (dP - D)
+        dq[b] = np.matmul(dS, k[b]) * scale
+        dk[b] = np.matmul(np.swapaxes(dS, -1, -2), q[b]) * scale
+    return dq, dk, dv
+
+
+# ----------------------------------------------------------------------------
+# cross-entropy with ignore_index = -1 (R3, R4)
+# ----------------------------------------------------------------------------
+
+def cross_entropy(logits, targets):
+    """logits (N, Vp), targets (N,) with -1 = ignored.  Returns the mean loss
+    over valid rows, d(loss)/d(logits), the per-row losses and n_valid."""
+    valid = targets != -1
+    n_valid = int(valid.sum())
+    m = logits.max(axis=-1, keepdims=True)
+    e = np.exp(logits - m)
+    z = e.sum(axis=-1, keepdims=True)
+    lse = (m + np.log(z))[:, 0]
+    rows = np.nonzero(valid)[0]
+    row_loss = np.zeros(logits.shape[0], dtype=logits.dtype)
+    row_loss[rows] = lse[rows] - logits[rows, targets[rows]]
+    dlogits = e                                # reuse the buffer: softmax in place
+    dlogits /= z
+    dlogits[rows, targets[rows]] -= 1.0
+    dlogits[~valid] = 0.0
+    if n_valid == 0:
+        return logits.dtype.type(0.0), np.zeros_like(logits), row_loss, 0
+    dlogits /= logits.dtype.type(n_valid)
+    loss = row_loss.sum(dtype=np.float64) / n_valid
+    return logits.dtype.type(loss), dlogits, row_loss, n_valid
+
+
+# ----------------------------------------------------------------------------
+# the model ("The full model", "The Block: pre-LN and residuals")
+# ----------------------------------------------------------------------------
+
+def forward(flat_params, idx, targets, cfg: Config, keep_logits=False):
+    """Returns (loss, cache).  idx and targets are (B, T) integer arrays;
+    targets may be None (then loss is None and logits are kept)."""
+    P = unflatten(flat_params, cfg)
+    dt = flat_params.dtype
+    B, T = idx.shape
+    assert T <= cfg.block_size
+    C, H = cfg.n_embd, cfg.n_head
+    hd = C // H
+    x = P["wte"][idx] + P["wpe"][np.arange(T)]
+    cache = {"idx": idx, "targets": targets, "layers": [], "B": B, "T": T}
+    for l in range(cfg.n_layer):
+        p = f"h.{l}."
+        lc = {"x_in": x}
+        u, lc["xhat1"], lc["rstd1"] = layernorm_fwd(x, P[p + "ln_1.weight"], P[p + "ln_1.bias"])
+        lc["u1"] = u
+        qkv = u @ P[p + "attn.c_attn.weight"].T + P[p + "attn.c_attn.bias"]
+        q, k, v = (qkv[..., i * C:(i + 1) * C].reshape(B, T, H, hd).transpose(0, 2, 1, 3)
+                   for i in range(3))
+        O, lse = causal_attention_fwd(np.ascontiguousarray(q), np.ascontiguousarray(k),
+                                      np.ascontiguousarray(v))
+        y = O.transpose(0, 2, 1, 3).reshape(B, T, C)
+        lc.update(q=q, k=k, v=v, lse=lse, y=y, qkv=qkv)
+        x = x + (y @ P[p + "attn.c_proj.weight"].T + P[p + "attn.c_proj.bias"])
+        lc["x_mid"] = x
+        u2, lc["xhat2"], lc["rstd2"] = layernorm_fwd(x, P[p + "ln_2.weight"], P[p + "ln_2.bias"])
+        lc["u2"] = u2
+        h = u2 @ P[p + "mlp.c_fc.weight"].T + P[p + "mlp.c_fc.bias"]
+        g = gelu_tanh(h)
+        lc.update(h=h, g=g)
+        x = x + (g @ P[p + "mlp.c_proj.weight"].T + P[p + "mlp.c_proj.bias"])
+        cache["layers"].append(lc)
+    cache["x_final"] = x
+    z, cache["xhatf"], cache["rstdf"] = layernorm_fwd(x, P["ln_f.weight"], P["ln_f.bias"])
+    cache["z"] = z
+    logits = z.reshape(B * T, C) @ P["wte"].T                 # tied lm_head, no bias
+    if targets is None:
+        cache["logits"] = logits.reshape(B, T, -1)
+        return None, cache
+    loss, dlogits, row_loss, n_valid = cross_entropy(logits, targets.reshape(-1))
+    cache.update(dlogits=dlogits, row_loss=row_loss, n_valid=n_valid)
+    if keep_logits:
+        cache["logits"] = logits.reshape(B, T, -1)
+    return loss, cache
+
+
+def backward(flat_params, cache, cfg: Config, loss_scale=1.0, grads=None):
+    """Accumulates loss_scale * d(loss)/d(params) into `grads` (flat, same
+    layout) and returns it.  The tied wte receives both the lm_head and the
+    embedding contribution."""
+    P = unflatten(flat_params, cfg)
+    dt = flat_params.dtype
+    if grads is None:
+        grads = np.zeros_like(flat_params)
+    G = unflatten(grads, cfg)
+    B, T = cache["B"], cache["T"]
+    C, H = cfg.n_embd, cfg.n_head
+    hd = C // H
+    s = dt.type(loss_scale)
+    dlogits = cache["dlogits"] * s                             # (B*T, Vp)
+    z = cache["z"].reshape(B * T, C)
+    G["wte"] += dlogits.T @ z                                  # lm_head part of the tie
+    dz = (dlogits @ P["wte"]).reshape(B, T, C)
+    dx, dw, db = layernorm_bwd(dz, cache["xhatf"], cache["rstdf"], P["ln_f.weight"])
+    G["ln_f.weight"] += dw
+    G["ln_f.bias"] += db
+    for l in reversed(range(cfg.n_layer)):
+        p = f"h.{l}."
+        lc = cache["layers"][l]
+        # x_out = x_mid + c_proj(gelu(c_fc(ln_2(x_mid))))
+        W2 = P[p + "mlp.c_proj.weight"]
+        G[p + "mlp.c_proj.weight"] += dx.reshape(-1, C).T @ lc["g"].reshape(-1, 4 * C)
+        G[p + "mlp.c_proj.bias"] += dx.sum(axis=(0, 1))
+        dg = dx @ W2
+        dh = dg * gelu_tanh_grad(lc["h"])
+        G[p + "mlp.c_fc.weight"] += dh.reshape(-1, 4 * C).T @ lc["u2"].reshape(-1, C)
+        G[p + "mlp.c_fc.bias"] += dh.sum(axis=(0, 1))
+        du2 = dh @ P[p + "mlp.c_fc.weight"]
+        d, dw, db = layernorm_bwd(du2, lc["xhat2"], lc["rstd2"], P[p + "ln_2.weight"])
+        G[p + "ln_2.weight"] += dw
+        G[p + "ln_2.bias"] += db
+        dx = dx + d
+        # x_mid = x_in + c_proj(attn(ln_1(x_in)))
+        G[p + "attn.c_proj.weight"] += dx.reshape(-1, C).T @ lc["y"].reshape(-1, C)
+        G[p + "attn.c_proj.bias"] += dx.sum(axis=(0, 1))
+        dy = (dx @ P[p + "attn.c_proj.weight"]).reshape(B, T, H, hd).transpose(0, 2, 1, 3)
+        dq, dk, dv = causal_attention_bwd(np.ascontiguousarray(dy), lc["q"], lc["k"], lc["v"],
+                                          lc["lse"])
+        dqkv = np.concatenate([a.transpose(0, 2, 1, 3).reshape(B, T, C) for a in (dq, dk, dv)],
+                              axis=-1)
+        G[p + "attn.c_attn.weight"] += dqkv.reshape(-1, 3 * C).T @ lc["u1"].reshape(-1, C)
+        G[p + "attn.c_attn.bias"] += dqkv.sum(axis=(0, 1))
+        du = dqkv @ P[p + "attn.c_attn.weight"]
+        d, dw, db = layernorm_bwd(du, lc["xhat1"], lc["rstd1"], P[p + "ln_1.weight"])
+        G[p + "ln_1.weight"] += dw
+        G[p + "ln_1.bias"] += db
+        dx = dx + d
+    # x = wte[idx] + wpe[0:T]
+    np.add.at(G["wte"], cache["idx"].reshape(-1), dx.reshape(-1, C))
+    G["wpe"][:T] += dx.sum(axis=0)
+    return grads
+
+
+# ----------------------------------------------------------------------------
+# optimizer ("Gradient clipping", "AdamW, ...", "Warmup and cosine decay")
+# ----------------------------------------------------------------------------
+
+def grad_norm(grads):
+    """Global L2 norm over every parameter, the tied tensor counted once."""
+    return float(np.sqrt(np.sum(grads.astype(np.float64) ** 2)))
+
+
+def clip_coefficient(norm, max_norm):
+    """R5."""
+    return min(1.0, max_norm / (norm + 1e-6))
+
+
+def adamw_update(params, grads, m, v, t, lr, beta1, beta2, eps, weight_decay, decay):
+    """One AdamW step in place (R6).  `decay` is the per-element 0/1 mask of
+    decayed tensors, `t` the 1-based step count.  grads must already be
+    clipped."""
+    dt = params.dtype.type
+    params *= (1.0 - dt(lr) * dt(weight_decay) * decay).astype(params.dtype)
+    m *= dt(beta1)
+    m += dt(1.0 - beta1) * grads
+    v *= dt(beta2)
+    v += dt(1.0 - beta2) * grads * grads
+    bc1 = 1.0 - beta1 ** t
+    bc2 = 1.0 - beta2 ** t
+    params -= dt(lr / bc1) * m / (np.sqrt(v) / dt(math.sqrt(bc2)) + dt(eps))
+    return params, m, v
+
+
+def clip_and_adamw(params, grads, m, v, t, lr, beta1=0.9, beta2=0.95, eps=1e-8,
+                   weight_decay=0.1, max_norm=1.0, decay=None, cfg=None):
+    """Global-norm clip then AdamW; returns the pre-clip norm.  `grads` is
+    scaled in place by the clip coefficient."""
+    if decay is None:
+        decay = decay_mask(cfg, params.dtype)
+    norm = grad_norm(grads)
+    c = clip_coefficient(norm, max_norm)
+    grads *= grads.dtype.type(c)
+    adamw_update(params, grads, m, v, t, lr, beta1, beta2, eps, weight_decay, decay)
+    return norm
+
+
+def lr_at(step, max_lr=6e-4, min_lr=6e-5, warmup=100, max_steps=2000):
+    """Linear warmup over `warmup` steps starting at max_lr/warmup, cosine from
+    max_lr at step=warmup down to min_lr at step=max_steps, min_lr after."""
+    if step < warmup:
+        return max_lr * (step + 1) / warmup
+    if step > max_steps:
+        return min_lr
+    progress = (step - warmup) / max(1, max_steps - warmup)
+    return min_lr + 0.5 * (max_lr - min_lr) * (1.0 + math.cos(math.pi * progress))
+
+
+def train_step(params, m, v, t, micro_batches, cfg, lr, beta1=0.9, beta2=0.95, eps=1e-8,
+               weight_decay=0.1, max_norm=1.0):
+    """One optimizer step over a list of (idx, targets) micro-batches with the
+    loss of each divided by their count ("How to scale up").  Updates params,
+    m, v in place; returns (mean loss, pre-clip norm, grads)."""
+    k = len(micro_batches)
+    grads = np.zeros_like(params)
+    losses = []
+    for idx, tgt in micro_batches:
+        loss, cache = forward(params, idx, tgt, cfg)
+        backward(params, cache, cfg, loss_scale=1.0 / k, grads=grads)
+        losses.append(float(loss))
+    norm = clip_and_adamw(params, grads, m, v, t, lr, beta1, beta2, eps, weight_decay,
+                          max_norm, cfg=cfg)
+    return sum(losses) / k, norm, grads

@@ -1,0 +1,189 @@
+#!/usr/bin/env python3
+"""Throughput of one GPT-2 training step on one MI355X.
+
+A step is the whole hot path over one batch of synthetic tokens:
+zero_grad, forward with the fused softmax cross-entropy, backward, global
+gradient-norm clip and AdamW -- all through the C ABI of libgpt2.so.
+
+  python bench.py [--steps K] [--warmup W] [--workload gpt2-124m|gpt2-xl|sft]
+
+Prints ONE JSON line.  value = tokens per second over the K timed steps
+(inputs already resident in device memory).  roofline = the lm_head forward
+GEMM (the largest single kernel: 2*B*T*Vp*C flops per launch) timed live with
+HIP events on the library's stream during the timed steps, against the bf16
+dense matrix-core peak.  cpu_baseline = the CPU oracle (numpy) on a bounded
+sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 matrix-core peak
+PEAK_HBM_GBS = 8000.0
+
+WORKLOADS = {
+    "gpt2-124m": dict(model="gpt2-124m", B=16, T=1024, data="zipf", lr=6e-4, wd=0.1,
+                      desc="GPT-2 124M training step (fwd + bwd + clip + AdamW), bf16, B=16, "
+                           "T=1024, Zipf(1.1) token ids with end-of-text separators"),
+    "sft": dict(model="gpt2-124m", B=16, T=1024, data="sft", lr=2e-5, wd=0.0,
+                desc="GPT-2 124M masked fine-tuning step, bf16, B=16, T=1024, prompt targets -1"),
+    "gpt2-xl": dict(model="gpt2-xl", B=8, T=1024, data="zipf", lr=6e-4, wd=0.1,
+                    desc="GPT-2 XL-shape training step (L=48, C=1600, H=25), bf16, B=8, T=1024"),
+}
+
+
+def flops_per_token(d, T):
+    L, C, Vp = d["n_layer"], d["n_embd"], d["padded_vocab_size"]
+    causal = 6 * (12 * L * C * C + C * Vp) + 6 * L * C * T
+    n_nonemb = 12 * L * C * C + 13 * L * C + 2 * C
+    nanogpt = 6 * n_nonemb + 12 * L * C * T
+    return causal, nanogpt
+
+
+def cpu_baseline(d, wl, seconds_hint=20.0):
+    """The oracle as it stands, on one sequence of the workload (B=1, full T):
+    forward, backward, clip and AdamW over every parameter."""
+    import numpy as np
+    import oracle
+    import synthetic
+    try:
+        import threadpoolctl
+        threads = max(i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()) \
+            if threadpoolctl.threadpool_info() else 1
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    cfg = oracle.Config(**d)
+    T = wl["T"]
+    flat = synthetic.init_params(d, seed=42)
+    if wl["data"] == "sft":
+        idx, tgt = synthetic.sft_batch(1, T, seed=1004)
+    else:
+        idx, tgt = synthetic.zipf_batch(1, T, seed=1002)
+    m, v = np.zeros_like(flat), np.zeros_like(flat)
+    t0 = time.perf_counter()
+    oracle.train_step(flat, m, v, 1, [(idx, tgt)], cfg, lr=wl["lr"], weight_decay=wl["wd"])
+    dt = time.perf_counter() - t0
+    return {"value": round(T / dt, 2), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"one full step (fwd+bwd+clip+AdamW over all params) on 1 x {T} tokens "
+                      f"of the same workload; {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="gpt2-124m", choices=sorted(WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--breakdown", action="store_true", help="also time every launch site")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(run with --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import synthetic
+    from decoder_only_transformer_03_amd import gpt2 as G
+
+    wl = WORKLOADS[args.workload]
+    d = synthetic.model_dims(wl["model"])
+    B, T = wl["B"], wl["T"]
+    cfg = G.make_config(max_batch=B, precision="bf16", **d)
+    model = G.GPT2(cfg, device="cuda:0")
+    model.set_params(synthetic.init_params(d, seed=42))
+    if wl["data"] == "sft":
+        idx, tgt = synthetic.sft_batch(B, T, seed=1004)
+    else:
+        idx, tgt = synthetic.zipf_batch(B, T, seed=1002)
+    di = torch.tensor(idx, dtype=torch.int32, device="cuda:0")
+    dt = torch.tensor(tgt, dtype=torch.int32, device="cuda:0")
+
+    def step():
+        model.zero_grad()
+        model.forward(di, dt)
+        model.backward(1.0)
+        model.adamw_step(wl["lr"], 0.9, 0.95, 1e-8, wl["wd"], 1.0)
+
+    for _ in range(args.warmup):
+        step()
+    model.sync()
+    stream = torch.cuda.current_stream()
+    model.timing_begin(["LMHEAD_FWD"])
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_total = e0.elapsed_time(e1)
+    sites = model.timing_end()
+    loss = model.get_loss()
+    norm = model.get_grad_norm()
+    model.sync()
+    ms_step = ms_total / args.steps
+    tokens = B * T
+    tok_s = tokens * args.steps / (ms_total / 1e3)
+    f_causal, f_nano = flops_per_token(d, T)
+
+    lm_ms, lm_n = sites.get("LMHEAD_FWD", (0.0, 0))
+    lm_avg = lm_ms / max(lm_n, 1)
+    lm_flops = 2.0 * tokens * d["padded_vocab_size"] * d["n_embd"]
+    achieved = lm_flops / (lm_avg / 1e3) / 1e12 if lm_avg > 0 else 0.0
+
+    breakdown = None
+    if args.breakdown:
+        model.timing_begin(None)
+        for _ in range(2):
+            step()
+        br = model.timing_end()
+        breakdown = {k: round(v[0] / 2, 4) for k, v in sorted(br.items(), key=lambda x: -x[1][0])}
+
+    out = {
+        "metric": "training tokens/sec + MFU, GPT-2 124M bf16 B=16 T=1024 on one MI355X",
+        "value": round(tok_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl["desc"], "global_batch": B, "seq_len": T,
+                   "precision": "bf16 matmuls, fp32 master weights and optimizer state"},
+        "mfu": round(tok_s * f_causal / (PEAK_BF16_TFLOPS * 1e12), 4),
+        "mfu_nanogpt_count": round(tok_s * f_nano / (PEAK_BF16_TFLOPS * 1e12), 4),
+        "gflop_per_token": round(f_causal / 1e9, 4),
+        "loss_last_step": round(loss, 5),
+        "grad_norm_last_step": round(norm, 5),
+        "host_wall_s": round(wall, 3),
+        "roofline": {"kernel": "lm_head forward GEMM (gemm_kernel<256,256,NT,store bf16>)",
+                     "bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": None, "avg_launch_ms": round(lm_avg, 4), "launches": lm_n,
+                     "flops_per_launch": lm_flops},
+    }
+    if breakdown:
+        out["site_ms_per_step"] = breakdown
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(d, wl)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

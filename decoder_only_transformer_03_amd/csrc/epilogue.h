@@ -1,0 +1,72 @@
+// GEMM epilogues: what happens to a finished fp32 accumulator C[m][n].
+// Every epilogue handles four consecutive columns n..n+3 of one row m.
+#pragma once
+#include "common.h"
+
+enum EpiKind : int {
+  EPI_STORE = 0,     // out[m][n] = alpha*c (+ bias[n])                       (out: TO)
+  EPI_BIAS_GELU = 1, // h = c + bias[n]; out[m][n] = h; out2[m][n] = gelu(h)  (out, out2: TO)
+  EPI_RESID = 2,     // out[m][n] = resid[m][n] + c + bias[n]                  (out, resid: fp32)
+  EPI_ACCUM = 3,     // out[m][n] += alpha*c            one writer per element (out: fp32)
+  EPI_ATOMIC = 4,    // atomically out[m][n] += alpha*c  split-K               (out: fp32)
+  EPI_GELU_BWD = 5,  // out[m][n] = alpha*c * gelu'(aux[m][n])                 (out, aux: TO)
+};
+
+struct EpiArgs {
+  void* out;
+  long ldo;
+  void* out2;
+  const float* bias;
+  const float* resid;
+  long ldr;
+  const void* aux;
+  long ldx;
+  float alpha;
+};
+
+template <int EPI, typename TO>
+__device__ __forceinline__ void epi_apply4(const EpiArgs& e, long m, int n, const float c[4]) {
+  float r[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) r[j] = e.alpha * c[j];
+  if constexpr (EPI == EPI_STORE || EPI == EPI_BIAS_GELU || EPI == EPI_RESID) {
+    if (e.bias) {
+      float b[4];
+      ld4(e.bias + n, b);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) r[j] += b[j];
+    }
+  }
+  if constexpr (EPI == EPI_STORE) {
+    st4(reinterpret_cast<TO*>(e.out) + m * e.ldo + n, r);
+  } else if constexpr (EPI == EPI_BIAS_GELU) {
+    st4(reinterpret_cast<TO*>(e.out) + m * e.ldo + n, r);
+    float g[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) g[j] = gelu_tanh_f(r[j]);
+    st4(reinterpret_cast<TO*>(e.out2) + m * e.ldo + n, g);
+  } else if constexpr (EPI == EPI_RESID) {
+    float x[4];
+    ld4(e.resid + m * e.ldr + n, x);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) r[j] += x[j];
+    st4(reinterpret_cast<float*>(e.out) + m * e.ldo + n, r);
+  } else if constexpr (EPI == EPI_ACCUM) {
+    float* o = reinterpret_cast<float*>(e.out) + m * e.ldo + n;
+    float x[4];
+    ld4(o, x);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) r[j] += x[j];
+    st4(o, r);
+  } else if constexpr (EPI == EPI_ATOMIC) {
+    float* o = reinterpret_cast<float*>(e.out) + m * e.ldo + n;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) atomicAdd(o + j, r[j]);
+  } else if constexpr (EPI == EPI_GELU_BWD) {
+    float h[4];
+    ld4(reinterpret_cast<const TO*>(e.aux) + m * e.ldx + n, h);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) r[j] *= gelu_tanh_grad_f(h[j]);
+    st4(reinterpret_cast<TO*>(e.out) + m * e.ldo + n, r);
+  }
+}

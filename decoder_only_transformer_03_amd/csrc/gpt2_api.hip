@@ -1,0 +1,692 @@
+// libgpt2 runtime: workspace layout, the launch plan of one training step,
+// and the C ABI declared in include/gpt2.h.
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/gpt2.h"
+#include "kernels.h"
+
+namespace {
+
+struct LayerOff {  // element offsets of one block's parameters in the flat vector
+  long ln1w, ln1b, attnw, attnb, projw, projb, ln2w, ln2b, fcw, fcb, fc2w, fc2b;
+};
+
+struct LayerAct {  // saved activations of one block
+  float* x_in;
+  float *mean1, *rstd1;
+  void* u1;
+  void* qkv;
+  void* y;
+  float* lse;
+  float* x_mid;
+  float *mean2, *rstd2;
+  void* u2;
+  void* h;
+  void* g;
+};
+
+struct Layout {
+  long P = 0;
+  long wte = 0, wpe = 0, lnfw = 0, lnfb = 0;
+  std::vector<LayerOff> layer;
+  // (offset, length, decay) of every tensor in canonical order
+  std::vector<long> t_off, t_len;
+  std::vector<int> t_decay;
+};
+
+bool valid_config(const gpt2_config* c, std::string* why) {
+  auto fail = [&](const char* m) {
+    if (why) *why = m;
+    return false;
+  };
+  if (!c) return fail("config is NULL");
+  if (c->n_layer < 1 || c->n_head < 1 || c->n_embd < 1) return fail("n_layer, n_head, n_embd must be >= 1");
+  if (c->n_embd % c->n_head) return fail("n_embd must be a multiple of n_head");
+  if (c->n_embd % 64 || c->n_embd > 2048) return fail("n_embd must be a multiple of 64 and <= 2048");
+  int hd = c->n_embd / c->n_head;
+  if (c->precision == GPT2_BF16) {
+    if (hd != 64) return fail("bf16 precision needs head width n_embd/n_head == 64");
+  } else if (c->precision == GPT2_FP32) {
+    if (hd != 32 && hd != 64) return fail("fp32 precision needs head width 32 or 64");
+  } else {
+    return fail("precision must be GPT2_FP32 or GPT2_BF16");
+  }
+  if (c->vocab_size < 1 || c->padded_vocab_size < c->vocab_size)
+    return fail("need 1 <= vocab_size <= padded_vocab_size");
+  if (c->padded_vocab_size % 64 || c->padded_vocab_size > 51200)
+    return fail("padded_vocab_size must be a multiple of 64 and <= 51200");
+  if (c->block_size < 1 || c->max_batch < 1) return fail("block_size and max_batch must be >= 1");
+  return true;
+}
+
+Layout make_layout(const gpt2_config* c) {
+  Layout L;
+  const long C = c->n_embd, Vp = c->padded_vocab_size;
+  auto add = [&](long n, int decay) {
+    long o = L.P;
+    L.t_off.push_back(o);
+    L.t_len.push_back(n);
+    L.t_decay.push_back(decay);
+    L.P += n;
+    return o;
+  };
+  L.wte = add(Vp * C, 1);
+  L.wpe = add((long)c->block_size * C, 1);
+  for (int l = 0; l < c->n_layer; ++l) {
+    LayerOff o;
+    o.ln1w = add(C, 0);
+    o.ln1b = add(C, 0);
+    o.attnw = add(3 * C * C, 1);
+    o.attnb = add(3 * C, 0);
+    o.projw = add(C * C, 1);
+    o.projb = add(C, 0);
+    o.ln2w = add(C, 0);
+    o.ln2b = add(C, 0);
+    o.fcw = add(4 * C * C, 1);
+    o.fcb = add(4 * C, 0);
+    o.fc2w = add(4 * C * C, 1);
+    o.fc2b = add(C, 0);
+    L.layer.push_back(o);
+  }
+  L.lnfw = add(C, 0);
+  L.lnfb = add(C, 0);
+  return L;
+}
+
+constexpr long ADAM_CHUNK = 16384;
+
+std::vector<AdamChunk> make_chunks(const Layout& L) {
+  std::vector<AdamChunk> v;
+  for (size_t t = 0; t < L.t_off.size(); ++t)
+    for (long s = 0; s < L.t_len[t]; s += ADAM_CHUNK) {
+      AdamChunk ck;
+      ck.start = L.t_off[t] + s;
+      ck.len = (int)std::min(ADAM_CHUNK, L.t_len[t] - s);
+      ck.flags = L.t_decay[t];
+      v.push_back(ck);
+    }
+  return v;
+}
+
+// Bump allocator over the workspace (256-byte aligned pieces).
+struct Arena {
+  char* base;
+  size_t off = 0;
+  explicit Arena(char* b) : base(b) {}
+  void* take(size_t bytes) {
+    off = (off + 255) & ~(size_t)255;
+    void* p = base ? base + off : nullptr;
+    off += bytes;
+    return p;
+  }
+  template <typename T> T* take_n(size_t n) { return reinterpret_cast<T*>(take(n * sizeof(T))); }
+};
+
+}  // namespace
+
+struct gpt2 {
+  gpt2_config cfg;
+  hipStream_t stream;
+  DType act;
+  size_t act_size;
+  Layout lay;
+  int nchunks = 0;
+  // persistent state
+  float *params, *grads, *m, *v;
+  bf16_t* shadow;
+  AdamChunk* chunks;
+  int* err;
+  int* n_valid;
+  float *loss, *norm, *clip;
+  double* norm_partial;
+  int32_t* idx;
+  // activations
+  std::vector<LayerAct> A;
+  float* x_final;
+  float *meanf, *rstdf;
+  void* z;
+  void* logits;
+  float* row_loss;
+  // backward scratch
+  float* dres;
+  void* dres_b;
+  float* dxtmp;
+  void* dbig;
+  void* dqkv;
+  void* dy;
+  float* dbuf;
+  float* ln_partial;
+  float* bias_partial;
+  // state
+  int B = 0, T = 0;
+  bool have_targets = false;
+  bool forward_done = false;
+  int64_t step = 0;
+  std::string last_error;
+  // kernel timing (gpt2_timing_begin/end)
+  uint64_t timing_mask = 0;
+  std::vector<hipEvent_t> ev_pool;  // pairs: start, end
+  std::vector<int> ev_site;
+  size_t ev_used = 0;
+  ~gpt2() {
+    for (hipEvent_t e : ev_pool) (void)hipEventDestroy(e);
+  }
+};
+
+namespace {
+
+// Lays out the whole workspace; with h == nullptr only measures it.
+size_t plan(const gpt2_config* c, char* base, gpt2* h) {
+  Arena a(base);
+  Layout L = make_layout(c);
+  const size_t P = (size_t)L.P;
+  const size_t C = c->n_embd, H = c->n_head, Vp = c->padded_vocab_size;
+  const size_t BT = (size_t)c->max_batch * c->block_size;
+  const size_t es = c->precision == GPT2_BF16 ? 2 : 4;
+  std::vector<AdamChunk> ch = make_chunks(L);
+  float* params = a.take_n<float>(P);
+  float* grads = a.take_n<float>(P);
+  float* m = a.take_n<float>(P);
+  float* v = a.take_n<float>(P);
+  bf16_t* shadow = c->precision == GPT2_BF16 ? a.take_n<bf16_t>(P) : nullptr;
+  AdamChunk* chunks = a.take_n<AdamChunk>(ch.size());
+  int* err = a.take_n<int>(1);
+  int* n_valid = a.take_n<int>(1);
+  float* loss = a.take_n<float>(1);
+  float* norm = a.take_n<float>(1);
+  float* clip = a.take_n<float>(1);
+  double* norm_partial = a.take_n<double>(NORM_PARTS);
+  int32_t* idx = a.take_n<int32_t>(BT);
+  std::vector<LayerAct> acts(c->n_layer);
+  for (int l = 0; l < c->n_layer; ++l) {
+    LayerAct& x = acts[l];
+    x.x_in = a.take_n<float>(BT * C);
+    x.mean1 = a.take_n<float>(BT);
+    x.rstd1 = a.take_n<float>(BT);
+    x.u1 = a.take(BT * C * es);
+    x.qkv = a.take(BT * 3 * C * es);
+    x.y = a.take(BT * C * es);
+    x.lse = a.take_n<float>(BT * H);
+    x.x_mid = a.take_n<float>(BT * C);
+    x.mean2 = a.take_n<float>(BT);
+    x.rstd2 = a.take_n<float>(BT);
+    x.u2 = a.take(BT * C * es);
+    x.h = a.take(BT * 4 * C * es);
+    x.g = a.take(BT * 4 * C * es);
+  }
+  float* x_final = a.take_n<float>(BT * C);
+  float* meanf = a.take_n<float>(BT);
+  float* rstdf = a.take_n<float>(BT);
+  void* z = a.take(BT * C * es);
+  void* logits = a.take(BT * Vp * es);
+  float* row_loss = a.take_n<float>(BT);
+  float* dres = a.take_n<float>(BT * C);
+  void* dres_b = c->precision == GPT2_BF16 ? a.take(BT * C * es) : nullptr;
+  float* dxtmp = a.take_n<float>(BT * C);
+  void* dbig = a.take(BT * 4 * C * es);
+  void* dqkv = a.take(BT * 3 * C * es);
+  void* dy = a.take(BT * C * es);
+  float* dbuf = a.take_n<float>(BT * H);
+  float* ln_partial = a.take_n<float>((size_t)ln_bwd_blocks((long)BT) * 2 * C);
+  float* bias_partial = a.take_n<float>((size_t)BIAS_SPLITS * 4 * C);
+  size_t total = (a.off + 255) & ~(size_t)255;
+  if (h) {
+    h->lay = L;
+    h->nchunks = (int)ch.size();
+    h->params = params; h->grads = grads; h->m = m; h->v = v; h->shadow = shadow;
+    h->chunks = chunks; h->err = err; h->n_valid = n_valid; h->loss = loss; h->norm = norm;
+    h->clip = clip; h->norm_partial = norm_partial; h->idx = idx;
+    h->A = acts;
+    h->x_final = x_final; h->meanf = meanf; h->rstdf = rstdf; h->z = z; h->logits = logits;
+    h->row_loss = row_loss;
+    h->dres = dres; h->dres_b = dres_b; h->dxtmp = dxtmp; h->dbig = dbig; h->dqkv = dqkv;
+    h->dy = dy; h->dbuf = dbuf; h->ln_partial = ln_partial; h->bias_partial = bias_partial;
+  }
+  return total;
+}
+
+gpt2_status fail(gpt2* h, gpt2_status s, const std::string& msg) {
+  if (h) h->last_error = msg;
+  return s;
+}
+
+#define HIPTRY(h, expr)                                                              \
+  do {                                                                               \
+    hipError_t e_ = (expr);                                                          \
+    if (e_ != hipSuccess)                                                            \
+      return fail((h), GPT2_E_HIP, std::string(#expr) + ": " + hipGetErrorString(e_)); \
+  } while (0)
+
+// bf16 copy of the weights in bf16 mode, the fp32 master otherwise
+const void* W(const gpt2* h, long off) {
+  return h->act == DT_BF16 ? (const void*)(h->shadow + off) : (const void*)(h->params + off);
+}
+
+// Records an event pair around one launch when its site is being timed.
+struct Site {
+  gpt2* h;
+  long pair = -1;
+  Site(gpt2* hh, int site) : h(hh) {
+    if (!((h->timing_mask >> site) & 1)) return;
+    size_t i = h->ev_used;
+    while (h->ev_pool.size() < 2 * (i + 1)) {
+      hipEvent_t e;
+      if (hipEventCreate(&e) != hipSuccess) return;
+      h->ev_pool.push_back(e);
+    }
+    if (h->ev_site.size() < i + 1) h->ev_site.resize(i + 1);
+    h->ev_site[i] = site;
+    h->ev_used = i + 1;
+    pair = (long)i;
+    (void)hipEventRecord(h->ev_pool[2 * i], h->stream);
+  }
+  ~Site() {
+    if (pair >= 0) (void)hipEventRecord(h->ev_pool[2 * pair + 1], h->stream);
+  }
+};
+
+#define TIMED(h, site, expr) \
+  do {                       \
+    Site ts_((h), (site));   \
+    HIPTRY((h), (expr));     \
+  } while (0)
+
+EpiArgs epi(void* out, long ldo, float alpha = 1.f) {
+  EpiArgs e;
+  std::memset(&e, 0, sizeof(e));
+  e.out = out;
+  e.ldo = ldo;
+  e.alpha = alpha;
+  return e;
+}
+
+gpt2_status check_device_flags(gpt2* h) {
+  int f = 0;
+  HIPTRY(h, hipMemcpy(&f, h->err, sizeof(int), hipMemcpyDeviceToHost));
+  if (f) {
+    HIPTRY(h, hipMemset(h->err, 0, sizeof(int)));
+    std::string m;
+    if (f & ERRF_IDX) m += "token id outside [0, padded_vocab_size); ";
+    if (f & ERRF_TARGET) m += "target outside {-1} U [0, padded_vocab_size); ";
+    return fail(h, GPT2_E_RANGE, m + "offending values were read as 0");
+  }
+  return GPT2_OK;
+}
+
+gpt2_status sync(gpt2* h) {
+  HIPTRY(h, hipStreamSynchronize(h->stream));
+  return check_device_flags(h);
+}
+
+gpt2_status run_forward(gpt2* h, const int32_t* d_idx, const int32_t* d_tgt, int B, int T) {
+  const gpt2_config& c = h->cfg;
+  const int C = c.n_embd, H = c.n_head, hd = C / H, Vp = c.padded_vocab_size;
+  const long BT = (long)B * T;
+  const DType at = h->act;
+  hipStream_t s = h->stream;
+  float* P = h->params;
+  TIMED(h, GPT2_SITE_EMBED_FWD, launch_embed_fwd(d_idx, h->idx, P + h->lay.wte, P + h->lay.wpe, h->A[0].x_in, B, T, C,
+                             Vp, h->err, s));
+  for (int l = 0; l < c.n_layer; ++l) {
+    const LayerOff& o = h->lay.layer[l];
+    LayerAct& a = h->A[l];
+    float* x_out = l + 1 < c.n_layer ? h->A[l + 1].x_in : h->x_final;
+    TIMED(h, GPT2_SITE_LN_FWD, launch_layernorm_fwd(at, a.x_in, P + o.ln1w, P + o.ln1b, a.u1, a.mean1, a.rstd1, BT,
+                                   C, s));
+    EpiArgs e = epi(a.qkv, 3 * C);
+    e.bias = P + o.attnb;
+    TIMED(h, GPT2_SITE_QKV_FWD, launch_gemm(at, (int)BT, 3 * C, C, a.u1, C, false, W(h, o.attnw), C, false, EPI_STORE,
+                          at, e, 0, s));
+    TIMED(h, GPT2_SITE_ATTN_FWD, launch_attn_fwd(at, a.qkv, a.y, a.lse, B, T, H, hd, s));
+    e = epi(a.x_mid, C);
+    e.bias = P + o.projb;
+    e.resid = a.x_in;
+    e.ldr = C;
+    TIMED(h, GPT2_SITE_PROJ_FWD, launch_gemm(at, (int)BT, C, C, a.y, C, false, W(h, o.projw), C, false, EPI_RESID,
+                          DT_F32, e, 0, s));
+    TIMED(h, GPT2_SITE_LN_FWD, launch_layernorm_fwd(at, a.x_mid, P + o.ln2w, P + o.ln2b, a.u2, a.mean2, a.rstd2, BT,
+                                   C, s));
+    e = epi(a.h, 4 * C);
+    e.out2 = a.g;
+    e.bias = P + o.fcb;
+    TIMED(h, GPT2_SITE_FC_FWD, launch_gemm(at, (int)BT, 4 * C, C, a.u2, C, false, W(h, o.fcw), C, false,
+                          EPI_BIAS_GELU, at, e, 0, s));
+    e = epi(x_out, C);
+    e.bias = P + o.fc2b;
+    e.resid = a.x_mid;
+    e.ldr = C;
+    TIMED(h, GPT2_SITE_FCPROJ_FWD, launch_gemm(at, (int)BT, C, 4 * C, a.g, 4 * C, false, W(h, o.fc2w), 4 * C, false,
+                          EPI_RESID, DT_F32, e, 0, s));
+  }
+  TIMED(h, GPT2_SITE_LN_FWD, launch_layernorm_fwd(at, h->x_final, P + h->lay.lnfw, P + h->lay.lnfb, h->z, h->meanf,
+                                 h->rstdf, BT, C, s));
+  EpiArgs e = epi(h->logits, Vp);
+  TIMED(h, GPT2_SITE_LMHEAD_FWD, launch_gemm(at, (int)BT, Vp, C, h->z, C, false, W(h, h->lay.wte), C, false, EPI_STORE,
+                        at, e, 0, s));
+  if (d_tgt)
+    TIMED(h, GPT2_SITE_XENT, launch_xent(at, h->logits, d_tgt, h->n_valid, h->row_loss, h->loss, BT, Vp, h->err,
+                          s));
+  return GPT2_OK;
+}
+
+gpt2_status run_backward(gpt2* h, float scale) {
+  const gpt2_config& c = h->cfg;
+  const int B = h->B, T = h->T;
+  const int C = c.n_embd, H = c.n_head, hd = C / H, Vp = c.padded_vocab_size;
+  const long BT = (long)B * T;
+  const int M = (int)BT;
+  const DType at = h->act;
+  hipStream_t s = h->stream;
+  float* P = h->params;
+  float* G = h->grads;
+  const void* dres_in = at == DT_BF16 ? h->dres_b : (const void*)h->dres;
+  void* dres_copy = at == DT_BF16 ? h->dres_b : nullptr;
+
+  // lm_head (tied): dz = s dlogits wte ; dwte += s dlogits^T z
+  TIMED(h, GPT2_SITE_LMHEAD_DX, launch_gemm(at, M, C, Vp, h->logits, Vp, false, W(h, h->lay.wte), C, true, EPI_STORE,
+                        DT_F32, epi(h->dxtmp, C, scale), 0, s));
+  TIMED(h, GPT2_SITE_LMHEAD_DW, launch_gemm(at, Vp, C, M, h->logits, Vp, true, h->z, C, true, EPI_ACCUM, DT_F32,
+                        epi(G + h->lay.wte, C, scale), 0, s));
+  TIMED(h, GPT2_SITE_LN_BWD, launch_layernorm_bwd(at, h->dxtmp, h->x_final, h->meanf, h->rstdf, P + h->lay.lnfw,
+                                 h->dres, dres_copy, 0, h->ln_partial, G + h->lay.lnfw,
+                                 G + h->lay.lnfb, BT, C, s));
+  for (int l = c.n_layer - 1; l >= 0; --l) {
+    const LayerOff& o = h->lay.layer[l];
+    LayerAct& a = h->A[l];
+    // x_out = x_mid + c_proj(gelu(c_fc(ln_2(x_mid))))
+    EpiArgs e = epi(h->dbig, 4 * C);
+    e.aux = a.h;
+    e.ldx = 4 * C;
+    TIMED(h, GPT2_SITE_FCPROJ_DX, launch_gemm(at, M, 4 * C, C, dres_in, C, false, W(h, o.fc2w), 4 * C, true,
+                          EPI_GELU_BWD, at, e, 0, s));
+    TIMED(h, GPT2_SITE_FCPROJ_DW, launch_gemm(at, C, 4 * C, M, dres_in, C, true, a.g, 4 * C, true, EPI_ATOMIC, DT_F32,
+                          epi(G + o.fc2w, 4 * C), 0, s));
+    TIMED(h, GPT2_SITE_BIAS_GRAD, launch_bias_grad(DT_F32, h->dres, BT, C, C, h->bias_partial, G + o.fc2b, s));
+    TIMED(h, GPT2_SITE_FC_DX, launch_gemm(at, M, C, 4 * C, h->dbig, 4 * C, false, W(h, o.fcw), C, true, EPI_STORE,
+                          DT_F32, epi(h->dxtmp, C), 0, s));
+    TIMED(h, GPT2_SITE_FC_DW, launch_gemm(at, 4 * C, C, M, h->dbig, 4 * C, true, a.u2, C, true, EPI_ATOMIC, DT_F32,
+                          epi(G + o.fcw, C), 0, s));
+    TIMED(h, GPT2_SITE_BIAS_GRAD, launch_bias_grad(at, h->dbig, BT, 4 * C, 4 * C, h->bias_partial, G + o.fcb, s));
+    TIMED(h, GPT2_SITE_LN_BWD, launch_layernorm_bwd(at, h->dxtmp, a.x_mid, a.mean2, a.rstd2, P + o.ln2w, h->dres,
+                                   dres_copy, 1, h->ln_partial, G + o.ln2w, G + o.ln2b, BT, C, s));
+    // x_mid = x_in + c_proj(attn(ln_1(x_in)))
+    TIMED(h, GPT2_SITE_PROJ_DX, launch_gemm(at, M, C, C, dres_in, C, false, W(h, o.projw), C, true, EPI_STORE, at,
+                          epi(h->dy, C), 0, s));
+    TIMED(h, GPT2_SITE_PROJ_DW, launch_gemm(at, C, C, M, dres_in, C, true, a.y, C, true, EPI_ATOMIC, DT_F32,
+                          epi(G + o.projw, C), 0, s));
+    TIMED(h, GPT2_SITE_BIAS_GRAD, launch_bias_grad(DT_F32, h->dres, BT, C, C, h->bias_partial, G + o.projb, s));
+    TIMED(h, GPT2_SITE_ATTN_BWD, launch_attn_bwd(at, a.qkv, a.y, a.lse, h->dy, h->dqkv, h->dbuf, B, T, H, hd, s));
+    TIMED(h, GPT2_SITE_QKV_DX, launch_gemm(at, M, C, 3 * C, h->dqkv, 3 * C, false, W(h, o.attnw), C, true,
+                          EPI_STORE, DT_F32, epi(h->dxtmp, C), 0, s));
+    TIMED(h, GPT2_SITE_QKV_DW, launch_gemm(at, 3 * C, C, M, h->dqkv, 3 * C, true, a.u1, C, true, EPI_ATOMIC, DT_F32,
+                          epi(G + o.attnw, C), 0, s));
+    TIMED(h, GPT2_SITE_BIAS_GRAD, launch_bias_grad(at, h->dqkv, BT, 3 * C, 3 * C, h->bias_partial, G + o.attnb, s));
+    TIMED(h, GPT2_SITE_LN_BWD, launch_layernorm_bwd(at, h->dxtmp, a.x_in, a.mean1, a.rstd1, P + o.ln1w, h->dres,
+                                   dres_copy, 1, h->ln_partial, G + o.ln1w, G + o.ln1b, BT, C, s));
+  }
+  TIMED(h, GPT2_SITE_EMBED_BWD, launch_embed_bwd(h->idx, h->dres, G + h->lay.wte, G + h->lay.wpe, B, T, C, s));
+  return GPT2_OK;
+}
+
+float* state_ptr(gpt2* h, int which) {
+  switch (which) {
+    case GPT2_PARAMS: return h->params;
+    case GPT2_GRADS: return h->grads;
+    case GPT2_ADAM_M: return h->m;
+    case GPT2_ADAM_V: return h->v;
+  }
+  return nullptr;
+}
+
+}  // namespace
+
+// ===========================================================================
+// C ABI
+// ===========================================================================
+extern "C" {
+
+size_t gpt2_num_params(const gpt2_config* cfg) {
+  if (!valid_config(cfg, nullptr)) return 0;
+  return (size_t)make_layout(cfg).P;
+}
+
+gpt2_status gpt2_workspace_bytes(const gpt2_config* cfg, size_t* bytes) {
+  if (!bytes || !valid_config(cfg, nullptr)) return GPT2_E_ARG;
+  *bytes = plan(cfg, nullptr, nullptr);
+  return GPT2_OK;
+}
+
+gpt2_status gpt2_init(const gpt2_config* cfg, void* d_workspace, size_t ws_bytes,
+                      void* hip_stream, gpt2_t** out) {
+  if (!out) return GPT2_E_ARG;
+  *out = nullptr;
+  if (!valid_config(cfg, nullptr) || !d_workspace) return GPT2_E_ARG;
+  if (reinterpret_cast<uintptr_t>(d_workspace) % 256) return GPT2_E_ARG;
+  size_t need = plan(cfg, nullptr, nullptr);
+  if (ws_bytes < need) return GPT2_E_ARG;
+  gpt2* h = new gpt2();
+  h->cfg = *cfg;
+  h->stream = reinterpret_cast<hipStream_t>(hip_stream);
+  h->act = cfg->precision == GPT2_BF16 ? DT_BF16 : DT_F32;
+  h->act_size = h->act == DT_BF16 ? 2 : 4;
+  plan(cfg, reinterpret_cast<char*>(d_workspace), h);
+  std::vector<AdamChunk> ch = make_chunks(h->lay);
+  hipError_t e = hipMemcpyAsync(h->chunks, ch.data(), ch.size() * sizeof(AdamChunk),
+                                hipMemcpyHostToDevice, h->stream);
+  for (float* t : {h->params, h->grads, h->m, h->v})
+    if (e == hipSuccess) e = launch_fill(t, h->lay.P, 0.f, h->stream);
+  if (e == hipSuccess && h->shadow) e = hipMemsetAsync(h->shadow, 0, h->lay.P * 2, h->stream);
+  if (e == hipSuccess) e = hipMemsetAsync(h->err, 0, sizeof(int), h->stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(h->stream);
+  if (e != hipSuccess) {
+    delete h;
+    return GPT2_E_HIP;
+  }
+  *out = h;
+  return GPT2_OK;
+}
+
+gpt2_status gpt2_set_params(gpt2_t* h, const float* src, size_t n, int src_on_device) {
+  if (!h || !src) return GPT2_E_ARG;
+  if (n != (size_t)h->lay.P) return fail(h, GPT2_E_ARG, "n != gpt2_num_params");
+  HIPTRY(h, hipMemcpyAsync(h->params, src, n * 4,
+                           src_on_device ? hipMemcpyDeviceToDevice : hipMemcpyHostToDevice,
+                           h->stream));
+  if (h->shadow) HIPTRY(h, launch_f32_to_bf16(h->params, h->shadow, (long)n, h->stream));
+  for (float* t : {h->grads, h->m, h->v}) HIPTRY(h, launch_fill(t, (long)n, 0.f, h->stream));
+  h->step = 0;
+  if (!src_on_device) HIPTRY(h, hipStreamSynchronize(h->stream));
+  return GPT2_OK;
+}
+
+gpt2_status gpt2_get(gpt2_t* h, int which, float* dst, size_t n, int dst_on_device) {
+  if (!h || !dst) return GPT2_E_ARG;
+  float* p = state_ptr(h, which);
+  if (!p) return fail(h, GPT2_E_ARG, "unknown state id");
+  if (n != (size_t)h->lay.P) return fail(h, GPT2_E_ARG, "n != gpt2_num_params");
+  HIPTRY(h, hipMemcpyAsync(dst, p, n * 4,
+                           dst_on_device ? hipMemcpyDeviceToDevice : hipMemcpyDeviceToHost,
+                           h->stream));
+  if (!dst_on_device) return sync(h);
+  return GPT2_OK;
+}
+
+gpt2_status gpt2_set_state(gpt2_t* h, int which, const float* src, size_t n, int src_on_device) {
+  if (!h || !src) return GPT2_E_ARG;
+  if (which == GPT2_PARAMS) return fail(h, GPT2_E_ARG, "use gpt2_set_params for parameters");
+  float* p = state_ptr(h, which);
+  if (!p) return fail(h, GPT2_E_ARG, "unknown state id");
+  if (n != (size_t)h->lay.P) return fail(h, GPT2_E_ARG, "n != gpt2_num_params");
+  HIPTRY(h, hipMemcpyAsync(p, src, n * 4,
+                           src_on_device ? hipMemcpyDeviceToDevice : hipMemcpyHostToDevice,
+                           h->stream));
+  if (!src_on_device) HIPTRY(h, hipStreamSynchronize(h->stream));
+  return GPT2_OK;
+}
+
+gpt2_status gpt2_get_step(const gpt2_t* h, int64_t* t) {
+  if (!h || !t) return GPT2_E_ARG;
+  *t = h->step;
+  return GPT2_OK;
+}
+
+gpt2_status gpt2_set_step(gpt2_t* h, int64_t t) {
+  if (!h || t < 0) return GPT2_E_ARG;
+  h->step = t;
+  return GPT2_OK;
+}
+
+gpt2_status gpt2_forward(gpt2_t* h, const int32_t* d_idx, const int32_t* d_targets, int B, int T,
+                         float* h_loss) {
+  if (!h || !d_idx) return GPT2_E_ARG;
+  if (B < 1 || B > h->cfg.max_batch || T < 1 || T > h->cfg.block_size)
+    return fail(h, GPT2_E_SHAPE, "need 1 <= B <= max_batch and 1 <= T <= block_size");
+  h->B = B;
+  h->T = T;
+  h->have_targets = false;
+  h->forward_done = false;
+  gpt2_status st = run_forward(h, d_idx, d_targets, B, T);
+  if (st != GPT2_OK) return st;
+  h->forward_done = true;
+  h->have_targets = d_targets != nullptr;
+  if (h_loss) {
+    if (!d_targets) return fail(h, GPT2_E_ARG, "h_loss given without targets");
+    return gpt2_get_loss(h, h_loss);
+  }
+  return GPT2_OK;
+}
+
+gpt2_status gpt2_get_loss(gpt2_t* h, float* h_loss) {
+  if (!h || !h_loss) return GPT2_E_ARG;
+  gpt2_status st = sync(h);
+  if (st != GPT2_OK) return st;
+  HIPTRY(h, hipMemcpy(h_loss, h->loss, sizeof(float), hipMemcpyDeviceToHost));
+  return GPT2_OK;
+}
+
+gpt2_status gpt2_zero_grad(gpt2_t* h) {
+  if (!h) return GPT2_E_ARG;
+  TIMED(h, GPT2_SITE_ZERO_GRAD, launch_fill(h->grads, h->lay.P, 0.f, h->stream));
+  return GPT2_OK;
+}
+
+gpt2_status gpt2_backward(gpt2_t* h, float loss_scale) {
+  if (!h) return GPT2_E_ARG;
+  if (!h->forward_done || !h->have_targets)
+    return fail(h, GPT2_E_STATE, "backward needs a preceding forward with targets");
+  h->have_targets = false;  // the logit gradient is consumed
+  return run_backward(h, loss_scale);
+}
+
+gpt2_status gpt2_adamw_step(gpt2_t* h, float lr, float beta1, float beta2, float eps,
+                            float weight_decay, float max_grad_norm, float* h_grad_norm) {
+  if (!h) return GPT2_E_ARG;
+  if (!(beta1 >= 0.f && beta1 < 1.f && beta2 >= 0.f && beta2 < 1.f && eps >= 0.f))
+    return fail(h, GPT2_E_ARG, "need 0 <= beta < 1 and eps >= 0");
+  h->step += 1;
+  const double t = (double)h->step;
+  const double bc1 = 1.0 - std::pow((double)beta1, t);
+  const double bc2 = 1.0 - std::pow((double)beta2, t);
+  const float step_size = (float)(lr / bc1);
+  const float inv_sqrt_bc2 = (float)(1.0 / std::sqrt(bc2));
+  TIMED(h, GPT2_SITE_GRAD_NORM, launch_grad_norm(h->grads, h->lay.P, h->norm_partial, max_grad_norm, h->norm, h->clip,
+                             h->stream));
+  TIMED(h, GPT2_SITE_ADAMW, launch_adamw(h->chunks, h->nchunks, h->params, h->grads, h->m, h->v, h->shadow,
+                         h->clip, lr, beta1, beta2, eps, weight_decay, step_size, inv_sqrt_bc2,
+                         h->stream));
+  if (h_grad_norm) return gpt2_get_grad_norm(h, h_grad_norm);
+  return GPT2_OK;
+}
+
+gpt2_status gpt2_get_grad_norm(gpt2_t* h, float* h_norm) {
+  if (!h || !h_norm) return GPT2_E_ARG;
+  gpt2_status st = sync(h);
+  if (st != GPT2_OK) return st;
+  HIPTRY(h, hipMemcpy(h_norm, h->norm, sizeof(float), hipMemcpyDeviceToHost));
+  return GPT2_OK;
+}
+
+gpt2_status gpt2_sync(gpt2_t* h) {
+  if (!h) return GPT2_E_ARG;
+  return sync(h);
+}
+
+gpt2_status gpt2_timing_begin(gpt2_t* h, uint64_t site_mask) {
+  if (!h) return GPT2_E_ARG;
+  h->timing_mask = site_mask;
+  h->ev_used = 0;
+  return GPT2_OK;
+}
+
+gpt2_status gpt2_timing_end(gpt2_t* h, double* ms, int32_t* launches) {
+  if (!h) return GPT2_E_ARG;
+  h->timing_mask = 0;
+  HIPTRY(h, hipStreamSynchronize(h->stream));
+  std::vector<double> acc(GPT2_NUM_SITES, 0.0);
+  std::vector<int32_t> cnt(GPT2_NUM_SITES, 0);
+  for (size_t i = 0; i < h->ev_used; ++i) {
+    float t = 0.f;
+    HIPTRY(h, hipEventElapsedTime(&t, h->ev_pool[2 * i], h->ev_pool[2 * i + 1]));
+    acc[h->ev_site[i]] += t;
+    cnt[h->ev_site[i]] += 1;
+  }
+  h->ev_used = 0;
+  for (int i = 0; i < GPT2_NUM_SITES; ++i) {
+    if (ms) ms[i] = acc[i];
+    if (launches) launches[i] = cnt[i];
+  }
+  return GPT2_OK;
+}
+
+const char* gpt2_last_error(const gpt2_t* h) { return h ? h->last_error.c_str() : "null handle"; }
+
+void gpt2_destroy(gpt2_t* h) { delete h; }
+
+gpt2_status gpt2_get_activation(gpt2_t* h, int which, int layer, float* h_dst, size_t n) {
+  if (!h || !h_dst) return GPT2_E_ARG;
+  if (!h->forward_done) return fail(h, GPT2_E_STATE, "no forward pass has run");
+  const gpt2_config& c = h->cfg;
+  const size_t BT = (size_t)h->B * h->T, C = c.n_embd;
+  const void* src = nullptr;
+  size_t count = 0;
+  bool f32 = false;
+  bool per_layer = which != GPT2_ACT_LNF && which != GPT2_ACT_LOGITS && which != GPT2_ACT_ROW_LOSS;
+  int maxl = which == GPT2_ACT_X_IN ? c.n_layer : c.n_layer - 1;
+  if (per_layer && (layer < 0 || layer > maxl)) return fail(h, GPT2_E_ARG, "layer out of range");
+  const LayerAct* a = per_layer && layer < c.n_layer ? &h->A[layer] : nullptr;
+  switch (which) {
+    case GPT2_ACT_X_IN: src = layer == c.n_layer ? h->x_final : a->x_in; count = BT * C; f32 = true; break;
+    case GPT2_ACT_LN1: src = a->u1; count = BT * C; break;
+    case GPT2_ACT_QKV: src = a->qkv; count = BT * 3 * C; break;
+    case GPT2_ACT_ATTN_Y: src = a->y; count = BT * C; break;
+    case GPT2_ACT_LSE: src = a->lse; count = BT * c.n_head; f32 = true; break;
+    case GPT2_ACT_X_MID: src = a->x_mid; count = BT * C; f32 = true; break;
+    case GPT2_ACT_LN2: src = a->u2; count = BT * C; break;
+    case GPT2_ACT_FC_PRE: src = a->h; count = BT * 4 * C; break;
+    case GPT2_ACT_FC_GELU: src = a->g; count = BT * 4 * C; break;
+    case GPT2_ACT_LNF: src = h->z; count = BT * C; break;
+    case GPT2_ACT_LOGITS: src = h->logits; count = BT * c.padded_vocab_size; break;
+    case GPT2_ACT_ROW_LOSS: src = h->row_loss; count = BT; f32 = true; break;
+    default: return fail(h, GPT2_E_ARG, "unknown activation id");
+  }
+  if (n != count) return fail(h, GPT2_E_ARG, "n does not match the activation's element count");
+  gpt2_status st = sync(h);
+  if (st != GPT2_OK) return st;
+  if (f32 || h->act == DT_F32) {
+    HIPTRY(h, hipMemcpy(h_dst, src, count * 4, hipMemcpyDeviceToHost));
+  } else {
+    std::vector<uint16_t> tmp(count);
+    HIPTRY(h, hipMemcpy(tmp.data(), src, count * 2, hipMemcpyDeviceToHost));
+    for (size_t i = 0; i < count; ++i) {
+      uint32_t u = (uint32_t)tmp[i] << 16;
+      std::memcpy(h_dst + i, &u, 4);
+    }
+  }
+  return GPT2_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,568 @@
+// Causal self-attention ("GPT-2 from Scratch", CausalSelfAttention;
+// "Let's reproduce GPT-2 (124M)", FlashAttention paragraph):
+//   S = q k^T / sqrt(hd), S[i][j>i] = -inf, P = softmax(S), O = P v,
+// computed with an online softmax over key blocks so that the T x T matrix is
+// never stored; the backward pass rebuilds P from the saved row log-sum-exp.
+//
+// bf16, head width 64: matrix-core kernels (v_mfma_f32_32x32x16_bf16).
+// fp32 (any head width <= 64): one thread per (batch, head, position).
+#include "kernels.h"
+
+#define NEG_INF (-__builtin_inff())
+constexpr float LOG2E_F = 1.4426950408889634f;
+constexpr float LN2_F = 0.6931471805599453f;
+
+// ===========================================================================
+// fp32 path
+// ===========================================================================
+template <typename T, int HD>
+__global__ __launch_bounds__(128) void attn_fwd_simt(const T* __restrict__ qkv, T* __restrict__ y,
+                                                     float* __restrict__ lse, int B, int Tn, int H,
+                                                     int C) {
+  long i = (long)blockIdx.x * 128 + threadIdx.x;
+  if (i >= (long)B * H * Tn) return;
+  int t = (int)(i % Tn);
+  int bh = (int)(i / Tn), h = bh % H, b = bh / H;
+  const long ld = 3L * C;
+  const float scale = 1.0f / sqrtf((float)HD);
+  const T* qr = qkv + ((long)b * Tn + t) * ld + h * HD;
+  float q[HD], o[HD];
+#pragma unroll
+  for (int d = 0; d < HD; ++d) {
+    q[d] = ldf(qr + d) * scale;
+    o[d] = 0.f;
+  }
+  float m = NEG_INF, l = 0.f;
+  for (int j = 0; j <= t; ++j) {
+    const T* kr = qkv + ((long)b * Tn + j) * ld + C + h * HD;
+    float sc = 0.f;
+#pragma unroll
+    for (int d = 0; d < HD; ++d) sc += q[d] * ldf(kr + d);
+    float mn = fmaxf(m, sc);
+    float a = expf(m - mn), p = expf(sc - mn);
+    l = l * a + p;
+    const T* vr = kr + C;
+#pragma unroll
+    for (int d = 0; d < HD; ++d) o[d] = o[d] * a + p * ldf(vr + d);
+    m = mn;
+  }
+  T* yr = y + ((long)b * Tn + t) * C + h * HD;
+#pragma unroll
+  for (int d = 0; d < HD; ++d) stf(yr + d, o[d] / l);
+  lse[i] = m + logf(l);
+}
+
+// dQ for one (b, h, t) and D = rowsum(dO * O), which the dK/dV pass reuses.
+template <typename T, int HD>
+__global__ __launch_bounds__(128) void attn_bwd_dq_simt(const T* __restrict__ qkv,
+                                                        const T* __restrict__ y,
+                                                        const float* __restrict__ lse,
+                                                        const T* __restrict__ dy,
+                                                        T* __restrict__ dqkv, float* __restrict__ dbuf,
+                                                        int B, int Tn, int H, int C) {
+  long i = (long)blockIdx.x * 128 + threadIdx.x;
+  if (i >= (long)B * H * Tn) return;
+  int t = (int)(i % Tn);
+  int bh = (int)(i / Tn), h = bh % H, b = bh / H;
+  const long ld = 3L * C;
+  const float scale = 1.0f / sqrtf((float)HD);
+  const long row = (long)b * Tn + t;
+  float q[HD], go[HD], dq[HD];
+  float D = 0.f;
+#pragma unroll
+  for (int d = 0; d < HD; ++d) {
+    q[d] = ldf(qkv + row * ld + h * HD + d);
+    go[d] = ldf(dy + row * C + h * HD + d);
+    D += go[d] * ldf(y + row * C + h * HD + d);
+    dq[d] = 0.f;
+  }
+  dbuf[i] = D;
+  const float L = lse[i];
+  for (int j = 0; j <= t; ++j) {
+    const T* kr = qkv + ((long)b * Tn + j) * ld + C + h * HD;
+    const T* vr = kr + C;
+    float sc = 0.f, dp = 0.f;
+#pragma unroll
+    for (int d = 0; d < HD; ++d) {
+      sc += q[d] * ldf(kr + d);
+      dp += go[d] * ldf(vr + d);
+    }
+    float p = expf(sc * scale - L);
+    float ds = p * (dp - D);
+#pragma unroll
+    for (int d = 0; d < HD; ++d) dq[d] += ds * ldf(kr + d);
+  }
+#pragma unroll
+  for (int d = 0; d < HD; ++d) stf(dqkv + row * ld + h * HD + d, dq[d] * scale);
+}
+
+template <typename T, int HD>
+__global__ __launch_bounds__(128) void attn_bwd_dkv_simt(const T* __restrict__ qkv,
+                                                         const float* __restrict__ lse,
+                                                         const T* __restrict__ dy,
+                                                         const float* __restrict__ dbuf,
+                                                         T* __restrict__ dqkv, int B, int Tn, int H,
+                                                         int C) {
+  long i = (long)blockIdx.x * 128 + threadIdx.x;
+  if (i >= (long)B * H * Tn) return;
+  int j = (int)(i % Tn);
+  int bh = (int)(i / Tn), h = bh % H, b = bh / H;
+  const long ld = 3L * C;
+  const float scale = 1.0f / sqrtf((float)HD);
+  const long row = (long)b * Tn + j;
+  float k[HD], v[HD], dk[HD], dv[HD];
+#pragma unroll
+  for (int d = 0; d < HD; ++d) {
+    k[d] = ldf(qkv + row * ld + C + h * HD + d);
+    v[d] = ldf(qkv + row * ld + 2 * C + h * HD + d);
+    dk[d] = dv[d] = 0.f;
+  }
+  for (int t = j; t < Tn; ++t) {
+    const long r = (long)b * Tn + t;
+    const T* qr = qkv + r * ld + h * HD;
+    const T* gr = dy + r * C + h * HD;
+    float sc = 0.f, dp = 0.f;
+#pragma unroll
+    for (int d = 0; d < HD; ++d) {
+      sc += ldf(qr + d) * k[d];
+      dp += ldf(gr + d) * v[d];
+    }
+    long li = (long)bh * Tn + t;
+    float p = expf(sc * scale - lse[li]);
+    float ds = p * (dp - dbuf[li]);
+#pragma unroll
+    for (int d = 0; d < HD; ++d) {
+      dv[d] += p * ldf(gr + d);
+      dk[d] += ds * ldf(qr + d);
+    }
+  }
+#pragma unroll
+  for (int d = 0; d < HD; ++d) {
+    stf(dqkv + row * ld + C + h * HD + d, dk[d] * scale);
+    stf(dqkv + row * ld + 2 * C + h * HD + d, dv[d]);
+  }
+}
+
+// ===========================================================================
+// bf16 matrix-core path, head width 64
+//
+// Each workgroup has 4 wavefronts; a wavefront owns 32 queries (forward, dQ)
+// or 32 keys (dK/dV).  Within a 32x32 MFMA tile the lane index l maps to
+// column l%32 and the half l/32 selects which 8 of the 16 contraction slots
+// the lane supplies.  Scores are formed transposed where the softmax runs per
+// query (S^T = K Q^T: lane <-> query, so the row max/sum are per lane plus
+// one exchange with lane^32), and untransposed where the reduction runs over
+// queries (S = Q K^T in the dK/dV pass: lane <-> key).  The probability tile
+// stays in registers and feeds the next MFMA as its 32-wide operand: its 16
+// accumulator values per lane are {8i + 4(l/32) + j}, and the other operand
+// is read from a transposed LDS tile in exactly that contraction order
+// (which is free to choose, since it is a sum).
+// ===========================================================================
+namespace {
+constexpr int ATS = 68;  // row stride (elements) of transposed LDS tiles [64 d][64 + 4]
+
+__device__ __forceinline__ int swz(int row, int c) { return c ^ ((row ^ (row >> 3)) & 7); }
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
+
+// 64 rows x 64 columns (16-byte chunks swizzled by row), rows row0.. of X.
+__device__ __forceinline__ void stage_rows(bf16_t* s, const bf16_t* __restrict__ X, long ld,
+                                           int row0, int nrows, int tid) {
+  const int c = tid & 7;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    int r = (tid >> 3) + 32 * i;
+    int row = row0 + r;
+    uint4 v = row < nrows ? *reinterpret_cast<const uint4*>(X + (long)row * ld + c * 8)
+                          : make_uint4(0, 0, 0, 0);
+    *reinterpret_cast<uint4*>(s + r * 64 + swz(r, c) * 8) = v;
+  }
+}
+
+// Transposed: s[d][r] = X[row0 + r][d] for d, r < 64 (row stride ATS).
+__device__ __forceinline__ void stage_cols(bf16_t* s, const bf16_t* __restrict__ X, long ld,
+                                           int row0, int nrows, int tid) {
+  const int dp = tid & 31, kg = tid >> 5;
+  uint32_t u[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    int row = row0 + kg * 8 + j;
+    u[j] = row < nrows ? *reinterpret_cast<const uint32_t*>(X + (long)row * ld + 2 * dp) : 0u;
+  }
+  bf16_t* d0 = s + (2 * dp) * ATS + kg * 8;
+  bf16_t* d1 = d0 + ATS;
+  *reinterpret_cast<uint2*>(d0) =
+      make_uint2(__byte_perm(u[0], u[1], 0x5410u), __byte_perm(u[2], u[3], 0x5410u));
+  *reinterpret_cast<uint2*>(d0 + 4) =
+      make_uint2(__byte_perm(u[4], u[5], 0x5410u), __byte_perm(u[6], u[7], 0x5410u));
+  *reinterpret_cast<uint2*>(d1) =
+      make_uint2(__byte_perm(u[0], u[1], 0x7632u), __byte_perm(u[2], u[3], 0x7632u));
+  *reinterpret_cast<uint2*>(d1 + 4) =
+      make_uint2(__byte_perm(u[4], u[5], 0x7632u), __byte_perm(u[6], u[7], 0x7632u));
+}
+
+__device__ __forceinline__ bf16x8_t frag_rows(const bf16_t* s, int row, int c) {
+  return *reinterpret_cast<const bf16x8_t*>(s + row * 64 + swz(row, c) * 8);
+}
+
+// Operand fragment of a transposed tile for contraction slots
+// {base + 4h + 0..3, base + 8 + 4h + 0..3} of row d.
+__device__ __forceinline__ bf16x8_t frag_cols(const bf16_t* s, int d, int base, int h) {
+  uint2 lo = *reinterpret_cast<const uint2*>(s + d * ATS + base + 4 * h);
+  uint2 hi = *reinterpret_cast<const uint2*>(s + d * ATS + base + 8 + 4 * h);
+  return as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
+}
+
+// Accumulator values 8u .. 8u+7 as a bf16 operand (contraction slots 16u..16u+15).
+__device__ __forceinline__ bf16x8_t pack_acc(const f32x16_t& a, int u) {
+  return as_bf16x8(make_uint4(pack_bf2(a[8 * u + 0], a[8 * u + 1]), pack_bf2(a[8 * u + 2], a[8 * u + 3]),
+                              pack_bf2(a[8 * u + 4], a[8 * u + 5]), pack_bf2(a[8 * u + 6], a[8 * u + 7])));
+}
+
+__device__ __forceinline__ f32x16_t mfma(bf16x8_t a, bf16x8_t b, f32x16_t c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x16_t zero16() {
+  f32x16_t z;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) z[i] = 0.f;
+  return z;
+}
+
+__device__ __forceinline__ float dot8(uint4 a, uint4 b) {
+  float s = 0.f;
+  uint32_t aw[4] = {a.x, a.y, a.z, a.w}, bw[4] = {b.x, b.y, b.z, b.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    s += __uint_as_float(aw[i] << 16) * __uint_as_float(bw[i] << 16);
+    s += __uint_as_float(aw[i] & 0xffff0000u) * __uint_as_float(bw[i] & 0xffff0000u);
+  }
+  return s;
+}
+}  // namespace
+
+__global__ __launch_bounds__(256) void attn_fwd_mfma(const bf16_t* __restrict__ qkv,
+                                                     bf16_t* __restrict__ y,
+                                                     float* __restrict__ lse, int Tn, int H, int C) {
+  __shared__ __attribute__((aligned(16))) bf16_t sK[64 * 64];
+  __shared__ __attribute__((aligned(16))) bf16_t sVt[64 * ATS];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, half = lane >> 5, l32 = lane & 31;
+  const int qb = gridDim.x - 1 - blockIdx.x;  // longest rows first
+  const int bh = blockIdx.y, b = bh / H, h = bh % H;
+  const long ld = 3L * C;
+  const bf16_t* base = qkv + (long)b * Tn * ld;
+  const int q0w = qb * 128 + w * 32;
+  const int myq = q0w + l32;
+  const float sl2 = 0.125f * LOG2E_F;
+
+  bf16x8_t qf[4];
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk)
+    qf[kk] = as_bf16x8(myq < Tn ? *reinterpret_cast<const uint4*>(base + (long)myq * ld + h * 64 +
+                                                                 kk * 16 + half * 8)
+                                : make_uint4(0, 0, 0, 0));
+  f32x16_t o0 = zero16(), o1 = zero16();
+  float m2 = NEG_INF, ls = 0.f;
+  const int kend = Tn < qb * 128 + 128 ? Tn : qb * 128 + 128;
+  for (int k0 = 0; k0 < kend; k0 += 64) {
+    __syncthreads();
+    stage_rows(sK, base + C + h * 64, ld, k0, Tn, tid);
+    stage_cols(sVt, base + 2 * C + h * 64, ld, k0, Tn, tid);
+    __syncthreads();
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const int kb = k0 + 32 * s;
+      if (kb > q0w + 31 || kb >= Tn) break;
+      f32x16_t st = zero16();
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) st = mfma(frag_rows(sK, 32 * s + l32, kk * 2 + half), qf[kk], st);
+      float mx = NEG_INF;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        int key = kb + 8 * (r >> 2) + 4 * half + (r & 3);
+        float x = st[r] * sl2;
+        if (key > myq || key >= Tn) x = NEG_INF;
+        st[r] = x;
+        mx = fmaxf(mx, x);
+      }
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      const float mn = fmaxf(m2, mx);
+      const float ms = mn == NEG_INF ? 0.f : mn;
+      const float alpha = exp2f(m2 - ms);
+      m2 = mn;
+      ls *= alpha;
+      o0 *= alpha;
+      o1 *= alpha;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        st[r] = exp2f(st[r] - ms);
+        ls += st[r];
+      }
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        bf16x8_t pb = pack_acc(st, u);
+        o0 = mfma(frag_cols(sVt, l32, 32 * s + 16 * u, half), pb, o0);
+        o1 = mfma(frag_cols(sVt, 32 + l32, 32 * s + 16 * u, half), pb, o1);
+      }
+    }
+  }
+  const float lt = ls + __shfl_xor(ls, 32, 64);
+  const float inv = 1.0f / lt;
+  if (myq < Tn) {
+    bf16_t* yr = y + ((long)b * Tn + myq) * C + h * 64;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float v0[4] = {o0[4 * i] * inv, o0[4 * i + 1] * inv, o0[4 * i + 2] * inv, o0[4 * i + 3] * inv};
+      float v1[4] = {o1[4 * i] * inv, o1[4 * i + 1] * inv, o1[4 * i + 2] * inv, o1[4 * i + 3] * inv};
+      st4(yr + 8 * i + 4 * half, v0);
+      st4(yr + 32 + 8 * i + 4 * half, v1);
+    }
+    if (half == 0) lse[(long)bh * Tn + myq] = (m2 + log2f(lt)) * LN2_F;
+  }
+}
+
+// dQ = (P o (dP - D)) K / sqrt(hd) per block of 128 queries; also D = rowsum(dO o O).
+__global__ __launch_bounds__(256) void attn_bwd_dq_mfma(const bf16_t* __restrict__ qkv,
+                                                        const bf16_t* __restrict__ y,
+                                                        const float* __restrict__ lse,
+                                                        const bf16_t* __restrict__ dy,
+                                                        bf16_t* __restrict__ dqkv,
+                                                        float* __restrict__ dbuf, int Tn, int H,
+                                                        int C) {
+  __shared__ __attribute__((aligned(16))) bf16_t sK[64 * 64];
+  __shared__ __attribute__((aligned(16))) bf16_t sV[64 * 64];
+  __shared__ __attribute__((aligned(16))) bf16_t sKt[64 * ATS];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, half = lane >> 5, l32 = lane & 31;
+  const int qb = gridDim.x - 1 - blockIdx.x;
+  const int bh = blockIdx.y, b = bh / H, h = bh % H;
+  const long ld = 3L * C;
+  const bf16_t* base = qkv + (long)b * Tn * ld;
+  const bf16_t* dyb = dy + (long)b * Tn * C;
+  const bf16_t* yb = y + (long)b * Tn * C;
+  const int q0w = qb * 128 + w * 32;
+  const int myq = q0w + l32;
+  const float sl2 = 0.125f * LOG2E_F;
+
+  bf16x8_t qf[4], gf[4];
+  float dd = 0.f;
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+    uint4 q = make_uint4(0, 0, 0, 0), g = q, o = q;
+    if (myq < Tn) {
+      q = *reinterpret_cast<const uint4*>(base + (long)myq * ld + h * 64 + kk * 16 + half * 8);
+      g = *reinterpret_cast<const uint4*>(dyb + (long)myq * C + h * 64 + kk * 16 + half * 8);
+      o = *reinterpret_cast<const uint4*>(yb + (long)myq * C + h * 64 + kk * 16 + half * 8);
+    }
+    qf[kk] = as_bf16x8(q);
+    gf[kk] = as_bf16x8(g);
+    dd += dot8(g, o);
+  }
+  dd += __shfl_xor(dd, 32, 64);
+  if (myq < Tn && half == 0) dbuf[(long)bh * Tn + myq] = dd;
+  const float lse2 = myq < Tn ? lse[(long)bh * Tn + myq] * LOG2E_F : 0.f;
+
+  f32x16_t dq0 = zero16(), dq1 = zero16();
+  const int kend = Tn < qb * 128 + 128 ? Tn : qb * 128 + 128;
+  for (int k0 = 0; k0 < kend; k0 += 64) {
+    __syncthreads();
+    stage_rows(sK, base + C + h * 64, ld, k0, Tn, tid);
+    stage_rows(sV, base + 2 * C + h * 64, ld, k0, Tn, tid);
+    stage_cols(sKt, base + C + h * 64, ld, k0, Tn, tid);
+    __syncthreads();
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const int kb = k0 + 32 * s;
+      if (kb > q0w + 31 || kb >= Tn) break;
+      f32x16_t st = zero16(), dp = zero16();
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        st = mfma(frag_rows(sK, 32 * s + l32, kk * 2 + half), qf[kk], st);
+        dp = mfma(frag_rows(sV, 32 * s + l32, kk * 2 + half), gf[kk], dp);
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        int key = kb + 8 * (r >> 2) + 4 * half + (r & 3);
+        float p = (key <= myq && key < Tn) ? exp2f(st[r] * sl2 - lse2) : 0.f;
+        st[r] = p * (dp[r] - dd);
+      }
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        bf16x8_t pb = pack_acc(st, u);
+        dq0 = mfma(frag_cols(sKt, l32, 32 * s + 16 * u, half), pb, dq0);
+        dq1 = mfma(frag_cols(sKt, 32 + l32, 32 * s + 16 * u, half), pb, dq1);
+      }
+    }
+  }
+  if (myq < Tn) {
+    bf16_t* o = dqkv + ((long)b * Tn + myq) * ld + h * 64;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float v0[4] = {dq0[4 * i] * 0.125f, dq0[4 * i + 1] * 0.125f, dq0[4 * i + 2] * 0.125f,
+                     dq0[4 * i + 3] * 0.125f};
+      float v1[4] = {dq1[4 * i] * 0.125f, dq1[4 * i + 1] * 0.125f, dq1[4 * i + 2] * 0.125f,
+                     dq1[4 * i + 3] * 0.125f};
+      st4(o + 8 * i + 4 * half, v0);
+      st4(o + 32 + 8 * i + 4 * half, v1);
+    }
+  }
+}
+
+// dV = P^T dO and dK = (P o (dP - D))^T Q / sqrt(hd) per block of 128 keys.
+__global__ __launch_bounds__(256) void attn_bwd_dkv_mfma(const bf16_t* __restrict__ qkv,
+                                                         const float* __restrict__ lse,
+                                                         const bf16_t* __restrict__ dy,
+                                                         const float* __restrict__ dbuf,
+                                                         bf16_t* __restrict__ dqkv, int Tn, int H,
+                                                         int C) {
+  __shared__ __attribute__((aligned(16))) bf16_t sQ[64 * 64];
+  __shared__ __attribute__((aligned(16))) bf16_t sG[64 * 64];
+  __shared__ __attribute__((aligned(16))) bf16_t sQt[64 * ATS];
+  __shared__ __attribute__((aligned(16))) bf16_t sGt[64 * ATS];
+  __shared__ float sL[64], sD[64];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, half = lane >> 5, l32 = lane & 31;
+  const int kbk = blockIdx.x;  // key block 0 has the most queries: dispatched first
+  const int bh = blockIdx.y, b = bh / H, h = bh % H;
+  const long ld = 3L * C;
+  const bf16_t* base = qkv + (long)b * Tn * ld;
+  const bf16_t* dyb = dy + (long)b * Tn * C;
+  const int kw0 = kbk * 128 + w * 32;
+  const int mykey = kw0 + l32;
+  const float sl2 = 0.125f * LOG2E_F;
+
+  bf16x8_t kf[4], vf[4];
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) {
+    uint4 k = make_uint4(0, 0, 0, 0), v = k;
+    if (mykey < Tn) {
+      k = *reinterpret_cast<const uint4*>(base + (long)mykey * ld + C + h * 64 + kk * 16 + half * 8);
+      v = *reinterpret_cast<const uint4*>(base + (long)mykey * ld + 2 * C + h * 64 + kk * 16 +
+                                          half * 8);
+    }
+    kf[kk] = as_bf16x8(k);
+    vf[kk] = as_bf16x8(v);
+  }
+  f32x16_t dv0 = zero16(), dv1 = zero16(), dk0 = zero16(), dk1 = zero16();
+  for (int q0 = kbk * 128; q0 < Tn; q0 += 64) {
+    __syncthreads();
+    stage_rows(sQ, base + h * 64, ld, q0, Tn, tid);
+    stage_cols(sQt, base + h * 64, ld, q0, Tn, tid);
+    stage_rows(sG, dyb + h * 64, C, q0, Tn, tid);
+    stage_cols(sGt, dyb + h * 64, C, q0, Tn, tid);
+    if (tid < 64) {
+      int q = q0 + tid;
+      sL[tid] = q < Tn ? lse[(long)bh * Tn + q] * LOG2E_F : 0.f;
+      sD[tid] = q < Tn ? dbuf[(long)bh * Tn + q] : 0.f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const int qs = q0 + 32 * s;
+      if (qs + 31 < kw0 || qs >= Tn) continue;
+      f32x16_t st = zero16(), dp = zero16();
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        st = mfma(frag_rows(sQ, 32 * s + l32, kk * 2 + half), kf[kk], st);
+        dp = mfma(frag_rows(sG, 32 * s + l32, kk * 2 + half), vf[kk], dp);
+      }
+      f32x16_t pv;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        int qi = 32 * s + 8 * (r >> 2) + 4 * half + (r & 3);
+        int q = q0 + qi;
+        float p = (mykey <= q && q < Tn) ? exp2f(st[r] * sl2 - sL[qi]) : 0.f;
+        pv[r] = p;
+        st[r] = p * (dp[r] - sD[qi]);
+      }
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        bf16x8_t pp = pack_acc(pv, u), ps = pack_acc(st, u);
+        dv0 = mfma(frag_cols(sGt, l32, 32 * s + 16 * u, half), pp, dv0);
+        dv1 = mfma(frag_cols(sGt, 32 + l32, 32 * s + 16 * u, half), pp, dv1);
+        dk0 = mfma(frag_cols(sQt, l32, 32 * s + 16 * u, half), ps, dk0);
+        dk1 = mfma(frag_cols(sQt, 32 + l32, 32 * s + 16 * u, half), ps, dk1);
+      }
+    }
+  }
+  if (mykey < Tn) {
+    bf16_t* o = dqkv + ((long)b * Tn + mykey) * ld + h * 64;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float k0[4] = {dk0[4 * i] * 0.125f, dk0[4 * i + 1] * 0.125f, dk0[4 * i + 2] * 0.125f,
+                     dk0[4 * i + 3] * 0.125f};
+      float k1[4] = {dk1[4 * i] * 0.125f, dk1[4 * i + 1] * 0.125f, dk1[4 * i + 2] * 0.125f,
+                     dk1[4 * i + 3] * 0.125f};
+      float v0[4] = {dv0[4 * i], dv0[4 * i + 1], dv0[4 * i + 2], dv0[4 * i + 3]};
+      float v1[4] = {dv1[4 * i], dv1[4 * i + 1], dv1[4 * i + 2], dv1[4 * i + 3]};
+      st4(o + C + 8 * i + 4 * half, k0);
+      st4(o + C + 32 + 8 * i + 4 * half, k1);
+      st4(o + 2 * C + 8 * i + 4 * half, v0);
+      st4(o + 2 * C + 32 + 8 * i + 4 * half, v1);
+    }
+  }
+}
+
+// ===========================================================================
+// launchers
+// ===========================================================================
+template <typename T>
+static hipError_t simt_fwd(const void* qkv, void* y, float* lse, int B, int Tn, int H, int hd,
+                           hipStream_t s) {
+  long n = (long)B * H * Tn;
+  unsigned g = (unsigned)((n + 127) / 128);
+  int C = H * hd;
+  if (hd == 32)
+    attn_fwd_simt<T, 32><<<g, 128, 0, s>>>((const T*)qkv, (T*)y, lse, B, Tn, H, C);
+  else
+    attn_fwd_simt<T, 64><<<g, 128, 0, s>>>((const T*)qkv, (T*)y, lse, B, Tn, H, C);
+  return hipGetLastError();
+}
+
+template <typename T>
+static hipError_t simt_bwd(const void* qkv, const void* y, const float* lse, const void* dy,
+                           void* dqkv, float* dbuf, int B, int Tn, int H, int hd, hipStream_t s) {
+  long n = (long)B * H * Tn;
+  unsigned g = (unsigned)((n + 127) / 128);
+  int C = H * hd;
+  if (hd == 32) {
+    attn_bwd_dq_simt<T, 32><<<g, 128, 0, s>>>((const T*)qkv, (const T*)y, lse, (const T*)dy,
+                                              (T*)dqkv, dbuf, B, Tn, H, C);
+    attn_bwd_dkv_simt<T, 32><<<g, 128, 0, s>>>((const T*)qkv, lse, (const T*)dy, dbuf, (T*)dqkv,
+                                               B, Tn, H, C);
+  } else {
+    attn_bwd_dq_simt<T, 64><<<g, 128, 0, s>>>((const T*)qkv, (const T*)y, lse, (const T*)dy,
+                                              (T*)dqkv, dbuf, B, Tn, H, C);
+    attn_bwd_dkv_simt<T, 64><<<g, 128, 0, s>>>((const T*)qkv, lse, (const T*)dy, dbuf, (T*)dqkv,
+                                               B, Tn, H, C);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_fwd(DType t, const void* qkv, void* y, float* lse, int B, int Tn, int H,
+                           int hd, hipStream_t s) {
+  if (t == DT_BF16) {
+    if (hd != 64) return hipErrorInvalidValue;
+    dim3 grid((Tn + 127) / 128, B * H);
+    attn_fwd_mfma<<<grid, 256, 0, s>>>((const bf16_t*)qkv, (bf16_t*)y, lse, Tn, H, H * 64);
+    return hipGetLastError();
+  }
+  if (hd != 32 && hd != 64) return hipErrorInvalidValue;
+  return simt_fwd<float>(qkv, y, lse, B, Tn, H, hd, s);
+}
+
+hipError_t launch_attn_bwd(DType t, const void* qkv, const void* y, const float* lse,
+                           const void* dy, void* dqkv, float* dbuf, int B, int Tn, int H, int hd,
+                           hipStream_t s) {
+  if (t == DT_BF16) {
+    if (hd != 64) return hipErrorInvalidValue;
+    dim3 grid((Tn + 127) / 128, B * H);
+    int C = H * 64;
+    attn_bwd_dq_mfma<<<grid, 256, 0, s>>>((const bf16_t*)qkv, (const bf16_t*)y, lse,
+                                          (const bf16_t*)dy, (bf16_t*)dqkv, dbuf, Tn, H, C);
+    attn_bwd_dkv_mfma<<<grid, 256, 0, s>>>((const bf16_t*)qkv, lse, (const bf16_t*)dy, dbuf,
+                                           (bf16_t*)dqkv, Tn, H, C);
+    return hipGetLastError();
+  }
+  if (hd != 32 && hd != 64) return hipErrorInvalidValue;
+  return simt_bwd<float>(qkv, y, lse, dy, dqkv, dbuf, B, Tn, H, hd, s);
+}

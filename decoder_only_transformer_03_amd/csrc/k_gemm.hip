@@ -1,0 +1,125 @@
+// GEMM entry: fp32 operands run on a vector-ALU tiled kernel (fp32 mode),
+// bf16 operands on the matrix-core kernel (gemm_mfma.h).
+#include "kernels.h"
+
+namespace gemm_mfma {
+template <bool AT, bool BT>
+hipError_t dispatch(int M, int N, int K, const bf16_t* A, long lda, const bf16_t* B, long ldb,
+                    int epi, DType out_t, const EpiArgs& e, int split_k, hipStream_t s);
+}
+
+// fp32 C[m][n] = sum_k A(m,k) B(n,k): 64 x 64 tile, 16-deep k steps through
+// LDS, each thread a 4 x 4 block of C with 4 consecutive n.
+template <bool AT, bool BT, int EPI, typename TO>
+__global__ __launch_bounds__(256) void gemm_f32_kernel(int M, int N, int K,
+                                                       const float* __restrict__ A, long lda,
+                                                       const float* __restrict__ B, long ldb,
+                                                       EpiArgs e, int kchunk) {
+  __shared__ float As[16][68];
+  __shared__ float Bs[16][68];
+  const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
+  const long m0 = (long)blockIdx.y * 64;
+  const long n0 = (long)blockIdx.x * 64;
+  const int kb = blockIdx.z * kchunk;
+  const int ke = kb + kchunk < K ? kb + kchunk : K;
+  float acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = 0.f;
+  for (int k0 = kb; k0 < ke; k0 += 16) {
+    for (int i = tid; i < 1024; i += 256) {
+      int r, kk;
+      if (AT) { r = i & 63; kk = i >> 6; } else { kk = i & 15; r = i >> 4; }
+      long m = m0 + r;
+      int k = k0 + kk;
+      As[kk][r] = (m < M && k < ke) ? (AT ? A[(long)k * lda + m] : A[m * lda + k]) : 0.f;
+      if (BT) { r = i & 63; kk = i >> 6; } else { kk = i & 15; r = i >> 4; }
+      long n = n0 + r;
+      k = k0 + kk;
+      Bs[kk][r] = (n < N && k < ke) ? (BT ? B[(long)k * ldb + n] : B[n * ldb + k]) : 0.f;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < 16; ++kk) {
+      float a[4], b[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[i] = As[kk][ty * 4 + i];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) b[j] = Bs[kk][tx * 4 + j];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] += a[i] * b[j];
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    long m = m0 + ty * 4 + i;
+    long n = n0 + tx * 4;
+    if (m < M && n < N) epi_apply4<EPI, TO>(e, m, (int)n, acc[i]);
+  }
+}
+
+template <bool AT, bool BT, int EPI>
+static hipError_t f32_run(int M, int N, int K, const float* A, long lda, const float* B, long ldb,
+                          const EpiArgs& e, int split_k, hipStream_t s) {
+  if (split_k < 1) split_k = 1;
+  int kchunk = (K + split_k - 1) / split_k;
+  kchunk = (kchunk + 15) / 16 * 16;
+  int splits = (K + kchunk - 1) / kchunk;
+  dim3 grid((N + 63) / 64, (M + 63) / 64, splits);
+  gemm_f32_kernel<AT, BT, EPI, float><<<grid, 256, 0, s>>>(M, N, K, A, lda, B, ldb, e, kchunk);
+  return hipGetLastError();
+}
+
+template <bool AT, bool BT>
+static hipError_t f32_by_epi(int M, int N, int K, const float* A, long lda, const float* B,
+                             long ldb, int epi, const EpiArgs& e, int split_k, hipStream_t s) {
+  switch (epi) {
+    case EPI_STORE: return f32_run<AT, BT, EPI_STORE>(M, N, K, A, lda, B, ldb, e, 1, s);
+    case EPI_BIAS_GELU: return f32_run<AT, BT, EPI_BIAS_GELU>(M, N, K, A, lda, B, ldb, e, 1, s);
+    case EPI_RESID: return f32_run<AT, BT, EPI_RESID>(M, N, K, A, lda, B, ldb, e, 1, s);
+    case EPI_ACCUM: return f32_run<AT, BT, EPI_ACCUM>(M, N, K, A, lda, B, ldb, e, 1, s);
+    case EPI_ATOMIC: {
+      if (split_k == 0) {
+        long tiles = (long)((M + 63) / 64) * ((N + 63) / 64);
+        long want = (512 + tiles - 1) / tiles, cap = K / 64 > 0 ? K / 64 : 1;
+        split_k = (int)(want < cap ? want : cap);
+      }
+      return f32_run<AT, BT, EPI_ATOMIC>(M, N, K, A, lda, B, ldb, e, split_k, s);
+    }
+    case EPI_GELU_BWD: return f32_run<AT, BT, EPI_GELU_BWD>(M, N, K, A, lda, B, ldb, e, 1, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_gemm(DType in_t, int M, int N, int K, const void* A, long lda, bool a_t,
+                       const void* B, long ldb, bool b_t, int epi, DType out_t, const EpiArgs& e,
+                       int split_k, hipStream_t s) {
+  if (M <= 0 || N <= 0 || K <= 0) return hipSuccess;
+  if (N % 4) return hipErrorInvalidValue;
+  if (in_t == DT_F32) {
+    if (out_t != DT_F32) return hipErrorInvalidValue;
+    const float* a = (const float*)A;
+    const float* b = (const float*)B;
+    if (!a_t && !b_t) return f32_by_epi<false, false>(M, N, K, a, lda, b, ldb, epi, e, split_k, s);
+    if (!a_t && b_t) return f32_by_epi<false, true>(M, N, K, a, lda, b, ldb, epi, e, split_k, s);
+    if (a_t && b_t) return f32_by_epi<true, true>(M, N, K, a, lda, b, ldb, epi, e, split_k, s);
+    return f32_by_epi<true, false>(M, N, K, a, lda, b, ldb, epi, e, split_k, s);
+  }
+  // bf16: 16-byte chunks along the contiguous dimension of each operand
+  if (lda % 8 || ldb % 8) return hipErrorInvalidValue;
+  if ((!a_t || !b_t) && K % 8) return hipErrorInvalidValue;
+  if ((a_t && M % 8) || (b_t && N % 8)) return hipErrorInvalidValue;
+  const bf16_t* a = (const bf16_t*)A;
+  const bf16_t* b = (const bf16_t*)B;
+  if (!a_t && !b_t)
+    return gemm_mfma::dispatch<false, false>(M, N, K, a, lda, b, ldb, epi, out_t, e, split_k, s);
+  if (!a_t && b_t)
+    return gemm_mfma::dispatch<false, true>(M, N, K, a, lda, b, ldb, epi, out_t, e, split_k, s);
+  if (a_t && b_t)
+    return gemm_mfma::dispatch<true, true>(M, N, K, a, lda, b, ldb, epi, out_t, e, split_k, s);
+  return hipErrorInvalidValue;
+}

@@ -1,0 +1,3 @@
+// bf16 MFMA GEMM instantiations for operand layout AT=0, BT=0.
+#include "gemm_mfma.h"
+GEMM_MFMA_DEFINE_DISPATCH(false, false)

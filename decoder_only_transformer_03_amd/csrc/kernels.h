@@ -1,0 +1,65 @@
+// Host-side launchers of the libgpt2 kernels (internal interface).
+#pragma once
+#include <hip/hip_runtime.h>
+#include "common.h"
+#include "epilogue.h"
+
+enum DType : int { DT_F32 = 0, DT_BF16 = 1 };
+
+// LayerNorm backward: rows per workgroup (partials of dw/db are per workgroup)
+constexpr int LN_BWD_ROWS = 32;
+// bias-gradient column sums: row splits (partials of width N each)
+constexpr int BIAS_SPLITS = 64;
+// grad-norm: workgroups of the sum-of-squares pass (fp64 partials)
+constexpr int NORM_PARTS = 1024;
+
+struct AdamChunk {
+  long start;  // first element in the flat parameter vector (multiple of 4)
+  int len;     // elements (multiple of 4)
+  int flags;   // bit 0: weight decay applies (tensor has dim >= 2)
+};
+
+int ln_bwd_blocks(long rows);
+
+hipError_t launch_embed_fwd(const int32_t* idx_in, int32_t* idx_saved, const float* wte,
+                            const float* wpe, float* x, int B, int T, int C, int Vp, int* err,
+                            hipStream_t s);
+hipError_t launch_embed_bwd(const int32_t* idx, const float* dx, float* dwte, float* dwpe, int B,
+                            int T, int C, hipStream_t s);
+hipError_t launch_layernorm_fwd(DType out_t, const float* x, const float* w, const float* b,
+                                void* y, float* mean, float* rstd, long rows, int C,
+                                hipStream_t s);
+hipError_t launch_layernorm_bwd(DType copy_t, const float* dy, const float* x, const float* mean,
+                                const float* rstd, const float* w, float* dres, void* dres_copy,
+                                int accumulate, float* partial, float* dw, float* db, long rows,
+                                int C, hipStream_t s);
+hipError_t launch_bias_grad(DType in_t, const void* X, long rows, int N, long ldx, float* partial,
+                            float* db, hipStream_t s);
+hipError_t launch_xent(DType t, void* logits, const int32_t* targets, int* n_valid,
+                       float* row_loss, float* loss, long rows, int Vp, int* err, hipStream_t s);
+hipError_t launch_grad_norm(const float* g, long n, double* partial, float max_norm,
+                            float* norm_out, float* clip_out, hipStream_t s);
+hipError_t launch_adamw(const AdamChunk* chunks, int nchunks, float* p, const float* g, float* m,
+                        float* v, bf16_t* shadow, const float* clip, float lr, float b1, float b2,
+                        float eps, float wd, float step_size, float inv_sqrt_bc2, hipStream_t s);
+hipError_t launch_fill(float* p, long n, float val, hipStream_t s);
+hipError_t launch_f32_to_bf16(const float* src, bf16_t* dst, long n, hipStream_t s);
+hipError_t launch_bf16_to_f32(const bf16_t* src, float* dst, long n, hipStream_t s);
+
+// C[m][n] = sum_k A(m,k) B(n,k) followed by epilogue `epi`, where
+// A(m,k) = a_t ? A[k*lda + m] : A[m*lda + k] and B(n,k) = b_t ? B[k*ldb + n] : B[n*ldb + k].
+// Operands are `in_t`; the epilogue's TO type is `out_t`.  split_k > 1 is
+// only valid with EPI_ATOMIC; 0 lets the launcher choose.
+hipError_t launch_gemm(DType in_t, int M, int N, int K, const void* A, long lda, bool a_t,
+                       const void* B, long ldb, bool b_t, int epi, DType out_t, const EpiArgs& e,
+                       int split_k, hipStream_t s);
+
+// Causal self-attention on the fused qkv activation (B*T, 3C), head h of q,
+// k, v at columns h*hd, C + h*hd, 2C + h*hd.  y is (B*T, C) with heads
+// re-interleaved; lse is (B, H, T), natural log of the scaled, masked scores.
+hipError_t launch_attn_fwd(DType t, const void* qkv, void* y, float* lse, int B, int T, int H,
+                           int hd, hipStream_t s);
+// Gradients into dqkv (B*T, 3C) given dy (B*T, C); dbuf (B, H, T) fp32 scratch.
+hipError_t launch_attn_bwd(DType t, const void* qkv, const void* y, const float* lse,
+                           const void* dy, void* dqkv, float* dbuf, int B, int T, int H, int hd,
+                           hipStream_t s);

@@ -1,0 +1,225 @@
+/*
+ * gpt2.h - C ABI of libgpt2.so: one GPT-2 training step on an MI355X (gfx950).
+ *
+ * The library computes, on one GPU, what a PyTorch GPT-2 training step
+ * computes ("GPT-2 from Scratch", sections "The full model", "The loop",
+ * "How to scale up"; "Let's reproduce GPT-2 (124M)", optimizer and
+ * accumulation paragraphs):
+ *
+ *   loss   = gpt2_forward(idx, targets)       model(idx, targets) -> mean CE
+ *            gpt2_backward(loss_scale)        (loss * loss_scale).backward()
+ *   norm   = gpt2_adamw_step(lr, ...)         clip_grad_norm_(params, max) + AdamW.step()
+ *
+ * Model: pre-LayerNorm decoder-only transformer with learned positions,
+ * fused qkv projection, causal softmax attention, GELU (tanh form) MLP of
+ * width 4C, final LayerNorm, lm_head tied to the token embedding, padded
+ * vocabulary.  Cross-entropy ignores targets equal to -1 and averages over
+ * the remaining positions.
+ *
+ * Memory.  The caller allocates ONE device buffer (the workspace) of
+ * gpt2_workspace_bytes() bytes and keeps it alive until gpt2_destroy.  The
+ * library never allocates device memory; parameters, gradients, AdamW
+ * moments, the bf16 weight copy, saved activations and scratch all live in
+ * the workspace at offsets the library chooses.
+ *
+ * Streams.  Every call enqueues its work on the HIP stream given to
+ * gpt2_init (hipStream_t passed as void*; NULL is the default stream) and
+ * returns without waiting, except where a host output pointer is given
+ * (h_loss, h_grad_norm, host copies), in which case it waits for the stream.
+ * A handle must not be used from two threads at once.
+ *
+ * Errors.  Every call returns a gpt2_status; nothing aborts.  Argument and
+ * shape errors are detected on the host before anything is enqueued.  Token
+ * ids outside [0, padded_vocab_size) and targets outside
+ * {-1} U [0, padded_vocab_size) are detected on the device: the kernels clamp
+ * the offending read so nothing faults, set a device flag, and the next
+ * synchronising call (gpt2_sync, or any call given a host output) returns
+ * GPT2_E_RANGE.  gpt2_last_error() gives a human-readable message.
+ *
+ * Precision.  GPT2_FP32: every tensor and every product in fp32.
+ * GPT2_BF16: matrix products (the five linear layers and attention) take
+ * bf16 operands rounded to nearest-even from fp32 and accumulate in fp32;
+ * the residual stream, LayerNorm statistics, softmax, cross-entropy,
+ * gradients of parameters, master weights and AdamW state are fp32; other
+ * saved activations (LayerNorm outputs, qkv, attention output, MLP hidden,
+ * logits) are stored in bf16.  This is the placement torch.autocast with
+ * bfloat16 gives ("Let's reproduce GPT-2 (124M)", precision paragraph).
+ */
+#ifndef GPT2_H
+#define GPT2_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  GPT2_OK = 0,
+  GPT2_E_ARG = -1,    /* bad argument: NULL pointer, size mismatch, unsupported config */
+  GPT2_E_SHAPE = -2,  /* B < 1, B > max_batch, T < 1 or T > block_size */
+  GPT2_E_RANGE = -3,  /* a token id or target was out of range (device-detected) */
+  GPT2_E_STATE = -4,  /* call order violated (backward without a forward with targets) */
+  GPT2_E_HIP = -5     /* a HIP runtime call failed; see gpt2_last_error */
+} gpt2_status;
+
+typedef enum { GPT2_FP32 = 0, GPT2_BF16 = 1 } gpt2_precision;
+
+/* Model and capacity.  n_embd % n_head == 0.  In GPT2_BF16 the head width
+ * n_embd / n_head must be 64 (every released GPT-2 size, "The config");
+ * GPT2_FP32 accepts head widths 32 and 64.  n_embd must be a multiple of 64
+ * and padded_vocab_size a multiple of 64 and >= vocab_size.  max_batch
+ * bounds B for the activation storage. */
+typedef struct {
+  int32_t n_layer;
+  int32_t n_head;
+  int32_t n_embd;
+  int32_t vocab_size;
+  int32_t padded_vocab_size;
+  int32_t block_size;
+  int32_t max_batch;
+  int32_t precision; /* gpt2_precision */
+} gpt2_config;
+
+typedef struct gpt2 gpt2_t; /* opaque handle */
+
+/* Number of parameters with the tied embedding counted once, in the
+ * canonical order used by gpt2_set_params/gpt2_get:
+ *   wte (Vp, C); wpe (block_size, C);
+ *   per layer: ln_1.w (C), ln_1.b (C), c_attn.w (3C, C), c_attn.b (3C),
+ *              attn c_proj.w (C, C), attn c_proj.b (C), ln_2.w (C), ln_2.b (C),
+ *              c_fc.w (4C, C), c_fc.b (4C), mlp c_proj.w (C, 4C), mlp c_proj.b (C);
+ *   ln_f.w (C), ln_f.b (C).
+ * Matrices are row-major (out, in) as for a torch Linear.  ("GPT-2 from
+ * Scratch": "Embeddings", "CausalSelfAttention", "The MLP", "The Block",
+ * "Weight tying".)  Returns 0 for an invalid config. */
+size_t gpt2_num_params(const gpt2_config* cfg);
+
+/* Bytes of device workspace a handle needs for this config. */
+gpt2_status gpt2_workspace_bytes(const gpt2_config* cfg, size_t* bytes);
+
+/* Creates a handle over a caller-owned device workspace (256-byte aligned,
+ * at least gpt2_workspace_bytes).  Parameters start at zero; call
+ * gpt2_set_params before training.  hip_stream: the hipStream_t to use. */
+gpt2_status gpt2_init(const gpt2_config* cfg, void* d_workspace, size_t ws_bytes,
+                      void* hip_stream, gpt2_t** out);
+
+/* Loads all parameters (fp32, canonical order, n == gpt2_num_params) from
+ * host (src_on_device = 0) or device memory, refreshes the bf16 weight copy,
+ * zeroes the AdamW moments and gradients, and resets the step count to 0. */
+gpt2_status gpt2_set_params(gpt2_t* h, const float* src, size_t n, int src_on_device);
+
+enum { GPT2_PARAMS = 0, GPT2_GRADS = 1, GPT2_ADAM_M = 2, GPT2_ADAM_V = 3 };
+
+/* Copies one fp32 state vector (canonical order, n == gpt2_num_params) to
+ * host or device memory.  Host copies wait for the stream. */
+gpt2_status gpt2_get(gpt2_t* h, int which, float* dst, size_t n, int dst_on_device);
+
+/* Overwrites one state vector (GRADS, ADAM_M or ADAM_V; PARAMS goes through
+ * gpt2_set_params) without other side effects.  Used to resume. */
+gpt2_status gpt2_set_state(gpt2_t* h, int which, const float* src, size_t n, int src_on_device);
+
+/* AdamW step counter t (number of gpt2_adamw_step calls since set_params). */
+gpt2_status gpt2_get_step(const gpt2_t* h, int64_t* t);
+gpt2_status gpt2_set_step(gpt2_t* h, int64_t t);
+
+/* Forward pass over a batch: d_idx, d_targets are device int32 arrays of B*T
+ * ids, row-major (B, T); targets[b][t] is the id that should follow
+ * idx[b][t], or -1 to leave the position out of the loss.  d_targets may be
+ * NULL: then only logits are computed (read them with gpt2_get_activation).
+ * With targets, the loss is the mean of -log softmax(logits)[target] over
+ * positions with target != -1 (0 if there are none), and the gradient of
+ * the loss with respect to the logits is formed in the same pass, in place of
+ * the logits, ready for gpt2_backward.  If h_loss is non-NULL the call waits
+ * and stores the loss there.  Both arrays are read before the call's work
+ * completes on the stream; the ids are copied into the workspace for the
+ * backward pass. */
+gpt2_status gpt2_forward(gpt2_t* h, const int32_t* d_idx, const int32_t* d_targets,
+                         int B, int T, float* h_loss);
+
+/* Loss of the last forward with targets; waits for the stream. */
+gpt2_status gpt2_get_loss(gpt2_t* h, float* h_loss);
+
+/* Sets every gradient to zero. */
+gpt2_status gpt2_zero_grad(gpt2_t* h);
+
+/* Backward pass of the last forward with targets: adds loss_scale *
+ * d(loss)/d(param) into the gradients (use loss_scale = 1/k for k
+ * accumulation micro-steps, "How to scale up").  The tied embedding gets the
+ * sum of its lm_head and embedding contributions.  GPT2_E_STATE if the last
+ * forward had no targets or a backward already consumed it. */
+gpt2_status gpt2_backward(gpt2_t* h, float loss_scale);
+
+/* Global-norm clip and AdamW ("Gradient clipping"; "AdamW, and weight decay
+ * on matrices only"): norm = ||g||_2 over all parameters; g is scaled by
+ * min(1, max_grad_norm / (norm + 1e-6)); then, per element, with t the
+ * updated step count (1 on the first call):
+ *   p <- p * (1 - lr * weight_decay)   only for tensors with dim >= 2
+ *   m <- beta1 m + (1 - beta1) g ;  v <- beta2 v + (1 - beta2) g^2
+ *   p <- p - lr / (1 - beta1^t) * m / (sqrt(v) / sqrt(1 - beta2^t) + eps)
+ * The bf16 weight copy is refreshed.  Gradients are left unchanged (not
+ * clipped in place).  If h_grad_norm is non-NULL the call waits and stores
+ * the pre-clip norm there. */
+gpt2_status gpt2_adamw_step(gpt2_t* h, float lr, float beta1, float beta2, float eps,
+                            float weight_decay, float max_grad_norm, float* h_grad_norm);
+
+/* Pre-clip gradient norm of the last gpt2_adamw_step; waits. */
+gpt2_status gpt2_get_grad_norm(gpt2_t* h, float* h_norm);
+
+/* Waits for the stream and reports device-side errors (GPT2_E_RANGE). */
+gpt2_status gpt2_sync(gpt2_t* h);
+
+/* Message describing the last error on this handle ("" if none). */
+const char* gpt2_last_error(const gpt2_t* h);
+
+/* Releases the handle (not the workspace, which the caller owns). */
+void gpt2_destroy(gpt2_t* h);
+
+/* Saved activations of the last forward, for layer-by-layer comparison
+ * against a reference.  `layer` selects the block where it applies.  The
+ * tensor is converted to fp32 and copied to host memory (waits); n must equal
+ * the element count given for each id below (B, T of the last forward):
+ *   X_IN      residual stream entering block `layer` (layer == n_layer: after the last block), B*T*C
+ *   LN1       ln_1 output, B*T*C          QKV    c_attn output, B*T*3C ([q | k | v])
+ *   ATTN_Y    attention output with heads re-interleaved, B*T*C
+ *   LSE       per (b, head, t) log-sum-exp of the scaled, masked scores, B*H*T
+ *   X_MID     residual stream after attention, B*T*C
+ *   LN2       ln_2 output, B*T*C          FC_PRE  c_fc output before GELU, B*T*4C
+ *   FC_GELU   GELU output, B*T*4C         LNF     ln_f output, B*T*C
+ *   LOGITS    logits (forward without targets) or, after a forward with
+ *             targets, d(loss)/d(logits) which replaces them, B*T*Vp
+ *   ROW_LOSS  per-position loss (0 where target == -1), B*T */
+enum {
+  GPT2_ACT_X_IN = 0, GPT2_ACT_LN1, GPT2_ACT_QKV, GPT2_ACT_ATTN_Y, GPT2_ACT_LSE, GPT2_ACT_X_MID,
+  GPT2_ACT_LN2, GPT2_ACT_FC_PRE, GPT2_ACT_FC_GELU, GPT2_ACT_LNF, GPT2_ACT_LOGITS,
+  GPT2_ACT_ROW_LOSS
+};
+gpt2_status gpt2_get_activation(gpt2_t* h, int which, int layer, float* h_dst, size_t n);
+
+/* Kernel timing.  Launch sites of the step, for per-kernel measurement with
+ * HIP events recorded on the handle's stream around each launch. */
+enum {
+  GPT2_SITE_EMBED_FWD = 0, GPT2_SITE_LN_FWD, GPT2_SITE_QKV_FWD, GPT2_SITE_ATTN_FWD,
+  GPT2_SITE_PROJ_FWD, GPT2_SITE_FC_FWD, GPT2_SITE_FCPROJ_FWD, GPT2_SITE_LMHEAD_FWD,
+  GPT2_SITE_XENT, GPT2_SITE_LMHEAD_DX, GPT2_SITE_LMHEAD_DW, GPT2_SITE_LN_BWD,
+  GPT2_SITE_FCPROJ_DX, GPT2_SITE_FCPROJ_DW, GPT2_SITE_FC_DX, GPT2_SITE_FC_DW,
+  GPT2_SITE_PROJ_DX, GPT2_SITE_PROJ_DW, GPT2_SITE_ATTN_BWD, GPT2_SITE_QKV_DX,
+  GPT2_SITE_QKV_DW, GPT2_SITE_BIAS_GRAD, GPT2_SITE_EMBED_BWD, GPT2_SITE_GRAD_NORM,
+  GPT2_SITE_ADAMW, GPT2_SITE_ZERO_GRAD, GPT2_NUM_SITES
+};
+
+/* From now on, record an event pair around every launch of each site whose
+ * bit is set in site_mask (bit i = site i).  Clears earlier records.  Event
+ * objects are created on first use and kept for later sessions. */
+gpt2_status gpt2_timing_begin(gpt2_t* h, uint64_t site_mask);
+
+/* Stops recording, waits for the stream, and returns per site the summed
+ * duration in milliseconds (ms[GPT2_NUM_SITES]) and the number of launches
+ * (launches[GPT2_NUM_SITES]); either pointer may be NULL. */
+gpt2_status gpt2_timing_end(gpt2_t* h, double* ms, int32_t* launches);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* GPT2_H */

@@ -1,0 +1,54 @@
+/*
+ * gpt2_ops.h - single-kernel entry points of libgpt2.so on caller-owned
+ * device buffers.  They run the same kernels as the training step and exist
+ * for layer-by-layer comparison against a reference (compare every
+ * intermediate on the same input; rounding-level differences are expected,
+ * larger ones locate a bug - "Reproducing GPT-2: How a Hidden Bug Affected
+ * Weight Training", layer-by-layer comparison of activations).
+ *
+ * All pointers are device pointers; work is enqueued on hip_stream
+ * (hipStream_t as void*, NULL = default stream) and the call returns without
+ * waiting.  dtype is GPT2_FP32 (operands float) or GPT2_BF16 (operands bf16,
+ * stored as uint16, fp32 accumulation).  Nothing is allocated.  Returns
+ * GPT2_E_ARG for an unsupported shape/alignment and GPT2_E_HIP if the launch
+ * fails.
+ */
+#ifndef GPT2_OPS_H
+#define GPT2_OPS_H
+#include "gpt2.h"
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Matrix product of a linear layer ("GPT-2 from Scratch": every nn.Linear):
+ *   C[m][n] = alpha * sum_k A(m,k) B(n,k)            mode 0: store
+ *   C[m][n] += alpha * sum_k A(m,k) B(n,k)           mode 1: accumulate
+ *   same as mode 1, split over k with atomic adds     mode 2 (split_k 0 = auto)
+ * A(m,k) = A[m*lda + k], or A[k*lda + m] if a_trans; B(n,k) = B[n*ldb + k], or
+ * B[k*ldb + n] if b_trans; C is fp32 row-major with leading dimension ldc.
+ * bf16 requires lda, ldb multiples of 8, K a multiple of 8 when an operand is
+ * k-contiguous, M (N) a multiple of 8 when A (B) is transposed, N a multiple
+ * of 4, and (a_trans, b_trans) != (1, 0). */
+gpt2_status gpt2_op_gemm(int dtype, int M, int N, int K, const void* A, long lda, int a_trans,
+                         const void* B, long ldb, int b_trans, float* C, long ldc, float alpha,
+                         int mode, int split_k, void* hip_stream);
+
+/* Causal self-attention forward ("CausalSelfAttention"): qkv is (B*T, 3C) in
+ * dtype with [q | k | v] and head h at columns h*hd of each third; writes y
+ * (B*T, C) in dtype with heads re-interleaved and lse (B, H, T) fp32, the
+ * natural-log log-sum-exp of the scaled, masked scores of each query.
+ * bf16 needs hd == 64; fp32 accepts hd 32 or 64. */
+gpt2_status gpt2_op_attention_fwd(int dtype, const void* qkv, void* y, float* lse, int B, int T,
+                                  int H, int hd, void* hip_stream);
+
+/* Its backward: given dy (B*T, C) writes dqkv (B*T, 3C) in dtype; dbuf is
+ * (B, H, T) fp32 scratch that receives D = rowsum(dy * y). */
+gpt2_status gpt2_op_attention_bwd(int dtype, const void* qkv, const void* y, const float* lse,
+                                  const void* dy, void* dqkv, float* dbuf, int B, int T, int H,
+                                  int hd, void* hip_stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* GPT2_OPS_H */

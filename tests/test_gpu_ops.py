@@ -1,0 +1,143 @@
+"""Kernel-level parity on the GPU, through the C ABI (include/gpt2_ops.h).
+
+GEMM: against a float64 matrix product of the same bf16 (or fp32) operands;
+products of two bf16 values are exact in fp32, so the only difference is the
+order of fp32 additions: |err| <= K * 2^-24 * sum|a||b| in the worst case,
+checked at 2e-5 of the largest output (fp32 mode 1e-5).
+Attention: against the oracle's causal attention in float64 on the same bf16
+q, k, v.  The kernel stores y in bf16 (half-ulp 2^-9 relative) and feeds the
+probabilities to the matrix cores in bf16, so the bound is 1e-2 of the
+largest |y| (about four half-ulps); the log-sum-exp stays in fp32 (2e-4
+absolute).  Backward: bf16 storage of dq, dk, dv and bf16 rounding of P and
+dS give a bound of 2e-2 of the largest gradient of each tensor."""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+from decoder_only_transformer_03_amd import gpt2 as G
+from oracle import gpt2_oracle as O
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def bf16_tensor(shape, seed, scale=1.0):
+    g = torch.Generator().manual_seed(seed)
+    t = (torch.randn(*shape, generator=g) * scale).to(torch.bfloat16)
+    return t.to(DEV), t.float().numpy().astype(np.float64)
+
+
+def f32_tensor(shape, seed, scale=1.0):
+    g = torch.Generator().manual_seed(seed)
+    t = torch.randn(*shape, generator=g) * scale
+    return t.to(DEV), t.numpy().astype(np.float64)
+
+
+def maxrel(a, b):
+    return float(np.max(np.abs(a - b)) / max(np.max(np.abs(b)), 1e-30))
+
+
+LAYOUTS = [(False, False), (False, True), (True, True)]
+SHAPES = [(256, 256, 128), (200, 136, 72), (64, 8, 8), (1024, 768, 768), (520, 2304, 200),
+          (4096, 6144, 192)]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+@pytest.mark.parametrize("layout", LAYOUTS)
+@pytest.mark.parametrize("shape", SHAPES)
+def test_gemm_store(dtype, layout, shape):
+    M, N, K = shape
+    a_t, b_t = layout
+    if dtype == "fp32" and M * N > 2_000_000:
+        pytest.skip("fp32 SIMT path is for small shapes")
+    mk = bf16_tensor if dtype == "bf16" else f32_tensor
+    A, An = mk((K, M) if a_t else (M, K), seed=1)
+    B, Bn = mk((K, N) if b_t else (N, K), seed=2)
+    C = torch.full((M, N), 7.0, dtype=torch.float32, device=DEV)
+    dt = G.GPT2_BF16 if dtype == "bf16" else G.GPT2_FP32
+    G.gpt2_op_gemm(dt, M, N, K, A, M if a_t else K, a_t, B, N if b_t else K, b_t, C, N, 0.5, 0)
+    torch.cuda.synchronize()
+    ref = 0.5 * ((An.T if a_t else An) @ (Bn if b_t else Bn.T))
+    err = maxrel(C.cpu().numpy().astype(np.float64), ref)
+    print(f"gemm {dtype} {layout} {shape}: maxrel {err:.2e}")
+    assert err < (2e-5 if dtype == "bf16" else 1e-5)
+
+
+@pytest.mark.parametrize("mode", [1, 2])
+@pytest.mark.parametrize("layout", LAYOUTS)
+def test_gemm_accumulate(mode, layout):
+    M, N, K = 768, 2304, 4096
+    a_t, b_t = layout
+    A, An = bf16_tensor((K, M) if a_t else (M, K), seed=3)
+    B, Bn = bf16_tensor((K, N) if b_t else (N, K), seed=4)
+    C0, C0n = f32_tensor((M, N), seed=5, scale=10.0)
+    C = C0.clone()
+    G.gpt2_op_gemm(G.GPT2_BF16, M, N, K, A, M if a_t else K, a_t, B, N if b_t else K, b_t, C, N,
+                   0.25, mode, 0)
+    torch.cuda.synchronize()
+    ref = C0n + 0.25 * ((An.T if a_t else An) @ (Bn if b_t else Bn.T))
+    err = maxrel(C.cpu().numpy().astype(np.float64), ref)
+    print(f"gemm accumulate mode {mode} {layout}: maxrel {err:.2e}")
+    assert err < 2e-5
+
+
+def test_gemm_rejects_bad_alignment():
+    A, _ = bf16_tensor((64, 60), seed=1)
+    B, _ = bf16_tensor((64, 60), seed=2)
+    C = torch.zeros((64, 64), dtype=torch.float32, device=DEV)
+    with pytest.raises(G.GPT2Error):
+        G.gpt2_op_gemm(G.GPT2_BF16, 64, 64, 60, A, 60, False, B, 60, False, C, 64)
+
+
+def _qkv_split(qkv_np, B, T, H, hd):
+    C = H * hd
+    x = qkv_np.reshape(B, T, 3 * C)
+    return [np.ascontiguousarray(x[..., i * C:(i + 1) * C].reshape(B, T, H, hd).transpose(0, 2, 1, 3))
+            for i in range(3)]
+
+
+def _merge(t, B, T, H, hd):
+    return t.transpose(0, 2, 1, 3).reshape(B * T, H * hd)
+
+
+@pytest.mark.parametrize("dtype,hd", [("bf16", 64), ("fp32", 64), ("fp32", 32)])
+@pytest.mark.parametrize("T", [1, 5, 64, 127, 200, 256, 1024])
+def test_attention_fwd_bwd(dtype, hd, T):
+    B, H = 2, 3
+    if dtype == "fp32" and T > 256:
+        pytest.skip("fp32 path is for small shapes")
+    C = H * hd
+    mk = bf16_tensor if dtype == "bf16" else f32_tensor
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    qkv, qkvn = mk((B * T, 3 * C), seed=10 + T)
+    dy, dyn = mk((B * T, C), seed=20 + T)
+    y = torch.empty((B * T, C), dtype=tdt, device=DEV)
+    lse = torch.empty((B, H, T), dtype=torch.float32, device=DEV)
+    dqkv = torch.full((B * T, 3 * C), float("nan"), dtype=tdt, device=DEV)
+    dbuf = torch.empty((B, H, T), dtype=torch.float32, device=DEV)
+    dt = G.GPT2_BF16 if dtype == "bf16" else G.GPT2_FP32
+    G.gpt2_op_attention_fwd(dt, qkv, y, lse, B, T, H, hd)
+    G.gpt2_op_attention_bwd(dt, qkv, y, lse, dy, dqkv, dbuf, B, T, H, hd)
+    torch.cuda.synchronize()
+    q, k, v = _qkv_split(qkvn, B, T, H, hd)
+    Or, lse_r = O.causal_attention_fwd(q, k, v)
+    dOr = np.ascontiguousarray(dyn.reshape(B, T, H, hd).transpose(0, 2, 1, 3))
+    dq, dk, dv = O.causal_attention_bwd(dOr, q, k, v, lse_r)
+    y_g = y.float().cpu().numpy().astype(np.float64)
+    e_y = maxrel(y_g, _merge(Or, B, T, H, hd))
+    e_l = float(np.max(np.abs(lse.cpu().numpy() - lse_r)))
+    d_g = dqkv.float().cpu().numpy().astype(np.float64)
+    e_d = [maxrel(d_g[:, i * C:(i + 1) * C], _merge(r, B, T, H, hd)) for i, r in
+           enumerate((dq, dk, dv))]
+    # D = rowsum(dO * O) as the kernel saw it
+    D_ref = (dyn.reshape(B, T, H, hd) * y_g.reshape(B, T, H, hd)).sum(-1).transpose(0, 2, 1)
+    e_D = float(np.max(np.abs(dbuf.cpu().numpy() - D_ref)) / max(np.max(np.abs(D_ref)), 1e-30))
+    print(f"attn {dtype} hd={hd} T={T}: y {e_y:.2e} lse {e_l:.2e} dq/dk/dv "
+          f"{e_d[0]:.2e}/{e_d[1]:.2e}/{e_d[2]:.2e} D {e_D:.2e}")
+    tol_y, tol_d = (1e-2, 2e-2) if dtype == "bf16" else (1e-5, 1e-4)
+    assert e_y < tol_y
+    assert e_l < (2e-4 if dtype == "bf16" else 1e-5)
+    assert max(e_d) < tol_d
+    assert e_D < 1e-4
+    assert not torch.isnan(dqkv).any()

@@ -1,0 +1,281 @@
+"""End-to-end parity of the training step on the GPU against the CPU oracle,
+through the C ABI, on the same seeded inputs.
+
+fp32 (tiny model, 2 layers, C=128, head 32, V=512; B=4, T=64 and ragged
+shapes): loss within 1e-4 relative; every gradient, parameter and AdamW
+moment tensor within 1e-3 max-relative (max |diff| / max |oracle| per tensor);
+activations within 1e-4.  The key third of c_attn.bias has an analytically
+zero gradient (softmax is shift invariant per row), so its computed value is
+rounding noise on both sides and the step-1 AdamW update of those elements is
+noise/(|noise| + eps): it is excluded from parameter comparisons and checked
+to be tiny instead.
+
+Bit-exact: the embedding output in fp32 mode, the saved token ids, the
+number of valid targets, zero gradient rows for ignored targets, and causal
+invariance of the logits (changing tokens after t leaves logits at <= t
+unchanged)."""
+import math
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import oracle
+from oracle import gpt2_oracle as O
+import synthetic
+from decoder_only_transformer_03_amd import gpt2 as G
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+LR, B1, B2, EPS, WD, CLIP = 6e-4, 0.9, 0.95, 1e-8, 0.1, 1.0
+
+
+def dev_ids(a):
+    return torch.tensor(np.asarray(a), dtype=torch.int32, device=DEV).contiguous()
+
+
+def maxrel(a, b):
+    return float(np.max(np.abs(a - b)) / max(np.max(np.abs(b)), 1e-30))
+
+
+def key_bias_mask(cfg):
+    """True on the elements of every c_attn.bias[C:2C)."""
+    mask = np.zeros(O.num_params(cfg), bool)
+    off = 0
+    for name, shape in O.param_specs(cfg):
+        n = int(np.prod(shape))
+        if name.endswith("attn.c_attn.bias"):
+            mask[off + cfg.n_embd: off + 2 * cfg.n_embd] = True
+        off += n
+    return mask
+
+
+def per_tensor(cfg, a, b, skip=None):
+    """{name: max-relative error} over the canonical tensors."""
+    out, off = {}, 0
+    for name, shape in O.param_specs(cfg):
+        n = int(np.prod(shape))
+        x, y = a[off:off + n].astype(np.float64), b[off:off + n].astype(np.float64)
+        if skip is not None:
+            keep = ~skip[off:off + n]
+            x, y = x[keep], y[keep]
+        out[name] = maxrel(x, y) if x.size else 0.0
+        off += n
+    return out
+
+
+def run_gpu_step(d, prec, flat, idx, tgt, lr=LR, wd=WD):
+    cfg = G.make_config(max_batch=idx.shape[0], precision=prec, **d)
+    m = G.GPT2(cfg, device=DEV)
+    m.set_params(flat)
+    m.zero_grad()
+    loss = m.forward(dev_ids(idx), dev_ids(tgt), want_loss=True)
+    out = {"loss": loss, "model": m}
+    B, T = idx.shape
+    C = d["n_embd"]
+    out["x_in"] = [m.activation("X_IN", l, B * T * C) for l in range(d["n_layer"] + 1)]
+    out["row_loss"] = m.activation("ROW_LOSS", 0, B * T)
+    out["dlogits"] = m.activation("LOGITS", 0, B * T * d["padded_vocab_size"])
+    m.backward(1.0)
+    out["grads"] = m.get(G.GPT2_GRADS)
+    out["norm"] = m.adamw_step(lr, B1, B2, EPS, wd, CLIP, want_norm=True)
+    out["params"] = m.get(G.GPT2_PARAMS)
+    out["m"] = m.get(G.GPT2_ADAM_M)
+    out["v"] = m.get(G.GPT2_ADAM_V)
+    return out
+
+
+def run_oracle_step(d, flat, idx, tgt, lr=LR, wd=WD, dtype=np.float32):
+    cfg = O.Config(**d)
+    p = flat.astype(dtype).copy()
+    loss, cache = O.forward(p, idx, tgt, cfg)
+    g = O.backward(p, cache, cfg)
+    out = {"loss": float(loss), "grads": g.copy(), "cache": cache}
+    mm, vv = np.zeros_like(p), np.zeros_like(p)
+    out["norm"] = O.clip_and_adamw(p, g, mm, vv, 1, lr, B1, B2, EPS, wd, CLIP, cfg=cfg)
+    out.update(params=p, m=mm, v=vv)
+    return out
+
+
+# ----------------------------------------------------------------------------
+# fp32, tiny model (the oracle finishes in well under a second)
+# ----------------------------------------------------------------------------
+
+@pytest.mark.parametrize("B,T", [(4, 64), (3, 37), (1, 1), (2, 64)])
+def test_fp32_tiny_step_matches_oracle(B, T):
+    d = synthetic.model_dims("tiny")
+    cfg = O.Config(**d)
+    flat = synthetic.init_params(d, seed=42)
+    idx, tgt = synthetic.uniform_batch(B, T, 512, seed=1001 + T)
+    if B == 2:
+        tgt[0, :20] = -1                      # masked positions
+    g = run_gpu_step(d, "fp32", flat, idx, tgt)
+    r = run_oracle_step(d, flat, idx, tgt)
+    print(f"\nB={B} T={T} loss gpu {g['loss']:.7f} oracle {r['loss']:.7f} "
+          f"norm {g['norm']:.6f} / {r['norm']:.6f}")
+    assert abs(g["loss"] - r["loss"]) <= 1e-4 * abs(r["loss"])
+    assert abs(g["norm"] - r["norm"]) <= 1e-4 * r["norm"]
+    # activations
+    x0 = r["cache"]["layers"][0]["x_in"].reshape(-1)
+    assert np.array_equal(g["x_in"][0], x0)                     # gather + one add: bit-exact
+    for l in range(1, d["n_layer"]):
+        assert maxrel(g["x_in"][l], r["cache"]["layers"][l]["x_in"].reshape(-1)) < 1e-4
+    assert maxrel(g["x_in"][-1], r["cache"]["x_final"].reshape(-1)) < 1e-4
+    assert maxrel(g["row_loss"], r["cache"]["row_loss"]) < 1e-4
+    dl_ref = r["cache"]["dlogits"].reshape(-1)
+    assert maxrel(g["dlogits"], dl_ref) < 1e-4
+    ign = np.repeat(tgt.reshape(-1) == -1, d["padded_vocab_size"])
+    assert np.all(g["dlogits"][ign] == 0.0)
+    # gradients, per tensor
+    kb = key_bias_mask(cfg)
+    eg = per_tensor(cfg, g["grads"], r["grads"], skip=kb)
+    worst = max(eg, key=eg.get)
+    print(f"grads: worst {worst} {eg[worst]:.2e}")
+    assert eg[worst] < 1e-3, eg
+    # the key-bias gradient is zero up to rounding
+    qb = np.abs(r["grads"][np.roll(kb, -d["n_embd"])]).max()
+    assert np.abs(g["grads"][kb]).max() <= 1e-5 * max(qb, 1e-12) + 1e-9
+    # after one clipped AdamW step
+    for key in ("params", "m", "v"):
+        e = per_tensor(cfg, g[key], r[key], skip=kb)
+        w = max(e, key=e.get)
+        print(f"{key}: worst {w} {e[w]:.2e}")
+        assert e[w] < 1e-3, (key, w, e[w])
+
+
+def test_fp32_accumulation_equals_big_batch():
+    d = synthetic.model_dims("tiny")
+    flat = synthetic.init_params(d, seed=7)
+    idx, tgt = synthetic.uniform_batch(4, 64, 512, seed=8)
+    cfg = G.make_config(max_batch=4, precision="fp32", **d)
+    m = G.GPT2(cfg, device=DEV)
+    m.set_params(flat)
+    m.zero_grad()
+    big = m.forward(dev_ids(idx), dev_ids(tgt), want_loss=True)
+    m.backward(1.0)
+    g_big = m.get(G.GPT2_GRADS)
+    m.zero_grad()
+    losses = []
+    for b in range(4):
+        losses.append(m.forward(dev_ids(idx[b:b + 1]), dev_ids(tgt[b:b + 1]), want_loss=True))
+        m.backward(0.25)
+    g_acc = m.get(G.GPT2_GRADS)
+    assert abs(np.mean(losses) - big) < 1e-5 * big
+    assert maxrel(g_acc, g_big) < 1e-5
+
+
+@pytest.mark.parametrize("prec", ["fp32", "bf16"])
+def test_causal_invariance_bit_exact(prec):
+    d = synthetic.model_dims("tiny")
+    if prec == "bf16":
+        d = dict(d, n_head=2)                       # head width 64
+    flat = synthetic.init_params(d, seed=9)
+    B, T = 2, 64
+    idx, _ = synthetic.uniform_batch(B, T, 512, seed=10)
+    cfg = G.make_config(max_batch=B, precision=prec, **d)
+    m = G.GPT2(cfg, device=DEV)
+    m.set_params(flat)
+    m.forward(dev_ids(idx))
+    a = m.activation("LOGITS", 0, B * T * 512).reshape(B, T, 512)
+    for t in (0, 17, 40):
+        idx2 = idx.copy()
+        idx2[:, t + 1:] = (idx2[:, t + 1:] * 7 + 3) % 512
+        m.forward(dev_ids(idx2))
+        b = m.activation("LOGITS", 0, B * T * 512).reshape(B, T, 512)
+        assert np.array_equal(a[:, :t + 1], b[:, :t + 1]), t
+        if t + 1 < T:
+            assert not np.array_equal(a[:, t + 1:], b[:, t + 1:])
+
+
+def test_error_codes():
+    d = synthetic.model_dims("tiny")
+    cfg = G.make_config(max_batch=2, precision="fp32", **d)
+    m = G.GPT2(cfg, device=DEV)
+    m.set_params(synthetic.init_params(d, seed=1))
+    idx, tgt = synthetic.uniform_batch(2, 16, 512, seed=2)
+    with pytest.raises(G.GPT2Error) as e:
+        m.backward(1.0)
+    assert e.value.status == G.GPT2_E_STATE
+    big = np.zeros((3, 16), np.int64)
+    with pytest.raises(G.GPT2Error) as e:
+        m.forward(dev_ids(big), dev_ids(big))
+    assert e.value.status == G.GPT2_E_SHAPE
+    long_ = np.zeros((1, 65), np.int64)
+    with pytest.raises(G.GPT2Error) as e:
+        m.forward(dev_ids(long_), dev_ids(long_))
+    assert e.value.status == G.GPT2_E_SHAPE
+    bad = idx.copy()
+    bad[1, 3] = 512 + 9
+    with pytest.raises(G.GPT2Error) as e:
+        m.forward(dev_ids(bad), dev_ids(tgt), want_loss=True)
+    assert e.value.status == G.GPT2_E_RANGE
+    badt = tgt.copy()
+    badt[0, 0] = -2
+    with pytest.raises(G.GPT2Error) as e:
+        m.forward(dev_ids(idx), dev_ids(badt), want_loss=True)
+    assert e.value.status == G.GPT2_E_RANGE
+    # flags are cleared once reported; a good batch works again
+    loss = m.forward(dev_ids(idx), dev_ids(tgt), want_loss=True)
+    assert math.isfinite(loss)
+    m.backward(1.0)
+    with pytest.raises(G.GPT2Error) as e:
+        m.backward(1.0)                             # consumed
+    assert e.value.status == G.GPT2_E_STATE
+    # no valid target: loss 0, zero gradient
+    m.zero_grad()
+    none = np.full_like(tgt, -1)
+    assert m.forward(dev_ids(idx), dev_ids(none), want_loss=True) == 0.0
+    m.backward(1.0)
+    assert np.all(m.get(G.GPT2_GRADS) == 0.0)
+
+
+# ----------------------------------------------------------------------------
+# bf16, GPT-2 124M shape
+# ----------------------------------------------------------------------------
+
+@pytest.fixture(scope="module")
+def step_124m_b2():
+    d = synthetic.model_dims("gpt2-124m")
+    flat = synthetic.init_params(d, seed=42)
+    idx, tgt = synthetic.zipf_batch(2, 1024, seed=1002)
+    g = run_gpu_step(d, "bf16", flat, idx, tgt)
+    r = run_oracle_step(d, flat, idx, tgt)
+    return d, flat, idx, tgt, g, r
+
+
+def test_bf16_124m_loss_and_activations(step_124m_b2):
+    d, flat, idx, tgt, g, r = step_124m_b2
+    print(f"\n124M bf16 B=2: loss gpu {g['loss']:.5f} oracle {r['loss']:.5f} "
+          f"norm {g['norm']:.5f} / {r['norm']:.5f}")
+    assert abs(g["loss"] - r["loss"]) < 2e-2
+    for l in (1, 6, 12):
+        ref = r["cache"]["layers"][l]["x_in"] if l < 12 else r["cache"]["x_final"]
+        e = maxrel(g["x_in"][l], ref.reshape(-1))
+        print(f"x_in[{l}] maxrel {e:.2e}")
+        assert e < 2e-2
+    assert maxrel(g["row_loss"], r["cache"]["row_loss"]) < 2e-2
+
+
+def test_bf16_124m_grads_and_update(step_124m_b2):
+    d, flat, idx, tgt, g, r = step_124m_b2
+    cfg = O.Config(**d)
+    kb = key_bias_mask(cfg)
+    off = 0
+    worst_g, worst_p = 0.0, 0.0
+    for name, shape in O.param_specs(cfg):
+        n = int(np.prod(shape))
+        sl = slice(off, off + n)
+        keep = ~kb[sl]
+        ga, gr = g["grads"][sl][keep].astype(np.float64), r["grads"][sl][keep].astype(np.float64)
+        eg = np.linalg.norm(ga - gr) / max(np.linalg.norm(gr), 1e-30)
+        pa, pr = g["params"][sl][keep].astype(np.float64), r["params"][sl][keep].astype(np.float64)
+        ep = np.linalg.norm(pa - pr) / max(np.linalg.norm(pr), 1e-30)
+        flips = float(np.mean(np.sign(ga) != np.sign(gr)))
+        worst_g, worst_p = max(worst_g, eg), max(worst_p, ep)
+        if name.startswith(("wte", "wpe", "h.0.", "h.11.", "ln_f")):
+            print(f"{name:28s} grad normrel {eg:.2e}  param normrel {ep:.2e}  sign flips {flips:.2e}")
+        off += n
+    print(f"worst grad normrel {worst_g:.2e}, worst param normrel {worst_p:.2e}")
+    assert abs(g["norm"] - r["norm"]) < 2e-2 * r["norm"]
+    assert worst_p < 5e-3

@@ -73,14 +73,22 @@ __device__ __forceinline__ double wave_sum_d(double v) {
 // device error flags (bit set by kernels, read back by the host at sync points)
 enum : int { ERRF_IDX = 1, ERRF_TARGET = 2 };
 
-// GELU, tanh form, and its derivative.
-__device__ __forceinline__ float gelu_tanh_f(float x) {
+// GELU, tanh form: 0.5 x (1 + tanh(u)) with u = sqrt(2/pi) (x + 0.044715 x^3).
+// Evaluated through the identity 0.5 (1 + tanh(u)) = 1 / (1 + exp(-2u)), with
+// the hardware exp and reciprocal (a few ulp in fp32).
+__device__ __forceinline__ float gelu_sig_f(float x, float* du) {
   const float a = 0.7978845608028654f;  // sqrt(2/pi)
-  float t = tanhf(a * (x + 0.044715f * x * x * x));
-  return 0.5f * x * (1.0f + t);
+  const float c = 0.044715f;
+  float x2 = x * x;
+  float u = a * x * (1.0f + c * x2);
+  float s = __builtin_amdgcn_rcpf(1.0f + __expf(-2.0f * u));
+  if (du) *du = a * (1.0f + 3.0f * c * x2);
+  return s;
 }
+__device__ __forceinline__ float gelu_tanh_f(float x) { return x * gelu_sig_f(x, nullptr); }
+// d/dx: s + 2 x s (1 - s) u'(x)
 __device__ __forceinline__ float gelu_tanh_grad_f(float x) {
-  const float a = 0.7978845608028654f;
-  float t = tanhf(a * (x + 0.044715f * x * x * x));
-  return 0.5f * (1.0f + t) + 0.5f * x * (1.0f - t * t) * a * (1.0f + 3.0f * 0.044715f * x * x);
+  float du;
+  float s = gelu_sig_f(x, &du);
+  return s + 2.0f * x * s * (1.0f - s) * du;
 }

@@ -10,6 +10,7 @@ enum EpiKind : int {
   EPI_ACCUM = 3,     // out[m][n] += alpha*c            one writer per element (out: fp32)
   EPI_ATOMIC = 4,    // atomically out[m][n] += alpha*c  split-K               (out: fp32)
   EPI_GELU_BWD = 5,  // out[m][n] = alpha*c * gelu'(aux[m][n])                 (out, aux: TO)
+  EPI_PARTIAL = 6,   // split-K slice z = blockIdx.y: out[z*split_stride + m*ldo + n] = alpha*c (fp32)
 };
 
 struct EpiArgs {
@@ -22,6 +23,7 @@ struct EpiArgs {
   const void* aux;
   long ldx;
   float alpha;
+  long split_stride;
 };
 
 template <int EPI, typename TO>
@@ -62,6 +64,8 @@ __device__ __forceinline__ void epi_apply4(const EpiArgs& e, long m, int n, cons
     float* o = reinterpret_cast<float*>(e.out) + m * e.ldo + n;
 #pragma unroll
     for (int j = 0; j < 4; ++j) atomicAdd(o + j, r[j]);
+  } else if constexpr (EPI == EPI_PARTIAL) {
+    st4(reinterpret_cast<float*>(e.out) + blockIdx.y * e.split_stride + m * e.ldo + n, r);
   } else if constexpr (EPI == EPI_GELU_BWD) {
     float h[4];
     ld4(reinterpret_cast<const TO*>(e.aux) + m * e.ldx + n, h);

@@ -251,6 +251,8 @@ hipError_t dispatch(int M, int N, int K, const bf16_t* A, long lda, const bf16_t
         return run<BM, BN, AT, BT, EPI_ATOMIC, float>(M, N, K, A, lda, B, ldb, e, sk, s);       \
       case EPI_GELU_BWD:                                                                        \
         return run<BM, BN, AT, BT, EPI_GELU_BWD, bf16_t>(M, N, K, A, lda, B, ldb, e, 1, s);     \
+      case EPI_PARTIAL:                                                                         \
+        return run<BM, BN, AT, BT, EPI_PARTIAL, float>(M, N, K, A, lda, B, ldb, e, sk, s);      \
     }                                                                                           \
     return hipErrorInvalidValue;                                                                \
   }                                                                                             \
@@ -263,7 +265,7 @@ hipError_t dispatch(int M, int N, int K, const bf16_t* A, long lda, const bf16_t
     long t128 = (long)((M + 127) / 128) * ((N + 127) / 128);                                    \
     int bm = 128, bn = 128;                                                                     \
     long tiles = t128;                                                                          \
-    if (t256 >= 384 || (epi == EPI_ATOMIC && t256 >= 16)) {                                     \
+    if (t256 >= 384 || (epi == EPI_ATOMIC && t256 >= 16) || epi == EPI_PARTIAL) {               \
       bm = bn = 256; tiles = t256;                                                              \
     } else if (t256x128 >= 256) {                                                               \
       bm = 256; tiles = t256x128;                                                               \

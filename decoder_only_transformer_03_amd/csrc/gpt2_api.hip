@@ -161,6 +161,7 @@ struct gpt2 {
   float* dbuf;
   float* ln_partial;
   float* bias_partial;
+  float* splitk;
   // state
   int B = 0, T = 0;
   bool have_targets = false;
@@ -231,8 +232,9 @@ size_t plan(const gpt2_config* c, char* base, gpt2* h) {
   void* dqkv = a.take(BT * 3 * C * es);
   void* dy = a.take(BT * C * es);
   float* dbuf = a.take_n<float>(BT * H);
-  float* ln_partial = a.take_n<float>((size_t)ln_bwd_blocks((long)BT) * 2 * C);
+  float* ln_partial = a.take_n<float>((size_t)ln_bwd_scratch((long)BT, (int)C));
   float* bias_partial = a.take_n<float>((size_t)BIAS_SPLITS * 4 * C);
+  float* splitk = a.take_n<float>((size_t)SPLITK_PART_ELEMS);
   size_t total = (a.off + 255) & ~(size_t)255;
   if (h) {
     h->lay = L;
@@ -245,6 +247,7 @@ size_t plan(const gpt2_config* c, char* base, gpt2* h) {
     h->row_loss = row_loss;
     h->dres = dres; h->dres_b = dres_b; h->dxtmp = dxtmp; h->dbig = dbig; h->dqkv = dqkv;
     h->dy = dy; h->dbuf = dbuf; h->ln_partial = ln_partial; h->bias_partial = bias_partial;
+    h->splitk = splitk;
   }
   return total;
 }
@@ -389,11 +392,13 @@ gpt2_status run_backward(gpt2* h, float scale) {
   // lm_head (tied): dz = s dlogits wte ; dwte += s dlogits^T z
   TIMED(h, GPT2_SITE_LMHEAD_DX, launch_gemm(at, M, C, Vp, h->logits, Vp, false, W(h, h->lay.wte), C, true, EPI_STORE,
                         DT_F32, epi(h->dxtmp, C, scale), 0, s));
-  TIMED(h, GPT2_SITE_LMHEAD_DW, launch_gemm(at, Vp, C, M, h->logits, Vp, true, h->z, C, true, EPI_ACCUM, DT_F32,
-                        epi(G + h->lay.wte, C, scale), 0, s));
+  TIMED(h, GPT2_SITE_LMHEAD_DW, launch_gemm_wgrad(at, Vp, C, M, h->logits, Vp, true, h->z, C, true,
+                                                  G + h->lay.wte, C, scale, h->splitk,
+                                                  SPLITK_PART_ELEMS, s));
+  // also the bias gradient of the last block's mlp c_proj: sum of dres
   TIMED(h, GPT2_SITE_LN_BWD, launch_layernorm_bwd(at, h->dxtmp, h->x_final, h->meanf, h->rstdf, P + h->lay.lnfw,
                                  h->dres, dres_copy, 0, h->ln_partial, G + h->lay.lnfw,
-                                 G + h->lay.lnfb, BT, C, s));
+                                 G + h->lay.lnfb, G + h->lay.layer[c.n_layer - 1].fc2b, BT, C, s));
   for (int l = c.n_layer - 1; l >= 0; --l) {
     const LayerOff& o = h->lay.layer[l];
     LayerAct& a = h->A[l];
@@ -403,30 +408,35 @@ gpt2_status run_backward(gpt2* h, float scale) {
     e.ldx = 4 * C;
     TIMED(h, GPT2_SITE_FCPROJ_DX, launch_gemm(at, M, 4 * C, C, dres_in, C, false, W(h, o.fc2w), 4 * C, true,
                           EPI_GELU_BWD, at, e, 0, s));
-    TIMED(h, GPT2_SITE_FCPROJ_DW, launch_gemm(at, C, 4 * C, M, dres_in, C, true, a.g, 4 * C, true, EPI_ATOMIC, DT_F32,
-                          epi(G + o.fc2w, 4 * C), 0, s));
-    TIMED(h, GPT2_SITE_BIAS_GRAD, launch_bias_grad(DT_F32, h->dres, BT, C, C, h->bias_partial, G + o.fc2b, s));
+    TIMED(h, GPT2_SITE_FCPROJ_DW, launch_gemm_wgrad(at, C, 4 * C, M, dres_in, C, true, a.g, 4 * C, true,
+                                                    G + o.fc2w, 4 * C, 1.f, h->splitk,
+                                                    SPLITK_PART_ELEMS, s));
     TIMED(h, GPT2_SITE_FC_DX, launch_gemm(at, M, C, 4 * C, h->dbig, 4 * C, false, W(h, o.fcw), C, true, EPI_STORE,
                           DT_F32, epi(h->dxtmp, C), 0, s));
-    TIMED(h, GPT2_SITE_FC_DW, launch_gemm(at, 4 * C, C, M, h->dbig, 4 * C, true, a.u2, C, true, EPI_ATOMIC, DT_F32,
-                          epi(G + o.fcw, C), 0, s));
+    TIMED(h, GPT2_SITE_FC_DW, launch_gemm_wgrad(at, 4 * C, C, M, h->dbig, 4 * C, true, a.u2, C, true,
+                                                G + o.fcw, C, 1.f, h->splitk, SPLITK_PART_ELEMS, s));
     TIMED(h, GPT2_SITE_BIAS_GRAD, launch_bias_grad(at, h->dbig, BT, 4 * C, 4 * C, h->bias_partial, G + o.fcb, s));
     TIMED(h, GPT2_SITE_LN_BWD, launch_layernorm_bwd(at, h->dxtmp, a.x_mid, a.mean2, a.rstd2, P + o.ln2w, h->dres,
-                                   dres_copy, 1, h->ln_partial, G + o.ln2w, G + o.ln2b, BT, C, s));
+                                   dres_copy, 1, h->ln_partial, G + o.ln2w, G + o.ln2b,
+                                   G + o.projb, BT, C, s));
     // x_mid = x_in + c_proj(attn(ln_1(x_in)))
     TIMED(h, GPT2_SITE_PROJ_DX, launch_gemm(at, M, C, C, dres_in, C, false, W(h, o.projw), C, true, EPI_STORE, at,
                           epi(h->dy, C), 0, s));
-    TIMED(h, GPT2_SITE_PROJ_DW, launch_gemm(at, C, C, M, dres_in, C, true, a.y, C, true, EPI_ATOMIC, DT_F32,
-                          epi(G + o.projw, C), 0, s));
-    TIMED(h, GPT2_SITE_BIAS_GRAD, launch_bias_grad(DT_F32, h->dres, BT, C, C, h->bias_partial, G + o.projb, s));
+    TIMED(h, GPT2_SITE_PROJ_DW, launch_gemm_wgrad(at, C, C, M, dres_in, C, true, a.y, C, true,
+                                                  G + o.projw, C, 1.f, h->splitk, SPLITK_PART_ELEMS,
+                                                  s));
     TIMED(h, GPT2_SITE_ATTN_BWD, launch_attn_bwd(at, a.qkv, a.y, a.lse, h->dy, h->dqkv, h->dbuf, B, T, H, hd, s));
     TIMED(h, GPT2_SITE_QKV_DX, launch_gemm(at, M, C, 3 * C, h->dqkv, 3 * C, false, W(h, o.attnw), C, true,
                           EPI_STORE, DT_F32, epi(h->dxtmp, C), 0, s));
-    TIMED(h, GPT2_SITE_QKV_DW, launch_gemm(at, 3 * C, C, M, h->dqkv, 3 * C, true, a.u1, C, true, EPI_ATOMIC, DT_F32,
-                          epi(G + o.attnw, C), 0, s));
+    TIMED(h, GPT2_SITE_QKV_DW, launch_gemm_wgrad(at, 3 * C, C, M, h->dqkv, 3 * C, true, a.u1, C, true,
+                                                 G + o.attnw, C, 1.f, h->splitk, SPLITK_PART_ELEMS,
+                                                 s));
     TIMED(h, GPT2_SITE_BIAS_GRAD, launch_bias_grad(at, h->dqkv, BT, 3 * C, 3 * C, h->bias_partial, G + o.attnb, s));
+    // the new dres also gives the bias gradient of the previous block's mlp c_proj
+    float* dsum = l > 0 ? G + h->lay.layer[l - 1].fc2b : nullptr;
     TIMED(h, GPT2_SITE_LN_BWD, launch_layernorm_bwd(at, h->dxtmp, a.x_in, a.mean1, a.rstd1, P + o.ln1w, h->dres,
-                                   dres_copy, 1, h->ln_partial, G + o.ln1w, G + o.ln1b, BT, C, s));
+                                   dres_copy, 1, h->ln_partial, G + o.ln1w, G + o.ln1b, dsum,
+                                   BT, C, s));
   }
   TIMED(h, GPT2_SITE_EMBED_BWD, launch_embed_bwd(h->idx, h->dres, G + h->lay.wte, G + h->lay.wpe, B, T, C, s));
   return GPT2_OK;

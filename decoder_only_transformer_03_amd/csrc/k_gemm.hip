@@ -1,5 +1,7 @@
 // GEMM entry: fp32 operands run on a vector-ALU tiled kernel (fp32 mode),
 // bf16 operands on the matrix-core kernel (gemm_mfma.h).
+#include <cstring>
+
 #include "kernels.h"
 
 namespace gemm_mfma {
@@ -18,9 +20,9 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(int M, int N, int K,
   __shared__ float As[16][68];
   __shared__ float Bs[16][68];
   const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
-  const long m0 = (long)blockIdx.y * 64;
+  const long m0 = (long)blockIdx.z * 64;
   const long n0 = (long)blockIdx.x * 64;
-  const int kb = blockIdx.z * kchunk;
+  const int kb = blockIdx.y * kchunk;  // split-K slice (the epilogue reads blockIdx.y)
   const int ke = kb + kchunk < K ? kb + kchunk : K;
   float acc[4][4];
 #pragma unroll
@@ -69,7 +71,7 @@ static hipError_t f32_run(int M, int N, int K, const float* A, long lda, const f
   int kchunk = (K + split_k - 1) / split_k;
   kchunk = (kchunk + 15) / 16 * 16;
   int splits = (K + kchunk - 1) / kchunk;
-  dim3 grid((N + 63) / 64, (M + 63) / 64, splits);
+  dim3 grid((N + 63) / 64, splits, (M + 63) / 64);
   gemm_f32_kernel<AT, BT, EPI, float><<<grid, 256, 0, s>>>(M, N, K, A, lda, B, ldb, e, kchunk);
   return hipGetLastError();
 }
@@ -91,8 +93,77 @@ static hipError_t f32_by_epi(int M, int N, int K, const float* A, long lda, cons
       return f32_run<AT, BT, EPI_ATOMIC>(M, N, K, A, lda, B, ldb, e, split_k, s);
     }
     case EPI_GELU_BWD: return f32_run<AT, BT, EPI_GELU_BWD>(M, N, K, A, lda, B, ldb, e, 1, s);
+    case EPI_PARTIAL: return f32_run<AT, BT, EPI_PARTIAL>(M, N, K, A, lda, B, ldb, e, split_k, s);
   }
   return hipErrorInvalidValue;
+}
+
+// Split count of a weight-gradient GEMM (long contraction, small output):
+// enough K-slices that the 256x256 (bf16) or 64x64 (fp32) tiles fill the
+// GPU once, each slice at least 4 k-tiles deep.
+// The number of slices a launch with `s` requested actually produces (the
+// launchers round the slice depth up to whole k-tiles).
+static int exact_splits(DType in_t, int K, int s) {
+  if (s <= 1) return 1;
+  if (in_t == DT_BF16) {
+    int nkt = (K + 63) / 64;
+    int kps = (nkt + s - 1) / s;
+    return (nkt + kps - 1) / kps;
+  }
+  int kchunk = ((K + s - 1) / s + 15) / 16 * 16;
+  return (K + kchunk - 1) / kchunk;
+}
+
+int gemm_partial_splits(DType in_t, int M, int N, int K) {
+  const int tile = in_t == DT_BF16 ? 256 : 64;
+  const int kt = in_t == DT_BF16 ? 64 : 16;
+  long tiles = (long)((M + tile - 1) / tile) * ((N + tile - 1) / tile);
+  long s = 256 / tiles;
+  long cap = (K / kt) / 4;
+  if (s > cap) s = cap;
+  if (s > 64) s = 64;
+  return exact_splits(in_t, K, s < 1 ? 1 : (int)s);
+}
+
+// out[m*ldo + n] += sum_z part[z][m][n]
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ part,
+                                                            int splits, long MN, int N,
+                                                            float* __restrict__ out, long ldo) {
+  long i4 = ((long)blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i4 >= MN) return;
+  float4 a = *reinterpret_cast<const float4*>(part + i4);
+  for (int z = 1; z < splits; ++z) {
+    float4 b = *reinterpret_cast<const float4*>(part + (long)z * MN + i4);
+    a.x += b.x; a.y += b.y; a.z += b.z; a.w += b.w;
+  }
+  long m = i4 / N;
+  int n = (int)(i4 - m * N);
+  float4* o = reinterpret_cast<float4*>(out + m * ldo + n);
+  float4 c = *o;
+  *o = make_float4(c.x + a.x, c.y + a.y, c.z + a.z, c.w + a.w);
+}
+
+hipError_t launch_gemm_wgrad(DType in_t, int M, int N, int K, const void* A, long lda, bool a_t,
+                             const void* B, long ldb, bool b_t, float* out, long ldo, float alpha,
+                             float* part, long part_elems, hipStream_t s) {
+  int S = gemm_partial_splits(in_t, M, N, K);
+  while (S > 1 && (long)S * M * N > part_elems) S = exact_splits(in_t, K, S - 1);
+  EpiArgs e;
+  memset(&e, 0, sizeof(e));
+  e.alpha = alpha;
+  if (S == 1) {
+    e.out = out;
+    e.ldo = ldo;
+    return launch_gemm(in_t, M, N, K, A, lda, a_t, B, ldb, b_t, EPI_ACCUM, DT_F32, e, 1, s);
+  }
+  e.out = part;
+  e.ldo = N;
+  e.split_stride = (long)M * N;
+  hipError_t r = launch_gemm(in_t, M, N, K, A, lda, a_t, B, ldb, b_t, EPI_PARTIAL, DT_F32, e, S, s);
+  if (r != hipSuccess) return r;
+  long MN = (long)M * N;
+  splitk_reduce_kernel<<<(unsigned)((MN / 4 + 255) / 256), 256, 0, s>>>(part, S, MN, N, out, ldo);
+  return hipGetLastError();
 }
 
 hipError_t launch_gemm(DType in_t, int M, int N, int K, const void* A, long lda, bool a_t,

@@ -72,7 +72,7 @@ __global__ __launch_bounds__(256) void embed_bwd_wpe_kernel(const float* __restr
 // ---------------------------------------------------------------------------
 constexpr int LN_MAXV = 8;  // float4 per lane: C <= 2048
 
-template <typename TO>
+template <int NV, typename TO>
 __global__ __launch_bounds__(256) void layernorm_fwd_kernel(const float* __restrict__ x,
                                                             const float* __restrict__ w,
                                                             const float* __restrict__ b,
@@ -84,10 +84,10 @@ __global__ __launch_bounds__(256) void layernorm_fwd_kernel(const float* __restr
   int lane = threadIdx.x & 63;
   if (row >= rows) return;
   const float* xr = x + row * C;
-  float v[LN_MAXV][4];
+  float v[NV][4];
   float s = 0.f;
 #pragma unroll
-  for (int i = 0; i < LN_MAXV; ++i) {
+  for (int i = 0; i < NV; ++i) {
     int c = (i * 64 + lane) * 4;
     if (c < C) {
       ld4(xr + c, v[i]);
@@ -97,7 +97,7 @@ __global__ __launch_bounds__(256) void layernorm_fwd_kernel(const float* __restr
   float mean = wave_sum(s) / (float)C;
   float q = 0.f;
 #pragma unroll
-  for (int i = 0; i < LN_MAXV; ++i) {
+  for (int i = 0; i < NV; ++i) {
     int c = (i * 64 + lane) * 4;
     if (c < C) {
 #pragma unroll
@@ -111,7 +111,7 @@ __global__ __launch_bounds__(256) void layernorm_fwd_kernel(const float* __restr
   float rstd = 1.0f / sqrtf(var + 1e-5f);
   TO* yr = y + row * C;
 #pragma unroll
-  for (int i = 0; i < LN_MAXV; ++i) {
+  for (int i = 0; i < NV; ++i) {
     int c = (i * 64 + lane) * 4;
     if (c < C) {
       float g[4], bb[4], o[4];
@@ -132,33 +132,34 @@ __global__ __launch_bounds__(256) void layernorm_fwd_kernel(const float* __restr
 // LayerNorm backward.  With xhat = (x - mean) rstd and d = dy * w:
 //   dx = rstd (d - mean(d) - xhat mean(d xhat)),  dw = sum dy xhat, db = sum dy.
 // dres = dx (accumulate = 0) or dres += dx; an optional bf16 copy of the new
-// dres feeds the next bf16 GEMM.  dw/db: per-block partial sums, reduced by
-// colsum_partials_kernel (deterministic).
+// dres feeds the next bf16 GEMM.  Per-workgroup partial column sums of
+// [dw | db | new dres] (the last is the bias gradient of the linear layer
+// that consumes dres) go to partial[blockIdx.x][3C].
 // ---------------------------------------------------------------------------
-template <typename TB>
+template <int NV, typename TB>
 __global__ __launch_bounds__(256) void layernorm_bwd_kernel(
     const float* __restrict__ dy, const float* __restrict__ x, const float* __restrict__ mean,
     const float* __restrict__ rstd, const float* __restrict__ w, float* __restrict__ dres,
     TB* __restrict__ dres_copy, int accumulate, float* __restrict__ partial, long rows, int C,
     int rows_per_block) {
-  extern __shared__ float sred[];  // [4][2C]
+  extern __shared__ float sred[];  // [4][3C]
   int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  float dg[LN_MAXV][4], db[LN_MAXV][4], wv[LN_MAXV][4];
+  float dg[NV][4], db[NV][4], ds[NV][4], wv[NV][4];
 #pragma unroll
-  for (int i = 0; i < LN_MAXV; ++i) {
+  for (int i = 0; i < NV; ++i) {
     int c = (i * 64 + lane) * 4;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) dg[i][j] = db[i][j] = 0.f;
+    for (int j = 0; j < 4; ++j) dg[i][j] = db[i][j] = ds[i][j] = 0.f;
     if (c < C) ld4(w + c, wv[i]);
   }
   long r0 = (long)blockIdx.x * rows_per_block;
   long r1 = r0 + rows_per_block < rows ? r0 + rows_per_block : rows;
   for (long row = r0 + wave; row < r1; row += 4) {
     float mu = mean[row], rs = rstd[row];
-    float g[LN_MAXV][4], xh[LN_MAXV][4];
+    float g[NV][4], xh[NV][4];
     float s1 = 0.f, s2 = 0.f;
 #pragma unroll
-    for (int i = 0; i < LN_MAXV; ++i) {
+    for (int i = 0; i < NV; ++i) {
       int c = (i * 64 + lane) * 4;
       if (c < C) {
         float xv[4];
@@ -179,7 +180,7 @@ __global__ __launch_bounds__(256) void layernorm_bwd_kernel(
     s1 = wave_sum(s1) / (float)C;
     s2 = wave_sum(s2) / (float)C;
 #pragma unroll
-    for (int i = 0; i < LN_MAXV; ++i) {
+    for (int i = 0; i < NV; ++i) {
       int c = (i * 64 + lane) * 4;
       if (c < C) {
         float o[4];
@@ -189,6 +190,7 @@ __global__ __launch_bounds__(256) void layernorm_bwd_kernel(
         for (int j = 0; j < 4; ++j) {
           float dx = rs * (g[i][j] - s1 - xh[i][j] * s2);
           o[j] = accumulate ? o[j] + dx : dx;
+          ds[i][j] += o[j];
         }
         st4(dr, o);
         if (dres_copy) st4(dres_copy + row * C + c, o);
@@ -196,49 +198,63 @@ __global__ __launch_bounds__(256) void layernorm_bwd_kernel(
     }
   }
 #pragma unroll
-  for (int i = 0; i < LN_MAXV; ++i) {
+  for (int i = 0; i < NV; ++i) {
     int c = (i * 64 + lane) * 4;
     if (c < C) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        sred[wave * 2 * C + c + j] = dg[i][j];
-        sred[wave * 2 * C + C + c + j] = db[i][j];
+        sred[wave * 3 * C + c + j] = dg[i][j];
+        sred[wave * 3 * C + C + c + j] = db[i][j];
+        sred[wave * 3 * C + 2 * C + c + j] = ds[i][j];
       }
     }
   }
   __syncthreads();
-  for (int c = threadIdx.x; c < 2 * C; c += 256) {
-    float s = sred[c] + sred[2 * C + c] + sred[4 * C + c] + sred[6 * C + c];
-    partial[(long)blockIdx.x * 2 * C + c] = s;
+  for (int c = threadIdx.x; c < 3 * C; c += 256) {
+    float t = (sred[c] + sred[3 * C + c]) + (sred[6 * C + c] + sred[9 * C + c]);
+    partial[(long)blockIdx.x * 3 * C + c] = t;
   }
 }
 
-// out[c] += sum_p partial[p][c]   (one thread per column, fixed order)
-__global__ __launch_bounds__(256) void colsum_partials_kernel(const float* __restrict__ partial,
-                                                              int nparts, int width,
-                                                              float* __restrict__ out0,
-                                                              float* __restrict__ out1,
-                                                              int split) {
-  int c = blockIdx.x * 256 + threadIdx.x;
-  if (c >= width) return;
-  float s = 0.f;
-  for (int p = 0; p < nparts; ++p) s += partial[(long)p * width + c];
-  if (c < split) out0[c] += s;
-  else out1[c - split] += s;
-}
-
-// Column sums of a (rows x N) matrix into per-split partials: bias gradients.
+// Column sums of a (rows x N) matrix: workgroup (64 columns) x (rows of one
+// split), 4 row phases per workgroup, fixed summation order.
+// partial[split][n] = sum over the split's rows.
 template <typename T>
 __global__ __launch_bounds__(256) void colsum_kernel(const T* __restrict__ X, long rows, int N,
                                                      long ldx, float* __restrict__ partial,
                                                      long rows_per_split) {
-  int n = blockIdx.x * 256 + threadIdx.x;
-  if (n >= N) return;
-  long r0 = (long)blockIdx.y * rows_per_split;
-  long r1 = r0 + rows_per_split < rows ? r0 + rows_per_split : rows;
+  __shared__ float s[4][64];
+  const int c = threadIdx.x & 63, g = threadIdx.x >> 6;
+  const int n = blockIdx.x * 64 + c;
+  const long r0 = (long)blockIdx.y * rows_per_split;
+  const long r1 = r0 + rows_per_split < rows ? r0 + rows_per_split : rows;
+  float a = 0.f;
+  if (n < N) {
+    long r = r0 + g;
+    for (; r + 12 < r1; r += 16)
+      a += (ldf(X + r * ldx + n) + ldf(X + (r + 4) * ldx + n)) +
+           (ldf(X + (r + 8) * ldx + n) + ldf(X + (r + 12) * ldx + n));
+    for (; r < r1; r += 4) a += ldf(X + r * ldx + n);
+  }
+  s[g][c] = a;
+  __syncthreads();
+  if (g == 0 && n < N) partial[(long)blockIdx.y * N + n] = (s[0][c] + s[1][c]) + (s[2][c] + s[3][c]);
+}
+
+// dst_k[c] += sum_p partial[p][k*w + c] for the non-null destinations (k = 0..2).
+__global__ __launch_bounds__(256) void colsum_finish_kernel(const float* __restrict__ partial,
+                                                            int nparts, int w,
+                                                            float* __restrict__ d0,
+                                                            float* __restrict__ d1,
+                                                            float* __restrict__ d2, int ncols) {
+  int c = blockIdx.x * 256 + threadIdx.x;
+  if (c >= ncols) return;
+  int k = c / w, cc = c - k * w;
+  float* d = k == 0 ? d0 : k == 1 ? d1 : d2;
+  if (!d) return;
   float s = 0.f;
-  for (long r = r0; r < r1; ++r) s += ldf(X + r * ldx + n);
-  partial[(long)blockIdx.y * N + n] = s;
+  for (int p = 0; p < nparts; ++p) s += partial[(long)p * ncols + c];
+  d[cc] += s;
 }
 
 // ---------------------------------------------------------------------------
@@ -307,74 +323,75 @@ template <> struct Row8<float> {
   }
 };
 
-__device__ __forceinline__ float block_reduce_256(float v, bool is_max, float* s4) {
-  v = is_max ? wave_max(v) : wave_sum(v);
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) s4[threadIdx.x >> 6] = v;
-  __syncthreads();
-  return is_max ? fmaxf(fmaxf(s4[0], s4[1]), fmaxf(s4[2], s4[3]))
-                : (s4[0] + s4[1]) + (s4[2] + s4[3]);
-}
 
-// One workgroup per row; the row is read once into registers, its
-// log-sum-exp formed, and the row is overwritten with
+// One workgroup per row.  Pass 1 streams the row once keeping a running
+// (max, sum of exp) per thread; the block combines them into the row's
+// log-sum-exp.  Pass 2 re-reads the row (now resident in the on-die caches)
+// and overwrites it with
 //   d(loss)/d(logits) = (softmax - onehot(target)) / n_valid   (0 if ignored).
 // Padded vocabulary columns take part like real ones.
-template <typename T, int MAXCH>
-__global__ __launch_bounds__(256) void xent_fused_kernel(T* __restrict__ logits,
-                                                         const int32_t* __restrict__ targets,
-                                                         const int* __restrict__ n_valid,
-                                                         float* __restrict__ row_loss, int Vp) {
-  __shared__ float s4[4];
-  long row = blockIdx.x;
+template <typename T, int NT>
+__global__ __launch_bounds__(NT) void xent_fused_kernel(T* __restrict__ logits,
+                                                        const int32_t* __restrict__ targets,
+                                                        const int* __restrict__ n_valid,
+                                                        float* __restrict__ row_loss, int Vp) {
+  constexpr int NW = NT / 64;
+  __shared__ float sm[NW], ss[NW];
+  const long row = blockIdx.x;
   T* lr = logits + row * (long)Vp;
   int tgt = targets[row];
-  bool valid = tgt != -1;
+  const bool valid = tgt != -1;
   if (tgt < 0 || tgt >= Vp) tgt = -1;  // out-of-range already flagged by count_valid
-  int nchunks = Vp >> 3;
-  Row8<T> v[MAXCH];
-  float mx = -INFINITY;
+  const float xt = valid && tgt >= 0 ? ldf(lr + tgt) : 0.f;
+  const int nchunks = Vp >> 3;
+  float m = -__builtin_inff(), sum = 0.f;
+#pragma unroll 2
+  for (int ch = threadIdx.x; ch < nchunks; ch += NT) {
+    Row8<T> v;
+    v.load(lr + ch * 8);
+    float cm = v.get(0);
 #pragma unroll
-  for (int i = 0; i < MAXCH; ++i) {
-    int ch = i * 256 + threadIdx.x;
-    if (ch < nchunks) {
-      v[i].load(lr + ch * 8);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) mx = fmaxf(mx, v[i].get(j));
+    for (int j = 1; j < 8; ++j) cm = fmaxf(cm, v.get(j));
+    if (cm > m) {
+      sum *= __expf(m - cm);
+      m = cm;
     }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) sum += __expf(v.get(j) - m);
   }
-  mx = block_reduce_256(mx, true, s4);
-  float sum = 0.f, xt = 0.f;
+  // combine (m, sum) over the wavefront, then over the workgroup
 #pragma unroll
-  for (int i = 0; i < MAXCH; ++i) {
-    int ch = i * 256 + threadIdx.x;
-    if (ch < nchunks) {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        float e = v[i].get(j);
-        sum += __expf(e - mx);
-        if (ch * 8 + j == tgt) xt = e;
-      }
-    }
+  for (int o = 32; o > 0; o >>= 1) {
+    float om = __shfl_xor(m, o, 64), os = __shfl_xor(sum, o, 64);
+    float nm = fmaxf(m, om);
+    sum = (m == nm ? sum : sum * __expf(m - nm)) + (om == nm ? os : os * __expf(om - nm));
+    m = nm;
   }
-  sum = block_reduce_256(sum, false, s4);
-  xt = block_reduce_256(xt, false, s4);  // exactly one thread holds a non-zero term
-  float lse = mx + __logf(sum);
-  int nv = *n_valid;
-  float inv = nv > 0 ? 1.0f / (float)nv : 0.f;
-  float scale = valid ? inv : 0.f;
+  if ((threadIdx.x & 63) == 0) {
+    sm[threadIdx.x >> 6] = m;
+    ss[threadIdx.x >> 6] = sum;
+  }
+  __syncthreads();
+  float M = sm[0];
 #pragma unroll
-  for (int i = 0; i < MAXCH; ++i) {
-    int ch = i * 256 + threadIdx.x;
-    if (ch < nchunks) {
-      float o[8];
+  for (int i = 1; i < NW; ++i) M = fmaxf(M, sm[i]);
+  float S = 0.f;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        float p = __expf(v[i].get(j) - lse);
-        o[j] = (p - (ch * 8 + j == tgt ? 1.0f : 0.0f)) * scale;
-      }
-      Row8<T>::store(lr + ch * 8, o);
+  for (int i = 0; i < NW; ++i) S += ss[i] * __expf(sm[i] - M);
+  const float lse = M + __logf(S);
+  const int nv = *n_valid;
+  const float scale = valid && nv > 0 ? 1.0f / (float)nv : 0.f;
+#pragma unroll 2
+  for (int ch = threadIdx.x; ch < nchunks; ch += NT) {
+    Row8<T> v;
+    v.load(lr + ch * 8);
+    float o[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      float p = __expf(v.get(j) - lse);
+      o[j] = (p - (ch * 8 + j == tgt ? 1.0f : 0.0f)) * scale;
     }
+    Row8<T>::store(lr + ch * 8, o);
   }
   if (threadIdx.x == 0) row_loss[row] = valid ? lse - xt : 0.f;
 }
@@ -522,67 +539,114 @@ hipError_t launch_embed_bwd(const int32_t* idx, const float* dx, float* dwte, fl
   return hipGetLastError();
 }
 
+template <int NV>
+static void ln_fwd_nv(DType out_t, const float* x, const float* w, const float* b, void* y,
+                      float* mean, float* rstd, long rows, int C, hipStream_t s) {
+  if (out_t == DT_BF16)
+    layernorm_fwd_kernel<NV, bf16_t><<<nblk(rows, 4), 256, 0, s>>>(x, w, b, (bf16_t*)y, mean, rstd,
+                                                                   rows, C);
+  else
+    layernorm_fwd_kernel<NV, float><<<nblk(rows, 4), 256, 0, s>>>(x, w, b, (float*)y, mean, rstd,
+                                                                  rows, C);
+}
+
 hipError_t launch_layernorm_fwd(DType out_t, const float* x, const float* w, const float* b,
                                 void* y, float* mean, float* rstd, long rows, int C,
                                 hipStream_t s) {
-  if (out_t == DT_BF16)
-    layernorm_fwd_kernel<bf16_t><<<nblk(rows, 4), 256, 0, s>>>(x, w, b, (bf16_t*)y, mean, rstd,
-                                                               rows, C);
-  else
-    layernorm_fwd_kernel<float><<<nblk(rows, 4), 256, 0, s>>>(x, w, b, (float*)y, mean, rstd,
-                                                              rows, C);
+  switch ((C + 255) / 256) {
+    case 1: ln_fwd_nv<1>(out_t, x, w, b, y, mean, rstd, rows, C, s); break;
+    case 2: ln_fwd_nv<2>(out_t, x, w, b, y, mean, rstd, rows, C, s); break;
+    case 3: ln_fwd_nv<3>(out_t, x, w, b, y, mean, rstd, rows, C, s); break;
+    case 4: ln_fwd_nv<4>(out_t, x, w, b, y, mean, rstd, rows, C, s); break;
+    case 5: ln_fwd_nv<5>(out_t, x, w, b, y, mean, rstd, rows, C, s); break;
+    case 6: ln_fwd_nv<6>(out_t, x, w, b, y, mean, rstd, rows, C, s); break;
+    case 7: ln_fwd_nv<7>(out_t, x, w, b, y, mean, rstd, rows, C, s); break;
+    case 8: ln_fwd_nv<8>(out_t, x, w, b, y, mean, rstd, rows, C, s); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
 int ln_bwd_blocks(long rows) { return (int)((rows + LN_BWD_ROWS - 1) / LN_BWD_ROWS); }
 
+// Column sums of `partial` (nparts x ncols) in two passes: COLSUM_SPLITS row
+// slices, then the fixed-order finish into up to three destinations.
+static hipError_t colsum_into(const float* X, long rows, int ncols, float* scratch, int w,
+                              float* d0, float* d1, float* d2, hipStream_t s) {
+  int splits = rows >= 64 * COLSUM_SPLITS ? COLSUM_SPLITS : 1;
+  long rps = (rows + splits - 1) / splits;
+  float* part2 = scratch;
+  colsum_kernel<float><<<dim3(nblk(ncols, 64), splits), 256, 0, s>>>(X, rows, ncols, ncols, part2,
+                                                                    rps);
+  colsum_finish_kernel<<<nblk(ncols, 256), 256, 0, s>>>(part2, splits, w, d0, d1, d2, ncols);
+  return hipGetLastError();
+}
+
+template <int NV>
+static hipError_t ln_bwd_nv(DType copy_t, const float* dy, const float* x, const float* mean,
+                            const float* rstd, const float* w, float* dres, void* dres_copy,
+                            int accumulate, float* partial, long rows, int C, int nb, size_t shm,
+                            hipStream_t s) {
+  if (shm > 65536) {  // wide models: allow more than the default dynamic LDS
+    hipError_t e = copy_t == DT_BF16
+        ? hipFuncSetAttribute((const void*)layernorm_bwd_kernel<NV, bf16_t>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm)
+        : hipFuncSetAttribute((const void*)layernorm_bwd_kernel<NV, float>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)shm);
+    if (e != hipSuccess) return e;
+  }
+  if (copy_t == DT_BF16)
+    layernorm_bwd_kernel<NV, bf16_t><<<nb, 256, shm, s>>>(dy, x, mean, rstd, w, dres,
+                                                           (bf16_t*)dres_copy, accumulate, partial,
+                                                           rows, C, LN_BWD_ROWS);
+  else
+    layernorm_bwd_kernel<NV, float><<<nb, 256, shm, s>>>(dy, x, mean, rstd, w, dres,
+                                                          (float*)dres_copy, accumulate, partial,
+                                                          rows, C, LN_BWD_ROWS);
+  return hipGetLastError();
+}
+
 hipError_t launch_layernorm_bwd(DType copy_t, const float* dy, const float* x, const float* mean,
                                 const float* rstd, const float* w, float* dres, void* dres_copy,
-                                int accumulate, float* partial, float* dw, float* db, long rows,
-                                int C, hipStream_t s) {
+                                int accumulate, float* partial, float* dw, float* db,
+                                float* dsum, long rows, int C, hipStream_t s) {
   int nb = ln_bwd_blocks(rows);
-  size_t shm = (size_t)8 * C * sizeof(float);
-  if (copy_t == DT_BF16)
-    layernorm_bwd_kernel<bf16_t><<<nb, 256, shm, s>>>(dy, x, mean, rstd, w, dres,
-                                                       (bf16_t*)dres_copy, accumulate, partial,
-                                                       rows, C, LN_BWD_ROWS);
-  else
-    layernorm_bwd_kernel<float><<<nb, 256, shm, s>>>(dy, x, mean, rstd, w, dres,
-                                                      (float*)dres_copy, accumulate, partial, rows,
-                                                      C, LN_BWD_ROWS);
-  colsum_partials_kernel<<<nblk(2 * C, 256), 256, 0, s>>>(partial, nb, 2 * C, dw, db, C);
-  return hipGetLastError();
+  size_t shm = (size_t)12 * C * sizeof(float);
+  hipError_t e;
+  switch ((C + 255) / 256) {
+#define LNB(NV) \
+  case NV: e = ln_bwd_nv<NV>(copy_t, dy, x, mean, rstd, w, dres, dres_copy, accumulate, partial, rows, C, nb, shm, s); break;
+    LNB(1) LNB(2) LNB(3) LNB(4) LNB(5) LNB(6) LNB(7) LNB(8)
+#undef LNB
+    default: return hipErrorInvalidValue;
+  }
+  if (e != hipSuccess) return e;
+  float* scratch = partial + (long)nb * 3 * C;
+  return colsum_into(partial, nb, 3 * C, scratch, C, dw, db, dsum, s);
 }
 
 hipError_t launch_bias_grad(DType in_t, const void* X, long rows, int N, long ldx, float* partial,
                             float* db, hipStream_t s) {
   int splits = BIAS_SPLITS;
   long rps = (rows + splits - 1) / splits;
-  dim3 grid(nblk(N, 256), splits);
+  dim3 grid(nblk(N, 64), splits);
   if (in_t == DT_BF16)
     colsum_kernel<bf16_t><<<grid, 256, 0, s>>>((const bf16_t*)X, rows, N, ldx, partial, rps);
   else
     colsum_kernel<float><<<grid, 256, 0, s>>>((const float*)X, rows, N, ldx, partial, rps);
-  colsum_partials_kernel<<<nblk(N, 256), 256, 0, s>>>(partial, splits, N, db, db, N);
+  colsum_finish_kernel<<<nblk(N, 256), 256, 0, s>>>(partial, splits, N, db, nullptr, nullptr, N);
   return hipGetLastError();
 }
 
 hipError_t launch_xent(DType t, void* logits, const int32_t* targets, int* n_valid,
                        float* row_loss, float* loss, long rows, int Vp, int* err, hipStream_t s) {
   count_valid_kernel<<<1, 1024, 0, s>>>(targets, rows, Vp, n_valid, err);
-  if (t == DT_BF16) {
-    if (Vp > 256 * 8 * 25) return hipErrorInvalidValue;
-    xent_fused_kernel<bf16_t, 25><<<(unsigned)rows, 256, 0, s>>>((bf16_t*)logits, targets,
-                                                                  n_valid, row_loss, Vp);
-  } else {
-    if (Vp > 256 * 8 * 25) return hipErrorInvalidValue;
-    if (Vp <= 256 * 8 * 4)
-      xent_fused_kernel<float, 4><<<(unsigned)rows, 256, 0, s>>>((float*)logits, targets,
-                                                                  n_valid, row_loss, Vp);
-    else
-      xent_fused_kernel<float, 25><<<(unsigned)rows, 256, 0, s>>>((float*)logits, targets,
+  if (t == DT_BF16)
+    xent_fused_kernel<bf16_t, 256><<<(unsigned)rows, 256, 0, s>>>((bf16_t*)logits, targets,
                                                                    n_valid, row_loss, Vp);
-  }
+  else
+    xent_fused_kernel<float, 256><<<(unsigned)rows, 256, 0, s>>>((float*)logits, targets, n_valid,
+                                                                  row_loss, Vp);
   loss_reduce_kernel<<<1, 1024, 0, s>>>(row_loss, rows, n_valid, loss);
   return hipGetLastError();
 }

@@ -6,10 +6,16 @@
 
 enum DType : int { DT_F32 = 0, DT_BF16 = 1 };
 
-// LayerNorm backward: rows per workgroup (partials of dw/db are per workgroup)
-constexpr int LN_BWD_ROWS = 32;
+// LayerNorm backward: rows per workgroup (partials of dw/db/dsum are per workgroup)
+constexpr int LN_BWD_ROWS = 16;
 // bias-gradient column sums: row splits (partials of width N each)
 constexpr int BIAS_SPLITS = 64;
+// second-level column sums of the LayerNorm partials
+constexpr int COLSUM_SPLITS = 16;
+// floats of scratch launch_layernorm_bwd needs for rows x C
+inline long ln_bwd_scratch(long rows, int C) {
+  return ((rows + LN_BWD_ROWS - 1) / LN_BWD_ROWS) * 3L * C + (long)COLSUM_SPLITS * 3 * C;
+}
 // grad-norm: workgroups of the sum-of-squares pass (fp64 partials)
 constexpr int NORM_PARTS = 1024;
 
@@ -29,10 +35,12 @@ hipError_t launch_embed_bwd(const int32_t* idx, const float* dx, float* dwte, fl
 hipError_t launch_layernorm_fwd(DType out_t, const float* x, const float* w, const float* b,
                                 void* y, float* mean, float* rstd, long rows, int C,
                                 hipStream_t s);
+// dw, db += LayerNorm parameter gradients; dsum (may be null) += column sums
+// of the new dres.  partial: ln_bwd_scratch(rows, C) floats.
 hipError_t launch_layernorm_bwd(DType copy_t, const float* dy, const float* x, const float* mean,
                                 const float* rstd, const float* w, float* dres, void* dres_copy,
-                                int accumulate, float* partial, float* dw, float* db, long rows,
-                                int C, hipStream_t s);
+                                int accumulate, float* partial, float* dw, float* db,
+                                float* dsum, long rows, int C, hipStream_t s);
 hipError_t launch_bias_grad(DType in_t, const void* X, long rows, int N, long ldx, float* partial,
                             float* db, hipStream_t s);
 hipError_t launch_xent(DType t, void* logits, const int32_t* targets, int* n_valid,
@@ -53,6 +61,15 @@ hipError_t launch_bf16_to_f32(const bf16_t* src, float* dst, long n, hipStream_t
 hipError_t launch_gemm(DType in_t, int M, int N, int K, const void* A, long lda, bool a_t,
                        const void* B, long ldb, bool b_t, int epi, DType out_t, const EpiArgs& e,
                        int split_k, hipStream_t s);
+
+// Weight gradient out[m][n] += alpha * sum_k A(m,k) B(n,k) for a long
+// contraction: split over k into fp32 slices of `part` (part_elems floats of
+// scratch), then summed in fixed order into out (deterministic).
+hipError_t launch_gemm_wgrad(DType in_t, int M, int N, int K, const void* A, long lda, bool a_t,
+                             const void* B, long ldb, bool b_t, float* out, long ldo, float alpha,
+                             float* part, long part_elems, hipStream_t s);
+int gemm_partial_splits(DType in_t, int M, int N, int K);
+constexpr long SPLITK_PART_ELEMS = 256L * 256 * 256;
 
 // Causal self-attention on the fused qkv activation (B*T, 3C), head h of q,
 // k, v at columns h*hd, C + h*hd, 2C + h*hd.  y is (B*T, C) with heads

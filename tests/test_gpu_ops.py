@@ -138,6 +138,13 @@ def test_attention_fwd_bwd(dtype, hd, T):
     tol_y, tol_d = (1e-2, 2e-2) if dtype == "bf16" else (1e-5, 1e-4)
     assert e_y < tol_y
     assert e_l < (2e-4 if dtype == "bf16" else 1e-5)
-    assert max(e_d) < tol_d
+    if T == 1:
+        # one key: P = 1, so dS = P (dP - D) = 0 and dq = dk = 0 exactly; the
+        # kernel's values are rounding noise, bounded against the size of dv
+        scale = np.max(np.abs(dv))
+        assert np.max(np.abs(d_g[:, :2 * C])) <= tol_d * scale
+        assert e_d[2] < tol_d
+    else:
+        assert max(e_d) < tol_d
     assert e_D < 1e-4
     assert not torch.isnan(dqkv).any()

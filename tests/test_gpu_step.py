@@ -258,24 +258,56 @@ def test_bf16_124m_loss_and_activations(step_124m_b2):
 
 
 def test_bf16_124m_grads_and_update(step_124m_b2):
+    """bf16: gradients per tensor within 1.2e-2 normwise (bf16 storage of
+    activations and of the gradients flowing between layers, about
+    sqrt(#roundings) * 2^-9); the AdamW kernel exactly (the oracle's update
+    applied to the GPU's own gradients, 1e-5); and the parameters after one
+    step within 5e-3 normwise of the oracle's over the elements whose oracle
+    gradient exceeds the measured bf16 gradient noise of its tensor (4 x rms
+    of gpu - oracle over the element's row).  Below that floor the sign of g is not determined by
+    any bf16 computation, and Adam's first step is lr * sign(g): those
+    elements may differ by up to 2 lr, which is asserted instead."""
     d, flat, idx, tgt, g, r = step_124m_b2
     cfg = O.Config(**d)
     kb = key_bias_mask(cfg)
+    # the GPU's own gradients through the oracle's clip + AdamW
+    p_or = flat.astype(np.float32).copy()
+    g_own = g["grads"].copy()
+    O.clip_and_adamw(p_or, g_own, np.zeros_like(p_or), np.zeros_like(p_or), 1, LR, B1, B2, EPS, WD,
+                     CLIP, cfg=cfg)
     off = 0
-    worst_g, worst_p = 0.0, 0.0
+    worst_g = worst_p = worst_opt = 0.0
+    excluded = 0
     for name, shape in O.param_specs(cfg):
         n = int(np.prod(shape))
         sl = slice(off, off + n)
+        off += n
         keep = ~kb[sl]
         ga, gr = g["grads"][sl][keep].astype(np.float64), r["grads"][sl][keep].astype(np.float64)
-        eg = np.linalg.norm(ga - gr) / max(np.linalg.norm(gr), 1e-30)
         pa, pr = g["params"][sl][keep].astype(np.float64), r["params"][sl][keep].astype(np.float64)
-        ep = np.linalg.norm(pa - pr) / max(np.linalg.norm(pr), 1e-30)
-        flips = float(np.mean(np.sign(ga) != np.sign(gr)))
-        worst_g, worst_p = max(worst_g, eg), max(worst_p, ep)
+        po = p_or[sl][keep].astype(np.float64)
+        eg = np.linalg.norm(ga - gr) / max(np.linalg.norm(gr), 1e-30)
+        eo = np.max(np.abs(pa - po)) / max(np.max(np.abs(po)), 1e-30)
+        # noise floor per output row of a matrix (rows differ in scale: token
+        # rows absent from the batch, q/k/v thirds), per tensor for vectors
+        rows = shape[0] if len(shape) == 2 else 1
+        diff2 = np.zeros(n)
+        diff2[keep] = (ga - gr) ** 2
+        noise = np.sqrt(diff2.reshape(rows, -1).mean(axis=1))
+        noise = np.repeat(noise, n // rows)[keep]
+        det = np.abs(gr) > 4 * noise
+        ep = np.linalg.norm(pa[det] - pr[det]) / max(np.linalg.norm(pr[det]), 1e-30)
+        excluded += int((~det).sum())
+        assert np.max(np.abs(pa[~det] - pr[~det]), initial=0.0) <= 2.0 * LR * 1.001 + 1e-7, name
+        worst_g, worst_p, worst_opt = max(worst_g, eg), max(worst_p, ep), max(worst_opt, eo)
         if name.startswith(("wte", "wpe", "h.0.", "h.11.", "ln_f")):
-            print(f"{name:28s} grad normrel {eg:.2e}  param normrel {ep:.2e}  sign flips {flips:.2e}")
-        off += n
-    print(f"worst grad normrel {worst_g:.2e}, worst param normrel {worst_p:.2e}")
+            print(f"{name:28s} grad {eg:.2e} param(det) {ep:.2e} adamw {eo:.1e} "
+                  f"below-noise {np.mean(~det):.2e}")
+    frac = excluded / float((~kb).sum())
+    print(f"worst: grad {worst_g:.2e}, param {worst_p:.2e}, adamw {worst_opt:.2e}; "
+          f"below-noise fraction {frac:.3e}")
     assert abs(g["norm"] - r["norm"]) < 2e-2 * r["norm"]
+    assert worst_g < 1.2e-2
+    assert worst_opt < 1e-5
     assert worst_p < 5e-3
+    assert frac < 0.05

@@ -26,18 +26,46 @@ struct EpiArgs {
   long split_stride;
 };
 
+// Does the epilogue read memory per element (residual, old value, aux)?
+constexpr bool epi_reads(int EPI) {
+  return EPI == EPI_RESID || EPI == EPI_ACCUM || EPI == EPI_GELU_BWD;
+}
+constexpr bool epi_bias(int EPI) {
+  return EPI == EPI_STORE || EPI == EPI_BIAS_GELU || EPI == EPI_RESID;
+}
+
+// Phase 1: the per-element input of the epilogue (issue these for a whole
+// block of outputs before any store, so the loads overlap).
 template <int EPI, typename TO>
-__device__ __forceinline__ void epi_apply4(const EpiArgs& e, long m, int n, const float c[4]) {
+__device__ __forceinline__ void epi_load4(const EpiArgs& e, long m, int n, float in[4]) {
+  if constexpr (EPI == EPI_RESID) {
+    ld4(e.resid + m * e.ldr + n, in);
+  } else if constexpr (EPI == EPI_ACCUM) {
+    ld4(reinterpret_cast<const float*>(e.out) + m * e.ldo + n, in);
+  } else if constexpr (EPI == EPI_GELU_BWD) {
+    ld4(reinterpret_cast<const TO*>(e.aux) + m * e.ldx + n, in);
+  }
+}
+
+__device__ __forceinline__ void epi_load_bias(const EpiArgs& e, int n, float b[4]) {
+  if (e.bias) {
+    ld4(e.bias + n, b);
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) b[j] = 0.f;
+  }
+}
+
+// Phase 2: combine accumulator c, input `in` and bias `b`, and store.
+template <int EPI, typename TO>
+__device__ __forceinline__ void epi_store4(const EpiArgs& e, long m, int n, const float c[4],
+                                           const float in[4], const float b[4]) {
   float r[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) r[j] = e.alpha * c[j];
-  if constexpr (EPI == EPI_STORE || EPI == EPI_BIAS_GELU || EPI == EPI_RESID) {
-    if (e.bias) {
-      float b[4];
-      ld4(e.bias + n, b);
+  if constexpr (epi_bias(EPI)) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) r[j] += b[j];
-    }
+    for (int j = 0; j < 4; ++j) r[j] += b[j];
   }
   if constexpr (EPI == EPI_STORE) {
     st4(reinterpret_cast<TO*>(e.out) + m * e.ldo + n, r);
@@ -48,18 +76,13 @@ __device__ __forceinline__ void epi_apply4(const EpiArgs& e, long m, int n, cons
     for (int j = 0; j < 4; ++j) g[j] = gelu_tanh_f(r[j]);
     st4(reinterpret_cast<TO*>(e.out2) + m * e.ldo + n, g);
   } else if constexpr (EPI == EPI_RESID) {
-    float x[4];
-    ld4(e.resid + m * e.ldr + n, x);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) r[j] += x[j];
+    for (int j = 0; j < 4; ++j) r[j] += in[j];
     st4(reinterpret_cast<float*>(e.out) + m * e.ldo + n, r);
   } else if constexpr (EPI == EPI_ACCUM) {
-    float* o = reinterpret_cast<float*>(e.out) + m * e.ldo + n;
-    float x[4];
-    ld4(o, x);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) r[j] += x[j];
-    st4(o, r);
+    for (int j = 0; j < 4; ++j) r[j] += in[j];
+    st4(reinterpret_cast<float*>(e.out) + m * e.ldo + n, r);
   } else if constexpr (EPI == EPI_ATOMIC) {
     float* o = reinterpret_cast<float*>(e.out) + m * e.ldo + n;
 #pragma unroll
@@ -67,10 +90,17 @@ __device__ __forceinline__ void epi_apply4(const EpiArgs& e, long m, int n, cons
   } else if constexpr (EPI == EPI_PARTIAL) {
     st4(reinterpret_cast<float*>(e.out) + blockIdx.y * e.split_stride + m * e.ldo + n, r);
   } else if constexpr (EPI == EPI_GELU_BWD) {
-    float h[4];
-    ld4(reinterpret_cast<const TO*>(e.aux) + m * e.ldx + n, h);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) r[j] *= gelu_tanh_grad_f(h[j]);
+    for (int j = 0; j < 4; ++j) r[j] *= gelu_tanh_grad_f(in[j]);
     st4(reinterpret_cast<TO*>(e.out) + m * e.ldo + n, r);
   }
+}
+
+// Both phases for one group of four columns.
+template <int EPI, typename TO>
+__device__ __forceinline__ void epi_apply4(const EpiArgs& e, long m, int n, const float c[4]) {
+  float in[4] = {0.f, 0.f, 0.f, 0.f}, b[4];
+  epi_load4<EPI, TO>(e, m, n, in);
+  epi_load_bias(e, n, b);
+  epi_store4<EPI, TO>(e, m, n, c, in, b);
 }

@@ -32,86 +32,133 @@ __device__ __forceinline__ uint32_t word(const uint4& v, int i) {
   return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
 }
 
-// R rows x 64 k, k contiguous in global memory.
-template <int R>
+// R rows x 64 k, k contiguous in global memory; NT threads.  issue():
+// 16-byte global loads into registers; commit(): ds_write into the stage.
+template <int R, int NT>
 struct LoaderK {
-  uint4 v[R / 32];
-  __device__ __forceinline__ void load(const bf16_t* __restrict__ X, long ld, long r0, long rtot,
-                                       int k, int K, int tid) {
+  static constexpr int RPP = NT / 8;  // rows per pass
+  uint4 v[R / RPP];
+  __device__ __forceinline__ void issue(const bf16_t* __restrict__ X, long ld, long r0, long rtot,
+                                        int k, int K, int tid, bf16_t*) {
     int c = tid & 7, rr = tid >> 3;
     bool kin = k + c * 8 < K;
 #pragma unroll
-    for (int i = 0; i < R / 32; ++i) {
-      long row = r0 + rr + 32 * i;
+    for (int i = 0; i < R / RPP; ++i) {
+      long row = r0 + rr + RPP * i;
       if (kin && row < rtot)
         v[i] = *reinterpret_cast<const uint4*>(X + row * ld + k + c * 8);
       else
         v[i] = make_uint4(0, 0, 0, 0);
     }
   }
-  __device__ __forceinline__ void store(bf16_t* s, int tid) const {
+  __device__ __forceinline__ void commit(bf16_t* s, int tid) const {
     int c = tid & 7, rr = tid >> 3;
 #pragma unroll
-    for (int i = 0; i < R / 32; ++i) {
-      int row = rr + 32 * i;
+    for (int i = 0; i < R / RPP; ++i) {
+      int row = rr + RPP * i;
       *reinterpret_cast<uint4*>(s + row * BK + swz(row, c) * 8) = v[i];
     }
   }
 };
 
-// R rows x 64 k, rows contiguous in global memory (X[k*ld + row]).
-template <int R>
+// R rows x 64 k, k contiguous, K a multiple of 64: loaded straight into LDS
+// with global_load_lds_dwordx4.  One wavefront instruction fills 1 KB of LDS
+// = 8 rows; lane i lands in row i/8, physical chunk i%8, so it fetches the
+// logical chunk (i%8) ^ swizzle(row).  Rows past the matrix edge re-read the
+// last row (their products are never stored).
+template <int R, int NT>
+struct LoaderD {
+  static constexpr int NW = NT / 64;
+  static constexpr int PER_WAVE = R / 8 / NW;  // wavefront instructions per tile
+  __device__ __forceinline__ void issue(const bf16_t* __restrict__ X, long ld, long r0, long rtot,
+                                        int k, int, int tid, bf16_t* s) {
+    const int lane = tid & 63, w = tid >> 6;
+#pragma unroll
+    for (int j = 0; j < PER_WAVE; ++j) {
+      const int rbase = (w * PER_WAVE + j) * 8;
+      const int row = rbase + (lane >> 3);
+      const int c = (lane & 7) ^ ((row ^ (row >> 3)) & 7);
+      long grow = r0 + row;
+      grow = grow < rtot ? grow : rtot - 1;
+      const bf16_t* src = X + grow * ld + k + c * 8;
+      __builtin_amdgcn_global_load_lds(
+          (const __attribute__((address_space(1))) void*)src,
+          (__attribute__((address_space(3))) void*)(s + rbase * BK), 16, 0, 0);
+    }
+  }
+  __device__ __forceinline__ void commit(bf16_t*, int) const {}
+};
+
+// R rows x 64 k, rows contiguous in global memory (X[k*ld + row]).  Thread t
+// moves a KR (k) x 8 (row) block, KR = 8R/NT: KR 16-byte loads along the
+// rows, a register transpose with v_perm_b32, and 8 LDS writes of KR values.
+template <int R, int NT>
 struct LoaderT {
-  static constexpr int RC = R / 8;  // 8-row chunks across the tile
-  uint4 v[8];
-  __device__ __forceinline__ void load(const bf16_t* __restrict__ X, long ld, long r0, long rtot,
-                                       int k, int K, int tid) {
-    if (tid >= R) return;
+  static constexpr int RC = R / 8;        // 8-row chunks across the tile
+  static constexpr int KR = 8 * R / NT;   // k rows per thread (2, 4 or 8)
+  static_assert(KR == 2 || KR == 4 || KR == 8, "tile/thread combination");
+  uint4 v[KR];
+  __device__ __forceinline__ void issue(const bf16_t* __restrict__ X, long ld, long r0, long rtot,
+                                        int k, int K, int tid, bf16_t*) {
     int rc = tid % RC, kg = tid / RC;
     long col = r0 + rc * 8;
     bool cin = col < rtot;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      int kk = k + kg * 8 + j;
+    for (int j = 0; j < KR; ++j) {
+      int kk = k + kg * KR + j;
       if (cin && kk < K)
         v[j] = *reinterpret_cast<const uint4*>(X + (long)kk * ld + col);
       else
         v[j] = make_uint4(0, 0, 0, 0);
     }
   }
-  __device__ __forceinline__ void store(bf16_t* s, int tid) const {
-    if (tid >= R) return;
+  __device__ __forceinline__ void commit(bf16_t* s, int tid) const {
     int rc = tid % RC, kg = tid / RC;
+    const int kbase = kg * KR;  // first k of this thread inside the 64-deep tile
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
       const unsigned sel = (r & 1) ? 0x7632u : 0x5410u;
-      uint4 o;
-      o.x = __byte_perm(word(v[0], r >> 1), word(v[1], r >> 1), sel);
-      o.y = __byte_perm(word(v[2], r >> 1), word(v[3], r >> 1), sel);
-      o.z = __byte_perm(word(v[4], r >> 1), word(v[5], r >> 1), sel);
-      o.w = __byte_perm(word(v[6], r >> 1), word(v[7], r >> 1), sel);
       int row = rc * 8 + r;
-      *reinterpret_cast<uint4*>(s + row * BK + swz(row, kg) * 8) = o;
+      bf16_t* dst = s + row * BK + swz(row, kbase >> 3) * 8 + (kbase & 7);
+      if constexpr (KR == 8) {
+        uint4 o;
+        o.x = __byte_perm(word(v[0], r >> 1), word(v[1], r >> 1), sel);
+        o.y = __byte_perm(word(v[2], r >> 1), word(v[3], r >> 1), sel);
+        o.z = __byte_perm(word(v[4], r >> 1), word(v[5], r >> 1), sel);
+        o.w = __byte_perm(word(v[6], r >> 1), word(v[7], r >> 1), sel);
+        *reinterpret_cast<uint4*>(dst) = o;
+      } else if constexpr (KR == 4) {
+        uint2 o;
+        o.x = __byte_perm(word(v[0], r >> 1), word(v[1], r >> 1), sel);
+        o.y = __byte_perm(word(v[2], r >> 1), word(v[3], r >> 1), sel);
+        *reinterpret_cast<uint2*>(dst) = o;
+      } else {
+        *reinterpret_cast<uint32_t*>(dst) = __byte_perm(word(v[0], r >> 1), word(v[1], r >> 1), sel);
+      }
     }
   }
 };
 
-template <int R, bool T> struct Loader;
-template <int R> struct Loader<R, false> : LoaderK<R> {};
-template <int R> struct Loader<R, true> : LoaderT<R> {};
+// Operand layout: 0 k-contiguous via registers, 1 transposed, 2 k-contiguous direct to LDS.
+template <int R, int L, int NT> struct Loader;
+template <int R, int NT> struct Loader<R, 0, NT> : LoaderK<R, NT> {};
+template <int R, int NT> struct Loader<R, 1, NT> : LoaderT<R, NT> {};
+template <int R, int NT> struct Loader<R, 2, NT> : LoaderD<R, NT> {};
 
-template <int BM, int BN, bool AT, bool BT, int EPI, typename TO>
-__global__ __launch_bounds__(256, 1) void gemm_kernel(int M, int N, int K,
+// WM x WN wavefronts; each owns a (BM/WM) x (BN/WN) sub-tile.
+template <int BM, int BN, int WM, int WN, int LA, int LB, int EPI, typename TO>
+__global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(int M, int N, int K,
                                                       const bf16_t* __restrict__ A, long lda,
                                                       const bf16_t* __restrict__ B, long ldb,
                                                       EpiArgs e, int tiles_m, int tiles_n,
                                                       int kt_per_split) {
-  constexpr int WTM = BM / 2, WTN = BN / 2;
+  constexpr int NT = 64 * WM * WN;
+  constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int SM = WTM / 32, SN = WTN / 32;
   __shared__ __attribute__((aligned(16))) bf16_t smem[2][(BM + BN) * BK];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave & 1, wn = wave >> 1;
+  const int wm = wave % WM, wn = wave / WM;
 
   // Tile order.  Workgroups are dispatched round-robin over the 8 XCDs; give
   // each XCD a contiguous range of tile ids so that tiles sharing operand
@@ -144,54 +191,86 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(int M, int N, int K,
 #pragma unroll
       for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.f;
 
-  Loader<BM, AT> la;
-  Loader<BN, BT> lb;
-  la.load(A, lda, m0, M, kt0 * BK, K, tid);
-  lb.load(B, ldb, n0, N, kt0 * BK, K, tid);
-  la.store(smem[0], tid);
-  lb.store(smem[0] + BM * BK, tid);
+  Loader<BM, LA, NT> la;
+  Loader<BN, LB, NT> lb;
+  la.issue(A, lda, m0, M, kt0 * BK, K, tid, smem[0]);
+  lb.issue(B, ldb, n0, N, kt0 * BK, K, tid, smem[0] + BM * BK);
+  la.commit(smem[0], tid);
+  lb.commit(smem[0] + BM * BK, tid);
+  if constexpr (LA == 2 || LB == 2) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
 
+  // Fragments of k-substep kk (16 deep) for this wavefront's sub-tiles.
+  auto load_frags = [&](const bf16_t* sA, const bf16_t* sB, int kk, bf16x8_t* fa, bf16x8_t* fb) {
+    const int c = kk * 2 + (lane >> 5);
+#pragma unroll
+    for (int sm = 0; sm < SM; ++sm) {
+      int row = wm * WTM + sm * 32 + (lane & 31);
+      fa[sm] = *reinterpret_cast<const bf16x8_t*>(sA + row * BK + swz(row, c) * 8);
+    }
+#pragma unroll
+    for (int sn = 0; sn < SN; ++sn) {
+      int row = wn * WTN + sn * 32 + (lane & 31);
+      fb[sn] = *reinterpret_cast<const bf16x8_t*>(sB + row * BK + swz(row, c) * 8);
+    }
+  };
+
+  // Software pipeline: the global loads of k-tile t+1 are in flight during
+  // the MFMAs of tile t, and the LDS fragments of substep kk+1 are read while
+  // the MFMAs of substep kk run.
+  bf16x8_t fa[2][SM], fb[2][SN];
+  load_frags(smem[0], smem[0] + BM * BK, 0, fa[0], fb[0]);
   for (int kt = kt0; kt < kt1; ++kt) {
     const int cur = (kt - kt0) & 1;
     const bool more = kt + 1 < kt1;
     if (more) {
-      la.load(A, lda, m0, M, (kt + 1) * BK, K, tid);
-      lb.load(B, ldb, n0, N, (kt + 1) * BK, K, tid);
+      la.issue(A, lda, m0, M, (kt + 1) * BK, K, tid, smem[cur ^ 1]);
+      lb.issue(B, ldb, n0, N, (kt + 1) * BK, K, tid, smem[cur ^ 1] + BM * BK);
     }
     const bf16_t* sA = smem[cur];
     const bf16_t* sB = smem[cur] + BM * BK;
-#pragma unroll 1
+#pragma unroll
     for (int kk = 0; kk < BK / 16; ++kk) {
-      const int c = kk * 2 + (lane >> 5);
-      bf16x8_t fa[SM], fb[SN];
-#pragma unroll
-      for (int sm = 0; sm < SM; ++sm) {
-        int row = wm * WTM + sm * 32 + (lane & 31);
-        fa[sm] = *reinterpret_cast<const bf16x8_t*>(sA + row * BK + swz(row, c) * 8);
-      }
-#pragma unroll
-      for (int sn = 0; sn < SN; ++sn) {
-        int row = wn * WTN + sn * 32 + (lane & 31);
-        fb[sn] = *reinterpret_cast<const bf16x8_t*>(sB + row * BK + swz(row, c) * 8);
-      }
+      if (kk + 1 < BK / 16) load_frags(sA, sB, kk + 1, fa[(kk + 1) & 1], fb[(kk + 1) & 1]);
 #pragma unroll
       for (int sn = 0; sn < SN; ++sn)
 #pragma unroll
         for (int sm = 0; sm < SM; ++sm)
-          acc[sn][sm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[sn], fa[sm], acc[sn][sm], 0, 0, 0);
+          acc[sn][sm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[kk & 1][sn], fa[kk & 1][sm],
+                                                                acc[sn][sm], 0, 0, 0);
+      // keep the two-deep fragment pipeline: nothing moves across substeps
+      __builtin_amdgcn_sched_barrier(0);
     }
     if (more) {
-      la.store(smem[cur ^ 1], tid);
-      lb.store(smem[cur ^ 1] + BM * BK, tid);
+      la.commit(smem[cur ^ 1], tid);
+      lb.commit(smem[cur ^ 1] + BM * BK, tid);
+      if constexpr (LA == 2 || LB == 2) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     }
     __syncthreads();
+    if (more) load_frags(smem[cur ^ 1], smem[cur ^ 1] + BM * BK, 0, fa[0], fb[0]);
   }
 
   // acc[sn][sm][4i + j] is C[m][n] with m = sm*32 + lane%32 and
-  // n = sn*32 + 8i + 4(lane/32) + j inside the wavefront's sub-tile.
+  // n = sn*32 + 8i + 4(lane/32) + j inside the wavefront's sub-tile.  Per
+  // n-subtile: all epilogue inputs are loaded first, then combined and stored.
 #pragma unroll
-  for (int sn = 0; sn < SN; ++sn)
+  for (int sn = 0; sn < SN; ++sn) {
+    float bias[4][4];
+    float in[SM][4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const long n = n0 + wn * WTN + sn * 32 + 8 * i + 4 * (lane >> 5);
+      if constexpr (epi_bias(EPI)) {
+        if (n < N) epi_load_bias(e, (int)n, bias[i]);
+      }
+      if constexpr (epi_reads(EPI)) {
+#pragma unroll
+        for (int sm = 0; sm < SM; ++sm) {
+          const long m = m0 + wm * WTM + sm * 32 + (lane & 31);
+          if (m < M && n < N) epi_load4<EPI, TO>(e, m, (int)n, in[sm][i]);
+        }
+      }
+    }
 #pragma unroll
     for (int sm = 0; sm < SM; ++sm) {
       const long m = m0 + wm * WTM + sm * 32 + (lane & 31);
@@ -201,14 +280,15 @@ __global__ __launch_bounds__(256, 1) void gemm_kernel(int M, int N, int K,
         if (m < M && n < N) {
           float c4[4] = {acc[sn][sm][4 * i + 0], acc[sn][sm][4 * i + 1], acc[sn][sm][4 * i + 2],
                          acc[sn][sm][4 * i + 3]};
-          epi_apply4<EPI, TO>(e, m, (int)n, c4);
+          epi_store4<EPI, TO>(e, m, (int)n, c4, in[sm][i], bias[i]);
         }
       }
     }
+  }
 }
 
 // Host side: launch one instantiation.
-template <int BM, int BN, bool AT, bool BT, int EPI, typename TO>
+template <int BM, int BN, int WM, int WN, int LA, int LB, int EPI, typename TO>
 hipError_t run(int M, int N, int K, const bf16_t* A, long lda, const bf16_t* B, long ldb,
                const EpiArgs& e, int split_k, hipStream_t s) {
   int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
@@ -217,8 +297,8 @@ hipError_t run(int M, int N, int K, const bf16_t* A, long lda, const bf16_t* B, 
   int kps = (nkt + split_k - 1) / split_k;
   int splits = (nkt + kps - 1) / kps;
   dim3 grid(tiles_m * tiles_n, splits);
-  gemm_kernel<BM, BN, AT, BT, EPI, TO><<<grid, 256, 0, s>>>(M, N, K, A, lda, B, ldb, e, tiles_m,
-                                                             tiles_n, kps);
+  gemm_kernel<BM, BN, WM, WN, LA, LB, EPI, TO><<<grid, 64 * WM * WN, 0, s>>>(
+      M, N, K, A, lda, B, ldb, e, tiles_m, tiles_n, kps);
   return hipGetLastError();
 }
 
@@ -229,30 +309,31 @@ hipError_t dispatch(int M, int N, int K, const bf16_t* A, long lda, const bf16_t
 
 }  // namespace gemm_mfma
 
-// Explicit instantiation of all tile shapes and epilogues of one layout.
+// Explicit instantiation of the epilogues of one operand layout.  One tile
+// shape: 256 x 256 x 64 with 8 wavefronts (2 x 4, each 128 x 64).
 #define GEMM_MFMA_DEFINE_DISPATCH(AT, BT)                                                       \
   namespace gemm_mfma {                                                                         \
-  template <int BM, int BN>                                                                     \
+  template <int LA, int LB>                                                                     \
   static hipError_t by_epi(int M, int N, int K, const bf16_t* A, long lda, const bf16_t* B,    \
                            long ldb, int epi, DType out_t, const EpiArgs& e, int sk,            \
                            hipStream_t s) {                                                     \
     switch (epi) {                                                                              \
       case EPI_STORE:                                                                           \
         return out_t == DT_BF16                                                                 \
-                   ? run<BM, BN, AT, BT, EPI_STORE, bf16_t>(M, N, K, A, lda, B, ldb, e, 1, s)   \
-                   : run<BM, BN, AT, BT, EPI_STORE, float>(M, N, K, A, lda, B, ldb, e, 1, s);   \
+                   ? run<256, 256, 2, 4, LA, LB, EPI_STORE, bf16_t>(M, N, K, A, lda, B, ldb, e, 1, s) \
+                   : run<256, 256, 2, 4, LA, LB, EPI_STORE, float>(M, N, K, A, lda, B, ldb, e, 1, s); \
       case EPI_BIAS_GELU:                                                                       \
-        return run<BM, BN, AT, BT, EPI_BIAS_GELU, bf16_t>(M, N, K, A, lda, B, ldb, e, 1, s);    \
+        return run<256, 256, 2, 4, LA, LB, EPI_BIAS_GELU, bf16_t>(M, N, K, A, lda, B, ldb, e, 1, s); \
       case EPI_RESID:                                                                           \
-        return run<BM, BN, AT, BT, EPI_RESID, float>(M, N, K, A, lda, B, ldb, e, 1, s);         \
+        return run<256, 256, 2, 4, LA, LB, EPI_RESID, float>(M, N, K, A, lda, B, ldb, e, 1, s); \
       case EPI_ACCUM:                                                                           \
-        return run<BM, BN, AT, BT, EPI_ACCUM, float>(M, N, K, A, lda, B, ldb, e, 1, s);         \
+        return run<256, 256, 2, 4, LA, LB, EPI_ACCUM, float>(M, N, K, A, lda, B, ldb, e, 1, s); \
       case EPI_ATOMIC:                                                                          \
-        return run<BM, BN, AT, BT, EPI_ATOMIC, float>(M, N, K, A, lda, B, ldb, e, sk, s);       \
+        return run<256, 256, 2, 4, LA, LB, EPI_ATOMIC, float>(M, N, K, A, lda, B, ldb, e, sk, s); \
       case EPI_GELU_BWD:                                                                        \
-        return run<BM, BN, AT, BT, EPI_GELU_BWD, bf16_t>(M, N, K, A, lda, B, ldb, e, 1, s);     \
+        return run<256, 256, 2, 4, LA, LB, EPI_GELU_BWD, bf16_t>(M, N, K, A, lda, B, ldb, e, 1, s); \
       case EPI_PARTIAL:                                                                         \
-        return run<BM, BN, AT, BT, EPI_PARTIAL, float>(M, N, K, A, lda, B, ldb, e, sk, s);      \
+        return run<256, 256, 2, 4, LA, LB, EPI_PARTIAL, float>(M, N, K, A, lda, B, ldb, e, sk, s); \
     }                                                                                           \
     return hipErrorInvalidValue;                                                                \
   }                                                                                             \
@@ -260,26 +341,17 @@ hipError_t dispatch(int M, int N, int K, const bf16_t* A, long lda, const bf16_t
   hipError_t dispatch<AT, BT>(int M, int N, int K, const bf16_t* A, long lda, const bf16_t* B,  \
                               long ldb, int epi, DType out_t, const EpiArgs& e, int split_k,    \
                               hipStream_t s) {                                                  \
-    long t256 = (long)((M + 255) / 256) * ((N + 255) / 256);                                    \
-    long t256x128 = (long)((M + 255) / 256) * ((N + 127) / 128);                                \
-    long t128 = (long)((M + 127) / 128) * ((N + 127) / 128);                                    \
-    int bm = 128, bn = 128;                                                                     \
-    long tiles = t128;                                                                          \
-    if (t256 >= 384 || (epi == EPI_ATOMIC && t256 >= 16) || epi == EPI_PARTIAL) {               \
-      bm = bn = 256; tiles = t256;                                                              \
-    } else if (t256x128 >= 256) {                                                               \
-      bm = 256; tiles = t256x128;                                                               \
-    }                                                                                           \
     if (epi == EPI_ATOMIC && split_k == 0) {                                                    \
+      long tiles = (long)((M + 255) / 256) * ((N + 255) / 256);                                 \
       int nkt = (K + BK - 1) / BK;                                                              \
       long want = (512 + tiles - 1) / tiles;                                                    \
       long cap = nkt / 4 > 0 ? nkt / 4 : 1;                                                     \
       split_k = (int)(want < cap ? want : cap);                                                 \
     }                                                                                           \
-    if (bm == 256 && bn == 256)                                                                 \
-      return by_epi<256, 256>(M, N, K, A, lda, B, ldb, epi, out_t, e, split_k, s);              \
-    if (bm == 256)                                                                              \
-      return by_epi<256, 128>(M, N, K, A, lda, B, ldb, epi, out_t, e, split_k, s);              \
-    return by_epi<128, 128>(M, N, K, A, lda, B, ldb, epi, out_t, e, split_k, s);                \
+    /* k-contiguous operands go straight to LDS when whole 64-deep tiles exist */              \
+    const bool direct = K % 64 == 0;                                                            \
+    constexpr int TA = AT ? 1 : 0, TB = BT ? 1 : 0;                                             \
+    if (direct) return by_epi<AT ? 1 : 2, BT ? 1 : 2>(M, N, K, A, lda, B, ldb, epi, out_t, e, split_k, s); \
+    return by_epi<TA, TB>(M, N, K, A, lda, B, ldb, epi, out_t, e, split_k, s);                 \
   }                                                                                             \
   }

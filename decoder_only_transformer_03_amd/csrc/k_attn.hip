@@ -165,41 +165,57 @@ __device__ __forceinline__ int swz(int row, int c) { return c ^ ((row ^ (row >> 
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
 
-// 64 rows x 64 columns (16-byte chunks swizzled by row), rows row0.. of X.
-__device__ __forceinline__ void stage_rows(bf16_t* s, const bf16_t* __restrict__ X, long ld,
-                                           int row0, int nrows, int tid) {
-  const int c = tid & 7;
+// Staging of 64-row blocks of q/k/v/dy into LDS, split into a global load
+// into registers (issued one block ahead) and the LDS write.
+// Rows layout: 64 rows x 64 columns, 16-byte chunks swizzled by row.
+struct RowsStage {
+  uint4 v[2];
+  __device__ __forceinline__ void load(const bf16_t* __restrict__ X, long ld, int row0, int nrows,
+                                       int tid) {
+    const int c = tid & 7;
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    int r = (tid >> 3) + 32 * i;
-    int row = row0 + r;
-    uint4 v = row < nrows ? *reinterpret_cast<const uint4*>(X + (long)row * ld + c * 8)
-                          : make_uint4(0, 0, 0, 0);
-    *reinterpret_cast<uint4*>(s + r * 64 + swz(r, c) * 8) = v;
+    for (int i = 0; i < 2; ++i) {
+      int row = row0 + (tid >> 3) + 32 * i;
+      v[i] = row < nrows ? *reinterpret_cast<const uint4*>(X + (long)row * ld + c * 8)
+                         : make_uint4(0, 0, 0, 0);
+    }
   }
-}
+  __device__ __forceinline__ void store(bf16_t* s, int tid) const {
+    const int c = tid & 7;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      int r = (tid >> 3) + 32 * i;
+      *reinterpret_cast<uint4*>(s + r * 64 + swz(r, c) * 8) = v[i];
+    }
+  }
+};
 
-// Transposed: s[d][r] = X[row0 + r][d] for d, r < 64 (row stride ATS).
-__device__ __forceinline__ void stage_cols(bf16_t* s, const bf16_t* __restrict__ X, long ld,
-                                           int row0, int nrows, int tid) {
-  const int dp = tid & 31, kg = tid >> 5;
+// Transposed layout: s[d][r] = X[row0 + r][d] for d, r < 64 (row stride ATS).
+struct ColsStage {
   uint32_t u[8];
+  __device__ __forceinline__ void load(const bf16_t* __restrict__ X, long ld, int row0, int nrows,
+                                       int tid) {
+    const int dp = tid & 31, kg = tid >> 5;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    int row = row0 + kg * 8 + j;
-    u[j] = row < nrows ? *reinterpret_cast<const uint32_t*>(X + (long)row * ld + 2 * dp) : 0u;
+    for (int j = 0; j < 8; ++j) {
+      int row = row0 + kg * 8 + j;
+      u[j] = row < nrows ? *reinterpret_cast<const uint32_t*>(X + (long)row * ld + 2 * dp) : 0u;
+    }
   }
-  bf16_t* d0 = s + (2 * dp) * ATS + kg * 8;
-  bf16_t* d1 = d0 + ATS;
-  *reinterpret_cast<uint2*>(d0) =
-      make_uint2(__byte_perm(u[0], u[1], 0x5410u), __byte_perm(u[2], u[3], 0x5410u));
-  *reinterpret_cast<uint2*>(d0 + 4) =
-      make_uint2(__byte_perm(u[4], u[5], 0x5410u), __byte_perm(u[6], u[7], 0x5410u));
-  *reinterpret_cast<uint2*>(d1) =
-      make_uint2(__byte_perm(u[0], u[1], 0x7632u), __byte_perm(u[2], u[3], 0x7632u));
-  *reinterpret_cast<uint2*>(d1 + 4) =
-      make_uint2(__byte_perm(u[4], u[5], 0x7632u), __byte_perm(u[6], u[7], 0x7632u));
-}
+  __device__ __forceinline__ void store(bf16_t* s, int tid) const {
+    const int dp = tid & 31, kg = tid >> 5;
+    bf16_t* d0 = s + (2 * dp) * ATS + kg * 8;
+    bf16_t* d1 = d0 + ATS;
+    *reinterpret_cast<uint2*>(d0) =
+        make_uint2(__byte_perm(u[0], u[1], 0x5410u), __byte_perm(u[2], u[3], 0x5410u));
+    *reinterpret_cast<uint2*>(d0 + 4) =
+        make_uint2(__byte_perm(u[4], u[5], 0x5410u), __byte_perm(u[6], u[7], 0x5410u));
+    *reinterpret_cast<uint2*>(d1) =
+        make_uint2(__byte_perm(u[0], u[1], 0x7632u), __byte_perm(u[2], u[3], 0x7632u));
+    *reinterpret_cast<uint2*>(d1 + 4) =
+        make_uint2(__byte_perm(u[4], u[5], 0x7632u), __byte_perm(u[6], u[7], 0x7632u));
+  }
+};
 
 __device__ __forceinline__ bf16x8_t frag_rows(const bf16_t* s, int row, int c) {
   return *reinterpret_cast<const bf16x8_t*>(s + row * 64 + swz(row, c) * 8);
@@ -245,13 +261,15 @@ __device__ __forceinline__ float dot8(uint4 a, uint4 b) {
 __global__ __launch_bounds__(256) void attn_fwd_mfma(const bf16_t* __restrict__ qkv,
                                                      bf16_t* __restrict__ y,
                                                      float* __restrict__ lse, int Tn, int H, int C) {
-  __shared__ __attribute__((aligned(16))) bf16_t sK[64 * 64];
-  __shared__ __attribute__((aligned(16))) bf16_t sVt[64 * ATS];
+  __shared__ __attribute__((aligned(16))) bf16_t sK[2][64 * 64];
+  __shared__ __attribute__((aligned(16))) bf16_t sVt[2][64 * ATS];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, half = lane >> 5, l32 = lane & 31;
   const int qb = gridDim.x - 1 - blockIdx.x;  // longest rows first
   const int bh = blockIdx.y, b = bh / H, h = bh % H;
   const long ld = 3L * C;
   const bf16_t* base = qkv + (long)b * Tn * ld;
+  const bf16_t* kbase = base + C + h * 64;
+  const bf16_t* vbase = base + 2 * C + h * 64;
   const int q0w = qb * 128 + w * 32;
   const int myq = q0w + l32;
   const float sl2 = 0.125f * LOG2E_F;
@@ -265,26 +283,43 @@ __global__ __launch_bounds__(256) void attn_fwd_mfma(const bf16_t* __restrict__ 
   f32x16_t o0 = zero16(), o1 = zero16();
   float m2 = NEG_INF, ls = 0.f;
   const int kend = Tn < qb * 128 + 128 ? Tn : qb * 128 + 128;
-  for (int k0 = 0; k0 < kend; k0 += 64) {
-    __syncthreads();
-    stage_rows(sK, base + C + h * 64, ld, k0, Tn, tid);
-    stage_cols(sVt, base + 2 * C + h * 64, ld, k0, Tn, tid);
-    __syncthreads();
+  RowsStage gk;
+  ColsStage gv;
+  gk.load(kbase, ld, 0, Tn, tid);
+  gv.load(vbase, ld, 0, Tn, tid);
+  gk.store(sK[0], tid);
+  gv.store(sVt[0], tid);
+  __syncthreads();
+  int cur = 0;
+  for (int k0 = 0; k0 < kend; k0 += 64, cur ^= 1) {
+    const bool more = k0 + 64 < kend;
+    if (more) {
+      gk.load(kbase, ld, k0 + 64, Tn, tid);
+      gv.load(vbase, ld, k0 + 64, Tn, tid);
+    }
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       const int kb = k0 + 32 * s;
       if (kb > q0w + 31 || kb >= Tn) break;
       f32x16_t st = zero16();
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) st = mfma(frag_rows(sK, 32 * s + l32, kk * 2 + half), qf[kk], st);
+      for (int kk = 0; kk < 4; ++kk)
+        st = mfma(frag_rows(sK[cur], 32 * s + l32, kk * 2 + half), qf[kk], st);
       float mx = NEG_INF;
+      if (kb + 31 > q0w || kb + 31 >= Tn) {  // diagonal or ragged block: mask
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        int key = kb + 8 * (r >> 2) + 4 * half + (r & 3);
-        float x = st[r] * sl2;
-        if (key > myq || key >= Tn) x = NEG_INF;
-        st[r] = x;
-        mx = fmaxf(mx, x);
+        for (int r = 0; r < 16; ++r) {
+          int key = kb + 8 * (r >> 2) + 4 * half + (r & 3);
+          float x = (key > myq || key >= Tn) ? NEG_INF : st[r] * sl2;
+          st[r] = x;
+          mx = fmaxf(mx, x);
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          st[r] *= sl2;
+          mx = fmaxf(mx, st[r]);
+        }
       }
       mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
       const float mn = fmaxf(m2, mx);
@@ -302,10 +337,15 @@ __global__ __launch_bounds__(256) void attn_fwd_mfma(const bf16_t* __restrict__ 
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         bf16x8_t pb = pack_acc(st, u);
-        o0 = mfma(frag_cols(sVt, l32, 32 * s + 16 * u, half), pb, o0);
-        o1 = mfma(frag_cols(sVt, 32 + l32, 32 * s + 16 * u, half), pb, o1);
+        o0 = mfma(frag_cols(sVt[cur], l32, 32 * s + 16 * u, half), pb, o0);
+        o1 = mfma(frag_cols(sVt[cur], 32 + l32, 32 * s + 16 * u, half), pb, o1);
       }
     }
+    if (more) {
+      gk.store(sK[cur ^ 1], tid);
+      gv.store(sVt[cur ^ 1], tid);
+    }
+    __syncthreads();
   }
   const float lt = ls + __shfl_xor(ls, 32, 64);
   const float inv = 1.0f / lt;
@@ -330,9 +370,9 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_mfma(const bf16_t* __restrict
                                                         bf16_t* __restrict__ dqkv,
                                                         float* __restrict__ dbuf, int Tn, int H,
                                                         int C) {
-  __shared__ __attribute__((aligned(16))) bf16_t sK[64 * 64];
-  __shared__ __attribute__((aligned(16))) bf16_t sV[64 * 64];
-  __shared__ __attribute__((aligned(16))) bf16_t sKt[64 * ATS];
+  __shared__ __attribute__((aligned(16))) bf16_t sK[2][64 * 64];
+  __shared__ __attribute__((aligned(16))) bf16_t sV[2][64 * 64];
+  __shared__ __attribute__((aligned(16))) bf16_t sKt[2][64 * ATS];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, half = lane >> 5, l32 = lane & 31;
   const int qb = gridDim.x - 1 - blockIdx.x;
   const int bh = blockIdx.y, b = bh / H, h = bh % H;
@@ -364,12 +404,25 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_mfma(const bf16_t* __restrict
 
   f32x16_t dq0 = zero16(), dq1 = zero16();
   const int kend = Tn < qb * 128 + 128 ? Tn : qb * 128 + 128;
-  for (int k0 = 0; k0 < kend; k0 += 64) {
-    __syncthreads();
-    stage_rows(sK, base + C + h * 64, ld, k0, Tn, tid);
-    stage_rows(sV, base + 2 * C + h * 64, ld, k0, Tn, tid);
-    stage_cols(sKt, base + C + h * 64, ld, k0, Tn, tid);
-    __syncthreads();
+  const bf16_t* kbase = base + C + h * 64;
+  const bf16_t* vbase = base + 2 * C + h * 64;
+  RowsStage gk, gv;
+  ColsStage gkt;
+  gk.load(kbase, ld, 0, Tn, tid);
+  gv.load(vbase, ld, 0, Tn, tid);
+  gkt.load(kbase, ld, 0, Tn, tid);
+  gk.store(sK[0], tid);
+  gv.store(sV[0], tid);
+  gkt.store(sKt[0], tid);
+  __syncthreads();
+  int cur = 0;
+  for (int k0 = 0; k0 < kend; k0 += 64, cur ^= 1) {
+    const bool more = k0 + 64 < kend;
+    if (more) {
+      gk.load(kbase, ld, k0 + 64, Tn, tid);
+      gv.load(vbase, ld, k0 + 64, Tn, tid);
+      gkt.load(kbase, ld, k0 + 64, Tn, tid);
+    }
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       const int kb = k0 + 32 * s;
@@ -377,22 +430,33 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_mfma(const bf16_t* __restrict
       f32x16_t st = zero16(), dp = zero16();
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
-        st = mfma(frag_rows(sK, 32 * s + l32, kk * 2 + half), qf[kk], st);
-        dp = mfma(frag_rows(sV, 32 * s + l32, kk * 2 + half), gf[kk], dp);
+        st = mfma(frag_rows(sK[cur], 32 * s + l32, kk * 2 + half), qf[kk], st);
+        dp = mfma(frag_rows(sV[cur], 32 * s + l32, kk * 2 + half), gf[kk], dp);
       }
+      if (kb + 31 > q0w || kb + 31 >= Tn) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        int key = kb + 8 * (r >> 2) + 4 * half + (r & 3);
-        float p = (key <= myq && key < Tn) ? exp2f(st[r] * sl2 - lse2) : 0.f;
-        st[r] = p * (dp[r] - dd);
+        for (int r = 0; r < 16; ++r) {
+          int key = kb + 8 * (r >> 2) + 4 * half + (r & 3);
+          float p = (key <= myq && key < Tn) ? exp2f(st[r] * sl2 - lse2) : 0.f;
+          st[r] = p * (dp[r] - dd);
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) st[r] = exp2f(st[r] * sl2 - lse2) * (dp[r] - dd);
       }
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         bf16x8_t pb = pack_acc(st, u);
-        dq0 = mfma(frag_cols(sKt, l32, 32 * s + 16 * u, half), pb, dq0);
-        dq1 = mfma(frag_cols(sKt, 32 + l32, 32 * s + 16 * u, half), pb, dq1);
+        dq0 = mfma(frag_cols(sKt[cur], l32, 32 * s + 16 * u, half), pb, dq0);
+        dq1 = mfma(frag_cols(sKt[cur], 32 + l32, 32 * s + 16 * u, half), pb, dq1);
       }
     }
+    if (more) {
+      gk.store(sK[cur ^ 1], tid);
+      gv.store(sV[cur ^ 1], tid);
+      gkt.store(sKt[cur ^ 1], tid);
+    }
+    __syncthreads();
   }
   if (myq < Tn) {
     bf16_t* o = dqkv + ((long)b * Tn + myq) * ld + h * 64;
@@ -415,11 +479,11 @@ __global__ __launch_bounds__(256) void attn_bwd_dkv_mfma(const bf16_t* __restric
                                                          const float* __restrict__ dbuf,
                                                          bf16_t* __restrict__ dqkv, int Tn, int H,
                                                          int C) {
-  __shared__ __attribute__((aligned(16))) bf16_t sQ[64 * 64];
-  __shared__ __attribute__((aligned(16))) bf16_t sG[64 * 64];
-  __shared__ __attribute__((aligned(16))) bf16_t sQt[64 * ATS];
-  __shared__ __attribute__((aligned(16))) bf16_t sGt[64 * ATS];
-  __shared__ float sL[64], sD[64];
+  __shared__ __attribute__((aligned(16))) bf16_t sQ[2][64 * 64];
+  __shared__ __attribute__((aligned(16))) bf16_t sG[2][64 * 64];
+  __shared__ __attribute__((aligned(16))) bf16_t sQt[2][64 * ATS];
+  __shared__ __attribute__((aligned(16))) bf16_t sGt[2][64 * ATS];
+  __shared__ float sL[2][64], sD[2][64];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, half = lane >> 5, l32 = lane & 31;
   const int kbk = blockIdx.x;  // key block 0 has the most queries: dispatched first
   const int bh = blockIdx.y, b = bh / H, h = bh % H;
@@ -443,18 +507,44 @@ __global__ __launch_bounds__(256) void attn_bwd_dkv_mfma(const bf16_t* __restric
     vf[kk] = as_bf16x8(v);
   }
   f32x16_t dv0 = zero16(), dv1 = zero16(), dk0 = zero16(), dk1 = zero16();
-  for (int q0 = kbk * 128; q0 < Tn; q0 += 64) {
-    __syncthreads();
-    stage_rows(sQ, base + h * 64, ld, q0, Tn, tid);
-    stage_cols(sQt, base + h * 64, ld, q0, Tn, tid);
-    stage_rows(sG, dyb + h * 64, C, q0, Tn, tid);
-    stage_cols(sGt, dyb + h * 64, C, q0, Tn, tid);
+  const bf16_t* qbase = base + h * 64;
+  const bf16_t* gbase = dyb + h * 64;
+  const float* lrow = lse + (long)bh * Tn;
+  const float* drow = dbuf + (long)bh * Tn;
+  RowsStage gq, gg;
+  ColsStage gqt, ggt;
+  float ll = 0.f, dl = 0.f;
+  auto load_all = [&](int q0) {
+    gq.load(qbase, ld, q0, Tn, tid);
+    gqt.load(qbase, ld, q0, Tn, tid);
+    gg.load(gbase, C, q0, Tn, tid);
+    ggt.load(gbase, C, q0, Tn, tid);
     if (tid < 64) {
       int q = q0 + tid;
-      sL[tid] = q < Tn ? lse[(long)bh * Tn + q] * LOG2E_F : 0.f;
-      sD[tid] = q < Tn ? dbuf[(long)bh * Tn + q] : 0.f;
+      ll = q < Tn ? lrow[q] * LOG2E_F : 0.f;
+      dl = q < Tn ? drow[q] : 0.f;
     }
-    __syncthreads();
+  };
+  auto store_all = [&](int buf) {
+    gq.store(sQ[buf], tid);
+    gqt.store(sQt[buf], tid);
+    gg.store(sG[buf], tid);
+    ggt.store(sGt[buf], tid);
+    if (tid < 64) {
+      sL[buf][tid] = ll;
+      sD[buf][tid] = dl;
+    }
+  };
+  const int qstart = kbk * 128;
+  if (qstart < Tn) {
+    load_all(qstart);
+    store_all(0);
+  }
+  __syncthreads();
+  int cur = 0;
+  for (int q0 = qstart; q0 < Tn; q0 += 64, cur ^= 1) {
+    const bool more = q0 + 64 < Tn;
+    if (more) load_all(q0 + 64);
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       const int qs = q0 + 32 * s;
@@ -462,27 +552,31 @@ __global__ __launch_bounds__(256) void attn_bwd_dkv_mfma(const bf16_t* __restric
       f32x16_t st = zero16(), dp = zero16();
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk) {
-        st = mfma(frag_rows(sQ, 32 * s + l32, kk * 2 + half), kf[kk], st);
-        dp = mfma(frag_rows(sG, 32 * s + l32, kk * 2 + half), vf[kk], dp);
+        st = mfma(frag_rows(sQ[cur], 32 * s + l32, kk * 2 + half), kf[kk], st);
+        dp = mfma(frag_rows(sG[cur], 32 * s + l32, kk * 2 + half), vf[kk], dp);
       }
       f32x16_t pv;
+      const bool edge = qs < kw0 + 31 || qs + 31 >= Tn;  // some (q, key) pair masked
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         int qi = 32 * s + 8 * (r >> 2) + 4 * half + (r & 3);
         int q = q0 + qi;
-        float p = (mykey <= q && q < Tn) ? exp2f(st[r] * sl2 - sL[qi]) : 0.f;
+        float p = exp2f(st[r] * sl2 - sL[cur][qi]);
+        if (edge && !(mykey <= q && q < Tn)) p = 0.f;
         pv[r] = p;
-        st[r] = p * (dp[r] - sD[qi]);
+        st[r] = p * (dp[r] - sD[cur][qi]);
       }
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         bf16x8_t pp = pack_acc(pv, u), ps = pack_acc(st, u);
-        dv0 = mfma(frag_cols(sGt, l32, 32 * s + 16 * u, half), pp, dv0);
-        dv1 = mfma(frag_cols(sGt, 32 + l32, 32 * s + 16 * u, half), pp, dv1);
-        dk0 = mfma(frag_cols(sQt, l32, 32 * s + 16 * u, half), ps, dk0);
-        dk1 = mfma(frag_cols(sQt, 32 + l32, 32 * s + 16 * u, half), ps, dk1);
+        dv0 = mfma(frag_cols(sGt[cur], l32, 32 * s + 16 * u, half), pp, dv0);
+        dv1 = mfma(frag_cols(sGt[cur], 32 + l32, 32 * s + 16 * u, half), pp, dv1);
+        dk0 = mfma(frag_cols(sQt[cur], l32, 32 * s + 16 * u, half), ps, dk0);
+        dk1 = mfma(frag_cols(sQt[cur], 32 + l32, 32 * s + 16 * u, half), ps, dk1);
       }
     }
+    if (more) store_all(cur ^ 1);
+    __syncthreads();
   }
   if (mykey < Tn) {
     bf16_t* o = dqkv + ((long)b * Tn + mykey) * ld + h * 64;

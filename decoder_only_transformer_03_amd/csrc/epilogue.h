@@ -10,7 +10,7 @@ enum EpiKind : int {
   EPI_ACCUM = 3,     // out[m][n] += alpha*c            one writer per element (out: fp32)
   EPI_ATOMIC = 4,    // atomically out[m][n] += alpha*c  split-K               (out: fp32)
   EPI_GELU_BWD = 5,  // out[m][n] = alpha*c * gelu'(aux[m][n])                 (out, aux: TO)
-  EPI_PARTIAL = 6,   // split-K slice z = blockIdx.y: out[z*split_stride + m*ldo + n] = alpha*c (fp32)
+  EPI_PARTIAL = 6,   // split-K slice z: out[z*split_stride + m*ldo + n] = alpha*c  (fp32)
 };
 
 struct EpiArgs {
@@ -59,7 +59,7 @@ __device__ __forceinline__ void epi_load_bias(const EpiArgs& e, int n, float b[4
 // Phase 2: combine accumulator c, input `in` and bias `b`, and store.
 template <int EPI, typename TO>
 __device__ __forceinline__ void epi_store4(const EpiArgs& e, long m, int n, const float c[4],
-                                           const float in[4], const float b[4]) {
+                                           const float in[4], const float b[4], int split) {
   float r[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) r[j] = e.alpha * c[j];
@@ -88,7 +88,7 @@ __device__ __forceinline__ void epi_store4(const EpiArgs& e, long m, int n, cons
 #pragma unroll
     for (int j = 0; j < 4; ++j) atomicAdd(o + j, r[j]);
   } else if constexpr (EPI == EPI_PARTIAL) {
-    st4(reinterpret_cast<float*>(e.out) + blockIdx.y * e.split_stride + m * e.ldo + n, r);
+    st4(reinterpret_cast<float*>(e.out) + split * e.split_stride + m * e.ldo + n, r);
   } else if constexpr (EPI == EPI_GELU_BWD) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) r[j] *= gelu_tanh_grad_f(in[j]);
@@ -96,11 +96,12 @@ __device__ __forceinline__ void epi_store4(const EpiArgs& e, long m, int n, cons
   }
 }
 
-// Both phases for one group of four columns.
+// Both phases for one group of four columns (split: the split-K slice).
 template <int EPI, typename TO>
-__device__ __forceinline__ void epi_apply4(const EpiArgs& e, long m, int n, const float c[4]) {
+__device__ __forceinline__ void epi_apply4(const EpiArgs& e, long m, int n, const float c[4],
+                                           int split) {
   float in[4] = {0.f, 0.f, 0.f, 0.f}, b[4];
   epi_load4<EPI, TO>(e, m, n, in);
   epi_load_bias(e, n, b);
-  epi_store4<EPI, TO>(e, m, n, c, in, b);
+  epi_store4<EPI, TO>(e, m, n, c, in, b, split);
 }

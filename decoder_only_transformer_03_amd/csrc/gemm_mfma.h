@@ -145,7 +145,123 @@ template <int R, int NT> struct Loader<R, 0, NT> : LoaderK<R, NT> {};
 template <int R, int NT> struct Loader<R, 1, NT> : LoaderT<R, NT> {};
 template <int R, int NT> struct Loader<R, 2, NT> : LoaderD<R, NT> {};
 
-// WM x WN wavefronts; each owns a (BM/WM) x (BN/WN) sub-tile.
+// Epilogue of one output tile, staged through LDS so that global memory sees
+// whole row segments.  acc[sn][sm][4i + j] is C[m][n] with m = sm*32 +
+// lane%32 and n = sn*32 + 8i + 4(lane/32) + j inside the wavefront's
+// (BM/WM) x (BN/WN) sub-tile.  Each wavefront owns 8 KB of scratch LDS and
+// moves its sub-tile in rounds of 32 rows: (1) lanes write alpha * their
+// accumulator fragments, fp32, into a row-major round buffer (16-byte chunks
+// XOR-swizzled by row, so both the fragment writes and the row reads are
+// bank-conflict free); (2) lanes read back 8 consecutive columns of one row
+// each -- 8 lanes cover the 64 columns of a row -- apply the elementwise
+// epilogue and store 16-byte pieces, so one store instruction writes 8
+// complete row segments.
+template <int BM, int BN, int WM, int WN, int EPI, typename TO, int SN, int SM>
+__device__ __forceinline__ void tile_epilogue(const EpiArgs& e, const f32x16_t (&acc)[SN][SM],
+                                              long m0, long n0, int split, int M, int N, int lane,
+                                              int wm, int wn, bf16_t* scratch) {
+  constexpr int WTM = BM / WM, WTN = BN / WN;
+  static_assert(WTN == 64, "staged epilogue assumes 64-column wavefront sub-tiles");
+  static_assert((BM + BN) * BK >= WM * WN * 4096, "epilogue scratch must fit one LDS stage");
+  float* sf = reinterpret_cast<float*>(scratch);  // [32 rows][64 fp32]
+  const long mw = m0 + wm * WTM;                  // first row of the sub-tile
+  const long nl = n0 + wn * WTN + (lane & 7) * 8; // this lane's 8 columns in the read phase
+  const bool ncol = nl < N;
+  float bias8[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) bias8[j] = 0.f;
+  if constexpr (epi_bias(EPI)) {
+    if (e.bias && ncol) {
+      ld4(e.bias + nl, bias8);
+      ld4(e.bias + nl + 4, bias8 + 4);
+    }
+  }
+#pragma unroll
+  for (int sm = 0; sm < SM; ++sm) {
+    // (1) fragments -> round buffer (row = lane%32, one 16-byte chunk each)
+    {
+      const int row = lane & 31;
+#pragma unroll
+      for (int sn = 0; sn < SN; ++sn)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int c = (sn * 32 + 8 * i + 4 * (lane >> 5)) >> 2;
+          const int pc = c ^ (row & 7);
+          *reinterpret_cast<float4*>(sf + row * 64 + pc * 4) =
+              make_float4(e.alpha * acc[sn][sm][4 * i + 0], e.alpha * acc[sn][sm][4 * i + 1],
+                          e.alpha * acc[sn][sm][4 * i + 2], e.alpha * acc[sn][sm][4 * i + 3]);
+        }
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    // (2) rows of the round -> global, 8 lanes per row
+#pragma unroll
+    for (int r8 = 0; r8 < 4; ++r8) {
+      const int row = r8 * 8 + (lane >> 3);
+      const long m = mw + sm * 32 + row;
+      const int c0 = (2 * (lane & 7)) ^ (row & 7), c1 = (2 * (lane & 7) + 1) ^ (row & 7);
+      const float4 a = *reinterpret_cast<const float4*>(sf + row * 64 + c0 * 4);
+      const float4 b = *reinterpret_cast<const float4*>(sf + row * 64 + c1 * 4);
+      float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+      if (m < M && ncol) {
+        if constexpr (epi_bias(EPI)) {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) v[j] += bias8[j];
+        }
+        if constexpr (EPI == EPI_STORE) {
+          st4(reinterpret_cast<TO*>(e.out) + m * e.ldo + nl, v);
+          st4(reinterpret_cast<TO*>(e.out) + m * e.ldo + nl + 4, v + 4);
+        } else if constexpr (EPI == EPI_BIAS_GELU) {
+          st4(reinterpret_cast<TO*>(e.out) + m * e.ldo + nl, v);
+          st4(reinterpret_cast<TO*>(e.out) + m * e.ldo + nl + 4, v + 4);
+#pragma unroll
+          for (int j = 0; j < 8; ++j) v[j] = gelu_tanh_f(v[j]);
+          st4(reinterpret_cast<TO*>(e.out2) + m * e.ldo + nl, v);
+          st4(reinterpret_cast<TO*>(e.out2) + m * e.ldo + nl + 4, v + 4);
+        } else if constexpr (EPI == EPI_RESID) {
+          float x[8];
+          ld4(e.resid + m * e.ldr + nl, x);
+          ld4(e.resid + m * e.ldr + nl + 4, x + 4);
+#pragma unroll
+          for (int j = 0; j < 8; ++j) v[j] += x[j];
+          st4(reinterpret_cast<float*>(e.out) + m * e.ldo + nl, v);
+          st4(reinterpret_cast<float*>(e.out) + m * e.ldo + nl + 4, v + 4);
+        } else if constexpr (EPI == EPI_ACCUM) {
+          float* o = reinterpret_cast<float*>(e.out) + m * e.ldo + nl;
+          float x[8];
+          ld4(o, x);
+          ld4(o + 4, x + 4);
+#pragma unroll
+          for (int j = 0; j < 8; ++j) v[j] += x[j];
+          st4(o, v);
+          st4(o + 4, v + 4);
+        } else if constexpr (EPI == EPI_ATOMIC) {
+          float* o = reinterpret_cast<float*>(e.out) + m * e.ldo + nl;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) atomicAdd(o + j, v[j]);
+        } else if constexpr (EPI == EPI_PARTIAL) {
+          float* o = reinterpret_cast<float*>(e.out) + split * e.split_stride + m * e.ldo + nl;
+          st4(o, v);
+          st4(o + 4, v + 4);
+        } else if constexpr (EPI == EPI_GELU_BWD) {
+          float hh[8];
+          ld4(reinterpret_cast<const TO*>(e.aux) + m * e.ldx + nl, hh);
+          ld4(reinterpret_cast<const TO*>(e.aux) + m * e.ldx + nl + 4, hh + 4);
+#pragma unroll
+          for (int j = 0; j < 8; ++j) v[j] *= gelu_tanh_grad_f(hh[j]);
+          st4(reinterpret_cast<TO*>(e.out) + m * e.ldo + nl, v);
+          st4(reinterpret_cast<TO*>(e.out) + m * e.ldo + nl + 4, v + 4);
+        }
+      }
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// WM x WN wavefronts; each owns a (BM/WM) x (BN/WN) sub-tile.  Persistent:
+// the grid is about one workgroup per CU; each walks the work items
+// (tile, k-slice) blockIdx.x, +gridDim.x, ...
 template <int BM, int BN, int WM, int WN, int LA, int LB, int EPI, typename TO>
 __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(int M, int N, int K,
                                                       const bf16_t* __restrict__ A, long lda,
@@ -160,28 +276,34 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(int M, int N, int
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave % WM, wn = wave / WM;
 
-  // Tile order.  Workgroups are dispatched round-robin over the 8 XCDs; give
-  // each XCD a contiguous range of tile ids so that tiles sharing operand
-  // rows share that XCD's L2, then walk the range in groups of 8 M-tiles.
+  // Tile order: item i runs on XCD i % 8 (the grid is a multiple of 8), so
+  // each XCD is given a contiguous range of tile ids -- tiles sharing operand
+  // rows share that XCD's L2 -- walked in groups of 8 M-tiles.
   const int ntiles = tiles_m * tiles_n;
-  int pid = blockIdx.x;
-  {
-    int q = ntiles >> 3, r = ntiles & 7, x = pid & 7, loc = pid >> 3;
-    pid = x * q + (x < r ? x : r) + loc;
-  }
-  constexpr int GROUP = 8;
-  const int per_group = GROUP * tiles_n;
-  const int first_m = (pid / per_group) * GROUP;
-  const int gsize = (tiles_m - first_m) < GROUP ? (tiles_m - first_m) : GROUP;
-  const int tm = first_m + (pid % per_group) % gsize;
-  const int tn = (pid % per_group) / gsize;
-  const long m0 = (long)tm * BM;
-  const long n0 = (long)tn * BN;
-
   const int nkt = (K + BK - 1) / BK;
-  const int kt0 = blockIdx.y * kt_per_split;
-  const int kt1 = (kt0 + kt_per_split) < nkt ? (kt0 + kt_per_split) : nkt;
-  if (kt0 >= kt1) return;
+  const int nsplit = (nkt + kt_per_split - 1) / kt_per_split;
+  const long nitems = (long)ntiles * nsplit;
+  long m0 = 0, n0 = 0;
+  int kt0 = 0, kt1 = 0, split = 0;
+  auto decode = [&](long it) {
+    split = (int)(it / ntiles);
+    int pid = (int)(it - (long)split * ntiles);
+    {
+      int q = ntiles >> 3, r = ntiles & 7, x = pid & 7, loc = pid >> 3;
+      pid = x * q + (x < r ? x : r) + loc;
+    }
+    constexpr int GROUP = 8;
+    const int per_group = GROUP * tiles_n;
+    const int first_m = (pid / per_group) * GROUP;
+    const int gsize = (tiles_m - first_m) < GROUP ? (tiles_m - first_m) : GROUP;
+    m0 = (long)(first_m + (pid % per_group) % gsize) * BM;
+    n0 = (long)((pid % per_group) / gsize) * BN;
+    kt0 = split * kt_per_split;
+    kt1 = (kt0 + kt_per_split) < nkt ? (kt0 + kt_per_split) : nkt;
+  };
+  long item = blockIdx.x;
+  if (item >= nitems) return;
+  decode(item);
 
   f32x16_t acc[SN][SM];
 #pragma unroll
@@ -215,79 +337,83 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(int M, int N, int
     }
   };
 
-  // Software pipeline: the global loads of k-tile t+1 are in flight during
-  // the MFMAs of tile t, and the LDS fragments of substep kk+1 are read while
-  // the MFMAs of substep kk run.
+  // Software pipeline: the loads of the next k-tile -- of this item, or the
+  // first k-tile of the next item -- are in flight during the MFMAs of the
+  // current one, and the LDS fragments of substep kk+1 are read while the
+  // MFMAs of substep kk run.  The epilogue's stores overlap the next item.
   bf16x8_t fa[2][SM], fb[2][SN];
   load_frags(smem[0], smem[0] + BM * BK, 0, fa[0], fb[0]);
-  for (int kt = kt0; kt < kt1; ++kt) {
-    const int cur = (kt - kt0) & 1;
-    const bool more = kt + 1 < kt1;
-    if (more) {
-      la.issue(A, lda, m0, M, (kt + 1) * BK, K, tid, smem[cur ^ 1]);
-      lb.issue(B, ldb, n0, N, (kt + 1) * BK, K, tid, smem[cur ^ 1] + BM * BK);
-    }
-    const bf16_t* sA = smem[cur];
-    const bf16_t* sB = smem[cur] + BM * BK;
-#pragma unroll
-    for (int kk = 0; kk < BK / 16; ++kk) {
-      if (kk + 1 < BK / 16) load_frags(sA, sB, kk + 1, fa[(kk + 1) & 1], fb[(kk + 1) & 1]);
-#pragma unroll
-      for (int sn = 0; sn < SN; ++sn)
-#pragma unroll
-        for (int sm = 0; sm < SM; ++sm)
-          acc[sn][sm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[kk & 1][sn], fa[kk & 1][sm],
-                                                                acc[sn][sm], 0, 0, 0);
-      // keep the two-deep fragment pipeline: nothing moves across substeps
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    if (more) {
-      la.commit(smem[cur ^ 1], tid);
-      lb.commit(smem[cur ^ 1] + BM * BK, tid);
-      if constexpr (LA == 2 || LB == 2) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    }
-    __syncthreads();
-    if (more) load_frags(smem[cur ^ 1], smem[cur ^ 1] + BM * BK, 0, fa[0], fb[0]);
-  }
-
-  // acc[sn][sm][4i + j] is C[m][n] with m = sm*32 + lane%32 and
-  // n = sn*32 + 8i + 4(lane/32) + j inside the wavefront's sub-tile.  Per
-  // n-subtile: all epilogue inputs are loaded first, then combined and stored.
-#pragma unroll
-  for (int sn = 0; sn < SN; ++sn) {
-    float bias[4][4];
-    float in[SM][4][4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const long n = n0 + wn * WTN + sn * 32 + 8 * i + 4 * (lane >> 5);
-      if constexpr (epi_bias(EPI)) {
-        if (n < N) epi_load_bias(e, (int)n, bias[i]);
+  int cur = 0;
+  while (true) {
+    const long em0 = m0, en0 = n0;  // this item's output tile
+    const int ekt1 = kt1, esplit = split;
+    for (int kt = kt0; kt < ekt1; ++kt) {
+      const bool last_k = kt + 1 == ekt1;
+      const bool more = !last_k || item + gridDim.x < nitems;
+      if (more) {
+        if (last_k) decode(item + gridDim.x);
+        const int nk = last_k ? kt0 : kt + 1;
+        la.issue(A, lda, m0, M, nk * BK, K, tid, smem[cur ^ 1]);
+        lb.issue(B, ldb, n0, N, nk * BK, K, tid, smem[cur ^ 1] + BM * BK);
       }
-      if constexpr (epi_reads(EPI)) {
+      const bf16_t* sA = smem[cur];
+      const bf16_t* sB = smem[cur] + BM * BK;
 #pragma unroll
-        for (int sm = 0; sm < SM; ++sm) {
-          const long m = m0 + wm * WTM + sm * 32 + (lane & 31);
-          if (m < M && n < N) epi_load4<EPI, TO>(e, m, (int)n, in[sm][i]);
-        }
+      for (int kk = 0; kk < BK / 16; ++kk) {
+        if (kk + 1 < BK / 16) load_frags(sA, sB, kk + 1, fa[(kk + 1) & 1], fb[(kk + 1) & 1]);
+#pragma unroll
+        for (int sn = 0; sn < SN; ++sn)
+#pragma unroll
+          for (int sm = 0; sm < SM; ++sm)
+            acc[sn][sm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[kk & 1][sn], fa[kk & 1][sm],
+                                                                  acc[sn][sm], 0, 0, 0);
+        // keep the two-deep fragment pipeline: nothing moves across substeps
+        __builtin_amdgcn_sched_barrier(0);
       }
-    }
-#pragma unroll
-    for (int sm = 0; sm < SM; ++sm) {
-      const long m = m0 + wm * WTM + sm * 32 + (lane & 31);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const long n = n0 + wn * WTN + sn * 32 + 8 * i + 4 * (lane >> 5);
-        if (m < M && n < N) {
-          float c4[4] = {acc[sn][sm][4 * i + 0], acc[sn][sm][4 * i + 1], acc[sn][sm][4 * i + 2],
-                         acc[sn][sm][4 * i + 3]};
-          epi_store4<EPI, TO>(e, m, (int)n, c4, in[sm][i], bias[i]);
-        }
+      if (more) {
+        la.commit(smem[cur ^ 1], tid);
+        lb.commit(smem[cur ^ 1] + BM * BK, tid);
+        if constexpr (LA == 2 || LB == 2) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       }
+      __syncthreads();
+      // (the next item's first fragments are read after the epilogue, so
+      // they are not live across it)
+      if (more && !last_k) load_frags(smem[cur ^ 1], smem[cur ^ 1] + BM * BK, 0, fa[0], fb[0]);
+      cur ^= 1;
     }
+    // the stage not holding the next item's first k-tile is free: 8 KB of
+    // epilogue scratch per wavefront
+    tile_epilogue<BM, BN, WM, WN, EPI, TO, SN, SM>(e, acc, em0, en0, esplit, M, N, lane, wm, wn,
+                                                   smem[cur ^ 1] + wave * 4096);
+    item += gridDim.x;
+    if (item >= nitems) break;
+    __syncthreads();  // scratch reads done before the next k-tile lands there
+#pragma unroll
+    for (int a = 0; a < SN; ++a)
+#pragma unroll
+      for (int b = 0; b < SM; ++b)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.f;
+    load_frags(smem[cur], smem[cur] + BM * BK, 0, fa[0], fb[0]);
   }
 }
 
 // Host side: launch one instantiation.
+// Workgroups resident at once: one per CU (the 256 x 256 tile uses 128 KB of
+// LDS); rounded to a multiple of the 8 XCDs.
+inline int persistent_slots() {
+  static int slots = 0;
+  if (!slots) {
+    int dev = 0, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus <= 0)
+      cus = 256;
+    slots = (cus + 7) / 8 * 8;
+  }
+  return slots;
+}
+
 template <int BM, int BN, int WM, int WN, int LA, int LB, int EPI, typename TO>
 hipError_t run(int M, int N, int K, const bf16_t* A, long lda, const bf16_t* B, long ldb,
                const EpiArgs& e, int split_k, hipStream_t s) {
@@ -296,8 +422,9 @@ hipError_t run(int M, int N, int K, const bf16_t* A, long lda, const bf16_t* B, 
   if (split_k < 1) split_k = 1;
   int kps = (nkt + split_k - 1) / split_k;
   int splits = (nkt + kps - 1) / kps;
-  dim3 grid(tiles_m * tiles_n, splits);
-  gemm_kernel<BM, BN, WM, WN, LA, LB, EPI, TO><<<grid, 64 * WM * WN, 0, s>>>(
+  long items = (long)tiles_m * tiles_n * splits;
+  long grid = items < persistent_slots() ? items : persistent_slots();
+  gemm_kernel<BM, BN, WM, WN, LA, LB, EPI, TO><<<(unsigned)grid, 64 * WM * WN, 0, s>>>(
       M, N, K, A, lda, B, ldb, e, tiles_m, tiles_n, kps);
   return hipGetLastError();
 }

@@ -60,7 +60,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(int M, int N, int K,
   for (int i = 0; i < 4; ++i) {
     long m = m0 + ty * 4 + i;
     long n = n0 + tx * 4;
-    if (m < M && n < N) epi_apply4<EPI, TO>(e, m, (int)n, acc[i]);
+    if (m < M && n < N) epi_apply4<EPI, TO>(e, m, (int)n, acc[i], blockIdx.y);
   }
 }
 
@@ -180,8 +180,9 @@ hipError_t launch_gemm(DType in_t, int M, int N, int K, const void* A, long lda,
     if (a_t && b_t) return f32_by_epi<true, true>(M, N, K, a, lda, b, ldb, epi, e, split_k, s);
     return f32_by_epi<true, false>(M, N, K, a, lda, b, ldb, epi, e, split_k, s);
   }
-  // bf16: 16-byte chunks along the contiguous dimension of each operand
-  if (lda % 8 || ldb % 8) return hipErrorInvalidValue;
+  // bf16: 16-byte chunks along the contiguous dimension of each operand, and
+  // the epilogue writes 8 consecutive columns per lane
+  if (lda % 8 || ldb % 8 || N % 8) return hipErrorInvalidValue;
   if ((!a_t || !b_t) && K % 8) return hipErrorInvalidValue;
   if ((a_t && M % 8) || (b_t && N % 8)) return hipErrorInvalidValue;
   const bf16_t* a = (const bf16_t*)A;

@@ -36,7 +36,21 @@ WORKLOADS = {
                 desc="GPT-2 124M masked fine-tuning step, bf16, B=16, T=1024, prompt targets -1"),
     "gpt2-xl": dict(model="gpt2-xl", B=8, T=1024, data="zipf", lr=6e-4, wd=0.1,
                     desc="GPT-2 XL-shape training step (L=48, C=1600, H=25), bf16, B=8, T=1024"),
+    "gpt2-124m-accum": dict(model="gpt2-124m", B=16, T=1024, data="zipf", accum=32, lr=None,
+                            wd=0.1,
+                            desc="GPT-2 124M full optimizer step: 32 micro-batches of 16x1024 "
+                                 "(524,288 tokens) with gradient accumulation, clip 1.0, AdamW, "
+                                 "lr warmup 715 steps then cosine 6e-4 -> 6e-5"),
 }
+
+METRIC = "training tokens/sec + MFU, GPT-2 124M bf16 B=16 T=1024 on one MI355X"
+
+# HBM traffic of the lm_head forward GEMM per launch, from two rocprofv3 --pmc
+# passes (FETCH_SIZE, then WRITE_SIZE) over `bench.py --steps 2 --warmup 1
+# --no-cpu-baseline --copy-probe`, each scaled by what the same counter reads
+# for a device copy of known size.  None until measured for the kernel as it
+# stands.
+LMHEAD_TRAFFIC_BYTES = None
 
 
 def flops_per_token(d, T):
@@ -68,7 +82,8 @@ def cpu_baseline(d, wl, seconds_hint=20.0):
         idx, tgt = synthetic.zipf_batch(1, T, seed=1002)
     m, v = np.zeros_like(flat), np.zeros_like(flat)
     t0 = time.perf_counter()
-    oracle.train_step(flat, m, v, 1, [(idx, tgt)], cfg, lr=wl["lr"], weight_decay=wl["wd"])
+    lr = wl["lr"] if wl["lr"] is not None else 6e-4 / 715
+    oracle.train_step(flat, m, v, 1, [(idx, tgt)], cfg, lr=lr, weight_decay=wl["wd"])
     dt = time.perf_counter() - t0
     return {"value": round(T / dt, 2), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
             "sample": f"one full step (fwd+bwd+clip+AdamW over all params) on 1 x {T} tokens "
@@ -83,6 +98,8 @@ def main():
     ap.add_argument("--workload", default="gpt2-124m", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--breakdown", action="store_true", help="also time every launch site")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="first run three 1 GiB device copies (calibrates HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
@@ -100,18 +117,32 @@ def main():
     cfg = G.make_config(max_batch=B, precision="bf16", **d)
     model = G.GPT2(cfg, device="cuda:0")
     model.set_params(synthetic.init_params(d, seed=42))
+    if args.copy_probe:
+        src = torch.ones(1 << 29, dtype=torch.bfloat16, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    accum = wl.get("accum", 1)
     if wl["data"] == "sft":
-        idx, tgt = synthetic.sft_batch(B, T, seed=1004)
+        batches = [synthetic.sft_batch(B, T, seed=1004)]
+    elif accum > 1:
+        batches = [synthetic.zipf_batch(B, T, seed=10030 + i) for i in range(accum)]
     else:
-        idx, tgt = synthetic.zipf_batch(B, T, seed=1002)
-    di = torch.tensor(idx, dtype=torch.int32, device="cuda:0")
-    dt = torch.tensor(tgt, dtype=torch.int32, device="cuda:0")
+        batches = [synthetic.zipf_batch(B, T, seed=1002)]
+    dev = [(torch.tensor(i, dtype=torch.int32, device="cuda:0"),
+            torch.tensor(t, dtype=torch.int32, device="cuda:0")) for i, t in batches]
+    opt_step = [0]
 
     def step():
         model.zero_grad()
-        model.forward(di, dt)
-        model.backward(1.0)
-        model.adamw_step(wl["lr"], 0.9, 0.95, 1e-8, wl["wd"], 1.0)
+        for di, dt in dev:
+            model.forward(di, dt)
+            model.backward(1.0 / len(dev))
+        lr = wl["lr"] if wl["lr"] is not None else G.lr_schedule(opt_step[0])
+        model.adamw_step(lr, 0.9, 0.95, 1e-8, wl["wd"], 1.0)
+        opt_step[0] += 1
 
     for _ in range(args.warmup):
         step()
@@ -134,13 +165,13 @@ def main():
     norm = model.get_grad_norm()
     model.sync()
     ms_step = ms_total / args.steps
-    tokens = B * T
+    tokens = B * T * accum
     tok_s = tokens * args.steps / (ms_total / 1e3)
     f_causal, f_nano = flops_per_token(d, T)
 
     lm_ms, lm_n = sites.get("LMHEAD_FWD", (0.0, 0))
     lm_avg = lm_ms / max(lm_n, 1)
-    lm_flops = 2.0 * tokens * d["padded_vocab_size"] * d["n_embd"]
+    lm_flops = 2.0 * B * T * d["padded_vocab_size"] * d["n_embd"]
     achieved = lm_flops / (lm_avg / 1e3) / 1e12 if lm_avg > 0 else 0.0
 
     breakdown = None
@@ -152,7 +183,8 @@ def main():
         breakdown = {k: round(v[0] / 2, 4) for k, v in sorted(br.items(), key=lambda x: -x[1][0])}
 
     out = {
-        "metric": "training tokens/sec + MFU, GPT-2 124M bf16 B=16 T=1024 on one MI355X",
+        "metric": METRIC if args.workload == "gpt2-124m" else
+                  f"training tokens/sec + MFU, {args.workload} on one MI355X",
         "value": round(tok_s, 1),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -164,7 +196,8 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": wl["desc"], "global_batch": B, "seq_len": T,
+        "config": {"workload": wl["desc"], "global_batch": B * accum, "seq_len": T,
+                   "micro_batches": accum,
                    "precision": "bf16 matmuls, fp32 master weights and optimizer state"},
         "mfu": round(tok_s * f_causal / (PEAK_BF16_TFLOPS * 1e12), 4),
         "mfu_nanogpt_count": round(tok_s * f_nano / (PEAK_BF16_TFLOPS * 1e12), 4),
@@ -175,7 +208,7 @@ def main():
         "roofline": {"kernel": "lm_head forward GEMM (gemm_kernel<256,256,NT,store bf16>)",
                      "bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": None, "avg_launch_ms": round(lm_avg, 4), "launches": lm_n,
+                     "traffic": LMHEAD_TRAFFIC_BYTES, "avg_launch_ms": round(lm_avg, 4), "launches": lm_n,
                      "flops_per_launch": lm_flops},
     }
     if breakdown:

@@ -4,13 +4,14 @@
 #include "common.h"
 
 enum EpiKind : int {
-  EPI_STORE = 0,     // out[m][n] = alpha*c (+ bias[n])                       (out: TO)
+  EPI_STORE = 0,     // out[m][n] = alpha*c                                   (out: TO)
   EPI_BIAS_GELU = 1, // h = c + bias[n]; out[m][n] = h; out2[m][n] = gelu(h)  (out, out2: TO)
   EPI_RESID = 2,     // out[m][n] = resid[m][n] + c + bias[n]                  (out, resid: fp32)
   EPI_ACCUM = 3,     // out[m][n] += alpha*c            one writer per element (out: fp32)
   EPI_ATOMIC = 4,    // atomically out[m][n] += alpha*c  split-K               (out: fp32)
   EPI_GELU_BWD = 5,  // out[m][n] = alpha*c * gelu'(aux[m][n])                 (out, aux: TO)
   EPI_PARTIAL = 6,   // split-K slice z: out[z*split_stride + m*ldo + n] = alpha*c  (fp32)
+  EPI_BIAS = 7,      // out[m][n] = alpha*c + bias[n]                         (out: TO)
 };
 
 struct EpiArgs {
@@ -31,7 +32,7 @@ constexpr bool epi_reads(int EPI) {
   return EPI == EPI_RESID || EPI == EPI_ACCUM || EPI == EPI_GELU_BWD;
 }
 constexpr bool epi_bias(int EPI) {
-  return EPI == EPI_STORE || EPI == EPI_BIAS_GELU || EPI == EPI_RESID;
+  return EPI == EPI_BIAS || EPI == EPI_BIAS_GELU || EPI == EPI_RESID;
 }
 
 // Phase 1: the per-element input of the epilogue (issue these for a whole
@@ -67,7 +68,7 @@ __device__ __forceinline__ void epi_store4(const EpiArgs& e, long m, int n, cons
 #pragma unroll
     for (int j = 0; j < 4; ++j) r[j] += b[j];
   }
-  if constexpr (EPI == EPI_STORE) {
+  if constexpr (EPI == EPI_STORE || EPI == EPI_BIAS) {
     st4(reinterpret_cast<TO*>(e.out) + m * e.ldo + n, r);
   } else if constexpr (EPI == EPI_BIAS_GELU) {
     st4(reinterpret_cast<TO*>(e.out) + m * e.ldo + n, r);

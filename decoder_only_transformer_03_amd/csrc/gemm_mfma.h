@@ -208,7 +208,7 @@ __device__ __forceinline__ void tile_epilogue(const EpiArgs& e, const f32x16_t (
 #pragma unroll
           for (int j = 0; j < 8; ++j) v[j] += bias8[j];
         }
-        if constexpr (EPI == EPI_STORE) {
+        if constexpr (EPI == EPI_STORE || EPI == EPI_BIAS) {
           st4(reinterpret_cast<TO*>(e.out) + m * e.ldo + nl, v);
           st4(reinterpret_cast<TO*>(e.out) + m * e.ldo + nl + 4, v + 4);
         } else if constexpr (EPI == EPI_BIAS_GELU) {
@@ -449,6 +449,9 @@ hipError_t dispatch(int M, int N, int K, const bf16_t* A, long lda, const bf16_t
         return out_t == DT_BF16                                                                 \
                    ? run<256, 256, 2, 4, LA, LB, EPI_STORE, bf16_t>(M, N, K, A, lda, B, ldb, e, 1, s) \
                    : run<256, 256, 2, 4, LA, LB, EPI_STORE, float>(M, N, K, A, lda, B, ldb, e, 1, s); \
+      case EPI_BIAS:                                                                            \
+        if (out_t != DT_BF16) return hipErrorInvalidValue;                                      \
+        return run<256, 256, 2, 4, LA, LB, EPI_BIAS, bf16_t>(M, N, K, A, lda, B, ldb, e, 1, s);  \
       case EPI_BIAS_GELU:                                                                       \
         return run<256, 256, 2, 4, LA, LB, EPI_BIAS_GELU, bf16_t>(M, N, K, A, lda, B, ldb, e, 1, s); \
       case EPI_RESID:                                                                           \

@@ -342,7 +342,7 @@ gpt2_status run_forward(gpt2* h, const int32_t* d_idx, const int32_t* d_tgt, int
                                    C, s));
     EpiArgs e = epi(a.qkv, 3 * C);
     e.bias = P + o.attnb;
-    TIMED(h, GPT2_SITE_QKV_FWD, launch_gemm(at, (int)BT, 3 * C, C, a.u1, C, false, W(h, o.attnw), C, false, EPI_STORE,
+    TIMED(h, GPT2_SITE_QKV_FWD, launch_gemm(at, (int)BT, 3 * C, C, a.u1, C, false, W(h, o.attnw), C, false, EPI_BIAS,
                           at, e, 0, s));
     TIMED(h, GPT2_SITE_ATTN_FWD, launch_attn_fwd(at, a.qkv, a.y, a.lse, B, T, H, hd, s));
     e = epi(a.x_mid, C);
@@ -683,7 +683,8 @@ gpt2_status gpt2_get_activation(gpt2_t* h, int which, int layer, float* h_dst, s
     case GPT2_ACT_ROW_LOSS: src = h->row_loss; count = BT; f32 = true; break;
     default: return fail(h, GPT2_E_ARG, "unknown activation id");
   }
-  if (n != count) return fail(h, GPT2_E_ARG, "n does not match the activation's element count");
+  if (n > count) return fail(h, GPT2_E_ARG, "n exceeds the activation's element count");
+  count = n;
   gpt2_status st = sync(h);
   if (st != GPT2_OK) return st;
   if (f32 || h->act == DT_F32) {

@@ -81,6 +81,7 @@ static hipError_t f32_by_epi(int M, int N, int K, const float* A, long lda, cons
                              long ldb, int epi, const EpiArgs& e, int split_k, hipStream_t s) {
   switch (epi) {
     case EPI_STORE: return f32_run<AT, BT, EPI_STORE>(M, N, K, A, lda, B, ldb, e, 1, s);
+    case EPI_BIAS: return f32_run<AT, BT, EPI_BIAS>(M, N, K, A, lda, B, ldb, e, 1, s);
     case EPI_BIAS_GELU: return f32_run<AT, BT, EPI_BIAS_GELU>(M, N, K, A, lda, B, ldb, e, 1, s);
     case EPI_RESID: return f32_run<AT, BT, EPI_RESID>(M, N, K, A, lda, B, ldb, e, 1, s);
     case EPI_ACCUM: return f32_run<AT, BT, EPI_ACCUM>(M, N, K, A, lda, B, ldb, e, 1, s);

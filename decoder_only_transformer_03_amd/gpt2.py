@@ -8,6 +8,7 @@ loading fails loudly otherwise -- there is no fallback.
 from __future__ import annotations
 
 import ctypes as ct
+import math
 import os
 
 import numpy as np
@@ -242,6 +243,19 @@ class GPT2:
         out = np.empty(count, np.float32)
         self._check(lib().gpt2_get_activation(self.h, ACT[name], layer, out.ctypes.data, count))
         return out
+
+
+def lr_schedule(step, max_lr=6e-4, min_lr=6e-5, warmup_steps=715, max_steps=19073):
+    """Learning rate of optimizer step `step` (0-based), as the host sets it
+    before each gpt2_adamw_step ("GPT-2 from Scratch", learning-rate schedule
+    section): a linear ramp (step+1)/warmup_steps * max_lr, then a half cosine
+    from max_lr at warmup_steps down to min_lr at max_steps, and min_lr after."""
+    if step < warmup_steps:
+        return max_lr * (step + 1) / warmup_steps
+    if step > max_steps:
+        return min_lr
+    frac = (step - warmup_steps) / max(1, max_steps - warmup_steps)
+    return min_lr + (max_lr - min_lr) * 0.5 * (1.0 + math.cos(math.pi * frac))
 
 
 def _st(st, what):

@@ -178,8 +178,9 @@ void gpt2_destroy(gpt2_t* h);
 
 /* Saved activations of the last forward, for layer-by-layer comparison
  * against a reference.  `layer` selects the block where it applies.  The
- * tensor is converted to fp32 and copied to host memory (waits); n must equal
- * the element count given for each id below (B, T of the last forward):
+ * tensor is converted to fp32 and copied to host memory (waits).  The first
+ * n elements (row-major) are copied; n may not exceed the element count given
+ * for each id below (B, T of the last forward):
  *   X_IN      residual stream entering block `layer` (layer == n_layer: after the last block), B*T*C
  *   LN1       ln_1 output, B*T*C          QKV    c_attn output, B*T*3C ([q | k | v])
  *   ATTN_Y    attention output with heads re-interleaved, B*T*C

@@ -239,6 +239,10 @@ __device__ __forceinline__ f32x16_t mfma(bf16x8_t a, bf16x8_t b, f32x16_t c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// 2^x on the transcendental unit (results below 2^-126 flush to zero, which
+// does not matter for probabilities).
+__device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
+
 __device__ __forceinline__ f32x16_t zero16() {
   f32x16_t z;
 #pragma unroll
@@ -297,48 +301,54 @@ __global__ __launch_bounds__(256) void attn_fwd_mfma(const bf16_t* __restrict__ 
       gk.load(kbase, ld, k0 + 64, Tn, tid);
       gv.load(vbase, ld, k0 + 64, Tn, tid);
     }
+    if (k0 <= q0w + 31) {  // this wavefront has unmasked keys in the block
+      // S^T for keys k0..k0+31 (sa) and k0+32..k0+63 (sb): two independent chains
+      f32x16_t sa = zero16(), sb = zero16();
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      const int kb = k0 + 32 * s;
-      if (kb > q0w + 31 || kb >= Tn) break;
-      f32x16_t st = zero16();
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk)
-        st = mfma(frag_rows(sK[cur], 32 * s + l32, kk * 2 + half), qf[kk], st);
+      for (int kk = 0; kk < 4; ++kk) {
+        sa = mfma(frag_rows(sK[cur], l32, kk * 2 + half), qf[kk], sa);
+        sb = mfma(frag_rows(sK[cur], 32 + l32, kk * 2 + half), qf[kk], sb);
+      }
       float mx = NEG_INF;
-      if (kb + 31 > q0w || kb + 31 >= Tn) {  // diagonal or ragged block: mask
+      if (k0 + 63 > q0w || k0 + 63 >= Tn) {  // diagonal or ragged block: mask
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          int key = kb + 8 * (r >> 2) + 4 * half + (r & 3);
-          float x = (key > myq || key >= Tn) ? NEG_INF : st[r] * sl2;
-          st[r] = x;
-          mx = fmaxf(mx, x);
+          const int key = k0 + 8 * (r >> 2) + 4 * half + (r & 3);
+          sa[r] = (key > myq || key >= Tn) ? NEG_INF : sa[r];
+          sb[r] = (key + 32 > myq || key + 32 >= Tn) ? NEG_INF : sb[r];
+          mx = fmaxf(mx, fmaxf(sa[r], sb[r]));
         }
       } else {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          st[r] *= sl2;
-          mx = fmaxf(mx, st[r]);
-        }
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, fmaxf(sa[r], sb[r]));
       }
       mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float mn = fmaxf(m2, mx);
-      const float ms = mn == NEG_INF ? 0.f : mn;
-      const float alpha = exp2f(m2 - ms);
-      m2 = mn;
-      ls *= alpha;
-      o0 *= alpha;
-      o1 *= alpha;
+      // Lazy rescaling: the running maximum m2 (log2 units) only moves when a
+      // score exceeds it by more than 8, so most blocks skip rescaling O.
+      // Probabilities are then bounded by 2^8, harmless in fp32 and bf16.
+      const float mnew = mx * sl2;
+      const bool need = mnew > m2 + 8.0f;
+      if (__any(need)) {
+        const float alpha = need ? ex2(m2 - mnew) : 1.0f;
+        m2 = need ? mnew : m2;
+        ls *= alpha;
+        o0 *= alpha;
+        o1 *= alpha;
+      }
+      const float ms = m2 == NEG_INF ? 0.f : m2;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        st[r] = exp2f(st[r] - ms);
-        ls += st[r];
+        sa[r] = ex2(fmaf(sa[r], sl2, -ms));
+        sb[r] = ex2(fmaf(sb[r], sl2, -ms));
+        ls += sa[r] + sb[r];
       }
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
-        bf16x8_t pb = pack_acc(st, u);
-        o0 = mfma(frag_cols(sVt[cur], l32, 32 * s + 16 * u, half), pb, o0);
-        o1 = mfma(frag_cols(sVt[cur], 32 + l32, 32 * s + 16 * u, half), pb, o1);
+        const bf16x8_t pa = pack_acc(sa, u), pb = pack_acc(sb, u);
+        o0 = mfma(frag_cols(sVt[cur], l32, 16 * u, half), pa, o0);
+        o1 = mfma(frag_cols(sVt[cur], 32 + l32, 16 * u, half), pa, o1);
+        o0 = mfma(frag_cols(sVt[cur], l32, 32 + 16 * u, half), pb, o0);
+        o1 = mfma(frag_cols(sVt[cur], 32 + l32, 32 + 16 * u, half), pb, o1);
       }
     }
     if (more) {
@@ -433,20 +443,20 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_mfma(const bf16_t* __restrict
         st = mfma(frag_rows(sK[cur], 32 * s + l32, kk * 2 + half), qf[kk], st);
         dp = mfma(frag_rows(sV[cur], 32 * s + l32, kk * 2 + half), gf[kk], dp);
       }
-      if (kb + 31 > q0w || kb + 31 >= Tn) {
+      if (kb + 31 > q0w || kb + 31 >= Tn) {  // diagonal or ragged block: mask
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          int key = kb + 8 * (r >> 2) + 4 * half + (r & 3);
-          float p = (key <= myq && key < Tn) ? exp2f(st[r] * sl2 - lse2) : 0.f;
+          const int key = kb + 8 * (r >> 2) + 4 * half + (r & 3);
+          const float p = (key <= myq && key < Tn) ? ex2(fmaf(st[r], sl2, -lse2)) : 0.f;
           st[r] = p * (dp[r] - dd);
         }
       } else {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) st[r] = exp2f(st[r] * sl2 - lse2) * (dp[r] - dd);
+        for (int r = 0; r < 16; ++r) st[r] = ex2(fmaf(st[r], sl2, -lse2)) * (dp[r] - dd);
       }
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
-        bf16x8_t pb = pack_acc(st, u);
+        const bf16x8_t pb = pack_acc(st, u);
         dq0 = mfma(frag_cols(sKt[cur], l32, 32 * s + 16 * u, half), pb, dq0);
         dq1 = mfma(frag_cols(sKt[cur], 32 + l32, 32 * s + 16 * u, half), pb, dq1);
       }
@@ -561,7 +571,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dkv_mfma(const bf16_t* __restric
       for (int r = 0; r < 16; ++r) {
         int qi = 32 * s + 8 * (r >> 2) + 4 * half + (r & 3);
         int q = q0 + qi;
-        float p = exp2f(st[r] * sl2 - sL[cur][qi]);
+        float p = ex2(fmaf(st[r], sl2, -sL[cur][qi]));
         if (edge && !(mykey <= q && q < Tn)) p = 0.f;
         pv[r] = p;
         st[r] = p * (dp[r] - sD[cur][qi]);

@@ -36,22 +36,53 @@ __global__ __launch_bounds__(256) void embed_fwd_kernel(const int32_t* __restric
 
 // dwte[idx[p],:] += dx[p,:]  (adds onto the lm_head part already there: the
 // tied weight's gradient is the sum of both uses, "Weight tying").
+// dwte[idx[r]] += dx[r] for a chunk of EMB_CHUNK rows per block.  The chunk's
+// (id, row) pairs are ranked in LDS so that rows with the same id are summed in
+// registers first and each distinct id costs one atomic per column: with the
+// skewed token statistics of text, most of a chunk's rows share a few ids, and
+// atomics on one address serialise.
+constexpr int EMB_CHUNK = 64;
 __global__ __launch_bounds__(256) void embed_bwd_wte_kernel(const int32_t* __restrict__ idx,
                                                             const float* __restrict__ dx,
                                                             float* __restrict__ dwte, int C,
                                                             long rows) {
-  long row = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
-  int lane = threadIdx.x & 63;
-  if (row >= rows) return;
-  int id = idx[row];
-  const float* s = dx + row * C;
-  float* d = dwte + (long)id * C;
-  for (int c = lane * 4; c < C; c += 256) {
-    float4 v = *reinterpret_cast<const float4*>(s + c);
-    atomicAdd(d + c + 0, v.x);
-    atomicAdd(d + c + 1, v.y);
-    atomicAdd(d + c + 2, v.z);
-    atomicAdd(d + c + 3, v.w);
+  __shared__ unsigned key[EMB_CHUNK], sorted[EMB_CHUNK];
+  const long r0 = (long)blockIdx.x * EMB_CHUNK;
+  const int n = rows - r0 < EMB_CHUNK ? (int)(rows - r0) : EMB_CHUNK;
+  const int t = threadIdx.x;
+  if (t < n) key[t] = ((unsigned)idx[r0 + t] << 6) | (unsigned)t;  // ids < 2^26
+  __syncthreads();
+  if (t < n) {
+    const unsigned k = key[t];
+    int rank = 0;
+    for (int j = 0; j < n; ++j) rank += key[j] < k;
+    sorted[rank] = k;
+  }
+  __syncthreads();
+  for (int c = t * 4; c < C; c += 1024) {
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int q0 = 0; q0 < n; q0 += 8) {
+      float4 v[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j)  // issue the batch's loads before using any
+        if (q0 + j < n)
+          v[j] = *reinterpret_cast<const float4*>(dx + (r0 + (sorted[q0 + j] & 63u)) * C + c);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int q = q0 + j;
+        if (q >= n) break;
+        const unsigned k = sorted[q];
+        acc.x += v[j].x; acc.y += v[j].y; acc.z += v[j].z; acc.w += v[j].w;
+        if (q + 1 == n || (sorted[q + 1] >> 6) != (k >> 6)) {
+          float* d = dwte + (long)(k >> 6) * C + c;
+          atomicAdd(d + 0, acc.x);
+          atomicAdd(d + 1, acc.y);
+          atomicAdd(d + 2, acc.z);
+          atomicAdd(d + 3, acc.w);
+          acc = make_float4(0.f, 0.f, 0.f, 0.f);
+        }
+      }
+    }
   }
 }
 
@@ -242,19 +273,30 @@ __global__ __launch_bounds__(256) void colsum_kernel(const T* __restrict__ X, lo
 }
 
 // dst_k[c] += sum_p partial[p][k*w + c] for the non-null destinations (k = 0..2).
+// 64 columns per block, four row phases per column (fixed summation order).
 __global__ __launch_bounds__(256) void colsum_finish_kernel(const float* __restrict__ partial,
                                                             int nparts, int w,
                                                             float* __restrict__ d0,
                                                             float* __restrict__ d1,
                                                             float* __restrict__ d2, int ncols) {
-  int c = blockIdx.x * 256 + threadIdx.x;
-  if (c >= ncols) return;
-  int k = c / w, cc = c - k * w;
+  __shared__ float sh[4][64];
+  const int cl = threadIdx.x & 63, g = threadIdx.x >> 6;
+  const int c = blockIdx.x * 64 + cl;
+  float a0 = 0.f, a1 = 0.f;
+  if (c < ncols) {
+    int p = g;
+    for (; p + 4 < nparts; p += 8) {
+      a0 += partial[(long)p * ncols + c];
+      a1 += partial[(long)(p + 4) * ncols + c];
+    }
+    if (p < nparts) a0 += partial[(long)p * ncols + c];
+  }
+  sh[g][cl] = a0 + a1;
+  __syncthreads();
+  if (g != 0 || c >= ncols) return;
+  const int k = c / w, cc = c - k * w;
   float* d = k == 0 ? d0 : k == 1 ? d1 : d2;
-  if (!d) return;
-  float s = 0.f;
-  for (int p = 0; p < nparts; ++p) s += partial[(long)p * ncols + c];
-  d[cc] += s;
+  if (d) d[cc] += (sh[0][cl] + sh[1][cl]) + (sh[2][cl] + sh[3][cl]);
 }
 
 // ---------------------------------------------------------------------------
@@ -324,74 +366,71 @@ template <> struct Row8<float> {
 };
 
 
-// One workgroup per row.  Pass 1 streams the row once keeping a running
-// (max, sum of exp) per thread; the block combines them into the row's
-// log-sum-exp.  Pass 2 re-reads the row (now resident in the on-die caches)
-// and overwrites it with
+// One workgroup per row.  The row is read from memory once into registers
+// (XENT_KPT chunks of 8 per thread), reduced to its maximum and sum of
+// exponentials over the workgroup, and overwritten with
 //   d(loss)/d(logits) = (softmax - onehot(target)) / n_valid   (0 if ignored).
 // Padded vocabulary columns take part like real ones.
-template <typename T, int NT>
-__global__ __launch_bounds__(NT) void xent_fused_kernel(T* __restrict__ logits,
-                                                        const int32_t* __restrict__ targets,
-                                                        const int* __restrict__ n_valid,
-                                                        float* __restrict__ row_loss, int Vp) {
-  constexpr int NW = NT / 64;
-  __shared__ float sm[NW], ss[NW];
+constexpr int XENT_NT = 512, XENT_KPT = 13;  // rows up to 8 * 512 * 13 = 53248 wide
+template <typename T>
+__global__ __launch_bounds__(XENT_NT) void xent_fused_kernel(T* __restrict__ logits,
+                                                             const int32_t* __restrict__ targets,
+                                                             const int* __restrict__ n_valid,
+                                                             float* __restrict__ row_loss, int Vp) {
+  constexpr int NW = XENT_NT / 64;
+  __shared__ float red[2][NW];
   const long row = blockIdx.x;
   T* lr = logits + row * (long)Vp;
   int tgt = targets[row];
   const bool valid = tgt != -1;
   if (tgt < 0 || tgt >= Vp) tgt = -1;  // out-of-range already flagged by count_valid
   const float xt = valid && tgt >= 0 ? ldf(lr + tgt) : 0.f;
-  const int nchunks = Vp >> 3;
-  float m = -__builtin_inff(), sum = 0.f;
-#pragma unroll 2
-  for (int ch = threadIdx.x; ch < nchunks; ch += NT) {
-    Row8<T> v;
-    v.load(lr + ch * 8);
-    float cm = v.get(0);
+  const int nchunks = Vp >> 3, lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  Row8<T> v[XENT_KPT];
 #pragma unroll
-    for (int j = 1; j < 8; ++j) cm = fmaxf(cm, v.get(j));
-    if (cm > m) {
-      sum *= __expf(m - cm);
-      m = cm;
-    }
+  for (int i = 0; i < XENT_KPT; ++i) {
+    const int ch = threadIdx.x + i * XENT_NT;
+    if (ch < nchunks) v[i].load(lr + ch * 8);
+  }
+  float m = -__builtin_inff();
 #pragma unroll
-    for (int j = 0; j < 8; ++j) sum += __expf(v.get(j) - m);
-  }
-  // combine (m, sum) over the wavefront, then over the workgroup
+  for (int i = 0; i < XENT_KPT; ++i)
+    if (threadIdx.x + i * XENT_NT < nchunks)
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    float om = __shfl_xor(m, o, 64), os = __shfl_xor(sum, o, 64);
-    float nm = fmaxf(m, om);
-    sum = (m == nm ? sum : sum * __expf(m - nm)) + (om == nm ? os : os * __expf(om - nm));
-    m = nm;
-  }
-  if ((threadIdx.x & 63) == 0) {
-    sm[threadIdx.x >> 6] = m;
-    ss[threadIdx.x >> 6] = sum;
-  }
+      for (int j = 0; j < 8; ++j) m = fmaxf(m, v[i].get(j));
+  m = wave_max(m);
+  if (lane == 0) red[0][w] = m;
   __syncthreads();
-  float M = sm[0];
+  float M = red[0][0];
 #pragma unroll
-  for (int i = 1; i < NW; ++i) M = fmaxf(M, sm[i]);
+  for (int i = 1; i < NW; ++i) M = fmaxf(M, red[0][i]);
+  float sum = 0.f;
+#pragma unroll
+  for (int i = 0; i < XENT_KPT; ++i)
+    if (threadIdx.x + i * XENT_NT < nchunks)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) sum += __expf(v[i].get(j) - M);
+  sum = wave_sum(sum);
+  if (lane == 0) red[1][w] = sum;
+  __syncthreads();
   float S = 0.f;
 #pragma unroll
-  for (int i = 0; i < NW; ++i) S += ss[i] * __expf(sm[i] - M);
+  for (int i = 0; i < NW; ++i) S += red[1][i];
   const float lse = M + __logf(S);
   const int nv = *n_valid;
   const float scale = valid && nv > 0 ? 1.0f / (float)nv : 0.f;
-#pragma unroll 2
-  for (int ch = threadIdx.x; ch < nchunks; ch += NT) {
-    Row8<T> v;
-    v.load(lr + ch * 8);
-    float o[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      float p = __expf(v.get(j) - lse);
-      o[j] = (p - (ch * 8 + j == tgt ? 1.0f : 0.0f)) * scale;
+  for (int i = 0; i < XENT_KPT; ++i) {
+    const int ch = threadIdx.x + i * XENT_NT;
+    if (ch < nchunks) {
+      float o[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float p = __expf(v[i].get(j) - lse);
+        o[j] = (p - (ch * 8 + j == tgt ? 1.0f : 0.0f)) * scale;
+      }
+      Row8<T>::store(lr + ch * 8, o);
     }
-    Row8<T>::store(lr + ch * 8, o);
   }
   if (threadIdx.x == 0) row_loss[row] = valid ? lse - xt : 0.f;
 }
@@ -534,7 +573,7 @@ hipError_t launch_embed_fwd(const int32_t* idx_in, int32_t* idx_saved, const flo
 hipError_t launch_embed_bwd(const int32_t* idx, const float* dx, float* dwte, float* dwpe, int B,
                             int T, int C, hipStream_t s) {
   long rows = (long)B * T;
-  embed_bwd_wte_kernel<<<nblk(rows, 4), 256, 0, s>>>(idx, dx, dwte, C, rows);
+  embed_bwd_wte_kernel<<<nblk(rows, EMB_CHUNK), 256, 0, s>>>(idx, dx, dwte, C, rows);
   embed_bwd_wpe_kernel<<<nblk((long)T * C, 256), 256, 0, s>>>(dx, dwpe, B, T, C);
   return hipGetLastError();
 }
@@ -578,7 +617,7 @@ static hipError_t colsum_into(const float* X, long rows, int ncols, float* scrat
   float* part2 = scratch;
   colsum_kernel<float><<<dim3(nblk(ncols, 64), splits), 256, 0, s>>>(X, rows, ncols, ncols, part2,
                                                                     rps);
-  colsum_finish_kernel<<<nblk(ncols, 256), 256, 0, s>>>(part2, splits, w, d0, d1, d2, ncols);
+  colsum_finish_kernel<<<nblk(ncols, 64), 256, 0, s>>>(part2, splits, w, d0, d1, d2, ncols);
   return hipGetLastError();
 }
 
@@ -634,19 +673,20 @@ hipError_t launch_bias_grad(DType in_t, const void* X, long rows, int N, long ld
     colsum_kernel<bf16_t><<<grid, 256, 0, s>>>((const bf16_t*)X, rows, N, ldx, partial, rps);
   else
     colsum_kernel<float><<<grid, 256, 0, s>>>((const float*)X, rows, N, ldx, partial, rps);
-  colsum_finish_kernel<<<nblk(N, 256), 256, 0, s>>>(partial, splits, N, db, nullptr, nullptr, N);
+  colsum_finish_kernel<<<nblk(N, 64), 256, 0, s>>>(partial, splits, N, db, nullptr, nullptr, N);
   return hipGetLastError();
 }
 
 hipError_t launch_xent(DType t, void* logits, const int32_t* targets, int* n_valid,
                        float* row_loss, float* loss, long rows, int Vp, int* err, hipStream_t s) {
+  if (Vp % 8 || Vp > 8 * XENT_NT * XENT_KPT) return hipErrorInvalidValue;
   count_valid_kernel<<<1, 1024, 0, s>>>(targets, rows, Vp, n_valid, err);
   if (t == DT_BF16)
-    xent_fused_kernel<bf16_t, 256><<<(unsigned)rows, 256, 0, s>>>((bf16_t*)logits, targets,
-                                                                   n_valid, row_loss, Vp);
+    xent_fused_kernel<bf16_t><<<(unsigned)rows, XENT_NT, 0, s>>>((bf16_t*)logits, targets,
+                                                                  n_valid, row_loss, Vp);
   else
-    xent_fused_kernel<float, 256><<<(unsigned)rows, 256, 0, s>>>((float*)logits, targets, n_valid,
-                                                                  row_loss, Vp);
+    xent_fused_kernel<float><<<(unsigned)rows, XENT_NT, 0, s>>>((float*)logits, targets, n_valid,
+                                                                 row_loss, Vp);
   loss_reduce_kernel<<<1, 1024, 0, s>>>(row_loss, rows, n_valid, loss);
   return hipGetLastError();
 }

@@ -25,11 +25,17 @@ CFLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-result",
 ]
+# Per-source additions.  Attention: matrix-core results in ordinary VGPRs, so
+# the softmax and the running rescale of the output act on them in place
+# instead of copying accumulators out of and back into AGPRs.
+EXTRA = {
+    "k_attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+}
 
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src).replace(".hip", ".o"))
-    cmd = [HIPCC, *CFLAGS, "-c", src, "-o", obj]
+    cmd = [HIPCC, *CFLAGS, *EXTRA.get(os.path.basename(src), []), "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         noise = "is not a recognized feature for this target"

@@ -159,73 +159,60 @@ __global__ __launch_bounds__(128) void attn_bwd_dkv_simt(const T* __restrict__ q
 // (which is free to choose, since it is a sum).
 // ===========================================================================
 namespace {
-constexpr int ATS = 68;  // row stride (elements) of transposed LDS tiles [64 d][64 + 4]
-
-__device__ __forceinline__ int swz(int row, int c) { return c ^ ((row ^ (row >> 3)) & 7); }
+// LDS tiles hold 64 rows x 64 bf16 (128 bytes per row) in row-major order,
+// with the eight 16-byte chunks of each row permuted by xr(row).  The
+// permutation keeps both read patterns free of bank conflicts: 16-byte
+// fragment reads of 16 consecutive rows at one chunk, and transpose reads of
+// 4 consecutive rows x 64 bytes per half-wavefront.
+__device__ __forceinline__ int xr(int row) { return (((row >> 1) & 1) << 2) | ((row >> 2) & 3); }
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
 
-// Staging of 64-row blocks of q/k/v/dy into LDS, split into a global load
-// into registers (issued one block ahead) and the LDS write.
-// Rows layout: 64 rows x 64 columns, 16-byte chunks swizzled by row.
-struct RowsStage {
-  uint4 v[2];
-  __device__ __forceinline__ void load(const bf16_t* __restrict__ X, long ld, int row0, int nrows,
-                                       int tid) {
-    const int c = tid & 7;
+// Rows row0 .. row0+63 of X (row stride ld, 64 columns from X) copied straight
+// from global memory into the LDS tile s by the 4 wavefronts of the block,
+// 16 bytes per lane.  Rows at or past nrows repeat row nrows-1 (finite data
+// that the callers mask).  Completion: s_waitcnt vmcnt(0), then a barrier.
+__device__ __forceinline__ void tile_load(const bf16_t* __restrict__ X, long ld, int row0,
+                                          int nrows, int tid, bf16_t* s) {
+  const int lane = tid & 63, w = tid >> 6;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      int row = row0 + (tid >> 3) + 32 * i;
-      v[i] = row < nrows ? *reinterpret_cast<const uint4*>(X + (long)row * ld + c * 8)
-                         : make_uint4(0, 0, 0, 0);
-    }
+  for (int j = 0; j < 2; ++j) {
+    const int rbase = (w * 2 + j) * 8;
+    const int row = rbase + (lane >> 3);
+    const int c = (lane & 7) ^ xr(row);
+    const int grow = row0 + row < nrows ? row0 + row : nrows - 1;
+    __builtin_amdgcn_global_load_lds(
+        (const __attribute__((address_space(1))) void*)(X + (long)grow * ld + c * 8),
+        (__attribute__((address_space(3))) void*)(s + rbase * 64), 16, 0, 0);
   }
-  __device__ __forceinline__ void store(bf16_t* s, int tid) const {
-    const int c = tid & 7;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      int r = (tid >> 3) + 32 * i;
-      *reinterpret_cast<uint4*>(s + r * 64 + swz(r, c) * 8) = v[i];
-    }
-  }
-};
-
-// Transposed layout: s[d][r] = X[row0 + r][d] for d, r < 64 (row stride ATS).
-struct ColsStage {
-  uint32_t u[8];
-  __device__ __forceinline__ void load(const bf16_t* __restrict__ X, long ld, int row0, int nrows,
-                                       int tid) {
-    const int dp = tid & 31, kg = tid >> 5;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      int row = row0 + kg * 8 + j;
-      u[j] = row < nrows ? *reinterpret_cast<const uint32_t*>(X + (long)row * ld + 2 * dp) : 0u;
-    }
-  }
-  __device__ __forceinline__ void store(bf16_t* s, int tid) const {
-    const int dp = tid & 31, kg = tid >> 5;
-    bf16_t* d0 = s + (2 * dp) * ATS + kg * 8;
-    bf16_t* d1 = d0 + ATS;
-    *reinterpret_cast<uint2*>(d0) =
-        make_uint2(__byte_perm(u[0], u[1], 0x5410u), __byte_perm(u[2], u[3], 0x5410u));
-    *reinterpret_cast<uint2*>(d0 + 4) =
-        make_uint2(__byte_perm(u[4], u[5], 0x5410u), __byte_perm(u[6], u[7], 0x5410u));
-    *reinterpret_cast<uint2*>(d1) =
-        make_uint2(__byte_perm(u[0], u[1], 0x7632u), __byte_perm(u[2], u[3], 0x7632u));
-    *reinterpret_cast<uint2*>(d1 + 4) =
-        make_uint2(__byte_perm(u[4], u[5], 0x7632u), __byte_perm(u[6], u[7], 0x7632u));
-  }
-};
-
-__device__ __forceinline__ bf16x8_t frag_rows(const bf16_t* s, int row, int c) {
-  return *reinterpret_cast<const bf16x8_t*>(s + row * 64 + swz(row, c) * 8);
 }
 
-// Operand fragment of a transposed tile for contraction slots
-// {base + 4h + 0..3, base + 8 + 4h + 0..3} of row d.
-__device__ __forceinline__ bf16x8_t frag_cols(const bf16_t* s, int d, int base, int h) {
-  uint2 lo = *reinterpret_cast<const uint2*>(s + d * ATS + base + 4 * h);
-  uint2 hi = *reinterpret_cast<const uint2*>(s + d * ATS + base + 8 + 4 * h);
+__device__ __forceinline__ void tile_wait() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// 16-byte fragment: 8 consecutive columns (chunk c) of one row.
+__device__ __forceinline__ bf16x8_t frag_rows(const bf16_t* s, int row, int c) {
+  return *reinterpret_cast<const bf16x8_t*>(s + row * 64 + ((c ^ xr(row)) << 3));
+}
+
+typedef short short4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint2 read_tr(const bf16_t* s, int row, int col) {
+  const bf16_t* p = s + row * 64 + (((col >> 3) ^ xr(row)) << 3) + (col & 7);
+  const short4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) short4_t*)((__attribute__((address_space(3))) bf16_t*)p));
+  return __builtin_bit_cast(uint2, v);
+}
+
+// Operand fragment of the transposed tile: lane l supplies row d = dbase +
+// l%32 of the transpose (column d of the tile) at contraction slots
+// {base + 4h + 0..3, base + 8 + 4h + 0..3}, h = l/32, i.e. tile rows.  Each
+// transpose read gathers, for a group of 16 lanes, a 4-row x 16-column block:
+// lane t of the group addresses row t/4, columns 4(t%4)..+3, and receives
+// column t of the 4 rows.
+__device__ __forceinline__ bf16x8_t frag_tr(const bf16_t* s, int dbase, int base, int lane) {
+  const int g = lane >> 4, t = lane & 15;
+  const int row = base + 4 * (g >> 1) + (t >> 2);
+  const int col = dbase + 16 * (g & 1) + 4 * (t & 3);
+  const uint2 lo = read_tr(s, row, col), hi = read_tr(s, row + 8, col);
   return as_bf16x8(make_uint4(lo.x, lo.y, hi.x, hi.y));
 }
 
@@ -266,7 +253,7 @@ __global__ __launch_bounds__(256) void attn_fwd_mfma(const bf16_t* __restrict__ 
                                                      bf16_t* __restrict__ y,
                                                      float* __restrict__ lse, int Tn, int H, int C) {
   __shared__ __attribute__((aligned(16))) bf16_t sK[2][64 * 64];
-  __shared__ __attribute__((aligned(16))) bf16_t sVt[2][64 * ATS];
+  __shared__ __attribute__((aligned(16))) bf16_t sV[2][64 * 64];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, half = lane >> 5, l32 = lane & 31;
   const int qb = gridDim.x - 1 - blockIdx.x;  // longest rows first
   const int bh = blockIdx.y, b = bh / H, h = bh % H;
@@ -287,19 +274,16 @@ __global__ __launch_bounds__(256) void attn_fwd_mfma(const bf16_t* __restrict__ 
   f32x16_t o0 = zero16(), o1 = zero16();
   float m2 = NEG_INF, ls = 0.f;
   const int kend = Tn < qb * 128 + 128 ? Tn : qb * 128 + 128;
-  RowsStage gk;
-  ColsStage gv;
-  gk.load(kbase, ld, 0, Tn, tid);
-  gv.load(vbase, ld, 0, Tn, tid);
-  gk.store(sK[0], tid);
-  gv.store(sVt[0], tid);
+  tile_load(kbase, ld, 0, Tn, tid, sK[0]);
+  tile_load(vbase, ld, 0, Tn, tid, sV[0]);
+  tile_wait();
   __syncthreads();
   int cur = 0;
   for (int k0 = 0; k0 < kend; k0 += 64, cur ^= 1) {
     const bool more = k0 + 64 < kend;
     if (more) {
-      gk.load(kbase, ld, k0 + 64, Tn, tid);
-      gv.load(vbase, ld, k0 + 64, Tn, tid);
+      tile_load(kbase, ld, k0 + 64, Tn, tid, sK[cur ^ 1]);
+      tile_load(vbase, ld, k0 + 64, Tn, tid, sV[cur ^ 1]);
     }
     if (k0 <= q0w + 31) {  // this wavefront has unmasked keys in the block
       // S^T for keys k0..k0+31 (sa) and k0+32..k0+63 (sb): two independent chains
@@ -345,16 +329,13 @@ __global__ __launch_bounds__(256) void attn_fwd_mfma(const bf16_t* __restrict__ 
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         const bf16x8_t pa = pack_acc(sa, u), pb = pack_acc(sb, u);
-        o0 = mfma(frag_cols(sVt[cur], l32, 16 * u, half), pa, o0);
-        o1 = mfma(frag_cols(sVt[cur], 32 + l32, 16 * u, half), pa, o1);
-        o0 = mfma(frag_cols(sVt[cur], l32, 32 + 16 * u, half), pb, o0);
-        o1 = mfma(frag_cols(sVt[cur], 32 + l32, 32 + 16 * u, half), pb, o1);
+        o0 = mfma(frag_tr(sV[cur], 0, 16 * u, lane), pa, o0);
+        o1 = mfma(frag_tr(sV[cur], 32, 16 * u, lane), pa, o1);
+        o0 = mfma(frag_tr(sV[cur], 0, 32 + 16 * u, lane), pb, o0);
+        o1 = mfma(frag_tr(sV[cur], 32, 32 + 16 * u, lane), pb, o1);
       }
     }
-    if (more) {
-      gk.store(sK[cur ^ 1], tid);
-      gv.store(sVt[cur ^ 1], tid);
-    }
+    tile_wait();
     __syncthreads();
   }
   const float lt = ls + __shfl_xor(ls, 32, 64);
@@ -382,7 +363,6 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_mfma(const bf16_t* __restrict
                                                         int C) {
   __shared__ __attribute__((aligned(16))) bf16_t sK[2][64 * 64];
   __shared__ __attribute__((aligned(16))) bf16_t sV[2][64 * 64];
-  __shared__ __attribute__((aligned(16))) bf16_t sKt[2][64 * ATS];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, half = lane >> 5, l32 = lane & 31;
   const int qb = gridDim.x - 1 - blockIdx.x;
   const int bh = blockIdx.y, b = bh / H, h = bh % H;
@@ -416,22 +396,16 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_mfma(const bf16_t* __restrict
   const int kend = Tn < qb * 128 + 128 ? Tn : qb * 128 + 128;
   const bf16_t* kbase = base + C + h * 64;
   const bf16_t* vbase = base + 2 * C + h * 64;
-  RowsStage gk, gv;
-  ColsStage gkt;
-  gk.load(kbase, ld, 0, Tn, tid);
-  gv.load(vbase, ld, 0, Tn, tid);
-  gkt.load(kbase, ld, 0, Tn, tid);
-  gk.store(sK[0], tid);
-  gv.store(sV[0], tid);
-  gkt.store(sKt[0], tid);
+  tile_load(kbase, ld, 0, Tn, tid, sK[0]);
+  tile_load(vbase, ld, 0, Tn, tid, sV[0]);
+  tile_wait();
   __syncthreads();
   int cur = 0;
   for (int k0 = 0; k0 < kend; k0 += 64, cur ^= 1) {
     const bool more = k0 + 64 < kend;
     if (more) {
-      gk.load(kbase, ld, k0 + 64, Tn, tid);
-      gv.load(vbase, ld, k0 + 64, Tn, tid);
-      gkt.load(kbase, ld, k0 + 64, Tn, tid);
+      tile_load(kbase, ld, k0 + 64, Tn, tid, sK[cur ^ 1]);
+      tile_load(vbase, ld, k0 + 64, Tn, tid, sV[cur ^ 1]);
     }
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
@@ -457,15 +431,11 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_mfma(const bf16_t* __restrict
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         const bf16x8_t pb = pack_acc(st, u);
-        dq0 = mfma(frag_cols(sKt[cur], l32, 32 * s + 16 * u, half), pb, dq0);
-        dq1 = mfma(frag_cols(sKt[cur], 32 + l32, 32 * s + 16 * u, half), pb, dq1);
+        dq0 = mfma(frag_tr(sK[cur], 0, 32 * s + 16 * u, lane), pb, dq0);
+        dq1 = mfma(frag_tr(sK[cur], 32, 32 * s + 16 * u, lane), pb, dq1);
       }
     }
-    if (more) {
-      gk.store(sK[cur ^ 1], tid);
-      gv.store(sV[cur ^ 1], tid);
-      gkt.store(sKt[cur ^ 1], tid);
-    }
+    tile_wait();
     __syncthreads();
   }
   if (myq < Tn) {
@@ -491,8 +461,6 @@ __global__ __launch_bounds__(256) void attn_bwd_dkv_mfma(const bf16_t* __restric
                                                          int C) {
   __shared__ __attribute__((aligned(16))) bf16_t sQ[2][64 * 64];
   __shared__ __attribute__((aligned(16))) bf16_t sG[2][64 * 64];
-  __shared__ __attribute__((aligned(16))) bf16_t sQt[2][64 * ATS];
-  __shared__ __attribute__((aligned(16))) bf16_t sGt[2][64 * ATS];
   __shared__ float sL[2][64], sD[2][64];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, half = lane >> 5, l32 = lane & 31;
   const int kbk = blockIdx.x;  // key block 0 has the most queries: dispatched first
@@ -521,14 +489,10 @@ __global__ __launch_bounds__(256) void attn_bwd_dkv_mfma(const bf16_t* __restric
   const bf16_t* gbase = dyb + h * 64;
   const float* lrow = lse + (long)bh * Tn;
   const float* drow = dbuf + (long)bh * Tn;
-  RowsStage gq, gg;
-  ColsStage gqt, ggt;
   float ll = 0.f, dl = 0.f;
-  auto load_all = [&](int q0) {
-    gq.load(qbase, ld, q0, Tn, tid);
-    gqt.load(qbase, ld, q0, Tn, tid);
-    gg.load(gbase, C, q0, Tn, tid);
-    ggt.load(gbase, C, q0, Tn, tid);
+  auto load_all = [&](int q0, int buf) {
+    tile_load(qbase, ld, q0, Tn, tid, sQ[buf]);
+    tile_load(gbase, C, q0, Tn, tid, sG[buf]);
     if (tid < 64) {
       int q = q0 + tid;
       ll = q < Tn ? lrow[q] * LOG2E_F : 0.f;
@@ -536,10 +500,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dkv_mfma(const bf16_t* __restric
     }
   };
   auto store_all = [&](int buf) {
-    gq.store(sQ[buf], tid);
-    gqt.store(sQt[buf], tid);
-    gg.store(sG[buf], tid);
-    ggt.store(sGt[buf], tid);
+    tile_wait();
     if (tid < 64) {
       sL[buf][tid] = ll;
       sD[buf][tid] = dl;
@@ -547,14 +508,14 @@ __global__ __launch_bounds__(256) void attn_bwd_dkv_mfma(const bf16_t* __restric
   };
   const int qstart = kbk * 128;
   if (qstart < Tn) {
-    load_all(qstart);
+    load_all(qstart, 0);
     store_all(0);
   }
   __syncthreads();
   int cur = 0;
   for (int q0 = qstart; q0 < Tn; q0 += 64, cur ^= 1) {
     const bool more = q0 + 64 < Tn;
-    if (more) load_all(q0 + 64);
+    if (more) load_all(q0 + 64, cur ^ 1);
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       const int qs = q0 + 32 * s;
@@ -579,10 +540,10 @@ __global__ __launch_bounds__(256) void attn_bwd_dkv_mfma(const bf16_t* __restric
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         bf16x8_t pp = pack_acc(pv, u), ps = pack_acc(st, u);
-        dv0 = mfma(frag_cols(sGt[cur], l32, 32 * s + 16 * u, half), pp, dv0);
-        dv1 = mfma(frag_cols(sGt[cur], 32 + l32, 32 * s + 16 * u, half), pp, dv1);
-        dk0 = mfma(frag_cols(sQt[cur], l32, 32 * s + 16 * u, half), ps, dk0);
-        dk1 = mfma(frag_cols(sQt[cur], 32 + l32, 32 * s + 16 * u, half), ps, dk1);
+        dv0 = mfma(frag_tr(sG[cur], 0, 32 * s + 16 * u, lane), pp, dv0);
+        dv1 = mfma(frag_tr(sG[cur], 32, 32 * s + 16 * u, lane), pp, dv1);
+        dk0 = mfma(frag_tr(sQ[cur], 0, 32 * s + 16 * u, lane), ps, dk0);
+        dk1 = mfma(frag_tr(sQ[cur], 32, 32 * s + 16 * u, lane), ps, dk1);
       }
     }
     if (more) store_all(cur ^ 1);

@@ -527,15 +527,23 @@ __global__ __launch_bounds__(256) void attn_bwd_dkv_mfma(const bf16_t* __restric
         dp = mfma(frag_rows(sG[cur], 32 * s + l32, kk * 2 + half), vf[kk], dp);
       }
       f32x16_t pv;
-      const bool edge = qs < kw0 + 31 || qs + 31 >= Tn;  // some (q, key) pair masked
+      if (qs < kw0 + 31 || qs + 31 >= Tn) {  // some (query, key) pair masked
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        int qi = 32 * s + 8 * (r >> 2) + 4 * half + (r & 3);
-        int q = q0 + qi;
-        float p = ex2(fmaf(st[r], sl2, -sL[cur][qi]));
-        if (edge && !(mykey <= q && q < Tn)) p = 0.f;
-        pv[r] = p;
-        st[r] = p * (dp[r] - sD[cur][qi]);
+        for (int r = 0; r < 16; ++r) {
+          const int qi = 32 * s + 8 * (r >> 2) + 4 * half + (r & 3);
+          const int q = q0 + qi;
+          const float p = (mykey <= q && q < Tn) ? ex2(fmaf(st[r], sl2, -sL[cur][qi])) : 0.f;
+          pv[r] = p;
+          st[r] = p * (dp[r] - sD[cur][qi]);
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int qi = 32 * s + 8 * (r >> 2) + 4 * half + (r & 3);
+          const float p = ex2(fmaf(st[r], sl2, -sL[cur][qi]));
+          pv[r] = p;
+          st[r] = p * (dp[r] - sD[cur][qi]);
+        }
       }
 #pragma unroll
       for (int u = 0; u < 2; ++u) {

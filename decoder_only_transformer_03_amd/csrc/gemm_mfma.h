@@ -38,6 +38,7 @@ template <int R, int NT>
 struct LoaderK {
   static constexpr int RPP = NT / 8;  // rows per pass
   uint4 v[R / RPP];
+  __device__ __forceinline__ void setup(const bf16_t*, long, long, long, int) {}
   __device__ __forceinline__ void issue(const bf16_t* __restrict__ X, long ld, long r0, long rtot,
                                         int k, int K, int tid, bf16_t*) {
     int c = tid & 7, rr = tid >> 3;
@@ -70,19 +71,31 @@ template <int R, int NT>
 struct LoaderD {
   static constexpr int NW = NT / 64;
   static constexpr int PER_WAVE = R / 8 / NW;  // wavefront instructions per tile
-  __device__ __forceinline__ void issue(const bf16_t* __restrict__ X, long ld, long r0, long rtot,
-                                        int k, int, int tid, bf16_t* s) {
+  // Per tile (setup): each lane's byte offsets from the tile's first row, so
+  // that a k-step only moves the wavefront-uniform base pointer.
+  const char* base;
+  uint32_t off[PER_WAVE];
+  __device__ __forceinline__ void setup(const bf16_t* __restrict__ X, long ld, long r0, long rtot,
+                                        int tid) {
     const int lane = tid & 63, w = tid >> 6;
+    base = reinterpret_cast<const char*>(X + r0 * ld);
+#pragma unroll
+    for (int j = 0; j < PER_WAVE; ++j) {
+      const int row = (w * PER_WAVE + j) * 8 + (lane >> 3);
+      const int c = (lane & 7) ^ ((row ^ (row >> 3)) & 7);
+      const long lrow = r0 + row < rtot ? row : rtot - 1 - r0;
+      off[j] = (uint32_t)((lrow * ld + c * 8) * 2);
+    }
+  }
+  __device__ __forceinline__ void issue(const bf16_t* __restrict__, long, long, long, int k, int,
+                                        int tid, bf16_t* s) {
+    const int w = tid >> 6;
+    const char* kb = base + 2L * k;
 #pragma unroll
     for (int j = 0; j < PER_WAVE; ++j) {
       const int rbase = (w * PER_WAVE + j) * 8;
-      const int row = rbase + (lane >> 3);
-      const int c = (lane & 7) ^ ((row ^ (row >> 3)) & 7);
-      long grow = r0 + row;
-      grow = grow < rtot ? grow : rtot - 1;
-      const bf16_t* src = X + grow * ld + k + c * 8;
       __builtin_amdgcn_global_load_lds(
-          (const __attribute__((address_space(1))) void*)src,
+          (const __attribute__((address_space(1))) void*)(kb + off[j]),
           (__attribute__((address_space(3))) void*)(s + rbase * BK), 16, 0, 0);
     }
   }
@@ -98,6 +111,7 @@ struct LoaderT {
   static constexpr int KR = 8 * R / NT;   // k rows per thread (2, 4 or 8)
   static_assert(KR == 2 || KR == 4 || KR == 8, "tile/thread combination");
   uint4 v[KR];
+  __device__ __forceinline__ void setup(const bf16_t*, long, long, long, int) {}
   __device__ __forceinline__ void issue(const bf16_t* __restrict__ X, long ld, long r0, long rtot,
                                         int k, int K, int tid, bf16_t*) {
     int rc = tid % RC, kg = tid / RC;
@@ -139,11 +153,83 @@ struct LoaderT {
   }
 };
 
-// Operand layout: 0 k-contiguous via registers, 1 transposed, 2 k-contiguous direct to LDS.
+// R rows x 64 k of a transposed operand (X[k*ld + row], rows contiguous), K a
+// multiple of 64, loaded straight into LDS as [64 k][R rows].  A wavefront
+// instruction fills 1 KB = 1024/(2R) k-rows; the 16-byte chunk c of k-row kr
+// is stored at chunk c ^ 4(kr%4), which keeps the transpose reads of the
+// fragments (4 consecutive k-rows x 64 bytes per half-wavefront) free of bank
+// conflicts.  Columns past the matrix edge re-read the last 8 (their products
+// are never stored).
+template <int R, int NT>
+struct LoaderDT {
+  static constexpr int NW = NT / 64;
+  static constexpr int CPR = R / 8;                     // 16-byte chunks per k-row
+  static constexpr int KPI = 64 / CPR;                  // k-rows per wavefront instruction
+  static constexpr int PER_WAVE = BK / KPI / NW;        // instructions per wavefront
+  static_assert(KPI * CPR == 64 && PER_WAVE * KPI * NW == BK, "tile/thread combination");
+  const char* base;
+  uint32_t off[PER_WAVE];
+  long ldb2;  // bytes per k-row in global memory
+  __device__ __forceinline__ void setup(const bf16_t* __restrict__ X, long ld, long r0, long rtot,
+                                        int tid) {
+    const int lane = tid & 63, w = tid >> 6;
+    base = reinterpret_cast<const char*>(X + r0);
+    ldb2 = 2 * ld;
+#pragma unroll
+    for (int j = 0; j < PER_WAVE; ++j) {
+      const int kr = (w * PER_WAVE + j) * KPI + lane / CPR;
+      const int c = (lane % CPR) ^ (4 * (kr & 3));
+      long col = (long)c * 8;
+      if (r0 + col + 8 > rtot) col = rtot - 8 - r0;
+      off[j] = (uint32_t)((kr * ld + col) * 2);
+    }
+  }
+  __device__ __forceinline__ void issue(const bf16_t* __restrict__, long, long, long, int k, int,
+                                        int tid, bf16_t* s) {
+    const int w = tid >> 6;
+    const char* kb = base + ldb2 * k;
+#pragma unroll
+    for (int j = 0; j < PER_WAVE; ++j) {
+      const int kr0 = (w * PER_WAVE + j) * KPI;
+      __builtin_amdgcn_global_load_lds(
+          (const __attribute__((address_space(1))) void*)(kb + off[j]),
+          (__attribute__((address_space(3))) void*)(s + kr0 * R), 16, 0, 0);
+    }
+  }
+  __device__ __forceinline__ void commit(bf16_t*, int) const {}
+};
+
+typedef short gemm_short4 __attribute__((ext_vector_type(4)));
+
+// Fragment of a [64 k][R] tile for matrix row `row` (this lane's row) and
+// contraction slots 8h + 0..7 of substep kk (h = lane/32), from two LDS
+// transpose reads: in each 16-lane group, lane t addresses k-row t/4 and rows
+// 4(t%4)..+3 of the matrix, and receives matrix row t of the 4 k-rows.
+template <int R>
+__device__ __forceinline__ bf16x8_t frag_tr(const bf16_t* s, int rbase, int kk, int lane) {
+  const int g = lane >> 4, t = lane & 15;
+  const int col = rbase + 16 * (g & 1) + 4 * (t & 3);
+  uint32_t w[4];
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    const int kr = 16 * kk + 8 * (g >> 1) + 4 * half + (t >> 2);
+    const bf16_t* p = s + kr * R + ((((col >> 3) ^ (4 * (kr & 3)))) << 3) + (col & 7);
+    const gemm_short4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) gemm_short4*)((__attribute__((address_space(3))) bf16_t*)p));
+    const uint2 u = __builtin_bit_cast(uint2, v);
+    w[2 * half] = u.x;
+    w[2 * half + 1] = u.y;
+  }
+  return __builtin_bit_cast(bf16x8_t, make_uint4(w[0], w[1], w[2], w[3]));
+}
+
+// Operand layout: 0 k-contiguous via registers, 1 transposed via registers,
+// 2 k-contiguous direct to LDS, 3 transposed direct to LDS.
 template <int R, int L, int NT> struct Loader;
 template <int R, int NT> struct Loader<R, 0, NT> : LoaderK<R, NT> {};
 template <int R, int NT> struct Loader<R, 1, NT> : LoaderT<R, NT> {};
 template <int R, int NT> struct Loader<R, 2, NT> : LoaderD<R, NT> {};
+template <int R, int NT> struct Loader<R, 3, NT> : LoaderDT<R, NT> {};
 
 // Epilogue of one output tile, staged through LDS so that global memory sees
 // whole row segments.  acc[sn][sm][4i + j] is C[m][n] with m = sm*32 +
@@ -315,11 +401,13 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(int M, int N, int
 
   Loader<BM, LA, NT> la;
   Loader<BN, LB, NT> lb;
+  la.setup(A, lda, m0, M, tid);
+  lb.setup(B, ldb, n0, N, tid);
   la.issue(A, lda, m0, M, kt0 * BK, K, tid, smem[0]);
   lb.issue(B, ldb, n0, N, kt0 * BK, K, tid, smem[0] + BM * BK);
   la.commit(smem[0], tid);
   lb.commit(smem[0] + BM * BK, tid);
-  if constexpr (LA == 2 || LB == 2) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  if constexpr (LA >= 2 || LB >= 2) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
 
   // Fragments of k-substep kk (16 deep) for this wavefront's sub-tiles.
@@ -327,13 +415,21 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(int M, int N, int
     const int c = kk * 2 + (lane >> 5);
 #pragma unroll
     for (int sm = 0; sm < SM; ++sm) {
-      int row = wm * WTM + sm * 32 + (lane & 31);
-      fa[sm] = *reinterpret_cast<const bf16x8_t*>(sA + row * BK + swz(row, c) * 8);
+      if constexpr (LA == 3) {
+        fa[sm] = frag_tr<BM>(sA, wm * WTM + sm * 32, kk, lane);
+      } else {
+        int row = wm * WTM + sm * 32 + (lane & 31);
+        fa[sm] = *reinterpret_cast<const bf16x8_t*>(sA + row * BK + swz(row, c) * 8);
+      }
     }
 #pragma unroll
     for (int sn = 0; sn < SN; ++sn) {
-      int row = wn * WTN + sn * 32 + (lane & 31);
-      fb[sn] = *reinterpret_cast<const bf16x8_t*>(sB + row * BK + swz(row, c) * 8);
+      if constexpr (LB == 3) {
+        fb[sn] = frag_tr<BN>(sB, wn * WTN + sn * 32, kk, lane);
+      } else {
+        int row = wn * WTN + sn * 32 + (lane & 31);
+        fb[sn] = *reinterpret_cast<const bf16x8_t*>(sB + row * BK + swz(row, c) * 8);
+      }
     }
   };
 
@@ -351,7 +447,11 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(int M, int N, int
       const bool last_k = kt + 1 == ekt1;
       const bool more = !last_k || item + gridDim.x < nitems;
       if (more) {
-        if (last_k) decode(item + gridDim.x);
+        if (last_k) {
+          decode(item + gridDim.x);
+          la.setup(A, lda, m0, M, tid);
+          lb.setup(B, ldb, n0, N, tid);
+        }
         const int nk = last_k ? kt0 : kt + 1;
         la.issue(A, lda, m0, M, nk * BK, K, tid, smem[cur ^ 1]);
         lb.issue(B, ldb, n0, N, nk * BK, K, tid, smem[cur ^ 1] + BM * BK);
@@ -373,7 +473,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(int M, int N, int
       if (more) {
         la.commit(smem[cur ^ 1], tid);
         lb.commit(smem[cur ^ 1] + BM * BK, tid);
-        if constexpr (LA == 2 || LB == 2) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        if constexpr (LA >= 2 || LB >= 2) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       }
       __syncthreads();
       // (the next item's first fragments are read after the epilogue, so
@@ -478,10 +578,10 @@ hipError_t dispatch(int M, int N, int K, const bf16_t* A, long lda, const bf16_t
       long cap = nkt / 4 > 0 ? nkt / 4 : 1;                                                     \
       split_k = (int)(want < cap ? want : cap);                                                 \
     }                                                                                           \
-    /* k-contiguous operands go straight to LDS when whole 64-deep tiles exist */              \
+    /* operands go straight to LDS when whole 64-deep tiles exist */                            \
     const bool direct = K % 64 == 0;                                                            \
     constexpr int TA = AT ? 1 : 0, TB = BT ? 1 : 0;                                             \
-    if (direct) return by_epi<AT ? 1 : 2, BT ? 1 : 2>(M, N, K, A, lda, B, ldb, epi, out_t, e, split_k, s); \
+    if (direct) return by_epi<AT ? 3 : 2, BT ? 3 : 2>(M, N, K, A, lda, B, ldb, epi, out_t, e, split_k, s); \
     return by_epi<TA, TB>(M, N, K, A, lda, B, ldb, epi, out_t, e, split_k, s);                 \
   }                                                                                             \
   }

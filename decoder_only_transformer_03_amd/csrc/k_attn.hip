@@ -189,6 +189,19 @@ __device__ __forceinline__ void tile_load(const bf16_t* __restrict__ X, long ld,
 
 __device__ __forceinline__ void tile_wait() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
+// Work item of this workgroup: (block index along the sequence, batch*head).
+// Workgroups are handed to the 8 XCDs round-robin by flat id; the ids are
+// permuted so that each XCD gets a contiguous range of heads and all sequence
+// blocks of a head run on one XCD, sharing its L2 for that head's K/V (or
+// Q/dO).  Within a head, blocks come in the order given by `rev`.
+__device__ __forceinline__ void attn_item(bool rev, int& blk, int& bh) {
+  const int nb = gridDim.x, total = nb * gridDim.y;
+  int id = blockIdx.y * nb + blockIdx.x;
+  if ((total & 7) == 0) id = (id & 7) * (total >> 3) + (id >> 3);
+  bh = id / nb;
+  blk = rev ? nb - 1 - id % nb : id % nb;
+}
+
 // 16-byte fragment: 8 consecutive columns (chunk c) of one row.
 __device__ __forceinline__ bf16x8_t frag_rows(const bf16_t* s, int row, int c) {
   return *reinterpret_cast<const bf16x8_t*>(s + row * 64 + ((c ^ xr(row)) << 3));
@@ -255,8 +268,9 @@ __global__ __launch_bounds__(256) void attn_fwd_mfma(const bf16_t* __restrict__ 
   __shared__ __attribute__((aligned(16))) bf16_t sK[2][64 * 64];
   __shared__ __attribute__((aligned(16))) bf16_t sV[2][64 * 64];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, half = lane >> 5, l32 = lane & 31;
-  const int qb = gridDim.x - 1 - blockIdx.x;  // longest rows first
-  const int bh = blockIdx.y, b = bh / H, h = bh % H;
+  int qb, bh;
+  attn_item(true, qb, bh);  // longest rows first
+  const int b = bh / H, h = bh % H;
   const long ld = 3L * C;
   const bf16_t* base = qkv + (long)b * Tn * ld;
   const bf16_t* kbase = base + C + h * 64;
@@ -364,8 +378,9 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_mfma(const bf16_t* __restrict
   __shared__ __attribute__((aligned(16))) bf16_t sK[2][64 * 64];
   __shared__ __attribute__((aligned(16))) bf16_t sV[2][64 * 64];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, half = lane >> 5, l32 = lane & 31;
-  const int qb = gridDim.x - 1 - blockIdx.x;
-  const int bh = blockIdx.y, b = bh / H, h = bh % H;
+  int qb, bh;
+  attn_item(true, qb, bh);
+  const int b = bh / H, h = bh % H;
   const long ld = 3L * C;
   const bf16_t* base = qkv + (long)b * Tn * ld;
   const bf16_t* dyb = dy + (long)b * Tn * C;
@@ -463,8 +478,9 @@ __global__ __launch_bounds__(256) void attn_bwd_dkv_mfma(const bf16_t* __restric
   __shared__ __attribute__((aligned(16))) bf16_t sG[2][64 * 64];
   __shared__ float sL[2][64], sD[2][64];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, half = lane >> 5, l32 = lane & 31;
-  const int kbk = blockIdx.x;  // key block 0 has the most queries: dispatched first
-  const int bh = blockIdx.y, b = bh / H, h = bh % H;
+  int kbk, bh;
+  attn_item(false, kbk, bh);  // key block 0 has the most queries: dispatched first
+  const int b = bh / H, h = bh % H;
   const long ld = 3L * C;
   const bf16_t* base = qkv + (long)b * Tn * ld;
   const bf16_t* dyb = dy + (long)b * Tn * C;

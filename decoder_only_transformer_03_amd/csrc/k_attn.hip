@@ -300,46 +300,69 @@ __global__ __launch_bounds__(256) void attn_fwd_mfma(const bf16_t* __restrict__ 
       tile_load(vbase, ld, k0 + 64, Tn, tid, sV[cur ^ 1]);
     }
     if (k0 <= q0w + 31) {  // this wavefront has unmasked keys in the block
-      // S^T for keys k0..k0+31 (sa) and k0+32..k0+63 (sb): two independent chains
-      f32x16_t sa = zero16(), sb = zero16();
+      // S^T for keys k0..k0+31 (sa) and k0+32..k0+63 (sb): two independent
+      // chains; masked entries -inf
+      f32x16_t sa, sb;
+      auto scores = [&]() {
+        sa = zero16();
+        sb = zero16();
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        sa = mfma(frag_rows(sK[cur], l32, kk * 2 + half), qf[kk], sa);
-        sb = mfma(frag_rows(sK[cur], 32 + l32, kk * 2 + half), qf[kk], sb);
-      }
-      float mx = NEG_INF;
-      if (k0 + 63 > q0w || k0 + 63 >= Tn) {  // diagonal or ragged block: mask
+        for (int kk = 0; kk < 4; ++kk) {
+          sa = mfma(frag_rows(sK[cur], l32, kk * 2 + half), qf[kk], sa);
+          sb = mfma(frag_rows(sK[cur], 32 + l32, kk * 2 + half), qf[kk], sb);
+        }
+        if (k0 + 63 > q0w || k0 + 63 >= Tn) {  // diagonal or ragged block
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = k0 + 8 * (r >> 2) + 4 * half + (r & 3);
+            sa[r] = (key > myq || key >= Tn) ? NEG_INF : sa[r];
+            sb[r] = (key + 32 > myq || key + 32 >= Tn) ? NEG_INF : sb[r];
+          }
+        }
+      };
+      scores();
+      // Probabilities are taken against the running reference m2 (log2
+      // units) without looking for the block maximum.  Only when a block's
+      // sum exceeds 2^16 -- some score rose far above m2 -- or on the first
+      // block is the block rescored, its maximum taken, and O and the sum
+      // rescaled to the new reference.  Probabilities stay below 2^16 or so:
+      // harmless in fp32 and bf16, and the normalisation at the end is exact.
+      // (key 0 is visible to every query, so after the wavefront's first
+      // block, k0 == 0, every lane has a finite reference)
+      const bool first = k0 == 0;
+      float bs = 0.f;
+      bool redo = first;
+      if (!first) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int key = k0 + 8 * (r >> 2) + 4 * half + (r & 3);
-          sa[r] = (key > myq || key >= Tn) ? NEG_INF : sa[r];
-          sb[r] = (key + 32 > myq || key + 32 >= Tn) ? NEG_INF : sb[r];
-          mx = fmaxf(mx, fmaxf(sa[r], sb[r]));
+          sa[r] = ex2(fmaf(sa[r], sl2, -m2));
+          sb[r] = ex2(fmaf(sb[r], sl2, -m2));
+          bs += sa[r] + sb[r];
         }
-      } else {
+        redo = !(bs <= 65536.0f);
+      }
+      if (__any(redo)) {
+        if (!first) scores();
+        float mx = NEG_INF;
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, fmaxf(sa[r], sb[r]));
-      }
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      // Lazy rescaling: the running maximum m2 (log2 units) only moves when a
-      // score exceeds it by more than 8, so most blocks skip rescaling O.
-      // Probabilities are then bounded by 2^8, harmless in fp32 and bf16.
-      const float mnew = mx * sl2;
-      const bool need = mnew > m2 + 8.0f;
-      if (__any(need)) {
-        const float alpha = need ? ex2(m2 - mnew) : 1.0f;
-        m2 = need ? mnew : m2;
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        const float mn = fmaxf(m2, mx * sl2);
+        const float alpha = first ? 0.f : ex2(m2 - mn);
+        m2 = mn;
         ls *= alpha;
         o0 *= alpha;
         o1 *= alpha;
-      }
-      const float ms = m2 == NEG_INF ? 0.f : m2;
+        const float ms = m2 == NEG_INF ? 0.f : m2;
+        bs = 0.f;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        sa[r] = ex2(fmaf(sa[r], sl2, -ms));
-        sb[r] = ex2(fmaf(sb[r], sl2, -ms));
-        ls += sa[r] + sb[r];
+        for (int r = 0; r < 16; ++r) {
+          sa[r] = ex2(fmaf(sa[r], sl2, -ms));
+          sb[r] = ex2(fmaf(sb[r], sl2, -ms));
+          bs += sa[r] + sb[r];
+        }
       }
+      ls += bs;
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
         const bf16x8_t pa = pack_acc(sa, u), pb = pack_acc(sb, u);

@@ -92,3 +92,10 @@ __device__ __forceinline__ float gelu_tanh_grad_f(float x) {
   float s = gelu_sig_f(x, &du);
   return s + 2.0f * x * s * (1.0f - s) * du;
 }
+// Both at once (one exponential): returns gelu(x), stores gelu'(x).
+__device__ __forceinline__ float gelu_tanh_and_grad_f(float x, float* grad) {
+  float du;
+  float s = gelu_sig_f(x, &du);
+  *grad = s + 2.0f * x * s * (1.0f - s) * du;
+  return x * s;
+}

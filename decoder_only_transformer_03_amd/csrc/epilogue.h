@@ -5,11 +5,12 @@
 
 enum EpiKind : int {
   EPI_STORE = 0,     // out[m][n] = alpha*c                                   (out: TO)
-  EPI_BIAS_GELU = 1, // h = c + bias[n]; out[m][n] = h; out2[m][n] = gelu(h)  (out, out2: TO)
+  EPI_BIAS_GELU = 1, // h = c + bias[n]; out[m][n] = gelu'(h); out2[m][n] = gelu(h)  (TO)
   EPI_RESID = 2,     // out[m][n] = resid[m][n] + c + bias[n]                  (out, resid: fp32)
   EPI_ACCUM = 3,     // out[m][n] += alpha*c            one writer per element (out: fp32)
   EPI_ATOMIC = 4,    // atomically out[m][n] += alpha*c  split-K               (out: fp32)
-  EPI_GELU_BWD = 5,  // out[m][n] = alpha*c * gelu'(aux[m][n])                 (out, aux: TO)
+  EPI_GELU_BWD = 5,  // out[m][n] = alpha*c * aux[m][n], aux = gelu'(h)          (out, aux: TO)
+                     // (+ column sums of the fp32 result into colsum, if set)
   EPI_PARTIAL = 6,   // split-K slice z: out[z*split_stride + m*ldo + n] = alpha*c  (fp32)
   EPI_BIAS = 7,      // out[m][n] = alpha*c + bias[n]                         (out: TO)
 };
@@ -25,6 +26,7 @@ struct EpiArgs {
   long ldx;
   float alpha;
   long split_stride;
+  float* colsum;  // EPI_GELU_BWD: [row block of 128][N] partial column sums, or null
 };
 
 // Does the epilogue read memory per element (residual, old value, aux)?
@@ -71,10 +73,10 @@ __device__ __forceinline__ void epi_store4(const EpiArgs& e, long m, int n, cons
   if constexpr (EPI == EPI_STORE || EPI == EPI_BIAS) {
     st4(reinterpret_cast<TO*>(e.out) + m * e.ldo + n, r);
   } else if constexpr (EPI == EPI_BIAS_GELU) {
-    st4(reinterpret_cast<TO*>(e.out) + m * e.ldo + n, r);
-    float g[4];
+    float g[4], d[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) g[j] = gelu_tanh_f(r[j]);
+    for (int j = 0; j < 4; ++j) g[j] = gelu_tanh_and_grad_f(r[j], d + j);
+    st4(reinterpret_cast<TO*>(e.out) + m * e.ldo + n, d);
     st4(reinterpret_cast<TO*>(e.out2) + m * e.ldo + n, g);
   } else if constexpr (EPI == EPI_RESID) {
 #pragma unroll
@@ -92,7 +94,7 @@ __device__ __forceinline__ void epi_store4(const EpiArgs& e, long m, int n, cons
     st4(reinterpret_cast<float*>(e.out) + split * e.split_stride + m * e.ldo + n, r);
   } else if constexpr (EPI == EPI_GELU_BWD) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) r[j] *= gelu_tanh_grad_f(in[j]);
+    for (int j = 0; j < 4; ++j) r[j] *= in[j];
     st4(reinterpret_cast<TO*>(e.out) + m * e.ldo + n, r);
   }
 }

@@ -262,6 +262,11 @@ __device__ __forceinline__ void tile_epilogue(const EpiArgs& e, const f32x16_t (
       ld4(e.bias + nl + 4, bias8 + 4);
     }
   }
+  // EPI_GELU_BWD: column sums of the result over the sub-tile's rows (the
+  // bias gradient of the layer that produced the pre-activation)
+  float csum[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) csum[j] = 0.f;
 #pragma unroll
   for (int sm = 0; sm < SM; ++sm) {
     // (1) fragments -> round buffer (row = lane%32, one 16-byte chunk each)
@@ -298,10 +303,11 @@ __device__ __forceinline__ void tile_epilogue(const EpiArgs& e, const f32x16_t (
           st4(reinterpret_cast<TO*>(e.out) + m * e.ldo + nl, v);
           st4(reinterpret_cast<TO*>(e.out) + m * e.ldo + nl + 4, v + 4);
         } else if constexpr (EPI == EPI_BIAS_GELU) {
-          st4(reinterpret_cast<TO*>(e.out) + m * e.ldo + nl, v);
-          st4(reinterpret_cast<TO*>(e.out) + m * e.ldo + nl + 4, v + 4);
+          float d[8];
 #pragma unroll
-          for (int j = 0; j < 8; ++j) v[j] = gelu_tanh_f(v[j]);
+          for (int j = 0; j < 8; ++j) v[j] = gelu_tanh_and_grad_f(v[j], d + j);
+          st4(reinterpret_cast<TO*>(e.out) + m * e.ldo + nl, d);
+          st4(reinterpret_cast<TO*>(e.out) + m * e.ldo + nl + 4, d + 4);
           st4(reinterpret_cast<TO*>(e.out2) + m * e.ldo + nl, v);
           st4(reinterpret_cast<TO*>(e.out2) + m * e.ldo + nl + 4, v + 4);
         } else if constexpr (EPI == EPI_RESID) {
@@ -330,11 +336,14 @@ __device__ __forceinline__ void tile_epilogue(const EpiArgs& e, const f32x16_t (
           st4(o, v);
           st4(o + 4, v + 4);
         } else if constexpr (EPI == EPI_GELU_BWD) {
-          float hh[8];
-          ld4(reinterpret_cast<const TO*>(e.aux) + m * e.ldx + nl, hh);
-          ld4(reinterpret_cast<const TO*>(e.aux) + m * e.ldx + nl + 4, hh + 4);
+          float dg[8];
+          ld4(reinterpret_cast<const TO*>(e.aux) + m * e.ldx + nl, dg);
+          ld4(reinterpret_cast<const TO*>(e.aux) + m * e.ldx + nl + 4, dg + 4);
 #pragma unroll
-          for (int j = 0; j < 8; ++j) v[j] *= gelu_tanh_grad_f(hh[j]);
+          for (int j = 0; j < 8; ++j) {
+            v[j] *= dg[j];
+            csum[j] += v[j];
+          }
           st4(reinterpret_cast<TO*>(e.out) + m * e.ldo + nl, v);
           st4(reinterpret_cast<TO*>(e.out) + m * e.ldo + nl + 4, v + 4);
         }
@@ -342,6 +351,21 @@ __device__ __forceinline__ void tile_epilogue(const EpiArgs& e, const f32x16_t (
     }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
+  }
+  if constexpr (EPI == EPI_GELU_BWD) {
+    if (e.colsum) {
+      // lanes l, l^8, ..., l^56 hold the same 8 columns for different rows
+#pragma unroll
+      for (int o = 8; o < 64; o <<= 1)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) csum[j] += __shfl_xor(csum[j], o, 64);
+      static_assert(WTM == 128, "column sums are kept per 128-row block");
+      if (lane < 8 && ncol) {
+        float* dst = e.colsum + (mw / 128) * (long)N + nl;
+        st4(dst, csum);
+        st4(dst + 4, csum + 4);
+      }
+    }
   }
 }
 

@@ -162,6 +162,7 @@ struct gpt2 {
   float* ln_partial;
   float* bias_partial;
   float* splitk;
+  float* colsum_partial;  // per-128-row column sums of dh (c_fc bias gradient)
   // state
   int B = 0, T = 0;
   bool have_targets = false;
@@ -234,6 +235,7 @@ size_t plan(const gpt2_config* c, char* base, gpt2* h) {
   float* dbuf = a.take_n<float>(BT * H);
   float* ln_partial = a.take_n<float>((size_t)ln_bwd_scratch((long)BT, (int)C));
   float* bias_partial = a.take_n<float>((size_t)BIAS_SPLITS * 4 * C);
+  float* colsum_partial = a.take_n<float>((BT + 127) / 128 * 4 * C);
   float* splitk = a.take_n<float>((size_t)SPLITK_PART_ELEMS);
   size_t total = (a.off + 255) & ~(size_t)255;
   if (h) {
@@ -248,6 +250,7 @@ size_t plan(const gpt2_config* c, char* base, gpt2* h) {
     h->dres = dres; h->dres_b = dres_b; h->dxtmp = dxtmp; h->dbig = dbig; h->dqkv = dqkv;
     h->dy = dy; h->dbuf = dbuf; h->ln_partial = ln_partial; h->bias_partial = bias_partial;
     h->splitk = splitk;
+    h->colsum_partial = colsum_partial;
   }
   return total;
 }
@@ -403,9 +406,13 @@ gpt2_status run_backward(gpt2* h, float scale) {
     const LayerOff& o = h->lay.layer[l];
     LayerAct& a = h->A[l];
     // x_out = x_mid + c_proj(gelu(c_fc(ln_2(x_mid))))
+    // dh = dg * gelu'(h), the forward having saved gelu'(h); in bf16 mode the
+    // same epilogue leaves per-128-row column sums of dh (the c_fc bias
+    // gradient) in colsum_partial
     EpiArgs e = epi(h->dbig, 4 * C);
     e.aux = a.h;
     e.ldx = 4 * C;
+    if (at == DT_BF16) e.colsum = h->colsum_partial;
     TIMED(h, GPT2_SITE_FCPROJ_DX, launch_gemm(at, M, 4 * C, C, dres_in, C, false, W(h, o.fc2w), 4 * C, true,
                           EPI_GELU_BWD, at, e, 0, s));
     TIMED(h, GPT2_SITE_FCPROJ_DW, launch_gemm_wgrad(at, C, 4 * C, M, dres_in, C, true, a.g, 4 * C, true,
@@ -415,7 +422,10 @@ gpt2_status run_backward(gpt2* h, float scale) {
                           DT_F32, epi(h->dxtmp, C), 0, s));
     TIMED(h, GPT2_SITE_FC_DW, launch_gemm_wgrad(at, 4 * C, C, M, h->dbig, 4 * C, true, a.u2, C, true,
                                                 G + o.fcw, C, 1.f, h->splitk, SPLITK_PART_ELEMS, s));
-    TIMED(h, GPT2_SITE_BIAS_GRAD, launch_bias_grad(at, h->dbig, BT, 4 * C, 4 * C, h->bias_partial, G + o.fcb, s));
+    if (at == DT_BF16)
+      TIMED(h, GPT2_SITE_BIAS_GRAD, launch_colsum_finish(h->colsum_partial, (M + 127) / 128, 4 * C, G + o.fcb, s));
+    else
+      TIMED(h, GPT2_SITE_BIAS_GRAD, launch_bias_grad(at, h->dbig, BT, 4 * C, 4 * C, h->bias_partial, G + o.fcb, s));
     TIMED(h, GPT2_SITE_LN_BWD, launch_layernorm_bwd(at, h->dxtmp, a.x_mid, a.mean2, a.rstd2, P + o.ln2w, h->dres,
                                    dres_copy, 1, h->ln_partial, G + o.ln2w, G + o.ln2b,
                                    G + o.projb, BT, C, s));
@@ -676,7 +686,7 @@ gpt2_status gpt2_get_activation(gpt2_t* h, int which, int layer, float* h_dst, s
     case GPT2_ACT_LSE: src = a->lse; count = BT * c.n_head; f32 = true; break;
     case GPT2_ACT_X_MID: src = a->x_mid; count = BT * C; f32 = true; break;
     case GPT2_ACT_LN2: src = a->u2; count = BT * C; break;
-    case GPT2_ACT_FC_PRE: src = a->h; count = BT * 4 * C; break;
+    case GPT2_ACT_FC_DGELU: src = a->h; count = BT * 4 * C; break;
     case GPT2_ACT_FC_GELU: src = a->g; count = BT * 4 * C; break;
     case GPT2_ACT_LNF: src = h->z; count = BT * C; break;
     case GPT2_ACT_LOGITS: src = h->logits; count = BT * c.padded_vocab_size; break;

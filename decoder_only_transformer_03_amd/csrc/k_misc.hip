@@ -664,6 +664,13 @@ hipError_t launch_layernorm_bwd(DType copy_t, const float* dy, const float* x, c
   return colsum_into(partial, nb, 3 * C, scratch, C, dw, db, dsum, s);
 }
 
+hipError_t launch_colsum_finish(const float* partial, int nparts, int ncols, float* dst,
+                                hipStream_t s) {
+  colsum_finish_kernel<<<nblk(ncols, 64), 256, 0, s>>>(partial, nparts, ncols, dst, nullptr,
+                                                       nullptr, ncols);
+  return hipGetLastError();
+}
+
 hipError_t launch_bias_grad(DType in_t, const void* X, long rows, int N, long ldx, float* partial,
                             float* db, hipStream_t s) {
   int splits = BIAS_SPLITS;

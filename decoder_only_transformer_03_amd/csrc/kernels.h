@@ -41,6 +41,9 @@ hipError_t launch_layernorm_bwd(DType copy_t, const float* dy, const float* x, c
                                 const float* rstd, const float* w, float* dres, void* dres_copy,
                                 int accumulate, float* partial, float* dw, float* db,
                                 float* dsum, long rows, int C, hipStream_t s);
+// dst[c] += sum_p partial[p*ncols + c], p = 0..nparts-1 in order.
+hipError_t launch_colsum_finish(const float* partial, int nparts, int ncols, float* dst,
+                                hipStream_t s);
 hipError_t launch_bias_grad(DType in_t, const void* X, long rows, int N, long ldx, float* partial,
                             float* db, hipStream_t s);
 hipError_t launch_xent(DType t, void* logits, const int32_t* targets, int* n_valid,

@@ -24,7 +24,7 @@ SITES = ["EMBED_FWD", "LN_FWD", "QKV_FWD", "ATTN_FWD", "PROJ_FWD", "FC_FWD", "FC
          "FC_DW", "PROJ_DX", "PROJ_DW", "ATTN_BWD", "QKV_DX", "QKV_DW", "BIAS_GRAD", "EMBED_BWD",
          "GRAD_NORM", "ADAMW", "ZERO_GRAD"]
 ACT = {n: i for i, n in enumerate([
-    "X_IN", "LN1", "QKV", "ATTN_Y", "LSE", "X_MID", "LN2", "FC_PRE", "FC_GELU", "LNF", "LOGITS",
+    "X_IN", "LN1", "QKV", "ATTN_Y", "LSE", "X_MID", "LN2", "FC_DGELU", "FC_GELU", "LNF", "LOGITS",
     "ROW_LOSS"])}
 STATUS_NAMES = {0: "GPT2_OK", -1: "GPT2_E_ARG", -2: "GPT2_E_SHAPE", -3: "GPT2_E_RANGE",
                 -4: "GPT2_E_STATE", -5: "GPT2_E_HIP"}

@@ -186,14 +186,15 @@ void gpt2_destroy(gpt2_t* h);
  *   ATTN_Y    attention output with heads re-interleaved, B*T*C
  *   LSE       per (b, head, t) log-sum-exp of the scaled, masked scores, B*H*T
  *   X_MID     residual stream after attention, B*T*C
- *   LN2       ln_2 output, B*T*C          FC_PRE  c_fc output before GELU, B*T*4C
+ *   LN2       ln_2 output, B*T*C
+ *   FC_DGELU  GELU derivative at the c_fc output, gelu'(h) (saved for the backward), B*T*4C
  *   FC_GELU   GELU output, B*T*4C         LNF     ln_f output, B*T*C
  *   LOGITS    logits (forward without targets) or, after a forward with
  *             targets, d(loss)/d(logits) which replaces them, B*T*Vp
  *   ROW_LOSS  per-position loss (0 where target == -1), B*T */
 enum {
   GPT2_ACT_X_IN = 0, GPT2_ACT_LN1, GPT2_ACT_QKV, GPT2_ACT_ATTN_Y, GPT2_ACT_LSE, GPT2_ACT_X_MID,
-  GPT2_ACT_LN2, GPT2_ACT_FC_PRE, GPT2_ACT_FC_GELU, GPT2_ACT_LNF, GPT2_ACT_LOGITS,
+  GPT2_ACT_LN2, GPT2_ACT_FC_DGELU, GPT2_ACT_FC_GELU, GPT2_ACT_LNF, GPT2_ACT_LOGITS,
   GPT2_ACT_ROW_LOSS
 };
 gpt2_status gpt2_get_activation(gpt2_t* h, int which, int layer, float* h_dst, size_t n);

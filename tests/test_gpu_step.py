@@ -76,6 +76,8 @@ def run_gpu_step(d, prec, flat, idx, tgt, lr=LR, wd=WD):
     C = d["n_embd"]
     out["x_in"] = [m.activation("X_IN", l, B * T * C) for l in range(d["n_layer"] + 1)]
     out["row_loss"] = m.activation("ROW_LOSS", 0, B * T)
+    out["dgelu"] = [m.activation("FC_DGELU", l, B * T * 4 * C) for l in range(d["n_layer"])]
+    out["gelu"] = [m.activation("FC_GELU", l, B * T * 4 * C) for l in range(d["n_layer"])]
     out["dlogits"] = m.activation("LOGITS", 0, B * T * d["padded_vocab_size"])
     m.backward(1.0)
     out["grads"] = m.get(G.GPT2_GRADS)
@@ -123,6 +125,12 @@ def test_fp32_tiny_step_matches_oracle(B, T):
         assert maxrel(g["x_in"][l], r["cache"]["layers"][l]["x_in"].reshape(-1)) < 1e-4
     assert maxrel(g["x_in"][-1], r["cache"]["x_final"].reshape(-1)) < 1e-4
     assert maxrel(g["row_loss"], r["cache"]["row_loss"]) < 1e-4
+    # the MLP's saved activations: gelu(h) and the derivative gelu'(h) that
+    # the backward pass multiplies by
+    for l in range(d["n_layer"]):
+        h_ref = r["cache"]["layers"][l]["h"].reshape(-1).astype(np.float64)
+        assert maxrel(g["gelu"][l], O.gelu_tanh(h_ref)) < 1e-4
+        assert maxrel(g["dgelu"][l], O.gelu_tanh_grad(h_ref)) < 1e-4
     dl_ref = r["cache"]["dlogits"].reshape(-1)
     assert maxrel(g["dlogits"], dl_ref) < 1e-4
     ign = np.repeat(tgt.reshape(-1) == -1, d["padded_vocab_size"])

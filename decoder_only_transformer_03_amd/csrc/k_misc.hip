@@ -185,46 +185,67 @@ __global__ __launch_bounds__(256) void layernorm_bwd_kernel(
   }
   long r0 = (long)blockIdx.x * rows_per_block;
   long r1 = r0 + rows_per_block < rows ? r0 + rows_per_block : rows;
-  for (long row = r0 + wave; row < r1; row += 4) {
-    float mu = mean[row], rs = rstd[row];
-    float g[NV][4], xh[NV][4];
-    float s1 = 0.f, s2 = 0.f;
+  // two rows per wavefront at a time (row, row + 4): all their loads -- dy,
+  // x and the old dres -- are issued before any reduction needs them
+  for (long row0 = r0 + wave; row0 < r1; row0 += 8) {
+    float g[2][NV][4], xh[2][NV][4], o[2][NV][4], mu[2], rs[2];
 #pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      int c = (i * 64 + lane) * 4;
-      if (c < C) {
-        float xv[4];
-        ld4(dy + row * C + c, g[i]);
-        ld4(x + row * C + c, xv);
+    for (int q = 0; q < 2; ++q) {
+      const long row = row0 + 4 * q;
+      const bool on = row < r1;
+      mu[q] = on ? mean[row] : 0.f;
+      rs[q] = on ? rstd[row] : 0.f;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          xh[i][j] = (xv[j] - mu) * rs;
-          dg[i][j] += g[i][j] * xh[i][j];
-          db[i][j] += g[i][j];
-          float d = g[i][j] * wv[i][j];
-          g[i][j] = d;
-          s1 += d;
-          s2 += d * xh[i][j];
+      for (int i = 0; i < NV; ++i) {
+        int c = (i * 64 + lane) * 4;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) g[q][i][j] = xh[q][i][j] = o[q][i][j] = 0.f;
+        if (on && c < C) {
+          ld4(dy + row * C + c, g[q][i]);
+          ld4(x + row * C + c, xh[q][i]);
+          if (accumulate) ld4(dres + row * C + c, o[q][i]);
         }
       }
     }
-    s1 = wave_sum(s1) / (float)C;
-    s2 = wave_sum(s2) / (float)C;
 #pragma unroll
-    for (int i = 0; i < NV; ++i) {
-      int c = (i * 64 + lane) * 4;
-      if (c < C) {
-        float o[4];
-        float* dr = dres + row * C + c;
-        if (accumulate) ld4(dr, o);
+    for (int q = 0; q < 2; ++q) {
+      const long row = row0 + 4 * q;
+      if (row >= r1) break;
+      float s1 = 0.f, s2 = 0.f;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          float dx = rs * (g[i][j] - s1 - xh[i][j] * s2);
-          o[j] = accumulate ? o[j] + dx : dx;
-          ds[i][j] += o[j];
+      for (int i = 0; i < NV; ++i) {
+        int c = (i * 64 + lane) * 4;
+        if (c < C) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const float gg = g[q][i][j];
+            const float xhat = (xh[q][i][j] - mu[q]) * rs[q];
+            xh[q][i][j] = xhat;
+            dg[i][j] += gg * xhat;
+            db[i][j] += gg;
+            const float d = gg * wv[i][j];
+            g[q][i][j] = d;
+            s1 += d;
+            s2 += d * xhat;
+          }
         }
-        st4(dr, o);
-        if (dres_copy) st4(dres_copy + row * C + c, o);
+      }
+      s1 = wave_sum(s1) / (float)C;
+      s2 = wave_sum(s2) / (float)C;
+#pragma unroll
+      for (int i = 0; i < NV; ++i) {
+        int c = (i * 64 + lane) * 4;
+        if (c < C) {
+          float* ov = o[q][i];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const float dx = rs[q] * (g[q][i][j] - s1 - xh[q][i][j] * s2);
+            ov[j] = accumulate ? ov[j] + dx : dx;
+            ds[i][j] += ov[j];
+          }
+          st4(dres + row * C + c, ov);
+          if (dres_copy) st4(dres_copy + row * C + c, ov);
+        }
       }
     }
   }
@@ -337,6 +358,8 @@ __global__ __launch_bounds__(1024) void count_valid_kernel(const int32_t* __rest
 template <typename T> struct Row8;
 template <> struct Row8<bf16_t> {
   uint4 r;
+  // opaque to the optimiser: values derived from r before this are not reused
+  __device__ void touch() { asm volatile("" : "+v"(r.x), "+v"(r.y), "+v"(r.z), "+v"(r.w)); }
   __device__ void load(const bf16_t* p) { r = *reinterpret_cast<const uint4*>(p); }
   __device__ float get(int j) const {
     uint32_t w = j < 2 ? r.x : j < 4 ? r.y : j < 6 ? r.z : r.w;
@@ -399,6 +422,10 @@ __global__ __launch_bounds__(XENT_NT) void xent_fused_kernel(T* __restrict__ log
 #pragma unroll
       for (int j = 0; j < 8; ++j) m = fmaxf(m, v[i].get(j));
   m = wave_max(m);
+  if constexpr (sizeof(T) == 2) {
+#pragma unroll
+    for (int i = 0; i < XENT_KPT; ++i) v[i].touch();
+  }
   if (lane == 0) red[0][w] = m;
   __syncthreads();
   float M = red[0][0];
@@ -411,6 +438,12 @@ __global__ __launch_bounds__(XENT_NT) void xent_fused_kernel(T* __restrict__ log
 #pragma unroll
       for (int j = 0; j < 8; ++j) sum += __expf(v[i].get(j) - M);
   sum = wave_sum(sum);
+  if constexpr (sizeof(T) == 2) {
+    // keep only the packed row live across the reduction (the float copies
+    // would double the registers and halve the blocks per CU)
+#pragma unroll
+    for (int i = 0; i < XENT_KPT; ++i) v[i].touch();
+  }
   if (lane == 0) red[1][w] = sum;
   __syncthreads();
   float S = 0.f;
@@ -464,7 +497,18 @@ __global__ __launch_bounds__(256) void sumsq_kernel(const float* __restrict__ g,
   __shared__ double s[4];
   double a = 0.0;
   const float4* g4 = reinterpret_cast<const float4*>(g);
-  for (long i = (long)blockIdx.x * 256 + threadIdx.x; i < n4; i += (long)gridDim.x * 256) {
+  const long stride = (long)gridDim.x * 256;
+  long i = (long)blockIdx.x * 256 + threadIdx.x;
+  for (; i + 3 * stride < n4; i += 4 * stride) {  // four loads in flight
+    float4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) v[u] = g4[i + u * stride];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      a += (double)v[u].x * v[u].x + (double)v[u].y * v[u].y + (double)v[u].z * v[u].z +
+           (double)v[u].w * v[u].w;
+  }
+  for (; i < n4; i += stride) {
     float4 v = g4[i];
     a += (double)v.x * v.x + (double)v.y * v.y + (double)v.z * v.z + (double)v.w * v.w;
   }
@@ -512,6 +556,7 @@ __global__ __launch_bounds__(256) void adamw_kernel(const AdamChunk* __restrict_
   float4* m4 = reinterpret_cast<float4*>(m + ck.start);
   float4* v4 = reinterpret_cast<float4*>(v + ck.start);
   int n4 = ck.len >> 2;
+#pragma unroll 4
   for (int i = threadIdx.x; i < n4; i += 256) {
     float4 pp = p4[i], gg = g4[i], mm = m4[i], vv = v4[i];
     float P[4] = {pp.x, pp.y, pp.z, pp.w}, G[4] = {gg.x, gg.y, gg.z, gg.w};

@@ -36,6 +36,10 @@ WORKLOADS = {
                 desc="GPT-2 124M masked fine-tuning step, bf16, B=16, T=1024, prompt targets -1"),
     "gpt2-xl": dict(model="gpt2-xl", B=8, T=1024, data="zipf", lr=6e-4, wd=0.1,
                     desc="GPT-2 XL-shape training step (L=48, C=1600, H=25), bf16, B=8, T=1024"),
+    "gpt2-124m-eval": dict(model="gpt2-124m", B=16, T=1024, data="zipf", lr=None, wd=0.0,
+                           eval=True,
+                           desc="GPT-2 124M evaluation pass (forward + losses + per-sequence "
+                                "mean losses, no gradient), bf16, B=16, T=1024, Zipf ids"),
     "gpt2-124m-accum": dict(model="gpt2-124m", B=16, T=1024, data="zipf", accum=32, lr=None,
                             wd=0.1,
                             desc="GPT-2 124M full optimizer step: 32 micro-batches of 16x1024 "
@@ -83,12 +87,17 @@ def cpu_baseline(d, wl, seconds_hint=20.0):
         idx, tgt = synthetic.zipf_batch(1, T, seed=1002)
     m, v = np.zeros_like(flat), np.zeros_like(flat)
     t0 = time.perf_counter()
-    lr = wl["lr"] if wl["lr"] is not None else 6e-4 / 715
-    oracle.train_step(flat, m, v, 1, [(idx, tgt)], cfg, lr=lr, weight_decay=wl["wd"])
+    if wl.get("eval"):
+        _, cache = oracle.forward(flat, idx, tgt, cfg)
+        oracle.sequence_losses(cache["row_loss"], tgt)
+        what = "forward + losses + per-sequence mean losses"
+    else:
+        lr = wl["lr"] if wl["lr"] is not None else 6e-4 / 715
+        oracle.train_step(flat, m, v, 1, [(idx, tgt)], cfg, lr=lr, weight_decay=wl["wd"])
+        what = "one full step (fwd+bwd+clip+AdamW over all params)"
     dt = time.perf_counter() - t0
     return {"value": round(T / dt, 2), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"one full step (fwd+bwd+clip+AdamW over all params) on 1 x {T} tokens "
-                      f"of the same workload; {dt:.1f} s"}
+            "sample": f"{what} on 1 x {T} tokens of the same workload; {dt:.1f} s"}
 
 
 def main():
@@ -136,7 +145,12 @@ def main():
             torch.tensor(t, dtype=torch.int32, device="cuda:0")) for i, t in batches]
     opt_step = [0]
 
+    seq_loss = torch.zeros((B,), dtype=torch.float32, device="cuda:0")
+
     def step():
+        if wl.get("eval"):
+            model.eval(dev[0][0], dev[0][1], seq_loss=seq_loss)
+            return
         model.zero_grad()
         for di, dt in dev:
             model.forward(di, dt)
@@ -169,6 +183,8 @@ def main():
     tokens = B * T * accum
     tok_s = tokens * args.steps / (ms_total / 1e3)
     f_causal, f_nano = flops_per_token(d, T)
+    if wl.get("eval"):  # forward only: a third of the training step's work
+        f_causal, f_nano = f_causal / 3.0, f_nano / 3.0
 
     lm_ms, lm_n = sites.get("LMHEAD_FWD", (0.0, 0))
     lm_avg = lm_ms / max(lm_n, 1)
@@ -185,7 +201,7 @@ def main():
 
     out = {
         "metric": METRIC if args.workload == "gpt2-124m" else
-                  f"training tokens/sec + MFU, {args.workload} on one MI355X",
+                  f"tokens/sec + MFU, {args.workload} on one MI355X",
         "value": round(tok_s, 1),
         "unit": "tokens/s",
         "n_gpus": 1,

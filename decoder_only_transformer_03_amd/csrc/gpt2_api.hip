@@ -328,7 +328,8 @@ gpt2_status sync(gpt2* h) {
   return check_device_flags(h);
 }
 
-gpt2_status run_forward(gpt2* h, const int32_t* d_idx, const int32_t* d_tgt, int B, int T) {
+gpt2_status run_forward(gpt2* h, const int32_t* d_idx, const int32_t* d_tgt, int B, int T,
+                        bool grad) {
   const gpt2_config& c = h->cfg;
   const int C = c.n_embd, H = c.n_head, hd = C / H, Vp = c.padded_vocab_size;
   const long BT = (long)B * T;
@@ -375,7 +376,7 @@ gpt2_status run_forward(gpt2* h, const int32_t* d_idx, const int32_t* d_tgt, int
                         at, e, 0, s));
   if (d_tgt)
     TIMED(h, GPT2_SITE_XENT, launch_xent(at, h->logits, d_tgt, h->n_valid, h->row_loss, h->loss, BT, Vp, h->err,
-                          s));
+                          grad, s));
   return GPT2_OK;
 }
 
@@ -569,7 +570,7 @@ gpt2_status gpt2_forward(gpt2_t* h, const int32_t* d_idx, const int32_t* d_targe
   h->T = T;
   h->have_targets = false;
   h->forward_done = false;
-  gpt2_status st = run_forward(h, d_idx, d_targets, B, T);
+  gpt2_status st = run_forward(h, d_idx, d_targets, B, T, true);
   if (st != GPT2_OK) return st;
   h->forward_done = true;
   h->have_targets = d_targets != nullptr;
@@ -578,6 +579,22 @@ gpt2_status gpt2_forward(gpt2_t* h, const int32_t* d_idx, const int32_t* d_targe
     return gpt2_get_loss(h, h_loss);
   }
   return GPT2_OK;
+}
+
+gpt2_status gpt2_eval(gpt2_t* h, const int32_t* d_idx, const int32_t* d_targets, int B, int T,
+                      float* d_seq_loss, float* h_loss) {
+  if (!h || !d_idx || !d_targets) return GPT2_E_ARG;
+  if (B < 1 || B > h->cfg.max_batch || T < 1 || T > h->cfg.block_size)
+    return fail(h, GPT2_E_SHAPE, "need 1 <= B <= max_batch and 1 <= T <= block_size");
+  h->B = B;
+  h->T = T;
+  h->have_targets = false;
+  h->forward_done = false;
+  gpt2_status st = run_forward(h, d_idx, d_targets, B, T, false);
+  if (st != GPT2_OK) return st;
+  if (d_seq_loss) HIPTRY(h, launch_seq_loss(h->row_loss, d_targets, B, T, d_seq_loss, h->stream));
+  h->forward_done = true;  // logits and losses readable; no gradient was formed
+  return h_loss ? gpt2_get_loss(h, h_loss) : GPT2_OK;
 }
 
 gpt2_status gpt2_get_loss(gpt2_t* h, float* h_loss) {

@@ -395,7 +395,7 @@ template <> struct Row8<float> {
 //   d(loss)/d(logits) = (softmax - onehot(target)) / n_valid   (0 if ignored).
 // Padded vocabulary columns take part like real ones.
 constexpr int XENT_NT = 512, XENT_KPT = 13;  // rows up to 8 * 512 * 13 = 53248 wide
-template <typename T>
+template <typename T, bool GRAD>
 __global__ __launch_bounds__(XENT_NT) void xent_fused_kernel(T* __restrict__ logits,
                                                              const int32_t* __restrict__ targets,
                                                              const int* __restrict__ n_valid,
@@ -452,6 +452,7 @@ __global__ __launch_bounds__(XENT_NT) void xent_fused_kernel(T* __restrict__ log
   const float lse = M + __logf(S);
   const int nv = *n_valid;
   const float scale = valid && nv > 0 ? 1.0f / (float)nv : 0.f;
+  if constexpr (GRAD)
 #pragma unroll
   for (int i = 0; i < XENT_KPT; ++i) {
     const int ch = threadIdx.x + i * XENT_NT;
@@ -485,6 +486,42 @@ __global__ __launch_bounds__(1024) void loss_reduce_kernel(const float* __restri
     int nv = *n_valid;
     *loss = nv > 0 ? (float)(t / nv) : 0.f;
   }
+}
+
+// Per-sequence mean loss over the positions with a target:
+// seq_loss[b] = sum_t row_loss[b*T + t] / #{t : targets[b*T + t] != -1}, 0 if none.
+// One workgroup per sequence; fp64 sum in a fixed order.
+__global__ __launch_bounds__(256) void seq_loss_kernel(const float* __restrict__ row_loss,
+                                                       const int32_t* __restrict__ targets,
+                                                       int T, float* __restrict__ seq_loss) {
+  __shared__ double s[4];
+  __shared__ int c[4];
+  const long r0 = (long)blockIdx.x * T;
+  double a = 0.0;
+  int n = 0;
+  for (int t = threadIdx.x; t < T; t += 256) {
+    a += (double)row_loss[r0 + t];
+    n += targets[r0 + t] != -1;
+  }
+  a = wave_sum_d(a);
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) n += __shfl_xor(n, o, 64);
+  if ((threadIdx.x & 63) == 0) {
+    s[threadIdx.x >> 6] = a;
+    c[threadIdx.x >> 6] = n;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const double t = (s[0] + s[1]) + (s[2] + s[3]);
+    const int nn = (c[0] + c[1]) + (c[2] + c[3]);
+    seq_loss[blockIdx.x] = nn > 0 ? (float)(t / nn) : 0.f;
+  }
+}
+
+hipError_t launch_seq_loss(const float* row_loss, const int32_t* targets, int B, int T,
+                           float* seq_loss, hipStream_t s) {
+  seq_loss_kernel<<<B, 256, 0, s>>>(row_loss, targets, T, seq_loss);
+  return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
@@ -730,15 +767,20 @@ hipError_t launch_bias_grad(DType in_t, const void* X, long rows, int N, long ld
 }
 
 hipError_t launch_xent(DType t, void* logits, const int32_t* targets, int* n_valid,
-                       float* row_loss, float* loss, long rows, int Vp, int* err, hipStream_t s) {
+                       float* row_loss, float* loss, long rows, int Vp, int* err, bool grad,
+                       hipStream_t s) {
   if (Vp % 8 || Vp > 8 * XENT_NT * XENT_KPT) return hipErrorInvalidValue;
   count_valid_kernel<<<1, 1024, 0, s>>>(targets, rows, Vp, n_valid, err);
   if (t == DT_BF16)
-    xent_fused_kernel<bf16_t><<<(unsigned)rows, XENT_NT, 0, s>>>((bf16_t*)logits, targets,
-                                                                  n_valid, row_loss, Vp);
+    grad ? xent_fused_kernel<bf16_t, true><<<(unsigned)rows, XENT_NT, 0, s>>>(
+               (bf16_t*)logits, targets, n_valid, row_loss, Vp)
+         : xent_fused_kernel<bf16_t, false><<<(unsigned)rows, XENT_NT, 0, s>>>(
+               (bf16_t*)logits, targets, n_valid, row_loss, Vp);
   else
-    xent_fused_kernel<float><<<(unsigned)rows, XENT_NT, 0, s>>>((float*)logits, targets, n_valid,
-                                                                 row_loss, Vp);
+    grad ? xent_fused_kernel<float, true><<<(unsigned)rows, XENT_NT, 0, s>>>(
+               (float*)logits, targets, n_valid, row_loss, Vp)
+         : xent_fused_kernel<float, false><<<(unsigned)rows, XENT_NT, 0, s>>>(
+               (float*)logits, targets, n_valid, row_loss, Vp);
   loss_reduce_kernel<<<1, 1024, 0, s>>>(row_loss, rows, n_valid, loss);
   return hipGetLastError();
 }

@@ -46,8 +46,13 @@ hipError_t launch_colsum_finish(const float* partial, int nparts, int ncols, flo
                                 hipStream_t s);
 hipError_t launch_bias_grad(DType in_t, const void* X, long rows, int N, long ldx, float* partial,
                             float* db, hipStream_t s);
+// Fused softmax cross-entropy; with grad the logits are overwritten by
+// d(loss)/d(logits), without only the losses are formed.
 hipError_t launch_xent(DType t, void* logits, const int32_t* targets, int* n_valid,
-                       float* row_loss, float* loss, long rows, int Vp, int* err, hipStream_t s);
+                       float* row_loss, float* loss, long rows, int Vp, int* err, bool grad,
+                       hipStream_t s);
+hipError_t launch_seq_loss(const float* row_loss, const int32_t* targets, int B, int T,
+                           float* seq_loss, hipStream_t s);
 hipError_t launch_grad_norm(const float* g, long n, double* partial, float max_norm,
                             float* norm_out, float* clip_out, hipStream_t s);
 hipError_t launch_adamw(const AdamChunk* chunks, int nchunks, float* p, const float* g, float* m,

@@ -65,6 +65,7 @@ def lib():
             "gpt2_get_step": (i32, [vp, ct.POINTER(i64)]),
             "gpt2_set_step": (i32, [vp, i64]),
             "gpt2_forward": (i32, [vp, vp, vp, i32, i32, ct.POINTER(f32)]),
+            "gpt2_eval": (i32, [vp, vp, vp, i32, i32, vp, ct.POINTER(f32)]),
             "gpt2_get_loss": (i32, [vp, ct.POINTER(f32)]),
             "gpt2_zero_grad": (i32, [vp]),
             "gpt2_backward": (i32, [vp, f32]),
@@ -90,7 +91,8 @@ def lib():
 
 
 EXPORTED = ["gpt2_num_params", "gpt2_workspace_bytes", "gpt2_init", "gpt2_set_params", "gpt2_get",
-            "gpt2_set_state", "gpt2_get_step", "gpt2_set_step", "gpt2_forward", "gpt2_get_loss",
+            "gpt2_set_state", "gpt2_get_step", "gpt2_set_step", "gpt2_forward", "gpt2_eval",
+            "gpt2_get_loss",
             "gpt2_zero_grad", "gpt2_backward", "gpt2_adamw_step", "gpt2_get_grad_norm",
             "gpt2_sync", "gpt2_last_error", "gpt2_destroy", "gpt2_get_activation",
             "gpt2_timing_begin", "gpt2_timing_end",
@@ -198,6 +200,18 @@ class GPT2:
         loss = ct.c_float(0.0)
         st = lib().gpt2_forward(self.h, _ptr(idx), _ptr(targets), B, T,
                                 ct.byref(loss) if want_loss else None)
+        self._check(st)
+        return loss.value if want_loss else None
+
+    def eval(self, idx, targets, seq_loss=None, want_loss=False):
+        """Forward pass and losses only (no gradient).  idx, targets: int32
+        device tensors (B, T); seq_loss: optional float32 device tensor (B,)
+        that receives each sequence's mean loss over its valid targets."""
+        B, T = idx.shape
+        loss = ct.c_float(0.0)
+        st = lib().gpt2_eval(self.h, _ptr(idx), _ptr(targets), B, T,
+                             _ptr(seq_loss) if seq_loss is not None else None,
+                             ct.byref(loss) if want_loss else None)
         self._check(st)
         return loss.value if want_loss else None
 

@@ -138,6 +138,19 @@ gpt2_status gpt2_set_step(gpt2_t* h, int64_t t);
 gpt2_status gpt2_forward(gpt2_t* h, const int32_t* d_idx, const int32_t* d_targets,
                          int B, int T, float* h_loss);
 
+/* Evaluation pass ("Measuring held-out loss"; per-sequence scoring of
+ * candidate continuations, as multiple-choice evaluations do): the forward
+ * pass and the cross-entropy losses only -- no gradient is formed, the logits
+ * stay in place (gpt2_get_activation LOGITS) and a following gpt2_backward
+ * returns GPT2_E_STATE.  d_targets is required (device int32, B*T, -1 =
+ * ignored).  d_seq_loss (device, B floats, may be NULL) receives for each
+ * sequence b the mean loss over its positions with a target,
+ *   sum_t loss[b][t] / #{t : targets[b][t] != -1}   (0 if there is none),
+ * and h_loss (host, may be NULL; waits) the mean over all such positions of
+ * the batch, exactly what gpt2_forward would report. */
+gpt2_status gpt2_eval(gpt2_t* h, const int32_t* d_idx, const int32_t* d_targets, int B, int T,
+                      float* d_seq_loss, float* h_loss);
+
 /* Loss of the last forward with targets; waits for the stream. */
 gpt2_status gpt2_get_loss(gpt2_t* h, float* h_loss);
 

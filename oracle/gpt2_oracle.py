@@ -380,6 +380,21 @@ def clip_and_adamw(params, grads, m, v, t, lr, beta1=0.9, beta2=0.95, eps=1e-8,
     return norm
 
 
+def sequence_losses(row_loss, targets):
+    """Mean loss of each sequence over its positions with a target ("GPT-2
+    from Scratch", Measuring held-out loss; the per-candidate score of a
+    multiple-choice evaluation in "Build-GPT-2", Evaluation): row_loss and
+    targets are (B, T); positions with target -1 carry no loss and are not
+    counted.  A sequence with no target scores 0."""
+    row_loss = np.asarray(row_loss, dtype=np.float64).reshape(targets.shape)
+    valid = np.asarray(targets) != -1
+    out = np.zeros(targets.shape[0])
+    for b in range(targets.shape[0]):
+        n = int(valid[b].sum())
+        out[b] = row_loss[b][valid[b]].sum() / n if n else 0.0
+    return out
+
+
 def lr_at(step, max_lr=6e-4, min_lr=6e-5, warmup=100, max_steps=2000):
     """Linear warmup over `warmup` steps starting at max_lr/warmup, cosine from
     max_lr at step=warmup down to min_lr at step=max_steps, min_lr after."""

@@ -1,0 +1,78 @@
+"""Evaluation pass (gpt2_eval): forward and losses only, per-sequence mean
+losses over the valid targets, against the oracle.
+
+fp32 tiny model: the batch loss is bit-identical to what gpt2_forward reports
+(same kernels, the gradient store is simply skipped); per-sequence scores
+within 1e-4 of the oracle's (a sequence with no target scores exactly 0); the
+logits left in place within 1e-4; a backward afterwards is refused.
+bf16 GPT-2 124M, masked fine-tuning batch (B=16, T=1024): sampled
+sequences' scores against the oracle run on those sequences, to the loss
+tolerance 2e-2."""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+from oracle import gpt2_oracle as O
+import synthetic
+from decoder_only_transformer_03_amd import gpt2 as G
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def dev_ids(a):
+    return torch.tensor(np.ascontiguousarray(a), dtype=torch.int32, device=DEV)
+
+
+def test_eval_fp32_tiny():
+    d = synthetic.model_dims("tiny")
+    cfg = O.Config(**d)
+    B, T = 4, 64
+    flat = synthetic.init_params(d, seed=42)
+    idx, tgt = synthetic.uniform_batch(B, T, 512, seed=1101)
+    tgt[1, :40] = -1
+    tgt[3, :] = -1                                  # nothing to score
+    m = G.GPT2(G.make_config(max_batch=B, precision="fp32", **d), device=DEV)
+    m.set_params(flat)
+    di, dt = dev_ids(idx), dev_ids(tgt)
+    loss_f = m.forward(di, dt, want_loss=True)
+    seq = torch.full((B,), float("nan"), dtype=torch.float32, device=DEV)
+    loss_e = m.eval(di, dt, seq_loss=seq, want_loss=True)
+    assert loss_e == loss_f                          # bit-identical
+    logits = m.activation("LOGITS", 0, B * T * d["padded_vocab_size"])
+    with pytest.raises(G.GPT2Error):
+        m.backward(1.0)
+    r_loss, cache = O.forward(flat, idx, tgt, cfg, keep_logits=True)
+    ref = O.sequence_losses(cache["row_loss"], tgt)
+    got = seq.cpu().numpy().astype(np.float64)
+    print(f"\neval tiny: loss {loss_e:.7f} / {float(r_loss):.7f}; seq {got} / {ref}")
+    assert abs(loss_e - float(r_loss)) <= 1e-4 * abs(float(r_loss))
+    assert got[3] == 0.0
+    assert np.max(np.abs(got - ref)) <= 1e-4 * np.max(np.abs(ref))
+    lref = cache["logits"].reshape(-1).astype(np.float64)
+    assert np.max(np.abs(logits - lref)) <= 1e-4 * np.max(np.abs(lref))
+
+
+def test_eval_bf16_124m_sft_scores():
+    d = synthetic.model_dims("gpt2-124m")
+    cfg = O.Config(**d)
+    B, T = 16, 1024
+    flat = synthetic.init_params(d, seed=42)
+    idx, tgt = synthetic.sft_batch(B, T, seed=1004)
+    m = G.GPT2(G.make_config(max_batch=B, precision="bf16", **d), device=DEV)
+    try:
+        m.set_params(flat)
+        seq = torch.zeros((B,), dtype=torch.float32, device=DEV)
+        loss = m.eval(dev_ids(idx), dev_ids(tgt), seq_loss=seq, want_loss=True)
+        got = seq.cpu().numpy().astype(np.float64)
+        n = (tgt != -1).sum(axis=1)
+        # the batch loss is the count-weighted mean of the scores
+        assert abs((got * n).sum() / n.sum() - loss) <= 1e-5 * abs(loss)
+    finally:
+        m.close()
+    rows = [0, 9]
+    _, cache = O.forward(flat, idx[rows], tgt[rows], cfg)
+    ref = O.sequence_losses(cache["row_loss"], tgt[rows])
+    print(f"\neval 124M SFT: scores {got[rows]} oracle {ref}")
+    assert np.max(np.abs(got[rows] - ref)) < 2e-2

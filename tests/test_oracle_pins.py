@@ -384,3 +384,24 @@ def test_overfit_single_batch():
         first = loss if first is None else first
     assert first > 6.0
     assert loss < 0.05, loss
+
+
+def test_sequence_losses_pins():
+    """Per-sequence mean over valid targets: a hand-worked case (mean of the
+    two middle losses, an all-ignored sequence scoring 0, gaps skipped), and
+    on a real forward pass the count-weighted mean of the sequences' scores
+    is the batch loss."""
+    rl = np.array([[1.0, 2.0, 3.0, 4.0], [0.0, 0.0, 0.0, 0.0], [5.0, 0.0, 7.0, 0.0]])
+    tg = np.array([[-1, 5, 6, -1], [-1, -1, -1, -1], [1, -1, 2, -1]])
+    assert O.sequence_losses(rl, tg).tolist() == [2.5, 0.0, 6.0]
+    d = synthetic.model_dims("tiny")
+    cfg = O.Config(**d)
+    flat = synthetic.init_params(d, seed=42).astype(np.float64)
+    idx, tgt = synthetic.uniform_batch(3, 16, 512, seed=7)
+    tgt[0, :10] = -1
+    tgt[2, :] = -1
+    loss, cache = O.forward(flat, idx, tgt, cfg)
+    seq = O.sequence_losses(cache["row_loss"], tgt)
+    n = (tgt != -1).sum(axis=1)
+    assert seq[2] == 0.0
+    assert abs((seq * n).sum() / n.sum() - float(loss)) < 1e-12

@@ -154,19 +154,42 @@ struct LoaderT {
 };
 
 // R rows x 64 k of a transposed operand (X[k*ld + row], rows contiguous), K a
-// multiple of 64, loaded straight into LDS as [64 k][R rows].  A wavefront
-// instruction fills 1 KB = 1024/(2R) k-rows; the 16-byte chunk c of k-row kr
-// is stored at chunk c ^ 4(kr%4), which keeps the transpose reads of the
-// fragments (4 consecutive k-rows x 64 bytes per half-wavefront) free of bank
-// conflicts.  Columns past the matrix edge re-read the last 8 (their products
-// are never stored).
+// multiple of 64, loaded straight into LDS as [64 k][R rows] (R = 256 or 192).
+// Wavefront instruction g fills bytes [1 KB g, 1 KB (g+1)) of the tile; the
+// 16-byte chunk c of k-row kr is stored at chunk dt_phys(kr, c), which keeps
+// the transpose reads of the fragments (4 consecutive k-rows x 64 bytes per
+// half-wavefront) free of bank conflicts: for R = 256 (512-byte k-rows) chunk
+// c ^ 4(kr%4); for R = 192 (384-byte k-rows, alternate rows half a bank
+// window apart) a rotation by 4 chunks on k-rows 2 and 3 of every 4.
+// Columns past the matrix edge re-read the last 8 (their products are never
+// stored).
+template <int R>
+__device__ __forceinline__ int dt_phys(int kr, int c) {
+  if constexpr (R == 256) {
+    return c ^ (4 * (kr & 3));
+  } else {
+    static_assert(R == 192, "transposed direct tiles are 256 or 192 wide");
+    const int p = c + 4 * ((kr >> 1) & 1);
+    return p >= R / 8 ? p - R / 8 : p;
+  }
+}
+template <int R>
+__device__ __forceinline__ int dt_logical(int kr, int p) {
+  if constexpr (R == 256) {
+    return p ^ (4 * (kr & 3));
+  } else {
+    const int c = p - 4 * ((kr >> 1) & 1);
+    return c < 0 ? c + R / 8 : c;
+  }
+}
+
 template <int R, int NT>
 struct LoaderDT {
   static constexpr int NW = NT / 64;
-  static constexpr int CPR = R / 8;                     // 16-byte chunks per k-row
-  static constexpr int KPI = 64 / CPR;                  // k-rows per wavefront instruction
-  static constexpr int PER_WAVE = BK / KPI / NW;        // instructions per wavefront
-  static_assert(KPI * CPR == 64 && PER_WAVE * KPI * NW == BK, "tile/thread combination");
+  static constexpr int CPR = R / 8;                 // 16-byte chunks per k-row
+  static constexpr int NINST = BK * R * 2 / 1024;   // wavefront instructions per tile
+  static constexpr int PER_WAVE = NINST / NW;
+  static_assert(PER_WAVE * NW == NINST, "tile/thread combination");
   const char* base;
   uint32_t off[PER_WAVE];
   long ldb2;  // bytes per k-row in global memory
@@ -177,8 +200,9 @@ struct LoaderDT {
     ldb2 = 2 * ld;
 #pragma unroll
     for (int j = 0; j < PER_WAVE; ++j) {
-      const int kr = (w * PER_WAVE + j) * KPI + lane / CPR;
-      const int c = (lane % CPR) ^ (4 * (kr & 3));
+      const int chunk = (w * PER_WAVE + j) * 64 + lane;  // 16-byte chunk index in the tile
+      const int kr = chunk / CPR;
+      const int c = dt_logical<R>(kr, chunk - kr * CPR);
       long col = (long)c * 8;
       if (r0 + col + 8 > rtot) col = rtot - 8 - r0;
       off[j] = (uint32_t)((kr * ld + col) * 2);
@@ -190,10 +214,10 @@ struct LoaderDT {
     const char* kb = base + ldb2 * k;
 #pragma unroll
     for (int j = 0; j < PER_WAVE; ++j) {
-      const int kr0 = (w * PER_WAVE + j) * KPI;
+      const int g = w * PER_WAVE + j;
       __builtin_amdgcn_global_load_lds(
           (const __attribute__((address_space(1))) void*)(kb + off[j]),
-          (__attribute__((address_space(3))) void*)(s + kr0 * R), 16, 0, 0);
+          (__attribute__((address_space(3))) void*)(s + g * 512), 16, 0, 0);
     }
   }
   __device__ __forceinline__ void commit(bf16_t*, int) const {}
@@ -213,7 +237,7 @@ __device__ __forceinline__ bf16x8_t frag_tr(const bf16_t* s, int rbase, int kk, 
 #pragma unroll
   for (int half = 0; half < 2; ++half) {
     const int kr = 16 * kk + 8 * (g >> 1) + 4 * half + (t >> 2);
-    const bf16_t* p = s + kr * R + ((((col >> 3) ^ (4 * (kr & 3)))) << 3) + (col & 7);
+    const bf16_t* p = s + kr * R + (dt_phys<R>(kr, col >> 3) << 3) + (col & 7);
     const gemm_short4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
         (__attribute__((address_space(3))) gemm_short4*)((__attribute__((address_space(3))) bf16_t*)p));
     const uint2 u = __builtin_bit_cast(uint2, v);
@@ -369,6 +393,117 @@ __device__ __forceinline__ void tile_epilogue(const EpiArgs& e, const f32x16_t (
   }
 }
 
+// The same staged epilogue for 64 x 96 wavefront sub-tiles (the 256 x 192
+// tile): rounds of 16 rows x 96 fp32, rows padded to 100 fp32 (400 bytes,
+// 6.25 KB of scratch per wavefront), which spreads both the fragment writes
+// (16 rows at one chunk) and the row reads over all banks.  In the read
+// phase the round's 16 x 12 groups of 8 columns are spread over the lanes,
+// three per lane.
+template <int BM, int BN, int WM, int WN, int EPI, typename TO, int SN, int SM>
+__device__ __forceinline__ void tile_epilogue_w96(const EpiArgs& e, const f32x16_t (&acc)[SN][SM],
+                                                  long m0, long n0, int split, int M, int N,
+                                                  int lane, int wm, int wn, bf16_t* scratch) {
+  constexpr int WTM = BM / WM, WTN = BN / WN;
+  static_assert(WTN == 96 && SN == 3, "64 x 96 wavefront sub-tiles");
+  static_assert(EPI != EPI_GELU_BWD, "column sums are produced by the 64-column epilogue only");
+  static_assert((BM + BN) * BK >= WM * WN * 3200, "epilogue scratch must fit one LDS stage");
+  constexpr int RS = WTN + 4;  // padded round-row stride (fp32)
+  float* sf = reinterpret_cast<float*>(scratch);  // [16 rows][RS fp32]
+  const long mw = m0 + wm * WTM;
+  const long nw = n0 + wn * WTN;
+  // this lane's three (row, 8-column group) items of every round
+  int irow[3], icol[3];
+  float bias[3][8];
+#pragma unroll
+  for (int t = 0; t < 3; ++t) {
+    const int p = lane + 64 * t;
+    irow[t] = p / 12;
+    icol[t] = (p % 12) * 8;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) bias[t][j] = 0.f;
+    if constexpr (epi_bias(EPI)) {
+      if (e.bias && nw + icol[t] < N) {
+        ld4(e.bias + nw + icol[t], bias[t]);
+        ld4(e.bias + nw + icol[t] + 4, bias[t] + 4);
+      }
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < WTM / 16; ++q) {
+    const int sm = q >> 1;
+    // (1) fragments of rows 16q .. 16q+15 -> round buffer
+    if (((lane & 31) >> 4) == (q & 1)) {
+      const int row = lane & 15;
+#pragma unroll
+      for (int sn = 0; sn < SN; ++sn)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int c = sn * 8 + 2 * i + (lane >> 5);
+          *reinterpret_cast<float4*>(sf + row * RS + c * 4) =
+              make_float4(e.alpha * acc[sn][sm][4 * i + 0], e.alpha * acc[sn][sm][4 * i + 1],
+                          e.alpha * acc[sn][sm][4 * i + 2], e.alpha * acc[sn][sm][4 * i + 3]);
+        }
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    // (2) rows of the round -> global
+#pragma unroll
+    for (int t = 0; t < 3; ++t) {
+      const int row = irow[t];
+      const long m = mw + q * 16 + row;
+      const long n = nw + icol[t];
+      const float4 a = *reinterpret_cast<const float4*>(sf + row * RS + icol[t]);
+      const float4 b = *reinterpret_cast<const float4*>(sf + row * RS + icol[t] + 4);
+      float v[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+      if (m < M && n < N) {
+        if constexpr (epi_bias(EPI)) {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) v[j] += bias[t][j];
+        }
+        if constexpr (EPI == EPI_STORE || EPI == EPI_BIAS) {
+          st4(reinterpret_cast<TO*>(e.out) + m * e.ldo + n, v);
+          st4(reinterpret_cast<TO*>(e.out) + m * e.ldo + n + 4, v + 4);
+        } else if constexpr (EPI == EPI_BIAS_GELU) {
+          float d[8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) v[j] = gelu_tanh_and_grad_f(v[j], d + j);
+          st4(reinterpret_cast<TO*>(e.out) + m * e.ldo + n, d);
+          st4(reinterpret_cast<TO*>(e.out) + m * e.ldo + n + 4, d + 4);
+          st4(reinterpret_cast<TO*>(e.out2) + m * e.ldo + n, v);
+          st4(reinterpret_cast<TO*>(e.out2) + m * e.ldo + n + 4, v + 4);
+        } else if constexpr (EPI == EPI_RESID) {
+          float x[8];
+          ld4(e.resid + m * e.ldr + n, x);
+          ld4(e.resid + m * e.ldr + n + 4, x + 4);
+#pragma unroll
+          for (int j = 0; j < 8; ++j) v[j] += x[j];
+          st4(reinterpret_cast<float*>(e.out) + m * e.ldo + n, v);
+          st4(reinterpret_cast<float*>(e.out) + m * e.ldo + n + 4, v + 4);
+        } else if constexpr (EPI == EPI_ACCUM) {
+          float* o = reinterpret_cast<float*>(e.out) + m * e.ldo + n;
+          float x[8];
+          ld4(o, x);
+          ld4(o + 4, x + 4);
+#pragma unroll
+          for (int j = 0; j < 8; ++j) v[j] += x[j];
+          st4(o, v);
+          st4(o + 4, v + 4);
+        } else if constexpr (EPI == EPI_ATOMIC) {
+          float* o = reinterpret_cast<float*>(e.out) + m * e.ldo + n;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) atomicAdd(o + j, v[j]);
+        } else if constexpr (EPI == EPI_PARTIAL) {
+          float* o = reinterpret_cast<float*>(e.out) + split * e.split_stride + m * e.ldo + n;
+          st4(o, v);
+          st4(o + 4, v + 4);
+        }
+      }
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
 // WM x WN wavefronts; each owns a (BM/WM) x (BN/WN) sub-tile.  Persistent:
 // the grid is about one workgroup per CU; each walks the work items
 // (tile, k-slice) blockIdx.x, +gridDim.x, ...
@@ -507,8 +642,12 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(int M, int N, int
     }
     // the stage not holding the next item's first k-tile is free: 8 KB of
     // epilogue scratch per wavefront
-    tile_epilogue<BM, BN, WM, WN, EPI, TO, SN, SM>(e, acc, em0, en0, esplit, M, N, lane, wm, wn,
-                                                   smem[cur ^ 1] + wave * 4096);
+    if constexpr (WTN == 64)
+      tile_epilogue<BM, BN, WM, WN, EPI, TO, SN, SM>(e, acc, em0, en0, esplit, M, N, lane, wm, wn,
+                                                     smem[cur ^ 1] + wave * 4096);
+    else
+      tile_epilogue_w96<BM, BN, WM, WN, EPI, TO, SN, SM>(e, acc, em0, en0, esplit, M, N, lane, wm,
+                                                         wn, smem[cur ^ 1] + wave * 3200);
     item += gridDim.x;
     if (item >= nitems) break;
     __syncthreads();  // scratch reads done before the next k-tile lands there
@@ -560,36 +699,51 @@ hipError_t dispatch(int M, int N, int K, const bf16_t* A, long lda, const bf16_t
 
 }  // namespace gemm_mfma
 
-// Explicit instantiation of the epilogues of one operand layout.  One tile
-// shape: 256 x 256 x 64 with 8 wavefronts (2 x 4, each 128 x 64).
+// Explicit instantiation of the epilogues of one operand layout.  Tile
+// shapes: 256 x 256 x 64 with 8 wavefronts (2 x 4, each 128 x 64), and for
+// outputs whose width is a multiple of 192 -- where it keeps more CUs busy --
+// 256 x 192 x 64 with 8 wavefronts (4 x 2, each 64 x 96; direct loads only,
+// no split-K or column-sum epilogues).
 #define GEMM_MFMA_DEFINE_DISPATCH(AT, BT)                                                       \
   namespace gemm_mfma {                                                                         \
-  template <int LA, int LB>                                                                     \
+  template <int BN_, int WM_, int WN_, int LA, int LB>                                         \
   static hipError_t by_epi(int M, int N, int K, const bf16_t* A, long lda, const bf16_t* B,    \
                            long ldb, int epi, DType out_t, const EpiArgs& e, int sk,            \
                            hipStream_t s) {                                                     \
     switch (epi) {                                                                              \
       case EPI_STORE:                                                                           \
         return out_t == DT_BF16                                                                 \
-                   ? run<256, 256, 2, 4, LA, LB, EPI_STORE, bf16_t>(M, N, K, A, lda, B, ldb, e, 1, s) \
-                   : run<256, 256, 2, 4, LA, LB, EPI_STORE, float>(M, N, K, A, lda, B, ldb, e, 1, s); \
+                   ? run<256, BN_, WM_, WN_, LA, LB, EPI_STORE, bf16_t>(M, N, K, A, lda, B, ldb, e, 1, s) \
+                   : run<256, BN_, WM_, WN_, LA, LB, EPI_STORE, float>(M, N, K, A, lda, B, ldb, e, 1, s); \
       case EPI_BIAS:                                                                            \
         if (out_t != DT_BF16) return hipErrorInvalidValue;                                      \
-        return run<256, 256, 2, 4, LA, LB, EPI_BIAS, bf16_t>(M, N, K, A, lda, B, ldb, e, 1, s);  \
+        return run<256, BN_, WM_, WN_, LA, LB, EPI_BIAS, bf16_t>(M, N, K, A, lda, B, ldb, e, 1, s); \
       case EPI_BIAS_GELU:                                                                       \
-        return run<256, 256, 2, 4, LA, LB, EPI_BIAS_GELU, bf16_t>(M, N, K, A, lda, B, ldb, e, 1, s); \
+        return run<256, BN_, WM_, WN_, LA, LB, EPI_BIAS_GELU, bf16_t>(M, N, K, A, lda, B, ldb, e, 1, s); \
       case EPI_RESID:                                                                           \
-        return run<256, 256, 2, 4, LA, LB, EPI_RESID, float>(M, N, K, A, lda, B, ldb, e, 1, s); \
+        return run<256, BN_, WM_, WN_, LA, LB, EPI_RESID, float>(M, N, K, A, lda, B, ldb, e, 1, s); \
       case EPI_ACCUM:                                                                           \
-        return run<256, 256, 2, 4, LA, LB, EPI_ACCUM, float>(M, N, K, A, lda, B, ldb, e, 1, s); \
+        return run<256, BN_, WM_, WN_, LA, LB, EPI_ACCUM, float>(M, N, K, A, lda, B, ldb, e, 1, s); \
       case EPI_ATOMIC:                                                                          \
-        return run<256, 256, 2, 4, LA, LB, EPI_ATOMIC, float>(M, N, K, A, lda, B, ldb, e, sk, s); \
+        if constexpr (BN_ == 256)                                                               \
+          return run<256, 256, 2, 4, LA, LB, EPI_ATOMIC, float>(M, N, K, A, lda, B, ldb, e, sk, s); \
+        break;                                                                                  \
       case EPI_GELU_BWD:                                                                        \
-        return run<256, 256, 2, 4, LA, LB, EPI_GELU_BWD, bf16_t>(M, N, K, A, lda, B, ldb, e, 1, s); \
+        if constexpr (BN_ == 256)                                                               \
+          return run<256, 256, 2, 4, LA, LB, EPI_GELU_BWD, bf16_t>(M, N, K, A, lda, B, ldb, e, 1, s); \
+        break;                                                                                  \
       case EPI_PARTIAL:                                                                         \
-        return run<256, 256, 2, 4, LA, LB, EPI_PARTIAL, float>(M, N, K, A, lda, B, ldb, e, sk, s); \
+        if constexpr (BN_ == 256)                                                               \
+          return run<256, 256, 2, 4, LA, LB, EPI_PARTIAL, float>(M, N, K, A, lda, B, ldb, e, sk, s); \
+        break;                                                                                  \
     }                                                                                           \
     return hipErrorInvalidValue;                                                                \
+  }                                                                                             \
+  /* fraction of the persistent workgroup slots busy over the rounds of tiles */               \
+  static double slot_use(long tiles) {                                                         \
+    const long slots = persistent_slots();                                                     \
+    const long rounds = (tiles + slots - 1) / slots;                                           \
+    return (double)tiles / (double)(rounds * slots);                                           \
   }                                                                                             \
   template <>                                                                                   \
   hipError_t dispatch<AT, BT>(int M, int N, int K, const bf16_t* A, long lda, const bf16_t* B,  \
@@ -605,7 +759,15 @@ hipError_t dispatch(int M, int N, int K, const bf16_t* A, long lda, const bf16_t
     /* operands go straight to LDS when whole 64-deep tiles exist */                            \
     const bool direct = K % 64 == 0;                                                            \
     constexpr int TA = AT ? 1 : 0, TB = BT ? 1 : 0;                                             \
-    if (direct) return by_epi<AT ? 3 : 2, BT ? 3 : 2>(M, N, K, A, lda, B, ldb, epi, out_t, e, split_k, s); \
-    return by_epi<TA, TB>(M, N, K, A, lda, B, ldb, epi, out_t, e, split_k, s);                 \
+    if (direct) {                                                                               \
+      const bool w192 = N % 192 == 0 && !e.colsum &&                                            \
+                        (epi == EPI_STORE || epi == EPI_BIAS || epi == EPI_BIAS_GELU ||         \
+                         epi == EPI_RESID || epi == EPI_ACCUM);                                 \
+      const long tm = (M + 255) / 256;                                                          \
+      if (w192 && slot_use(tm * (N / 192)) > slot_use(tm * ((N + 255) / 256)) + 0.02)          \
+        return by_epi<192, 4, 2, AT ? 3 : 2, BT ? 3 : 2>(M, N, K, A, lda, B, ldb, epi, out_t, e, split_k, s); \
+      return by_epi<256, 2, 4, AT ? 3 : 2, BT ? 3 : 2>(M, N, K, A, lda, B, ldb, epi, out_t, e, split_k, s); \
+    }                                                                                           \
+    return by_epi<256, 2, 4, TA, TB>(M, N, K, A, lda, B, ldb, epi, out_t, e, split_k, s);      \
   }                                                                                             \
   }

@@ -40,7 +40,9 @@ def maxrel(a, b):
 
 LAYOUTS = [(False, False), (False, True), (True, True)]
 SHAPES = [(256, 256, 128), (200, 136, 72), (64, 8, 8), (1024, 768, 768), (520, 2304, 200),
-          (4096, 6144, 192), (328, 136, 128), (520, 264, 256), (8, 776, 64)]
+          (4096, 6144, 192), (328, 136, 128), (520, 264, 256), (8, 776, 64),
+          # widths that fill the CUs better with 256 x 192 tiles
+          (16384, 768, 256), (16000, 768, 128)]
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "fp32"])

@@ -497,9 +497,10 @@ __global__ __launch_bounds__(256) void attn_bwd_dkv_mfma(const bf16_t* __restric
                                                          const float* __restrict__ dbuf,
                                                          bf16_t* __restrict__ dqkv, int Tn, int H,
                                                          int C) {
-  __shared__ __attribute__((aligned(16))) bf16_t sQ[2][64 * 64];
-  __shared__ __attribute__((aligned(16))) bf16_t sG[2][64 * 64];
-  __shared__ float sL[2][64], sD[2][64];
+  constexpr int QT = 128;  // queries staged per step (two 64-row tiles)
+  __shared__ __attribute__((aligned(16))) bf16_t sQ[2][QT * 64];
+  __shared__ __attribute__((aligned(16))) bf16_t sG[2][QT * 64];
+  __shared__ float sL[2][QT], sD[2][QT];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, half = lane >> 5, l32 = lane & 31;
   int kbk, bh;
   attn_item(false, kbk, bh);  // key block 0 has the most queries: dispatched first
@@ -530,9 +531,12 @@ __global__ __launch_bounds__(256) void attn_bwd_dkv_mfma(const bf16_t* __restric
   const float* drow = dbuf + (long)bh * Tn;
   float ll = 0.f, dl = 0.f;
   auto load_all = [&](int q0, int buf) {
-    tile_load(qbase, ld, q0, Tn, tid, sQ[buf]);
-    tile_load(gbase, C, q0, Tn, tid, sG[buf]);
-    if (tid < 64) {
+#pragma unroll
+    for (int t = 0; t < QT / 64; ++t) {
+      tile_load(qbase, ld, q0 + 64 * t, Tn, tid, sQ[buf] + t * 4096);
+      tile_load(gbase, C, q0 + 64 * t, Tn, tid, sG[buf] + t * 4096);
+    }
+    if (tid < QT) {
       int q = q0 + tid;
       ll = q < Tn ? lrow[q] * LOG2E_F : 0.f;
       dl = q < Tn ? drow[q] : 0.f;
@@ -540,7 +544,7 @@ __global__ __launch_bounds__(256) void attn_bwd_dkv_mfma(const bf16_t* __restric
   };
   auto store_all = [&](int buf) {
     tile_wait();
-    if (tid < 64) {
+    if (tid < QT) {
       sL[buf][tid] = ll;
       sD[buf][tid] = dl;
     }
@@ -552,11 +556,11 @@ __global__ __launch_bounds__(256) void attn_bwd_dkv_mfma(const bf16_t* __restric
   }
   __syncthreads();
   int cur = 0;
-  for (int q0 = qstart; q0 < Tn; q0 += 64, cur ^= 1) {
-    const bool more = q0 + 64 < Tn;
-    if (more) load_all(q0 + 64, cur ^ 1);
+  for (int q0 = qstart; q0 < Tn; q0 += QT, cur ^= 1) {
+    const bool more = q0 + QT < Tn;
+    if (more) load_all(q0 + QT, cur ^ 1);
 #pragma unroll
-    for (int s = 0; s < 2; ++s) {
+    for (int s = 0; s < QT / 32; ++s) {
       const int qs = q0 + 32 * s;
       if (qs + 31 < kw0 || qs >= Tn) continue;
       f32x16_t st = zero16(), dp = zero16();

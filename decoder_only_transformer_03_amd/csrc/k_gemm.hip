@@ -155,6 +155,42 @@ hipError_t launch_gemm_wgrad(DType in_t, int M, int N, int K, const void* A, lon
   if (S == 1) {
     e.out = out;
     e.ldo = ldo;
+    // Whole rounds of 256 x 256 tiles leave a last, partly idle round when
+    // the tile count is not a multiple of the workgroup slots (the tied
+    // lm_head: 197 x 3 tiles).  Then the leading rows run as whole rounds and
+    // the remaining rows as split-K slices that fill one more round.
+    if (in_t == DT_BF16 && K % 64 == 0) {
+      const long slots = gemm_slots();
+      const int tn = (N + 255) / 256, tm = (M + 255) / 256;
+      const long tiles = (long)tm * tn, rounds = tiles / slots, tail = tiles - rounds * slots;
+      const int nkt = K / 64;
+      const int M1 = (int)((rounds * slots) / tn) * 256;
+      if (rounds >= 1 && tail > 0 && tail * 10 < slots * 8 && nkt >= 32 && M1 > 0 && M1 < M) {
+        hipError_t r = launch_gemm(in_t, M1, N, K, A, lda, a_t, B, ldb, b_t, EPI_ACCUM, DT_F32, e,
+                                   1, s);
+        if (r != hipSuccess) return r;
+        const int M2 = M - M1;
+        const bf16_t* A2 = reinterpret_cast<const bf16_t*>(A) + (a_t ? (long)M1 : (long)M1 * lda);
+        const long tiles2 = (long)((M2 + 255) / 256) * tn;
+        int S2 = (int)(slots / tiles2);
+        if (S2 > nkt / 4) S2 = nkt / 4;
+        S2 = exact_splits(in_t, K, S2 < 1 ? 1 : S2);
+        while (S2 > 1 && (long)S2 * M2 * N > part_elems) S2 = exact_splits(in_t, K, S2 - 1);
+        EpiArgs e2 = e;
+        e2.out = out + (long)M1 * ldo;
+        if (S2 == 1)
+          return launch_gemm(in_t, M2, N, K, A2, lda, a_t, B, ldb, b_t, EPI_ACCUM, DT_F32, e2, 1, s);
+        e2.out = part;
+        e2.ldo = N;
+        e2.split_stride = (long)M2 * N;
+        r = launch_gemm(in_t, M2, N, K, A2, lda, a_t, B, ldb, b_t, EPI_PARTIAL, DT_F32, e2, S2, s);
+        if (r != hipSuccess) return r;
+        const long MN2 = (long)M2 * N;
+        splitk_reduce_kernel<<<(unsigned)((MN2 / 4 + 255) / 256), 256, 0, s>>>(
+            part, S2, MN2, N, out + (long)M1 * ldo, ldo);
+        return hipGetLastError();
+      }
+    }
     return launch_gemm(in_t, M, N, K, A, lda, a_t, B, ldb, b_t, EPI_ACCUM, DT_F32, e, 1, s);
   }
   e.out = part;

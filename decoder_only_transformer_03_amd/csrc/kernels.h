@@ -73,6 +73,7 @@ hipError_t launch_gemm(DType in_t, int M, int N, int K, const void* A, long lda,
 // Weight gradient out[m][n] += alpha * sum_k A(m,k) B(n,k) for a long
 // contraction: split over k into fp32 slices of `part` (part_elems floats of
 // scratch), then summed in fixed order into out (deterministic).
+int gemm_slots();  // workgroup slots of the persistent bf16 GEMM grid
 hipError_t launch_gemm_wgrad(DType in_t, int M, int N, int K, const void* A, long lda, bool a_t,
                              const void* B, long ldb, bool b_t, float* out, long ldo, float alpha,
                              float* part, long part_elems, hipStream_t s);

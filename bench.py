@@ -45,6 +45,16 @@ WORKLOADS = {
                             desc="GPT-2 124M full optimizer step: 32 micro-batches of 16x1024 "
                                  "(524,288 tokens) with gradient accumulation, clip 1.0, AdamW, "
                                  "lr warmup 715 steps then cosine 6e-4 -> 6e-5"),
+    "gpt2-124m-fusedhead": dict(model="gpt2-124m", B=16, T=1024, data="zipf", lr=6e-4, wd=0.1,
+                                head_chunk=4096,
+                                desc="GPT-2 124M training step, bf16, B=16, T=1024, Zipf ids, with "
+                                     "the fused lm_head + cross-entropy (no logits tensor; the "
+                                     "backward recomputes logits in slices of 4096 vocabulary "
+                                     "columns, a recomputation MFU does not count)"),
+    "gpt2-124m-eval-fusedhead": dict(model="gpt2-124m", B=16, T=1024, data="zipf", lr=None,
+                                     wd=0.0, eval=True, head_chunk=4096,
+                                     desc="GPT-2 124M evaluation pass, bf16, B=16, T=1024, Zipf "
+                                          "ids, fused lm_head + cross-entropy (no logits tensor)"),
 }
 
 METRIC = "training tokens/sec + MFU, GPT-2 124M bf16 B=16 T=1024 on one MI355X"
@@ -124,7 +134,8 @@ def main():
     wl = WORKLOADS[args.workload]
     d = synthetic.model_dims(wl["model"])
     B, T = wl["B"], wl["T"]
-    cfg = G.make_config(max_batch=B, precision="bf16", **d)
+    fused = wl.get("head_chunk", 0)
+    cfg = G.make_config(max_batch=B, precision="bf16", head_chunk=fused, **d)
     model = G.GPT2(cfg, device="cuda:0")
     model.set_params(synthetic.init_params(d, seed=42))
     if args.copy_probe:
@@ -222,10 +233,13 @@ def main():
         "loss_last_step": round(loss, 5),
         "grad_norm_last_step": round(norm, 5),
         "host_wall_s": round(wall, 3),
-        "roofline": {"kernel": "lm_head forward GEMM (gemm_kernel<256,256,NT,store bf16>)",
+        "roofline": {"kernel": "lm_head forward GEMM with the log-sum-exp epilogue "
+                               "(gemm_kernel<256,256,NT,lse>)" if fused else
+                               "lm_head forward GEMM (gemm_kernel<256,256,NT,store bf16>)",
                      "bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": LMHEAD_TRAFFIC_BYTES, "avg_launch_ms": round(lm_avg, 4), "launches": lm_n,
+                     "traffic": None if fused else LMHEAD_TRAFFIC_BYTES,
+                     "avg_launch_ms": round(lm_avg, 4), "launches": lm_n,
                      "flops_per_launch": lm_flops},
     }
     if breakdown:

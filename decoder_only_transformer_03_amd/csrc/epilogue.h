@@ -13,6 +13,12 @@ enum EpiKind : int {
                      // (+ column sums of the fp32 result into colsum, if set)
   EPI_PARTIAL = 6,   // split-K slice z: out[z*split_stride + m*ldo + n] = alpha*c  (fp32)
   EPI_BIAS = 7,      // out[m][n] = alpha*c + bias[n]                         (out: TO)
+  // Fused lm_head + cross-entropy (c = a logit; column n is vocabulary entry col0 + n):
+  EPI_LSE = 8,       // per row m and 64-column block b = n/64: (max, sum exp(c - max)) over
+                     // the block into part[2 (m*nblk + b) + 0, 1]; tlogit[m] = c at the
+                     // target's column                                       (fp32)
+  EPI_DLOGITS = 9,   // out[m][n] = (exp(c - lse[m]) - [col0 + n == tgt[m]]) / n_valid,
+                     // 0 for rows whose target is -1                        (out: TO)
 };
 
 struct EpiArgs {
@@ -27,7 +33,25 @@ struct EpiArgs {
   float alpha;
   long split_stride;
   float* colsum;  // EPI_GELU_BWD: [row block of 128][N] partial column sums, or null
+  // EPI_LSE / EPI_DLOGITS
+  const int32_t* tgt;   // target per row, -1 = no target
+  const float* lse;     // log-sum-exp per row (EPI_DLOGITS)
+  float* part;          // block partials, 2 floats per (row, 64-column block) (EPI_LSE)
+  float* tlogit;        // logit of the target per row (EPI_LSE)
+  const int* n_valid;   // rows with a target (EPI_DLOGITS)
+  long col0;            // vocabulary index of output column 0
+  int nblk;             // 64-column blocks per row of part (EPI_LSE)
 };
+
+// d(mean cross-entropy)/d(logit) of one element: softmax - onehot, times
+// `scale` (1/n_valid for a row with a target, else 0).
+__device__ __forceinline__ float dlogit(float c, float lse, bool is_target, float scale) {
+  return (__expf(c - lse) - (is_target ? 1.0f : 0.0f)) * scale;
+}
+__device__ __forceinline__ float dlogit_scale(const EpiArgs& e, int t) {
+  const int nv = *e.n_valid;
+  return t != -1 && nv > 0 ? 1.0f / (float)nv : 0.f;
+}
 
 // Does the epilogue read memory per element (residual, old value, aux)?
 constexpr bool epi_reads(int EPI) {
@@ -95,6 +119,12 @@ __device__ __forceinline__ void epi_store4(const EpiArgs& e, long m, int n, cons
   } else if constexpr (EPI == EPI_GELU_BWD) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) r[j] *= in[j];
+    st4(reinterpret_cast<TO*>(e.out) + m * e.ldo + n, r);
+  } else if constexpr (EPI == EPI_DLOGITS) {
+    const int t = e.tgt[m];
+    const float l = e.lse[m], sc = dlogit_scale(e, t);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) r[j] = dlogit(r[j], l, e.col0 + n + j == t, sc);
     st4(reinterpret_cast<TO*>(e.out) + m * e.ldo + n, r);
   }
 }

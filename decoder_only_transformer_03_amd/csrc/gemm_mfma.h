@@ -291,8 +291,25 @@ __device__ __forceinline__ void tile_epilogue(const EpiArgs& e, const f32x16_t (
   float csum[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) csum[j] = 0.f;
+  float dl_nv = 0.f;  // EPI_DLOGITS: 1 / n_valid
+  if constexpr (EPI == EPI_DLOGITS) {
+    const int nv = *e.n_valid;
+    dl_nv = nv > 0 ? 1.0f / (float)nv : 0.f;
+  }
 #pragma unroll
   for (int sm = 0; sm < SM; ++sm) {
+    // EPI_DLOGITS: target and log-sum-exp of this lane's rows of the round,
+    // loaded ahead of the LDS round trip
+    int dtg[4];
+    float dls[4];
+    if constexpr (EPI == EPI_DLOGITS) {
+#pragma unroll
+      for (int r8 = 0; r8 < 4; ++r8) {
+        const long m = mw + sm * 32 + r8 * 8 + (lane >> 3);
+        dtg[r8] = m < M ? e.tgt[m] : -1;
+        dls[r8] = m < M ? e.lse[m] : 0.f;
+      }
+    }
     // (1) fragments -> round buffer (row = lane%32, one 16-byte chunk each)
     {
       const int row = lane & 31;
@@ -324,6 +341,13 @@ __device__ __forceinline__ void tile_epilogue(const EpiArgs& e, const f32x16_t (
           for (int j = 0; j < 8; ++j) v[j] += bias8[j];
         }
         if constexpr (EPI == EPI_STORE || EPI == EPI_BIAS) {
+          st4(reinterpret_cast<TO*>(e.out) + m * e.ldo + nl, v);
+          st4(reinterpret_cast<TO*>(e.out) + m * e.ldo + nl + 4, v + 4);
+        } else if constexpr (EPI == EPI_DLOGITS) {
+          const int t = dtg[r8];
+          const float l = dls[r8], sc = t != -1 ? dl_nv : 0.f;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) v[j] = dlogit(v[j], l, e.col0 + nl + j == t, sc);
           st4(reinterpret_cast<TO*>(e.out) + m * e.ldo + nl, v);
           st4(reinterpret_cast<TO*>(e.out) + m * e.ldo + nl + 4, v + 4);
         } else if constexpr (EPI == EPI_BIAS_GELU) {
@@ -388,6 +412,64 @@ __device__ __forceinline__ void tile_epilogue(const EpiArgs& e, const f32x16_t (
         float* dst = e.colsum + (mw / 128) * (long)N + nl;
         st4(dst, csum);
         st4(dst + 4, csum + 4);
+      }
+    }
+  }
+}
+
+// EPI_LSE straight from the accumulators, no LDS staging: for each of its
+// rows a lane holds 32 of the wavefront's 64 columns (col = sn*32 + 8i + 4h +
+// j, h = lane/32) and lane ^ 32 the other 32, so a row's block maximum and
+// sum of exponentials take 32 lane-local steps and one exchange.  (alpha is
+// not applied: the logits are the plain products.)
+template <int BM, int BN, int WM, int WN, int SN, int SM>
+__device__ __forceinline__ void lse_epilogue(const EpiArgs& e, const f32x16_t (&acc)[SN][SM],
+                                             long m0, long n0, int M, int N, int lane, int wm,
+                                             int wn) {
+  constexpr int WTM = BM / WM, WTN = BN / WN;
+  static_assert(WTN == 64 && SN == 2, "one 64-column block of the row partials per wavefront");
+  const long mw = m0 + wm * WTM, nw = n0 + wn * WTN;
+  if (nw >= N) return;  // the whole block lies past the last column
+  // valid columns of the block, a multiple of 8, so a lane's group of 4
+  // columns is valid or not as a whole
+  const int lim = N - nw < 64 ? (int)(N - nw) : 64;
+  const int h4 = 4 * (lane >> 5);
+  float2* part = reinterpret_cast<float2*>(e.part) + nw / 64;
+#pragma unroll
+  for (int sm = 0; sm < SM; ++sm) {
+    const long m = mw + sm * 32 + (lane & 31);
+    const bool mrow = m < M;
+    const int t = mrow ? e.tgt[m] : -1;
+    float mx = -__builtin_inff();
+#pragma unroll
+    for (int g = 0; g < 8; ++g) {  // g = sn*4 + i: columns 8g + h4 .. 8g + h4 + 3
+      if (8 * g + h4 < lim) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) mx = fmaxf(mx, acc[g >> 2][sm][4 * (g & 3) + j]);
+      }
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    float sum = 0.f;
+#pragma unroll
+    for (int g = 0; g < 8; ++g) {
+      if (8 * g + h4 < lim) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) sum += __expf(acc[g >> 2][sm][4 * (g & 3) + j] - mx);
+      }
+    }
+    sum += __shfl_xor(sum, 32, 64);
+    if (mrow) {
+      if (h4 == 0) part[m * e.nblk] = make_float2(mx, sum);
+      const long c = (long)t - e.col0 - nw;  // the target's column within the block
+      if (c >= 0 && c < lim && (int)(c & 4) == h4) {
+        const int cg = (int)(c >> 3), cj = (int)(c & 3);
+        float tl = 0.f;
+#pragma unroll
+        for (int g = 0; g < 8; ++g)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            if (g == cg && j == cj) tl = acc[g >> 2][sm][4 * (g & 3) + j];
+        e.tlogit[m] = tl;
       }
     }
   }
@@ -642,7 +724,9 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(int M, int N, int
     }
     // the stage not holding the next item's first k-tile is free: 8 KB of
     // epilogue scratch per wavefront
-    if constexpr (WTN == 64)
+    if constexpr (EPI == EPI_LSE)
+      lse_epilogue<BM, BN, WM, WN, SN, SM>(e, acc, em0, en0, M, N, lane, wm, wn);
+    else if constexpr (WTN == 64)
       tile_epilogue<BM, BN, WM, WN, EPI, TO, SN, SM>(e, acc, em0, en0, esplit, M, N, lane, wm, wn,
                                                      smem[cur ^ 1] + wave * 4096);
     else
@@ -735,6 +819,15 @@ hipError_t dispatch(int M, int N, int K, const bf16_t* A, long lda, const bf16_t
       case EPI_PARTIAL:                                                                         \
         if constexpr (BN_ == 256)                                                               \
           return run<256, 256, 2, 4, LA, LB, EPI_PARTIAL, float>(M, N, K, A, lda, B, ldb, e, sk, s); \
+        break;                                                                                  \
+      /* fused lm_head: logits = x wte^T only (neither operand transposed) */                    \
+      case EPI_LSE:                                                                             \
+        if constexpr (BN_ == 256 && LA % 2 == 0 && LB % 2 == 0)                                 \
+          return run<256, 256, 2, 4, LA, LB, EPI_LSE, float>(M, N, K, A, lda, B, ldb, e, 1, s); \
+        break;                                                                                  \
+      case EPI_DLOGITS:                                                                         \
+        if constexpr (BN_ == 256 && LA % 2 == 0 && LB % 2 == 0)                                 \
+          return run<256, 256, 2, 4, LA, LB, EPI_DLOGITS, bf16_t>(M, N, K, A, lda, B, ldb, e, 1, s); \
         break;                                                                                  \
     }                                                                                           \
     return hipErrorInvalidValue;                                                                \

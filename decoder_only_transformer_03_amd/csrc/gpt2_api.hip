@@ -60,6 +60,8 @@ bool valid_config(const gpt2_config* c, std::string* why) {
   if (c->padded_vocab_size % 64 || c->padded_vocab_size > 51200)
     return fail("padded_vocab_size must be a multiple of 64 and <= 51200");
   if (c->block_size < 1 || c->max_batch < 1) return fail("block_size and max_batch must be >= 1");
+  if (c->head_chunk < 0 || c->head_chunk % 64)
+    return fail("head_chunk must be 0 or a positive multiple of 64");
   return true;
 }
 
@@ -149,8 +151,15 @@ struct gpt2 {
   float* x_final;
   float *meanf, *rstdf;
   void* z;
-  void* logits;
+  void* logits;           // (B*T, Vp) logits, then d(loss)/d(logits); null with a fused head
   float* row_loss;
+  // fused lm_head + cross-entropy (head_chunk > 0)
+  int head_chunk = 0;     // vocabulary columns per backward slice (<= Vp)
+  void* hslice;           // d(loss)/d(logits) of one slice: (B*T, head_chunk)
+  float* hpart;           // (B*T, Vp/64) block partials (max, sum of exp)
+  float* hlse;            // (B*T) log-sum-exp
+  float* htlogit;         // (B*T) logit of the target
+  int32_t* tgt;           // (B*T) copy of the targets, read again by the backward
   // backward scratch
   float* dres;
   void* dres_b;
@@ -224,7 +233,13 @@ size_t plan(const gpt2_config* c, char* base, gpt2* h) {
   float* meanf = a.take_n<float>(BT);
   float* rstdf = a.take_n<float>(BT);
   void* z = a.take(BT * C * es);
-  void* logits = a.take(BT * Vp * es);
+  const size_t hc = c->head_chunk > 0 ? std::min<size_t>(c->head_chunk, Vp) : 0;
+  void* logits = hc ? nullptr : a.take(BT * Vp * es);
+  void* hslice = hc ? a.take(BT * hc * es) : nullptr;
+  float* hpart = hc ? a.take_n<float>(BT * (Vp / 64) * 2) : nullptr;
+  float* hlse = hc ? a.take_n<float>(BT) : nullptr;
+  float* htlogit = hc ? a.take_n<float>(BT) : nullptr;
+  int32_t* tgt = hc ? a.take_n<int32_t>(BT) : nullptr;
   float* row_loss = a.take_n<float>(BT);
   float* dres = a.take_n<float>(BT * C);
   void* dres_b = c->precision == GPT2_BF16 ? a.take(BT * C * es) : nullptr;
@@ -247,6 +262,8 @@ size_t plan(const gpt2_config* c, char* base, gpt2* h) {
     h->A = acts;
     h->x_final = x_final; h->meanf = meanf; h->rstdf = rstdf; h->z = z; h->logits = logits;
     h->row_loss = row_loss;
+    h->head_chunk = (int)hc; h->hslice = hslice; h->hpart = hpart; h->hlse = hlse;
+    h->htlogit = htlogit; h->tgt = tgt;
     h->dres = dres; h->dres_b = dres_b; h->dxtmp = dxtmp; h->dbig = dbig; h->dqkv = dqkv;
     h->dy = dy; h->dbuf = dbuf; h->ln_partial = ln_partial; h->bias_partial = bias_partial;
     h->splitk = splitk;
@@ -371,6 +388,23 @@ gpt2_status run_forward(gpt2* h, const int32_t* d_idx, const int32_t* d_tgt, int
   }
   TIMED(h, GPT2_SITE_LN_FWD, launch_layernorm_fwd(at, h->x_final, P + h->lay.lnfw, P + h->lay.lnfb, h->z, h->meanf,
                                  h->rstdf, BT, C, s));
+  if (h->head_chunk) {
+    // fused lm_head + cross-entropy: per-row log-sum-exp partials and the
+    // target's logit straight from the GEMM's accumulators; no logits kept
+    // (and without targets there is nothing to compute)
+    if (!d_tgt) return GPT2_OK;
+    HIPTRY(h, hipMemcpyAsync(h->tgt, d_tgt, BT * sizeof(int32_t), hipMemcpyDeviceToDevice, s));
+    EpiArgs e = epi(nullptr, 0);
+    e.tgt = h->tgt;
+    e.part = h->hpart;
+    e.tlogit = h->htlogit;
+    e.nblk = Vp / 64;
+    TIMED(h, GPT2_SITE_LMHEAD_FWD, launch_gemm(at, (int)BT, Vp, C, h->z, C, false, W(h, h->lay.wte), C,
+                                               false, EPI_LSE, DT_F32, e, 0, s));
+    TIMED(h, GPT2_SITE_XENT, launch_head_loss(h->hpart, Vp / 64, h->htlogit, h->tgt, h->n_valid, h->hlse,
+                                              h->row_loss, h->loss, BT, Vp, h->err, s));
+    return GPT2_OK;
+  }
   EpiArgs e = epi(h->logits, Vp);
   TIMED(h, GPT2_SITE_LMHEAD_FWD, launch_gemm(at, (int)BT, Vp, C, h->z, C, false, W(h, h->lay.wte), C, false, EPI_STORE,
                         at, e, 0, s));
@@ -394,11 +428,36 @@ gpt2_status run_backward(gpt2* h, float scale) {
   void* dres_copy = at == DT_BF16 ? h->dres_b : nullptr;
 
   // lm_head (tied): dz = s dlogits wte ; dwte += s dlogits^T z
-  TIMED(h, GPT2_SITE_LMHEAD_DX, launch_gemm(at, M, C, Vp, h->logits, Vp, false, W(h, h->lay.wte), C, true, EPI_STORE,
-                        DT_F32, epi(h->dxtmp, C, scale), 0, s));
-  TIMED(h, GPT2_SITE_LMHEAD_DW, launch_gemm_wgrad(at, Vp, C, M, h->logits, Vp, true, h->z, C, true,
-                                                  G + h->lay.wte, C, scale, h->splitk,
-                                                  SPLITK_PART_ELEMS, s));
+  if (h->head_chunk) {
+    // fused head: per slice of the vocabulary, recompute the logits and turn
+    // them into d(loss)/d(logits) in the GEMM epilogue, then the slice's
+    // share of dz (accumulated over slices in a fixed order) and its rows of
+    // dwte
+    for (int v0 = 0; v0 < Vp; v0 += h->head_chunk) {
+      const int nc = std::min(h->head_chunk, Vp - v0);
+      EpiArgs e = epi(h->hslice, nc);
+      e.tgt = h->tgt;
+      e.lse = h->hlse;
+      e.n_valid = h->n_valid;
+      e.col0 = v0;
+      TIMED(h, GPT2_SITE_LMHEAD_RECOMP, launch_gemm(at, M, nc, C, h->z, C, false,
+                                                    W(h, h->lay.wte + (long)v0 * C), C, false,
+                                                    EPI_DLOGITS, at, e, 0, s));
+      TIMED(h, GPT2_SITE_LMHEAD_DX, launch_gemm(at, M, C, nc, h->hslice, nc, false,
+                                                W(h, h->lay.wte + (long)v0 * C), C, true,
+                                                v0 == 0 ? EPI_STORE : EPI_ACCUM, DT_F32,
+                                                epi(h->dxtmp, C, scale), 0, s));
+      TIMED(h, GPT2_SITE_LMHEAD_DW, launch_gemm_wgrad(at, nc, C, M, h->hslice, nc, true, h->z, C, true,
+                                                      G + h->lay.wte + (long)v0 * C, C, scale,
+                                                      h->splitk, SPLITK_PART_ELEMS, s));
+    }
+  } else {
+    TIMED(h, GPT2_SITE_LMHEAD_DX, launch_gemm(at, M, C, Vp, h->logits, Vp, false, W(h, h->lay.wte), C, true,
+                                              EPI_STORE, DT_F32, epi(h->dxtmp, C, scale), 0, s));
+    TIMED(h, GPT2_SITE_LMHEAD_DW, launch_gemm_wgrad(at, Vp, C, M, h->logits, Vp, true, h->z, C, true,
+                                                    G + h->lay.wte, C, scale, h->splitk,
+                                                    SPLITK_PART_ELEMS, s));
+  }
   // also the bias gradient of the last block's mlp c_proj: sum of dres
   TIMED(h, GPT2_SITE_LN_BWD, launch_layernorm_bwd(at, h->dxtmp, h->x_final, h->meanf, h->rstdf, P + h->lay.lnfw,
                                  h->dres, dres_copy, 0, h->ln_partial, G + h->lay.lnfw,
@@ -706,7 +765,11 @@ gpt2_status gpt2_get_activation(gpt2_t* h, int which, int layer, float* h_dst, s
     case GPT2_ACT_FC_DGELU: src = a->h; count = BT * 4 * C; break;
     case GPT2_ACT_FC_GELU: src = a->g; count = BT * 4 * C; break;
     case GPT2_ACT_LNF: src = h->z; count = BT * C; break;
-    case GPT2_ACT_LOGITS: src = h->logits; count = BT * c.padded_vocab_size; break;
+    case GPT2_ACT_LOGITS:
+      if (!h->logits) return fail(h, GPT2_E_STATE, "a fused lm_head (head_chunk > 0) keeps no logits");
+      src = h->logits;
+      count = BT * c.padded_vocab_size;
+      break;
     case GPT2_ACT_ROW_LOSS: src = h->row_loss; count = BT; f32 = true; break;
     default: return fail(h, GPT2_E_ARG, "unknown activation id");
   }

@@ -56,6 +56,40 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(int M, int N, int K,
     }
     __syncthreads();
   }
+  if constexpr (EPI == EPI_LSE) {
+    // the 16 threads of one ty (lanes 16 ty .. 16 ty + 15 of a wavefront)
+    // hold the 64 columns of the tile's rows ty*4 .. ty*4+3
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const long m = m0 + ty * 4 + i;
+      const long n = n0 + tx * 4;
+      float x[4], mx = -__builtin_inff();
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        x[j] = n + j < N ? e.alpha * acc[i][j] : -__builtin_inff();
+        mx = fmaxf(mx, x[j]);
+      }
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+      float sum = 0.f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) sum += n + j < N ? __expf(x[j] - mx) : 0.f;
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1) sum += __shfl_xor(sum, o, 64);
+      if (m < M) {
+        if (tx == 0) {
+          float* p = e.part + 2 * (m * e.nblk + n0 / 64);
+          p[0] = mx;
+          p[1] = sum;
+        }
+        const long c = e.tgt[m] - e.col0 - n;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if (c == j && n + j < N) e.tlogit[m] = x[j];
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     long m = m0 + ty * 4 + i;
@@ -95,6 +129,8 @@ static hipError_t f32_by_epi(int M, int N, int K, const float* A, long lda, cons
     }
     case EPI_GELU_BWD: return f32_run<AT, BT, EPI_GELU_BWD>(M, N, K, A, lda, B, ldb, e, 1, s);
     case EPI_PARTIAL: return f32_run<AT, BT, EPI_PARTIAL>(M, N, K, A, lda, B, ldb, e, split_k, s);
+    case EPI_LSE: return f32_run<AT, BT, EPI_LSE>(M, N, K, A, lda, B, ldb, e, 1, s);
+    case EPI_DLOGITS: return f32_run<AT, BT, EPI_DLOGITS>(M, N, K, A, lda, B, ldb, e, 1, s);
   }
   return hipErrorInvalidValue;
 }

@@ -488,6 +488,38 @@ __global__ __launch_bounds__(1024) void loss_reduce_kernel(const float* __restri
   }
 }
 
+// Fused lm_head loss, one wavefront per row: the row's log-sum-exp from the
+// (max m_b, sum s_b of exp(logit - m_b)) partials of its 64-column blocks,
+//   lse = M + log(sum_b s_b exp(m_b - M)),  M = max_b m_b,
+// and row_loss = lse - logit[target] (0 without a target; an out-of-range
+// target, flagged by count_valid, counts its logit as 0).
+__global__ __launch_bounds__(256) void head_lse_kernel(const float* __restrict__ part, int nblk,
+                                                       const float* __restrict__ tlogit,
+                                                       const int32_t* __restrict__ targets,
+                                                       long rows, int Vp, float* __restrict__ lse,
+                                                       float* __restrict__ row_loss) {
+  const long row = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= rows) return;
+  const float2* p = reinterpret_cast<const float2*>(part) + row * nblk;
+  float mx = -__builtin_inff();
+  for (int b = lane; b < nblk; b += 64) mx = fmaxf(mx, p[b].x);
+  mx = wave_max(mx);
+  float sum = 0.f;
+  for (int b = lane; b < nblk; b += 64) {
+    const float2 q = p[b];
+    sum += q.y * __expf(q.x - mx);
+  }
+  sum = wave_sum(sum);
+  if (lane == 0) {
+    const float l = mx + __logf(sum);
+    const int t = targets[row];
+    const float xt = t >= 0 && t < Vp ? tlogit[row] : 0.f;
+    lse[row] = l;
+    row_loss[row] = t != -1 ? l - xt : 0.f;
+  }
+}
+
 // Per-sequence mean loss over the positions with a target:
 // seq_loss[b] = sum_t row_loss[b*T + t] / #{t : targets[b*T + t] != -1}, 0 if none.
 // One workgroup per sequence; fp64 sum in a fixed order.
@@ -781,6 +813,16 @@ hipError_t launch_xent(DType t, void* logits, const int32_t* targets, int* n_val
                (float*)logits, targets, n_valid, row_loss, Vp)
          : xent_fused_kernel<float, false><<<(unsigned)rows, XENT_NT, 0, s>>>(
                (float*)logits, targets, n_valid, row_loss, Vp);
+  loss_reduce_kernel<<<1, 1024, 0, s>>>(row_loss, rows, n_valid, loss);
+  return hipGetLastError();
+}
+
+hipError_t launch_head_loss(const float* part, int nblk, const float* tlogit,
+                           const int32_t* targets, int* n_valid, float* lse, float* row_loss,
+                           float* loss, long rows, int Vp, int* err, hipStream_t s) {
+  count_valid_kernel<<<1, 1024, 0, s>>>(targets, rows, Vp, n_valid, err);
+  head_lse_kernel<<<(unsigned)((rows + 3) / 4), 256, 0, s>>>(part, nblk, tlogit, targets, rows,
+                                                             Vp, lse, row_loss);
   loss_reduce_kernel<<<1, 1024, 0, s>>>(row_loss, rows, n_valid, loss);
   return hipGetLastError();
 }

@@ -51,6 +51,11 @@ hipError_t launch_bias_grad(DType in_t, const void* X, long rows, int N, long ld
 hipError_t launch_xent(DType t, void* logits, const int32_t* targets, int* n_valid,
                        float* row_loss, float* loss, long rows, int Vp, int* err, bool grad,
                        hipStream_t s);
+// Fused lm_head loss from EPI_LSE partials: counts the rows with a target,
+// writes lse and row_loss per row and the mean loss.
+hipError_t launch_head_loss(const float* part, int nblk, const float* tlogit,
+                           const int32_t* targets, int* n_valid, float* lse, float* row_loss,
+                           float* loss, long rows, int Vp, int* err, hipStream_t s);
 hipError_t launch_seq_loss(const float* row_loss, const int32_t* targets, int B, int T,
                            float* seq_loss, hipStream_t s);
 hipError_t launch_grad_norm(const float* g, long n, double* partial, float max_norm,

@@ -22,7 +22,7 @@ GPT2_PARAMS, GPT2_GRADS, GPT2_ADAM_M, GPT2_ADAM_V = 0, 1, 2, 3
 SITES = ["EMBED_FWD", "LN_FWD", "QKV_FWD", "ATTN_FWD", "PROJ_FWD", "FC_FWD", "FCPROJ_FWD",
          "LMHEAD_FWD", "XENT", "LMHEAD_DX", "LMHEAD_DW", "LN_BWD", "FCPROJ_DX", "FCPROJ_DW", "FC_DX",
          "FC_DW", "PROJ_DX", "PROJ_DW", "ATTN_BWD", "QKV_DX", "QKV_DW", "BIAS_GRAD", "EMBED_BWD",
-         "GRAD_NORM", "ADAMW", "ZERO_GRAD"]
+         "GRAD_NORM", "ADAMW", "ZERO_GRAD", "LMHEAD_RECOMP"]
 ACT = {n: i for i, n in enumerate([
     "X_IN", "LN1", "QKV", "ATTN_Y", "LSE", "X_MID", "LN2", "FC_DGELU", "FC_GELU", "LNF", "LOGITS",
     "ROW_LOSS"])}
@@ -33,7 +33,8 @@ STATUS_NAMES = {0: "GPT2_OK", -1: "GPT2_E_ARG", -2: "GPT2_E_SHAPE", -3: "GPT2_E_
 class gpt2_config(ct.Structure):
     _fields_ = [("n_layer", ct.c_int32), ("n_head", ct.c_int32), ("n_embd", ct.c_int32),
                 ("vocab_size", ct.c_int32), ("padded_vocab_size", ct.c_int32),
-                ("block_size", ct.c_int32), ("max_batch", ct.c_int32), ("precision", ct.c_int32)]
+                ("block_size", ct.c_int32), ("max_batch", ct.c_int32), ("precision", ct.c_int32),
+                ("head_chunk", ct.c_int32)]
 
 
 class GPT2Error(RuntimeError):
@@ -100,11 +101,13 @@ EXPORTED = ["gpt2_num_params", "gpt2_workspace_bytes", "gpt2_init", "gpt2_set_pa
 
 
 def make_config(n_layer, n_head, n_embd, vocab_size, padded_vocab_size, block_size, max_batch,
-                precision):
+                precision, head_chunk=0):
+    """head_chunk > 0 selects the fused lm_head + cross-entropy (no logits
+    tensor; the backward recomputes the logits head_chunk columns at a time)."""
     if isinstance(precision, str):
         precision = {"fp32": GPT2_FP32, "bf16": GPT2_BF16}[precision]
     return gpt2_config(n_layer, n_head, n_embd, vocab_size, padded_vocab_size, block_size,
-                       max_batch, precision)
+                       max_batch, precision, head_chunk)
 
 
 def gpt2_num_params(cfg: gpt2_config) -> int:

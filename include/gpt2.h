@@ -80,6 +80,20 @@ typedef struct {
   int32_t block_size;
   int32_t max_batch;
   int32_t precision; /* gpt2_precision */
+  /* 0: the lm_head writes the (B*T, padded_vocab_size) logits and the
+   * cross-entropy turns them into their gradient in place.  > 0 (a multiple
+   * of 64): fused lm_head + cross-entropy that never stores those logits.
+   * The forward's GEMM epilogue reduces each row's logits to log-sum-exp
+   * partials over 64-column blocks and picks out the target's logit; the
+   * backward recomputes the logits slice by slice, head_chunk vocabulary
+   * columns at a time, turns each slice into its gradient in the epilogue
+   * and applies it to dz and dwte.  Same results up to rounding ("Let's
+   * reproduce GPT-2 (124M)", the remark on the fp32 logits tensor of the
+   * loss); one more (B*T, C, Vp) product per step; the workspace holds one
+   * (B*T, head_chunk) slice instead of the logits.  With a fused head a
+   * forward without targets stops after the final LayerNorm and
+   * GPT2_ACT_LOGITS is not available. */
+  int32_t head_chunk;
 } gpt2_config;
 
 typedef struct gpt2 gpt2_t; /* opaque handle */
@@ -213,7 +227,10 @@ enum {
 gpt2_status gpt2_get_activation(gpt2_t* h, int which, int layer, float* h_dst, size_t n);
 
 /* Kernel timing.  Launch sites of the step, for per-kernel measurement with
- * HIP events recorded on the handle's stream around each launch. */
+ * HIP events recorded on the handle's stream around each launch.  With a
+ * fused head (head_chunk > 0) LMHEAD_FWD is the partials GEMM, XENT the
+ * log-sum-exp and loss reduction, LMHEAD_RECOMP the backward's recomputation
+ * of a slice of logits, LMHEAD_DX/DW the slices' shares of dz and dwte. */
 enum {
   GPT2_SITE_EMBED_FWD = 0, GPT2_SITE_LN_FWD, GPT2_SITE_QKV_FWD, GPT2_SITE_ATTN_FWD,
   GPT2_SITE_PROJ_FWD, GPT2_SITE_FC_FWD, GPT2_SITE_FCPROJ_FWD, GPT2_SITE_LMHEAD_FWD,
@@ -221,7 +238,7 @@ enum {
   GPT2_SITE_FCPROJ_DX, GPT2_SITE_FCPROJ_DW, GPT2_SITE_FC_DX, GPT2_SITE_FC_DW,
   GPT2_SITE_PROJ_DX, GPT2_SITE_PROJ_DW, GPT2_SITE_ATTN_BWD, GPT2_SITE_QKV_DX,
   GPT2_SITE_QKV_DW, GPT2_SITE_BIAS_GRAD, GPT2_SITE_EMBED_BWD, GPT2_SITE_GRAD_NORM,
-  GPT2_SITE_ADAMW, GPT2_SITE_ZERO_GRAD, GPT2_NUM_SITES
+  GPT2_SITE_ADAMW, GPT2_SITE_ZERO_GRAD, GPT2_SITE_LMHEAD_RECOMP, GPT2_NUM_SITES
 };
 
 /* From now on, record an event pair around every launch of each site whose

@@ -69,3 +69,24 @@ def test_workspace_scales_with_batch():
     assert b > a
     # logits alone are B*T*Vp bf16
     assert b - a > 1024 * 50304 * 2
+
+
+def test_fused_head_config():
+    """head_chunk: 0 or a positive multiple of 64; the fused head's workspace
+    holds one (B*T, head_chunk) slice and the row partials instead of the
+    (B*T, Vp) logits."""
+    d = synthetic.model_dims("gpt2-124m")
+    for hc in (-64, 100, 32):
+        cfg = G.make_config(max_batch=2, precision="bf16", head_chunk=hc, **d)
+        assert G.gpt2_num_params(cfg) == 0, hc
+        with pytest.raises(G.GPT2Error):
+            G.gpt2_workspace_bytes(cfg)
+    full = G.gpt2_workspace_bytes(G.make_config(max_batch=16, precision="bf16", **d))
+    fused = G.gpt2_workspace_bytes(G.make_config(max_batch=16, precision="bf16", head_chunk=4096, **d))
+    BT, Vp = 16 * 1024, 50304
+    saved = BT * Vp * 2 - BT * 4096 * 2 - BT * (Vp // 64) * 8 - 3 * BT * 4
+    assert abs((full - fused) - saved) < 8 * 256
+    # a slice wider than the vocabulary is one slice of Vp columns
+    one = G.gpt2_workspace_bytes(G.make_config(max_batch=16, precision="bf16", head_chunk=65536, **d))
+    two = G.gpt2_workspace_bytes(G.make_config(max_batch=16, precision="bf16", head_chunk=Vp, **d))
+    assert one == two

@@ -25,7 +25,9 @@ def dev_ids(a):
     return torch.tensor(np.ascontiguousarray(a), dtype=torch.int32, device=DEV)
 
 
-def test_eval_fp32_tiny():
+@pytest.mark.parametrize("hc", [0, 192])
+def test_eval_fp32_tiny(hc):
+    """hc > 0: the fused lm_head + cross-entropy (no logits kept)."""
     d = synthetic.model_dims("tiny")
     cfg = O.Config(**d)
     B, T = 4, 64
@@ -33,14 +35,18 @@ def test_eval_fp32_tiny():
     idx, tgt = synthetic.uniform_batch(B, T, 512, seed=1101)
     tgt[1, :40] = -1
     tgt[3, :] = -1                                  # nothing to score
-    m = G.GPT2(G.make_config(max_batch=B, precision="fp32", **d), device=DEV)
+    m = G.GPT2(G.make_config(max_batch=B, precision="fp32", head_chunk=hc, **d), device=DEV)
     m.set_params(flat)
     di, dt = dev_ids(idx), dev_ids(tgt)
     loss_f = m.forward(di, dt, want_loss=True)
     seq = torch.full((B,), float("nan"), dtype=torch.float32, device=DEV)
     loss_e = m.eval(di, dt, seq_loss=seq, want_loss=True)
     assert loss_e == loss_f                          # bit-identical
-    logits = m.activation("LOGITS", 0, B * T * d["padded_vocab_size"])
+    if hc:
+        with pytest.raises(G.GPT2Error):
+            m.activation("LOGITS", 0, 1)
+    else:
+        logits = m.activation("LOGITS", 0, B * T * d["padded_vocab_size"])
     with pytest.raises(G.GPT2Error):
         m.backward(1.0)
     r_loss, cache = O.forward(flat, idx, tgt, cfg, keep_logits=True)
@@ -50,17 +56,19 @@ def test_eval_fp32_tiny():
     assert abs(loss_e - float(r_loss)) <= 1e-4 * abs(float(r_loss))
     assert got[3] == 0.0
     assert np.max(np.abs(got - ref)) <= 1e-4 * np.max(np.abs(ref))
-    lref = cache["logits"].reshape(-1).astype(np.float64)
-    assert np.max(np.abs(logits - lref)) <= 1e-4 * np.max(np.abs(lref))
+    if not hc:
+        lref = cache["logits"].reshape(-1).astype(np.float64)
+        assert np.max(np.abs(logits - lref)) <= 1e-4 * np.max(np.abs(lref))
 
 
-def test_eval_bf16_124m_sft_scores():
+@pytest.mark.parametrize("hc", [0, 4096])
+def test_eval_bf16_124m_sft_scores(hc):
     d = synthetic.model_dims("gpt2-124m")
     cfg = O.Config(**d)
     B, T = 16, 1024
     flat = synthetic.init_params(d, seed=42)
     idx, tgt = synthetic.sft_batch(B, T, seed=1004)
-    m = G.GPT2(G.make_config(max_batch=B, precision="bf16", **d), device=DEV)
+    m = G.GPT2(G.make_config(max_batch=B, precision="bf16", head_chunk=hc, **d), device=DEV)
     try:
         m.set_params(flat)
         seq = torch.zeros((B,), dtype=torch.float32, device=DEV)

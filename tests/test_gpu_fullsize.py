@@ -142,6 +142,41 @@ def test_sft_b16_masked_targets(m124):
     check_adamw_closed_form(m, flat, d, 2e-5, 0.0, norm)
 
 
+@pytest.mark.parametrize("kind", ["zipf", "sft"])
+def test_124m_b16_fused_head(kind):
+    """The fused lm_head + cross-entropy (vocabulary slices of 4096 columns)
+    on the benchmark's batch and on the masked fine-tuning batch: sampled
+    sequences' per-position losses against the oracle, ignored targets at
+    exactly zero loss, the batch loss the mean of the per-position losses,
+    and the AdamW closed form on the GPU's own gradients."""
+    d = synthetic.model_dims("gpt2-124m")
+    flat = synthetic.init_params(d, seed=42)
+    B, T = 16, 1024
+    if kind == "zipf":
+        idx, tgt = synthetic.zipf_batch(B, T, seed=1002)
+        rows, lr, wd = [4, 11], LR, WD
+    else:
+        idx, tgt = synthetic.sft_batch(B, T, seed=1004)
+        rows, lr, wd = [3, 9], 2e-5, 0.0
+    cfg = G.make_config(max_batch=B, precision="bf16", head_chunk=4096, **d)
+    m = G.GPT2(cfg, device=DEV)
+    try:
+        m.set_params(flat)
+        m.zero_grad()
+        loss = m.forward(dev_ids(idx), dev_ids(tgt), want_loss=True)
+        rl = m.activation("ROW_LOSS", 0, B * T).astype(np.float64).reshape(B, T)
+        ignored = tgt == -1
+        assert np.all(rl[ignored] == 0.0)
+        assert abs(loss - rl.sum() / np.sum(~ignored)) <= 1e-5 * abs(loss)
+        m.backward(1.0)
+        norm = m.adamw_step(lr, B1, B2, EPS, wd, CLIP, want_norm=True)
+        check_adamw_closed_form(m, flat, d, lr, wd, norm)
+    finally:
+        m.close()
+    ref = oracle_position_losses(d, flat, idx, tgt, rows, T)
+    check_rows(rl[rows], ref, f"fused head, {kind} B=16 sequences {rows}")
+
+
 def test_xl_b8_sampled_prefixes():
     """XL shape (48 layers, C=1600, 25 heads of 64), B=8, T=1024: the first
     256 positions of sequences 0 and 5 against the oracle."""

@@ -65,8 +65,8 @@ def per_tensor(cfg, a, b, skip=None):
     return out
 
 
-def run_gpu_step(d, prec, flat, idx, tgt, lr=LR, wd=WD):
-    cfg = G.make_config(max_batch=idx.shape[0], precision=prec, **d)
+def run_gpu_step(d, prec, flat, idx, tgt, lr=LR, wd=WD, head_chunk=0):
+    cfg = G.make_config(max_batch=idx.shape[0], precision=prec, head_chunk=head_chunk, **d)
     m = G.GPT2(cfg, device=DEV)
     m.set_params(flat)
     m.zero_grad()
@@ -78,7 +78,8 @@ def run_gpu_step(d, prec, flat, idx, tgt, lr=LR, wd=WD):
     out["row_loss"] = m.activation("ROW_LOSS", 0, B * T)
     out["dgelu"] = [m.activation("FC_DGELU", l, B * T * 4 * C) for l in range(d["n_layer"])]
     out["gelu"] = [m.activation("FC_GELU", l, B * T * 4 * C) for l in range(d["n_layer"])]
-    out["dlogits"] = m.activation("LOGITS", 0, B * T * d["padded_vocab_size"])
+    if not head_chunk:                      # a fused head keeps no logits
+        out["dlogits"] = m.activation("LOGITS", 0, B * T * d["padded_vocab_size"])
     m.backward(1.0)
     out["grads"] = m.get(G.GPT2_GRADS)
     out["norm"] = m.adamw_step(lr, B1, B2, EPS, wd, CLIP, want_norm=True)
@@ -104,15 +105,18 @@ def run_oracle_step(d, flat, idx, tgt, lr=LR, wd=WD, dtype=np.float32):
 # fp32, tiny model (the oracle finishes in well under a second)
 # ----------------------------------------------------------------------------
 
-@pytest.mark.parametrize("B,T", [(4, 64), (3, 37), (1, 1), (2, 64)])
-def test_fp32_tiny_step_matches_oracle(B, T):
+# hc > 0: the fused lm_head + cross-entropy, the backward's vocabulary
+# slices of hc columns (192: slices 192, 192, 128 of Vp = 512; 64: eight)
+@pytest.mark.parametrize("B,T,hc", [(4, 64, 0), (3, 37, 0), (1, 1, 0), (2, 64, 0),
+                                    (4, 64, 192), (3, 37, 512), (1, 1, 128), (2, 64, 64)])
+def test_fp32_tiny_step_matches_oracle(B, T, hc):
     d = synthetic.model_dims("tiny")
     cfg = O.Config(**d)
     flat = synthetic.init_params(d, seed=42)
     idx, tgt = synthetic.uniform_batch(B, T, 512, seed=1001 + T)
     if B == 2:
         tgt[0, :20] = -1                      # masked positions
-    g = run_gpu_step(d, "fp32", flat, idx, tgt)
+    g = run_gpu_step(d, "fp32", flat, idx, tgt, head_chunk=hc)
     r = run_oracle_step(d, flat, idx, tgt)
     print(f"\nB={B} T={T} loss gpu {g['loss']:.7f} oracle {r['loss']:.7f} "
           f"norm {g['norm']:.6f} / {r['norm']:.6f}")
@@ -131,10 +135,11 @@ def test_fp32_tiny_step_matches_oracle(B, T):
         h_ref = r["cache"]["layers"][l]["h"].reshape(-1).astype(np.float64)
         assert maxrel(g["gelu"][l], O.gelu_tanh(h_ref)) < 1e-4
         assert maxrel(g["dgelu"][l], O.gelu_tanh_grad(h_ref)) < 1e-4
-    dl_ref = r["cache"]["dlogits"].reshape(-1)
-    assert maxrel(g["dlogits"], dl_ref) < 1e-4
-    ign = np.repeat(tgt.reshape(-1) == -1, d["padded_vocab_size"])
-    assert np.all(g["dlogits"][ign] == 0.0)
+    if not hc:
+        dl_ref = r["cache"]["dlogits"].reshape(-1)
+        assert maxrel(g["dlogits"], dl_ref) < 1e-4
+        ign = np.repeat(tgt.reshape(-1) == -1, d["padded_vocab_size"])
+        assert np.all(g["dlogits"][ign] == 0.0)
     # gradients, per tensor
     kb = key_bias_mask(cfg)
     eg = per_tensor(cfg, g["grads"], r["grads"], skip=kb)
@@ -238,6 +243,38 @@ def test_error_codes():
     assert np.all(m.get(G.GPT2_GRADS) == 0.0)
 
 
+def test_fused_head_edges():
+    """Fused lm_head (fp32 tiny, slices of 192): no logits to read; a forward
+    without targets computes no loss and leaves nothing to differentiate; no
+    valid target gives loss 0 and zero gradients; an out-of-range target is
+    reported like the materialised head reports it."""
+    d = synthetic.model_dims("tiny")
+    cfg = G.make_config(max_batch=2, precision="fp32", head_chunk=192, **d)
+    m = G.GPT2(cfg, device=DEV)
+    m.set_params(synthetic.init_params(d, seed=1))
+    idx, tgt = synthetic.uniform_batch(2, 16, 512, seed=2)
+    m.forward(dev_ids(idx))
+    with pytest.raises(G.GPT2Error) as e:
+        m.activation("LOGITS", 0, 16)
+    assert e.value.status == G.GPT2_E_STATE
+    with pytest.raises(G.GPT2Error) as e:
+        m.backward(1.0)
+    assert e.value.status == G.GPT2_E_STATE
+    m.zero_grad()
+    none = np.full_like(tgt, -1)
+    assert m.forward(dev_ids(idx), dev_ids(none), want_loss=True) == 0.0
+    assert np.all(m.activation("ROW_LOSS", 0, 32) == 0.0)
+    m.backward(1.0)
+    assert np.all(m.get(G.GPT2_GRADS) == 0.0)
+    badt = tgt.copy()
+    badt[1, 5] = 512
+    with pytest.raises(G.GPT2Error) as e:
+        m.forward(dev_ids(idx), dev_ids(badt), want_loss=True)
+    assert e.value.status == G.GPT2_E_RANGE
+    loss = m.forward(dev_ids(idx), dev_ids(tgt), want_loss=True)
+    assert math.isfinite(loss)
+
+
 # ----------------------------------------------------------------------------
 # bf16, GPT-2 124M shape
 # ----------------------------------------------------------------------------
@@ -266,6 +303,23 @@ def test_bf16_124m_loss_and_activations(step_124m_b2):
 
 
 def test_bf16_124m_grads_and_update(step_124m_b2):
+    d, flat, idx, tgt, g, r = step_124m_b2
+    check_bf16_step(d, flat, g, r)
+
+
+def test_bf16_124m_fused_head(step_124m_b2):
+    """The same step with the fused lm_head + cross-entropy (vocabulary
+    slices of 4096 columns: twelve and a ragged 1152), against the same
+    oracle step and to the same tolerances."""
+    d, flat, idx, tgt, _, r = step_124m_b2
+    g = run_gpu_step(d, "bf16", flat, idx, tgt, head_chunk=4096)
+    print(f"\n124M bf16 B=2 fused head: loss gpu {g['loss']:.5f} oracle {r['loss']:.5f}")
+    assert abs(g["loss"] - r["loss"]) < 2e-2
+    assert maxrel(g["row_loss"], r["cache"]["row_loss"]) < 2e-2
+    check_bf16_step(d, flat, g, r)
+
+
+def check_bf16_step(d, flat, g, r):
     """bf16: gradients per tensor within 1.2e-2 normwise (bf16 storage of
     activations and of the gradients flowing between layers, about
     sqrt(#roundings) * 2^-9); the AdamW kernel exactly (the oracle's update
@@ -275,7 +329,6 @@ def test_bf16_124m_grads_and_update(step_124m_b2):
     of gpu - oracle over the element's row).  Below that floor the sign of g is not determined by
     any bf16 computation, and Adam's first step is lr * sign(g): those
     elements may differ by up to 2 lr, which is asserted instead."""
-    d, flat, idx, tgt, g, r = step_124m_b2
     cfg = O.Config(**d)
     kb = key_bias_mask(cfg)
     # the GPU's own gradients through the oracle's clip + AdamW

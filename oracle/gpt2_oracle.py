@@ -34,6 +34,14 @@ in the design notes):
   R6  AdamW: decoupled decay p <- p (1 - lr wd) on tensors with dim >= 2,
       then the moment updates, bias correction with t starting at 1, eps added
       to sqrt(v_hat).
+  R7  Sampling ("GPT-2 from Scratch", A generation loop): the logits of the
+      last position are divided by the temperature; top-k keeps every entry
+      not below the k-th largest value (entries tied with it stay); the
+      multinomial draw is the inverse CDF of a caller-supplied uniform u in
+      [0, 1) over the vocabulary in index order: the smallest i whose
+      cumulative probability exceeds u (if rounding leaves none, the last
+      entry with non-zero probability).  The context is cropped to its last
+      block_size tokens before every forward pass.
 The backward pass is the chain rule of the forward pass; it is pinned by
 central differences and by torch autograd in the CPU tests.
 """
@@ -393,6 +401,47 @@ def sequence_losses(row_loss, targets):
         n = int(valid[b].sum())
         out[b] = row_loss[b][valid[b]].sum() / n if n else 0.0
     return out
+
+
+def last_logits(flat_params, idx, cfg: Config):
+    """Logits of the last position of each sequence, (B, Vp) ("GPT-2 from
+    Scratch", The full model: without targets only the last position goes
+    through the lm_head)."""
+    _, cache = forward(flat_params, idx, None, cfg)
+    return cache["logits"][:, -1, :]
+
+
+def sample_next(logits, temperature, top_k, u):
+    """One draw per row (R7).  logits (B, V), u (B,) uniforms in [0, 1);
+    top_k None or <= 0 keeps everything.  Returns int64 tokens (B,)."""
+    x = np.asarray(logits, dtype=np.float64) / float(temperature)
+    B, V = x.shape
+    if top_k is not None and top_k > 0:
+        k = min(int(top_k), V)
+        kth = np.sort(x, axis=1)[:, V - k][:, None]        # k-th largest per row
+        x = np.where(x < kth, -np.inf, x)
+    p = np.exp(x - x.max(axis=1, keepdims=True))
+    p /= p.sum(axis=1, keepdims=True)
+    cdf = np.cumsum(p, axis=1)
+    out = np.empty(B, dtype=np.int64)
+    for b in range(B):
+        i = int(np.searchsorted(cdf[b], u[b], side="right"))   # first cdf > u
+        if i >= V:
+            i = int(np.nonzero(p[b] > 0)[0][-1])
+        out[b] = i
+    return out
+
+
+def generate(flat_params, idx, n_new, temperature, top_k, uniforms, cfg: Config):
+    """The pages' sampling loop (R7): n_new times, crop the running sequences
+    to their last block_size tokens, take the last position's logits, draw
+    with uniforms[:, step], append.  idx (B, T0); returns (B, T0 + n_new)."""
+    seq = np.asarray(idx, dtype=np.int64).copy()
+    for s in range(n_new):
+        ctx = seq[:, -cfg.block_size:]
+        nxt = sample_next(last_logits(flat_params, ctx, cfg), temperature, top_k, uniforms[:, s])
+        seq = np.concatenate([seq, nxt[:, None]], axis=1)
+    return seq
 
 
 def lr_at(step, max_lr=6e-4, min_lr=6e-5, warmup=100, max_steps=2000):

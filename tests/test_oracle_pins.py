@@ -405,3 +405,91 @@ def test_sequence_losses_pins():
     n = (tgt != -1).sum(axis=1)
     assert seq[2] == 0.0
     assert abs((seq * n).sum() / n.sum() - float(loss)) < 1e-12
+
+
+# ----------------------------------------------------------------------------
+# Sampling and the generation loop ("GPT-2 from Scratch", A generation loop)
+# ----------------------------------------------------------------------------
+
+def test_sample_inverse_cdf_on_uniform_logits():
+    """Equal logits: every token has probability 1/V, so the draw is
+    floor(u V) -- pins the index order and the strict 'exceeds u' boundary."""
+    V = 10
+    u = np.array([0.0, 0.05, 0.0999, 0.1, 0.55, 0.9999])
+    got = O.sample_next(np.zeros((len(u), V)), 1.0, None, u)
+    assert list(got) == [0, 0, 0, 1, 5, 9]
+
+
+def test_sample_top1_is_argmax():
+    rng = np.random.default_rng(5)
+    logits = rng.normal(size=(16, 300))
+    for u in (0.0, 0.3, 0.999999):
+        got = O.sample_next(logits, 0.7, 1, np.full(16, u))
+        assert np.array_equal(got, logits.argmax(axis=1))
+
+
+def test_sample_frequencies_match_truncated_softmax():
+    """Over a fine grid of u, token i is drawn for a fraction of the grid
+    equal to its probability: softmax(logits / temperature) restricted to the
+    top-k entries and renormalised (closed form, to 1/N)."""
+    logits = np.array([[2.0, -1.0, 0.5, 3.0, 0.0, 1.5]])
+    N = 60000
+    u = (np.arange(N) + 0.5) / N
+    for temp, k in ((1.0, None), (0.5, 3), (2.0, 4)):
+        x = logits[0] / temp
+        keep = np.argsort(-x)[:k] if k else np.arange(6)
+        p = np.zeros(6)
+        p[keep] = np.exp(x[keep] - x.max())
+        p /= p.sum()
+        got = np.array([O.sample_next(logits, temp, k, np.array([ui]))[0] for ui in u[::37]])
+        freq = np.bincount(got, minlength=6) / len(got)
+        assert np.max(np.abs(freq - p)) < 2.0 * 37 / N + 1e-12, (temp, k, freq, p)
+        assert np.all(freq[p == 0] == 0)
+
+
+def test_sample_topk_keeps_ties_at_the_threshold():
+    """k = 2 with the 2nd-largest value repeated: every entry equal to the
+    k-th largest stays, so 4 of 5 entries are drawable."""
+    logits = np.array([[3.0, 1.0, 1.0, 1.0, 0.0]])
+    e = math.exp(1.0)
+    p_top = math.exp(3.0) / (math.exp(3.0) + 3 * e)
+    assert O.sample_next(logits, 1.0, 2, np.array([p_top - 1e-9]))[0] == 0
+    assert O.sample_next(logits, 1.0, 2, np.array([p_top + 1e-9]))[0] == 1
+    assert O.sample_next(logits, 1.0, 2, np.array([1.0 - 1e-12]))[0] == 3
+
+
+def test_sample_temperature_divides_logits():
+    rng = np.random.default_rng(11)
+    logits = rng.normal(size=(64, 50))
+    u = rng.random(64)
+    for temp in (0.3, 1.7):
+        a = O.sample_next(logits, temp, 10, u)
+        b = O.sample_next(logits / temp, 1.0, 10, u)
+        assert np.array_equal(a, b)
+    # a colder distribution concentrates on the argmax
+    cold = O.sample_next(logits, 1e-3, None, u)
+    assert np.array_equal(cold, logits.argmax(axis=1))
+
+
+def test_generate_crops_to_the_last_block():
+    """The context is cropped to its last block_size tokens, so tokens that
+    have left the window cannot change what is drawn next; greedy (top-1)
+    steps are the argmax of the last position's logits."""
+    d = synthetic.model_dims("tiny")
+    cfg = O.Config(**d)
+    flat = synthetic.init_params(d, seed=3)
+    rng = np.random.default_rng(4)
+    prompt = rng.integers(0, 512, size=(2, d["block_size"] + 6))
+    uni = rng.random((2, 3))
+    a = O.generate(flat, prompt, 3, 0.9, 40, uni, cfg)
+    b = O.generate(flat, prompt[:, 6:], 3, 0.9, 40, uni, cfg)
+    assert a.shape == (2, d["block_size"] + 9)
+    assert np.array_equal(a[:, -3:], b[:, -3:])
+    assert np.array_equal(a[:, :-3], prompt)
+    # a change inside the window does change the logits
+    p2 = prompt.copy()
+    p2[:, -1] = (p2[:, -1] + 1) % 512
+    assert not np.allclose(O.last_logits(flat, p2[:, -64:], cfg), O.last_logits(flat, prompt[:, -64:], cfg))
+    g = O.generate(flat, prompt[:, :10], 2, 1.0, 1, uni, cfg)
+    assert g[0, 10] == O.last_logits(flat, prompt[:1, :10], cfg)[0].argmax()
+    assert np.array_equal(O.generate(flat, prompt[:, :10], 0, 1.0, None, uni, cfg), prompt[:, :10])

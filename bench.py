@@ -55,6 +55,12 @@ WORKLOADS = {
                                      wd=0.0, eval=True, head_chunk=4096,
                                      desc="GPT-2 124M evaluation pass, bf16, B=16, T=1024, Zipf "
                                           "ids, fused lm_head + cross-entropy (no logits tensor)"),
+    "gpt2-124m-generate": dict(model="gpt2-124m", B=8, T=32, data="zipf", lr=None, wd=0.0,
+                               gen=96, top_k=50,
+                               desc="GPT-2 124M sampling loop, bf16: 8 sequences, 32-token Zipf "
+                                    "prompts, 96 new tokens each, temperature 1, top-k 50, the "
+                                    "whole cropped context recomputed per token (no key/value "
+                                    "cache); value = new tokens per second"),
 }
 
 METRIC = "training tokens/sec + MFU, GPT-2 124M bf16 B=16 T=1024 on one MI355X"
@@ -97,6 +103,15 @@ def cpu_baseline(d, wl, seconds_hint=20.0):
         idx, tgt = synthetic.zipf_batch(1, T, seed=1002)
     m, v = np.zeros_like(flat), np.zeros_like(flat)
     t0 = time.perf_counter()
+    if wl.get("gen"):
+        n = 4
+        uni = synthetic.uniforms((1, n), seed=99).astype(np.float64)
+        t0 = time.perf_counter()
+        oracle.generate(flat, idx, n, 1.0, wl["top_k"], uni, cfg)
+        dt = time.perf_counter() - t0
+        return {"value": round(n / dt, 3), "unit": "new tokens/s", "cores": int(threads),
+                "kind": "oracle",
+                "sample": f"{n} new tokens of 1 sequence after a {T}-token prompt; {dt:.1f} s"}
     if wl.get("eval"):
         _, cache = oracle.forward(flat, idx, tgt, cfg)
         oracle.sequence_losses(cache["row_loss"], tgt)
@@ -157,8 +172,15 @@ def main():
     opt_step = [0]
 
     seq_loss = torch.zeros((B,), dtype=torch.float32, device="cuda:0")
+    n_gen = wl.get("gen", 0)
+    if n_gen:
+        gen_u = torch.tensor(synthetic.uniforms((B, n_gen), seed=99), device="cuda:0")
+        gen_out = torch.zeros((B, T + n_gen), dtype=torch.int32, device="cuda:0")
 
     def step():
+        if n_gen:
+            model.generate(dev[0][0], n_gen, gen_u, gen_out, 1.0, wl["top_k"])
+            return
         if wl.get("eval"):
             model.eval(dev[0][0], dev[0][1], seq_loss=seq_loss)
             return
@@ -191,11 +213,13 @@ def main():
     norm = model.get_grad_norm()
     model.sync()
     ms_step = ms_total / args.steps
-    tokens = B * T * accum
+    tokens = B * n_gen if n_gen else B * T * accum
     tok_s = tokens * args.steps / (ms_total / 1e3)
     f_causal, f_nano = flops_per_token(d, T)
     if wl.get("eval"):  # forward only: a third of the training step's work
         f_causal, f_nano = f_causal / 3.0, f_nano / 3.0
+    if n_gen:  # model flops are not the measure of a recomputing sampling loop
+        f_causal = f_nano = 0.0
 
     lm_ms, lm_n = sites.get("LMHEAD_FWD", (0.0, 0))
     lm_avg = lm_ms / max(lm_n, 1)
@@ -210,11 +234,19 @@ def main():
         br = model.timing_end()
         breakdown = {k: round(v[0] / 2, 4) for k, v in sorted(br.items(), key=lambda x: -x[1][0])}
 
+    roofline = {"kernel": "lm_head forward GEMM with the log-sum-exp epilogue "
+                          "(gemm_kernel<256,256,NT,lse>)" if fused else
+                          "lm_head forward GEMM (gemm_kernel<256,256,NT,store bf16>)",
+                "bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                "traffic": None if fused else LMHEAD_TRAFFIC_BYTES,
+                "avg_launch_ms": round(lm_avg, 4), "launches": lm_n,
+                "flops_per_launch": lm_flops}
     out = {
         "metric": METRIC if args.workload == "gpt2-124m" else
                   f"tokens/sec + MFU, {args.workload} on one MI355X",
         "value": round(tok_s, 1),
-        "unit": "tokens/s",
+        "unit": "new tokens/s" if n_gen else "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
@@ -233,14 +265,7 @@ def main():
         "loss_last_step": round(loss, 5),
         "grad_norm_last_step": round(norm, 5),
         "host_wall_s": round(wall, 3),
-        "roofline": {"kernel": "lm_head forward GEMM with the log-sum-exp epilogue "
-                               "(gemm_kernel<256,256,NT,lse>)" if fused else
-                               "lm_head forward GEMM (gemm_kernel<256,256,NT,store bf16>)",
-                     "bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                     "traffic": None if fused else LMHEAD_TRAFFIC_BYTES,
-                     "avg_launch_ms": round(lm_avg, 4), "launches": lm_n,
-                     "flops_per_launch": lm_flops},
+        "roofline": None if n_gen else roofline,
     }
     if breakdown:
         out["site_ms_per_step"] = breakdown

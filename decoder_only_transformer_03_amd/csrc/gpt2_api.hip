@@ -160,6 +160,9 @@ struct gpt2 {
   float* hlse;            // (B*T) log-sum-exp
   float* htlogit;         // (B*T) logit of the target
   int32_t* tgt;           // (B*T) copy of the targets, read again by the backward
+  // generation
+  float* gen_logits;      // (max_batch, Vp) last-position logits
+  int32_t* gen_idx;       // (max_batch, block_size) cropped context
   // backward scratch
   float* dres;
   void* dres_b;
@@ -241,6 +244,8 @@ size_t plan(const gpt2_config* c, char* base, gpt2* h) {
   float* htlogit = hc ? a.take_n<float>(BT) : nullptr;
   int32_t* tgt = hc ? a.take_n<int32_t>(BT) : nullptr;
   float* row_loss = a.take_n<float>(BT);
+  float* gen_logits = a.take_n<float>((size_t)c->max_batch * Vp);
+  int32_t* gen_idx = a.take_n<int32_t>(BT);
   float* dres = a.take_n<float>(BT * C);
   void* dres_b = c->precision == GPT2_BF16 ? a.take(BT * C * es) : nullptr;
   float* dxtmp = a.take_n<float>(BT * C);
@@ -264,6 +269,7 @@ size_t plan(const gpt2_config* c, char* base, gpt2* h) {
     h->row_loss = row_loss;
     h->head_chunk = (int)hc; h->hslice = hslice; h->hpart = hpart; h->hlse = hlse;
     h->htlogit = htlogit; h->tgt = tgt;
+    h->gen_logits = gen_logits; h->gen_idx = gen_idx;
     h->dres = dres; h->dres_b = dres_b; h->dxtmp = dxtmp; h->dbig = dbig; h->dqkv = dqkv;
     h->dy = dy; h->dbuf = dbuf; h->ln_partial = ln_partial; h->bias_partial = bias_partial;
     h->splitk = splitk;
@@ -345,8 +351,10 @@ gpt2_status sync(gpt2* h) {
   return check_device_flags(h);
 }
 
+// last_logits != null: no targets; only the last position of each sequence
+// goes through the lm_head, into last_logits (B, Vp) fp32.
 gpt2_status run_forward(gpt2* h, const int32_t* d_idx, const int32_t* d_tgt, int B, int T,
-                        bool grad) {
+                        bool grad, float* last_logits = nullptr) {
   const gpt2_config& c = h->cfg;
   const int C = c.n_embd, H = c.n_head, hd = C / H, Vp = c.padded_vocab_size;
   const long BT = (long)B * T;
@@ -388,6 +396,14 @@ gpt2_status run_forward(gpt2* h, const int32_t* d_idx, const int32_t* d_tgt, int
   }
   TIMED(h, GPT2_SITE_LN_FWD, launch_layernorm_fwd(at, h->x_final, P + h->lay.lnfw, P + h->lay.lnfb, h->z, h->meanf,
                                  h->rstdf, BT, C, s));
+  if (last_logits) {
+    // rows T-1, 2T-1, ... of z: a row stride of T*C
+    const size_t es = at == DT_BF16 ? 2 : 4;
+    const void* zl = static_cast<const char*>(h->z) + (size_t)(T - 1) * C * es;
+    TIMED(h, GPT2_SITE_LMHEAD_FWD, launch_gemm(at, B, Vp, C, zl, (long)T * C, false, W(h, h->lay.wte), C,
+                                               false, EPI_STORE, DT_F32, epi(last_logits, Vp), 0, s));
+    return GPT2_OK;
+  }
   if (h->head_chunk) {
     // fused lm_head + cross-entropy: per-row log-sum-exp partials and the
     // target's logit straight from the GEMM's accumulators; no logits kept
@@ -636,6 +652,59 @@ gpt2_status gpt2_forward(gpt2_t* h, const int32_t* d_idx, const int32_t* d_targe
   if (h_loss) {
     if (!d_targets) return fail(h, GPT2_E_ARG, "h_loss given without targets");
     return gpt2_get_loss(h, h_loss);
+  }
+  return GPT2_OK;
+}
+
+gpt2_status gpt2_forward_last(gpt2_t* h, const int32_t* d_idx, int B, int T, float* d_logits) {
+  if (!h || !d_idx || !d_logits) return GPT2_E_ARG;
+  if (B < 1 || B > h->cfg.max_batch || T < 1 || T > h->cfg.block_size)
+    return fail(h, GPT2_E_SHAPE, "need 1 <= B <= max_batch and 1 <= T <= block_size");
+  h->B = B;
+  h->T = T;
+  h->have_targets = false;
+  h->forward_done = false;
+  gpt2_status st = run_forward(h, d_idx, nullptr, B, T, false, d_logits);
+  if (st != GPT2_OK) return st;
+  h->forward_done = true;
+  return GPT2_OK;
+}
+
+gpt2_status gpt2_sample(gpt2_t* h, const float* d_logits, long ld, int B, int V, float temperature,
+                        int top_k, const float* d_uniform, int32_t* d_tokens) {
+  if (!h || !d_logits || !d_uniform || !d_tokens) return GPT2_E_ARG;
+  if (B < 1 || V < 1 || V > 53248 || ld < V || ld % 4 ||
+      reinterpret_cast<uintptr_t>(d_logits) % 16)
+    return fail(h, GPT2_E_ARG, "need B >= 1, 1 <= V <= 53248, ld >= V, ld % 4 == 0, "
+                               "16-byte aligned logits");
+  if (!(temperature > 0.f)) return fail(h, GPT2_E_ARG, "temperature must be > 0");
+  HIPTRY(h, launch_sample(d_logits, ld, B, V, temperature, top_k, d_uniform, 1, d_tokens, 1,
+                          h->stream));
+  return GPT2_OK;
+}
+
+gpt2_status gpt2_generate(gpt2_t* h, const int32_t* d_prompt, int B, int T0, int n_new,
+                          float temperature, int top_k, const float* d_uniform, int32_t* d_out) {
+  if (!h || !d_prompt || !d_out || (n_new > 0 && !d_uniform)) return GPT2_E_ARG;
+  if (B < 1 || B > h->cfg.max_batch || T0 < 1 || n_new < 0)
+    return fail(h, GPT2_E_SHAPE, "need 1 <= B <= max_batch, T0 >= 1, n_new >= 0");
+  if (!(temperature > 0.f)) return fail(h, GPT2_E_ARG, "temperature must be > 0");
+  const int Vp = h->cfg.padded_vocab_size, bs = h->cfg.block_size;
+  const long L = (long)T0 + n_new;  // row length of d_out
+  hipStream_t s = h->stream;
+  h->have_targets = false;
+  h->forward_done = false;
+  HIPTRY(h, hipMemcpy2DAsync(d_out, L * 4, d_prompt, (size_t)T0 * 4, (size_t)T0 * 4, B,
+                             hipMemcpyDeviceToDevice, s));
+  for (int step = 0; step < n_new; ++step) {
+    const long cur = T0 + step;                 // tokens so far
+    const int T = cur < bs ? (int)cur : bs;     // the context: the last block_size of them
+    HIPTRY(h, hipMemcpy2DAsync(h->gen_idx, (size_t)T * 4, d_out + (cur - T), L * 4, (size_t)T * 4,
+                               B, hipMemcpyDeviceToDevice, s));
+    gpt2_status st = run_forward(h, h->gen_idx, nullptr, B, T, false, h->gen_logits);
+    if (st != GPT2_OK) return st;
+    HIPTRY(h, launch_sample(h->gen_logits, Vp, B, Vp, temperature, top_k, d_uniform + step, n_new,
+                            d_out + cur, L, s));
   }
   return GPT2_OK;
 }

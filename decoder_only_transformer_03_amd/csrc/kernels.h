@@ -56,6 +56,11 @@ hipError_t launch_xent(DType t, void* logits, const int32_t* targets, int* n_val
 hipError_t launch_head_loss(const float* part, int nblk, const float* tlogit,
                            const int32_t* targets, int* n_valid, float* lse, float* row_loss,
                            float* loss, long rows, int Vp, int* err, hipStream_t s);
+// One draw per row: temperature, top-k (<= 0: all), inverse CDF of uni[r * u_stride];
+// the token goes to out[r * out_stride].  logits 16-byte aligned, ld % 4 == 0.
+hipError_t launch_sample(const float* logits, long ld, int rows, int V, float temperature,
+                         int top_k, const float* uni, long u_stride, int32_t* out,
+                         long out_stride, hipStream_t s);
 hipError_t launch_seq_loss(const float* row_loss, const int32_t* targets, int B, int T,
                            float* seq_loss, hipStream_t s);
 hipError_t launch_grad_norm(const float* g, long n, double* partial, float max_norm,

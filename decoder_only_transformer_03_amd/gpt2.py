@@ -67,6 +67,9 @@ def lib():
             "gpt2_set_step": (i32, [vp, i64]),
             "gpt2_forward": (i32, [vp, vp, vp, i32, i32, ct.POINTER(f32)]),
             "gpt2_eval": (i32, [vp, vp, vp, i32, i32, vp, ct.POINTER(f32)]),
+            "gpt2_forward_last": (i32, [vp, vp, i32, i32, vp]),
+            "gpt2_sample": (i32, [vp, vp, ct.c_long, i32, i32, f32, i32, vp, vp]),
+            "gpt2_generate": (i32, [vp, vp, i32, i32, i32, f32, i32, vp, vp]),
             "gpt2_get_loss": (i32, [vp, ct.POINTER(f32)]),
             "gpt2_zero_grad": (i32, [vp]),
             "gpt2_backward": (i32, [vp, f32]),
@@ -93,7 +96,7 @@ def lib():
 
 EXPORTED = ["gpt2_num_params", "gpt2_workspace_bytes", "gpt2_init", "gpt2_set_params", "gpt2_get",
             "gpt2_set_state", "gpt2_get_step", "gpt2_set_step", "gpt2_forward", "gpt2_eval",
-            "gpt2_get_loss",
+            "gpt2_forward_last", "gpt2_sample", "gpt2_generate", "gpt2_get_loss",
             "gpt2_zero_grad", "gpt2_backward", "gpt2_adamw_step", "gpt2_get_grad_norm",
             "gpt2_sync", "gpt2_last_error", "gpt2_destroy", "gpt2_get_activation",
             "gpt2_timing_begin", "gpt2_timing_end",
@@ -217,6 +220,28 @@ class GPT2:
                              ct.byref(loss) if want_loss else None)
         self._check(st)
         return loss.value if want_loss else None
+
+    # --- generation --------------------------------------------------------
+    def forward_last(self, idx, logits):
+        """Last-position logits of each sequence: idx int32 (B, T) device
+        tensor; logits float32 (B, padded_vocab_size) device tensor."""
+        B, T = idx.shape
+        self._check(lib().gpt2_forward_last(self.h, _ptr(idx), B, T, _ptr(logits)))
+
+    def sample(self, logits, uniform, tokens, temperature=1.0, top_k=0, V=None):
+        """One draw per row of logits (float32 (B, ld) device tensor, first V
+        columns) with the caller's uniforms (float32 (B,)) into tokens (int32
+        (B,)); top_k <= 0 keeps every entry."""
+        B, ld = logits.shape
+        self._check(lib().gpt2_sample(self.h, _ptr(logits), ld, B, ld if V is None else V,
+                                      float(temperature), int(top_k), _ptr(uniform), _ptr(tokens)))
+
+    def generate(self, prompt, n_new, uniforms, out, temperature=1.0, top_k=0):
+        """prompt int32 (B, T0); uniforms float32 (B, n_new); out int32
+        (B, T0 + n_new), all device tensors."""
+        B, T0 = prompt.shape
+        self._check(lib().gpt2_generate(self.h, _ptr(prompt), B, T0, int(n_new), float(temperature),
+                                        int(top_k), _ptr(uniforms), _ptr(out)))
 
     def get_loss(self) -> float:
         loss = ct.c_float(0.0)

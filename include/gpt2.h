@@ -165,6 +165,41 @@ gpt2_status gpt2_forward(gpt2_t* h, const int32_t* d_idx, const int32_t* d_targe
 gpt2_status gpt2_eval(gpt2_t* h, const int32_t* d_idx, const int32_t* d_targets, int B, int T,
                       float* d_seq_loss, float* h_loss);
 
+/* Generation ("GPT-2 from Scratch", The full model: without targets only
+ * the last position goes through the lm_head; A generation loop).
+ *
+ * gpt2_forward_last: forward pass over (B, T) ids with no targets; writes the
+ * lm_head output of the last position of each sequence, d_logits (device,
+ * fp32, (B, padded_vocab_size) row-major).  Activations of the pass stay
+ * readable; a following gpt2_backward returns GPT2_E_STATE. */
+gpt2_status gpt2_forward_last(gpt2_t* h, const int32_t* d_idx, int B, int T, float* d_logits);
+
+/* One draw per row of d_logits (device fp32, B rows of V entries at a row
+ * stride of ld floats; ld % 4 == 0, 16-byte aligned, V <= 53248):
+ *   x = logits / temperature (temperature > 0);
+ *   top_k > 0 and < V: entries below the k-th largest x are dropped (entries
+ *   equal to it stay); top_k <= 0 keeps all;
+ *   p = softmax(x) over the entries kept;
+ *   d_tokens[b] (device int32) = the smallest i whose cumulative probability
+ *   exceeds d_uniform[b] (device fp32, a uniform in [0, 1) per row supplied by
+ *   the caller: the multinomial draw as an inverse CDF over the entries in
+ *   index order); if rounding leaves none, the last entry kept.
+ * The k-th largest value is selected exactly; the sums are fp32 in a fixed
+ * order, so equal inputs give equal tokens. */
+gpt2_status gpt2_sample(gpt2_t* h, const float* d_logits, long ld, int B, int V, float temperature,
+                        int top_k, const float* d_uniform, int32_t* d_tokens);
+
+/* The sampling loop: d_out (device int32, (B, T0 + n_new) row-major) gets the
+ * prompt d_prompt (device int32, (B, T0)) followed by n_new drawn tokens.
+ * Step s crops each running sequence to its last block_size tokens, runs
+ * gpt2_forward_last on them and draws with gpt2_sample's rule over the
+ * padded vocabulary, using d_uniform[b * n_new + s] (device fp32, (B, n_new)).
+ * Each step recomputes the whole cropped context (no key/value cache).
+ * Asynchronous: nothing waits; out-of-range prompt ids are reported by the
+ * next synchronising call.  Saved activations are not readable afterwards. */
+gpt2_status gpt2_generate(gpt2_t* h, const int32_t* d_prompt, int B, int T0, int n_new,
+                          float temperature, int top_k, const float* d_uniform, int32_t* d_out);
+
 /* Loss of the last forward with targets; waits for the stream. */
 gpt2_status gpt2_get_loss(gpt2_t* h, float* h_loss);
 

@@ -26,6 +26,10 @@ Recipes (sources by page title and section):
   end-of-text padding; targets are -1 except where the next token is a
   response token or the closing end-of-text ("Pretraining and fine-tuning
   nanoGPT-124M", Supervised fine-tuning, loss masking).
+* Sampling inputs ("GPT-2 from Scratch", A generation loop): the uniforms a
+  multinomial draw consumes, U[0, 1) per row and step; stand-alone logit rows
+  N(0, scale), optionally rounded to a coarse grid so that many entries tie
+  (top-k thresholds with ties).
 """
 from __future__ import annotations
 
@@ -143,3 +147,17 @@ def config_batch(config, B, T, seed):
     if config == "sft":
         return sft_batch(B, T, seed)
     return zipf_batch(B, T, seed)
+
+
+def uniforms(shape, seed):
+    """U[0, 1) draws, float32 (the random numbers the sampling step uses)."""
+    return np.random.default_rng(seed).random(shape).astype(np.float32)
+
+
+def logit_rows(B, V, seed, scale=2.0, grid=None):
+    """(B, V) float32 logits, N(0, scale); with `grid`, rounded to multiples
+    of it (ties)."""
+    x = np.random.default_rng(seed).normal(0.0, scale, size=(B, V))
+    if grid:
+        x = np.round(x / grid) * grid
+    return x.astype(np.float32)

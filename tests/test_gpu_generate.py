@@ -1,0 +1,199 @@
+"""Generation path against the oracle: the last-position lm_head, the
+temperature / top-k / multinomial draw, and the sampling loop with its
+context crop ("GPT-2 from Scratch", The full model; A generation loop).
+
+The draw is an integer decided by floating point: the kernel sums fp32
+exponentials in its own order, the oracle fp64 ones.  A GPU token is accepted
+when it is the oracle's token, or when u lies within 1e-5 of the boundary
+between the oracle's token and the GPU's (there both are correct draws).
+Top-k is checked exactly: the GPU token is always among the oracle's kept
+entries (ties at the k-th value included).  fp32 logits within 1e-4 of the
+oracle's; bf16 (GPT-2 124M) logits within 2e-2 of the largest.  The loop is
+checked step by step: every drawn token is a valid draw for the oracle's
+logits of the GPU's own cropped context at that step."""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+from oracle import gpt2_oracle as O
+import synthetic
+from decoder_only_transformer_03_amd import gpt2 as G
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+BAND = 1e-5
+
+
+def dev(a, dtype):
+    return torch.tensor(np.ascontiguousarray(a), dtype=dtype, device=DEV)
+
+
+def oracle_draw_info(logits, temperature, top_k, u):
+    """Per row: the oracle token, the kept mask and the cumulative
+    probabilities (fp64)."""
+    x = np.asarray(logits, np.float64) / temperature
+    V = x.shape[1]
+    keep = np.ones_like(x, bool)
+    if top_k and top_k > 0:
+        k = min(top_k, V)
+        kth = np.sort(x, axis=1)[:, V - k][:, None]
+        keep = x >= kth
+    tok = O.sample_next(logits, temperature, top_k, u)
+    p = np.where(keep, np.exp(x - x.max(axis=1, keepdims=True)), 0.0)
+    cdf = np.cumsum(p / p.sum(axis=1, keepdims=True), axis=1)
+    return tok, keep, cdf
+
+
+def check_draws(got, logits, temperature, top_k, u, band=BAND):
+    tok, keep, cdf = oracle_draw_info(logits, temperature, top_k, u)
+    exact = 0
+    for b in range(len(got)):
+        g = int(got[b])
+        assert 0 <= g < logits.shape[1] and keep[b, g], (b, g)
+        if g == tok[b]:
+            exact += 1
+            continue
+        # a different token is a correct draw only if u sits on the boundary
+        lo = cdf[b, g - 1] if g > 0 else 0.0
+        hi = cdf[b, g]
+        assert lo - band <= u[b] <= hi + band, (b, g, tok[b], u[b], lo, hi)
+    return exact
+
+
+@pytest.fixture(scope="module")
+def tiny():
+    d = synthetic.model_dims("tiny")
+    m = G.GPT2(G.make_config(max_batch=4, precision="fp32", **d), device=DEV)
+    flat = synthetic.init_params(d, seed=21)
+    m.set_params(flat)
+    return d, flat, m
+
+
+@pytest.mark.parametrize("V,ld,temperature,top_k,grid", [
+    (512, 512, 1.0, 0, None), (512, 512, 0.7, 50, None), (512, 512, 1.3, 1, None),
+    (512, 512, 1.0, 7, 0.5),                          # ties at the k-th value
+    (50304, 50304, 1.0, 50, None), (50304, 50304, 0.8, 0, None),
+    (50257, 50304, 1.0, 200, 0.25), (50304, 50304, 1.0, 50304, None),
+    (3, 4, 1.0, 2, None), (53248, 53248, 1.0, 5, None)])
+def test_sample_matches_oracle(tiny, V, ld, temperature, top_k, grid):
+    _, _, m = tiny
+    B = 64
+    full = synthetic.logit_rows(B, ld, seed=V + top_k, grid=grid)
+    u = synthetic.uniforms(B, seed=V + 7)
+    u[:4] = [0.0, 0.5, 0.999999, 1e-7]
+    tokens = torch.full((B,), -5, dtype=torch.int32, device=DEV)
+    m.sample(dev(full, torch.float32), dev(u, torch.float32), tokens, temperature, top_k, V=V)
+    got = tokens.cpu().numpy()
+    exact = check_draws(got, full[:, :V], temperature, top_k, u.astype(np.float64))
+    print(f"\nV={V} ld={ld} T={temperature} k={top_k}: {exact}/{B} identical to the oracle")
+    assert exact >= B - 2
+    if top_k == 1 and grid is None:
+        assert np.array_equal(got, (full[:, :V] / temperature).argmax(axis=1))
+    # the same inputs give the same tokens
+    again = torch.zeros_like(tokens)
+    m.sample(dev(full, torch.float32), dev(u, torch.float32), again, temperature, top_k, V=V)
+    assert np.array_equal(again.cpu().numpy(), got)
+
+
+def test_sample_rejects_bad_arguments(tiny):
+    _, _, m = tiny
+    lg = torch.zeros((2, 512), dtype=torch.float32, device=DEV)
+    u = torch.zeros((2,), dtype=torch.float32, device=DEV)
+    t = torch.zeros((2,), dtype=torch.int32, device=DEV)
+    for kw in (dict(temperature=0.0), dict(temperature=-1.0), dict(V=600)):
+        with pytest.raises(G.GPT2Error) as e:
+            m.sample(lg, u, t, **{"temperature": 1.0, **kw})
+        assert e.value.status == G.GPT2_E_ARG
+    big = torch.zeros((1, 53252), dtype=torch.float32, device=DEV)
+    with pytest.raises(G.GPT2Error):
+        m.sample(big, u[:1], t[:1])
+
+
+def test_forward_last_fp32(tiny):
+    d, flat, m = tiny
+    cfg = O.Config(**d)
+    for B, T in ((3, 37), (1, 1), (4, 64)):
+        idx, _ = synthetic.uniform_batch(B, T, 512, seed=300 + T)
+        out = torch.zeros((B, d["padded_vocab_size"]), dtype=torch.float32, device=DEV)
+        m.forward_last(dev(idx, torch.int32), out)
+        got = out.cpu().numpy().astype(np.float64)
+        ref = O.last_logits(flat, idx, cfg).astype(np.float64)
+        err = np.max(np.abs(got - ref)) / np.max(np.abs(ref))
+        print(f"\nforward_last fp32 B={B} T={T}: maxrel {err:.2e}")
+        assert err < 1e-4
+    with pytest.raises(G.GPT2Error) as e:
+        m.backward(1.0)
+    assert e.value.status == G.GPT2_E_STATE
+
+
+@pytest.mark.parametrize("T0,n_new,temperature,top_k", [(60, 10, 0.8, 40), (3, 5, 1.0, 0),
+                                                        (70, 4, 1.2, 1), (5, 0, 1.0, 10)])
+def test_generate_fp32_step_by_step(tiny, T0, n_new, temperature, top_k):
+    """The prompt is copied; every drawn token is a valid draw for the
+    oracle's logits of the GPU's own context cropped to the last block_size
+    tokens (T0 + n_new crosses block_size = 64 in the first case, the prompt
+    is longer than it in the third)."""
+    d, flat, m = tiny
+    cfg = O.Config(**d)
+    B = 3
+    rng = np.random.default_rng(T0 * 31 + n_new)
+    prompt = rng.integers(0, 512, size=(B, T0)).astype(np.int32)
+    uni = synthetic.uniforms((B, max(n_new, 1)), seed=T0 + n_new)[:, :n_new]
+    out = torch.full((B, T0 + n_new), -7, dtype=torch.int32, device=DEV)
+    m.generate(dev(prompt, torch.int32), n_new, dev(uni, torch.float32), out, temperature, top_k)
+    got = out.cpu().numpy()
+    assert np.array_equal(got[:, :T0], prompt)
+    exact = 0
+    for s in range(n_new):
+        ctx = got[:, :T0 + s][:, -cfg.block_size:]
+        lg = O.last_logits(flat, ctx, cfg)
+        exact += check_draws(got[:, T0 + s], lg, temperature, top_k, uni[:, s].astype(np.float64))
+    assert exact >= B * n_new - 1
+    if exact == B * n_new:
+        ref = O.generate(flat, prompt, n_new, temperature, top_k, uni.astype(np.float64), cfg)
+        assert np.array_equal(got, ref)
+    # deterministic
+    out2 = torch.zeros_like(out)
+    m.generate(dev(prompt, torch.int32), n_new, dev(uni, torch.float32), out2, temperature, top_k)
+    assert torch.equal(out, out2)
+
+
+def test_generate_bf16_124m():
+    """GPT-2 124M bf16: last-position logits of a long context against the
+    oracle; a greedy loop whose every token is a maximum of the oracle's
+    logits up to the bf16 tolerance; a top-50 loop whose every token is among
+    the oracle's top 50 up to that tolerance."""
+    d = synthetic.model_dims("gpt2-124m")
+    cfg = O.Config(**d)
+    flat = synthetic.init_params(d, seed=42)
+    B = 2
+    m = G.GPT2(G.make_config(max_batch=B, precision="bf16", **d), device=DEV)
+    try:
+        m.set_params(flat)
+        idx, _ = synthetic.zipf_batch(B, 300, seed=77)
+        out = torch.zeros((B, d["padded_vocab_size"]), dtype=torch.float32, device=DEV)
+        m.forward_last(dev(idx, torch.int32), out)
+        got = out.cpu().numpy().astype(np.float64)
+        ref = O.last_logits(flat, idx, cfg).astype(np.float64)
+        tol = 2e-2 * np.max(np.abs(ref))
+        assert np.max(np.abs(got - ref)) < tol
+        prompt = idx[:, :24].astype(np.int32)
+        n_new = 4
+        uni = synthetic.uniforms((B, n_new), seed=5)
+        res = {}
+        for k in (1, 50):
+            o = torch.zeros((B, 24 + n_new), dtype=torch.int32, device=DEV)
+            m.generate(dev(prompt, torch.int32), n_new, dev(uni, torch.float32), o, 1.0, k)
+            res[k] = o.cpu().numpy()
+    finally:
+        m.close()
+    for k, seq in res.items():
+        assert np.array_equal(seq[:, :24], prompt)
+        for s in range(n_new):
+            lg = O.last_logits(flat, seq[:, :24 + s], cfg).astype(np.float64)
+            t = seq[:, 24 + s]
+            kth = np.sort(lg, axis=1)[:, -k]
+            for b in range(B):
+                assert lg[b, t[b]] >= kth[b] - tol, (k, s, b)
+    print(f"\nbf16 124M: forward_last maxabs {np.max(np.abs(got - ref)):.3e} (tol {tol:.3e})")

@@ -307,6 +307,24 @@ def test_bf16_124m_grads_and_update(step_124m_b2):
     check_bf16_step(d, flat, g, r)
 
 
+def test_bf16_124m_ragged_step():
+    """A batch whose sizes fit no tile: B=3, T=333 (999 rows: a partial
+    256-row GEMM tile and a partial 64-key attention block per sequence), some
+    targets masked, the fused head with ragged slices of 4096; the full
+    oracle step to the bf16 tolerances."""
+    d = synthetic.model_dims("gpt2-124m")
+    flat = synthetic.init_params(d, seed=42)
+    idx, tgt = synthetic.zipf_batch(3, 333, seed=1013)
+    tgt[1, :100] = -1
+    r = run_oracle_step(d, flat, idx, tgt)
+    for hc in (0, 4096):
+        g = run_gpu_step(d, "bf16", flat, idx, tgt, head_chunk=hc)
+        print(f"\n124M bf16 B=3 T=333 head_chunk {hc}: loss gpu {g['loss']:.5f} oracle {r['loss']:.5f}")
+        assert abs(g["loss"] - r["loss"]) < 2e-2
+        assert maxrel(g["row_loss"], r["cache"]["row_loss"]) < 2e-2
+        check_bf16_step(d, flat, g, r)
+
+
 def test_bf16_124m_fused_head(step_124m_b2):
     """The same step with the fused lm_head + cross-entropy (vocabulary
     slices of 4096 columns: twelve and a ragged 1152), against the same

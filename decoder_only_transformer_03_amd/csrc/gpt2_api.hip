@@ -371,28 +371,29 @@ gpt2_status run_forward(gpt2* h, const int32_t* d_idx, const int32_t* d_tgt, int
                                    C, s));
     EpiArgs e = epi(a.qkv, 3 * C);
     e.bias = P + o.attnb;
-    TIMED(h, GPT2_SITE_QKV_FWD, launch_gemm(at, (int)BT, 3 * C, C, a.u1, C, false, W(h, o.attnw), C, false, EPI_BIAS,
-                          at, e, 0, s));
+    TIMED(h, GPT2_SITE_QKV_FWD, launch_gemm_fill(at, (int)BT, 3 * C, C, a.u1, C, false, W(h, o.attnw), C,
+                                                 false, EPI_BIAS, at, e, h->splitk, SPLITK_PART_ELEMS, s));
     TIMED(h, GPT2_SITE_ATTN_FWD, launch_attn_fwd(at, a.qkv, a.y, a.lse, B, T, H, hd, s));
     e = epi(a.x_mid, C);
     e.bias = P + o.projb;
     e.resid = a.x_in;
     e.ldr = C;
-    TIMED(h, GPT2_SITE_PROJ_FWD, launch_gemm(at, (int)BT, C, C, a.y, C, false, W(h, o.projw), C, false, EPI_RESID,
-                          DT_F32, e, 0, s));
+    TIMED(h, GPT2_SITE_PROJ_FWD, launch_gemm_fill(at, (int)BT, C, C, a.y, C, false, W(h, o.projw), C, false,
+                                                  EPI_RESID, DT_F32, e, h->splitk, SPLITK_PART_ELEMS, s));
     TIMED(h, GPT2_SITE_LN_FWD, launch_layernorm_fwd(at, a.x_mid, P + o.ln2w, P + o.ln2b, a.u2, a.mean2, a.rstd2, BT,
                                    C, s));
     e = epi(a.h, 4 * C);
     e.out2 = a.g;
     e.bias = P + o.fcb;
-    TIMED(h, GPT2_SITE_FC_FWD, launch_gemm(at, (int)BT, 4 * C, C, a.u2, C, false, W(h, o.fcw), C, false,
-                          EPI_BIAS_GELU, at, e, 0, s));
+    TIMED(h, GPT2_SITE_FC_FWD, launch_gemm_fill(at, (int)BT, 4 * C, C, a.u2, C, false, W(h, o.fcw), C,
+                                                false, EPI_BIAS_GELU, at, e, h->splitk, SPLITK_PART_ELEMS, s));
     e = epi(x_out, C);
     e.bias = P + o.fc2b;
     e.resid = a.x_mid;
     e.ldr = C;
-    TIMED(h, GPT2_SITE_FCPROJ_FWD, launch_gemm(at, (int)BT, C, 4 * C, a.g, 4 * C, false, W(h, o.fc2w), 4 * C, false,
-                          EPI_RESID, DT_F32, e, 0, s));
+    TIMED(h, GPT2_SITE_FCPROJ_FWD, launch_gemm_fill(at, (int)BT, C, 4 * C, a.g, 4 * C, false, W(h, o.fc2w),
+                                                    4 * C, false, EPI_RESID, DT_F32, e, h->splitk,
+                                                    SPLITK_PART_ELEMS, s));
   }
   TIMED(h, GPT2_SITE_LN_FWD, launch_layernorm_fwd(at, h->x_final, P + h->lay.lnfw, P + h->lay.lnfb, h->z, h->meanf,
                                  h->rstdf, BT, C, s));

@@ -239,6 +239,78 @@ hipError_t launch_gemm_wgrad(DType in_t, int M, int N, int K, const void* A, lon
   return hipGetLastError();
 }
 
+// out = epilogue(sum_z part[z]) per group of 4 columns, slices summed in
+// order z = 0, 1, ... (deterministic).
+template <int EPI, typename TO>
+__global__ __launch_bounds__(256) void splitk_epi_kernel(const float* __restrict__ part, int splits,
+                                                         int M, int N, EpiArgs e) {
+  const long g = (long)blockIdx.x * 256 + threadIdx.x;  // group of 4 columns
+  const int gpr = N / 4;
+  if (g >= (long)M * gpr) return;
+  const long m = g / gpr;
+  const int n = (int)(g - m * gpr) * 4;
+  const long MN = (long)M * N;
+  float4 a = *reinterpret_cast<const float4*>(part + m * N + n);
+  for (int z = 1; z < splits; ++z) {
+    const float4 b = *reinterpret_cast<const float4*>(part + z * MN + m * N + n);
+    a.x += b.x; a.y += b.y; a.z += b.z; a.w += b.w;
+  }
+  const float c[4] = {a.x, a.y, a.z, a.w};
+  epi_apply4<EPI, TO>(e, m, n, c, 0);
+}
+
+hipError_t launch_gemm_fill(DType in_t, int M, int N, int K, const void* A, long lda, bool a_t,
+                            const void* B, long ldb, bool b_t, int epi, DType out_t,
+                            const EpiArgs& e, float* part, long part_elems, hipStream_t s) {
+  // Too few 256-row tiles to fill the persistent grid (a few hundred rows: the
+  // sampling loop's forward passes) and a deep enough contraction: K-slices
+  // into fp32 scratch, then the epilogue over their sum.
+  const bool kinds = epi == EPI_STORE || epi == EPI_BIAS || epi == EPI_BIAS_GELU || epi == EPI_RESID;
+  if (in_t == DT_BF16 && kinds && part && K % 64 == 0 && N % 4 == 0) {
+    const long slots = gemm_slots();
+    const long tiles = (long)((M + 255) / 256) * ((N + 255) / 256);
+    const int nkt = K / 64;
+    int S = (int)(slots / tiles);
+    if (S > nkt / 4) S = nkt / 4;
+    if (tiles * 2 <= slots && S >= 2) {
+      S = exact_splits(in_t, K, S);
+      while (S > 1 && (long)S * M * N > part_elems) S = exact_splits(in_t, K, S - 1);
+      if (S > 1) {
+        EpiArgs ep;
+        memset(&ep, 0, sizeof(ep));
+        ep.out = part;
+        ep.ldo = N;
+        ep.alpha = 1.f;
+        ep.split_stride = (long)M * N;
+        hipError_t r = launch_gemm(in_t, M, N, K, A, lda, a_t, B, ldb, b_t, EPI_PARTIAL, DT_F32,
+                                   ep, S, s);
+        if (r != hipSuccess) return r;
+        const long groups = (long)M * (N / 4);
+        const unsigned blocks = (unsigned)((groups + 255) / 256);
+        switch (epi) {
+          case EPI_STORE:
+            if (out_t == DT_BF16)
+              splitk_epi_kernel<EPI_STORE, bf16_t><<<blocks, 256, 0, s>>>(part, S, M, N, e);
+            else
+              splitk_epi_kernel<EPI_STORE, float><<<blocks, 256, 0, s>>>(part, S, M, N, e);
+            break;
+          case EPI_BIAS:
+            splitk_epi_kernel<EPI_BIAS, bf16_t><<<blocks, 256, 0, s>>>(part, S, M, N, e);
+            break;
+          case EPI_BIAS_GELU:
+            splitk_epi_kernel<EPI_BIAS_GELU, bf16_t><<<blocks, 256, 0, s>>>(part, S, M, N, e);
+            break;
+          default:
+            splitk_epi_kernel<EPI_RESID, float><<<blocks, 256, 0, s>>>(part, S, M, N, e);
+            break;
+        }
+        return hipGetLastError();
+      }
+    }
+  }
+  return launch_gemm(in_t, M, N, K, A, lda, a_t, B, ldb, b_t, epi, out_t, e, 0, s);
+}
+
 hipError_t launch_gemm(DType in_t, int M, int N, int K, const void* A, long lda, bool a_t,
                        const void* B, long ldb, bool b_t, int epi, DType out_t, const EpiArgs& e,
                        int split_k, hipStream_t s) {

@@ -80,6 +80,14 @@ hipError_t launch_gemm(DType in_t, int M, int N, int K, const void* A, long lda,
                        const void* B, long ldb, bool b_t, int epi, DType out_t, const EpiArgs& e,
                        int split_k, hipStream_t s);
 
+// launch_gemm for the forward epilogues (STORE, BIAS, BIAS_GELU, RESID) that,
+// when the output has too few tiles to fill the GPU and K is deep enough,
+// splits K into fp32 slices of `part` and applies the epilogue to their sum
+// in a second pass (same result up to the order of the fp32 additions).
+hipError_t launch_gemm_fill(DType in_t, int M, int N, int K, const void* A, long lda, bool a_t,
+                            const void* B, long ldb, bool b_t, int epi, DType out_t,
+                            const EpiArgs& e, float* part, long part_elems, hipStream_t s);
+
 // Weight gradient out[m][n] += alpha * sum_k A(m,k) B(n,k) for a long
 // contraction: split over k into fp32 slices of `part` (part_elems floats of
 // scratch), then summed in fixed order into out (deterministic).

@@ -114,6 +114,26 @@ std::vector<AdamChunk> make_chunks(const Layout& L) {
   return v;
 }
 
+// 64 x 64 tiles of every weight matrix that a GEMM also reads transposed (the
+// input-gradient products dx = dy W): wte and, per block, c_attn, attn
+// c_proj, c_fc and mlp c_proj.
+std::vector<TTile> make_ttiles(const Layout& L, const gpt2_config* c) {
+  std::vector<TTile> v;
+  const int C = c->n_embd, Vp = c->padded_vocab_size;
+  auto add = [&](long off, int rows, int cols) {
+    for (int r = 0; r < rows; r += 64)
+      for (int q = 0; q < cols; q += 64) v.push_back(TTile{off, rows, cols, r, q});
+  };
+  add(L.wte, Vp, C);
+  for (const LayerOff& o : L.layer) {
+    add(o.attnw, 3 * C, C);
+    add(o.projw, C, C);
+    add(o.fcw, 4 * C, C);
+    add(o.fc2w, C, 4 * C);
+  }
+  return v;
+}
+
 // Bump allocator over the workspace (256-byte aligned pieces).
 struct Arena {
   char* base;
@@ -140,6 +160,9 @@ struct gpt2 {
   // persistent state
   float *params, *grads, *m, *v;
   bf16_t* shadow;
+  bf16_t* shadow_t;  // transposed bf16 copies of the matrices in ttiles (same offsets)
+  TTile* ttiles;
+  int nttiles = 0;
   AdamChunk* chunks;
   int* err;
   int* n_valid;
@@ -207,6 +230,9 @@ size_t plan(const gpt2_config* c, char* base, gpt2* h) {
   float* m = a.take_n<float>(P);
   float* v = a.take_n<float>(P);
   bf16_t* shadow = c->precision == GPT2_BF16 ? a.take_n<bf16_t>(P) : nullptr;
+  bf16_t* shadow_t = c->precision == GPT2_BF16 ? a.take_n<bf16_t>(P) : nullptr;
+  std::vector<TTile> tt = c->precision == GPT2_BF16 ? make_ttiles(L, c) : std::vector<TTile>();
+  TTile* ttiles = a.take_n<TTile>(tt.size());
   AdamChunk* chunks = a.take_n<AdamChunk>(ch.size());
   int* err = a.take_n<int>(1);
   int* n_valid = a.take_n<int>(1);
@@ -262,6 +288,7 @@ size_t plan(const gpt2_config* c, char* base, gpt2* h) {
     h->lay = L;
     h->nchunks = (int)ch.size();
     h->params = params; h->grads = grads; h->m = m; h->v = v; h->shadow = shadow;
+    h->shadow_t = shadow_t; h->ttiles = ttiles; h->nttiles = (int)tt.size();
     h->chunks = chunks; h->err = err; h->n_valid = n_valid; h->loss = loss; h->norm = norm;
     h->clip = clip; h->norm_partial = norm_partial; h->idx = idx;
     h->A = acts;
@@ -293,6 +320,20 @@ gpt2_status fail(gpt2* h, gpt2_status s, const std::string& msg) {
 // bf16 copy of the weights in bf16 mode, the fp32 master otherwise
 const void* W(const gpt2* h, long off) {
   return h->act == DT_BF16 ? (const void*)(h->shadow + off) : (const void*)(h->params + off);
+}
+
+// B operand of an input-gradient product dx = dy W for the matrix W (rows x
+// cols, row-major at `off`), starting at row r0 of W: B(n, k) = W[r0 + k][n].
+// bf16 mode reads the transposed copy, k-contiguous; fp32 mode reads the
+// master weights transposed.
+struct WOp {
+  const void* p;
+  long ld;
+  bool t;
+};
+WOp w_dx(const gpt2* h, long off, long rows, long cols, long r0 = 0) {
+  if (h->act == DT_BF16) return {h->shadow_t + off + r0, rows, false};
+  return {h->params + off + r0 * cols, cols, true};
 }
 
 // Records an event pair around one launch when its site is being timed.
@@ -460,8 +501,8 @@ gpt2_status run_backward(gpt2* h, float scale) {
       TIMED(h, GPT2_SITE_LMHEAD_RECOMP, launch_gemm(at, M, nc, C, h->z, C, false,
                                                     W(h, h->lay.wte + (long)v0 * C), C, false,
                                                     EPI_DLOGITS, at, e, 0, s));
-      TIMED(h, GPT2_SITE_LMHEAD_DX, launch_gemm(at, M, C, nc, h->hslice, nc, false,
-                                                W(h, h->lay.wte + (long)v0 * C), C, true,
+      const WOp ws = w_dx(h, h->lay.wte, Vp, C, v0);
+      TIMED(h, GPT2_SITE_LMHEAD_DX, launch_gemm(at, M, C, nc, h->hslice, nc, false, ws.p, ws.ld, ws.t,
                                                 v0 == 0 ? EPI_STORE : EPI_ACCUM, DT_F32,
                                                 epi(h->dxtmp, C, scale), 0, s));
       TIMED(h, GPT2_SITE_LMHEAD_DW, launch_gemm_wgrad(at, nc, C, M, h->hslice, nc, true, h->z, C, true,
@@ -469,7 +510,8 @@ gpt2_status run_backward(gpt2* h, float scale) {
                                                       h->splitk, SPLITK_PART_ELEMS, s));
     }
   } else {
-    TIMED(h, GPT2_SITE_LMHEAD_DX, launch_gemm(at, M, C, Vp, h->logits, Vp, false, W(h, h->lay.wte), C, true,
+    const WOp wl = w_dx(h, h->lay.wte, Vp, C);
+    TIMED(h, GPT2_SITE_LMHEAD_DX, launch_gemm(at, M, C, Vp, h->logits, Vp, false, wl.p, wl.ld, wl.t,
                                               EPI_STORE, DT_F32, epi(h->dxtmp, C, scale), 0, s));
     TIMED(h, GPT2_SITE_LMHEAD_DW, launch_gemm_wgrad(at, Vp, C, M, h->logits, Vp, true, h->z, C, true,
                                                     G + h->lay.wte, C, scale, h->splitk,
@@ -490,12 +532,14 @@ gpt2_status run_backward(gpt2* h, float scale) {
     e.aux = a.h;
     e.ldx = 4 * C;
     if (at == DT_BF16) e.colsum = h->colsum_partial;
-    TIMED(h, GPT2_SITE_FCPROJ_DX, launch_gemm(at, M, 4 * C, C, dres_in, C, false, W(h, o.fc2w), 4 * C, true,
+    const WOp w2 = w_dx(h, o.fc2w, C, 4 * C);
+    TIMED(h, GPT2_SITE_FCPROJ_DX, launch_gemm(at, M, 4 * C, C, dres_in, C, false, w2.p, w2.ld, w2.t,
                           EPI_GELU_BWD, at, e, 0, s));
     TIMED(h, GPT2_SITE_FCPROJ_DW, launch_gemm_wgrad(at, C, 4 * C, M, dres_in, C, true, a.g, 4 * C, true,
                                                     G + o.fc2w, 4 * C, 1.f, h->splitk,
                                                     SPLITK_PART_ELEMS, s));
-    TIMED(h, GPT2_SITE_FC_DX, launch_gemm(at, M, C, 4 * C, h->dbig, 4 * C, false, W(h, o.fcw), C, true, EPI_STORE,
+    const WOp w1 = w_dx(h, o.fcw, 4 * C, C);
+    TIMED(h, GPT2_SITE_FC_DX, launch_gemm(at, M, C, 4 * C, h->dbig, 4 * C, false, w1.p, w1.ld, w1.t, EPI_STORE,
                           DT_F32, epi(h->dxtmp, C), 0, s));
     TIMED(h, GPT2_SITE_FC_DW, launch_gemm_wgrad(at, 4 * C, C, M, h->dbig, 4 * C, true, a.u2, C, true,
                                                 G + o.fcw, C, 1.f, h->splitk, SPLITK_PART_ELEMS, s));
@@ -507,13 +551,15 @@ gpt2_status run_backward(gpt2* h, float scale) {
                                    dres_copy, 1, h->ln_partial, G + o.ln2w, G + o.ln2b,
                                    G + o.projb, BT, C, s));
     // x_mid = x_in + c_proj(attn(ln_1(x_in)))
-    TIMED(h, GPT2_SITE_PROJ_DX, launch_gemm(at, M, C, C, dres_in, C, false, W(h, o.projw), C, true, EPI_STORE, at,
+    const WOp wp = w_dx(h, o.projw, C, C);
+    TIMED(h, GPT2_SITE_PROJ_DX, launch_gemm(at, M, C, C, dres_in, C, false, wp.p, wp.ld, wp.t, EPI_STORE, at,
                           epi(h->dy, C), 0, s));
     TIMED(h, GPT2_SITE_PROJ_DW, launch_gemm_wgrad(at, C, C, M, dres_in, C, true, a.y, C, true,
                                                   G + o.projw, C, 1.f, h->splitk, SPLITK_PART_ELEMS,
                                                   s));
     TIMED(h, GPT2_SITE_ATTN_BWD, launch_attn_bwd(at, a.qkv, a.y, a.lse, h->dy, h->dqkv, h->dbuf, B, T, H, hd, s));
-    TIMED(h, GPT2_SITE_QKV_DX, launch_gemm(at, M, C, 3 * C, h->dqkv, 3 * C, false, W(h, o.attnw), C, true,
+    const WOp wq = w_dx(h, o.attnw, 3 * C, C);
+    TIMED(h, GPT2_SITE_QKV_DX, launch_gemm(at, M, C, 3 * C, h->dqkv, 3 * C, false, wq.p, wq.ld, wq.t,
                           EPI_STORE, DT_F32, epi(h->dxtmp, C), 0, s));
     TIMED(h, GPT2_SITE_QKV_DW, launch_gemm_wgrad(at, 3 * C, C, M, h->dqkv, 3 * C, true, a.u1, C, true,
                                                  G + o.attnw, C, 1.f, h->splitk, SPLITK_PART_ELEMS,
@@ -574,9 +620,14 @@ gpt2_status gpt2_init(const gpt2_config* cfg, void* d_workspace, size_t ws_bytes
   std::vector<AdamChunk> ch = make_chunks(h->lay);
   hipError_t e = hipMemcpyAsync(h->chunks, ch.data(), ch.size() * sizeof(AdamChunk),
                                 hipMemcpyHostToDevice, h->stream);
+  std::vector<TTile> tt = h->nttiles ? make_ttiles(h->lay, cfg) : std::vector<TTile>();
+  if (e == hipSuccess && !tt.empty())
+    e = hipMemcpyAsync(h->ttiles, tt.data(), tt.size() * sizeof(TTile), hipMemcpyHostToDevice,
+                       h->stream);
   for (float* t : {h->params, h->grads, h->m, h->v})
     if (e == hipSuccess) e = launch_fill(t, h->lay.P, 0.f, h->stream);
   if (e == hipSuccess && h->shadow) e = hipMemsetAsync(h->shadow, 0, h->lay.P * 2, h->stream);
+  if (e == hipSuccess && h->shadow_t) e = hipMemsetAsync(h->shadow_t, 0, h->lay.P * 2, h->stream);
   if (e == hipSuccess) e = hipMemsetAsync(h->err, 0, sizeof(int), h->stream);
   if (e == hipSuccess) e = hipStreamSynchronize(h->stream);
   if (e != hipSuccess) {
@@ -593,7 +644,10 @@ gpt2_status gpt2_set_params(gpt2_t* h, const float* src, size_t n, int src_on_de
   HIPTRY(h, hipMemcpyAsync(h->params, src, n * 4,
                            src_on_device ? hipMemcpyDeviceToDevice : hipMemcpyHostToDevice,
                            h->stream));
-  if (h->shadow) HIPTRY(h, launch_f32_to_bf16(h->params, h->shadow, (long)n, h->stream));
+  if (h->shadow) {
+    HIPTRY(h, launch_f32_to_bf16(h->params, h->shadow, (long)n, h->stream));
+    HIPTRY(h, launch_transpose_tiles(h->shadow, h->shadow_t, h->ttiles, h->nttiles, h->stream));
+  }
   for (float* t : {h->grads, h->m, h->v}) HIPTRY(h, launch_fill(t, (long)n, 0.f, h->stream));
   h->step = 0;
   if (!src_on_device) HIPTRY(h, hipStreamSynchronize(h->stream));
@@ -764,6 +818,9 @@ gpt2_status gpt2_adamw_step(gpt2_t* h, float lr, float beta1, float beta2, float
   TIMED(h, GPT2_SITE_ADAMW, launch_adamw(h->chunks, h->nchunks, h->params, h->grads, h->m, h->v, h->shadow,
                          h->clip, lr, beta1, beta2, eps, weight_decay, step_size, inv_sqrt_bc2,
                          h->stream));
+  if (h->shadow_t)
+    TIMED(h, GPT2_SITE_WEIGHT_T, launch_transpose_tiles(h->shadow, h->shadow_t, h->ttiles,
+                                                        h->nttiles, h->stream));
   if (h_grad_norm) return gpt2_get_grad_norm(h, h_grad_norm);
   return GPT2_OK;
 }

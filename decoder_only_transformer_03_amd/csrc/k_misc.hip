@@ -817,6 +817,46 @@ hipError_t launch_xent(DType t, void* logits, const int32_t* targets, int* n_val
   return hipGetLastError();
 }
 
+// Transposed copy of 64 x 64 bf16 tiles through LDS: 256 threads, each
+// moving two 8-element row pieces in and two 8-element column pieces out.
+__global__ __launch_bounds__(256) void transpose_tiles_kernel(const bf16_t* __restrict__ src,
+                                                              bf16_t* __restrict__ dst,
+                                                              const TTile* __restrict__ tiles) {
+  __shared__ uint16_t t[64][66];  // padded rows: column reads spread over the banks
+  const TTile tt = tiles[blockIdx.x];
+  const int tid = threadIdx.x, q = tid & 7;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int r = (tid >> 3) + 32 * h;
+    const uint4 v = *reinterpret_cast<const uint4*>(src + tt.off + (long)(tt.r0 + r) * tt.cols +
+                                                    tt.c0 + 8 * q);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      t[r][8 * q + 2 * j] = (uint16_t)(w[j] & 0xffffu);
+      t[r][8 * q + 2 * j + 1] = (uint16_t)(w[j] >> 16);
+    }
+  }
+  __syncthreads();
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int c = (tid >> 3) + 32 * h;
+    uint32_t w[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      w[j] = (uint32_t)t[8 * q + 2 * j][c] | ((uint32_t)t[8 * q + 2 * j + 1][c] << 16);
+    *reinterpret_cast<uint4*>(dst + tt.off + (long)(tt.c0 + c) * tt.rows + tt.r0 + 8 * q) =
+        make_uint4(w[0], w[1], w[2], w[3]);
+  }
+}
+
+hipError_t launch_transpose_tiles(const bf16_t* src, bf16_t* dst, const TTile* tiles, int ntiles,
+                                  hipStream_t s) {
+  if (ntiles <= 0) return hipSuccess;
+  transpose_tiles_kernel<<<(unsigned)ntiles, 256, 0, s>>>(src, dst, tiles);
+  return hipGetLastError();
+}
+
 hipError_t launch_head_loss(const float* part, int nblk, const float* tlogit,
                            const int32_t* targets, int* n_valid, float* lse, float* row_loss,
                            float* loss, long rows, int Vp, int* err, hipStream_t s) {

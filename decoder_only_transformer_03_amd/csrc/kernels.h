@@ -25,6 +25,16 @@ struct AdamChunk {
   int flags;   // bit 0: weight decay applies (tensor has dim >= 2)
 };
 
+// One 64 x 64 tile of a row-major bf16 matrix (rows x cols) at element
+// offset `off`, with its first row and column.
+struct TTile {
+  long off;
+  int rows, cols, r0, c0;
+};
+// dst (same offset) = the transpose, cols x rows, of every listed tile.
+hipError_t launch_transpose_tiles(const bf16_t* src, bf16_t* dst, const TTile* tiles, int ntiles,
+                                  hipStream_t s);
+
 int ln_bwd_blocks(long rows);
 
 hipError_t launch_embed_fwd(const int32_t* idx_in, int32_t* idx_saved, const float* wte,

@@ -265,7 +265,9 @@ gpt2_status gpt2_get_activation(gpt2_t* h, int which, int layer, float* h_dst, s
  * HIP events recorded on the handle's stream around each launch.  With a
  * fused head (head_chunk > 0) LMHEAD_FWD is the partials GEMM, XENT the
  * log-sum-exp and loss reduction, LMHEAD_RECOMP the backward's recomputation
- * of a slice of logits, LMHEAD_DX/DW the slices' shares of dz and dwte. */
+ * of a slice of logits, LMHEAD_DX/DW the slices' shares of dz and dwte.
+ * WEIGHT_T is the refresh, after each AdamW step, of the transposed bf16
+ * weight copies that the input-gradient products read. */
 enum {
   GPT2_SITE_EMBED_FWD = 0, GPT2_SITE_LN_FWD, GPT2_SITE_QKV_FWD, GPT2_SITE_ATTN_FWD,
   GPT2_SITE_PROJ_FWD, GPT2_SITE_FC_FWD, GPT2_SITE_FCPROJ_FWD, GPT2_SITE_LMHEAD_FWD,
@@ -273,7 +275,8 @@ enum {
   GPT2_SITE_FCPROJ_DX, GPT2_SITE_FCPROJ_DW, GPT2_SITE_FC_DX, GPT2_SITE_FC_DW,
   GPT2_SITE_PROJ_DX, GPT2_SITE_PROJ_DW, GPT2_SITE_ATTN_BWD, GPT2_SITE_QKV_DX,
   GPT2_SITE_QKV_DW, GPT2_SITE_BIAS_GRAD, GPT2_SITE_EMBED_BWD, GPT2_SITE_GRAD_NORM,
-  GPT2_SITE_ADAMW, GPT2_SITE_ZERO_GRAD, GPT2_SITE_LMHEAD_RECOMP, GPT2_NUM_SITES
+  GPT2_SITE_ADAMW, GPT2_SITE_ZERO_GRAD, GPT2_SITE_LMHEAD_RECOMP, GPT2_SITE_WEIGHT_T,
+  GPT2_NUM_SITES
 };
 
 /* From now on, record an event pair around every launch of each site whose

@@ -197,3 +197,20 @@ def test_generate_bf16_124m():
             for b in range(B):
                 assert lg[b, t[b]] >= kth[b] - tol, (k, s, b)
     print(f"\nbf16 124M: forward_last maxabs {np.max(np.abs(got - ref)):.3e} (tol {tol:.3e})")
+
+
+def test_generate_same_with_fused_head_config(tiny):
+    """A model configured with the fused lm_head runs the same last-position
+    head when generating: identical tokens for identical inputs."""
+    d, flat, m = tiny
+    m2 = G.GPT2(G.make_config(max_batch=4, precision="fp32", head_chunk=128, **d), device=DEV)
+    m2.set_params(flat)
+    B, T0, n_new = 3, 40, 6
+    prompt = np.random.default_rng(8).integers(0, 512, size=(B, T0)).astype(np.int32)
+    uni = synthetic.uniforms((B, n_new), seed=9)
+    outs = []
+    for mm in (m, m2):
+        o = torch.zeros((B, T0 + n_new), dtype=torch.int32, device=DEV)
+        mm.generate(dev(prompt, torch.int32), n_new, dev(uni, torch.float32), o, 0.9, 30)
+        outs.append(o.cpu().numpy())
+    assert np.array_equal(outs[0], outs[1])

@@ -94,6 +94,11 @@ def cpu_baseline(d, wl, seconds_hint=20.0):
             if threadpoolctl.threadpool_info() else 1
     except Exception:
         threads = len(os.sched_getaffinity(0))
+    try:
+        b = np.show_config(mode="dicts")["Build Dependencies"]["blas"]
+        blas = f"{b.get('name', '?')} {b.get('version', '')}".strip()
+    except Exception:
+        blas = "unknown"
     cfg = oracle.Config(**d)
     T = wl["T"]
     flat = synthetic.init_params(d, seed=42)
@@ -110,7 +115,7 @@ def cpu_baseline(d, wl, seconds_hint=20.0):
         oracle.generate(flat, idx, n, 1.0, wl["top_k"], uni, cfg)
         dt = time.perf_counter() - t0
         return {"value": round(n / dt, 3), "unit": "new tokens/s", "cores": int(threads),
-                "kind": "oracle",
+                "kind": "oracle", "blas": blas,
                 "sample": f"{n} new tokens of 1 sequence after a {T}-token prompt; {dt:.1f} s"}
     if wl.get("eval"):
         _, cache = oracle.forward(flat, idx, tgt, cfg)
@@ -122,6 +127,7 @@ def cpu_baseline(d, wl, seconds_hint=20.0):
         what = "one full step (fwd+bwd+clip+AdamW over all params)"
     dt = time.perf_counter() - t0
     return {"value": round(T / dt, 2), "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "blas": blas,
             "sample": f"{what} on 1 x {T} tokens of the same workload; {dt:.1f} s"}
 
 

@@ -500,7 +500,8 @@ __global__ __launch_bounds__(256) void attn_bwd_dkv_mfma(const bf16_t* __restric
   constexpr int QT = 128;  // queries staged per step (two 64-row tiles)
   __shared__ __attribute__((aligned(16))) bf16_t sQ[2][QT * 64];
   __shared__ __attribute__((aligned(16))) bf16_t sG[2][QT * 64];
-  __shared__ float sL[2][QT], sD[2][QT];
+  __shared__ __attribute__((aligned(16))) float sL[2][QT];
+  __shared__ __attribute__((aligned(16))) float sD[2][QT];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, half = lane >> 5, l32 = lane & 31;
   int kbk, bh;
   attn_item(false, kbk, bh);  // key block 0 has the most queries: dispatched first
@@ -569,23 +570,31 @@ __global__ __launch_bounds__(256) void attn_bwd_dkv_mfma(const bf16_t* __restric
         st = mfma(frag_rows(sQ[cur], 32 * s + l32, kk * 2 + half), kf[kk], st);
         dp = mfma(frag_rows(sG[cur], 32 * s + l32, kk * 2 + half), vf[kk], dp);
       }
+      // log-sum-exp and D of this lane's 16 queries: four runs of 4
+      float lq[16], dd[16];
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int qi = 32 * s + 8 * g + 4 * half;
+        const float4 a = *reinterpret_cast<const float4*>(&sL[cur][qi]);
+        const float4 c = *reinterpret_cast<const float4*>(&sD[cur][qi]);
+        lq[4 * g] = a.x; lq[4 * g + 1] = a.y; lq[4 * g + 2] = a.z; lq[4 * g + 3] = a.w;
+        dd[4 * g] = c.x; dd[4 * g + 1] = c.y; dd[4 * g + 2] = c.z; dd[4 * g + 3] = c.w;
+      }
       f32x16_t pv;
       if (qs < kw0 + 31 || qs + 31 >= Tn) {  // some (query, key) pair masked
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int qi = 32 * s + 8 * (r >> 2) + 4 * half + (r & 3);
-          const int q = q0 + qi;
-          const float p = (mykey <= q && q < Tn) ? ex2(fmaf(st[r], sl2, -sL[cur][qi])) : 0.f;
+          const int q = q0 + 32 * s + 8 * (r >> 2) + 4 * half + (r & 3);
+          const float p = (mykey <= q && q < Tn) ? ex2(fmaf(st[r], sl2, -lq[r])) : 0.f;
           pv[r] = p;
-          st[r] = p * (dp[r] - sD[cur][qi]);
+          st[r] = p * (dp[r] - dd[r]);
         }
       } else {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int qi = 32 * s + 8 * (r >> 2) + 4 * half + (r & 3);
-          const float p = ex2(fmaf(st[r], sl2, -sL[cur][qi]));
+          const float p = ex2(fmaf(st[r], sl2, -lq[r]));
           pv[r] = p;
-          st[r] = p * (dp[r] - sD[cur][qi]);
+          st[r] = p * (dp[r] - dd[r]);
         }
       }
 #pragma unroll

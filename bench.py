@@ -68,10 +68,10 @@ METRIC = "training tokens/sec + MFU, GPT-2 124M bf16 B=16 T=1024 on one MI355X"
 # HBM traffic of the lm_head forward GEMM per launch, from two rocprofv3 --pmc
 # passes (FETCH_SIZE, then WRITE_SIZE) over `bench.py --steps 2 --warmup 1
 # --no-cpu-baseline --copy-probe`, each scaled by what the same counter reads
-# for a 1 GiB device copy (fetch x2.000, write x1.000): 1,928,121,671 B read +
+# for a 1 GiB device copy (fetch x2.000, write x1.000): 1,928,107,510 B read +
 # 1,649,410,048 B written (profiles/gpt2_124m_b16_hbm_traffic.md).  Set to None
 # whenever the kernel changes until it is measured again.
-LMHEAD_TRAFFIC_BYTES = 3577531719
+LMHEAD_TRAFFIC_BYTES = 3577517558
 
 
 def flops_per_token(d, T):

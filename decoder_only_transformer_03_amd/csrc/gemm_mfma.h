@@ -589,12 +589,22 @@ __device__ __forceinline__ void tile_epilogue_w96(const EpiArgs& e, const f32x16
 // WM x WN wavefronts; each owns a (BM/WM) x (BN/WN) sub-tile.  Persistent:
 // the grid is about one workgroup per CU; each walks the work items
 // (tile, k-slice) blockIdx.x, +gridDim.x, ...
-template <int BM, int BN, int WM, int WN, int LA, int LB, int EPI, typename TO>
+//
+// GRP: a group of independent products sharing K, one persistent launch over
+// the tiles of all of them (no k-slices): tile t belongs to the problem p
+// with probs[p].item0 <= t < probs[p+1].item0; the kernel's M, N, A, B and
+// the epilogue's out, ldo, alpha come from that problem (the tiles_m x
+// tiles_n arguments are then the total tile count x 1).  Direct loaders only.
+template <int BM, int BN, int WM, int WN, int LA, int LB, int EPI, typename TO, bool GRP = false>
 __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(int M, int N, int K,
                                                       const bf16_t* __restrict__ A, long lda,
                                                       const bf16_t* __restrict__ B, long ldb,
                                                       EpiArgs e, int tiles_m, int tiles_n,
-                                                      int kt_per_split) {
+                                                      int kt_per_split,
+                                                      const GemmProblem* __restrict__ probs,
+                                                      int nprobs) {
+  static_assert(!GRP || (LA >= 2 && LB >= 2 && BM == 256 && BN == 256),
+                "grouped products use the direct loaders and 256 x 256 tiles");
   constexpr int NT = 64 * WM * WN;
   constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int SM = WTM / 32, SN = WTN / 32;
@@ -612,6 +622,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(int M, int N, int
   const long nitems = (long)ntiles * nsplit;
   long m0 = 0, n0 = 0;
   int kt0 = 0, kt1 = 0, split = 0;
+  int prob = 0;  // GRP: the problem of the decoded item
   auto decode = [&](long it) {
     split = (int)(it / ntiles);
     int pid = (int)(it - (long)split * ntiles);
@@ -619,14 +630,38 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(int M, int N, int
       int q = ntiles >> 3, r = ntiles & 7, x = pid & 7, loc = pid >> 3;
       pid = x * q + (x < r ? x : r) + loc;
     }
+    int tm = tiles_m, tn = tiles_n;
+    if constexpr (GRP) {
+      int lo = 0, hi = nprobs - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (probs[mid].item0 <= pid) lo = mid;
+        else hi = mid - 1;
+      }
+      prob = lo;
+      pid -= (int)probs[lo].item0;
+      tm = probs[lo].tiles_m;
+      tn = probs[lo].tiles_n;
+    }
     constexpr int GROUP = 8;
-    const int per_group = GROUP * tiles_n;
+    const int per_group = GROUP * tn;
     const int first_m = (pid / per_group) * GROUP;
-    const int gsize = (tiles_m - first_m) < GROUP ? (tiles_m - first_m) : GROUP;
+    const int gsize = (tm - first_m) < GROUP ? (tm - first_m) : GROUP;
     m0 = (long)(first_m + (pid % per_group) % gsize) * BM;
     n0 = (long)((pid % per_group) / gsize) * BN;
     kt0 = split * kt_per_split;
     kt1 = (kt0 + kt_per_split) < nkt ? (kt0 + kt_per_split) : nkt;
+  };
+  // operands of the decoded item's problem
+  auto setup = [&](auto& la_, auto& lb_) {
+    if constexpr (GRP) {
+      const GemmProblem& P = probs[prob];
+      la_.setup(P.A, P.lda, m0, P.M, tid);
+      lb_.setup(P.B, P.ldb, n0, P.N, tid);
+    } else {
+      la_.setup(A, lda, m0, M, tid);
+      lb_.setup(B, ldb, n0, N, tid);
+    }
   };
   long item = blockIdx.x;
   if (item >= nitems) return;
@@ -642,8 +677,7 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(int M, int N, int
 
   Loader<BM, LA, NT> la;
   Loader<BN, LB, NT> lb;
-  la.setup(A, lda, m0, M, tid);
-  lb.setup(B, ldb, n0, N, tid);
+  setup(la, lb);
   la.issue(A, lda, m0, M, kt0 * BK, K, tid, smem[0]);
   lb.issue(B, ldb, n0, N, kt0 * BK, K, tid, smem[0] + BM * BK);
   la.commit(smem[0], tid);
@@ -683,15 +717,14 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(int M, int N, int
   int cur = 0;
   while (true) {
     const long em0 = m0, en0 = n0;  // this item's output tile
-    const int ekt1 = kt1, esplit = split;
+    const int ekt1 = kt1, esplit = split, eprob = prob;
     for (int kt = kt0; kt < ekt1; ++kt) {
       const bool last_k = kt + 1 == ekt1;
       const bool more = !last_k || item + gridDim.x < nitems;
       if (more) {
         if (last_k) {
           decode(item + gridDim.x);
-          la.setup(A, lda, m0, M, tid);
-          lb.setup(B, ldb, n0, N, tid);
+          setup(la, lb);
         }
         const int nk = last_k ? kt0 : kt + 1;
         la.issue(A, lda, m0, M, nk * BK, K, tid, smem[cur ^ 1]);
@@ -724,7 +757,15 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(int M, int N, int
     }
     // the stage not holding the next item's first k-tile is free: 8 KB of
     // epilogue scratch per wavefront
-    if constexpr (EPI == EPI_LSE)
+    if constexpr (GRP) {
+      const GemmProblem& P = probs[eprob];
+      EpiArgs eg = e;
+      eg.out = P.out;
+      eg.ldo = P.ldo;
+      eg.alpha = P.scaled ? P.alpha * e.alpha : P.alpha;
+      tile_epilogue<BM, BN, WM, WN, EPI, TO, SN, SM>(eg, acc, em0, en0, esplit, P.M, P.N, lane, wm,
+                                                     wn, smem[cur ^ 1] + wave * 4096);
+    } else if constexpr (EPI == EPI_LSE)
       lse_epilogue<BM, BN, WM, WN, SN, SM>(e, acc, em0, en0, M, N, lane, wm, wn);
     else if constexpr (WTN == 64)
       tile_epilogue<BM, BN, WM, WN, EPI, TO, SN, SM>(e, acc, em0, en0, esplit, M, N, lane, wm, wn,
@@ -772,7 +813,23 @@ hipError_t run(int M, int N, int K, const bf16_t* A, long lda, const bf16_t* B, 
   long items = (long)tiles_m * tiles_n * splits;
   long grid = items < persistent_slots() ? items : persistent_slots();
   gemm_kernel<BM, BN, WM, WN, LA, LB, EPI, TO><<<(unsigned)grid, 64 * WM * WN, 0, s>>>(
-      M, N, K, A, lda, B, ldb, e, tiles_m, tiles_n, kps);
+      M, N, K, A, lda, B, ldb, e, tiles_m, tiles_n, kps, nullptr, 0);
+  return hipGetLastError();
+}
+
+// A group of products out_p += alpha_p A_p(m,k) B_p(n,k), both operands
+// transposed (k-major in memory, the weight-gradient form), all with the
+// same K (a multiple of 64), in one persistent launch over total_tiles
+// 256 x 256 tiles.  d_probs: nprobs device descriptors, item0 ascending from 0.
+inline hipError_t run_grouped_accum_tt(const GemmProblem* d_probs, int nprobs, long total_tiles,
+                                       int K, float scale, hipStream_t s) {
+  if (K % BK || total_tiles <= 0 || nprobs <= 0) return hipErrorInvalidValue;
+  EpiArgs e{};
+  e.alpha = scale;
+  const int nkt = K / BK;
+  long grid = total_tiles < persistent_slots() ? total_tiles : persistent_slots();
+  gemm_kernel<256, 256, 2, 4, 3, 3, EPI_ACCUM, float, true><<<(unsigned)grid, 512, 0, s>>>(
+      0, 0, K, nullptr, 0, nullptr, 0, e, (int)total_tiles, 1, nkt, d_probs, nprobs);
   return hipGetLastError();
 }
 

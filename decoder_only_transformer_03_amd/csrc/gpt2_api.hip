@@ -188,10 +188,15 @@ struct gpt2 {
   int32_t* gen_idx;       // (max_batch, block_size) cropped context
   // backward scratch
   float* dres;
-  void* dres_b;
+  void* dres_b;           // bf16 mode: 2L slots of the residual gradient (see run_backward)
   float* dxtmp;
-  void* dbig;
-  void* dqkv;
+  void* dbig;             // bf16 mode: one slot per layer, else one
+  void* dqkv;             // bf16 mode: one slot per layer, else one
+  // bf16 mode: the weight gradients of all blocks and of the lm_head as one
+  // grouped launch at the end of the backward pass
+  GemmProblem* wg_probs;
+  int wg_n = 0;
+  long wg_tiles = 0;
   void* dy;
   float* dbuf;
   float* ln_partial;
@@ -273,10 +278,13 @@ size_t plan(const gpt2_config* c, char* base, gpt2* h) {
   float* gen_logits = a.take_n<float>((size_t)c->max_batch * Vp);
   int32_t* gen_idx = a.take_n<int32_t>(BT);
   float* dres = a.take_n<float>(BT * C);
-  void* dres_b = c->precision == GPT2_BF16 ? a.take(BT * C * es) : nullptr;
+  const bool bf = c->precision == GPT2_BF16;
+  const size_t nl = (size_t)c->n_layer;
+  void* dres_b = bf ? a.take(2 * nl * BT * C * es) : nullptr;
   float* dxtmp = a.take_n<float>(BT * C);
-  void* dbig = a.take(BT * 4 * C * es);
-  void* dqkv = a.take(BT * 3 * C * es);
+  void* dbig = a.take((bf ? nl : 1) * BT * 4 * C * es);
+  void* dqkv = a.take((bf ? nl : 1) * BT * 3 * C * es);
+  GemmProblem* wg_probs = a.take_n<GemmProblem>(bf ? 4 * nl + 1 : 0);
   void* dy = a.take(BT * C * es);
   float* dbuf = a.take_n<float>(BT * H);
   float* ln_partial = a.take_n<float>((size_t)ln_bwd_scratch((long)BT, (int)C));
@@ -298,6 +306,7 @@ size_t plan(const gpt2_config* c, char* base, gpt2* h) {
     h->htlogit = htlogit; h->tgt = tgt;
     h->gen_logits = gen_logits; h->gen_idx = gen_idx;
     h->dres = dres; h->dres_b = dres_b; h->dxtmp = dxtmp; h->dbig = dbig; h->dqkv = dqkv;
+    h->wg_probs = wg_probs;
     h->dy = dy; h->dbuf = dbuf; h->ln_partial = ln_partial; h->bias_partial = bias_partial;
     h->splitk = splitk;
     h->colsum_partial = colsum_partial;
@@ -472,6 +481,65 @@ gpt2_status run_forward(gpt2* h, const int32_t* d_idx, const int32_t* d_tgt, int
   return GPT2_OK;
 }
 
+// bf16-mode backward buffers.  The residual gradient's bf16 copy has 2L
+// slots: 2l holds the gradient at block l's output (read by its mlp c_proj
+// products), 2l+1 the gradient at its x_mid (read by its attn c_proj
+// products).  dh (dbig) and dqkv have one slot per block.  Keeping every
+// slot until the end of the backward pass lets all weight gradients run as
+// one grouped launch there.
+size_t bt_max(const gpt2* h) { return (size_t)h->cfg.max_batch * h->cfg.block_size; }
+bf16_t* dres_slot(const gpt2* h, int i) {
+  return reinterpret_cast<bf16_t*>(h->dres_b) + (size_t)i * bt_max(h) * h->cfg.n_embd;
+}
+void* dbig_slot(const gpt2* h, int l) {
+  if (h->act != DT_BF16) return h->dbig;
+  return reinterpret_cast<bf16_t*>(h->dbig) + (size_t)l * bt_max(h) * 4 * h->cfg.n_embd;
+}
+void* dqkv_slot(const gpt2* h, int l) {
+  if (h->act != DT_BF16) return h->dqkv;
+  return reinterpret_cast<bf16_t*>(h->dqkv) + (size_t)l * bt_max(h) * 3 * h->cfg.n_embd;
+}
+
+// The grouped weight-gradient products (bf16 mode): the lm_head's (unless
+// the head is fused) and, per block, mlp c_proj, c_fc, attn c_proj, c_attn:
+// dW = dY^T X with dY, X the saved (B*T, width) activations.
+std::vector<GemmProblem> wgrad_problems(const gpt2* h, long* total_tiles) {
+  std::vector<GemmProblem> v;
+  const int C = h->cfg.n_embd, Vp = h->cfg.padded_vocab_size;
+  long item0 = 0;
+  auto add = [&](const void* dY, long ldy, const void* X, long ldx, float* out, int Mo, int No,
+                 int scaled) {
+    GemmProblem p;
+    p.A = static_cast<const bf16_t*>(dY);
+    p.B = static_cast<const bf16_t*>(X);
+    p.out = out;
+    p.lda = ldy;
+    p.ldb = ldx;
+    p.ldo = No;
+    p.M = Mo;
+    p.N = No;
+    p.tiles_m = (Mo + 255) / 256;
+    p.tiles_n = (No + 255) / 256;
+    p.item0 = item0;
+    p.alpha = 1.f;
+    p.scaled = scaled;
+    item0 += (long)p.tiles_m * p.tiles_n;
+    v.push_back(p);
+  };
+  float* G = h->grads;
+  if (!h->head_chunk) add(h->logits, Vp, h->z, C, G + h->lay.wte, Vp, C, 1);
+  for (int l = h->cfg.n_layer - 1; l >= 0; --l) {
+    const LayerOff& o = h->lay.layer[l];
+    const LayerAct& a = h->A[l];
+    add(dres_slot(h, 2 * l), C, a.g, 4 * C, G + o.fc2w, C, 4 * C, 0);
+    add(dbig_slot(h, l), 4 * C, a.u2, C, G + o.fcw, 4 * C, C, 0);
+    add(dres_slot(h, 2 * l + 1), C, a.y, C, G + o.projw, C, C, 0);
+    add(dqkv_slot(h, l), 3 * C, a.u1, C, G + o.attnw, 3 * C, C, 0);
+  }
+  *total_tiles = item0;
+  return v;
+}
+
 gpt2_status run_backward(gpt2* h, float scale) {
   const gpt2_config& c = h->cfg;
   const int B = h->B, T = h->T;
@@ -482,8 +550,10 @@ gpt2_status run_backward(gpt2* h, float scale) {
   hipStream_t s = h->stream;
   float* P = h->params;
   float* G = h->grads;
-  const void* dres_in = at == DT_BF16 ? h->dres_b : (const void*)h->dres;
-  void* dres_copy = at == DT_BF16 ? h->dres_b : nullptr;
+  const bool bf = at == DT_BF16;
+  // bf16: every weight gradient in one grouped launch at the end (whole
+  // tiles over the B*T contraction), when B*T is a multiple of 64
+  const bool grouped = bf && h->wg_n > 0 && M % 64 == 0;
 
   // lm_head (tied): dz = s dlogits wte ; dwte += s dlogits^T z
   if (h->head_chunk) {
@@ -513,65 +583,78 @@ gpt2_status run_backward(gpt2* h, float scale) {
     const WOp wl = w_dx(h, h->lay.wte, Vp, C);
     TIMED(h, GPT2_SITE_LMHEAD_DX, launch_gemm(at, M, C, Vp, h->logits, Vp, false, wl.p, wl.ld, wl.t,
                                               EPI_STORE, DT_F32, epi(h->dxtmp, C, scale), 0, s));
-    TIMED(h, GPT2_SITE_LMHEAD_DW, launch_gemm_wgrad(at, Vp, C, M, h->logits, Vp, true, h->z, C, true,
-                                                    G + h->lay.wte, C, scale, h->splitk,
-                                                    SPLITK_PART_ELEMS, s));
+    if (!grouped)
+      TIMED(h, GPT2_SITE_LMHEAD_DW, launch_gemm_wgrad(at, Vp, C, M, h->logits, Vp, true, h->z, C, true,
+                                                      G + h->lay.wte, C, scale, h->splitk,
+                                                      SPLITK_PART_ELEMS, s));
   }
   // also the bias gradient of the last block's mlp c_proj: sum of dres
   TIMED(h, GPT2_SITE_LN_BWD, launch_layernorm_bwd(at, h->dxtmp, h->x_final, h->meanf, h->rstdf, P + h->lay.lnfw,
-                                 h->dres, dres_copy, 0, h->ln_partial, G + h->lay.lnfw,
-                                 G + h->lay.lnfb, G + h->lay.layer[c.n_layer - 1].fc2b, BT, C, s));
+                                 h->dres, bf ? dres_slot(h, 2 * (c.n_layer - 1)) : nullptr, 0,
+                                 h->ln_partial, G + h->lay.lnfw, G + h->lay.lnfb,
+                                 G + h->lay.layer[c.n_layer - 1].fc2b, BT, C, s));
   for (int l = c.n_layer - 1; l >= 0; --l) {
     const LayerOff& o = h->lay.layer[l];
     LayerAct& a = h->A[l];
+    // this block's backward buffers (bf16 mode: its own slots)
+    const void* dres_out = bf ? (const void*)dres_slot(h, 2 * l) : (const void*)h->dres;
+    const void* dres_mid = bf ? (const void*)dres_slot(h, 2 * l + 1) : (const void*)h->dres;
+    void* dbig = dbig_slot(h, l);
+    void* dqkv = dqkv_slot(h, l);
     // x_out = x_mid + c_proj(gelu(c_fc(ln_2(x_mid))))
     // dh = dg * gelu'(h), the forward having saved gelu'(h); in bf16 mode the
     // same epilogue leaves per-128-row column sums of dh (the c_fc bias
     // gradient) in colsum_partial
-    EpiArgs e = epi(h->dbig, 4 * C);
+    EpiArgs e = epi(dbig, 4 * C);
     e.aux = a.h;
     e.ldx = 4 * C;
     if (at == DT_BF16) e.colsum = h->colsum_partial;
     const WOp w2 = w_dx(h, o.fc2w, C, 4 * C);
-    TIMED(h, GPT2_SITE_FCPROJ_DX, launch_gemm(at, M, 4 * C, C, dres_in, C, false, w2.p, w2.ld, w2.t,
+    TIMED(h, GPT2_SITE_FCPROJ_DX, launch_gemm(at, M, 4 * C, C, dres_out, C, false, w2.p, w2.ld, w2.t,
                           EPI_GELU_BWD, at, e, 0, s));
-    TIMED(h, GPT2_SITE_FCPROJ_DW, launch_gemm_wgrad(at, C, 4 * C, M, dres_in, C, true, a.g, 4 * C, true,
-                                                    G + o.fc2w, 4 * C, 1.f, h->splitk,
-                                                    SPLITK_PART_ELEMS, s));
+    if (!grouped)
+      TIMED(h, GPT2_SITE_FCPROJ_DW, launch_gemm_wgrad(at, C, 4 * C, M, dres_out, C, true, a.g, 4 * C,
+                                                      true, G + o.fc2w, 4 * C, 1.f, h->splitk,
+                                                      SPLITK_PART_ELEMS, s));
     const WOp w1 = w_dx(h, o.fcw, 4 * C, C);
-    TIMED(h, GPT2_SITE_FC_DX, launch_gemm(at, M, C, 4 * C, h->dbig, 4 * C, false, w1.p, w1.ld, w1.t, EPI_STORE,
+    TIMED(h, GPT2_SITE_FC_DX, launch_gemm(at, M, C, 4 * C, dbig, 4 * C, false, w1.p, w1.ld, w1.t, EPI_STORE,
                           DT_F32, epi(h->dxtmp, C), 0, s));
-    TIMED(h, GPT2_SITE_FC_DW, launch_gemm_wgrad(at, 4 * C, C, M, h->dbig, 4 * C, true, a.u2, C, true,
-                                                G + o.fcw, C, 1.f, h->splitk, SPLITK_PART_ELEMS, s));
-    if (at == DT_BF16)
+    if (!grouped)
+      TIMED(h, GPT2_SITE_FC_DW, launch_gemm_wgrad(at, 4 * C, C, M, dbig, 4 * C, true, a.u2, C, true,
+                                                  G + o.fcw, C, 1.f, h->splitk, SPLITK_PART_ELEMS, s));
+    if (bf)
       TIMED(h, GPT2_SITE_BIAS_GRAD, launch_colsum_finish(h->colsum_partial, (M + 127) / 128, 4 * C, G + o.fcb, s));
     else
-      TIMED(h, GPT2_SITE_BIAS_GRAD, launch_bias_grad(at, h->dbig, BT, 4 * C, 4 * C, h->bias_partial, G + o.fcb, s));
+      TIMED(h, GPT2_SITE_BIAS_GRAD, launch_bias_grad(at, dbig, BT, 4 * C, 4 * C, h->bias_partial, G + o.fcb, s));
     TIMED(h, GPT2_SITE_LN_BWD, launch_layernorm_bwd(at, h->dxtmp, a.x_mid, a.mean2, a.rstd2, P + o.ln2w, h->dres,
-                                   dres_copy, 1, h->ln_partial, G + o.ln2w, G + o.ln2b,
-                                   G + o.projb, BT, C, s));
+                                   bf ? dres_slot(h, 2 * l + 1) : nullptr, 1, h->ln_partial,
+                                   G + o.ln2w, G + o.ln2b, G + o.projb, BT, C, s));
     // x_mid = x_in + c_proj(attn(ln_1(x_in)))
     const WOp wp = w_dx(h, o.projw, C, C);
-    TIMED(h, GPT2_SITE_PROJ_DX, launch_gemm(at, M, C, C, dres_in, C, false, wp.p, wp.ld, wp.t, EPI_STORE, at,
+    TIMED(h, GPT2_SITE_PROJ_DX, launch_gemm(at, M, C, C, dres_mid, C, false, wp.p, wp.ld, wp.t, EPI_STORE, at,
                           epi(h->dy, C), 0, s));
-    TIMED(h, GPT2_SITE_PROJ_DW, launch_gemm_wgrad(at, C, C, M, dres_in, C, true, a.y, C, true,
-                                                  G + o.projw, C, 1.f, h->splitk, SPLITK_PART_ELEMS,
-                                                  s));
-    TIMED(h, GPT2_SITE_ATTN_BWD, launch_attn_bwd(at, a.qkv, a.y, a.lse, h->dy, h->dqkv, h->dbuf, B, T, H, hd, s));
+    if (!grouped)
+      TIMED(h, GPT2_SITE_PROJ_DW, launch_gemm_wgrad(at, C, C, M, dres_mid, C, true, a.y, C, true,
+                                                    G + o.projw, C, 1.f, h->splitk,
+                                                    SPLITK_PART_ELEMS, s));
+    TIMED(h, GPT2_SITE_ATTN_BWD, launch_attn_bwd(at, a.qkv, a.y, a.lse, h->dy, dqkv, h->dbuf, B, T, H, hd, s));
     const WOp wq = w_dx(h, o.attnw, 3 * C, C);
-    TIMED(h, GPT2_SITE_QKV_DX, launch_gemm(at, M, C, 3 * C, h->dqkv, 3 * C, false, wq.p, wq.ld, wq.t,
+    TIMED(h, GPT2_SITE_QKV_DX, launch_gemm(at, M, C, 3 * C, dqkv, 3 * C, false, wq.p, wq.ld, wq.t,
                           EPI_STORE, DT_F32, epi(h->dxtmp, C), 0, s));
-    TIMED(h, GPT2_SITE_QKV_DW, launch_gemm_wgrad(at, 3 * C, C, M, h->dqkv, 3 * C, true, a.u1, C, true,
-                                                 G + o.attnw, C, 1.f, h->splitk, SPLITK_PART_ELEMS,
-                                                 s));
-    TIMED(h, GPT2_SITE_BIAS_GRAD, launch_bias_grad(at, h->dqkv, BT, 3 * C, 3 * C, h->bias_partial, G + o.attnb, s));
+    if (!grouped)
+      TIMED(h, GPT2_SITE_QKV_DW, launch_gemm_wgrad(at, 3 * C, C, M, dqkv, 3 * C, true, a.u1, C, true,
+                                                   G + o.attnw, C, 1.f, h->splitk,
+                                                   SPLITK_PART_ELEMS, s));
+    TIMED(h, GPT2_SITE_BIAS_GRAD, launch_bias_grad(at, dqkv, BT, 3 * C, 3 * C, h->bias_partial, G + o.attnb, s));
     // the new dres also gives the bias gradient of the previous block's mlp c_proj
     float* dsum = l > 0 ? G + h->lay.layer[l - 1].fc2b : nullptr;
     TIMED(h, GPT2_SITE_LN_BWD, launch_layernorm_bwd(at, h->dxtmp, a.x_in, a.mean1, a.rstd1, P + o.ln1w, h->dres,
-                                   dres_copy, 1, h->ln_partial, G + o.ln1w, G + o.ln1b, dsum,
-                                   BT, C, s));
+                                   bf && l > 0 ? dres_slot(h, 2 * (l - 1)) : nullptr, 1,
+                                   h->ln_partial, G + o.ln1w, G + o.ln1b, dsum, BT, C, s));
   }
   TIMED(h, GPT2_SITE_EMBED_BWD, launch_embed_bwd(h->idx, h->dres, G + h->lay.wte, G + h->lay.wpe, B, T, C, s));
+  if (grouped)
+    TIMED(h, GPT2_SITE_WGRAD, launch_gemm_grouped_wgrad(h->wg_probs, h->wg_n, h->wg_tiles, M, scale, s));
   return GPT2_OK;
 }
 
@@ -621,6 +704,14 @@ gpt2_status gpt2_init(const gpt2_config* cfg, void* d_workspace, size_t ws_bytes
   hipError_t e = hipMemcpyAsync(h->chunks, ch.data(), ch.size() * sizeof(AdamChunk),
                                 hipMemcpyHostToDevice, h->stream);
   std::vector<TTile> tt = h->nttiles ? make_ttiles(h->lay, cfg) : std::vector<TTile>();
+  std::vector<GemmProblem> wg;
+  if (h->act == DT_BF16) {
+    wg = wgrad_problems(h, &h->wg_tiles);
+    h->wg_n = (int)wg.size();
+    if (e == hipSuccess)
+      e = hipMemcpyAsync(h->wg_probs, wg.data(), wg.size() * sizeof(GemmProblem),
+                         hipMemcpyHostToDevice, h->stream);
+  }
   if (e == hipSuccess && !tt.empty())
     e = hipMemcpyAsync(h->ttiles, tt.data(), tt.size() * sizeof(TTile), hipMemcpyHostToDevice,
                        h->stream);

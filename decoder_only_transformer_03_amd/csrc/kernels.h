@@ -106,6 +106,26 @@ hipError_t launch_gemm_wgrad(DType in_t, int M, int N, int K, const void* A, lon
                              const void* B, long ldb, bool b_t, float* out, long ldo, float alpha,
                              float* part, long part_elems, hipStream_t s);
 int gemm_partial_splits(DType in_t, int M, int N, int K);
+
+// One product of a grouped weight-gradient launch:
+// out[m*ldo + n] += a * sum_k A[k*lda + m] B[k*ldb + n], m < M, n < N, with
+// a = alpha, times the launch's scale if `scaled`; its tiles_m x tiles_n
+// 256 x 256 tiles are numbered from item0 in the group.
+struct GemmProblem {
+  const bf16_t* A;
+  const bf16_t* B;
+  float* out;
+  long lda, ldb, ldo;
+  int M, N, tiles_m, tiles_n;
+  long item0;
+  float alpha;
+  int scaled;
+};
+// All products of d_probs (device array, nprobs entries, item0 ascending
+// from 0, total_tiles in all) in one persistent launch; bf16 operands, K a
+// multiple of 64, whole tiles (no k-slices): deterministic.
+hipError_t launch_gemm_grouped_wgrad(const GemmProblem* d_probs, int nprobs, long total_tiles,
+                                     int K, float scale, hipStream_t s);
 constexpr long SPLITK_PART_ELEMS = 256L * 256 * 256;
 
 // Causal self-attention on the fused qkv activation (B*T, 3C), head h of q,

@@ -22,7 +22,7 @@ GPT2_PARAMS, GPT2_GRADS, GPT2_ADAM_M, GPT2_ADAM_V = 0, 1, 2, 3
 SITES = ["EMBED_FWD", "LN_FWD", "QKV_FWD", "ATTN_FWD", "PROJ_FWD", "FC_FWD", "FCPROJ_FWD",
          "LMHEAD_FWD", "XENT", "LMHEAD_DX", "LMHEAD_DW", "LN_BWD", "FCPROJ_DX", "FCPROJ_DW", "FC_DX",
          "FC_DW", "PROJ_DX", "PROJ_DW", "ATTN_BWD", "QKV_DX", "QKV_DW", "BIAS_GRAD", "EMBED_BWD",
-         "GRAD_NORM", "ADAMW", "ZERO_GRAD", "LMHEAD_RECOMP", "WEIGHT_T"]
+         "GRAD_NORM", "ADAMW", "ZERO_GRAD", "LMHEAD_RECOMP", "WEIGHT_T", "WGRAD"]
 ACT = {n: i for i, n in enumerate([
     "X_IN", "LN1", "QKV", "ATTN_Y", "LSE", "X_MID", "LN2", "FC_DGELU", "FC_GELU", "LNF", "LOGITS",
     "ROW_LOSS"])}

@@ -267,7 +267,10 @@ gpt2_status gpt2_get_activation(gpt2_t* h, int which, int layer, float* h_dst, s
  * log-sum-exp and loss reduction, LMHEAD_RECOMP the backward's recomputation
  * of a slice of logits, LMHEAD_DX/DW the slices' shares of dz and dwte.
  * WEIGHT_T is the refresh, after each AdamW step, of the transposed bf16
- * weight copies that the input-gradient products read. */
+ * weight copies that the input-gradient products read.  In GPT2_BF16 with
+ * B*T a multiple of 64, the weight gradients of all blocks (and of the
+ * lm_head, unless fused) run as one grouped launch at the end of the
+ * backward pass, timed as WGRAD; the per-product *_DW sites are then empty. */
 enum {
   GPT2_SITE_EMBED_FWD = 0, GPT2_SITE_LN_FWD, GPT2_SITE_QKV_FWD, GPT2_SITE_ATTN_FWD,
   GPT2_SITE_PROJ_FWD, GPT2_SITE_FC_FWD, GPT2_SITE_FCPROJ_FWD, GPT2_SITE_LMHEAD_FWD,
@@ -276,7 +279,7 @@ enum {
   GPT2_SITE_PROJ_DX, GPT2_SITE_PROJ_DW, GPT2_SITE_ATTN_BWD, GPT2_SITE_QKV_DX,
   GPT2_SITE_QKV_DW, GPT2_SITE_BIAS_GRAD, GPT2_SITE_EMBED_BWD, GPT2_SITE_GRAD_NORM,
   GPT2_SITE_ADAMW, GPT2_SITE_ZERO_GRAD, GPT2_SITE_LMHEAD_RECOMP, GPT2_SITE_WEIGHT_T,
-  GPT2_NUM_SITES
+  GPT2_SITE_WGRAD, GPT2_NUM_SITES
 };
 
 /* From now on, record an event pair around every launch of each site whose

@@ -197,6 +197,9 @@ struct gpt2 {
   GemmProblem* wg_probs;
   int wg_n = 0;
   long wg_tiles = 0;
+  // the last wg_tail.M rows of the first product, taken out of the group so
+  // that it ends on a full round of tiles; run as split-K slices after it
+  GemmProblem wg_tail{};
   void* dy;
   float* dbuf;
   float* ln_partial;
@@ -503,7 +506,7 @@ void* dqkv_slot(const gpt2* h, int l) {
 // The grouped weight-gradient products (bf16 mode): the lm_head's (unless
 // the head is fused) and, per block, mlp c_proj, c_fc, attn c_proj, c_attn:
 // dW = dY^T X with dY, X the saved (B*T, width) activations.
-std::vector<GemmProblem> wgrad_problems(const gpt2* h, long* total_tiles) {
+std::vector<GemmProblem> wgrad_problems(gpt2* h, long* total_tiles) {
   std::vector<GemmProblem> v;
   const int C = h->cfg.n_embd, Vp = h->cfg.padded_vocab_size;
   long item0 = 0;
@@ -535,6 +538,28 @@ std::vector<GemmProblem> wgrad_problems(const gpt2* h, long* total_tiles) {
     add(dbig_slot(h, l), 4 * C, a.u2, C, G + o.fcw, 4 * C, C, 0);
     add(dres_slot(h, 2 * l + 1), C, a.y, C, G + o.projw, C, C, 0);
     add(dqkv_slot(h, l), 3 * C, a.u1, C, G + o.attnw, 3 * C, C, 0);
+  }
+  // Whole rounds of tiles: a last round holding rem < slots/2 tiles would
+  // leave most CUs idle for a whole tile.  Move the last r tile-rows (r x
+  // tiles_n >= rem tiles) of the first product into a tail launch of split-K
+  // slices that fills the GPU for a fraction of that time.
+  h->wg_tail = GemmProblem{};
+  const long slots = gemm_slots();
+  const long rem = item0 % slots;
+  GemmProblem& p0 = v[0];
+  const int r = (int)((rem + p0.tiles_n - 1) / p0.tiles_n);
+  if (rem > 0 && rem * 2 < slots && r < p0.tiles_m && (long)r * p0.tiles_n * 2 <= slots) {
+    const int M1 = (p0.tiles_m - r) * 256;
+    GemmProblem t = p0;
+    t.A = p0.A + M1;
+    t.out = p0.out + (long)M1 * p0.ldo;
+    t.M = p0.M - M1;
+    h->wg_tail = t;
+    p0.M = M1;
+    p0.tiles_m -= r;
+    const long moved = (long)r * p0.tiles_n;
+    for (size_t i = 1; i < v.size(); ++i) v[i].item0 -= moved;
+    item0 -= moved;
   }
   *total_tiles = item0;
   return v;
@@ -653,8 +678,14 @@ gpt2_status run_backward(gpt2* h, float scale) {
                                    h->ln_partial, G + o.ln1w, G + o.ln1b, dsum, BT, C, s));
   }
   TIMED(h, GPT2_SITE_EMBED_BWD, launch_embed_bwd(h->idx, h->dres, G + h->lay.wte, G + h->lay.wpe, B, T, C, s));
-  if (grouped)
+  if (grouped) {
     TIMED(h, GPT2_SITE_WGRAD, launch_gemm_grouped_wgrad(h->wg_probs, h->wg_n, h->wg_tiles, M, scale, s));
+    const GemmProblem& t = h->wg_tail;
+    if (t.M > 0)
+      TIMED(h, GPT2_SITE_WGRAD, launch_gemm_wgrad(at, t.M, t.N, M, t.A, t.lda, true, t.B, t.ldb, true,
+                                                  t.out, t.ldo, t.scaled ? t.alpha * scale : t.alpha,
+                                                  h->splitk, SPLITK_PART_ELEMS, s));
+  }
   return GPT2_OK;
 }
 

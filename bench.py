@@ -8,11 +8,13 @@ gradient-norm clip and AdamW -- all through the C ABI of libgpt2.so.
   python bench.py [--steps K] [--warmup W] [--workload gpt2-124m|gpt2-xl|sft]
 
 Prints ONE JSON line.  value = tokens per second over the K timed steps
-(inputs already resident in device memory).  roofline = the lm_head forward
-GEMM (the largest single kernel: 2*B*T*Vp*C flops per launch) timed live with
-HIP events on the library's stream during the timed steps, against the bf16
-dense matrix-core peak.  cpu_baseline = the CPU oracle (numpy) on a bounded
-sample of the same workload.
+(inputs already resident in device memory).  roofline = the kernel with the
+most time of the two largest, timed live with HIP events on the library's
+stream during the timed steps, against the bf16 dense matrix-core peak: in a
+training step the grouped weight-gradient GEMM (2*B*T flops per gradient
+element it produces), in a forward-only pass the lm_head forward GEMM
+(2*B*T*Vp*C flops).  cpu_baseline = the CPU oracle (numpy) on a bounded sample
+of the same workload.
 """
 from __future__ import annotations
 
@@ -65,13 +67,17 @@ WORKLOADS = {
 
 METRIC = "training tokens/sec + MFU, GPT-2 124M bf16 B=16 T=1024 on one MI355X"
 
-# HBM traffic of the lm_head forward GEMM per launch, from two rocprofv3 --pmc
-# passes (FETCH_SIZE, then WRITE_SIZE) over `bench.py --steps 2 --warmup 1
-# --no-cpu-baseline --copy-probe`, each scaled by what the same counter reads
-# for a 1 GiB device copy (fetch x2.000, write x1.000): 1,928,107,510 B read +
-# 1,649,410,048 B written (profiles/gpt2_124m_b16_hbm_traffic.md).  Set to None
-# whenever the kernel changes until it is measured again.
-LMHEAD_TRAFFIC_BYTES = 3577517558
+# HBM traffic per launch of the two largest kernels of the GPT-2 124M step at
+# B=16, T=1024, from two rocprofv3 --pmc passes (FETCH_SIZE, then WRITE_SIZE)
+# over `bench.py --steps 2 --warmup 1 --no-cpu-baseline --copy-probe`, each
+# scaled by what the same counter reads for a 1 GiB device copy (fetch x2.000,
+# write x1.000); profiles/gpt2_124m_b16_hbm_traffic.md.
+#   grouped weight gradients: 9,569,395,035 B read + 469,500,245 B written
+#   lm_head forward GEMM:     1,928,124,680 B read + 1,649,410,048 B written
+# Remove an entry whenever its kernel changes, until it is measured again.
+TRAFFIC_BYTES = {("gpt2-124m", "WGRAD"): 10038895280,
+                 ("gpt2-124m", "LMHEAD_FWD"): 3577534728,
+                 ("gpt2-124m-eval", "LMHEAD_FWD"): 3577534728}
 
 
 def flops_per_token(d, T):
@@ -202,7 +208,7 @@ def main():
         step()
     model.sync()
     stream = torch.cuda.current_stream()
-    model.timing_begin(["LMHEAD_FWD"])
+    model.timing_begin(["LMHEAD_FWD", "WGRAD"])
     torch.cuda.synchronize()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
@@ -227,10 +233,17 @@ def main():
     if n_gen:  # model flops are not the measure of a recomputing sampling loop
         f_causal = f_nano = 0.0
 
-    lm_ms, lm_n = sites.get("LMHEAD_FWD", (0.0, 0))
-    lm_avg = lm_ms / max(lm_n, 1)
-    lm_flops = 2.0 * B * T * d["padded_vocab_size"] * d["n_embd"]
-    achieved = lm_flops / (lm_avg / 1e3) / 1e12 if lm_avg > 0 else 0.0
+    # the roofline kernel: whichever of the lm_head forward GEMM and the
+    # grouped weight-gradient GEMM took longer over the timed steps
+    grouped_elems, _, _ = model.wgrad_layout()
+    cands = {"LMHEAD_FWD": 2.0 * B * T * d["padded_vocab_size"] * d["n_embd"],
+             "WGRAD": 2.0 * B * T * grouped_elems}
+    timed = [k for k in cands if sites.get(k, (0.0, 0))[1] and cands[k] > 0]
+    site = max(timed, key=lambda k: sites[k][0]) if timed else "LMHEAD_FWD"
+    k_ms, k_n = sites.get(site, (0.0, 0))
+    k_avg = k_ms / max(k_n, 1)
+    k_flops = cands[site]
+    achieved = k_flops / (k_avg / 1e3) / 1e12 if k_avg > 0 else 0.0
 
     breakdown = None
     if args.breakdown:
@@ -240,14 +253,17 @@ def main():
         br = model.timing_end()
         breakdown = {k: round(v[0] / 2, 4) for k, v in sorted(br.items(), key=lambda x: -x[1][0])}
 
-    roofline = {"kernel": "lm_head forward GEMM with the log-sum-exp epilogue "
-                          "(gemm_kernel<256,256,NT,lse>)" if fused else
-                          "lm_head forward GEMM (gemm_kernel<256,256,NT,store bf16>)",
+    names = {"WGRAD": "weight gradients of every block" + ("" if fused else " and the lm_head") +
+                      ", one grouped GEMM launch (gemm_kernel<256,256,TT,accumulate fp32,grouped>)",
+             "LMHEAD_FWD": "lm_head forward GEMM with the log-sum-exp epilogue "
+                           "(gemm_kernel<256,256,NT,lse>)" if fused else
+                           "lm_head forward GEMM (gemm_kernel<256,256,NT,store bf16>)"}
+    roofline = {"kernel": names[site], "site": site,
                 "bound": "mfma", "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                "traffic": None if fused else LMHEAD_TRAFFIC_BYTES,
-                "avg_launch_ms": round(lm_avg, 4), "launches": lm_n,
-                "flops_per_launch": lm_flops}
+                "traffic": TRAFFIC_BYTES.get((args.workload, site)),
+                "avg_launch_ms": round(k_avg, 4), "launches": k_n,
+                "flops_per_launch": k_flops}
     out = {
         "metric": METRIC if args.workload == "gpt2-124m" else
                   f"tokens/sec + MFU, {args.workload} on one MI355X",

@@ -197,6 +197,7 @@ struct gpt2 {
   GemmProblem* wg_probs;
   int wg_n = 0;
   long wg_tiles = 0;
+  long wg_elems = 0;  // weight-gradient elements the grouped launch produces
   // the last wg_tail.M rows of the first product, taken out of the group so
   // that it ends on a full round of tiles; run as split-K slices after it
   GemmProblem wg_tail{};
@@ -682,9 +683,9 @@ gpt2_status run_backward(gpt2* h, float scale) {
     TIMED(h, GPT2_SITE_WGRAD, launch_gemm_grouped_wgrad(h->wg_probs, h->wg_n, h->wg_tiles, M, scale, s));
     const GemmProblem& t = h->wg_tail;
     if (t.M > 0)
-      TIMED(h, GPT2_SITE_WGRAD, launch_gemm_wgrad(at, t.M, t.N, M, t.A, t.lda, true, t.B, t.ldb, true,
-                                                  t.out, t.ldo, t.scaled ? t.alpha * scale : t.alpha,
-                                                  h->splitk, SPLITK_PART_ELEMS, s));
+      TIMED(h, GPT2_SITE_WGRAD_TAIL, launch_gemm_wgrad(at, t.M, t.N, M, t.A, t.lda, true, t.B, t.ldb, true,
+                                                       t.out, t.ldo, t.scaled ? t.alpha * scale : t.alpha,
+                                                       h->splitk, SPLITK_PART_ELEMS, s));
   }
   return GPT2_OK;
 }
@@ -739,6 +740,7 @@ gpt2_status gpt2_init(const gpt2_config* cfg, void* d_workspace, size_t ws_bytes
   if (h->act == DT_BF16) {
     wg = wgrad_problems(h, &h->wg_tiles);
     h->wg_n = (int)wg.size();
+    for (const GemmProblem& q : wg) h->wg_elems += (long)q.M * q.N;
     if (e == hipSuccess)
       e = hipMemcpyAsync(h->wg_probs, wg.data(), wg.size() * sizeof(GemmProblem),
                          hipMemcpyHostToDevice, h->stream);
@@ -804,6 +806,16 @@ gpt2_status gpt2_set_state(gpt2_t* h, int which, const float* src, size_t n, int
 gpt2_status gpt2_get_step(const gpt2_t* h, int64_t* t) {
   if (!h || !t) return GPT2_E_ARG;
   *t = h->step;
+  return GPT2_OK;
+}
+
+gpt2_status gpt2_wgrad_layout(const gpt2_t* h, int64_t* grouped_elems, int64_t* tail_elems,
+                              int64_t* grouped_tiles) {
+  if (!h) return GPT2_E_ARG;
+  const bool g = h->wg_n > 0;
+  if (grouped_elems) *grouped_elems = g ? h->wg_elems : 0;
+  if (tail_elems) *tail_elems = g ? (int64_t)h->wg_tail.M * h->wg_tail.N : 0;
+  if (grouped_tiles) *grouped_tiles = g ? h->wg_tiles : 0;
   return GPT2_OK;
 }
 

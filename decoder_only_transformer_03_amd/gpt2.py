@@ -22,7 +22,8 @@ GPT2_PARAMS, GPT2_GRADS, GPT2_ADAM_M, GPT2_ADAM_V = 0, 1, 2, 3
 SITES = ["EMBED_FWD", "LN_FWD", "QKV_FWD", "ATTN_FWD", "PROJ_FWD", "FC_FWD", "FCPROJ_FWD",
          "LMHEAD_FWD", "XENT", "LMHEAD_DX", "LMHEAD_DW", "LN_BWD", "FCPROJ_DX", "FCPROJ_DW", "FC_DX",
          "FC_DW", "PROJ_DX", "PROJ_DW", "ATTN_BWD", "QKV_DX", "QKV_DW", "BIAS_GRAD", "EMBED_BWD",
-         "GRAD_NORM", "ADAMW", "ZERO_GRAD", "LMHEAD_RECOMP", "WEIGHT_T", "WGRAD"]
+         "GRAD_NORM", "ADAMW", "ZERO_GRAD", "LMHEAD_RECOMP", "WEIGHT_T", "WGRAD",
+         "WGRAD_TAIL"]
 ACT = {n: i for i, n in enumerate([
     "X_IN", "LN1", "QKV", "ATTN_Y", "LSE", "X_MID", "LN2", "FC_DGELU", "FC_GELU", "LNF", "LOGITS",
     "ROW_LOSS"])}
@@ -81,6 +82,7 @@ def lib():
             "gpt2_get_activation": (i32, [vp, i32, i32, vp, sz]),
             "gpt2_timing_begin": (i32, [vp, ct.c_uint64]),
             "gpt2_timing_end": (i32, [vp, ct.POINTER(ct.c_double), ct.POINTER(ct.c_int32)]),
+            "gpt2_wgrad_layout": (i32, [vp, ct.POINTER(i64), ct.POINTER(i64), ct.POINTER(i64)]),
             "gpt2_op_gemm": (i32, [i32, i32, i32, i32, vp, ct.c_long, i32, vp, ct.c_long, i32, vp,
                                    ct.c_long, f32, i32, i32, vp]),
             "gpt2_op_attention_fwd": (i32, [i32, vp, vp, vp, i32, i32, i32, i32, vp]),
@@ -99,7 +101,7 @@ EXPORTED = ["gpt2_num_params", "gpt2_workspace_bytes", "gpt2_init", "gpt2_set_pa
             "gpt2_forward_last", "gpt2_sample", "gpt2_generate", "gpt2_get_loss",
             "gpt2_zero_grad", "gpt2_backward", "gpt2_adamw_step", "gpt2_get_grad_norm",
             "gpt2_sync", "gpt2_last_error", "gpt2_destroy", "gpt2_get_activation",
-            "gpt2_timing_begin", "gpt2_timing_end",
+            "gpt2_timing_begin", "gpt2_timing_end", "gpt2_wgrad_layout",
             "gpt2_op_gemm", "gpt2_op_attention_fwd", "gpt2_op_attention_bwd"]
 
 
@@ -280,6 +282,14 @@ class GPT2:
         cnt = (ct.c_int32 * len(SITES))()
         self._check(lib().gpt2_timing_end(self.h, ms, cnt))
         return {n: (ms[i], cnt[i]) for i, n in enumerate(SITES) if cnt[i]}
+
+    def wgrad_layout(self):
+        """(grouped_elems, tail_elems, grouped_tiles): weight-gradient elements
+        produced by the grouped launch and by the split-K tail, and the grouped
+        launch's output tiles (all 0 when products run one at a time)."""
+        g, t, n = ct.c_int64(0), ct.c_int64(0), ct.c_int64(0)
+        self._check(lib().gpt2_wgrad_layout(self.h, ct.byref(g), ct.byref(t), ct.byref(n)))
+        return g.value, t.value, n.value
 
     def activation(self, name, layer, count):
         out = np.empty(count, np.float32)

@@ -270,7 +270,10 @@ gpt2_status gpt2_get_activation(gpt2_t* h, int which, int layer, float* h_dst, s
  * weight copies that the input-gradient products read.  In GPT2_BF16 with
  * B*T a multiple of 64, the weight gradients of all blocks (and of the
  * lm_head, unless fused) run as one grouped launch at the end of the
- * backward pass, timed as WGRAD; the per-product *_DW sites are then empty. */
+ * backward pass, timed as WGRAD; the per-product *_DW sites are then empty.
+ * When the group's tile count would leave the last round of the launch mostly
+ * idle, the first product's last tile-rows are taken out of the group and run
+ * afterwards as a small split-K product, timed as WGRAD_TAIL. */
 enum {
   GPT2_SITE_EMBED_FWD = 0, GPT2_SITE_LN_FWD, GPT2_SITE_QKV_FWD, GPT2_SITE_ATTN_FWD,
   GPT2_SITE_PROJ_FWD, GPT2_SITE_FC_FWD, GPT2_SITE_FCPROJ_FWD, GPT2_SITE_LMHEAD_FWD,
@@ -279,7 +282,7 @@ enum {
   GPT2_SITE_PROJ_DX, GPT2_SITE_PROJ_DW, GPT2_SITE_ATTN_BWD, GPT2_SITE_QKV_DX,
   GPT2_SITE_QKV_DW, GPT2_SITE_BIAS_GRAD, GPT2_SITE_EMBED_BWD, GPT2_SITE_GRAD_NORM,
   GPT2_SITE_ADAMW, GPT2_SITE_ZERO_GRAD, GPT2_SITE_LMHEAD_RECOMP, GPT2_SITE_WEIGHT_T,
-  GPT2_SITE_WGRAD, GPT2_NUM_SITES
+  GPT2_SITE_WGRAD, GPT2_SITE_WGRAD_TAIL, GPT2_NUM_SITES
 };
 
 /* From now on, record an event pair around every launch of each site whose
@@ -291,6 +294,18 @@ gpt2_status gpt2_timing_begin(gpt2_t* h, uint64_t site_mask);
  * duration in milliseconds (ms[GPT2_NUM_SITES]) and the number of launches
  * (launches[GPT2_NUM_SITES]); either pointer may be NULL. */
 gpt2_status gpt2_timing_end(gpt2_t* h, double* ms, int32_t* launches);
+
+/* How the backward launches its weight gradients (fixed at gpt2_init, the
+ * same for every B, T): the number of weight-matrix gradient elements that
+ * the grouped launch (site WGRAD) produces, the number that the split-K tail
+ * (site WGRAD_TAIL) produces, and the grouped launch's 256x256 output tiles.
+ * Each element is a dot product over the B*T positions, so a launch's matrix
+ * work is 2*B*T times its element count.  All three are 0 when the weight
+ * gradients run one product at a time (GPT2_FP32; in GPT2_BF16 also any
+ * backward whose B*T is not a multiple of 64, which ignores this layout).  Any pointer may be NULL;
+ * h NULL returns GPT2_E_ARG. */
+gpt2_status gpt2_wgrad_layout(const gpt2_t* h, int64_t* grouped_elems, int64_t* tail_elems,
+                              int64_t* grouped_tiles);
 
 #ifdef __cplusplus
 }

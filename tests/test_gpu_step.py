@@ -337,6 +337,53 @@ def test_bf16_124m_fused_head(step_124m_b2):
     check_bf16_step(d, flat, g, r)
 
 
+def test_bf16_124m_weight_gradient_layout(step_124m_b2):
+    """In bf16 the weight gradients run as one grouped launch and at most one
+    split-K tail: together they produce every weight-matrix gradient element
+    once (the lm_head's unless the head is fused, and the four products of
+    every block), the grouped launch's tiles cover its share, and the
+    per-product weight-gradient sites stay empty.  fp32 runs the products one
+    at a time."""
+    d, flat, idx, tgt, g, _ = step_124m_b2
+    L, C, Vp = d["n_layer"], d["n_embd"], d["padded_vocab_size"]
+    per_product = ("LMHEAD_DW", "FCPROJ_DW", "FC_DW", "PROJ_DW", "QKV_DW")
+    m = g["model"]
+    ge, te, nt = m.wgrad_layout()
+    print(f"\n124M bf16: grouped {ge} elements in {nt} tiles, tail {te}")
+    assert ge + te == Vp * C + 12 * L * C * C
+    assert 0 < ge <= nt * 256 * 256 and te % C == 0
+    m.timing_begin(None)
+    m.zero_grad()
+    m.forward(dev_ids(idx), dev_ids(tgt))
+    m.backward(1.0)
+    sites = m.timing_end()
+    assert sites["WGRAD"][1] == 1 and sites["WGRAD"][0] > 0
+    assert sites.get("WGRAD_TAIL", (0.0, 0))[1] == (1 if te else 0)
+    assert not [k for k in per_product if k in sites]
+    assert sites["LMHEAD_FWD"][1] == 1
+    fused = G.GPT2(G.make_config(max_batch=2, precision="bf16", head_chunk=4096, **d), device=DEV)
+    try:
+        ge2, te2, _ = fused.wgrad_layout()
+    finally:
+        fused.close()
+    assert ge2 + te2 == 12 * L * C * C
+    dt = synthetic.model_dims("tiny")
+    tiny = G.GPT2(G.make_config(max_batch=2, precision="fp32", **dt), device=DEV)
+    try:
+        assert tiny.wgrad_layout() == (0, 0, 0)
+        tiny.set_params(synthetic.init_params(dt, seed=3))
+        i2, t2 = synthetic.uniform_batch(2, 64, dt["vocab_size"], seed=4)
+        tiny.timing_begin(None)
+        tiny.zero_grad()
+        tiny.forward(dev_ids(i2), dev_ids(t2))
+        tiny.backward(1.0)
+        s2 = tiny.timing_end()
+    finally:
+        tiny.close()
+    assert "WGRAD" not in s2 and "WGRAD_TAIL" not in s2
+    assert s2["FC_DW"][1] == dt["n_layer"] and s2["LMHEAD_DW"][1] == 1
+
+
 def check_bf16_step(d, flat, g, r):
     """bf16: gradients per tensor within 1.2e-2 normwise (bf16 storage of
     activations and of the gradients flowing between layers, about

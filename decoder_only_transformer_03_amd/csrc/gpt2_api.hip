@@ -203,10 +203,17 @@ struct gpt2 {
   GemmProblem wg_tail{};
   void* dy;
   float* dbuf;
-  float* ln_partial;
-  float* bias_partial;
+  // partial column sums, one slot per producing launch, summed by one grouped
+  // launch at the end of the backward pass: the 2L+1 LayerNorm backwards (slot
+  // 2l: ln_1 of block l, 2l+1: ln_2, 2L: ln_f), and per block the c_fc and
+  // c_attn bias gradients
+  float* ln_parts;
+  float* fcb_parts;
+  float* attnb_parts;
+  ColsumProblem* cs_probs;
+  int cs_n = 0;
+  int cs_chunks = 0;
   float* splitk;
-  float* colsum_partial;  // per-128-row column sums of dh (c_fc bias gradient)
   // state
   int B = 0, T = 0;
   bool have_targets = false;
@@ -224,6 +231,10 @@ struct gpt2 {
 };
 
 namespace {
+
+// Rows of a c_fc bias-gradient partial slot: per-128-row sums from the
+// GEMM epilogue (bf16) or BIAS_SPLITS row slices (fp32), whichever is more.
+size_t fcb_part_rows(size_t BT) { return std::max<size_t>((BT + 127) / 128, BIAS_SPLITS); }
 
 // Lays out the whole workspace; with h == nullptr only measures it.
 size_t plan(const gpt2_config* c, char* base, gpt2* h) {
@@ -291,9 +302,10 @@ size_t plan(const gpt2_config* c, char* base, gpt2* h) {
   GemmProblem* wg_probs = a.take_n<GemmProblem>(bf ? 4 * nl + 1 : 0);
   void* dy = a.take(BT * C * es);
   float* dbuf = a.take_n<float>(BT * H);
-  float* ln_partial = a.take_n<float>((size_t)ln_bwd_scratch((long)BT, (int)C));
-  float* bias_partial = a.take_n<float>((size_t)BIAS_SPLITS * 4 * C);
-  float* colsum_partial = a.take_n<float>((BT + 127) / 128 * 4 * C);
+  float* ln_parts = a.take_n<float>((2 * nl + 1) * (size_t)ln_bwd_scratch((long)BT, (int)C));
+  float* fcb_parts = a.take_n<float>(nl * fcb_part_rows(BT) * 4 * C);
+  float* attnb_parts = a.take_n<float>(nl * (size_t)BIAS_SPLITS * 3 * C);
+  ColsumProblem* cs_probs = a.take_n<ColsumProblem>(4 * nl + 1);
   float* splitk = a.take_n<float>((size_t)SPLITK_PART_ELEMS);
   size_t total = (a.off + 255) & ~(size_t)255;
   if (h) {
@@ -311,9 +323,10 @@ size_t plan(const gpt2_config* c, char* base, gpt2* h) {
     h->gen_logits = gen_logits; h->gen_idx = gen_idx;
     h->dres = dres; h->dres_b = dres_b; h->dxtmp = dxtmp; h->dbig = dbig; h->dqkv = dqkv;
     h->wg_probs = wg_probs;
-    h->dy = dy; h->dbuf = dbuf; h->ln_partial = ln_partial; h->bias_partial = bias_partial;
+    h->dy = dy; h->dbuf = dbuf;
+    h->ln_parts = ln_parts; h->fcb_parts = fcb_parts; h->attnb_parts = attnb_parts;
+    h->cs_probs = cs_probs;
     h->splitk = splitk;
-    h->colsum_partial = colsum_partial;
   }
   return total;
 }
@@ -504,6 +517,50 @@ void* dqkv_slot(const gpt2* h, int l) {
   return reinterpret_cast<bf16_t*>(h->dqkv) + (size_t)l * bt_max(h) * 3 * h->cfg.n_embd;
 }
 
+float* ln_slot(const gpt2* h, int i) {
+  return h->ln_parts + (size_t)i * ln_bwd_scratch(bt_max(h), h->cfg.n_embd);
+}
+float* fcb_slot(const gpt2* h, int l) {
+  return h->fcb_parts + (size_t)l * fcb_part_rows(bt_max(h)) * 4 * h->cfg.n_embd;
+}
+float* attnb_slot(const gpt2* h, int l) {
+  return h->attnb_parts + (size_t)l * BIAS_SPLITS * 3 * h->cfg.n_embd;
+}
+
+// The column sums the backward defers to its end: LayerNorm weight, bias and
+// the residual-gradient sums that are the c_proj bias gradients, the c_fc and
+// the c_attn bias gradients.  Every destination appears once.
+std::vector<ColsumProblem> colsum_problems(gpt2* h, int* total_chunks) {
+  std::vector<ColsumProblem> v;
+  const int C = h->cfg.n_embd, L = h->cfg.n_layer;
+  float* G = h->grads;
+  int chunk0 = 0;
+  auto add = [&](const float* part, int ncols, int w, float* d0, float* d1, float* d2, int rpp,
+                 int fixed) {
+    ColsumProblem q{};
+    q.partial = part;
+    q.dst[0] = d0; q.dst[1] = d1; q.dst[2] = d2;
+    q.ncols = ncols; q.w = w;
+    q.rows_per_part = rpp; q.fixed_parts = fixed;
+    q.chunk0 = chunk0;
+    chunk0 += (ncols + 63) / 64;
+    v.push_back(q);
+  };
+  const bool bf = h->act == DT_BF16;
+  add(ln_slot(h, 2 * L), 3 * C, C, G + h->lay.lnfw, G + h->lay.lnfb, G + h->lay.layer[L - 1].fc2b,
+      LN_BWD_ROWS, 0);
+  for (int l = L - 1; l >= 0; --l) {
+    const LayerOff& o = h->lay.layer[l];
+    add(fcb_slot(h, l), 4 * C, 4 * C, G + o.fcb, nullptr, nullptr, bf ? 128 : 0, bf ? 0 : BIAS_SPLITS);
+    add(ln_slot(h, 2 * l + 1), 3 * C, C, G + o.ln2w, G + o.ln2b, G + o.projb, LN_BWD_ROWS, 0);
+    add(attnb_slot(h, l), 3 * C, 3 * C, G + o.attnb, nullptr, nullptr, 0, BIAS_SPLITS);
+    add(ln_slot(h, 2 * l), 3 * C, C, G + o.ln1w, G + o.ln1b,
+        l > 0 ? G + h->lay.layer[l - 1].fc2b : nullptr, LN_BWD_ROWS, 0);
+  }
+  *total_chunks = chunk0;
+  return v;
+}
+
 // The grouped weight-gradient products (bf16 mode): the lm_head's (unless
 // the head is fused) and, per block, mlp c_proj, c_fc, attn c_proj, c_attn:
 // dW = dY^T X with dY, X the saved (B*T, width) activations.
@@ -617,8 +674,7 @@ gpt2_status run_backward(gpt2* h, float scale) {
   // also the bias gradient of the last block's mlp c_proj: sum of dres
   TIMED(h, GPT2_SITE_LN_BWD, launch_layernorm_bwd(at, h->dxtmp, h->x_final, h->meanf, h->rstdf, P + h->lay.lnfw,
                                  h->dres, bf ? dres_slot(h, 2 * (c.n_layer - 1)) : nullptr, 0,
-                                 h->ln_partial, G + h->lay.lnfw, G + h->lay.lnfb,
-                                 G + h->lay.layer[c.n_layer - 1].fc2b, BT, C, s));
+                                 ln_slot(h, 2 * c.n_layer), BT, C, s));
   for (int l = c.n_layer - 1; l >= 0; --l) {
     const LayerOff& o = h->lay.layer[l];
     LayerAct& a = h->A[l];
@@ -630,11 +686,11 @@ gpt2_status run_backward(gpt2* h, float scale) {
     // x_out = x_mid + c_proj(gelu(c_fc(ln_2(x_mid))))
     // dh = dg * gelu'(h), the forward having saved gelu'(h); in bf16 mode the
     // same epilogue leaves per-128-row column sums of dh (the c_fc bias
-    // gradient) in colsum_partial
+    // gradient) in the block's slot
     EpiArgs e = epi(dbig, 4 * C);
     e.aux = a.h;
     e.ldx = 4 * C;
-    if (at == DT_BF16) e.colsum = h->colsum_partial;
+    if (at == DT_BF16) e.colsum = fcb_slot(h, l);
     const WOp w2 = w_dx(h, o.fc2w, C, 4 * C);
     TIMED(h, GPT2_SITE_FCPROJ_DX, launch_gemm(at, M, 4 * C, C, dres_out, C, false, w2.p, w2.ld, w2.t,
                           EPI_GELU_BWD, at, e, 0, s));
@@ -648,13 +704,11 @@ gpt2_status run_backward(gpt2* h, float scale) {
     if (!grouped)
       TIMED(h, GPT2_SITE_FC_DW, launch_gemm_wgrad(at, 4 * C, C, M, dbig, 4 * C, true, a.u2, C, true,
                                                   G + o.fcw, C, 1.f, h->splitk, SPLITK_PART_ELEMS, s));
-    if (bf)
-      TIMED(h, GPT2_SITE_BIAS_GRAD, launch_colsum_finish(h->colsum_partial, (M + 127) / 128, 4 * C, G + o.fcb, s));
-    else
-      TIMED(h, GPT2_SITE_BIAS_GRAD, launch_bias_grad(at, dbig, BT, 4 * C, 4 * C, h->bias_partial, G + o.fcb, s));
+    if (!bf)
+      TIMED(h, GPT2_SITE_BIAS_GRAD, launch_colsum_parts(at, dbig, BT, 4 * C, 4 * C, fcb_slot(h, l), s));
     TIMED(h, GPT2_SITE_LN_BWD, launch_layernorm_bwd(at, h->dxtmp, a.x_mid, a.mean2, a.rstd2, P + o.ln2w, h->dres,
-                                   bf ? dres_slot(h, 2 * l + 1) : nullptr, 1, h->ln_partial,
-                                   G + o.ln2w, G + o.ln2b, G + o.projb, BT, C, s));
+                                   bf ? dres_slot(h, 2 * l + 1) : nullptr, 1, ln_slot(h, 2 * l + 1),
+                                   BT, C, s));
     // x_mid = x_in + c_proj(attn(ln_1(x_in)))
     const WOp wp = w_dx(h, o.projw, C, C);
     TIMED(h, GPT2_SITE_PROJ_DX, launch_gemm(at, M, C, C, dres_mid, C, false, wp.p, wp.ld, wp.t, EPI_STORE, at,
@@ -671,14 +725,16 @@ gpt2_status run_backward(gpt2* h, float scale) {
       TIMED(h, GPT2_SITE_QKV_DW, launch_gemm_wgrad(at, 3 * C, C, M, dqkv, 3 * C, true, a.u1, C, true,
                                                    G + o.attnw, C, 1.f, h->splitk,
                                                    SPLITK_PART_ELEMS, s));
-    TIMED(h, GPT2_SITE_BIAS_GRAD, launch_bias_grad(at, dqkv, BT, 3 * C, 3 * C, h->bias_partial, G + o.attnb, s));
-    // the new dres also gives the bias gradient of the previous block's mlp c_proj
-    float* dsum = l > 0 ? G + h->lay.layer[l - 1].fc2b : nullptr;
+    TIMED(h, GPT2_SITE_BIAS_GRAD, launch_colsum_parts(at, dqkv, BT, 3 * C, 3 * C, attnb_slot(h, l), s));
+    // the new dres also gives the bias gradient of the previous block's mlp
+    // c_proj (its column sums, in the same slot)
     TIMED(h, GPT2_SITE_LN_BWD, launch_layernorm_bwd(at, h->dxtmp, a.x_in, a.mean1, a.rstd1, P + o.ln1w, h->dres,
                                    bf && l > 0 ? dres_slot(h, 2 * (l - 1)) : nullptr, 1,
-                                   h->ln_partial, G + o.ln1w, G + o.ln1b, dsum, BT, C, s));
+                                   ln_slot(h, 2 * l), BT, C, s));
   }
   TIMED(h, GPT2_SITE_EMBED_BWD, launch_embed_bwd(h->idx, h->dres, G + h->lay.wte, G + h->lay.wpe, B, T, C, s));
+  // LayerNorm parameter and bias gradients from every slot of partial sums
+  TIMED(h, GPT2_SITE_BIAS_GRAD, launch_colsum_grouped(h->cs_probs, h->cs_n, h->cs_chunks, M, s));
   if (grouped) {
     TIMED(h, GPT2_SITE_WGRAD, launch_gemm_grouped_wgrad(h->wg_probs, h->wg_n, h->wg_tiles, M, scale, s));
     const GemmProblem& t = h->wg_tail;
@@ -748,6 +804,11 @@ gpt2_status gpt2_init(const gpt2_config* cfg, void* d_workspace, size_t ws_bytes
   if (e == hipSuccess && !tt.empty())
     e = hipMemcpyAsync(h->ttiles, tt.data(), tt.size() * sizeof(TTile), hipMemcpyHostToDevice,
                        h->stream);
+  std::vector<ColsumProblem> cs = colsum_problems(h, &h->cs_chunks);
+  h->cs_n = (int)cs.size();
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(h->cs_probs, cs.data(), cs.size() * sizeof(ColsumProblem),
+                       hipMemcpyHostToDevice, h->stream);
   for (float* t : {h->params, h->grads, h->m, h->v})
     if (e == hipSuccess) e = launch_fill(t, h->lay.P, 0.f, h->stream);
   if (e == hipSuccess && h->shadow) e = hipMemsetAsync(h->shadow, 0, h->lay.P * 2, h->stream);

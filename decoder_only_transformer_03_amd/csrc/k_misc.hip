@@ -293,31 +293,43 @@ __global__ __launch_bounds__(256) void colsum_kernel(const T* __restrict__ X, lo
   if (g == 0 && n < N) partial[(long)blockIdx.y * N + n] = (s[0][c] + s[1][c]) + (s[2][c] + s[3][c]);
 }
 
-// dst_k[c] += sum_p partial[p][k*w + c] for the non-null destinations (k = 0..2).
-// 64 columns per block, four row phases per column (fixed summation order).
-__global__ __launch_bounds__(256) void colsum_finish_kernel(const float* __restrict__ partial,
-                                                            int nparts, int w,
-                                                            float* __restrict__ d0,
-                                                            float* __restrict__ d1,
-                                                            float* __restrict__ d2, int ncols) {
+// Column sums of every listed partial-sum matrix, one launch: a workgroup per
+// 64-column chunk of one problem (found by binary search over the problems'
+// first chunks), four row phases per column with four accumulators each, in a
+// fixed order.  dst[k][j] += sum over the parts of column k*w + j.
+__global__ __launch_bounds__(256) void colsum_grouped_kernel(const ColsumProblem* __restrict__ probs,
+                                                             int nprobs, long M) {
   __shared__ float sh[4][64];
-  const int cl = threadIdx.x & 63, g = threadIdx.x >> 6;
-  const int c = blockIdx.x * 64 + cl;
-  float a0 = 0.f, a1 = 0.f;
-  if (c < ncols) {
-    int p = g;
-    for (; p + 4 < nparts; p += 8) {
-      a0 += partial[(long)p * ncols + c];
-      a1 += partial[(long)(p + 4) * ncols + c];
-    }
-    if (p < nparts) a0 += partial[(long)p * ncols + c];
+  int lo = 0, hi = nprobs - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (probs[mid].chunk0 <= (int)blockIdx.x) lo = mid;
+    else hi = mid - 1;
   }
-  sh[g][cl] = a0 + a1;
+  const ColsumProblem& P = probs[lo];
+  const int ncols = P.ncols;
+  const long nparts = P.rows_per_part > 0 ? (M + P.rows_per_part - 1) / P.rows_per_part
+                                          : (long)P.fixed_parts;
+  const int cl = threadIdx.x & 63, g = threadIdx.x >> 6;
+  const int c = ((int)blockIdx.x - P.chunk0) * 64 + cl;
+  float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+  if (c < ncols) {
+    const float* p = P.partial + c;
+    long r = g;
+    for (; r + 12 < nparts; r += 16) {
+      a0 += p[r * ncols];
+      a1 += p[(r + 4) * ncols];
+      a2 += p[(r + 8) * ncols];
+      a3 += p[(r + 12) * ncols];
+    }
+    for (; r < nparts; r += 4) a0 += p[r * ncols];
+  }
+  sh[g][cl] = (a0 + a1) + (a2 + a3);
   __syncthreads();
   if (g != 0 || c >= ncols) return;
-  const int k = c / w, cc = c - k * w;
-  float* d = k == 0 ? d0 : k == 1 ? d1 : d2;
-  if (d) d[cc] += (sh[0][cl] + sh[1][cl]) + (sh[2][cl] + sh[3][cl]);
+  const int k = c / P.w, j = c - k * P.w;
+  float* d = P.dst[k];
+  if (d) d[j] += (sh[0][cl] + sh[1][cl]) + (sh[2][cl] + sh[3][cl]);
 }
 
 // ---------------------------------------------------------------------------
@@ -722,19 +734,6 @@ hipError_t launch_layernorm_fwd(DType out_t, const float* x, const float* w, con
 
 int ln_bwd_blocks(long rows) { return (int)((rows + LN_BWD_ROWS - 1) / LN_BWD_ROWS); }
 
-// Column sums of `partial` (nparts x ncols) in two passes: COLSUM_SPLITS row
-// slices, then the fixed-order finish into up to three destinations.
-static hipError_t colsum_into(const float* X, long rows, int ncols, float* scratch, int w,
-                              float* d0, float* d1, float* d2, hipStream_t s) {
-  int splits = rows >= 64 * COLSUM_SPLITS ? COLSUM_SPLITS : 1;
-  long rps = (rows + splits - 1) / splits;
-  float* part2 = scratch;
-  colsum_kernel<float><<<dim3(nblk(ncols, 64), splits), 256, 0, s>>>(X, rows, ncols, ncols, part2,
-                                                                    rps);
-  colsum_finish_kernel<<<nblk(ncols, 64), 256, 0, s>>>(part2, splits, w, d0, d1, d2, ncols);
-  return hipGetLastError();
-}
-
 template <int NV>
 static hipError_t ln_bwd_nv(DType copy_t, const float* dy, const float* x, const float* mean,
                             const float* rstd, const float* w, float* dres, void* dres_copy,
@@ -761,8 +760,7 @@ static hipError_t ln_bwd_nv(DType copy_t, const float* dy, const float* x, const
 
 hipError_t launch_layernorm_bwd(DType copy_t, const float* dy, const float* x, const float* mean,
                                 const float* rstd, const float* w, float* dres, void* dres_copy,
-                                int accumulate, float* partial, float* dw, float* db,
-                                float* dsum, long rows, int C, hipStream_t s) {
+                                int accumulate, float* partial, long rows, int C, hipStream_t s) {
   int nb = ln_bwd_blocks(rows);
   size_t shm = (size_t)12 * C * sizeof(float);
   hipError_t e;
@@ -773,20 +771,18 @@ hipError_t launch_layernorm_bwd(DType copy_t, const float* dy, const float* x, c
 #undef LNB
     default: return hipErrorInvalidValue;
   }
-  if (e != hipSuccess) return e;
-  float* scratch = partial + (long)nb * 3 * C;
-  return colsum_into(partial, nb, 3 * C, scratch, C, dw, db, dsum, s);
+  return e;
 }
 
-hipError_t launch_colsum_finish(const float* partial, int nparts, int ncols, float* dst,
-                                hipStream_t s) {
-  colsum_finish_kernel<<<nblk(ncols, 64), 256, 0, s>>>(partial, nparts, ncols, dst, nullptr,
-                                                       nullptr, ncols);
+hipError_t launch_colsum_grouped(const ColsumProblem* d_probs, int nprobs, int total_chunks, long M,
+                                 hipStream_t s) {
+  if (nprobs <= 0 || total_chunks <= 0) return hipSuccess;
+  colsum_grouped_kernel<<<total_chunks, 256, 0, s>>>(d_probs, nprobs, M);
   return hipGetLastError();
 }
 
-hipError_t launch_bias_grad(DType in_t, const void* X, long rows, int N, long ldx, float* partial,
-                            float* db, hipStream_t s) {
+hipError_t launch_colsum_parts(DType in_t, const void* X, long rows, int N, long ldx, float* partial,
+                               hipStream_t s) {
   int splits = BIAS_SPLITS;
   long rps = (rows + splits - 1) / splits;
   dim3 grid(nblk(N, 64), splits);
@@ -794,7 +790,6 @@ hipError_t launch_bias_grad(DType in_t, const void* X, long rows, int N, long ld
     colsum_kernel<bf16_t><<<grid, 256, 0, s>>>((const bf16_t*)X, rows, N, ldx, partial, rps);
   else
     colsum_kernel<float><<<grid, 256, 0, s>>>((const float*)X, rows, N, ldx, partial, rps);
-  colsum_finish_kernel<<<nblk(N, 64), 256, 0, s>>>(partial, splits, N, db, nullptr, nullptr, N);
   return hipGetLastError();
 }
 

@@ -10,12 +10,25 @@ enum DType : int { DT_F32 = 0, DT_BF16 = 1 };
 constexpr int LN_BWD_ROWS = 16;
 // bias-gradient column sums: row splits (partials of width N each)
 constexpr int BIAS_SPLITS = 64;
-// second-level column sums of the LayerNorm partials
-constexpr int COLSUM_SPLITS = 16;
-// floats of scratch launch_layernorm_bwd needs for rows x C
+// floats of partials launch_layernorm_bwd writes for rows x C
 inline long ln_bwd_scratch(long rows, int C) {
-  return ((rows + LN_BWD_ROWS - 1) / LN_BWD_ROWS) * 3L * C + (long)COLSUM_SPLITS * 3 * C;
+  return ((rows + LN_BWD_ROWS - 1) / LN_BWD_ROWS) * 3L * C;
 }
+
+// One matrix of partial column sums (nparts x ncols, row-major) whose column
+// sums go to up to three destinations: dst[k][j] += sum over the parts of
+// column k*w + j (null: skipped).  nparts = ceil(M / rows_per_part) for the
+// launch's M when rows_per_part > 0, else fixed_parts.  chunk0: the problem's
+// first 64-column chunk in the launch (problems in order, chunks contiguous).
+struct ColsumProblem {
+  const float* partial;
+  float* dst[3];
+  int ncols, w;
+  int rows_per_part, fixed_parts;
+  int chunk0;
+};
+hipError_t launch_colsum_grouped(const ColsumProblem* d_probs, int nprobs, int total_chunks, long M,
+                                 hipStream_t s);
 // grad-norm: workgroups of the sum-of-squares pass (fp64 partials)
 constexpr int NORM_PARTS = 1024;
 
@@ -45,17 +58,16 @@ hipError_t launch_embed_bwd(const int32_t* idx, const float* dx, float* dwte, fl
 hipError_t launch_layernorm_fwd(DType out_t, const float* x, const float* w, const float* b,
                                 void* y, float* mean, float* rstd, long rows, int C,
                                 hipStream_t s);
-// dw, db += LayerNorm parameter gradients; dsum (may be null) += column sums
-// of the new dres.  partial: ln_bwd_scratch(rows, C) floats.
+// LayerNorm backward into dres; partial (ln_bwd_scratch(rows, C) floats)
+// receives per-workgroup rows [dw | db | column sums of the new dres] of width
+// 3C each, ceil(rows / LN_BWD_ROWS) of them, for a column-sum launch.
 hipError_t launch_layernorm_bwd(DType copy_t, const float* dy, const float* x, const float* mean,
                                 const float* rstd, const float* w, float* dres, void* dres_copy,
-                                int accumulate, float* partial, float* dw, float* db,
-                                float* dsum, long rows, int C, hipStream_t s);
-// dst[c] += sum_p partial[p*ncols + c], p = 0..nparts-1 in order.
-hipError_t launch_colsum_finish(const float* partial, int nparts, int ncols, float* dst,
-                                hipStream_t s);
-hipError_t launch_bias_grad(DType in_t, const void* X, long rows, int N, long ldx, float* partial,
-                            float* db, hipStream_t s);
+                                int accumulate, float* partial, long rows, int C, hipStream_t s);
+// partial[BIAS_SPLITS][N]: column sums of X (rows x N, row stride ldx) over
+// BIAS_SPLITS row slices.
+hipError_t launch_colsum_parts(DType in_t, const void* X, long rows, int N, long ldx, float* partial,
+                               hipStream_t s);
 // Fused softmax cross-entropy; with grad the logits are overwritten by
 // d(loss)/d(logits), without only the losses are formed.
 hipError_t launch_xent(DType t, void* logits, const int32_t* targets, int* n_valid,

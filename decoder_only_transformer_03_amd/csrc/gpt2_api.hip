@@ -235,6 +235,12 @@ namespace {
 // Rows of a c_fc bias-gradient partial slot: per-128-row sums from the
 // GEMM epilogue (bf16) or BIAS_SPLITS row slices (fp32), whichever is more.
 size_t fcb_part_rows(size_t BT) { return std::max<size_t>((BT + 127) / 128, BIAS_SPLITS); }
+// Rows of a c_attn bias-gradient partial slot: per (sequence, 128-position
+// block) sums from the attention backward (bf16) or BIAS_SPLITS row slices
+// (fp32), whichever is more.
+size_t attnb_part_rows(const gpt2_config* c) {
+  return std::max<size_t>((size_t)c->max_batch * ((c->block_size + 127) / 128), BIAS_SPLITS);
+}
 
 // Lays out the whole workspace; with h == nullptr only measures it.
 size_t plan(const gpt2_config* c, char* base, gpt2* h) {
@@ -304,7 +310,7 @@ size_t plan(const gpt2_config* c, char* base, gpt2* h) {
   float* dbuf = a.take_n<float>(BT * H);
   float* ln_parts = a.take_n<float>((2 * nl + 1) * (size_t)ln_bwd_scratch((long)BT, (int)C));
   float* fcb_parts = a.take_n<float>(nl * fcb_part_rows(BT) * 4 * C);
-  float* attnb_parts = a.take_n<float>(nl * (size_t)BIAS_SPLITS * 3 * C);
+  float* attnb_parts = a.take_n<float>(nl * attnb_part_rows(c) * 3 * C);
   ColsumProblem* cs_probs = a.take_n<ColsumProblem>(4 * nl + 1);
   float* splitk = a.take_n<float>((size_t)SPLITK_PART_ELEMS);
   size_t total = (a.off + 255) & ~(size_t)255;
@@ -524,7 +530,7 @@ float* fcb_slot(const gpt2* h, int l) {
   return h->fcb_parts + (size_t)l * fcb_part_rows(bt_max(h)) * 4 * h->cfg.n_embd;
 }
 float* attnb_slot(const gpt2* h, int l) {
-  return h->attnb_parts + (size_t)l * BIAS_SPLITS * 3 * h->cfg.n_embd;
+  return h->attnb_parts + (size_t)l * attnb_part_rows(&h->cfg) * 3 * h->cfg.n_embd;
 }
 
 // The column sums the backward defers to its end: LayerNorm weight, bias and
@@ -553,7 +559,8 @@ std::vector<ColsumProblem> colsum_problems(gpt2* h, int* total_chunks) {
     const LayerOff& o = h->lay.layer[l];
     add(fcb_slot(h, l), 4 * C, 4 * C, G + o.fcb, nullptr, nullptr, bf ? 128 : 0, bf ? 0 : BIAS_SPLITS);
     add(ln_slot(h, 2 * l + 1), 3 * C, C, G + o.ln2w, G + o.ln2b, G + o.projb, LN_BWD_ROWS, 0);
-    add(attnb_slot(h, l), 3 * C, 3 * C, G + o.attnb, nullptr, nullptr, 0, BIAS_SPLITS);
+    add(attnb_slot(h, l), 3 * C, 3 * C, G + o.attnb, nullptr, nullptr, bf ? -1 : 0,
+        bf ? 0 : BIAS_SPLITS);
     add(ln_slot(h, 2 * l), 3 * C, C, G + o.ln1w, G + o.ln1b,
         l > 0 ? G + h->lay.layer[l - 1].fc2b : nullptr, LN_BWD_ROWS, 0);
   }
@@ -717,7 +724,10 @@ gpt2_status run_backward(gpt2* h, float scale) {
       TIMED(h, GPT2_SITE_PROJ_DW, launch_gemm_wgrad(at, C, C, M, dres_mid, C, true, a.y, C, true,
                                                     G + o.projw, C, 1.f, h->splitk,
                                                     SPLITK_PART_ELEMS, s));
-    TIMED(h, GPT2_SITE_ATTN_BWD, launch_attn_bwd(at, a.qkv, a.y, a.lse, h->dy, dqkv, h->dbuf, B, T, H, hd, s));
+    // (bf16: the attention backward also leaves the c_attn bias gradient's
+    // partial sums in the block's slot)
+    TIMED(h, GPT2_SITE_ATTN_BWD, launch_attn_bwd(at, a.qkv, a.y, a.lse, h->dy, dqkv, h->dbuf, B, T, H, hd,
+                                                 bf ? attnb_slot(h, l) : nullptr, s));
     const WOp wq = w_dx(h, o.attnw, 3 * C, C);
     TIMED(h, GPT2_SITE_QKV_DX, launch_gemm(at, M, C, 3 * C, dqkv, 3 * C, false, wq.p, wq.ld, wq.t,
                           EPI_STORE, DT_F32, epi(h->dxtmp, C), 0, s));
@@ -725,7 +735,8 @@ gpt2_status run_backward(gpt2* h, float scale) {
       TIMED(h, GPT2_SITE_QKV_DW, launch_gemm_wgrad(at, 3 * C, C, M, dqkv, 3 * C, true, a.u1, C, true,
                                                    G + o.attnw, C, 1.f, h->splitk,
                                                    SPLITK_PART_ELEMS, s));
-    TIMED(h, GPT2_SITE_BIAS_GRAD, launch_colsum_parts(at, dqkv, BT, 3 * C, 3 * C, attnb_slot(h, l), s));
+    if (!bf)
+      TIMED(h, GPT2_SITE_BIAS_GRAD, launch_colsum_parts(at, dqkv, BT, 3 * C, 3 * C, attnb_slot(h, l), s));
     // the new dres also gives the bias gradient of the previous block's mlp
     // c_proj (its column sums, in the same slot)
     TIMED(h, GPT2_SITE_LN_BWD, launch_layernorm_bwd(at, h->dxtmp, a.x_in, a.mean1, a.rstd1, P + o.ln1w, h->dres,
@@ -734,7 +745,8 @@ gpt2_status run_backward(gpt2* h, float scale) {
   }
   TIMED(h, GPT2_SITE_EMBED_BWD, launch_embed_bwd(h->idx, h->dres, G + h->lay.wte, G + h->lay.wpe, B, T, C, s));
   // LayerNorm parameter and bias gradients from every slot of partial sums
-  TIMED(h, GPT2_SITE_BIAS_GRAD, launch_colsum_grouped(h->cs_probs, h->cs_n, h->cs_chunks, M, s));
+  TIMED(h, GPT2_SITE_BIAS_GRAD, launch_colsum_grouped(h->cs_probs, h->cs_n, h->cs_chunks, M,
+                                                      B * ((T + 127) / 128), s));
   if (grouped) {
     TIMED(h, GPT2_SITE_WGRAD, launch_gemm_grouped_wgrad(h->wg_probs, h->wg_n, h->wg_tiles, M, scale, s));
     const GemmProblem& t = h->wg_tail;

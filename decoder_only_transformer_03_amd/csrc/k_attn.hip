@@ -250,6 +250,34 @@ __device__ __forceinline__ f32x16_t zero16() {
   return z;
 }
 
+// Column sums over a workgroup's 128 rows (row = 32 * wavefront + lane % 32)
+// of accumulator tiles whose lane holds dims 8i + 4(lane/32) + j, through an
+// LDS buffer of 128 rows x W floats; tile a of a row occupies dims 32a ..
+// 32a+31, its 16-byte slots XOR-permuted by row % 8.  red_put stores one
+// tile (zeros for invalid rows); after a barrier red_sum adds dim d over the
+// 128 rows in a fixed order.
+template <int W>
+__device__ __forceinline__ void red_put(float* red, const f32x16_t& v, int a, int row, int half,
+                                        bool valid) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int slot = (a * 8 + 2 * i + half) ^ (row & 7);
+    *reinterpret_cast<float4*>(red + row * W + slot * 4) =
+        valid ? make_float4(v[4 * i], v[4 * i + 1], v[4 * i + 2], v[4 * i + 3])
+              : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+}
+template <int W>
+__device__ __forceinline__ float red_sum(const float* red, int d) {
+  float s[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
+  for (int r = 0; r < 128; r += 4)
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      s[u] += red[(r + u) * W + ((((d >> 2) ^ ((r + u) & 7))) << 2) + (d & 3)];
+  return (s[0] + s[1]) + (s[2] + s[3]);
+}
+
 __device__ __forceinline__ float dot8(uint4 a, uint4 b) {
   float s = 0.f;
   uint32_t aw[4] = {a.x, a.y, a.z, a.w}, bw[4] = {b.x, b.y, b.z, b.w};
@@ -396,8 +424,9 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_mfma(const bf16_t* __restrict
                                                         const float* __restrict__ lse,
                                                         const bf16_t* __restrict__ dy,
                                                         bf16_t* __restrict__ dqkv,
-                                                        float* __restrict__ dbuf, int Tn, int H,
-                                                        int C) {
+                                                        float* __restrict__ dbuf,
+                                                        float* __restrict__ bias_part, int Tn,
+                                                        int H, int C) {
   __shared__ __attribute__((aligned(16))) bf16_t sK[2][64 * 64];
   __shared__ __attribute__((aligned(16))) bf16_t sV[2][64 * 64];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, half = lane >> 5, l32 = lane & 31;
@@ -488,6 +517,19 @@ __global__ __launch_bounds__(256) void attn_bwd_dq_mfma(const bf16_t* __restrict
       st4(o + 32 + 8 * i + 4 * half, v1);
     }
   }
+  if (bias_part) {
+    // the q part of the c_attn bias gradient: column sums of dQ over this
+    // workgroup's queries, one row of partials per (sequence, query block)
+    float* r0 = reinterpret_cast<float*>(sK);  // 128 x 32 floats each; K/V reads are done
+    float* r1 = reinterpret_cast<float*>(sV);
+    const int row = w * 32 + l32;
+    red_put<32>(r0, dq0, 0, row, half, myq < Tn);
+    red_put<32>(r1, dq1, 0, row, half, myq < Tn);
+    __syncthreads();
+    if (tid < 64)
+      bias_part[((long)b * gridDim.x + qb) * 3 * C + h * 64 + tid] =
+          red_sum<32>(tid < 32 ? r0 : r1, tid & 31) * 0.125f;
+  }
 }
 
 // dV = P^T dO and dK = (P o (dP - D))^T Q / sqrt(hd) per block of 128 keys.
@@ -495,8 +537,9 @@ __global__ __launch_bounds__(256) void attn_bwd_dkv_mfma(const bf16_t* __restric
                                                          const float* __restrict__ lse,
                                                          const bf16_t* __restrict__ dy,
                                                          const float* __restrict__ dbuf,
-                                                         bf16_t* __restrict__ dqkv, int Tn, int H,
-                                                         int C) {
+                                                         bf16_t* __restrict__ dqkv,
+                                                         float* __restrict__ bias_part, int Tn,
+                                                         int H, int C) {
   constexpr int QT = 128;  // queries staged per step (two 64-row tiles)
   __shared__ __attribute__((aligned(16))) bf16_t sQ[2][QT * 64];
   __shared__ __attribute__((aligned(16))) bf16_t sG[2][QT * 64];
@@ -625,6 +668,24 @@ __global__ __launch_bounds__(256) void attn_bwd_dkv_mfma(const bf16_t* __restric
       st4(o + 2 * C + 32 + 8 * i + 4 * half, v1);
     }
   }
+  if (bias_part) {
+    // the k and v parts of the c_attn bias gradient: column sums of dK and dV
+    // over this workgroup's keys, one row of partials per (sequence, key block)
+    float* rk = reinterpret_cast<float*>(sQ);  // 128 x 64 floats each; Q/dO reads are done
+    float* rv = reinterpret_cast<float*>(sG);
+    const int row = w * 32 + l32;
+    const bool ok = mykey < Tn;
+    red_put<64>(rk, dk0, 0, row, half, ok);
+    red_put<64>(rk, dk1, 1, row, half, ok);
+    red_put<64>(rv, dv0, 0, row, half, ok);
+    red_put<64>(rv, dv1, 1, row, half, ok);
+    __syncthreads();
+    if (tid < 128) {
+      float* out = bias_part + ((long)b * gridDim.x + kbk) * 3 * C + h * 64;
+      if (tid < 64) out[C + tid] = red_sum<64>(rk, tid) * 0.125f;
+      else out[2 * C + tid - 64] = red_sum<64>(rv, tid - 64);
+    }
+  }
 }
 
 // ===========================================================================
@@ -677,17 +738,18 @@ hipError_t launch_attn_fwd(DType t, const void* qkv, void* y, float* lse, int B,
 
 hipError_t launch_attn_bwd(DType t, const void* qkv, const void* y, const float* lse,
                            const void* dy, void* dqkv, float* dbuf, int B, int Tn, int H, int hd,
-                           hipStream_t s) {
+                           float* bias_part, hipStream_t s) {
   if (t == DT_BF16) {
     if (hd != 64) return hipErrorInvalidValue;
     dim3 grid((Tn + 127) / 128, B * H);
     int C = H * 64;
     attn_bwd_dq_mfma<<<grid, 256, 0, s>>>((const bf16_t*)qkv, (const bf16_t*)y, lse,
-                                          (const bf16_t*)dy, (bf16_t*)dqkv, dbuf, Tn, H, C);
+                                          (const bf16_t*)dy, (bf16_t*)dqkv, dbuf, bias_part, Tn,
+                                          H, C);
     attn_bwd_dkv_mfma<<<grid, 256, 0, s>>>((const bf16_t*)qkv, lse, (const bf16_t*)dy, dbuf,
-                                           (bf16_t*)dqkv, Tn, H, C);
+                                           (bf16_t*)dqkv, bias_part, Tn, H, C);
     return hipGetLastError();
   }
-  if (hd != 32 && hd != 64) return hipErrorInvalidValue;
+  if ((hd != 32 && hd != 64) || bias_part) return hipErrorInvalidValue;
   return simt_bwd<float>(qkv, y, lse, dy, dqkv, dbuf, B, Tn, H, hd, s);
 }

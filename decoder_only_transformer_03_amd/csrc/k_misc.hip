@@ -298,7 +298,7 @@ __global__ __launch_bounds__(256) void colsum_kernel(const T* __restrict__ X, lo
 // first chunks), four row phases per column with four accumulators each, in a
 // fixed order.  dst[k][j] += sum over the parts of column k*w + j.
 __global__ __launch_bounds__(256) void colsum_grouped_kernel(const ColsumProblem* __restrict__ probs,
-                                                             int nprobs, long M) {
+                                                             int nprobs, long M, int nblk) {
   __shared__ float sh[4][64];
   int lo = 0, hi = nprobs - 1;
   while (lo < hi) {
@@ -308,8 +308,9 @@ __global__ __launch_bounds__(256) void colsum_grouped_kernel(const ColsumProblem
   }
   const ColsumProblem& P = probs[lo];
   const int ncols = P.ncols;
-  const long nparts = P.rows_per_part > 0 ? (M + P.rows_per_part - 1) / P.rows_per_part
-                                          : (long)P.fixed_parts;
+  const long nparts = P.rows_per_part > 0   ? (M + P.rows_per_part - 1) / P.rows_per_part
+                      : P.rows_per_part < 0 ? (long)nblk
+                                            : (long)P.fixed_parts;
   const int cl = threadIdx.x & 63, g = threadIdx.x >> 6;
   const int c = ((int)blockIdx.x - P.chunk0) * 64 + cl;
   float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
@@ -775,9 +776,9 @@ hipError_t launch_layernorm_bwd(DType copy_t, const float* dy, const float* x, c
 }
 
 hipError_t launch_colsum_grouped(const ColsumProblem* d_probs, int nprobs, int total_chunks, long M,
-                                 hipStream_t s) {
+                                 int nblk, hipStream_t s) {
   if (nprobs <= 0 || total_chunks <= 0) return hipSuccess;
-  colsum_grouped_kernel<<<total_chunks, 256, 0, s>>>(d_probs, nprobs, M);
+  colsum_grouped_kernel<<<total_chunks, 256, 0, s>>>(d_probs, nprobs, M, nblk);
   return hipGetLastError();
 }
 

@@ -18,7 +18,8 @@ inline long ln_bwd_scratch(long rows, int C) {
 // One matrix of partial column sums (nparts x ncols, row-major) whose column
 // sums go to up to three destinations: dst[k][j] += sum over the parts of
 // column k*w + j (null: skipped).  nparts = ceil(M / rows_per_part) for the
-// launch's M when rows_per_part > 0, else fixed_parts.  chunk0: the problem's
+// launch's M when rows_per_part > 0, the launch's nblk when rows_per_part < 0,
+// else fixed_parts.  chunk0: the problem's
 // first 64-column chunk in the launch (problems in order, chunks contiguous).
 struct ColsumProblem {
   const float* partial;
@@ -28,7 +29,7 @@ struct ColsumProblem {
   int chunk0;
 };
 hipError_t launch_colsum_grouped(const ColsumProblem* d_probs, int nprobs, int total_chunks, long M,
-                                 hipStream_t s);
+                                 int nblk, hipStream_t s);
 // grad-norm: workgroups of the sum-of-squares pass (fp64 partials)
 constexpr int NORM_PARTS = 1024;
 
@@ -146,6 +147,8 @@ constexpr long SPLITK_PART_ELEMS = 256L * 256 * 256;
 hipError_t launch_attn_fwd(DType t, const void* qkv, void* y, float* lse, int B, int T, int H,
                            int hd, hipStream_t s);
 // Gradients into dqkv (B*T, 3C) given dy (B*T, C); dbuf (B, H, T) fp32 scratch.
+// bias_part (bf16 only; null: skipped): row b*ceil(T/128) + j receives the
+// column sums of dqkv over rows j*128 .. j*128+127 of sequence b, width 3C.
 hipError_t launch_attn_bwd(DType t, const void* qkv, const void* y, const float* lse,
                            const void* dy, void* dqkv, float* dbuf, int B, int T, int H, int hd,
-                           hipStream_t s);
+                           float* bias_part, hipStream_t s);

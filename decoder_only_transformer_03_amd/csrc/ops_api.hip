@@ -39,7 +39,8 @@ gpt2_status gpt2_op_attention_bwd(int dtype, const void* qkv, const void* y, con
                                   int hd, void* hip_stream) {
   if (!qkv || !y || !lse || !dy || !dqkv || !dbuf || B < 1 || T < 1 || H < 1) return GPT2_E_ARG;
   hipError_t r = launch_attn_bwd(dtype == GPT2_BF16 ? DT_BF16 : DT_F32, qkv, y, lse, dy, dqkv,
-                                 dbuf, B, T, H, hd, reinterpret_cast<hipStream_t>(hip_stream));
+                                 dbuf, B, T, H, hd, nullptr,
+                                 reinterpret_cast<hipStream_t>(hip_stream));
   if (r == hipErrorInvalidValue) return GPT2_E_ARG;
   return r == hipSuccess ? GPT2_OK : GPT2_E_HIP;
 }

@@ -211,6 +211,7 @@ struct gpt2 {
   float* fcb_parts;
   float* attnb_parts;
   ColsumProblem* cs_probs;
+  void* emb_scratch;  // embedding backward: id sort and per-chunk run sums
   int cs_n = 0;
   int cs_chunks = 0;
   float* splitk;
@@ -312,6 +313,7 @@ size_t plan(const gpt2_config* c, char* base, gpt2* h) {
   float* fcb_parts = a.take_n<float>(nl * fcb_part_rows(BT) * 4 * C);
   float* attnb_parts = a.take_n<float>(nl * attnb_part_rows(c) * 3 * C);
   ColsumProblem* cs_probs = a.take_n<ColsumProblem>(4 * nl + 1);
+  void* emb_scratch = a.take(embed_bwd_scratch_bytes((long)BT, (int)C));
   float* splitk = a.take_n<float>((size_t)SPLITK_PART_ELEMS);
   size_t total = (a.off + 255) & ~(size_t)255;
   if (h) {
@@ -332,6 +334,7 @@ size_t plan(const gpt2_config* c, char* base, gpt2* h) {
     h->dy = dy; h->dbuf = dbuf;
     h->ln_parts = ln_parts; h->fcb_parts = fcb_parts; h->attnb_parts = attnb_parts;
     h->cs_probs = cs_probs;
+    h->emb_scratch = emb_scratch;
     h->splitk = splitk;
   }
   return total;
@@ -743,7 +746,8 @@ gpt2_status run_backward(gpt2* h, float scale) {
                                    bf && l > 0 ? dres_slot(h, 2 * (l - 1)) : nullptr, 1,
                                    ln_slot(h, 2 * l), BT, C, s));
   }
-  TIMED(h, GPT2_SITE_EMBED_BWD, launch_embed_bwd(h->idx, h->dres, G + h->lay.wte, G + h->lay.wpe, B, T, C, s));
+  TIMED(h, GPT2_SITE_EMBED_BWD, launch_embed_bwd(h->idx, h->dres, G + h->lay.wte, G + h->lay.wpe, B, T, C,
+                                                 c.padded_vocab_size, h->emb_scratch, s));
   // LayerNorm parameter and bias gradients from every slot of partial sums
   TIMED(h, GPT2_SITE_BIAS_GRAD, launch_colsum_grouped(h->cs_probs, h->cs_n, h->cs_chunks, M,
                                                       B * ((T + 127) / 128), s));

@@ -36,53 +36,290 @@ __global__ __launch_bounds__(256) void embed_fwd_kernel(const int32_t* __restric
 
 // dwte[idx[p],:] += dx[p,:]  (adds onto the lm_head part already there: the
 // tied weight's gradient is the sum of both uses, "Weight tying").
-// dwte[idx[r]] += dx[r] for a chunk of EMB_CHUNK rows per block.  The chunk's
-// (id, row) pairs are ranked in LDS so that rows with the same id are summed in
-// registers first and each distinct id costs one atomic per column: with the
-// skewed token statistics of text, most of a chunk's rows share a few ids, and
-// atomics on one address serialise.
-constexpr int EMB_CHUNK = 64;
-__global__ __launch_bounds__(256) void embed_bwd_wte_kernel(const int32_t* __restrict__ idx,
-                                                            const float* __restrict__ dx,
-                                                            float* __restrict__ dwte, int C,
-                                                            long rows) {
-  __shared__ unsigned key[EMB_CHUNK], sorted[EMB_CHUNK];
-  const long r0 = (long)blockIdx.x * EMB_CHUNK;
-  const int n = rows - r0 < EMB_CHUNK ? (int)(rows - r0) : EMB_CHUNK;
-  const int t = threadIdx.x;
-  if (t < n) key[t] = ((unsigned)idx[r0 + t] << 6) | (unsigned)t;  // ids < 2^26
+// Deterministic, no atomics, in three launches:
+//  1. a stable sort of the positions by token id (one workgroup, radix sort);
+//  2. per chunk of EMB_CHUNK sorted positions, the sum of each run of equal
+//     ids in position order: a run wholly inside the chunk is added to its
+//     dwte row directly (its only writer); the piece of a run that continues
+//     into the next chunk (head) and the piece that continues from the
+//     previous one (tail) go to per-chunk slots instead;
+//  3. per head: head + the following chunks' tails of the same id, in chunk
+//     order, added to the dwte row.
+constexpr int EMB_CHUNK = 32;
+constexpr int SORT_THREADS = 1024;
+
+// Exclusive prefix sum over the workgroup (NTH threads) of v, and the total.
+template <int NTH>
+__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* wsum,
+                                                         uint32_t* total) {
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  uint32_t x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) wsum[w] = x;
   __syncthreads();
-  if (t < n) {
-    const unsigned k = key[t];
-    int rank = 0;
-    for (int j = 0; j < n; ++j) rank += key[j] < k;
-    sorted[rank] = k;
+  if (t == 0) {
+    uint32_t run = 0;
+    for (int i = 0; i < NTH / 64; ++i) {
+      const uint32_t c = wsum[i];
+      wsum[i] = run;
+      run += c;
+    }
+    wsum[NTH / 64] = run;
   }
   __syncthreads();
+  const uint32_t r = wsum[w] + x - v;
+  *total = wsum[NTH / 64];
+  __syncthreads();
+  return r;
+}
+
+// Stable LSD radix sort (4-bit digits, npass passes, npass even) of n keys
+// (token ids) with their positions as values, over global ping-pong buffers;
+// the result is in (ka, va).  Thread t owns a contiguous range of elements:
+// it counts their digits, a workgroup scan over the (digit, thread) counters
+// gives its output offsets, and it scatters them in their original order.
+__global__ __launch_bounds__(SORT_THREADS) void id_sort_kernel(const int32_t* __restrict__ idx,
+                                                               long n, int npass,
+                                                               uint32_t* __restrict__ ka,
+                                                               uint32_t* __restrict__ va,
+                                                               uint32_t* __restrict__ kb,
+                                                               uint32_t* __restrict__ vb) {
+  __shared__ uint32_t cnt[16 * SORT_THREADS];  // [digit][thread]
+  __shared__ uint32_t wsum[SORT_THREADS / 64 + 1];
+  const int t = threadIdx.x;
+  const long per = (n + SORT_THREADS - 1) / SORT_THREADS;
+  const long e0 = t * per < n ? t * per : n, e1 = e0 + per < n ? e0 + per : n;
+  for (long i = t; i < n; i += SORT_THREADS) {
+    ka[i] = (uint32_t)idx[i];
+    va[i] = (uint32_t)i;
+  }
+  __syncthreads();
+  uint32_t *ks = ka, *vs = va, *kd = kb, *vd = vb;
+  for (int pass = 0; pass < npass; ++pass) {
+    const int shift = 4 * pass;
+#pragma unroll
+    for (int d = 0; d < 16; ++d) cnt[d * SORT_THREADS + t] = 0;
+    for (long i = e0; i < e1; ++i) atomicAdd(&cnt[((ks[i] >> shift) & 15u) * SORT_THREADS + t], 1u);
+    __syncthreads();
+    // exclusive scan over the flattened counters, 16 consecutive per thread
+    uint32_t loc[16], sum = 0;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      loc[j] = sum;
+      sum += cnt[16 * t + j];
+    }
+    uint32_t total;
+    const uint32_t base = block_exclusive_scan<SORT_THREADS>(sum, wsum, &total);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) cnt[16 * t + j] = base + loc[j];
+    __syncthreads();
+    for (long i = e0; i < e1; ++i) {
+      const uint32_t k = ks[i];
+      const uint32_t o = atomicAdd(&cnt[((k >> shift) & 15u) * SORT_THREADS + t], 1u);
+      kd[o] = k;
+      vd[o] = vs[i];
+    }
+    __syncthreads();  // scattered keys visible to the whole workgroup
+    uint32_t* tk = ks; ks = kd; kd = tk;
+    uint32_t* tv = vs; vs = vd; vd = tv;
+    __syncthreads();
+  }
+}
+
+// The same sort held in LDS, for n <= SORT_LDS_N positions and ids below
+// 2^16: each element is packed as id << 16 | position, so sorting by the top
+// 16 bits carries the position along.  3-bit digits; 512 threads own 32
+// consecutive elements each, element e at LDS word e + e/32 so that the
+// threads of a wavefront stepping through their own ranges hit different
+// banks.  Per-thread digit counters live in LDS (column t of cnt): outside
+// the scan only thread t touches them, so its atomic adds there are plain
+// in-order counters.  The sorted ids and positions go to (ka, va).
+constexpr int SORT_LDS_N = 16384;
+constexpr int SORT_LDS_THREADS = 512;
+constexpr int SORT_LDS_DIGITS = 8;
+__device__ __forceinline__ int sort_slot(int e) { return e + (e >> 5); }
+__global__ __launch_bounds__(SORT_LDS_THREADS) void id_sort_lds_kernel(
+    const int32_t* __restrict__ idx, int n, int npass, uint32_t* __restrict__ ka,
+    uint32_t* __restrict__ va) {
+  __shared__ uint32_t buf[2][SORT_LDS_N + SORT_LDS_N / 32];
+  __shared__ uint32_t cnt[SORT_LDS_DIGITS * SORT_LDS_THREADS];  // [digit][thread]
+  __shared__ uint32_t wsum[SORT_LDS_THREADS / 64 + 1];
+  constexpr int PER = SORT_LDS_N / SORT_LDS_THREADS;
+  const int t = threadIdx.x;
+  const int e0 = t * PER, e1 = e0 + PER < n ? e0 + PER : n;  // (empty when e0 >= n)
+  // (fixed trip counts below, so that the loads of a loop are issued together)
+#pragma unroll 16
+  for (int j = 0; j < PER; ++j) {
+    const int i = j * SORT_LDS_THREADS + t;
+    if (i < n) buf[0][sort_slot(i)] = ((uint32_t)idx[i] << 16) | (uint32_t)i;
+  }
+  __syncthreads();
+  int src = 0;
+  for (int pass = 0; pass < npass; ++pass) {
+    const int shift = 16 + 3 * pass;
+    const uint32_t* ks = buf[src];
+    uint32_t* kd = buf[src ^ 1];
+#pragma unroll
+    for (int d = 0; d < SORT_LDS_DIGITS; ++d) cnt[d * SORT_LDS_THREADS + t] = 0;
+#pragma unroll 8
+    for (int j = 0; j < PER; ++j) {
+      const int i = e0 + j;
+      if (i >= e1) break;
+      const uint32_t d = (ks[sort_slot(i)] >> shift) & 7u;
+      atomicAdd(&cnt[d * SORT_LDS_THREADS + t], 1u);
+    }
+    __syncthreads();
+    // exclusive scan over the flattened (digit, thread) counters
+    uint32_t loc[SORT_LDS_DIGITS], sum = 0;
+#pragma unroll
+    for (int j = 0; j < SORT_LDS_DIGITS; ++j) {
+      loc[j] = sum;
+      sum += cnt[SORT_LDS_DIGITS * t + j];
+    }
+    uint32_t total;
+    const uint32_t base = block_exclusive_scan<SORT_LDS_THREADS>(sum, wsum, &total);
+#pragma unroll
+    for (int j = 0; j < SORT_LDS_DIGITS; ++j) cnt[SORT_LDS_DIGITS * t + j] = base + loc[j];
+    __syncthreads();
+    // scatter in order: each element takes the next slot of its digit
+#pragma unroll 8
+    for (int j = 0; j < PER; ++j) {
+      const int i = e0 + j;
+      if (i >= e1) break;
+      const uint32_t k = ks[sort_slot(i)];
+      const uint32_t o = atomicAdd(&cnt[((k >> shift) & 7u) * SORT_LDS_THREADS + t], 1u);
+      kd[sort_slot((int)o)] = k;
+    }
+    __syncthreads();
+    src ^= 1;
+  }
+#pragma unroll 16
+  for (int j = 0; j < PER; ++j) {
+    const int i = j * SORT_LDS_THREADS + t;
+    if (i < n) {
+      const uint32_t k = buf[src][sort_slot(i)];
+      ka[i] = k >> 16;
+      va[i] = k & 0xffffu;
+    }
+  }
+}
+
+// Step 2: one workgroup per chunk of EMB_CHUNK sorted positions (keys = ids,
+// vals = positions); thread t sums columns 4t.. (stride 1024).  head/tail:
+// [chunk][C] slots; hflag/tflag[chunk]: the id of the chunk's head / tail
+// piece, or -1.
+__global__ __launch_bounds__(256) void embed_bwd_chunk_kernel(const uint32_t* __restrict__ keys,
+                                                              const uint32_t* __restrict__ vals,
+                                                              const float* __restrict__ dx,
+                                                              float* __restrict__ dwte,
+                                                              float* __restrict__ head,
+                                                              float* __restrict__ tail,
+                                                              int* __restrict__ hflag,
+                                                              int* __restrict__ tflag, int C,
+                                                              long n) {
+  __shared__ uint32_t key[EMB_CHUNK], pos[EMB_CHUNK];
+  const long p0 = (long)blockIdx.x * EMB_CHUNK;
+  const int m = n - p0 < EMB_CHUNK ? (int)(n - p0) : EMB_CHUNK;
+  const int t = threadIdx.x;
+  if (t < m) {
+    key[t] = keys[p0 + t];
+    pos[t] = vals[p0 + t];
+  }
+  __syncthreads();
+  // does the first run continue from the previous chunk, the last into the next?
+  const bool cont_in = p0 > 0 && keys[p0 - 1] == key[0];
+  const bool cont_out = p0 + m < n && keys[p0 + m] == key[m - 1];
+  if (t == 0) {
+    tflag[blockIdx.x] = cont_in ? (int)key[0] : -1;
+    // a chunk inside one run has no head of its own: the run started earlier
+    const bool one_run = key[0] == key[m - 1];
+    hflag[blockIdx.x] = cont_out && !(one_run && cont_in) ? (int)key[m - 1] : -1;
+  }
   for (int c = t * 4; c < C; c += 1024) {
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int q0 = 0; q0 < n; q0 += 8) {
+    int qs = 0;  // first position of the current run in this chunk
+    for (int q0 = 0; q0 < m; q0 += 8) {
       float4 v[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j)  // issue the batch's loads before using any
-        if (q0 + j < n)
-          v[j] = *reinterpret_cast<const float4*>(dx + (r0 + (sorted[q0 + j] & 63u)) * C + c);
+        if (q0 + j < m) v[j] = *reinterpret_cast<const float4*>(dx + (long)pos[q0 + j] * C + c);
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const int q = q0 + j;
-        if (q >= n) break;
-        const unsigned k = sorted[q];
+        if (q >= m) break;
         acc.x += v[j].x; acc.y += v[j].y; acc.z += v[j].z; acc.w += v[j].w;
-        if (q + 1 == n || (sorted[q + 1] >> 6) != (k >> 6)) {
-          float* d = dwte + (long)(k >> 6) * C + c;
-          atomicAdd(d + 0, acc.x);
-          atomicAdd(d + 1, acc.y);
-          atomicAdd(d + 2, acc.z);
-          atomicAdd(d + 3, acc.w);
+        if (q + 1 == m || key[q + 1] != key[q]) {
+          const bool from_prev = qs == 0 && cont_in, to_next = q + 1 == m && cont_out;
+          float* d;
+          if (from_prev) d = tail + (long)blockIdx.x * C + c;           // continues a run
+          else if (to_next) d = head + (long)blockIdx.x * C + c;        // run goes on
+          else d = dwte + (long)key[q] * C + c;                         // whole run here
+          if (from_prev || to_next) {
+            *reinterpret_cast<float4*>(d) = acc;
+          } else {
+            float4 o = *reinterpret_cast<const float4*>(d);
+            o.x += acc.x; o.y += acc.y; o.z += acc.z; o.w += acc.w;
+            *reinterpret_cast<float4*>(d) = o;
+          }
           acc = make_float4(0.f, 0.f, 0.f, 0.f);
+          qs = q + 1;
         }
       }
     }
+  }
+}
+
+// Step 3: one workgroup per chunk with a head: head + tails of the following
+// chunks while they continue the same id, in chunk order, into the dwte row.
+// The run's last chunk is found first (all threads test one flag each), so
+// that the tails' loads can be issued in batches.
+__global__ __launch_bounds__(256) void embed_bwd_fix_kernel(const float* __restrict__ head,
+                                                            const float* __restrict__ tail,
+                                                            const int* __restrict__ hflag,
+                                                            const int* __restrict__ tflag,
+                                                            float* __restrict__ dwte, int C,
+                                                            int nchunks) {
+  __shared__ int stop;
+  const int ch = blockIdx.x;
+  const int id = hflag[ch];
+  if (id < 0) return;
+  // end = first chunk after ch that does not continue the run
+  int end = ch + 1;
+  for (;;) {
+    if (threadIdx.x == 0) stop = nchunks;
+    __syncthreads();
+    const int k = end + (int)threadIdx.x;
+    if (k < nchunks && tflag[k] != id) atomicMin(&stop, k);
+    __syncthreads();
+    const int st = stop;
+    __syncthreads();
+    if (st < nchunks || end + 256 >= nchunks) {
+      end = st < end + 256 ? st : (end + 256 < nchunks ? end + 256 : nchunks);
+      break;
+    }
+    end += 256;
+  }
+  for (int c = threadIdx.x * 4; c < C; c += 1024) {
+    float4 a = *reinterpret_cast<const float4*>(head + (long)ch * C + c);
+    for (int k0 = ch + 1; k0 < end; k0 += 8) {
+      float4 v[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (k0 + j < end) v[j] = *reinterpret_cast<const float4*>(tail + (long)(k0 + j) * C + c);
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (k0 + j < end) {
+          a.x += v[j].x; a.y += v[j].y; a.z += v[j].z; a.w += v[j].w;
+        }
+    }
+    float* d = dwte + (long)id * C + c;
+    float4 o = *reinterpret_cast<const float4*>(d);
+    o.x += a.x; o.y += a.y; o.z += a.z; o.w += a.w;
+    *reinterpret_cast<float4*>(d) = o;
   }
 }
 
@@ -697,10 +934,37 @@ hipError_t launch_embed_fwd(const int32_t* idx_in, int32_t* idx_saved, const flo
   return hipGetLastError();
 }
 
+size_t embed_bwd_scratch_bytes(long rows, int C) {
+  const long nch = (rows + EMB_CHUNK - 1) / EMB_CHUNK;
+  return (size_t)4 * rows * sizeof(uint32_t) + (size_t)2 * nch * C * sizeof(float) +
+         (size_t)2 * nch * sizeof(int) + 256;
+}
+
 hipError_t launch_embed_bwd(const int32_t* idx, const float* dx, float* dwte, float* dwpe, int B,
-                            int T, int C, hipStream_t s) {
-  long rows = (long)B * T;
-  embed_bwd_wte_kernel<<<nblk(rows, EMB_CHUNK), 256, 0, s>>>(idx, dx, dwte, C, rows);
+                            int T, int C, int Vp, void* scratch, hipStream_t s) {
+  const long rows = (long)B * T;
+  const long nch = (rows + EMB_CHUNK - 1) / EMB_CHUNK;
+  if (C % 4) return hipErrorInvalidValue;
+  uint32_t* ka = reinterpret_cast<uint32_t*>(scratch);
+  uint32_t* va = ka + rows;
+  uint32_t* kb = va + rows;
+  uint32_t* vb = kb + rows;
+  float* head = reinterpret_cast<float*>(vb + rows);
+  float* tail = head + nch * C;
+  int* hflag = reinterpret_cast<int*>(tail + nch * C);
+  int* tflag = hflag + nch;
+  int bits = 1;
+  while (bits < 31 && (1L << bits) < (long)Vp) ++bits;
+  if (rows <= SORT_LDS_N && bits <= 16) {
+    id_sort_lds_kernel<<<1, SORT_LDS_THREADS, 0, s>>>(idx, (int)rows, (bits + 2) / 3, ka, va);
+  } else {
+    int npass = (bits + 3) / 4;
+    npass += npass & 1;  // even: the sorted result ends in (ka, va)
+    id_sort_kernel<<<1, SORT_THREADS, 0, s>>>(idx, rows, npass, ka, va, kb, vb);
+  }
+  embed_bwd_chunk_kernel<<<(unsigned)nch, 256, 0, s>>>(ka, va, dx, dwte, head, tail, hflag, tflag,
+                                                       C, rows);
+  embed_bwd_fix_kernel<<<(unsigned)nch, 256, 0, s>>>(head, tail, hflag, tflag, dwte, C, (int)nch);
   embed_bwd_wpe_kernel<<<nblk((long)T * C, 256), 256, 0, s>>>(dx, dwpe, B, T, C);
   return hipGetLastError();
 }

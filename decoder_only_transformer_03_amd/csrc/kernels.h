@@ -54,8 +54,11 @@ int ln_bwd_blocks(long rows);
 hipError_t launch_embed_fwd(const int32_t* idx_in, int32_t* idx_saved, const float* wte,
                             const float* wpe, float* x, int B, int T, int C, int Vp, int* err,
                             hipStream_t s);
+// dwte[idx[r]] += dx[r] over the B*T rows (deterministic; ids in [0, Vp)),
+// dwpe[t] += sum_b dx[b,t]; scratch: embed_bwd_scratch_bytes(B*T, C) bytes.
+size_t embed_bwd_scratch_bytes(long rows, int C);
 hipError_t launch_embed_bwd(const int32_t* idx, const float* dx, float* dwte, float* dwpe, int B,
-                            int T, int C, hipStream_t s);
+                            int T, int C, int Vp, void* scratch, hipStream_t s);
 hipError_t launch_layernorm_fwd(DType out_t, const float* x, const float* w, const float* b,
                                 void* y, float* mean, float* rstd, long rows, int C,
                                 hipStream_t s);

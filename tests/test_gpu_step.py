@@ -157,6 +157,32 @@ def test_fp32_tiny_step_matches_oracle(B, T, hc):
         assert e[w] < 1e-3, (key, w, e[w])
 
 
+def test_fp32_embedding_backward_many_skewed_rows():
+    """More positions than the in-LDS id sort holds (300 x 64 = 19,200 > 16,384:
+    the sort runs over global memory) with heavily repeated ids (runs of one
+    id across many chunks of sorted positions): the wte and wpe gradients
+    against the oracle's, and bit-identical when the backward runs again."""
+    d = synthetic.model_dims("tiny")
+    B, T = 300, 64
+    flat = synthetic.init_params(d, seed=42)
+    rng = np.random.default_rng(77)
+    idx = ((rng.zipf(1.3, size=(B, T)) - 1) % d["vocab_size"]).astype(np.int64)
+    tgt = np.roll(idx, -1, axis=1)
+    g = run_gpu_step(d, "fp32", flat, idx, tgt)
+    r = run_oracle_step(d, flat, idx, tgt)
+    err = per_tensor(O.Config(**d), g["grads"], r["grads"])
+    print(f"\nB={B} T={T}: wte {err['wte']:.2e} wpe {err['wpe']:.2e}")
+    assert err["wte"] < 1e-3 and err["wpe"] < 1e-3
+    m = g["model"]  # (its parameters have taken one AdamW step since)
+    again = []
+    for _ in range(2):
+        m.zero_grad()
+        m.forward(dev_ids(idx), dev_ids(tgt))
+        m.backward(1.0)
+        again.append(m.get(G.GPT2_GRADS))
+    assert np.array_equal(again[0], again[1])
+
+
 def test_fp32_accumulation_equals_big_batch():
     d = synthetic.model_dims("tiny")
     flat = synthetic.init_params(d, seed=7)
@@ -382,6 +408,29 @@ def test_bf16_124m_weight_gradient_layout(step_124m_b2):
         tiny.close()
     assert "WGRAD" not in s2 and "WGRAD_TAIL" not in s2
     assert s2["FC_DW"][1] == dt["n_layer"] and s2["LMHEAD_DW"][1] == 1
+
+
+def test_bf16_124m_backward_is_deterministic(step_124m_b2):
+    """Every reduction of the backward runs in a fixed order (split-K slices
+    and column sums summed in order, weight-gradient tiles whole, one atomic
+    add per embedding row and column): the same step twice gives bit-identical
+    gradients, with the materialised and with the fused head."""
+    d, flat, idx, tgt, g, _ = step_124m_b2
+    ms = [g["model"], G.GPT2(G.make_config(max_batch=2, precision="bf16", head_chunk=4096, **d),
+                             device=DEV)]
+    try:
+        ms[1].set_params(flat)
+        for m in ms:
+            runs = []
+            for _ in range(2):
+                m.zero_grad()
+                m.forward(dev_ids(idx), dev_ids(tgt))
+                m.backward(1.0)
+                runs.append(m.get(G.GPT2_GRADS))
+            assert np.isfinite(runs[0]).all()
+            assert np.array_equal(runs[0], runs[1])
+    finally:
+        ms[1].close()
 
 
 def check_bf16_step(d, flat, g, r):

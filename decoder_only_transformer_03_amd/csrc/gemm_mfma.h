@@ -608,6 +608,12 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(int M, int N, int
   constexpr int NT = 64 * WM * WN;
   constexpr int WTM = BM / WM, WTN = BN / WN;
   constexpr int SM = WTM / 32, SN = WTN / 32;
+  // Where a k-step issues the loads of the next k-tile: right after its
+  // barrier, or -- with a transposed operand, whose fragment reads are the
+  // heavier -- once the fragments of its first two substeps are read, so
+  // that those reads do not queue behind the loads' address traffic.  (On
+  // the measured shapes each placement was the faster for its layout.)
+  constexpr bool issue_late = LA == 3 || LB == 3;
   __shared__ __attribute__((aligned(16))) bf16_t smem[2][(BM + BN) * BK];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -668,13 +674,6 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(int M, int N, int
   decode(item);
 
   f32x16_t acc[SN][SM];
-#pragma unroll
-  for (int a = 0; a < SN; ++a)
-#pragma unroll
-    for (int b = 0; b < SM; ++b)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.f;
-
   Loader<BM, LA, NT> la;
   Loader<BN, LB, NT> lb;
   setup(la, lb);
@@ -682,8 +681,6 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(int M, int N, int
   lb.issue(B, ldb, n0, N, kt0 * BK, K, tid, smem[0] + BM * BK);
   la.commit(smem[0], tid);
   lb.commit(smem[0] + BM * BK, tid);
-  if constexpr (LA >= 2 || LB >= 2) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
 
   // Fragments of k-substep kk (16 deep) for this wavefront's sub-tiles.
   auto load_frags = [&](const bf16_t* sA, const bf16_t* sB, int kk, bf16x8_t* fa, bf16x8_t* fb) {
@@ -708,53 +705,75 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(int M, int N, int
     }
   };
 
-  // Software pipeline: the loads of the next k-tile -- of this item, or the
-  // first k-tile of the next item -- are in flight during the MFMAs of the
-  // current one, and the LDS fragments of substep kk+1 are read while the
-  // MFMAs of substep kk run.  The epilogue's stores overlap the next item.
+  // Software pipeline: each k-step starts by waiting for its k-tile and a
+  // barrier; the loads of the next k-tile -- of this item, or the first
+  // k-tile of the next item -- go out at the start of the k-step and are in
+  // flight during the rest of it; the LDS fragments of substep kk+1 are
+  // read while the MFMAs of substep kk run.  The epilogue's stores overlap
+  // the next item's first k-step.
   bf16x8_t fa[2][SM], fb[2][SN];
-  load_frags(smem[0], smem[0] + BM * BK, 0, fa[0], fb[0]);
   int cur = 0;
   while (true) {
+#pragma unroll
+    for (int a = 0; a < SN; ++a)
+#pragma unroll
+      for (int b = 0; b < SM; ++b)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.f;
     const long em0 = m0, en0 = n0;  // this item's output tile
     const int ekt1 = kt1, esplit = split, eprob = prob;
     for (int kt = kt0; kt < ekt1; ++kt) {
       const bool last_k = kt + 1 == ekt1;
       const bool more = !last_k || item + gridDim.x < nitems;
-      if (more) {
-        if (last_k) {
-          decode(item + gridDim.x);
-          setup(la, lb);
-        }
-        const int nk = last_k ? kt0 : kt + 1;
-        la.issue(A, lda, m0, M, nk * BK, K, tid, smem[cur ^ 1]);
-        lb.issue(B, ldb, n0, N, nk * BK, K, tid, smem[cur ^ 1] + BM * BK);
-      }
+      // (the first k-tile of a later item was waited for before the previous
+      // epilogue, whose stores then drain during this k-step)
+      if constexpr (LA >= 2 || LB >= 2)
+        if (kt != kt0 || item == blockIdx.x) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();  // this k-tile is in LDS; the other stage is free
       const bf16_t* sA = smem[cur];
       const bf16_t* sB = smem[cur] + BM * BK;
-#pragma unroll
-      for (int kk = 0; kk < BK / 16; ++kk) {
-        if (kk + 1 < BK / 16) load_frags(sA, sB, kk + 1, fa[(kk + 1) & 1], fb[(kk + 1) & 1]);
+      auto issue_next = [&]() {
+        __builtin_amdgcn_sched_barrier(0);
+        if (more) {
+          if (last_k) {
+            decode(item + gridDim.x);
+            setup(la, lb);
+          }
+          const int nk = last_k ? kt0 : kt + 1;
+          la.issue(A, lda, m0, M, nk * BK, K, tid, smem[cur ^ 1]);
+          lb.issue(B, ldb, n0, N, nk * BK, K, tid, smem[cur ^ 1] + BM * BK);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      };
+      auto mfmas = [&](int j) {
 #pragma unroll
         for (int sn = 0; sn < SN; ++sn)
 #pragma unroll
           for (int sm = 0; sm < SM; ++sm)
-            acc[sn][sm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[kk & 1][sn], fa[kk & 1][sm],
-                                                                  acc[sn][sm], 0, 0, 0);
+            acc[sn][sm] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j][sn], fa[j][sm], acc[sn][sm],
+                                                                  0, 0, 0);
+      };
+      if constexpr (!issue_late) issue_next();
+      load_frags(sA, sB, 0, fa[0], fb[0]);
+      load_frags(sA, sB, 1, fa[1], fb[1]);
+      if constexpr (issue_late) issue_next();
+      mfmas(0);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int kk = 1; kk < BK / 16; ++kk) {
+        if (kk + 1 < BK / 16) load_frags(sA, sB, kk + 1, fa[(kk + 1) & 1], fb[(kk + 1) & 1]);
+        mfmas(kk & 1);
         // keep the two-deep fragment pipeline: nothing moves across substeps
         __builtin_amdgcn_sched_barrier(0);
       }
       if (more) {
         la.commit(smem[cur ^ 1], tid);
         lb.commit(smem[cur ^ 1] + BM * BK, tid);
-        if constexpr (LA >= 2 || LB >= 2) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       }
-      __syncthreads();
-      // (the next item's first fragments are read after the epilogue, so
-      // they are not live across it)
-      if (more && !last_k) load_frags(smem[cur ^ 1], smem[cur ^ 1] + BM * BK, 0, fa[0], fb[0]);
       cur ^= 1;
     }
+    if constexpr (LA >= 2 || LB >= 2) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();  // the last k-tile's stage is free; the next k-tile is in LDS
     // the stage not holding the next item's first k-tile is free: 8 KB of
     // epilogue scratch per wavefront
     if constexpr (GRP) {
@@ -774,15 +793,9 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(int M, int N, int
       tile_epilogue_w96<BM, BN, WM, WN, EPI, TO, SN, SM>(e, acc, em0, en0, esplit, M, N, lane, wm,
                                                          wn, smem[cur ^ 1] + wave * 3200);
     item += gridDim.x;
+    // (the next k-step's barrier orders the scratch reads before the loads
+    // that land in this stage)
     if (item >= nitems) break;
-    __syncthreads();  // scratch reads done before the next k-tile lands there
-#pragma unroll
-    for (int a = 0; a < SN; ++a)
-#pragma unroll
-      for (int b = 0; b < SM; ++b)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) acc[a][b][i] = 0.f;
-    load_frags(smem[cur], smem[cur] + BM * BK, 0, fa[0], fb[0]);
   }
 }
 

@@ -834,15 +834,20 @@ hipError_t run(int M, int N, int K, const bf16_t* A, long lda, const bf16_t* B, 
 // transposed (k-major in memory, the weight-gradient form), all with the
 // same K (a multiple of 64), in one persistent launch over total_tiles
 // 256 x 256 tiles.  d_probs: nprobs device descriptors, item0 ascending from 0.
+// store: out_p = instead of out_p +=.
 inline hipError_t run_grouped_accum_tt(const GemmProblem* d_probs, int nprobs, long total_tiles,
-                                       int K, float scale, hipStream_t s) {
+                                       int K, float scale, bool store, hipStream_t s) {
   if (K % BK || total_tiles <= 0 || nprobs <= 0) return hipErrorInvalidValue;
   EpiArgs e{};
   e.alpha = scale;
   const int nkt = K / BK;
   long grid = total_tiles < persistent_slots() ? total_tiles : persistent_slots();
-  gemm_kernel<256, 256, 2, 4, 3, 3, EPI_ACCUM, float, true><<<(unsigned)grid, 512, 0, s>>>(
-      0, 0, K, nullptr, 0, nullptr, 0, e, (int)total_tiles, 1, nkt, d_probs, nprobs);
+  if (store)
+    gemm_kernel<256, 256, 2, 4, 3, 3, EPI_STORE, float, true><<<(unsigned)grid, 512, 0, s>>>(
+        0, 0, K, nullptr, 0, nullptr, 0, e, (int)total_tiles, 1, nkt, d_probs, nprobs);
+  else
+    gemm_kernel<256, 256, 2, 4, 3, 3, EPI_ACCUM, float, true><<<(unsigned)grid, 512, 0, s>>>(
+        0, 0, K, nullptr, 0, nullptr, 0, e, (int)total_tiles, 1, nkt, d_probs, nprobs);
   return hipGetLastError();
 }
 

@@ -219,6 +219,10 @@ struct gpt2 {
   int B = 0, T = 0;
   bool have_targets = false;
   bool forward_done = false;
+  // gpt2_zero_grad was called and the gradients not yet zeroed: the next
+  // backward writes them instead of adding (when every gradient it produces
+  // is written whole), anything else that uses them zeroes them first
+  bool zero_pending = false;
   int64_t step = 0;
   std::string last_error;
   // kernel timing (gpt2_timing_begin/end)
@@ -633,6 +637,14 @@ std::vector<GemmProblem> wgrad_problems(gpt2* h, long* total_tiles) {
   return v;
 }
 
+// Carries out a deferred gpt2_zero_grad.
+gpt2_status settle_zero(gpt2* h) {
+  if (!h->zero_pending) return GPT2_OK;
+  h->zero_pending = false;
+  TIMED(h, GPT2_SITE_ZERO_GRAD, launch_fill(h->grads, h->lay.P, 0.f, h->stream));
+  return GPT2_OK;
+}
+
 gpt2_status run_backward(gpt2* h, float scale) {
   const gpt2_config& c = h->cfg;
   const int B = h->B, T = h->T;
@@ -647,6 +659,21 @@ gpt2_status run_backward(gpt2* h, float scale) {
   // bf16: every weight gradient in one grouped launch at the end (whole
   // tiles over the B*T contraction), when B*T is a multiple of 64
   const bool grouped = bf && h->wg_n > 0 && M % 64 == 0;
+  // After gpt2_zero_grad, with the grouped weight gradients and the
+  // materialised head every gradient element is written by exactly one of:
+  // the grouped launch and its tail (every matrix, wte whole), the grouped
+  // column sums (every vector), the wpe pass (rows < T; rows T.. zeroed
+  // here) -- so they store instead of adding, and nothing is zeroed first.
+  // The embedding's rows of dwte are added after the lm_head's are stored.
+  const bool store = h->zero_pending && grouped && !h->head_chunk;
+  if (store) {
+    h->zero_pending = false;
+    if (T < c.block_size)
+      HIPTRY(h, launch_fill(G + h->lay.wpe + (long)T * C, (long)(c.block_size - T) * C, 0.f, s));
+  } else {
+    const gpt2_status st = settle_zero(h);
+    if (st != GPT2_OK) return st;
+  }
 
   // lm_head (tied): dz = s dlogits wte ; dwte += s dlogits^T z
   if (h->head_chunk) {
@@ -746,19 +773,20 @@ gpt2_status run_backward(gpt2* h, float scale) {
                                    bf && l > 0 ? dres_slot(h, 2 * (l - 1)) : nullptr, 1,
                                    ln_slot(h, 2 * l), BT, C, s));
   }
-  TIMED(h, GPT2_SITE_EMBED_BWD, launch_embed_bwd(h->idx, h->dres, G + h->lay.wte, G + h->lay.wpe, B, T, C,
-                                                 c.padded_vocab_size, h->emb_scratch, s));
   // LayerNorm parameter and bias gradients from every slot of partial sums
   TIMED(h, GPT2_SITE_BIAS_GRAD, launch_colsum_grouped(h->cs_probs, h->cs_n, h->cs_chunks, M,
-                                                      B * ((T + 127) / 128), s));
+                                                      B * ((T + 127) / 128), store, s));
   if (grouped) {
-    TIMED(h, GPT2_SITE_WGRAD, launch_gemm_grouped_wgrad(h->wg_probs, h->wg_n, h->wg_tiles, M, scale, s));
+    TIMED(h, GPT2_SITE_WGRAD, launch_gemm_grouped_wgrad(h->wg_probs, h->wg_n, h->wg_tiles, M, scale,
+                                                        store, s));
     const GemmProblem& t = h->wg_tail;
     if (t.M > 0)
       TIMED(h, GPT2_SITE_WGRAD_TAIL, launch_gemm_wgrad(at, t.M, t.N, M, t.A, t.lda, true, t.B, t.ldb, true,
                                                        t.out, t.ldo, t.scaled ? t.alpha * scale : t.alpha,
-                                                       h->splitk, SPLITK_PART_ELEMS, s));
+                                                       h->splitk, SPLITK_PART_ELEMS, s, store));
   }
+  TIMED(h, GPT2_SITE_EMBED_BWD, launch_embed_bwd(h->idx, h->dres, G + h->lay.wte, G + h->lay.wpe, B, T, C,
+                                                 c.padded_vocab_size, h->emb_scratch, store, s));
   return GPT2_OK;
 }
 
@@ -850,6 +878,7 @@ gpt2_status gpt2_set_params(gpt2_t* h, const float* src, size_t n, int src_on_de
     HIPTRY(h, launch_transpose_tiles(h->shadow, h->shadow_t, h->ttiles, h->nttiles, h->stream));
   }
   for (float* t : {h->grads, h->m, h->v}) HIPTRY(h, launch_fill(t, (long)n, 0.f, h->stream));
+  h->zero_pending = false;
   h->step = 0;
   if (!src_on_device) HIPTRY(h, hipStreamSynchronize(h->stream));
   return GPT2_OK;
@@ -860,6 +889,10 @@ gpt2_status gpt2_get(gpt2_t* h, int which, float* dst, size_t n, int dst_on_devi
   float* p = state_ptr(h, which);
   if (!p) return fail(h, GPT2_E_ARG, "unknown state id");
   if (n != (size_t)h->lay.P) return fail(h, GPT2_E_ARG, "n != gpt2_num_params");
+  if (which == GPT2_GRADS) {
+    const gpt2_status st = settle_zero(h);
+    if (st != GPT2_OK) return st;
+  }
   HIPTRY(h, hipMemcpyAsync(dst, p, n * 4,
                            dst_on_device ? hipMemcpyDeviceToDevice : hipMemcpyDeviceToHost,
                            h->stream));
@@ -873,6 +906,7 @@ gpt2_status gpt2_set_state(gpt2_t* h, int which, const float* src, size_t n, int
   float* p = state_ptr(h, which);
   if (!p) return fail(h, GPT2_E_ARG, "unknown state id");
   if (n != (size_t)h->lay.P) return fail(h, GPT2_E_ARG, "n != gpt2_num_params");
+  if (which == GPT2_GRADS) h->zero_pending = false;  // overwritten whole
   HIPTRY(h, hipMemcpyAsync(p, src, n * 4,
                            src_on_device ? hipMemcpyDeviceToDevice : hipMemcpyHostToDevice,
                            h->stream));
@@ -1001,7 +1035,7 @@ gpt2_status gpt2_get_loss(gpt2_t* h, float* h_loss) {
 
 gpt2_status gpt2_zero_grad(gpt2_t* h) {
   if (!h) return GPT2_E_ARG;
-  TIMED(h, GPT2_SITE_ZERO_GRAD, launch_fill(h->grads, h->lay.P, 0.f, h->stream));
+  h->zero_pending = true;
   return GPT2_OK;
 }
 
@@ -1018,6 +1052,8 @@ gpt2_status gpt2_adamw_step(gpt2_t* h, float lr, float beta1, float beta2, float
   if (!h) return GPT2_E_ARG;
   if (!(beta1 >= 0.f && beta1 < 1.f && beta2 >= 0.f && beta2 < 1.f && eps >= 0.f))
     return fail(h, GPT2_E_ARG, "need 0 <= beta < 1 and eps >= 0");
+  const gpt2_status st = settle_zero(h);
+  if (st != GPT2_OK) return st;
   h->step += 1;
   const double t = (double)h->step;
   const double bc1 = 1.0 - std::pow((double)beta1, t);

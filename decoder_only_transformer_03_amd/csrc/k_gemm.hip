@@ -162,10 +162,11 @@ int gemm_partial_splits(DType in_t, int M, int N, int K) {
   return exact_splits(in_t, K, s < 1 ? 1 : (int)s);
 }
 
-// out[m*ldo + n] += sum_z part[z][m][n]
+// out[m*ldo + n] += sum_z part[z][m][n]  (store: out = ...)
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ part,
                                                             int splits, long MN, int N,
-                                                            float* __restrict__ out, long ldo) {
+                                                            float* __restrict__ out, long ldo,
+                                                            int store) {
   long i4 = ((long)blockIdx.x * 256 + threadIdx.x) * 4;
   if (i4 >= MN) return;
   float4 a = *reinterpret_cast<const float4*>(part + i4);
@@ -176,13 +177,18 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restr
   long m = i4 / N;
   int n = (int)(i4 - m * N);
   float4* o = reinterpret_cast<float4*>(out + m * ldo + n);
+  if (store) {
+    *o = a;
+    return;
+  }
   float4 c = *o;
   *o = make_float4(c.x + a.x, c.y + a.y, c.z + a.z, c.w + a.w);
 }
 
 hipError_t launch_gemm_wgrad(DType in_t, int M, int N, int K, const void* A, long lda, bool a_t,
                              const void* B, long ldb, bool b_t, float* out, long ldo, float alpha,
-                             float* part, long part_elems, hipStream_t s) {
+                             float* part, long part_elems, hipStream_t s, bool store) {
+  const int acc = store ? EPI_STORE : EPI_ACCUM;
   int S = gemm_partial_splits(in_t, M, N, K);
   while (S > 1 && (long)S * M * N > part_elems) S = exact_splits(in_t, K, S - 1);
   EpiArgs e;
@@ -202,8 +208,7 @@ hipError_t launch_gemm_wgrad(DType in_t, int M, int N, int K, const void* A, lon
       const int nkt = K / 64;
       const int M1 = (int)((rounds * slots) / tn) * 256;
       if (rounds >= 1 && tail > 0 && tail * 10 < slots * 8 && nkt >= 32 && M1 > 0 && M1 < M) {
-        hipError_t r = launch_gemm(in_t, M1, N, K, A, lda, a_t, B, ldb, b_t, EPI_ACCUM, DT_F32, e,
-                                   1, s);
+        hipError_t r = launch_gemm(in_t, M1, N, K, A, lda, a_t, B, ldb, b_t, acc, DT_F32, e, 1, s);
         if (r != hipSuccess) return r;
         const int M2 = M - M1;
         const bf16_t* A2 = reinterpret_cast<const bf16_t*>(A) + (a_t ? (long)M1 : (long)M1 * lda);
@@ -215,7 +220,7 @@ hipError_t launch_gemm_wgrad(DType in_t, int M, int N, int K, const void* A, lon
         EpiArgs e2 = e;
         e2.out = out + (long)M1 * ldo;
         if (S2 == 1)
-          return launch_gemm(in_t, M2, N, K, A2, lda, a_t, B, ldb, b_t, EPI_ACCUM, DT_F32, e2, 1, s);
+          return launch_gemm(in_t, M2, N, K, A2, lda, a_t, B, ldb, b_t, acc, DT_F32, e2, 1, s);
         e2.out = part;
         e2.ldo = N;
         e2.split_stride = (long)M2 * N;
@@ -223,11 +228,11 @@ hipError_t launch_gemm_wgrad(DType in_t, int M, int N, int K, const void* A, lon
         if (r != hipSuccess) return r;
         const long MN2 = (long)M2 * N;
         splitk_reduce_kernel<<<(unsigned)((MN2 / 4 + 255) / 256), 256, 0, s>>>(
-            part, S2, MN2, N, out + (long)M1 * ldo, ldo);
+            part, S2, MN2, N, out + (long)M1 * ldo, ldo, store ? 1 : 0);
         return hipGetLastError();
       }
     }
-    return launch_gemm(in_t, M, N, K, A, lda, a_t, B, ldb, b_t, EPI_ACCUM, DT_F32, e, 1, s);
+    return launch_gemm(in_t, M, N, K, A, lda, a_t, B, ldb, b_t, acc, DT_F32, e, 1, s);
   }
   e.out = part;
   e.ldo = N;
@@ -235,7 +240,8 @@ hipError_t launch_gemm_wgrad(DType in_t, int M, int N, int K, const void* A, lon
   hipError_t r = launch_gemm(in_t, M, N, K, A, lda, a_t, B, ldb, b_t, EPI_PARTIAL, DT_F32, e, S, s);
   if (r != hipSuccess) return r;
   long MN = (long)M * N;
-  splitk_reduce_kernel<<<(unsigned)((MN / 4 + 255) / 256), 256, 0, s>>>(part, S, MN, N, out, ldo);
+  splitk_reduce_kernel<<<(unsigned)((MN / 4 + 255) / 256), 256, 0, s>>>(part, S, MN, N, out, ldo,
+                                                                          store ? 1 : 0);
   return hipGetLastError();
 }
 

@@ -326,12 +326,12 @@ __global__ __launch_bounds__(256) void embed_bwd_fix_kernel(const float* __restr
 // dwpe[t,c] += sum_b dx[b,t,c]   (deterministic: one thread per (t, c))
 __global__ __launch_bounds__(256) void embed_bwd_wpe_kernel(const float* __restrict__ dx,
                                                             float* __restrict__ dwpe, int B, int T,
-                                                            int C) {
+                                                            int C, int store) {
   long i = (long)blockIdx.x * 256 + threadIdx.x;
   if (i >= (long)T * C) return;
   float s = 0.f;
   for (int b = 0; b < B; ++b) s += dx[(long)b * T * C + i];
-  dwpe[i] += s;
+  dwpe[i] = store ? s : dwpe[i] + s;
 }
 
 // ---------------------------------------------------------------------------
@@ -535,7 +535,8 @@ __global__ __launch_bounds__(256) void colsum_kernel(const T* __restrict__ X, lo
 // first chunks), four row phases per column with four accumulators each, in a
 // fixed order.  dst[k][j] += sum over the parts of column k*w + j.
 __global__ __launch_bounds__(256) void colsum_grouped_kernel(const ColsumProblem* __restrict__ probs,
-                                                             int nprobs, long M, int nblk) {
+                                                             int nprobs, long M, int nblk,
+                                                             int store) {
   __shared__ float sh[4][64];
   int lo = 0, hi = nprobs - 1;
   while (lo < hi) {
@@ -567,7 +568,10 @@ __global__ __launch_bounds__(256) void colsum_grouped_kernel(const ColsumProblem
   if (g != 0 || c >= ncols) return;
   const int k = c / P.w, j = c - k * P.w;
   float* d = P.dst[k];
-  if (d) d[j] += (sh[0][cl] + sh[1][cl]) + (sh[2][cl] + sh[3][cl]);
+  if (d) {
+    const float v = (sh[0][cl] + sh[1][cl]) + (sh[2][cl] + sh[3][cl]);
+    d[j] = store ? v : d[j] + v;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -941,7 +945,7 @@ size_t embed_bwd_scratch_bytes(long rows, int C) {
 }
 
 hipError_t launch_embed_bwd(const int32_t* idx, const float* dx, float* dwte, float* dwpe, int B,
-                            int T, int C, int Vp, void* scratch, hipStream_t s) {
+                            int T, int C, int Vp, void* scratch, bool wpe_store, hipStream_t s) {
   const long rows = (long)B * T;
   const long nch = (rows + EMB_CHUNK - 1) / EMB_CHUNK;
   if (C % 4) return hipErrorInvalidValue;
@@ -965,7 +969,7 @@ hipError_t launch_embed_bwd(const int32_t* idx, const float* dx, float* dwte, fl
   embed_bwd_chunk_kernel<<<(unsigned)nch, 256, 0, s>>>(ka, va, dx, dwte, head, tail, hflag, tflag,
                                                        C, rows);
   embed_bwd_fix_kernel<<<(unsigned)nch, 256, 0, s>>>(head, tail, hflag, tflag, dwte, C, (int)nch);
-  embed_bwd_wpe_kernel<<<nblk((long)T * C, 256), 256, 0, s>>>(dx, dwpe, B, T, C);
+  embed_bwd_wpe_kernel<<<nblk((long)T * C, 256), 256, 0, s>>>(dx, dwpe, B, T, C, wpe_store ? 1 : 0);
   return hipGetLastError();
 }
 
@@ -1040,9 +1044,9 @@ hipError_t launch_layernorm_bwd(DType copy_t, const float* dy, const float* x, c
 }
 
 hipError_t launch_colsum_grouped(const ColsumProblem* d_probs, int nprobs, int total_chunks, long M,
-                                 int nblk, hipStream_t s) {
+                                 int nblk, bool store, hipStream_t s) {
   if (nprobs <= 0 || total_chunks <= 0) return hipSuccess;
-  colsum_grouped_kernel<<<total_chunks, 256, 0, s>>>(d_probs, nprobs, M, nblk);
+  colsum_grouped_kernel<<<total_chunks, 256, 0, s>>>(d_probs, nprobs, M, nblk, store ? 1 : 0);
   return hipGetLastError();
 }
 

@@ -28,8 +28,9 @@ struct ColsumProblem {
   int rows_per_part, fixed_parts;
   int chunk0;
 };
+// store: dst = sum instead of dst += sum.
 hipError_t launch_colsum_grouped(const ColsumProblem* d_probs, int nprobs, int total_chunks, long M,
-                                 int nblk, hipStream_t s);
+                                 int nblk, bool store, hipStream_t s);
 // grad-norm: workgroups of the sum-of-squares pass (fp64 partials)
 constexpr int NORM_PARTS = 1024;
 
@@ -55,10 +56,11 @@ hipError_t launch_embed_fwd(const int32_t* idx_in, int32_t* idx_saved, const flo
                             const float* wpe, float* x, int B, int T, int C, int Vp, int* err,
                             hipStream_t s);
 // dwte[idx[r]] += dx[r] over the B*T rows (deterministic; ids in [0, Vp)),
-// dwpe[t] += sum_b dx[b,t]; scratch: embed_bwd_scratch_bytes(B*T, C) bytes.
+// dwpe[t] += sum_b dx[b,t] (wpe_store: dwpe[t] = ..., rows T.. untouched);
+// scratch: embed_bwd_scratch_bytes(B*T, C) bytes.
 size_t embed_bwd_scratch_bytes(long rows, int C);
 hipError_t launch_embed_bwd(const int32_t* idx, const float* dx, float* dwte, float* dwpe, int B,
-                            int T, int C, int Vp, void* scratch, hipStream_t s);
+                            int T, int C, int Vp, void* scratch, bool wpe_store, hipStream_t s);
 hipError_t launch_layernorm_fwd(DType out_t, const float* x, const float* w, const float* b,
                                 void* y, float* mean, float* rstd, long rows, int C,
                                 hipStream_t s);
@@ -116,11 +118,12 @@ hipError_t launch_gemm_fill(DType in_t, int M, int N, int K, const void* A, long
 
 // Weight gradient out[m][n] += alpha * sum_k A(m,k) B(n,k) for a long
 // contraction: split over k into fp32 slices of `part` (part_elems floats of
-// scratch), then summed in fixed order into out (deterministic).
+// scratch), then summed in fixed order into out (deterministic).  store:
+// out = instead of out +=.
 int gemm_slots();  // workgroup slots of the persistent bf16 GEMM grid
 hipError_t launch_gemm_wgrad(DType in_t, int M, int N, int K, const void* A, long lda, bool a_t,
                              const void* B, long ldb, bool b_t, float* out, long ldo, float alpha,
-                             float* part, long part_elems, hipStream_t s);
+                             float* part, long part_elems, hipStream_t s, bool store = false);
 int gemm_partial_splits(DType in_t, int M, int N, int K);
 
 // One product of a grouped weight-gradient launch:
@@ -140,8 +143,9 @@ struct GemmProblem {
 // All products of d_probs (device array, nprobs entries, item0 ascending
 // from 0, total_tiles in all) in one persistent launch; bf16 operands, K a
 // multiple of 64, whole tiles (no k-slices): deterministic.
+// store: out_p = instead of out_p +=.
 hipError_t launch_gemm_grouped_wgrad(const GemmProblem* d_probs, int nprobs, long total_tiles,
-                                     int K, float scale, hipStream_t s);
+                                     int K, float scale, bool store, hipStream_t s);
 constexpr long SPLITK_PART_ELEMS = 256L * 256 * 256;
 
 // Causal self-attention on the fused qkv activation (B*T, 3C), head h of q,

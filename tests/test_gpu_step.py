@@ -486,3 +486,55 @@ def check_bf16_step(d, flat, g, r):
     assert worst_opt < 1e-5
     assert worst_p < 5e-3
     assert frac < 0.05
+
+
+def test_bf16_deferred_zero_grad():
+    """gpt2_zero_grad is deferred: the next bf16 backward (grouped weight
+    gradients, materialised head) writes the gradients instead of adding to
+    them, and everything else zeroes them first.  Each result must be
+    bit-identical to adding onto gradients zeroed explicitly beforehand,
+    including the wpe rows past a shorter T, which must be exactly zero."""
+    d = dict(synthetic.model_dims("tiny"), n_head=2)   # head width 64
+    C, Vp, blk = d["n_embd"], d["padded_vocab_size"], d["block_size"]
+    flat = synthetic.init_params(d, seed=21)
+    cfg = G.make_config(max_batch=2, precision="bf16", **d)
+    m = G.GPT2(cfg, device=DEV)
+    m.set_params(flat)
+    P = flat.size
+    zeros = np.zeros(P, dtype=np.float32)
+    a_idx, a_tgt = synthetic.uniform_batch(2, 64, 512, seed=22)
+    b_idx, b_tgt = synthetic.uniform_batch(2, 32, 512, seed=23)
+
+    def backward_on(idx, tgt, scale=1.0):
+        m.forward(dev_ids(idx), dev_ids(tgt))
+        m.backward(scale)
+
+    # reference: explicit zeros, then one backward that adds
+    backward_on(a_idx, a_tgt)                      # leave non-zero gradients behind
+    m.set_state(G.GPT2_GRADS, zeros)
+    backward_on(b_idx, b_tgt)
+    ref = m.get(G.GPT2_GRADS)
+    # deferred zero: the backward stores
+    backward_on(a_idx, a_tgt)
+    m.zero_grad()
+    backward_on(b_idx, b_tgt)
+    got = m.get(G.GPT2_GRADS)
+    assert np.array_equal(got, ref)
+    wpe = got[Vp * C:(Vp + blk) * C].reshape(blk, C)
+    assert np.all(wpe[32:] == 0) and np.any(wpe[:32] != 0)
+    # a second backward adds onto the stored gradients
+    m.set_state(G.GPT2_GRADS, zeros)
+    backward_on(b_idx, b_tgt, 0.5)
+    backward_on(a_idx, a_tgt, 0.5)
+    ref2 = m.get(G.GPT2_GRADS)
+    m.zero_grad()
+    backward_on(b_idx, b_tgt, 0.5)
+    backward_on(a_idx, a_tgt, 0.5)
+    assert np.array_equal(m.get(G.GPT2_GRADS), ref2)
+    # zero_grad followed by a read, or by an optimizer step, sees zeros
+    m.zero_grad()
+    assert not np.any(m.get(G.GPT2_GRADS))
+    backward_on(a_idx, a_tgt)
+    m.zero_grad()
+    assert m.adamw_step(LR, B1, B2, EPS, WD, CLIP, want_norm=True) == 0.0
+    assert not np.any(m.get(G.GPT2_GRADS))

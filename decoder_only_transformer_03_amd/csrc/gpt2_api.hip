@@ -659,13 +659,14 @@ gpt2_status run_backward(gpt2* h, float scale) {
   // bf16: every weight gradient in one grouped launch at the end (whole
   // tiles over the B*T contraction), when B*T is a multiple of 64
   const bool grouped = bf && h->wg_n > 0 && M % 64 == 0;
-  // After gpt2_zero_grad, with the grouped weight gradients and the
-  // materialised head every gradient element is written by exactly one of:
-  // the grouped launch and its tail (every matrix, wte whole), the grouped
-  // column sums (every vector), the wpe pass (rows < T; rows T.. zeroed
-  // here) -- so they store instead of adding, and nothing is zeroed first.
-  // The embedding's rows of dwte are added after the lm_head's are stored.
-  const bool store = h->zero_pending && grouped && !h->head_chunk;
+  // After gpt2_zero_grad, with the grouped weight gradients every gradient
+  // element is written by exactly one of: the grouped launch and its tail
+  // (every matrix; wte whole with the materialised head), the fused head's
+  // slices (wte whole otherwise), the grouped column sums (every vector),
+  // the wpe pass (rows < T; rows T.. zeroed here) -- so they store instead
+  // of adding, and nothing is zeroed first.  The embedding's rows of dwte
+  // are added after the lm_head's are stored.
+  const bool store = h->zero_pending && grouped;
   if (store) {
     h->zero_pending = false;
     if (T < c.block_size)
@@ -697,7 +698,7 @@ gpt2_status run_backward(gpt2* h, float scale) {
                                                 epi(h->dxtmp, C, scale), 0, s));
       TIMED(h, GPT2_SITE_LMHEAD_DW, launch_gemm_wgrad(at, nc, C, M, h->hslice, nc, true, h->z, C, true,
                                                       G + h->lay.wte + (long)v0 * C, C, scale,
-                                                      h->splitk, SPLITK_PART_ELEMS, s));
+                                                      h->splitk, SPLITK_PART_ELEMS, s, store));
     }
   } else {
     const WOp wl = w_dx(h, h->lay.wte, Vp, C);

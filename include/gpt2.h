@@ -205,7 +205,7 @@ gpt2_status gpt2_get_loss(gpt2_t* h, float* h_loss);
 
 /* Sets every gradient to zero.  Deferred: the next backward then writes the
  * gradients it produces instead of adding them where it writes each one
- * whole (bf16 with B*T a multiple of 64 and the materialised head), and any
+ * whole (bf16 with B*T a multiple of 64), and any
  * other use of the gradients (gpt2_get, gpt2_adamw_step, a backward that
  * adds) zeroes them first; the result is the same. */
 gpt2_status gpt2_zero_grad(gpt2_t* h);

@@ -488,16 +488,18 @@ def check_bf16_step(d, flat, g, r):
     assert frac < 0.05
 
 
-def test_bf16_deferred_zero_grad():
+@pytest.mark.parametrize("hc", [0, 192])
+def test_bf16_deferred_zero_grad(hc):
     """gpt2_zero_grad is deferred: the next bf16 backward (grouped weight
-    gradients, materialised head) writes the gradients instead of adding to
-    them, and everything else zeroes them first.  Each result must be
-    bit-identical to adding onto gradients zeroed explicitly beforehand,
-    including the wpe rows past a shorter T, which must be exactly zero."""
+    gradients; materialised head, or the fused head's slices of dwte) writes
+    the gradients instead of adding to them, and everything else zeroes them
+    first.  Each result must be bit-identical to adding onto gradients zeroed
+    explicitly beforehand, including the wpe rows past a shorter T, which
+    must be exactly zero."""
     d = dict(synthetic.model_dims("tiny"), n_head=2)   # head width 64
     C, Vp, blk = d["n_embd"], d["padded_vocab_size"], d["block_size"]
     flat = synthetic.init_params(d, seed=21)
-    cfg = G.make_config(max_batch=2, precision="bf16", **d)
+    cfg = G.make_config(max_batch=2, precision="bf16", head_chunk=hc, **d)
     m = G.GPT2(cfg, device=DEV)
     m.set_params(flat)
     P = flat.size

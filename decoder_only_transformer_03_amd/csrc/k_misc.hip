@@ -323,7 +323,8 @@ __global__ __launch_bounds__(256) void embed_bwd_fix_kernel(const float* __restr
   }
 }
 
-// dwpe[t,c] += sum_b dx[b,t,c]   (deterministic: one thread per (t, c))
+// dwpe[t,c] += sum_b dx[b,t,c], or = with store   (deterministic: one thread
+// per (t, c))
 __global__ __launch_bounds__(256) void embed_bwd_wpe_kernel(const float* __restrict__ dx,
                                                             float* __restrict__ dwpe, int B, int T,
                                                             int C, int store) {
@@ -336,9 +337,12 @@ __global__ __launch_bounds__(256) void embed_bwd_wpe_kernel(const float* __restr
 
 // ---------------------------------------------------------------------------
 // LayerNorm forward: y = (x - mean) * rstd * w + b, rstd = 1/sqrt(var + 1e-5),
-// biased variance over C.  One wavefront per row, the row kept in registers.
+// biased variance over C.  One wavefront per two rows, both kept in
+// registers: their loads (and the weight and bias loads) are all in flight
+// before the first reduction.
 // ---------------------------------------------------------------------------
 constexpr int LN_MAXV = 8;  // float4 per lane: C <= 2048
+constexpr int LN_FWD_RPW = 2;  // rows per wavefront
 
 template <int NV, typename TO>
 __global__ __launch_bounds__(256) void layernorm_fwd_kernel(const float* __restrict__ x,
@@ -348,51 +352,65 @@ __global__ __launch_bounds__(256) void layernorm_fwd_kernel(const float* __restr
                                                             float* __restrict__ mean_out,
                                                             float* __restrict__ rstd_out,
                                                             long rows, int C) {
-  long row = (long)blockIdx.x * 4 + (threadIdx.x >> 6);
-  int lane = threadIdx.x & 63;
-  if (row >= rows) return;
-  const float* xr = x + row * C;
-  float v[NV][4];
-  float s = 0.f;
+  const long row0 = ((long)blockIdx.x * 4 + (threadIdx.x >> 6)) * LN_FWD_RPW;
+  const int lane = threadIdx.x & 63;
+  if (row0 >= rows) return;
+  float v[LN_FWD_RPW][NV][4], g[NV][4], bb[NV][4];
 #pragma unroll
-  for (int i = 0; i < NV; ++i) {
-    int c = (i * 64 + lane) * 4;
-    if (c < C) {
-      ld4(xr + c, v[i]);
-      s += (v[i][0] + v[i][1]) + (v[i][2] + v[i][3]);
+  for (int r = 0; r < LN_FWD_RPW; ++r) {
+    if (row0 + r >= rows) break;
+    const float* xr = x + (row0 + r) * C;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const int c = (i * 64 + lane) * 4;
+      if (c < C) ld4(xr + c, v[r][i]);
     }
   }
-  float mean = wave_sum(s) / (float)C;
-  float q = 0.f;
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
-    int c = (i * 64 + lane) * 4;
+    const int c = (i * 64 + lane) * 4;
     if (c < C) {
+      ld4(w + c, g[i]);
+      ld4(b + c, bb[i]);
+    }
+  }
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        float d = v[i][j] - mean;
-        q += d * d;
+  for (int r = 0; r < LN_FWD_RPW; ++r) {
+    const long row = row0 + r;
+    if (row >= rows) break;
+    float s = 0.f;
+#pragma unroll
+    for (int i = 0; i < NV; ++i)
+      if ((i * 64 + lane) * 4 < C) s += (v[r][i][0] + v[r][i][1]) + (v[r][i][2] + v[r][i][3]);
+    const float mean = wave_sum(s) / (float)C;
+    float q = 0.f;
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      if ((i * 64 + lane) * 4 < C) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float d = v[r][i][j] - mean;
+          q += d * d;
+        }
       }
     }
-  }
-  float var = wave_sum(q) / (float)C;
-  float rstd = 1.0f / sqrtf(var + 1e-5f);
-  TO* yr = y + row * C;
+    const float var = wave_sum(q) / (float)C;
+    const float rstd = 1.0f / sqrtf(var + 1e-5f);
+    TO* yr = y + row * C;
 #pragma unroll
-  for (int i = 0; i < NV; ++i) {
-    int c = (i * 64 + lane) * 4;
-    if (c < C) {
-      float g[4], bb[4], o[4];
-      ld4(w + c, g);
-      ld4(b + c, bb);
+    for (int i = 0; i < NV; ++i) {
+      const int c = (i * 64 + lane) * 4;
+      if (c < C) {
+        float o[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) o[j] = (v[i][j] - mean) * rstd * g[j] + bb[j];
-      st4(yr + c, o);
+        for (int j = 0; j < 4; ++j) o[j] = (v[r][i][j] - mean) * rstd * g[i][j] + bb[i][j];
+        st4(yr + c, o);
+      }
     }
-  }
-  if (lane == 0) {
-    mean_out[row] = mean;
-    rstd_out[row] = rstd;
+    if (lane == 0) {
+      mean_out[row] = mean;
+      rstd_out[row] = rstd;
+    }
   }
 }
 
@@ -977,11 +995,11 @@ template <int NV>
 static void ln_fwd_nv(DType out_t, const float* x, const float* w, const float* b, void* y,
                       float* mean, float* rstd, long rows, int C, hipStream_t s) {
   if (out_t == DT_BF16)
-    layernorm_fwd_kernel<NV, bf16_t><<<nblk(rows, 4), 256, 0, s>>>(x, w, b, (bf16_t*)y, mean, rstd,
-                                                                   rows, C);
+    layernorm_fwd_kernel<NV, bf16_t><<<nblk(rows, 4 * LN_FWD_RPW), 256, 0, s>>>(
+        x, w, b, (bf16_t*)y, mean, rstd, rows, C);
   else
-    layernorm_fwd_kernel<NV, float><<<nblk(rows, 4), 256, 0, s>>>(x, w, b, (float*)y, mean, rstd,
-                                                                  rows, C);
+    layernorm_fwd_kernel<NV, float><<<nblk(rows, 4 * LN_FWD_RPW), 256, 0, s>>>(
+        x, w, b, (float*)y, mean, rstd, rows, C);
 }
 
 hipError_t launch_layernorm_fwd(DType out_t, const float* x, const float* w, const float* b,

@@ -862,7 +862,7 @@ hipError_t dispatch(int M, int N, int K, const bf16_t* A, long lda, const bf16_t
 // shapes: 256 x 256 x 64 with 8 wavefronts (2 x 4, each 128 x 64), and for
 // outputs whose width is a multiple of 192 -- where it keeps more CUs busy --
 // 256 x 192 x 64 with 8 wavefronts (4 x 2, each 64 x 96; direct loads only,
-// no split-K or column-sum epilogues).
+// no atomic, column-sum or fused-head epilogues).
 #define GEMM_MFMA_DEFINE_DISPATCH(AT, BT)                                                       \
   namespace gemm_mfma {                                                                         \
   template <int BN_, int WM_, int WN_, int LA, int LB>                                         \
@@ -892,9 +892,7 @@ hipError_t dispatch(int M, int N, int K, const bf16_t* A, long lda, const bf16_t
           return run<256, 256, 2, 4, LA, LB, EPI_GELU_BWD, bf16_t>(M, N, K, A, lda, B, ldb, e, 1, s); \
         break;                                                                                  \
       case EPI_PARTIAL:                                                                         \
-        if constexpr (BN_ == 256)                                                               \
-          return run<256, 256, 2, 4, LA, LB, EPI_PARTIAL, float>(M, N, K, A, lda, B, ldb, e, sk, s); \
-        break;                                                                                  \
+        return run<256, BN_, WM_, WN_, LA, LB, EPI_PARTIAL, float>(M, N, K, A, lda, B, ldb, e, sk, s); \
       /* fused lm_head: logits = x wte^T only (neither operand transposed) */                    \
       case EPI_LSE:                                                                             \
         if constexpr (BN_ == 256 && LA % 2 == 0 && LB % 2 == 0)                                 \
@@ -930,7 +928,7 @@ hipError_t dispatch(int M, int N, int K, const bf16_t* A, long lda, const bf16_t
     if (direct) {                                                                               \
       const bool w192 = N % 192 == 0 && !e.colsum &&                                            \
                         (epi == EPI_STORE || epi == EPI_BIAS || epi == EPI_BIAS_GELU ||         \
-                         epi == EPI_RESID || epi == EPI_ACCUM);                                 \
+                         epi == EPI_RESID || epi == EPI_ACCUM || epi == EPI_PARTIAL);           \
       const long tm = (M + 255) / 256;                                                          \
       if (w192 && slot_use(tm * (N / 192)) > slot_use(tm * ((N + 255) / 256)) + 0.02)          \
         return by_epi<192, 4, 2, AT ? 3 : 2, BT ? 3 : 2>(M, N, K, A, lda, B, ldb, epi, out_t, e, split_k, s); \

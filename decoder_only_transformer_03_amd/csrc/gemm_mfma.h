@@ -929,7 +929,8 @@ hipError_t dispatch(int M, int N, int K, const bf16_t* A, long lda, const bf16_t
       const bool w192 = N % 192 == 0 && !e.colsum &&                                            \
                         (epi == EPI_STORE || epi == EPI_BIAS || epi == EPI_BIAS_GELU ||         \
                          epi == EPI_RESID || epi == EPI_ACCUM || epi == EPI_PARTIAL);           \
-      const long tm = (M + 255) / 256;                                                          \
+      /* work items: tiles, times the k-slices of a split-K product */                          \
+      const long tm = (M + 255) / 256 * (epi == EPI_PARTIAL && split_k > 1 ? split_k : 1);      \
       if (w192 && slot_use(tm * (N / 192)) > slot_use(tm * ((N + 255) / 256)) + 0.02)          \
         return by_epi<192, 4, 2, AT ? 3 : 2, BT ? 3 : 2>(M, N, K, A, lda, B, ldb, epi, out_t, e, split_k, s); \
       return by_epi<256, 2, 4, AT ? 3 : 2, BT ? 3 : 2>(M, N, K, A, lda, B, ldb, epi, out_t, e, split_k, s); \

@@ -112,6 +112,94 @@ def decay_mask(cfg: Config, dtype=np.float32) -> np.ndarray:
 
 
 # ----------------------------------------------------------------------------
+# seeded initialisation ("GPT-2 from Scratch", Initialization: 0.02, and the
+# residual scaling), from a counter-based normal stream
+# ----------------------------------------------------------------------------
+
+_U32 = np.uint64(0xFFFFFFFF)
+
+
+def philox4x32_10(counter, key):
+    """Philox4x32 with 10 rounds (Salmon, Moraes, Dror and Shaw, "Parallel
+    random numbers: as easy as 1, 2, 3", SC 2011).  counter: (n, 4) words,
+    key: 2 words (uint32 values).  Per round, words 0 and 2 are multiplied by
+    0xD2511F53 and 0xCD9E8D57 into 64-bit products; the new state is
+    (hi(w2 M1) ^ w1 ^ k0, lo(w2 M1), hi(w0 M0) ^ w3 ^ k1, lo(w0 M0)); then the
+    key advances by the Weyl increments 0x9E3779B9 and 0xBB67AE85 (mod 2^32).
+    Returns (n, 4) uint64 arrays holding the 32-bit output words."""
+    c = np.asarray(counter, dtype=np.uint64).reshape(-1, 4) & _U32
+    k0, k1 = int(key[0]) & 0xFFFFFFFF, int(key[1]) & 0xFFFFFFFF
+    x0, x1, x2, x3 = (c[:, i].copy() for i in range(4))
+    for _ in range(10):
+        p0 = x0 * np.uint64(0xD2511F53)                    # < 2^64: exact in uint64
+        p1 = x2 * np.uint64(0xCD9E8D57)
+        hi0, lo0 = p0 >> np.uint64(32), p0 & _U32
+        hi1, lo1 = p1 >> np.uint64(32), p1 & _U32
+        x0, x1, x2, x3 = hi1 ^ x1 ^ np.uint64(k0), lo1, hi0 ^ x3 ^ np.uint64(k1), lo0
+        k0 = (k0 + 0x9E3779B9) & 0xFFFFFFFF
+        k1 = (k1 + 0xBB67AE85) & 0xFFFFFFFF
+    return np.stack([x0, x1, x2, x3], axis=1)
+
+
+def normal_stream(elems, seed):
+    """Standard normal number e of the stream of `seed`, for each e in
+    `elems` (fp64).  Block b = e // 4 is the Philox counter (b mod 2^32,
+    b // 2^32, 0, 0) under the key (seed mod 2^32, seed // 2^32); each output
+    word x becomes the uniform (floor(x / 2^9) + 1/2) / 2^23 in (0, 1); the
+    pairs (u0, u1) and (u2, u3) go through Box and Muller's transform,
+    r = sqrt(-2 ln u_a), (r cos 2 pi u_b, r sin 2 pi u_b); element 4b + j takes
+    output j of its block."""
+    e = np.asarray(elems, dtype=np.int64).reshape(-1)
+    b = (e // 4).astype(np.uint64)
+    ctr = np.zeros((e.size, 4), dtype=np.uint64)
+    ctr[:, 0] = b & _U32
+    ctr[:, 1] = b >> np.uint64(32)
+    x = philox4x32_10(ctr, (seed & 0xFFFFFFFF, (seed >> 32) & 0xFFFFFFFF))
+    u = ((x >> np.uint64(9)).astype(np.float64) + 0.5) / 2.0 ** 23
+    j = e % 4
+    a = np.where(j < 2, u[:, 0], u[:, 2])                  # radius uniform of the pair
+    t = np.where(j < 2, u[:, 1], u[:, 3])                  # angle uniform of the pair
+    r = np.sqrt(-2.0 * np.log(a))
+    return np.where(j % 2 == 0, r * np.cos(2.0 * np.pi * t), r * np.sin(2.0 * np.pi * t))
+
+
+def init_std(cfg: Config):
+    """Per tensor of param_specs: the standard deviation of its normal init,
+    or None with the constant it starts at.  Weights and embeddings 0.02; the
+    two c_proj weights of a block (the projections back into the residual
+    stream) 0.02 / sqrt(2 n_layer); biases and LayerNorm shifts 0; LayerNorm
+    gains 1."""
+    out = []
+    for name, shape in param_specs(cfg):
+        if len(shape) == 2:
+            resid = name.endswith("c_proj.weight")
+            out.append((0.02 / math.sqrt(2 * cfg.n_layer) if resid else 0.02, None))
+        else:
+            out.append((None, 1.0 if name.endswith("ln_1.weight") or name.endswith("ln_2.weight")
+                        or name == "ln_f.weight" else 0.0))
+    return out
+
+
+def init_params(cfg: Config, seed, elems=None):
+    """The seeded initial parameter vector (fp64), or only its elements at the
+    flat indices `elems`: element e of a normal tensor is std * normal number e
+    of the seed's stream (e counts over the whole canonical vector)."""
+    n = num_params(cfg)
+    idx = np.arange(n) if elems is None else np.asarray(elems, dtype=np.int64)
+    out = np.empty(idx.size)
+    off = 0
+    for (name, shape), (std, const) in zip(param_specs(cfg), init_std(cfg)):
+        cnt = int(np.prod(shape))
+        sel = (idx >= off) & (idx < off + cnt)
+        if std is None:
+            out[sel] = const
+        else:
+            out[sel] = std * normal_stream(idx[sel], seed)
+        off += cnt
+    return out
+
+
+# ----------------------------------------------------------------------------
 # elementwise pieces
 # ----------------------------------------------------------------------------
 
@@ -444,15 +532,23 @@ def generate(flat_params, idx, n_new, temperature, top_k, uniforms, cfg: Config)
     return seq
 
 
-def lr_at(step, max_lr=6e-4, min_lr=6e-5, warmup=100, max_steps=2000):
-    """Linear warmup over `warmup` steps starting at max_lr/warmup, cosine from
-    max_lr at step=warmup down to min_lr at step=max_steps, min_lr after."""
-    if step < warmup:
-        return max_lr * (step + 1) / warmup
-    if step > max_steps:
-        return min_lr
-    progress = (step - warmup) / max(1, max_steps - warmup)
-    return min_lr + 0.5 * (max_lr - min_lr) * (1.0 + math.cos(math.pi * progress))
+def lr_at(t, eta_max, eta_min, t_w, t_max):
+    """Learning rate of optimizer step t (0-based) ("GPT-2 from Scratch",
+    Warmup and cosine decay).  Three phases:
+      ramp    t < t_w:           a straight line from zero, eta_max (t+1)/t_w,
+                                 so the last ramp step reaches eta_max;
+      cosine  t_w <= t <= t_max: eta_min + (eta_max - eta_min) (1 + cos(pi s))/2
+                                 with s = (t - t_w)/(t_max - t_w) going from 0 to 1
+                                 (eta_max at t_w, eta_min at t_max, their mean
+                                 halfway); s = 0 when t_max = t_w;
+      floor   t > t_max:         eta_min."""
+    if t < t_w:
+        return eta_max * (t + 1) / t_w
+    if t <= t_max:
+        span = t_max - t_w
+        s = (t - t_w) / span if span > 0 else 0.0
+        return eta_min + (eta_max - eta_min) * (1.0 + math.cos(math.pi * s)) / 2.0
+    return eta_min
 
 
 def train_step(params, m, v, t, micro_batches, cfg, lr, beta1=0.9, beta2=0.95, eps=1e-8,

@@ -493,3 +493,67 @@ def test_generate_crops_to_the_last_block():
     g = O.generate(flat, prompt[:, :10], 2, 1.0, 1, uni, cfg)
     assert g[0, 10] == O.last_logits(flat, prompt[:1, :10], cfg)[0].argmax()
     assert np.array_equal(O.generate(flat, prompt[:, :10], 0, 1.0, None, uni, cfg), prompt[:, :10])
+
+
+# --------------------------------------------------------------------------
+# seeded initialisation: the counter-based normal stream and the init recipe
+# --------------------------------------------------------------------------
+
+# Known-answer vectors of Philox4x32 with 10 rounds, as published with the
+# generator (Salmon, Moraes, Dror, Shaw, SC 2011; the Random123 library's
+# known-answer tests): (counter, key) -> output words.
+PHILOX_KAT = [
+    ((0x00000000, 0x00000000, 0x00000000, 0x00000000), (0x00000000, 0x00000000),
+     (0x6627e8d5, 0xe169c58d, 0xbc57ac4c, 0x9b00dbd8)),
+    ((0xffffffff, 0xffffffff, 0xffffffff, 0xffffffff), (0xffffffff, 0xffffffff),
+     (0x408f276d, 0x41c83b0e, 0xa20bc7c6, 0x6d5451fd)),
+    ((0x243f6a88, 0x85a308d3, 0x13198a2e, 0x03707344), (0xa4093822, 0x299f31d0),
+     (0xd16cfe09, 0x94fdcceb, 0x5001e420, 0x24126ea1)),
+]
+
+
+def test_philox_known_answers():
+    for ctr, key, want in PHILOX_KAT:
+        got = O.philox4x32_10(np.array([ctr], dtype=np.uint64), key)[0]
+        assert [int(x) for x in got] == list(want)
+
+
+def test_normal_stream_is_standard_normal():
+    """2^20 draws: mean, variance and the Kolmogorov-Smirnov distance against
+    the normal CDF; each pair of a block shares one radius (Box-Muller's
+    z_a^2 + z_b^2 = -2 ln u_a) and the two halves of a block are independent."""
+    from scipy import stats
+    n = 1 << 20
+    z = O.normal_stream(np.arange(n), seed=1234)
+    assert abs(z.mean()) < 5 / math.sqrt(n)
+    assert abs(z.var() - 1.0) < 5 * math.sqrt(2.0 / n)
+    assert stats.kstest(z, "norm").pvalue > 1e-3
+    r2 = (z[0::4] ** 2 + z[1::4] ** 2)
+    assert stats.kstest(r2, "expon", args=(0, 2)).pvalue > 1e-3     # chi-square with 2 dof
+    assert abs(np.corrcoef(z[0::4], z[2::4])[0, 1]) < 5 / math.sqrt(n / 4)
+    # counter-based: any subset of indices gives the same numbers
+    sub = np.array([0, 3, 4, 99999, n - 1])
+    assert np.array_equal(O.normal_stream(sub, seed=1234), z[sub])
+    assert not np.allclose(O.normal_stream(sub, seed=1235), z[sub])
+
+
+def test_seeded_init_follows_the_recipe():
+    """"GPT-2 from Scratch", Initialization: weights N(0, 0.02), both c_proj
+    weights N(0, 0.02/sqrt(2L)), biases 0, LayerNorm gains 1 and shifts 0."""
+    cfg, d = cfg_of("tiny")
+    p = O.init_params(cfg, seed=42)
+    assert p.size == O.num_params(cfg)
+    P = O.unflatten(p, cfg)
+    L = cfg.n_layer
+    for name, x in P.items():
+        if x.ndim == 2:
+            std = 0.02 / math.sqrt(2 * L) if name.endswith("c_proj.weight") else 0.02
+            n = x.size
+            assert abs(x.std() - std) < 6 * std / math.sqrt(2 * n), name
+            assert abs(x.mean()) < 6 * std / math.sqrt(n), name
+        elif name.endswith(("ln_1.weight", "ln_2.weight")) or name == "ln_f.weight":
+            assert np.all(x == 1.0), name
+        else:
+            assert np.all(x == 0.0), name
+    sub = np.array([0, 5, 1000, p.size - 1, O.num_params(cfg) // 2])
+    assert np.array_equal(O.init_params(cfg, seed=42, elems=sub), p[sub])

@@ -200,7 +200,7 @@ def main():
         for di, dt in dev:
             model.forward(di, dt)
             model.backward(1.0 / len(dev))
-        lr = wl["lr"] if wl["lr"] is not None else G.lr_schedule(opt_step[0])
+        lr = wl["lr"] if wl["lr"] is not None else G.gpt2_lr_at(opt_step[0])
         model.adamw_step(lr, 0.9, 0.95, 1e-8, wl["wd"], 1.0)
         opt_step[0] += 1
 

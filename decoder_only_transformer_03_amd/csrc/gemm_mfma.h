@@ -408,7 +408,9 @@ __device__ __forceinline__ void tile_epilogue(const EpiArgs& e, const f32x16_t (
 #pragma unroll
         for (int j = 0; j < 8; ++j) csum[j] += __shfl_xor(csum[j], o, 64);
       static_assert(WTM == 128, "column sums are kept per 128-row block");
-      if (lane < 8 && ncol) {
+      // a sub-tile wholly past the last row has no block of its own: its
+      // index ceil(M/128) is one past the rows the slot holds for M rows
+      if (lane < 8 && ncol && mw < M) {
         float* dst = e.colsum + (mw / 128) * (long)N + nl;
         st4(dst, csum);
         st4(dst + 4, csum + 4);

@@ -33,10 +33,17 @@ struct Layout {
   long P = 0;
   long wte = 0, wpe = 0, lnfw = 0, lnfb = 0;
   std::vector<LayerOff> layer;
-  // (offset, length, decay) of every tensor in canonical order
+  // (offset, length, decay, init) of every tensor in canonical order
   std::vector<long> t_off, t_len;
   std::vector<int> t_decay;
+  std::vector<int> t_init;
 };
+
+// How a tensor starts ("GPT-2 from Scratch", Initialization: 0.02, and the
+// residual scaling): weights and embeddings N(0, 0.02); the two c_proj
+// weights of a block N(0, 0.02 / sqrt(2 n_layer)); biases and LayerNorm
+// shifts 0; LayerNorm gains 1.
+enum { INIT_ZERO = 0, INIT_ONE = 1, INIT_NORMAL = 2, INIT_NORMAL_RESID = 3 };
 
 bool valid_config(const gpt2_config* c, std::string* why) {
   auto fail = [&](const char* m) {
@@ -68,34 +75,36 @@ bool valid_config(const gpt2_config* c, std::string* why) {
 Layout make_layout(const gpt2_config* c) {
   Layout L;
   const long C = c->n_embd, Vp = c->padded_vocab_size;
-  auto add = [&](long n, int decay) {
+  // matrices and embeddings (dim 2) are decayed, vectors are not
+  auto add = [&](long n, int init) {
     long o = L.P;
     L.t_off.push_back(o);
     L.t_len.push_back(n);
-    L.t_decay.push_back(decay);
+    L.t_decay.push_back(init >= INIT_NORMAL ? 1 : 0);
+    L.t_init.push_back(init);
     L.P += n;
     return o;
   };
-  L.wte = add(Vp * C, 1);
-  L.wpe = add((long)c->block_size * C, 1);
+  L.wte = add(Vp * C, INIT_NORMAL);
+  L.wpe = add((long)c->block_size * C, INIT_NORMAL);
   for (int l = 0; l < c->n_layer; ++l) {
     LayerOff o;
-    o.ln1w = add(C, 0);
-    o.ln1b = add(C, 0);
-    o.attnw = add(3 * C * C, 1);
-    o.attnb = add(3 * C, 0);
-    o.projw = add(C * C, 1);
-    o.projb = add(C, 0);
-    o.ln2w = add(C, 0);
-    o.ln2b = add(C, 0);
-    o.fcw = add(4 * C * C, 1);
-    o.fcb = add(4 * C, 0);
-    o.fc2w = add(4 * C * C, 1);
-    o.fc2b = add(C, 0);
+    o.ln1w = add(C, INIT_ONE);
+    o.ln1b = add(C, INIT_ZERO);
+    o.attnw = add(3 * C * C, INIT_NORMAL);
+    o.attnb = add(3 * C, INIT_ZERO);
+    o.projw = add(C * C, INIT_NORMAL_RESID);
+    o.projb = add(C, INIT_ZERO);
+    o.ln2w = add(C, INIT_ONE);
+    o.ln2b = add(C, INIT_ZERO);
+    o.fcw = add(4 * C * C, INIT_NORMAL);
+    o.fcb = add(4 * C, INIT_ZERO);
+    o.fc2w = add(4 * C * C, INIT_NORMAL_RESID);
+    o.fc2b = add(C, INIT_ZERO);
     L.layer.push_back(o);
   }
-  L.lnfw = add(C, 0);
-  L.lnfb = add(C, 0);
+  L.lnfw = add(C, INIT_ONE);
+  L.lnfb = add(C, INIT_ZERO);
   return L;
 }
 
@@ -791,6 +800,36 @@ gpt2_status run_backward(gpt2* h, float scale) {
   return GPT2_OK;
 }
 
+// The seeded initialisation of every tensor (Layout::t_init), then the bf16
+// weight copies the products read.
+hipError_t init_params(gpt2* h, uint64_t seed) {
+  const Layout& L = h->lay;
+  const float std_w = 0.02f;
+  const float std_r = (float)(0.02 / std::sqrt(2.0 * h->cfg.n_layer));
+  for (size_t t = 0; t < L.t_off.size(); ++t) {
+    float* p = h->params + L.t_off[t];
+    hipError_t e = hipSuccess;
+    switch (L.t_init[t]) {
+      case INIT_ZERO: e = launch_fill(p, L.t_len[t], 0.f, h->stream); break;
+      case INIT_ONE: e = launch_fill(p, L.t_len[t], 1.f, h->stream); break;
+      case INIT_NORMAL:
+        e = launch_init_normal(p, L.t_len[t], L.t_off[t], std_w, seed, h->stream);
+        break;
+      default:
+        e = launch_init_normal(p, L.t_len[t], L.t_off[t], std_r, seed, h->stream);
+        break;
+    }
+    if (e != hipSuccess) return e;
+  }
+  if (h->shadow) {
+    hipError_t e = launch_f32_to_bf16(h->params, h->shadow, L.P, h->stream);
+    if (e == hipSuccess)
+      e = launch_transpose_tiles(h->shadow, h->shadow_t, h->ttiles, h->nttiles, h->stream);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
 float* state_ptr(gpt2* h, int which) {
   switch (which) {
     case GPT2_PARAMS: return h->params;
@@ -820,7 +859,7 @@ gpt2_status gpt2_workspace_bytes(const gpt2_config* cfg, size_t* bytes) {
 }
 
 gpt2_status gpt2_init(const gpt2_config* cfg, void* d_workspace, size_t ws_bytes,
-                      void* hip_stream, gpt2_t** out) {
+                      void* hip_stream, uint64_t seed, gpt2_t** out) {
   if (!out) return GPT2_E_ARG;
   *out = nullptr;
   if (!valid_config(cfg, nullptr) || !d_workspace) return GPT2_E_ARG;
@@ -854,10 +893,9 @@ gpt2_status gpt2_init(const gpt2_config* cfg, void* d_workspace, size_t ws_bytes
   if (e == hipSuccess)
     e = hipMemcpyAsync(h->cs_probs, cs.data(), cs.size() * sizeof(ColsumProblem),
                        hipMemcpyHostToDevice, h->stream);
-  for (float* t : {h->params, h->grads, h->m, h->v})
+  for (float* t : {h->grads, h->m, h->v})
     if (e == hipSuccess) e = launch_fill(t, h->lay.P, 0.f, h->stream);
-  if (e == hipSuccess && h->shadow) e = hipMemsetAsync(h->shadow, 0, h->lay.P * 2, h->stream);
-  if (e == hipSuccess && h->shadow_t) e = hipMemsetAsync(h->shadow_t, 0, h->lay.P * 2, h->stream);
+  if (e == hipSuccess) e = init_params(h, seed);
   if (e == hipSuccess) e = hipMemsetAsync(h->err, 0, sizeof(int), h->stream);
   if (e == hipSuccess) e = hipStreamSynchronize(h->stream);
   if (e != hipSuccess) {
@@ -934,6 +972,25 @@ gpt2_status gpt2_wgrad_layout(const gpt2_t* h, int64_t* grouped_elems, int64_t* 
 gpt2_status gpt2_set_step(gpt2_t* h, int64_t t) {
   if (!h || t < 0) return GPT2_E_ARG;
   h->step = t;
+  return GPT2_OK;
+}
+
+gpt2_status gpt2_lr_at(int64_t step, double eta_max, double eta_min, int64_t warmup_steps,
+                       int64_t max_steps, double* lr) {
+  if (!lr || step < 0 || warmup_steps < 1 || max_steps < warmup_steps) return GPT2_E_ARG;
+  // which phase the step is in, and how far through it
+  double v;
+  if (step >= warmup_steps && step <= max_steps) {
+    const double span = (double)(max_steps - warmup_steps);
+    const double frac = span > 0 ? (double)(step - warmup_steps) / span : 0.0;
+    const double half_cos = 0.5 * (1.0 + std::cos(M_PI * frac));  // 1 at the start, 0 at the end
+    v = eta_min + (eta_max - eta_min) * half_cos;
+  } else if (step > max_steps) {
+    v = eta_min;
+  } else {
+    v = eta_max * (double)(step + 1) / (double)warmup_steps;
+  }
+  *lr = v;
   return GPT2_OK;
 }
 

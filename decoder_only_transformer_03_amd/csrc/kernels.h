@@ -97,6 +97,9 @@ hipError_t launch_adamw(const AdamChunk* chunks, int nchunks, float* p, const fl
                         float* v, bf16_t* shadow, const float* clip, float lr, float b1, float b2,
                         float eps, float wd, float step_size, float inv_sqrt_bc2, hipStream_t s);
 hipError_t launch_fill(float* p, long n, float val, hipStream_t s);
+// p[i] = std * (standard normal number e0 + i of the stream of `seed`), for
+// 0 <= i < n (Philox4x32-10 counters, Box-Muller; k_init.hip).
+hipError_t launch_init_normal(float* p, long n, long e0, float std, uint64_t seed, hipStream_t s);
 hipError_t launch_f32_to_bf16(const float* src, bf16_t* dst, long n, hipStream_t s);
 hipError_t launch_bf16_to_f32(const bf16_t* src, float* dst, long n, hipStream_t s);
 

@@ -8,7 +8,6 @@ loading fails loudly otherwise -- there is no fallback.
 from __future__ import annotations
 
 import ctypes as ct
-import math
 import os
 
 import numpy as np
@@ -60,7 +59,8 @@ def lib():
         sig = {
             "gpt2_num_params": (sz, [cfgp]),
             "gpt2_workspace_bytes": (i32, [cfgp, ct.POINTER(sz)]),
-            "gpt2_init": (i32, [cfgp, vp, sz, vp, ct.POINTER(vp)]),
+            "gpt2_init": (i32, [cfgp, vp, sz, vp, ct.c_uint64, ct.POINTER(vp)]),
+            "gpt2_lr_at": (i32, [i64, ct.c_double, ct.c_double, i64, i64, ct.POINTER(ct.c_double)]),
             "gpt2_set_params": (i32, [vp, vp, sz, i32]),
             "gpt2_get": (i32, [vp, i32, vp, sz, i32]),
             "gpt2_set_state": (i32, [vp, i32, vp, sz, i32]),
@@ -96,7 +96,8 @@ def lib():
     return _lib
 
 
-EXPORTED = ["gpt2_num_params", "gpt2_workspace_bytes", "gpt2_init", "gpt2_set_params", "gpt2_get",
+EXPORTED = ["gpt2_num_params", "gpt2_workspace_bytes", "gpt2_init", "gpt2_lr_at", "gpt2_set_params",
+            "gpt2_get",
             "gpt2_set_state", "gpt2_get_step", "gpt2_set_step", "gpt2_forward", "gpt2_eval",
             "gpt2_forward_last", "gpt2_sample", "gpt2_generate", "gpt2_get_loss",
             "gpt2_zero_grad", "gpt2_backward", "gpt2_adamw_step", "gpt2_get_grad_norm",
@@ -143,7 +144,8 @@ class GPT2:
 
     Methods map one to one onto the C functions of the same names."""
 
-    def __init__(self, cfg: gpt2_config, device="cuda", stream=None):
+    def __init__(self, cfg: gpt2_config, device="cuda", stream=None, seed=0):
+        """seed: the parameters start from gpt2_init's seeded initialisation."""
         import torch
         self.torch = torch
         self.cfg = cfg
@@ -156,7 +158,7 @@ class GPT2:
         self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=self.device)
         h = ct.c_void_p()
         st = lib().gpt2_init(ct.byref(cfg), self.workspace.data_ptr(), nbytes,
-                             self.stream.cuda_stream, ct.byref(h))
+                             self.stream.cuda_stream, int(seed), ct.byref(h))
         if st != GPT2_OK:
             raise GPT2Error(st, "gpt2_init failed")
         self.h = h
@@ -297,17 +299,13 @@ class GPT2:
         return out
 
 
-def lr_schedule(step, max_lr=6e-4, min_lr=6e-5, warmup_steps=715, max_steps=19073):
-    """Learning rate of optimizer step `step` (0-based), as the host sets it
-    before each gpt2_adamw_step ("GPT-2 from Scratch", learning-rate schedule
-    section): a linear ramp (step+1)/warmup_steps * max_lr, then a half cosine
-    from max_lr at warmup_steps down to min_lr at max_steps, and min_lr after."""
-    if step < warmup_steps:
-        return max_lr * (step + 1) / warmup_steps
-    if step > max_steps:
-        return min_lr
-    frac = (step - warmup_steps) / max(1, max_steps - warmup_steps)
-    return min_lr + (max_lr - min_lr) * 0.5 * (1.0 + math.cos(math.pi * frac))
+def gpt2_lr_at(step, eta_max=6e-4, eta_min=6e-5, warmup_steps=715, max_steps=19073):
+    """Learning rate of optimizer step `step` (0-based) from the library's
+    schedule (linear warmup, then cosine decay to eta_min at max_steps)."""
+    lr = ct.c_double(0.0)
+    _st(lib().gpt2_lr_at(int(step), float(eta_max), float(eta_min), int(warmup_steps),
+                         int(max_steps), ct.byref(lr)), "gpt2_lr_at")
+    return lr.value
 
 
 def _st(st, what):

@@ -114,10 +114,22 @@ size_t gpt2_num_params(const gpt2_config* cfg);
 gpt2_status gpt2_workspace_bytes(const gpt2_config* cfg, size_t* bytes);
 
 /* Creates a handle over a caller-owned device workspace (256-byte aligned,
- * at least gpt2_workspace_bytes).  Parameters start at zero; call
- * gpt2_set_params before training.  hip_stream: the hipStream_t to use. */
+ * at least gpt2_workspace_bytes) and initialises the parameters on the device
+ * from `seed` ("GPT-2 from Scratch", Initialization: 0.02, and the residual
+ * scaling): every weight matrix and both embeddings N(0, 0.02), the two
+ * c_proj weights of each block N(0, 0.02 / sqrt(2 n_layer)), biases and
+ * LayerNorm shifts 0, LayerNorm gains 1.  The normal numbers are a stream
+ * fixed by the seed alone: element e of the canonical vector (see
+ * gpt2_num_params) takes number e, produced by the counter-based generator
+ * Philox4x32-10 (Salmon et al., SC 2011) on counter (e/4 mod 2^32, e/4 / 2^32,
+ * 0, 0) and key (seed mod 2^32, seed / 2^32), its four words turned into
+ * uniforms (floor(x / 2^9) + 1/2) / 2^23 and two Box-Muller pairs (element
+ * 4b + j takes pair j/2's cosine (j even) or sine (j odd) branch).  Gradients
+ * and AdamW moments start at zero, the step count at 0.  gpt2_set_params
+ * replaces the parameters.  hip_stream: the hipStream_t to use.  On any
+ * failure *out is NULL; nothing is left allocated. */
 gpt2_status gpt2_init(const gpt2_config* cfg, void* d_workspace, size_t ws_bytes,
-                      void* hip_stream, gpt2_t** out);
+                      void* hip_stream, uint64_t seed, gpt2_t** out);
 
 /* Loads all parameters (fp32, canonical order, n == gpt2_num_params) from
  * host (src_on_device = 0) or device memory, refreshes the bf16 weight copy,
@@ -137,6 +149,19 @@ gpt2_status gpt2_set_state(gpt2_t* h, int which, const float* src, size_t n, int
 /* AdamW step counter t (number of gpt2_adamw_step calls since set_params). */
 gpt2_status gpt2_get_step(const gpt2_t* h, int64_t* t);
 gpt2_status gpt2_set_step(gpt2_t* h, int64_t t);
+
+/* Learning rate of optimizer step `step` (0-based), for the caller to pass
+ * to gpt2_adamw_step ("GPT-2 from Scratch", Warmup and cosine decay; the
+ * pretraining recipe of "Pretraining and fine-tuning nanoGPT-124M" uses
+ * eta_max 6e-4, eta_min 6e-5, 715 warmup steps): a linear ramp
+ * eta_max (step + 1) / warmup_steps while step < warmup_steps; then
+ * eta_min + (eta_max - eta_min) (1 + cos(pi s)) / 2 with
+ * s = (step - warmup_steps) / (max_steps - warmup_steps) (s = 0 when the two
+ * are equal) up to step == max_steps; eta_min after.  Host arithmetic in
+ * double, nothing is enqueued.  GPT2_E_ARG if lr is NULL, step < 0,
+ * warmup_steps < 1 or max_steps < warmup_steps. */
+gpt2_status gpt2_lr_at(int64_t step, double eta_max, double eta_min, int64_t warmup_steps,
+                       int64_t max_steps, double* lr);
 
 /* Forward pass over a batch: d_idx, d_targets are device int32 arrays of B*T
  * ids, row-major (B, T); targets[b][t] is the id that should follow

@@ -90,3 +90,26 @@ def test_fused_head_config():
     one = G.gpt2_workspace_bytes(G.make_config(max_batch=16, precision="bf16", head_chunk=65536, **d))
     two = G.gpt2_workspace_bytes(G.make_config(max_batch=16, precision="bf16", head_chunk=Vp, **d))
     assert one == two
+
+
+def test_lr_schedule_matches_oracle():
+    """gpt2_lr_at (host arithmetic in the library) against the oracle's
+    schedule ("GPT-2 from Scratch", Warmup and cosine decay) at the first
+    step, the last warmup step, the peak, the midpoint, the end and past it,
+    for the pretraining recipe (715 warmup steps of 19,073, 6e-4 -> 6e-5) and
+    the chapter's default horizon; and its argument checks."""
+    for eta_max, eta_min, tw, tmax in ((6e-4, 6e-5, 715, 19073), (6e-4, 6e-5, 100, 2000),
+                                       (1e-3, 0.0, 1, 1), (3e-4, 3e-5, 2, 5)):
+        mid = (tw + tmax) // 2
+        for t in sorted({0, 1, tw - 1, tw, tw + 1, mid, tmax - 1, tmax, tmax + 1, tmax + 1000}):
+            if t < 0:
+                continue
+            got = G.gpt2_lr_at(t, eta_max, eta_min, tw, tmax)
+            want = oracle.lr_at(t, eta_max, eta_min, tw, tmax)
+            assert abs(got - want) <= 1e-15 + 1e-12 * abs(want), (t, got, want)
+    # the section's fixed points
+    assert G.gpt2_lr_at(715, 6e-4, 6e-5, 715, 19073) == pytest.approx(6e-4, rel=1e-15)
+    assert G.gpt2_lr_at(19073, 6e-4, 6e-5, 715, 19073) == pytest.approx(6e-5, rel=1e-12)
+    for bad in ((-1, 6e-4, 6e-5, 10, 20), (0, 6e-4, 6e-5, 0, 20), (0, 6e-4, 6e-5, 30, 20)):
+        with pytest.raises(G.GPT2Error):
+            G.gpt2_lr_at(*bad)

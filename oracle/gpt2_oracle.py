@@ -42,6 +42,13 @@ in the design notes):
       cumulative probability exceeds u (if rounding leaves none, the last
       entry with non-zero probability).  The context is cropped to its last
       block_size tokens before every forward pass.
+  R8  bf16 placement ("Let's reproduce GPT-2 (124M)", the bf16 autocast step:
+      products in bf16, weights, LayerNorm and the loss in fp32): with
+      rnd=bf16_round, forward/backward round every product operand, weights
+      included, and the activations and gradients a mixed-precision step
+      stores in bf16; accumulation, LayerNorm, softmax, the residual stream
+      and parameter gradients stay fp32.  This only models the rounding
+      noise of such a step; the reference is the exact computation.
 The backward pass is the chain rule of the forward pass; it is pinned by
 central differences and by torch autograd in the CPU tests.
 """
@@ -246,13 +253,37 @@ def softmax_rows(s):
 
 
 # ----------------------------------------------------------------------------
+# rounding of operands: exact (the reference), or bf16 where the bf16
+# placement reading puts it (used only to size the rounding noise a bf16
+# computation carries)
+# ----------------------------------------------------------------------------
+
+def exact(x):
+    """No rounding: the reference computation."""
+    return x
+
+
+def bf16_round(x):
+    """fp32 -> bf16 -> fp32, round to nearest, ties to even, NaN kept NaN:
+    the conversion autocast applies to matrix-product operands ("Let's
+    reproduce GPT-2 (124M)", the bf16 autocast step)."""
+    x = np.asarray(x, dtype=np.float32)
+    u = x.view(np.uint32).astype(np.uint64)
+    keep_lsb = (u >> np.uint64(16)) & np.uint64(1)
+    r = ((u + np.uint64(0x7FFF) + keep_lsb) >> np.uint64(16)) << np.uint64(16)
+    out = r.astype(np.uint32).view(np.float32)
+    return np.where(np.isnan(x), x, out)
+
+
+# ----------------------------------------------------------------------------
 # causal self-attention ("CausalSelfAttention")
 # ----------------------------------------------------------------------------
 
-def causal_attention_fwd(q, k, v):
+def causal_attention_fwd(q, k, v, rnd=exact):
     """q, k, v: (B, H, T, hd).  S = q k^T / sqrt(hd), entries j > i set to
     -inf, P = row softmax, O = P v.  Also returns the row log-sum-exp of the
-    masked, scaled scores so that the backward pass can rebuild P."""
+    masked, scaled scores so that the backward pass can rebuild P.  rnd
+    rounds the probabilities as the operand of the product with v."""
     B, H, T, hd = q.shape
     scale = 1.0 / math.sqrt(hd)
     mask = np.triu(np.ones((T, T), dtype=bool), k=1)
@@ -264,7 +295,7 @@ def causal_attention_fwd(q, k, v):
         m = s.max(axis=-1, keepdims=True)
         e = np.exp(s - m)
         z = e.sum(axis=-1, keepdims=True)
-        O[b] = np.matmul(e / z, v[b])
+        O[b] = np.matmul(rnd(e), v[b]) / z
         lse[b] = (m + np.log(z))[..., 0]
     return O, lse
 
@@ -278,10 +309,13 @@ def attention_probs(q, k):
     return softmax_rows(s)
 
 
-def causal_attention_bwd(dO, q, k, v, lse):
+def causal_attention_bwd(dO, q, k, v, lse, rnd=exact, O=None):
     """Gradients of O = softmax(mask(q k^T/sqrt(hd))) v with P rebuilt from
     the saved log-sum-exp: dV = P^T dO, dP = dO V^T, dS = P (dP - rowsum(dP P)),
-    dQ = dS K / sqrt(hd), dK = dS^T Q / sqrt(hd)."""
+    dQ = dS K / sqrt(hd), dK = dS^T Q / sqrt(hd).  rnd rounds P and dS as
+    product operands.  Given the (stored) output O, the row term is formed as
+    rowsum(dO O) instead, the same number in exact arithmetic
+    (rowsum(dP P) = dO . (P V))."""
     B, H, T, hd = q.shape
     scale = q.dtype.type(1.0 / math.sqrt(hd))
     mask = np.triu(np.ones((T, T), dtype=bool), k=1)
@@ -290,10 +324,13 @@ def causal_attention_bwd(dO, q, k, v, lse):
         s = np.matmul(q[b], np.swapaxes(k[b], -1, -2)) * scale
         s[:, mask] = -np.inf
         P = np.exp(s - lse[b][..., None])
-        dv[b] = np.matmul(np.swapaxes(P, -1, -2), dO[b])
+        dv[b] = np.matmul(np.swapaxes(rnd(P), -1, -2), dO[b])
         dP = np.matmul(dO[b], np.swapaxes(v[b], -1, -2))
-        D = (dP * P).sum(axis=-1, keepdims=True)
-        dS = P * (dP - D)
+        if O is None:
+            D = (dP * P).sum(axis=-1, keepdims=True)
+        else:
+            D = (dO[b] * O[b]).sum(axis=-1, keepdims=True)
+        dS = rnd(P * (dP - D))
         dq[b] = np.matmul(dS, k[b]) * scale
         dk[b] = np.matmul(np.swapaxes(dS, -1, -2), q[b]) * scale
     return dq, dk, dv
@@ -330,47 +367,58 @@ def cross_entropy(logits, targets):
 # the model ("The full model", "The Block: pre-LN and residuals")
 # ----------------------------------------------------------------------------
 
-def forward(flat_params, idx, targets, cfg: Config, keep_logits=False):
+def forward(flat_params, idx, targets, cfg: Config, keep_logits=False, rnd=exact):
     """Returns (loss, cache).  idx and targets are (B, T) integer arrays;
-    targets may be None (then loss is None and logits are kept)."""
+    targets may be None (then loss is None and logits are kept).
+
+    rnd (default: exact) is applied to every matrix-product operand and to
+    the activations a mixed-precision step keeps in bf16 (LayerNorm outputs,
+    qkv, attention output, GELU output and derivative, logits and their
+    gradient, the gradients flowing into products); bf16_round gives the bf16
+    placement of reading R8 -- a model of that computation's rounding noise,
+    not a reference.  The backward pass applies the same rnd."""
     P = unflatten(flat_params, cfg)
+    r = rnd
     dt = flat_params.dtype
     B, T = idx.shape
     assert T <= cfg.block_size
     C, H = cfg.n_embd, cfg.n_head
     hd = C // H
     x = P["wte"][idx] + P["wpe"][np.arange(T)]
-    cache = {"idx": idx, "targets": targets, "layers": [], "B": B, "T": T}
+    cache = {"idx": idx, "targets": targets, "layers": [], "B": B, "T": T, "rnd": rnd}
     for l in range(cfg.n_layer):
         p = f"h.{l}."
         lc = {"x_in": x}
         u, lc["xhat1"], lc["rstd1"] = layernorm_fwd(x, P[p + "ln_1.weight"], P[p + "ln_1.bias"])
+        u = r(u)
         lc["u1"] = u
-        qkv = u @ P[p + "attn.c_attn.weight"].T + P[p + "attn.c_attn.bias"]
+        qkv = r(u @ r(P[p + "attn.c_attn.weight"]).T + P[p + "attn.c_attn.bias"])
         q, k, v = (qkv[..., i * C:(i + 1) * C].reshape(B, T, H, hd).transpose(0, 2, 1, 3)
                    for i in range(3))
         O, lse = causal_attention_fwd(np.ascontiguousarray(q), np.ascontiguousarray(k),
-                                      np.ascontiguousarray(v))
-        y = O.transpose(0, 2, 1, 3).reshape(B, T, C)
+                                      np.ascontiguousarray(v), rnd=r)
+        y = r(O.transpose(0, 2, 1, 3).reshape(B, T, C))
         lc.update(q=q, k=k, v=v, lse=lse, y=y, qkv=qkv)
-        x = x + (y @ P[p + "attn.c_proj.weight"].T + P[p + "attn.c_proj.bias"])
+        x = x + (y @ r(P[p + "attn.c_proj.weight"]).T + P[p + "attn.c_proj.bias"])
         lc["x_mid"] = x
         u2, lc["xhat2"], lc["rstd2"] = layernorm_fwd(x, P[p + "ln_2.weight"], P[p + "ln_2.bias"])
+        u2 = r(u2)
         lc["u2"] = u2
-        h = u2 @ P[p + "mlp.c_fc.weight"].T + P[p + "mlp.c_fc.bias"]
-        g = gelu_tanh(h)
+        h = u2 @ r(P[p + "mlp.c_fc.weight"]).T + P[p + "mlp.c_fc.bias"]
+        g = r(gelu_tanh(h))
         lc.update(h=h, g=g)
-        x = x + (g @ P[p + "mlp.c_proj.weight"].T + P[p + "mlp.c_proj.bias"])
+        x = x + (g @ r(P[p + "mlp.c_proj.weight"]).T + P[p + "mlp.c_proj.bias"])
         cache["layers"].append(lc)
     cache["x_final"] = x
     z, cache["xhatf"], cache["rstdf"] = layernorm_fwd(x, P["ln_f.weight"], P["ln_f.bias"])
+    z = r(z)
     cache["z"] = z
-    logits = z.reshape(B * T, C) @ P["wte"].T                 # tied lm_head, no bias
+    logits = r(z.reshape(B * T, C) @ r(P["wte"]).T)          # tied lm_head, no bias
     if targets is None:
         cache["logits"] = logits.reshape(B, T, -1)
         return None, cache
     loss, dlogits, row_loss, n_valid = cross_entropy(logits, targets.reshape(-1))
-    cache.update(dlogits=dlogits, row_loss=row_loss, n_valid=n_valid)
+    cache.update(dlogits=r(dlogits), row_loss=row_loss, n_valid=n_valid)
     if keep_logits:
         cache["logits"] = logits.reshape(B, T, -1)
     return loss, cache
@@ -382,6 +430,7 @@ def backward(flat_params, cache, cfg: Config, loss_scale=1.0, grads=None):
     embedding contribution."""
     P = unflatten(flat_params, cfg)
     dt = flat_params.dtype
+    r = cache["rnd"]
     if grads is None:
         grads = np.zeros_like(flat_params)
     G = unflatten(grads, cfg)
@@ -392,7 +441,7 @@ def backward(flat_params, cache, cfg: Config, loss_scale=1.0, grads=None):
     dlogits = cache["dlogits"] * s                             # (B*T, Vp)
     z = cache["z"].reshape(B * T, C)
     G["wte"] += dlogits.T @ z                                  # lm_head part of the tie
-    dz = (dlogits @ P["wte"]).reshape(B, T, C)
+    dz = (dlogits @ r(P["wte"])).reshape(B, T, C)
     dx, dw, db = layernorm_bwd(dz, cache["xhatf"], cache["rstdf"], P["ln_f.weight"])
     G["ln_f.weight"] += dw
     G["ln_f.bias"] += db
@@ -401,28 +450,36 @@ def backward(flat_params, cache, cfg: Config, loss_scale=1.0, grads=None):
         lc = cache["layers"][l]
         # x_out = x_mid + c_proj(gelu(c_fc(ln_2(x_mid))))
         W2 = P[p + "mlp.c_proj.weight"]
-        G[p + "mlp.c_proj.weight"] += dx.reshape(-1, C).T @ lc["g"].reshape(-1, 4 * C)
+        dxr = r(dx)
+        G[p + "mlp.c_proj.weight"] += dxr.reshape(-1, C).T @ lc["g"].reshape(-1, 4 * C)
         G[p + "mlp.c_proj.bias"] += dx.sum(axis=(0, 1))
-        dg = dx @ W2
-        dh = dg * gelu_tanh_grad(lc["h"])
-        G[p + "mlp.c_fc.weight"] += dh.reshape(-1, 4 * C).T @ lc["u2"].reshape(-1, C)
+        dg = dxr @ r(W2)
+        dh = dg * r(gelu_tanh_grad(lc["h"]))
         G[p + "mlp.c_fc.bias"] += dh.sum(axis=(0, 1))
-        du2 = dh @ P[p + "mlp.c_fc.weight"]
+        dh = r(dh)
+        G[p + "mlp.c_fc.weight"] += dh.reshape(-1, 4 * C).T @ lc["u2"].reshape(-1, C)
+        du2 = dh @ r(P[p + "mlp.c_fc.weight"])
         d, dw, db = layernorm_bwd(du2, lc["xhat2"], lc["rstd2"], P[p + "ln_2.weight"])
         G[p + "ln_2.weight"] += dw
         G[p + "ln_2.bias"] += db
         dx = dx + d
         # x_mid = x_in + c_proj(attn(ln_1(x_in)))
-        G[p + "attn.c_proj.weight"] += dx.reshape(-1, C).T @ lc["y"].reshape(-1, C)
+        dxr = r(dx)
+        G[p + "attn.c_proj.weight"] += dxr.reshape(-1, C).T @ lc["y"].reshape(-1, C)
         G[p + "attn.c_proj.bias"] += dx.sum(axis=(0, 1))
-        dy = (dx @ P[p + "attn.c_proj.weight"]).reshape(B, T, H, hd).transpose(0, 2, 1, 3)
+        dy = r(dxr @ r(P[p + "attn.c_proj.weight"])).reshape(B, T, H, hd).transpose(0, 2, 1, 3)
+        # with rounding, the row term of the softmax backward comes from the
+        # stored (rounded) output, as a computation that keeps only that has it
+        y_heads = None if r is exact else np.ascontiguousarray(
+            lc["y"].reshape(B, T, H, hd).transpose(0, 2, 1, 3))
         dq, dk, dv = causal_attention_bwd(np.ascontiguousarray(dy), lc["q"], lc["k"], lc["v"],
-                                          lc["lse"])
+                                          lc["lse"], rnd=r, O=y_heads)
         dqkv = np.concatenate([a.transpose(0, 2, 1, 3).reshape(B, T, C) for a in (dq, dk, dv)],
                               axis=-1)
-        G[p + "attn.c_attn.weight"] += dqkv.reshape(-1, 3 * C).T @ lc["u1"].reshape(-1, C)
         G[p + "attn.c_attn.bias"] += dqkv.sum(axis=(0, 1))
-        du = dqkv @ P[p + "attn.c_attn.weight"]
+        dqkv = r(dqkv)
+        G[p + "attn.c_attn.weight"] += dqkv.reshape(-1, 3 * C).T @ lc["u1"].reshape(-1, C)
+        du = dqkv @ r(P[p + "attn.c_attn.weight"])
         d, dw, db = layernorm_bwd(du, lc["xhat1"], lc["rstd1"], P[p + "ln_1.weight"])
         G[p + "ln_1.weight"] += dw
         G[p + "ln_1.bias"] += db

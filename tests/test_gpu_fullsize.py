@@ -6,8 +6,8 @@ Every sequence of a batch is processed independently, and the loss at
 position t depends only on tokens 0..t (causal attention), so the oracle's
 forward pass over one sampled sequence -- or over its first P tokens --
 gives the per-position losses the GPU computed for that sequence inside the
-full batch.  Those are compared to the bf16 tolerance of the loss (2e-2 of
-the largest per-position loss).  Properties that hold at any size are checked
+full batch.  Those are compared within 5e-3 of the largest per-position
+loss.  Properties that hold at any size are checked
 over the whole batch: the mean loss equals the sum of per-position losses
 over the number of valid targets; reversing the order of the sequences
 permutes the per-position losses bit for bit; ignored targets give exactly
@@ -42,7 +42,7 @@ def oracle_position_losses(d, flat, idx, tgt, rows, prefix):
 def check_rows(gpu_rows, ref_rows, what):
     err = float(np.max(np.abs(gpu_rows - ref_rows)) / max(np.max(np.abs(ref_rows)), 1e-30))
     print(f"{what}: per-position loss maxrel {err:.2e}")
-    assert err < 2e-2, what
+    assert err < 5e-3, what
 
 
 def check_adamw_closed_form(m, flat, d, lr, wd, norm):
@@ -94,7 +94,7 @@ def test_124m_b16_sampled_sequences(m124):
     check_rows(rl[rows], ref, "124M B=16 sequences 0, 7, 15")
     ref_mean = ref.sum() / np.sum(tgt[rows] != -1)
     gpu_mean = rl[rows].sum() / np.sum(tgt[rows] != -1)
-    assert abs(gpu_mean - ref_mean) < 2e-2
+    assert abs(gpu_mean - ref_mean) < 5e-3
     m.backward(1.0)
     norm = m.adamw_step(LR, B1, B2, EPS, WD, CLIP, want_norm=True)
     check_adamw_closed_form(m, flat, d, LR, WD, norm)

@@ -21,6 +21,7 @@ import pytest
 
 torch = pytest.importorskip("torch")
 
+import bf16_check
 import oracle
 from oracle import gpt2_oracle as O
 import synthetic
@@ -89,12 +90,19 @@ def run_gpu_step(d, prec, flat, idx, tgt, lr=LR, wd=WD, head_chunk=0):
     return out
 
 
-def run_oracle_step(d, flat, idx, tgt, lr=LR, wd=WD, dtype=np.float32):
+def run_oracle_step(d, flat, idx, tgt, lr=LR, wd=WD, dtype=np.float32, emul=False):
+    """The oracle's step; emul: also the gradient of the same step with the
+    bf16 rounding placement, the noise model of bf16_check."""
     cfg = O.Config(**d)
     p = flat.astype(dtype).copy()
+    out = {}
+    if emul:
+        _, cache = O.forward(p, idx, tgt, cfg, rnd=O.bf16_round)
+        out["grads_emul"] = O.backward(p, cache, cfg)
+        del cache
     loss, cache = O.forward(p, idx, tgt, cfg)
     g = O.backward(p, cache, cfg)
-    out = {"loss": float(loss), "grads": g.copy(), "cache": cache}
+    out.update({"loss": float(loss), "grads": g.copy(), "cache": cache})
     mm, vv = np.zeros_like(p), np.zeros_like(p)
     out["norm"] = O.clip_and_adamw(p, g, mm, vv, 1, lr, B1, B2, EPS, wd, CLIP, cfg=cfg)
     out.update(params=p, m=mm, v=vv)
@@ -311,7 +319,7 @@ def step_124m_b2():
     flat = synthetic.init_params(d, seed=42)
     idx, tgt = synthetic.zipf_batch(2, 1024, seed=1002)
     g = run_gpu_step(d, "bf16", flat, idx, tgt)
-    r = run_oracle_step(d, flat, idx, tgt)
+    r = run_oracle_step(d, flat, idx, tgt, emul=True)
     return d, flat, idx, tgt, g, r
 
 
@@ -319,13 +327,13 @@ def test_bf16_124m_loss_and_activations(step_124m_b2):
     d, flat, idx, tgt, g, r = step_124m_b2
     print(f"\n124M bf16 B=2: loss gpu {g['loss']:.5f} oracle {r['loss']:.5f} "
           f"norm {g['norm']:.5f} / {r['norm']:.5f}")
-    assert abs(g["loss"] - r["loss"]) < 2e-2
+    assert abs(g["loss"] - r["loss"]) < 5e-3
     for l in (1, 6, 12):
         ref = r["cache"]["layers"][l]["x_in"] if l < 12 else r["cache"]["x_final"]
         e = maxrel(g["x_in"][l], ref.reshape(-1))
         print(f"x_in[{l}] maxrel {e:.2e}")
         assert e < 2e-2
-    assert maxrel(g["row_loss"], r["cache"]["row_loss"]) < 2e-2
+    assert maxrel(g["row_loss"], r["cache"]["row_loss"]) < 5e-3
 
 
 def test_bf16_124m_grads_and_update(step_124m_b2):
@@ -342,12 +350,12 @@ def test_bf16_124m_ragged_step():
     flat = synthetic.init_params(d, seed=42)
     idx, tgt = synthetic.zipf_batch(3, 333, seed=1013)
     tgt[1, :100] = -1
-    r = run_oracle_step(d, flat, idx, tgt)
+    r = run_oracle_step(d, flat, idx, tgt, emul=True)
     for hc in (0, 4096):
         g = run_gpu_step(d, "bf16", flat, idx, tgt, head_chunk=hc)
         print(f"\n124M bf16 B=3 T=333 head_chunk {hc}: loss gpu {g['loss']:.5f} oracle {r['loss']:.5f}")
-        assert abs(g["loss"] - r["loss"]) < 2e-2
-        assert maxrel(g["row_loss"], r["cache"]["row_loss"]) < 2e-2
+        assert abs(g["loss"] - r["loss"]) < 5e-3
+        assert maxrel(g["row_loss"], r["cache"]["row_loss"]) < 5e-3
         check_bf16_step(d, flat, g, r)
 
 
@@ -358,8 +366,8 @@ def test_bf16_124m_fused_head(step_124m_b2):
     d, flat, idx, tgt, _, r = step_124m_b2
     g = run_gpu_step(d, "bf16", flat, idx, tgt, head_chunk=4096)
     print(f"\n124M bf16 B=2 fused head: loss gpu {g['loss']:.5f} oracle {r['loss']:.5f}")
-    assert abs(g["loss"] - r["loss"]) < 2e-2
-    assert maxrel(g["row_loss"], r["cache"]["row_loss"]) < 2e-2
+    assert abs(g["loss"] - r["loss"]) < 5e-3
+    assert maxrel(g["row_loss"], r["cache"]["row_loss"]) < 5e-3
     check_bf16_step(d, flat, g, r)
 
 
@@ -433,59 +441,17 @@ def test_bf16_124m_backward_is_deterministic(step_124m_b2):
         ms[1].close()
 
 
-def check_bf16_step(d, flat, g, r):
-    """bf16: gradients per tensor within 1.2e-2 normwise (bf16 storage of
-    activations and of the gradients flowing between layers, about
-    sqrt(#roundings) * 2^-9); the AdamW kernel exactly (the oracle's update
-    applied to the GPU's own gradients, 1e-5); and the parameters after one
-    step within 5e-3 normwise of the oracle's over the elements whose oracle
-    gradient exceeds the measured bf16 gradient noise of its tensor (4 x rms
-    of gpu - oracle over the element's row).  Below that floor the sign of g is not determined by
-    any bf16 computation, and Adam's first step is lr * sign(g): those
-    elements may differ by up to 2 lr, which is asserted instead."""
-    cfg = O.Config(**d)
-    kb = key_bias_mask(cfg)
-    # the GPU's own gradients through the oracle's clip + AdamW
-    p_or = flat.astype(np.float32).copy()
-    g_own = g["grads"].copy()
-    O.clip_and_adamw(p_or, g_own, np.zeros_like(p_or), np.zeros_like(p_or), 1, LR, B1, B2, EPS, WD,
-                     CLIP, cfg=cfg)
-    off = 0
-    worst_g = worst_p = worst_opt = 0.0
-    excluded = 0
-    for name, shape in O.param_specs(cfg):
-        n = int(np.prod(shape))
-        sl = slice(off, off + n)
-        off += n
-        keep = ~kb[sl]
-        ga, gr = g["grads"][sl][keep].astype(np.float64), r["grads"][sl][keep].astype(np.float64)
-        pa, pr = g["params"][sl][keep].astype(np.float64), r["params"][sl][keep].astype(np.float64)
-        po = p_or[sl][keep].astype(np.float64)
-        eg = np.linalg.norm(ga - gr) / max(np.linalg.norm(gr), 1e-30)
-        eo = np.max(np.abs(pa - po)) / max(np.max(np.abs(po)), 1e-30)
-        # noise floor per output row of a matrix (rows differ in scale: token
-        # rows absent from the batch, q/k/v thirds), per tensor for vectors
-        rows = shape[0] if len(shape) == 2 else 1
-        diff2 = np.zeros(n)
-        diff2[keep] = (ga - gr) ** 2
-        noise = np.sqrt(diff2.reshape(rows, -1).mean(axis=1))
-        noise = np.repeat(noise, n // rows)[keep]
-        det = np.abs(gr) > 4 * noise
-        ep = np.linalg.norm(pa[det] - pr[det]) / max(np.linalg.norm(pr[det]), 1e-30)
-        excluded += int((~det).sum())
-        assert np.max(np.abs(pa[~det] - pr[~det]), initial=0.0) <= 2.0 * LR * 1.001 + 1e-7, name
-        worst_g, worst_p, worst_opt = max(worst_g, eg), max(worst_p, ep), max(worst_opt, eo)
-        if name.startswith(("wte", "wpe", "h.0.", "h.11.", "ln_f")):
-            print(f"{name:28s} grad {eg:.2e} param(det) {ep:.2e} adamw {eo:.1e} "
-                  f"below-noise {np.mean(~det):.2e}")
-    frac = excluded / float((~kb).sum())
-    print(f"worst: grad {worst_g:.2e}, param {worst_p:.2e}, adamw {worst_opt:.2e}; "
-          f"below-noise fraction {frac:.3e}")
-    assert abs(g["norm"] - r["norm"]) < 2e-2 * r["norm"]
-    assert worst_g < 1.2e-2
-    assert worst_opt < 1e-5
-    assert worst_p < 5e-3
-    assert frac < 0.05
+def check_bf16_step(d, flat, g, r, lr=LR, wd=WD):
+    """The bf16 step against the oracle's (tests/bf16_check.py): gradients per
+    tensor and per row, each row's error against the bf16-rounded oracle's
+    error in that row; the AdamW kernel on the GPU's own gradients; the
+    parameters over the elements whose oracle gradient is well above that
+    rounding noise."""
+    fails, _ = bf16_check.compare_step(
+        O, O.Config(**d), p0=flat, g_gpu=g["grads"], g_ref=r["grads"], g_emul=r["grads_emul"],
+        p_gpu=g["params"], p_ref=r["params"], norm_gpu=g["norm"], norm_ref=r["norm"], lr=lr,
+        wd=wd, t=1)
+    assert not fails, fails
 
 
 @pytest.mark.parametrize("hc", [0, 192])

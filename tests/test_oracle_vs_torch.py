@@ -135,3 +135,46 @@ def test_layernorm_and_gelu_match_torch():
     assert np.max(np.abs(y - ref)) < 1e-12
     z = rng.standard_normal(10000) * 4
     assert np.max(np.abs(O.gelu_tanh(z) - F.gelu(torch.tensor(z), approximate="tanh").numpy())) < 1e-12
+
+
+def test_bf16_round_matches_torch_conversion():
+    """The oracle's bf16 rounding is torch's float32 -> bfloat16 conversion:
+    nearest, ties to even (exact halfway cases both ways), NaN and infinities
+    kept, values past the largest bf16 to infinity."""
+    rng = np.random.default_rng(3)
+    x = np.concatenate([
+        rng.standard_normal(100000).astype(np.float32) * np.float32(10.0) ** rng.integers(-30, 30, 100000).astype(np.float32),
+        np.array([0.0, -0.0, 1.0, np.inf, -np.inf, np.nan, 3.3895314e38, 3.39e38, 1e-40], np.float32),
+        # halfway cases: the dropped 16 bits are exactly 0x8000, kept lsb 0 and 1
+        np.array([0x3F808000, 0x3F818000, 0xBF808000, 0x3F80FFFF, 0x3F807FFF], np.uint32).view(np.float32),
+    ])
+    want = torch.from_numpy(x).to(torch.bfloat16).float().numpy()
+    got = O.bf16_round(x)
+    same = (got.view(np.uint32) == want.view(np.uint32)) | (np.isnan(got) & np.isnan(want))
+    assert same.all(), x[~same][:5]
+
+
+def test_bf16_placement_stays_near_the_exact_step():
+    """The bf16-rounded step (R8) is a perturbation of the exact one: loss
+    within 1e-3 relative, every gradient tensor within 3e-2 normwise; and the
+    exact rounding hook leaves the computation unchanged."""
+    d = synthetic.model_dims("tiny")
+    d = dict(d, n_head=2)
+    cfg = O.Config(**d)
+    flat = synthetic.init_params(d, seed=4)
+    idx, tgt = synthetic.uniform_batch(2, 64, 512, seed=5)
+    l0, c0 = O.forward(flat.copy(), idx, tgt, cfg)
+    g0 = O.backward(flat.copy(), c0, cfg)
+    l1, c1 = O.forward(flat.copy(), idx, tgt, cfg, rnd=O.exact)
+    assert l1 == l0 and np.array_equal(O.backward(flat.copy(), c1, cfg), g0)
+    lb, cb = O.forward(flat.copy(), idx, tgt, cfg, rnd=O.bf16_round)
+    gb = O.backward(flat.copy(), cb, cfg)
+    assert abs(lb - l0) < 1e-3 * l0
+    assert not np.array_equal(gb, g0)
+    off = 0
+    for name, shape in O.param_specs(cfg):
+        n = int(np.prod(shape))
+        a, b = gb[off:off + n].astype(np.float64), g0[off:off + n].astype(np.float64)
+        if np.linalg.norm(b) > 0 and not name.endswith("c_attn.bias"):
+            assert np.linalg.norm(a - b) / np.linalg.norm(b) < 3e-2, name
+        off += n

@@ -1,8 +1,42 @@
 // Single-kernel entry points (include/gpt2_ops.h).
 #include <cstring>
+#include <mutex>
 
 #include "../../include/gpt2_ops.h"
 #include "kernels.h"
+
+namespace {
+
+// Device scratch of gpt2_op_attention_bwd_noalloc: the per-(b, h, t) row term
+// D = rowsum(dO o O) that the dQ pass writes and the dK/dV pass reads.  Every
+// GPU the library runs on holds its own copy of this array until the process
+// ends.  In host code `attn_scratch` only names the symbol: kernels get the
+// per-device address from hipGetSymbolAddress.
+constexpr long ATTN_SCRATCH_FLOATS = 1L << 20;
+__device__ __align__(256) float attn_scratch[ATTN_SCRATCH_FLOATS];
+
+constexpr int MAX_DEVICES = 64;
+float* scratch_ptr[MAX_DEVICES];
+hipError_t scratch_err[MAX_DEVICES];
+std::once_flag scratch_once[MAX_DEVICES];
+
+// The address of attn_scratch on the current device, looked up once per
+// device with that device current.
+hipError_t attn_scratch_on_current_device(float** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= MAX_DEVICES) return hipErrorInvalidDevice;
+  std::call_once(scratch_once[dev], [dev] {
+    void* p = nullptr;
+    scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(attn_scratch));
+    scratch_ptr[dev] = static_cast<float*>(p);
+  });
+  *out = scratch_ptr[dev];
+  return scratch_err[dev];
+}
+
+}  // namespace
 
 extern "C" {
 
@@ -41,6 +75,19 @@ gpt2_status gpt2_op_attention_bwd(int dtype, const void* qkv, const void* y, con
   hipError_t r = launch_attn_bwd(dtype == GPT2_BF16 ? DT_BF16 : DT_F32, qkv, y, lse, dy, dqkv,
                                  dbuf, B, T, H, hd, nullptr,
                                  reinterpret_cast<hipStream_t>(hip_stream));
+  if (r == hipErrorInvalidValue) return GPT2_E_ARG;
+  return r == hipSuccess ? GPT2_OK : GPT2_E_HIP;
+}
+
+gpt2_status gpt2_op_attention_bwd_noalloc(int dtype, const void* qkv, const void* y,
+                                          const float* lse, const void* dy, void* dqkv, int B,
+                                          int T, int H, int hd, void* hip_stream) {
+  if (!qkv || !y || !lse || !dy || !dqkv || B < 1 || T < 1 || H < 1) return GPT2_E_ARG;
+  if ((long)B * H * T > ATTN_SCRATCH_FLOATS) return GPT2_E_ARG;
+  float* d = nullptr;
+  if (attn_scratch_on_current_device(&d) != hipSuccess || !d) return GPT2_E_HIP;
+  hipError_t r = launch_attn_bwd(dtype == GPT2_BF16 ? DT_BF16 : DT_F32, qkv, y, lse, dy, dqkv, d,
+                                 B, T, H, hd, nullptr, reinterpret_cast<hipStream_t>(hip_stream));
   if (r == hipErrorInvalidValue) return GPT2_E_ARG;
   return r == hipSuccess ? GPT2_OK : GPT2_E_HIP;
 }

@@ -87,6 +87,8 @@ def lib():
                                    ct.c_long, f32, i32, i32, vp]),
             "gpt2_op_attention_fwd": (i32, [i32, vp, vp, vp, i32, i32, i32, i32, vp]),
             "gpt2_op_attention_bwd": (i32, [i32, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, vp]),
+            "gpt2_op_attention_bwd_noalloc": (i32, [i32, vp, vp, vp, vp, vp, i32, i32, i32, i32,
+                                                    vp]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -103,7 +105,8 @@ EXPORTED = ["gpt2_num_params", "gpt2_workspace_bytes", "gpt2_init", "gpt2_lr_at"
             "gpt2_zero_grad", "gpt2_backward", "gpt2_adamw_step", "gpt2_get_grad_norm",
             "gpt2_sync", "gpt2_last_error", "gpt2_destroy", "gpt2_get_activation",
             "gpt2_timing_begin", "gpt2_timing_end", "gpt2_wgrad_layout",
-            "gpt2_op_gemm", "gpt2_op_attention_fwd", "gpt2_op_attention_bwd"]
+            "gpt2_op_gemm", "gpt2_op_attention_fwd", "gpt2_op_attention_bwd",
+            "gpt2_op_attention_bwd_noalloc"]
 
 
 def make_config(n_layer, n_head, n_embd, vocab_size, padded_vocab_size, block_size, max_batch,
@@ -331,3 +334,11 @@ def gpt2_op_attention_bwd(dtype, qkv, y, lse, dy, dqkv, dbuf, B, T, H, hd, strea
                                     _ptr(dbuf), B, T, H, hd,
                                     stream.cuda_stream if stream is not None else None),
         "gpt2_op_attention_bwd")
+
+
+def gpt2_op_attention_bwd_noalloc(dtype, qkv, y, lse, dy, dqkv, B, T, H, hd, stream=None):
+    """gpt2_op_attention_bwd with the library's fixed device scratch (no dbuf)."""
+    _st(lib().gpt2_op_attention_bwd_noalloc(dtype, _ptr(qkv), _ptr(y), _ptr(lse), _ptr(dy),
+                                            _ptr(dqkv), B, T, H, hd,
+                                            stream.cuda_stream if stream is not None else None),
+        "gpt2_op_attention_bwd_noalloc")

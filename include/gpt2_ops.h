@@ -48,6 +48,23 @@ gpt2_status gpt2_op_attention_bwd(int dtype, const void* qkv, const void* y, con
                                   const void* dy, void* dqkv, float* dbuf, int B, int T, int H,
                                   int hd, void* hip_stream);
 
+/* gpt2_op_attention_bwd for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): the same kernels and the same results, with the scratch for
+ * D taken from a fixed array of 1,048,576 floats (4 MiB) that the library
+ * keeps on each GPU it runs on, instead of a dbuf argument.  B * H * T may
+ * not exceed 1,048,576 (GPT2_E_ARG, nothing enqueued).  Nothing is
+ * allocated; the array's address on the current device is looked up on the
+ * first call on that device, so hip_stream must belong to the current
+ * device.  Every call on one GPU shares that GPU's array: calls that overlap
+ * on one GPU (other streams, other threads) race and give wrong results.
+ * Nothing in the array needs to start at a particular value: the dQ pass
+ * writes every D it uses before the dK/dV pass reads it.  GPT2_E_HIP if the
+ * lookup or a launch fails. */
+gpt2_status gpt2_op_attention_bwd_noalloc(int dtype, const void* qkv, const void* y,
+                                          const float* lse, const void* dy, void* dqkv, int B,
+                                          int T, int H, int hd, void* hip_stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -33,10 +33,13 @@ struct Layout {
   long P = 0;
   long wte = 0, wpe = 0, lnfw = 0, lnfb = 0;
   std::vector<LayerOff> layer;
-  // (offset, length, decay, init) of every tensor in canonical order
+  // (offset, length, decay, init) of every tensor in canonical order, and
+  // whether the input-gradient products also read it transposed (bf16 mode
+  // keeps a transposed bf16 copy of those matrices)
   std::vector<long> t_off, t_len;
   std::vector<int> t_decay;
   std::vector<int> t_init;
+  std::vector<int> t_trans;
 };
 
 // How a tensor starts ("GPT-2 from Scratch", Initialization: 0.02, and the
@@ -76,30 +79,31 @@ Layout make_layout(const gpt2_config* c) {
   Layout L;
   const long C = c->n_embd, Vp = c->padded_vocab_size;
   // matrices and embeddings (dim 2) are decayed, vectors are not
-  auto add = [&](long n, int init) {
+  auto add = [&](long n, int init, int trans = 0) {
     long o = L.P;
     L.t_off.push_back(o);
     L.t_len.push_back(n);
     L.t_decay.push_back(init >= INIT_NORMAL ? 1 : 0);
     L.t_init.push_back(init);
+    L.t_trans.push_back(trans);
     L.P += n;
     return o;
   };
-  L.wte = add(Vp * C, INIT_NORMAL);
+  L.wte = add(Vp * C, INIT_NORMAL, 1);
   L.wpe = add((long)c->block_size * C, INIT_NORMAL);
   for (int l = 0; l < c->n_layer; ++l) {
     LayerOff o;
     o.ln1w = add(C, INIT_ONE);
     o.ln1b = add(C, INIT_ZERO);
-    o.attnw = add(3 * C * C, INIT_NORMAL);
+    o.attnw = add(3 * C * C, INIT_NORMAL, 1);
     o.attnb = add(3 * C, INIT_ZERO);
-    o.projw = add(C * C, INIT_NORMAL_RESID);
+    o.projw = add(C * C, INIT_NORMAL_RESID, 1);
     o.projb = add(C, INIT_ZERO);
     o.ln2w = add(C, INIT_ONE);
     o.ln2b = add(C, INIT_ZERO);
-    o.fcw = add(4 * C * C, INIT_NORMAL);
+    o.fcw = add(4 * C * C, INIT_NORMAL, 1);
     o.fcb = add(4 * C, INIT_ZERO);
-    o.fc2w = add(4 * C * C, INIT_NORMAL_RESID);
+    o.fc2w = add(4 * C * C, INIT_NORMAL_RESID, 1);
     o.fc2b = add(C, INIT_ZERO);
     L.layer.push_back(o);
   }
@@ -110,9 +114,12 @@ Layout make_layout(const gpt2_config* c) {
 
 constexpr long ADAM_CHUNK = 16384;
 
-std::vector<AdamChunk> make_chunks(const Layout& L) {
+// Chunks of the flat AdamW pass; skip_trans: leave out the matrices that
+// the tiled pass (which also writes their transposed copy) updates.
+std::vector<AdamChunk> make_chunks(const Layout& L, bool skip_trans) {
   std::vector<AdamChunk> v;
-  for (size_t t = 0; t < L.t_off.size(); ++t)
+  for (size_t t = 0; t < L.t_off.size(); ++t) {
+    if (skip_trans && L.t_trans[t]) continue;
     for (long s = 0; s < L.t_len[t]; s += ADAM_CHUNK) {
       AdamChunk ck;
       ck.start = L.t_off[t] + s;
@@ -120,6 +127,7 @@ std::vector<AdamChunk> make_chunks(const Layout& L) {
       ck.flags = L.t_decay[t];
       v.push_back(ck);
     }
+  }
   return v;
 }
 
@@ -264,7 +272,7 @@ size_t plan(const gpt2_config* c, char* base, gpt2* h) {
   const size_t C = c->n_embd, H = c->n_head, Vp = c->padded_vocab_size;
   const size_t BT = (size_t)c->max_batch * c->block_size;
   const size_t es = c->precision == GPT2_BF16 ? 2 : 4;
-  std::vector<AdamChunk> ch = make_chunks(L);
+  std::vector<AdamChunk> ch = make_chunks(L, c->precision == GPT2_BF16);
   float* params = a.take_n<float>(P);
   float* grads = a.take_n<float>(P);
   float* m = a.take_n<float>(P);
@@ -872,7 +880,7 @@ gpt2_status gpt2_init(const gpt2_config* cfg, void* d_workspace, size_t ws_bytes
   h->act = cfg->precision == GPT2_BF16 ? DT_BF16 : DT_F32;
   h->act_size = h->act == DT_BF16 ? 2 : 4;
   plan(cfg, reinterpret_cast<char*>(d_workspace), h);
-  std::vector<AdamChunk> ch = make_chunks(h->lay);
+  std::vector<AdamChunk> ch = make_chunks(h->lay, h->act == DT_BF16);
   hipError_t e = hipMemcpyAsync(h->chunks, ch.data(), ch.size() * sizeof(AdamChunk),
                                 hipMemcpyHostToDevice, h->stream);
   std::vector<TTile> tt = h->nttiles ? make_ttiles(h->lay, cfg) : std::vector<TTile>();
@@ -1120,12 +1128,16 @@ gpt2_status gpt2_adamw_step(gpt2_t* h, float lr, float beta1, float beta2, float
   const float inv_sqrt_bc2 = (float)(1.0 / std::sqrt(bc2));
   TIMED(h, GPT2_SITE_GRAD_NORM, launch_grad_norm(h->grads, h->lay.P, h->norm_partial, max_grad_norm, h->norm, h->clip,
                              h->stream));
+  // bf16: the matrices that are also read transposed go tile by tile, writing
+  // both bf16 copies; the flat pass takes every other tensor
+  if (h->shadow_t)
+    TIMED(h, GPT2_SITE_ADAMW, launch_adamw_tiles(h->ttiles, h->nttiles, h->params, h->grads, h->m,
+                                                 h->v, h->shadow, h->shadow_t, h->clip, lr, beta1,
+                                                 beta2, eps, weight_decay, step_size,
+                                                 inv_sqrt_bc2, h->stream));
   TIMED(h, GPT2_SITE_ADAMW, launch_adamw(h->chunks, h->nchunks, h->params, h->grads, h->m, h->v, h->shadow,
                          h->clip, lr, beta1, beta2, eps, weight_decay, step_size, inv_sqrt_bc2,
                          h->stream));
-  if (h->shadow_t)
-    TIMED(h, GPT2_SITE_WEIGHT_T, launch_transpose_tiles(h->shadow, h->shadow_t, h->ttiles,
-                                                        h->nttiles, h->stream));
   if (h_grad_norm) return gpt2_get_grad_norm(h, h_grad_norm);
   return GPT2_OK;
 }

@@ -917,6 +917,69 @@ __global__ __launch_bounds__(256) void adamw_kernel(const AdamChunk* __restrict_
   }
 }
 
+// AdamW on 64 x 64 tiles of the decayed matrices that the input-gradient
+// products also read transposed: the same update as adamw_kernel, and besides
+// the bf16 copy at the same offset, its transpose (cols x rows) into
+// shadow_t, through LDS.  Each load or store instruction of a wavefront
+// covers four whole 64-element rows (16 lanes x 4 elements per row): lane l
+// of wavefront w takes rows 16w + 4q + l/16 (q = 0..3), columns 4 (l%16) ..
+// +3; the transposed tile is written the same way.
+__global__ __launch_bounds__(256) void adamw_tiles_kernel(const TTile* __restrict__ tiles,
+                                                          float* __restrict__ p,
+                                                          const float* __restrict__ g,
+                                                          float* __restrict__ m,
+                                                          float* __restrict__ v,
+                                                          bf16_t* __restrict__ shadow,
+                                                          bf16_t* __restrict__ shadow_t,
+                                                          const float* __restrict__ clip, float lr,
+                                                          float b1, float b2, float eps, float wd,
+                                                          float step_size, float inv_sqrt_bc2) {
+  __shared__ uint16_t t[64][66];  // padded rows: the column reads spread over the banks
+  const TTile tt = tiles[blockIdx.x];
+  const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, c4 = 4 * (l & 15);
+  const float c = *clip;
+  const float decay = 1.0f - lr * wd;
+  const long tile0 = tt.off + (long)tt.r0 * tt.cols + tt.c0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int r = 16 * w + 4 * q + (l >> 4);
+    const long e = tile0 + (long)r * tt.cols + c4;
+    const float4 pp = *reinterpret_cast<const float4*>(p + e);
+    const float4 gg = *reinterpret_cast<const float4*>(g + e);
+    const float4 mm = *reinterpret_cast<const float4*>(m + e);
+    const float4 vv = *reinterpret_cast<const float4*>(v + e);
+    float P[4] = {pp.x, pp.y, pp.z, pp.w}, G[4] = {gg.x, gg.y, gg.z, gg.w};
+    float M[4] = {mm.x, mm.y, mm.z, mm.w}, V[4] = {vv.x, vv.y, vv.z, vv.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float gj = G[j] * c;
+      P[j] *= decay;
+      M[j] = b1 * M[j] + (1.0f - b1) * gj;
+      V[j] = b2 * V[j] + (1.0f - b2) * gj * gj;
+      P[j] -= step_size * M[j] / (sqrtf(V[j]) * inv_sqrt_bc2 + eps);
+    }
+    *reinterpret_cast<float4*>(p + e) = make_float4(P[0], P[1], P[2], P[3]);
+    *reinterpret_cast<float4*>(m + e) = make_float4(M[0], M[1], M[2], M[3]);
+    *reinterpret_cast<float4*>(v + e) = make_float4(V[0], V[1], V[2], V[3]);
+    const uint32_t w0 = pack_bf2(P[0], P[1]), w1 = pack_bf2(P[2], P[3]);
+    *reinterpret_cast<uint2*>(shadow + e) = make_uint2(w0, w1);
+    t[r][c4] = (uint16_t)(w0 & 0xffffu);
+    t[r][c4 + 1] = (uint16_t)(w0 >> 16);
+    t[r][c4 + 2] = (uint16_t)(w1 & 0xffffu);
+    t[r][c4 + 3] = (uint16_t)(w1 >> 16);
+  }
+  __syncthreads();
+  // row oc of the transpose = column oc of the tile; this lane's 4 tile rows
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int oc = 16 * w + 4 * q + (l >> 4);
+    const uint32_t o0 = (uint32_t)t[c4][oc] | ((uint32_t)t[c4 + 1][oc] << 16);
+    const uint32_t o1 = (uint32_t)t[c4 + 2][oc] | ((uint32_t)t[c4 + 3][oc] << 16);
+    *reinterpret_cast<uint2*>(shadow_t + tt.off + (long)(tt.c0 + oc) * tt.rows + tt.r0 + c4) =
+        make_uint2(o0, o1);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // small utilities
 // ---------------------------------------------------------------------------
@@ -1161,6 +1224,17 @@ hipError_t launch_adamw(const AdamChunk* chunks, int nchunks, float* p, const fl
                         float eps, float wd, float step_size, float inv_sqrt_bc2, hipStream_t s) {
   adamw_kernel<<<nchunks, 256, 0, s>>>(chunks, p, g, m, v, shadow, clip, lr, b1, b2, eps, wd,
                                        step_size, inv_sqrt_bc2);
+  return hipGetLastError();
+}
+
+hipError_t launch_adamw_tiles(const TTile* tiles, int ntiles, float* p, const float* g, float* m,
+                              float* v, bf16_t* shadow, bf16_t* shadow_t, const float* clip,
+                              float lr, float b1, float b2, float eps, float wd, float step_size,
+                              float inv_sqrt_bc2, hipStream_t s) {
+  if (ntiles <= 0) return hipSuccess;
+  adamw_tiles_kernel<<<(unsigned)ntiles, 256, 0, s>>>(tiles, p, g, m, v, shadow, shadow_t, clip,
+                                                      lr, b1, b2, eps, wd, step_size,
+                                                      inv_sqrt_bc2);
   return hipGetLastError();
 }
 

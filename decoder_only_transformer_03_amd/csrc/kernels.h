@@ -96,6 +96,12 @@ hipError_t launch_grad_norm(const float* g, long n, double* partial, float max_n
 hipError_t launch_adamw(const AdamChunk* chunks, int nchunks, float* p, const float* g, float* m,
                         float* v, bf16_t* shadow, const float* clip, float lr, float b1, float b2,
                         float eps, float wd, float step_size, float inv_sqrt_bc2, hipStream_t s);
+// AdamW on the 64 x 64 tiles of decayed matrices, also writing the bf16 copy
+// (shadow) and its transpose (shadow_t, same offset, cols x rows).
+hipError_t launch_adamw_tiles(const TTile* tiles, int ntiles, float* p, const float* g, float* m,
+                              float* v, bf16_t* shadow, bf16_t* shadow_t, const float* clip,
+                              float lr, float b1, float b2, float eps, float wd, float step_size,
+                              float inv_sqrt_bc2, hipStream_t s);
 hipError_t launch_fill(float* p, long n, float val, hipStream_t s);
 // p[i] = std * (standard normal number e0 + i of the stream of `seed`), for
 // 0 <= i < n (Philox4x32-10 counters, Box-Muller; k_init.hip).

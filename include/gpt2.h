@@ -295,8 +295,11 @@ gpt2_status gpt2_get_activation(gpt2_t* h, int which, int layer, float* h_dst, s
  * fused head (head_chunk > 0) LMHEAD_FWD is the partials GEMM, XENT the
  * log-sum-exp and loss reduction, LMHEAD_RECOMP the backward's recomputation
  * of a slice of logits, LMHEAD_DX/DW the slices' shares of dz and dwte.
- * WEIGHT_T is the refresh, after each AdamW step, of the transposed bf16
- * weight copies that the input-gradient products read.  In GPT2_BF16 with
+ * ADAMW covers the optimizer update: in GPT2_BF16 one launch over 64 x 64
+ * tiles of the matrices that the input-gradient products read transposed
+ * (it also writes their bf16 and transposed bf16 copies) and one over every
+ * other tensor.  WEIGHT_T is kept for the numbering and records nothing.
+ * In GPT2_BF16 with
  * B*T a multiple of 64, the weight gradients of all blocks (and of the
  * lm_head, unless fused) run as one grouped launch at the end of the
  * backward pass, timed as WGRAD; the per-product *_DW sites are then empty.

@@ -57,6 +57,13 @@ WORKLOADS = {
                                      wd=0.0, eval=True, head_chunk=4096,
                                      desc="GPT-2 124M evaluation pass, bf16, B=16, T=1024, Zipf "
                                           "ids, fused lm_head + cross-entropy (no logits tensor)"),
+    "gpt2-124m-generate-cached": dict(model="gpt2-124m", B=8, T=32, data="zipf", lr=None, wd=0.0,
+                                      gen=96, top_k=50, cached=True,
+                                      desc="GPT-2 124M sampling loop with a key/value cache, bf16: "
+                                           "8 sequences, 32-token Zipf prompts, 96 new tokens "
+                                           "each, temperature 1, top-k 50; the prompt is "
+                                           "computed once, each new token runs the blocks for "
+                                           "its own position; value = new tokens per second"),
     "gpt2-124m-generate": dict(model="gpt2-124m", B=8, T=32, data="zipf", lr=None, wd=0.0,
                                gen=96, top_k=50,
                                desc="GPT-2 124M sampling loop, bf16: 8 sequences, 32-token Zipf "
@@ -191,7 +198,8 @@ def main():
 
     def step():
         if n_gen:
-            model.generate(dev[0][0], n_gen, gen_u, gen_out, 1.0, wl["top_k"])
+            gen = model.generate_cached if wl.get("cached") else model.generate
+            gen(dev[0][0], n_gen, gen_u, gen_out, 1.0, wl["top_k"])
             return
         if wl.get("eval"):
             model.eval(dev[0][0], dev[0][1], seq_loss=seq_loss)

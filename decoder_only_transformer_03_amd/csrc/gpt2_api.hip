@@ -203,6 +203,7 @@ struct gpt2 {
   // generation
   float* gen_logits;      // (max_batch, Vp) last-position logits
   int32_t* gen_idx;       // (max_batch, block_size) cropped context
+  void* kv;               // key/value cache: per block (max_batch, block_size, 2C)
   // backward scratch
   float* dres;
   void* dres_b;           // bf16 mode: 2L slots of the residual gradient (see run_backward)
@@ -320,6 +321,7 @@ size_t plan(const gpt2_config* c, char* base, gpt2* h) {
   float* row_loss = a.take_n<float>(BT);
   float* gen_logits = a.take_n<float>((size_t)c->max_batch * Vp);
   int32_t* gen_idx = a.take_n<int32_t>(BT);
+  void* kv = a.take((size_t)c->n_layer * BT * 2 * C * es);
   float* dres = a.take_n<float>(BT * C);
   const bool bf = c->precision == GPT2_BF16;
   const size_t nl = (size_t)c->n_layer;
@@ -349,7 +351,7 @@ size_t plan(const gpt2_config* c, char* base, gpt2* h) {
     h->row_loss = row_loss;
     h->head_chunk = (int)hc; h->hslice = hslice; h->hpart = hpart; h->hlse = hlse;
     h->htlogit = htlogit; h->tgt = tgt;
-    h->gen_logits = gen_logits; h->gen_idx = gen_idx;
+    h->gen_logits = gen_logits; h->gen_idx = gen_idx; h->kv = kv;
     h->dres = dres; h->dres_b = dres_b; h->dxtmp = dxtmp; h->dbig = dbig; h->dqkv = dqkv;
     h->wg_probs = wg_probs;
     h->dy = dy; h->dbuf = dbuf;
@@ -838,6 +840,71 @@ hipError_t init_params(gpt2* h, uint64_t seed) {
   return hipSuccess;
 }
 
+// Key/value cache of block l: (max_batch, block_size, 2C) rows [k | v].
+void* kv_slot(const gpt2* h, int l) {
+  return static_cast<char*>(h->kv) +
+         (size_t)l * bt_max(h) * 2 * h->cfg.n_embd * h->act_size;
+}
+
+// One decoding step: the blocks for position p of each sequence only, the
+// token ids d_tok (B, device), the keys and values of positions < p read from
+// the cache and those of p appended to it; the last-position logits (B, Vp)
+// fp32 into h->gen_logits.  The activations of layer 0 serve as scratch.
+gpt2_status run_decode(gpt2* h, const int32_t* d_tok, int B, int p) {
+  const gpt2_config& c = h->cfg;
+  const int C = c.n_embd, H = c.n_head, hd = C / H, Vp = c.padded_vocab_size;
+  const DType at = h->act;
+  hipStream_t s = h->stream;
+  float* P = h->params;
+  LayerAct& a = h->A[0];
+  float* x = a.x_in;      // residual stream, B rows
+  float* xm = a.x_mid;
+  TIMED(h, GPT2_SITE_EMBED_FWD, launch_embed_fwd(d_tok, h->idx, P + h->lay.wte,
+                                                 P + h->lay.wpe + (long)p * C, x, B, 1, C, Vp,
+                                                 h->err, s));
+  for (int l = 0; l < c.n_layer; ++l) {
+    const LayerOff& o = h->lay.layer[l];
+    TIMED(h, GPT2_SITE_LN_FWD, launch_layernorm_fwd(at, x, P + o.ln1w, P + o.ln1b, a.u1, a.mean1,
+                                                    a.rstd1, B, C, s));
+    EpiArgs e = epi(a.qkv, 3 * C);
+    e.bias = P + o.attnb;
+    TIMED(h, GPT2_SITE_QKV_FWD, launch_gemm_fill(at, B, 3 * C, C, a.u1, C, false, W(h, o.attnw), C,
+                                                 false, EPI_BIAS, at, e, h->splitk,
+                                                 SPLITK_PART_ELEMS, s));
+    HIPTRY(h, launch_kv_append(at, a.qkv, kv_slot(h, l), B, 1, p, c.block_size, C, s));
+    TIMED(h, GPT2_SITE_ATTN_FWD, launch_attn_decode(at, a.qkv, kv_slot(h, l), a.y, B, p,
+                                                    c.block_size, H, hd, s));
+    e = epi(xm, C);
+    e.bias = P + o.projb;
+    e.resid = x;
+    e.ldr = C;
+    TIMED(h, GPT2_SITE_PROJ_FWD, launch_gemm_fill(at, B, C, C, a.y, C, false, W(h, o.projw), C,
+                                                  false, EPI_RESID, DT_F32, e, h->splitk,
+                                                  SPLITK_PART_ELEMS, s));
+    TIMED(h, GPT2_SITE_LN_FWD, launch_layernorm_fwd(at, xm, P + o.ln2w, P + o.ln2b, a.u2, a.mean2,
+                                                    a.rstd2, B, C, s));
+    e = epi(a.h, 4 * C);
+    e.out2 = a.g;
+    e.bias = P + o.fcb;
+    TIMED(h, GPT2_SITE_FC_FWD, launch_gemm_fill(at, B, 4 * C, C, a.u2, C, false, W(h, o.fcw), C,
+                                                false, EPI_BIAS_GELU, at, e, h->splitk,
+                                                SPLITK_PART_ELEMS, s));
+    e = epi(x, C);
+    e.bias = P + o.fc2b;
+    e.resid = xm;
+    e.ldr = C;
+    TIMED(h, GPT2_SITE_FCPROJ_FWD, launch_gemm_fill(at, B, C, 4 * C, a.g, 4 * C, false,
+                                                    W(h, o.fc2w), 4 * C, false, EPI_RESID, DT_F32,
+                                                    e, h->splitk, SPLITK_PART_ELEMS, s));
+  }
+  TIMED(h, GPT2_SITE_LN_FWD, launch_layernorm_fwd(at, x, P + h->lay.lnfw, P + h->lay.lnfb, h->z,
+                                                  h->meanf, h->rstdf, B, C, s));
+  TIMED(h, GPT2_SITE_LMHEAD_FWD, launch_gemm(at, B, Vp, C, h->z, C, false, W(h, h->lay.wte), C,
+                                             false, EPI_STORE, DT_F32, epi(h->gen_logits, Vp), 0,
+                                             s));
+  return GPT2_OK;
+}
+
 float* state_ptr(gpt2* h, int which) {
   switch (which) {
     case GPT2_PARAMS: return h->params;
@@ -1068,6 +1135,49 @@ gpt2_status gpt2_generate(gpt2_t* h, const int32_t* d_prompt, int B, int T0, int
     HIPTRY(h, hipMemcpy2DAsync(h->gen_idx, (size_t)T * 4, d_out + (cur - T), L * 4, (size_t)T * 4,
                                B, hipMemcpyDeviceToDevice, s));
     gpt2_status st = run_forward(h, h->gen_idx, nullptr, B, T, false, h->gen_logits);
+    if (st != GPT2_OK) return st;
+    HIPTRY(h, launch_sample(h->gen_logits, Vp, B, Vp, temperature, top_k, d_uniform + step, n_new,
+                            d_out + cur, L, s));
+  }
+  return GPT2_OK;
+}
+
+gpt2_status gpt2_generate_cached(gpt2_t* h, const int32_t* d_prompt, int B, int T0, int n_new,
+                                 float temperature, int top_k, const float* d_uniform,
+                                 int32_t* d_out) {
+  if (!h || !d_prompt || !d_out || (n_new > 0 && !d_uniform)) return GPT2_E_ARG;
+  if (B < 1 || B > h->cfg.max_batch || T0 < 1 || n_new < 0)
+    return fail(h, GPT2_E_SHAPE, "need 1 <= B <= max_batch, T0 >= 1, n_new >= 0");
+  if (!(temperature > 0.f)) return fail(h, GPT2_E_ARG, "temperature must be > 0");
+  const int Vp = h->cfg.padded_vocab_size, bs = h->cfg.block_size;
+  if (bs > ATTN_DECODE_MAX_POS)
+    return fail(h, GPT2_E_ARG, "the key/value cache supports block_size <= 8192");
+  const long L = (long)T0 + n_new;  // row length of d_out
+  hipStream_t s = h->stream;
+  h->have_targets = false;
+  h->forward_done = false;
+  HIPTRY(h, hipMemcpy2DAsync(d_out, L * 4, d_prompt, (size_t)T0 * 4, (size_t)T0 * 4, B,
+                             hipMemcpyDeviceToDevice, s));
+  for (int step = 0; step < n_new; ++step) {
+    const long cur = T0 + step;  // tokens so far; the next one goes to position cur
+    gpt2_status st = GPT2_OK;
+    if (cur <= bs && step > 0) {
+      // the last drawn token at position cur - 1 against the cached ones
+      HIPTRY(h, hipMemcpy2DAsync(h->gen_idx, 4, d_out + (cur - 1), L * 4, 4, B,
+                                 hipMemcpyDeviceToDevice, s));
+      st = run_decode(h, h->gen_idx, B, (int)(cur - 1));
+    } else {
+      // the prompt (filling the cache), or a window that has shifted: the
+      // last block_size tokens at positions 0 .. T-1, recomputed whole
+      const int T = cur < bs ? (int)cur : bs;
+      HIPTRY(h, hipMemcpy2DAsync(h->gen_idx, (size_t)T * 4, d_out + (cur - T), L * 4,
+                                 (size_t)T * 4, B, hipMemcpyDeviceToDevice, s));
+      st = run_forward(h, h->gen_idx, nullptr, B, T, false, h->gen_logits);
+      if (st == GPT2_OK && step == 0 && cur <= bs)
+        for (int l = 0; l < h->cfg.n_layer; ++l)
+          HIPTRY(h, launch_kv_append(h->act, h->A[l].qkv, kv_slot(h, l), B, T, 0, bs,
+                                     h->cfg.n_embd, s));
+    }
     if (st != GPT2_OK) return st;
     HIPTRY(h, launch_sample(h->gen_logits, Vp, B, Vp, temperature, top_k, d_uniform + step, n_new,
                             d_out + cur, L, s));

@@ -689,6 +689,89 @@ __global__ __launch_bounds__(256) void attn_bwd_dkv_mfma(const bf16_t* __restric
 }
 
 // ===========================================================================
+// Decoding with a key/value cache: one new position per sequence.
+// ===========================================================================
+
+// The key and value parts of rows t of qkv ((B*T, 3C), sequence b at rows
+// b*T .. b*T+T-1) into the cache (B, bs, 2C) at positions pos0 + t.
+template <typename T>
+__global__ __launch_bounds__(256) void kv_append_kernel(const T* __restrict__ qkv,
+                                                        T* __restrict__ cache, int Tn, int pos0,
+                                                        int bs, int C, long rows) {
+  const long row = (long)blockIdx.x;
+  if (row >= rows) return;
+  const long b = row / Tn, t = row % Tn;
+  const T* src = qkv + row * 3L * C + C;
+  T* dst = cache + (b * bs + pos0 + t) * 2L * C;
+  for (int c = threadIdx.x; c < 2 * C; c += 256) dst[c] = src[c];
+}
+
+// Attention of the query of each (b, h) -- the single new position p -- over
+// the cached keys and values of positions 0 .. p (all visible: they precede
+// or are the query).  One workgroup per (b, h); fp32 arithmetic.  q is row b
+// of qkv (B, 3C); y row b of (B, C).
+template <typename T, int HD>
+__global__ __launch_bounds__(256) void attn_decode_kernel(const T* __restrict__ qkv,
+                                                          const T* __restrict__ cache,
+                                                          T* __restrict__ y, int p, int bs, int H,
+                                                          int C) {
+  extern __shared__ float dsh[];  // p+1 scores, then 256 reduction slots
+  float* sc = dsh;
+  float* red = dsh + ((p + 1 + 63) & ~63);
+  __shared__ float qs[HD];
+  const int bh = blockIdx.x, b = bh / H, h = bh % H, tid = threadIdx.x;
+  const float scale = 1.0f / sqrtf((float)HD);
+  if (tid < HD) qs[tid] = ldf(qkv + (long)b * 3 * C + h * HD + tid) * scale;
+  __syncthreads();
+  const T* kb = cache + (long)b * bs * 2 * C + h * HD;
+  const T* vb = kb + C;
+  float mx = -__builtin_inff();
+  for (int j = tid; j <= p; j += 256) {
+    const T* kr = kb + (long)j * 2 * C;
+    float s = 0.f;
+#pragma unroll 8
+    for (int d = 0; d < HD; ++d) s += qs[d] * ldf(kr + d);
+    sc[j] = s;
+    mx = fmaxf(mx, s);
+  }
+  red[tid] = mx;
+  __syncthreads();
+  for (int o = 128; o > 0; o >>= 1) {
+    if (tid < o) red[tid] = fmaxf(red[tid], red[tid + o]);
+    __syncthreads();
+  }
+  mx = red[0];
+  __syncthreads();
+  float sum = 0.f;
+  for (int j = tid; j <= p; j += 256) {
+    const float e = __expf(sc[j] - mx);
+    sc[j] = e;
+    sum += e;
+  }
+  red[tid] = sum;
+  __syncthreads();
+  for (int o = 128; o > 0; o >>= 1) {
+    if (tid < o) red[tid] += red[tid + o];
+    __syncthreads();
+  }
+  const float inv = 1.0f / red[0];
+  __syncthreads();
+  // O[d] = sum_j P_j V_j[d]: lanes of one group cover the HD dimensions,
+  // groups take every G-th position; the groups' sums meet in LDS
+  constexpr int G = 256 / HD;
+  const int d = tid % HD, g = tid / HD;
+  float acc = 0.f;
+  for (int j = g; j <= p; j += G) acc += sc[j] * ldf(vb + (long)j * 2 * C + d);
+  red[tid] = acc;
+  __syncthreads();
+  if (tid < HD) {
+    float o = 0.f;
+    for (int k = 0; k < G; ++k) o += red[k * HD + tid];
+    stf(y + (long)b * C + h * HD + tid, o * inv);
+  }
+}
+
+// ===========================================================================
 // launchers
 // ===========================================================================
 template <typename T>
@@ -752,4 +835,39 @@ hipError_t launch_attn_bwd(DType t, const void* qkv, const void* y, const float*
   }
   if ((hd != 32 && hd != 64) || bias_part) return hipErrorInvalidValue;
   return simt_bwd<float>(qkv, y, lse, dy, dqkv, dbuf, B, Tn, H, hd, s);
+}
+
+hipError_t launch_kv_append(DType t, const void* qkv, void* cache, int B, int Tn, int pos0, int bs,
+                            int C, hipStream_t s) {
+  const long rows = (long)B * Tn;
+  if (rows <= 0) return hipSuccess;
+  if (t == DT_BF16)
+    kv_append_kernel<bf16_t><<<(unsigned)rows, 256, 0, s>>>((const bf16_t*)qkv, (bf16_t*)cache,
+                                                            Tn, pos0, bs, C, rows);
+  else
+    kv_append_kernel<float><<<(unsigned)rows, 256, 0, s>>>((const float*)qkv, (float*)cache, Tn,
+                                                           pos0, bs, C, rows);
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_decode(DType t, const void* qkv, const void* cache, void* y, int B, int p,
+                              int bs, int H, int hd, hipStream_t s) {
+  if (p < 0 || p >= bs || p >= ATTN_DECODE_MAX_POS) return hipErrorInvalidValue;
+  const int C = H * hd;
+  const size_t lds = (size_t)(((p + 1 + 63) & ~63) + 256) * sizeof(float);
+  const unsigned g = (unsigned)(B * H);
+  if (t == DT_BF16) {
+    if (hd != 64) return hipErrorInvalidValue;
+    attn_decode_kernel<bf16_t, 64><<<g, 256, lds, s>>>((const bf16_t*)qkv, (const bf16_t*)cache,
+                                                       (bf16_t*)y, p, bs, H, C);
+  } else if (hd == 64) {
+    attn_decode_kernel<float, 64><<<g, 256, lds, s>>>((const float*)qkv, (const float*)cache,
+                                                      (float*)y, p, bs, H, C);
+  } else if (hd == 32) {
+    attn_decode_kernel<float, 32><<<g, 256, lds, s>>>((const float*)qkv, (const float*)cache,
+                                                      (float*)y, p, bs, H, C);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }

@@ -168,3 +168,13 @@ hipError_t launch_attn_fwd(DType t, const void* qkv, void* y, float* lse, int B,
 hipError_t launch_attn_bwd(DType t, const void* qkv, const void* y, const float* lse,
                            const void* dy, void* dqkv, float* dbuf, int B, int T, int H, int hd,
                            float* bias_part, hipStream_t s);
+
+// Key/value cache of the decoding path: per block (B, bs, 2C) [k | v] rows.
+// kv_append: the k, v parts of qkv rows (B*T, 3C) into positions pos0 .. pos0+T-1.
+hipError_t launch_kv_append(DType t, const void* qkv, void* cache, int B, int Tn, int pos0, int bs,
+                            int C, hipStream_t s);
+// attention of one new position p per sequence over the cached positions
+// 0 .. p: q from row b of qkv (B, 3C), output row b of y (B, C)
+constexpr int ATTN_DECODE_MAX_POS = 8192;  // scores of one (b, h) held in LDS (33 KB)
+hipError_t launch_attn_decode(DType t, const void* qkv, const void* cache, void* y, int B, int p,
+                              int bs, int H, int hd, hipStream_t s);

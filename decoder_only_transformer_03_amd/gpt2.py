@@ -71,6 +71,7 @@ def lib():
             "gpt2_forward_last": (i32, [vp, vp, i32, i32, vp]),
             "gpt2_sample": (i32, [vp, vp, ct.c_long, i32, i32, f32, i32, vp, vp]),
             "gpt2_generate": (i32, [vp, vp, i32, i32, i32, f32, i32, vp, vp]),
+            "gpt2_generate_cached": (i32, [vp, vp, i32, i32, i32, f32, i32, vp, vp]),
             "gpt2_get_loss": (i32, [vp, ct.POINTER(f32)]),
             "gpt2_zero_grad": (i32, [vp]),
             "gpt2_backward": (i32, [vp, f32]),
@@ -101,7 +102,8 @@ def lib():
 EXPORTED = ["gpt2_num_params", "gpt2_workspace_bytes", "gpt2_init", "gpt2_lr_at", "gpt2_set_params",
             "gpt2_get",
             "gpt2_set_state", "gpt2_get_step", "gpt2_set_step", "gpt2_forward", "gpt2_eval",
-            "gpt2_forward_last", "gpt2_sample", "gpt2_generate", "gpt2_get_loss",
+            "gpt2_forward_last", "gpt2_sample", "gpt2_generate", "gpt2_generate_cached",
+            "gpt2_get_loss",
             "gpt2_zero_grad", "gpt2_backward", "gpt2_adamw_step", "gpt2_get_grad_norm",
             "gpt2_sync", "gpt2_last_error", "gpt2_destroy", "gpt2_get_activation",
             "gpt2_timing_begin", "gpt2_timing_end", "gpt2_wgrad_layout",
@@ -249,6 +251,13 @@ class GPT2:
         B, T0 = prompt.shape
         self._check(lib().gpt2_generate(self.h, _ptr(prompt), B, T0, int(n_new), float(temperature),
                                         int(top_k), _ptr(uniforms), _ptr(out)))
+
+    def generate_cached(self, prompt, n_new, uniforms, out, temperature=1.0, top_k=0):
+        """generate with a key/value cache (same arguments and draws)."""
+        B, T0 = prompt.shape
+        self._check(lib().gpt2_generate_cached(self.h, _ptr(prompt), B, T0, int(n_new),
+                                               float(temperature), int(top_k), _ptr(uniforms),
+                                               _ptr(out)))
 
     def get_loss(self) -> float:
         loss = ct.c_float(0.0)

@@ -225,6 +225,23 @@ gpt2_status gpt2_sample(gpt2_t* h, const float* d_logits, long ld, int B, int V,
 gpt2_status gpt2_generate(gpt2_t* h, const int32_t* d_prompt, int B, int T0, int n_new,
                           float temperature, int top_k, const float* d_uniform, int32_t* d_out);
 
+/* gpt2_generate with a key/value cache ("GPT-2 from Scratch", A generation
+ * loop: recomputing the whole context for every new token is the quadratic
+ * cost a key/value cache removes).  Same arguments, the same draws up to the
+ * rounding of the products: the prompt's keys and values of every block are
+ * computed once, by one forward pass over (B, T0), and kept in the
+ * workspace; each new token then runs the blocks for its own position only,
+ * its attention reading the kept keys and values of the positions before it
+ * and adding its own.  Once a sequence has reached block_size tokens, every
+ * later step crops the window, which moves every position embedding, so
+ * those steps recompute the cropped window as gpt2_generate does (and a
+ * prompt longer than block_size is recomputed from the first step).
+ * GPT2_E_ARG if block_size > 8192.  Asynchronous like gpt2_generate;
+ * saved activations are not readable afterwards. */
+gpt2_status gpt2_generate_cached(gpt2_t* h, const int32_t* d_prompt, int B, int T0, int n_new,
+                                 float temperature, int top_k, const float* d_uniform,
+                                 int32_t* d_out);
+
 /* Loss of the last forward with targets; waits for the stream. */
 gpt2_status gpt2_get_loss(gpt2_t* h, float* h_loss);
 

@@ -214,3 +214,83 @@ def test_generate_same_with_fused_head_config(tiny):
         mm.generate(dev(prompt, torch.int32), n_new, dev(uni, torch.float32), o, 0.9, 30)
         outs.append(o.cpu().numpy())
     assert np.array_equal(outs[0], outs[1])
+
+
+@pytest.mark.parametrize("T0,n_new,temperature,top_k", [(60, 10, 0.8, 40), (3, 5, 1.0, 0),
+                                                        (70, 4, 1.2, 1), (2, 70, 1.0, 20),
+                                                        (5, 0, 1.0, 10)])
+def test_generate_cached_fp32(tiny, T0, n_new, temperature, top_k):
+    """gpt2_generate_cached: the prompt is copied; every drawn token is a
+    valid draw for the oracle's logits of its own context cropped to the last
+    block_size tokens -- decoded against the key/value cache while the
+    sequence is shorter than block_size (64), recomputed once the window
+    shifts (the first and fourth cases cross it, the third starts past it);
+    with no draw on a CDF boundary the tokens are those of gpt2_generate and
+    of the oracle's loop."""
+    d, flat, m = tiny
+    cfg = O.Config(**d)
+    B = 3
+    rng = np.random.default_rng(T0 * 17 + n_new)
+    prompt = rng.integers(0, 512, size=(B, T0)).astype(np.int32)
+    uni = synthetic.uniforms((B, max(n_new, 1)), seed=T0 + 3 * n_new)[:, :n_new]
+    out = torch.full((B, T0 + n_new), -7, dtype=torch.int32, device=DEV)
+    m.generate_cached(dev(prompt, torch.int32), n_new, dev(uni, torch.float32), out, temperature,
+                      top_k)
+    got = out.cpu().numpy()
+    assert np.array_equal(got[:, :T0], prompt)
+    exact = 0
+    for s in range(n_new):
+        ctx = got[:, :T0 + s][:, -cfg.block_size:]
+        lg = O.last_logits(flat, ctx, cfg)
+        exact += check_draws(got[:, T0 + s], lg, temperature, top_k, uni[:, s].astype(np.float64))
+    assert exact >= B * n_new - 1
+    if exact == B * n_new:
+        ref = O.generate(flat, prompt, n_new, temperature, top_k, uni.astype(np.float64), cfg)
+        assert np.array_equal(got, ref)
+        full = torch.zeros_like(out)
+        m.generate(dev(prompt, torch.int32), n_new, dev(uni, torch.float32), full, temperature,
+                   top_k)
+        assert np.array_equal(full.cpu().numpy(), got)
+    out2 = torch.zeros_like(out)
+    m.generate_cached(dev(prompt, torch.int32), n_new, dev(uni, torch.float32), out2, temperature,
+                      top_k)
+    assert torch.equal(out, out2)
+
+
+def test_generate_cached_bf16_124m():
+    """GPT-2 124M bf16, greedy: every token decoded against the cache is a
+    maximum of the oracle's logits of its context up to the bf16 tolerance,
+    and the tokens equal the recomputing loop's up to the first step where
+    the oracle's two best logits are within that tolerance of each other."""
+    d = synthetic.model_dims("gpt2-124m")
+    cfg = O.Config(**d)
+    flat = synthetic.init_params(d, seed=42)
+    B, T0, n_new = 2, 24, 12
+    m = G.GPT2(G.make_config(max_batch=B, precision="bf16", **d), device=DEV)
+    try:
+        m.set_params(flat)
+        idx, _ = synthetic.zipf_batch(B, T0, seed=78)
+        prompt = idx.astype(np.int32)
+        uni = synthetic.uniforms((B, n_new), seed=6)
+        outs = []
+        for fn in (m.generate_cached, m.generate):
+            o = torch.zeros((B, T0 + n_new), dtype=torch.int32, device=DEV)
+            fn(dev(prompt, torch.int32), n_new, dev(uni, torch.float32), o, 1.0, 1)
+            outs.append(o.cpu().numpy())
+    finally:
+        m.close()
+    cached, full = outs
+    assert np.array_equal(cached[:, :T0], prompt)
+    tol = None
+    for s in range(n_new):
+        lg = O.last_logits(flat, cached[:, :T0 + s], cfg).astype(np.float64)
+        tol = 2e-2 * np.max(np.abs(lg)) if tol is None else tol
+        top2 = np.sort(lg, axis=1)[:, -2:]
+        for b in range(B):
+            t = cached[b, T0 + s]
+            assert lg[b, t] >= top2[b, 1] - tol, (s, b)
+        if not np.array_equal(cached[:, :T0 + s + 1], full[:, :T0 + s + 1]):
+            # the loops may part only where the choice is within rounding
+            assert np.any(top2[:, 1] - top2[:, 0] < 2 * tol), s
+            break
+    print(f"\nbf16 124M cached greedy: {np.sum(cached == full)} of {cached.size} tokens equal")

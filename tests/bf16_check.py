@@ -49,6 +49,20 @@ bf16-stored output, and its rounding reaches dQ multiplied by the mean key.
 The key third of c_attn.bias has an analytically zero gradient (softmax is
 invariant to a per-row shift), so its computed value is rounding noise and
 its update is arbitrary: it is left out of every comparison.
+
+The rows of c_attn.weight are sums over positions t of d(q|k|v)[t, row] times
+the block's ln_1 output u1[t].  Write u1[t] as its sequence's mean plus the
+rest: the part of a row along the sequence means collects, per sequence, the
+plain sum of the row's bf16-rounded d(q|k|v) entries -- for the key rows that
+sum is exactly zero in exact arithmetic (sum_j dK_j = 0 for every query,
+since every row of dS sums to zero), so what a bf16 computation puts there is
+rounding noise alone, one random number per row and sequence.  Given the
+sequences' means (seq_means, from the exact oracle run), each row is split
+into that span and the rest: the rest is compared row by row as above, and
+the span part normwise over each third, within F_SPAN times the rounded
+oracle's.  On the CPU (stochastic rounding against round-to-nearest on a
+GPT-2 124M step) this brings the largest per-row ratio to the group median
+from 17.7 down to 3.8.
 """
 from __future__ import annotations
 
@@ -64,6 +78,22 @@ MAX_BELOW = 0.1       # largest fraction of elements under the floor at t = 1
 TOL_MOM = 2e-2        # per-tensor normwise error of m and v at t >= 2
 TOL_NORM = 2e-2       # relative error of the pre-clip gradient norm
 TOL_ADAMW = 1e-5      # the GPU's own gradients through the oracle's AdamW
+F_SPAN = 4.0          # c_attn.weight rows' part along the sequence means, per third
+
+
+def seq_means(cache):
+    """Per block, the per-sequence means of the ln_1 output of an oracle
+    forward cache: {block: (B, C)}."""
+    out = {}
+    for l, lc in enumerate(cache["layers"]):
+        u = np.asarray(lc["u1"], np.float64)
+        out[l] = u.reshape(cache["B"], cache["T"], -1).mean(axis=1)
+    return out
+
+
+def merge_seq_means(parts):
+    """seq_means of several micro-batches, stacked per block."""
+    return {l: np.concatenate([p[l] for p in parts]) for l in parts[0]}
 
 
 def tensor_slices(O, cfg):
@@ -90,10 +120,12 @@ def _normwise(a, b):
 
 def compare_step(O, cfg, *, p0, g_gpu, g_ref, g_emul, p_gpu, p_ref, norm_gpu, norm_ref, lr, wd,
                  t, m0=None, v0=None, m_gpu=None, m_ref=None, v_gpu=None, v_ref=None,
-                 beta1=0.9, beta2=0.95, eps=1e-8, clip=1.0, verbose=True):
+                 beta1=0.9, beta2=0.95, eps=1e-8, clip=1.0, seq_means=None, verbose=True):
     """Compares one bf16 step; returns (failures, stats).  p0, m0, v0: the
     state both sides started the step from (m0, v0 None: zeros, t = 1);
-    g_emul: the oracle's gradient of the same step with bf16 rounding."""
+    g_emul: the oracle's gradient of the same step with bf16 rounding;
+    seq_means: {block: (sequences, C)} from the exact oracle run (seq_means()),
+    or None to compare the c_attn.weight rows whole."""
     fails, stats = [], {}
     if abs(norm_gpu - norm_ref) > TOL_NORM * norm_ref:
         fails.append(f"pre-clip norm {norm_gpu} vs {norm_ref}")
@@ -127,12 +159,25 @@ def compare_step(O, cfg, *, p0, g_gpu, g_ref, g_emul, p_gpu, p_ref, norm_gpu, no
         if rows > 1:
             ga2, gr2, ge2 = ga.reshape(rows, -1), gr.reshape(rows, -1), ge.reshape(rows, -1)
             rn = np.linalg.norm(gr2, axis=1)
-            e_gpu = np.linalg.norm(ga2 - gr2, axis=1)
-            e_emul = np.linalg.norm(ge2 - gr2, axis=1)
+            da, de = ga2 - gr2, ge2 - gr2
+            groups = 3 if name.endswith("c_attn.weight") else 1
+            if groups == 3 and seq_means is not None:
+                # the part along the sequence means: normwise per third
+                blk = int(name.split(".")[1])
+                Q, _ = np.linalg.qr(np.asarray(seq_means[blk], np.float64).T)
+                for part, rs in zip("qkv", np.split(np.arange(rows), 3)):
+                    sa = np.linalg.norm(da[rs] @ Q)
+                    se = np.linalg.norm(de[rs] @ Q)
+                    bound = F_SPAN * se + 1e-3 * np.linalg.norm(gr2[rs])
+                    if sa > bound:
+                        fails.append(f"{name}: {part} rows along the sequence means, error "
+                                     f"{sa:.3e} > {bound:.3e} (rounded oracle {se:.3e})")
+                da, de = da - (da @ Q) @ Q.T, de - (de @ Q) @ Q.T
+            e_gpu = np.linalg.norm(da, axis=1)
+            e_emul = np.linalg.norm(de, axis=1)
             # a row's noise scale: its own rounded error, or the median over
             # its group of rows, whichever is larger (groups: the q, k, v
             # thirds of c_attn.weight, else the whole matrix)
-            groups = 3 if name.endswith("c_attn.weight") else 1
             typical = np.repeat([np.median(x) for x in np.split(e_emul, groups)], rows // groups)
             allowed = F_ROW * np.maximum(e_emul, typical) + ROW_SLACK * np.median(rn)
             ratio = e_gpu / np.maximum(allowed, 1e-30)

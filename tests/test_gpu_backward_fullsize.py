@@ -69,7 +69,7 @@ def oracle_step(d, flat, idx, tgt):
     loss, cache = O.forward(p, idx, tgt, cfg)
     g = O.backward(p, cache, cfg)
     out = dict(loss=float(loss), row_loss=cache["row_loss"].reshape(idx.shape), grads=g.copy(),
-               grads_emul=g_emul)
+               grads_emul=g_emul, seq_means=bf16_check.seq_means(cache))
     del cache
     out["norm"] = O.clip_and_adamw(p, g, np.zeros_like(p), np.zeros_like(p), 1, LR, B1, B2, EPS,
                                    WD, CLIP, cfg=cfg)
@@ -90,7 +90,7 @@ def compare(d, flat, g, r, keep, what):
     fails, _ = bf16_check.compare_step(
         O, O.Config(**d), p0=flat, g_gpu=g["grads"], g_ref=r["grads"], g_emul=r["grads_emul"],
         p_gpu=g["params"], p_ref=r["params"], norm_gpu=g["norm"], norm_ref=r["norm"], lr=LR,
-        wd=WD, t=1)
+        wd=WD, t=1, seq_means=r["seq_means"])
     assert not fails, fails
 
 

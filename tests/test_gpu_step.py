@@ -2,9 +2,11 @@
 through the C ABI, on the same seeded inputs.
 
 fp32 (tiny model, 2 layers, C=128, head 32, V=512; B=4, T=64 and ragged
-shapes): loss within 1e-4 relative; every gradient, parameter and AdamW
-moment tensor within 1e-3 max-relative (max |diff| / max |oracle| per tensor);
-activations within 1e-4.  The key third of c_attn.bias has an analytically
+shapes): loss within 1e-4 relative; every gradient and AdamW moment tensor
+within 1e-3 max-relative (max |diff| / max |oracle| per tensor); parameters
+within 1e-3 wherever the gradient fixes AdamW's first update (adam_floor),
+and everywhere equal to the oracle's AdamW on the GPU's own gradients
+within 1e-5; activations within 1e-4.  The key third of c_attn.bias has an analytically
 zero gradient (softmax is shift invariant per row), so its computed value is
 rounding noise on both sides and the step-1 AdamW update of those elements is
 noise/(|noise| + eps): it is excluded from parameter comparisons and checked
@@ -158,11 +160,59 @@ def test_fp32_tiny_step_matches_oracle(B, T, hc):
     qb = np.abs(r["grads"][np.roll(kb, -d["n_embd"])]).max()
     assert np.abs(g["grads"][kb]).max() <= 1e-5 * max(qb, 1e-12) + 1e-9
     # after one clipped AdamW step
-    for key in ("params", "m", "v"):
+    check_fp32_first_step(cfg, flat, g, r, kb)
+
+
+def adam_floor(cfg, g_ref, skip):
+    """Elements whose first AdamW update is fixed by the gradient at fp32
+    precision.  Step 1 moves a parameter by lr * g / (|g| + eps) (bias
+    correction makes m_hat = g, v_hat = g^2), whose slope in g is
+    lr * eps / (|g| + eps)^2: 1e8 lr at g = 0.  A gradient difference of
+    1e-5 of its tensor's largest element (the fp32 rounding of a sum over
+    positions is far below that) moves the parameter by at most 1e-3 lr
+    where |g| >= sqrt(eps * 1e-5 * max|g| / 1e-3).  Returns a boolean mask
+    over the flat vector (False on `skip`)."""
+    det = np.zeros(g_ref.size, bool)
+    off = 0
+    for name, shape in O.param_specs(cfg):
+        n = int(np.prod(shape))
+        x = np.abs(g_ref[off:off + n].astype(np.float64))
+        det[off:off + n] = x >= math.sqrt(EPS * 1e-5 * x.max() / 1e-3)
+        off += n
+    return det & ~skip
+
+
+def check_fp32_first_step(cfg, flat, g, r, kb):
+    """Parameters, m and v after step 1 ("AdamW, and weight decay on matrices
+    only").  m and v are linear and quadratic in g and are compared
+    everywhere (1e-3 max-relative).  Parameters: within 1e-3 over the
+    elements adam_floor keeps; the others within 2 lr, the width of the
+    update's range; and everywhere the GPU's parameters equal the oracle's
+    clip and AdamW applied to the GPU's own gradients (1e-5), which checks
+    the update arithmetic on every element."""
+    for key in ("m", "v"):
         e = per_tensor(cfg, g[key], r[key], skip=kb)
         w = max(e, key=e.get)
         print(f"{key}: worst {w} {e[w]:.2e}")
         assert e[w] < 1e-3, (key, w, e[w])
+    det = adam_floor(cfg, r["grads"], kb)
+    e = per_tensor(cfg, g["params"], r["params"], skip=~det)
+    w = max(e, key=e.get)
+    und = ~det & ~kb
+    dmax = float(np.max(np.abs(g["params"][und] - r["params"][und]), initial=0.0))
+    print(f"params: worst {w} {e[w]:.2e} over {det.sum()} elements; "
+          f"{und.sum()} below the floor, largest difference {dmax / LR:.2e} lr")
+    assert e[w] < 1e-3, ("params", w, e[w])
+    assert dmax <= 2.0 * LR * 1.001
+    p_own = flat.astype(np.float32).copy()
+    m0 = np.zeros_like(p_own)
+    v0 = np.zeros_like(p_own)
+    O.clip_and_adamw(p_own, g["grads"].astype(np.float32).copy(), m0, v0, 1, LR, B1, B2, EPS,
+                     WD, CLIP, cfg=cfg)
+    e = per_tensor(cfg, g["params"], p_own)
+    w = max(e, key=e.get)
+    print(f"params vs AdamW on the GPU's own gradients: worst {w} {e[w]:.2e}")
+    assert e[w] < 1e-5, ("own", w, e[w])
 
 
 def test_fp32_embedding_backward_many_skewed_rows():
@@ -450,7 +500,7 @@ def check_bf16_step(d, flat, g, r, lr=LR, wd=WD):
     fails, _ = bf16_check.compare_step(
         O, O.Config(**d), p0=flat, g_gpu=g["grads"], g_ref=r["grads"], g_emul=r["grads_emul"],
         p_gpu=g["params"], p_ref=r["params"], norm_gpu=g["norm"], norm_ref=r["norm"], lr=lr,
-        wd=wd, t=1)
+        wd=wd, t=1, seq_means=bf16_check.seq_means(r["cache"]))
     assert not fails, fails
 
 

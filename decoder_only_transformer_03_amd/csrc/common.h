@@ -74,28 +74,31 @@ __device__ __forceinline__ double wave_sum_d(double v) {
 enum : int { ERRF_IDX = 1, ERRF_TARGET = 2 };
 
 // GELU, tanh form: 0.5 x (1 + tanh(u)) with u = sqrt(2/pi) (x + 0.044715 x^3).
-// Evaluated through the identity 0.5 (1 + tanh(u)) = 1 / (1 + exp(-2u)), with
-// the hardware exp and reciprocal (a few ulp in fp32).
-__device__ __forceinline__ float gelu_sig_f(float x, float* du) {
+// Evaluated through the identity 0.5 (1 + tanh(u)) = 1 / (1 + exp(-2u)) =: s,
+// with the hardware exp2 and reciprocal (a few ulp in fp32); -2u log2(e) is
+// formed as x (k0 + k1 x^2) with the constants folded.
+__device__ __forceinline__ float gelu_sig_f(float x, float x2) {
   const float a = 0.7978845608028654f;  // sqrt(2/pi)
   const float c = 0.044715f;
-  float x2 = x * x;
-  float u = a * x * (1.0f + c * x2);
-  float s = __builtin_amdgcn_rcpf(1.0f + __expf(-2.0f * u));
-  if (du) *du = a * (1.0f + 3.0f * c * x2);
-  return s;
+  const float k0 = -2.0f * 1.4426950408889634f * a, k1 = k0 * c;
+  return __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(x * fmaf(x2, k1, k0)));
 }
-__device__ __forceinline__ float gelu_tanh_f(float x) { return x * gelu_sig_f(x, nullptr); }
-// d/dx: s + 2 x s (1 - s) u'(x)
+__device__ __forceinline__ float gelu_tanh_f(float x) { return x * gelu_sig_f(x, x * x); }
+// d/dx = s + 2 x s (1 - s) u'(x), u'(x) = sqrt(2/pi) (1 + 3 * 0.044715 x^2)
+__device__ __forceinline__ float gelu_grad_from_sig(float x, float x2, float s) {
+  const float a = 0.7978845608028654f;
+  const float c = 0.044715f;
+  const float q = x * fmaf(x2, 6.0f * a * c, 2.0f * a);  // 2 x u'(x)
+  return fmaf(q, fmaf(-s, s, s), s);                      // s + q s (1 - s)
+}
 __device__ __forceinline__ float gelu_tanh_grad_f(float x) {
-  float du;
-  float s = gelu_sig_f(x, &du);
-  return s + 2.0f * x * s * (1.0f - s) * du;
+  const float x2 = x * x;
+  return gelu_grad_from_sig(x, x2, gelu_sig_f(x, x2));
 }
 // Both at once (one exponential): returns gelu(x), stores gelu'(x).
 __device__ __forceinline__ float gelu_tanh_and_grad_f(float x, float* grad) {
-  float du;
-  float s = gelu_sig_f(x, &du);
-  *grad = s + 2.0f * x * s * (1.0f - s) * du;
+  const float x2 = x * x;
+  const float s = gelu_sig_f(x, x2);
+  *grad = gelu_grad_from_sig(x, x2, s);
   return x * s;
 }

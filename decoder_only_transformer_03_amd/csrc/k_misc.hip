@@ -666,7 +666,12 @@ template <> struct Row8<float> {
 // exponentials over the workgroup, and overwritten with
 //   d(loss)/d(logits) = (softmax - onehot(target)) / n_valid   (0 if ignored).
 // Padded vocabulary columns take part like real ones.
+// The exponentials run on exp2 with the scalings folded into one fma per
+// element: exp(x - M) = 2^(x log2e - M log2e), and softmax / n_valid =
+// 2^(x log2e - (lse log2e + log2 n_valid)).  Only the thread that holds the
+// target's chunk forms (softmax - 1) / n_valid, for that one element.
 constexpr int XENT_NT = 512, XENT_KPT = 13;  // rows up to 8 * 512 * 13 = 53248 wide
+constexpr float XENT_LOG2E = 1.4426950408889634f;
 template <typename T, bool GRAD>
 __global__ __launch_bounds__(XENT_NT) void xent_fused_kernel(T* __restrict__ logits,
                                                              const int32_t* __restrict__ targets,
@@ -681,6 +686,18 @@ __global__ __launch_bounds__(XENT_NT) void xent_fused_kernel(T* __restrict__ log
   if (tgt < 0 || tgt >= Vp) tgt = -1;  // out-of-range already flagged by count_valid
   const float xt = valid && tgt >= 0 ? ldf(lr + tgt) : 0.f;
   const int nchunks = Vp >> 3, lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int nv = *n_valid;
+  if (GRAD && !(valid && nv > 0)) {
+    // an ignored position (or none valid): its row of d(logits) is zero
+    float z[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < XENT_KPT; ++i) {
+      const int ch = threadIdx.x + i * XENT_NT;
+      if (ch < nchunks) Row8<T>::store(lr + ch * 8, z);
+    }
+    if (threadIdx.x == 0) row_loss[row] = 0.f;
+    return;
+  }
   Row8<T> v[XENT_KPT];
 #pragma unroll
   for (int i = 0; i < XENT_KPT; ++i) {
@@ -703,12 +720,13 @@ __global__ __launch_bounds__(XENT_NT) void xent_fused_kernel(T* __restrict__ log
   float M = red[0][0];
 #pragma unroll
   for (int i = 1; i < NW; ++i) M = fmaxf(M, red[0][i]);
+  const float mb = -M * XENT_LOG2E;
   float sum = 0.f;
 #pragma unroll
   for (int i = 0; i < XENT_KPT; ++i)
     if (threadIdx.x + i * XENT_NT < nchunks)
 #pragma unroll
-      for (int j = 0; j < 8; ++j) sum += __expf(v[i].get(j) - M);
+      for (int j = 0; j < 8; ++j) sum += __builtin_amdgcn_exp2f(fmaf(v[i].get(j), XENT_LOG2E, mb));
   sum = wave_sum(sum);
   if constexpr (sizeof(T) == 2) {
     // keep only the packed row live across the reduction (the float copies
@@ -722,21 +740,23 @@ __global__ __launch_bounds__(XENT_NT) void xent_fused_kernel(T* __restrict__ log
 #pragma unroll
   for (int i = 0; i < NW; ++i) S += red[1][i];
   const float lse = M + __logf(S);
-  const int nv = *n_valid;
-  const float scale = valid && nv > 0 ? 1.0f / (float)nv : 0.f;
-  if constexpr (GRAD)
+  if constexpr (GRAD) {
+    const float scale = 1.0f / (float)nv;
+    const float pb = -(lse * XENT_LOG2E + __log2f((float)nv));
 #pragma unroll
-  for (int i = 0; i < XENT_KPT; ++i) {
-    const int ch = threadIdx.x + i * XENT_NT;
-    if (ch < nchunks) {
-      float o[8];
+    for (int i = 0; i < XENT_KPT; ++i) {
+      const int ch = threadIdx.x + i * XENT_NT;
+      if (ch < nchunks) {
+        float o[8];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float p = __expf(v[i].get(j) - lse);
-        o[j] = (p - (ch * 8 + j == tgt ? 1.0f : 0.0f)) * scale;
+        for (int j = 0; j < 8; ++j) o[j] = __builtin_amdgcn_exp2f(fmaf(v[i].get(j), XENT_LOG2E, pb));
+        Row8<T>::store(lr + ch * 8, o);
       }
-      Row8<T>::store(lr + ch * 8, o);
     }
+    // the target's element, rewritten by the thread that stored its chunk
+    // (its two stores reach memory in program order)
+    if (tgt >= 0 && (tgt >> 3) % XENT_NT == (int)threadIdx.x)
+      stf(lr + tgt, (__expf(xt - lse) - 1.0f) * scale);
   }
   if (threadIdx.x == 0) row_loss[row] = valid ? lse - xt : 0.f;
 }

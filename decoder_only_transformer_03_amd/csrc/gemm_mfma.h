@@ -20,6 +20,8 @@
 // the "column" operand the A tile (m), so each lane's accumulator holds four
 // consecutive n of one m: the epilogue writes 4 consecutive columns per lane.
 #pragma once
+#include <type_traits>
+
 #include "kernels.h"
 
 namespace gemm_mfma {
@@ -255,6 +257,37 @@ template <int R, int NT> struct Loader<R, 1, NT> : LoaderT<R, NT> {};
 template <int R, int NT> struct Loader<R, 2, NT> : LoaderD<R, NT> {};
 template <int R, int NT> struct Loader<R, 3, NT> : LoaderDT<R, NT> {};
 
+// fp32 epilogue inputs loaded ahead per 32-row round: as many groups of
+// eight as fit the registers beside the accumulators in every variant
+constexpr int EPI_NPRE32 = 2;
+
+// Eight consecutive elements of an epilogue input held as loaded (bf16 stays
+// packed), so the load can be issued well before its values are needed.
+template <typename T> struct In8;
+template <> struct In8<float> {
+  float4 a, b;
+  __device__ __forceinline__ void load(const float* p) {
+    a = reinterpret_cast<const float4*>(p)[0];
+    b = reinterpret_cast<const float4*>(p)[1];
+  }
+  __device__ __forceinline__ void get(float v[8]) const {
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  }
+};
+template <> struct In8<bf16_t> {
+  uint4 a;
+  __device__ __forceinline__ void load(const bf16_t* p) { a = *reinterpret_cast<const uint4*>(p); }
+  __device__ __forceinline__ void get(float v[8]) const {
+    const uint32_t w[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = __uint_as_float(w[i] << 16);
+      v[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u);
+    }
+  }
+};
+
 // Epilogue of one output tile, staged through LDS so that global memory sees
 // whole row segments.  acc[sn][sm][4i + j] is C[m][n] with m = sm*32 +
 // lane%32 and n = sn*32 + 8i + 4(lane/32) + j inside the wavefront's
@@ -310,6 +343,28 @@ __device__ __forceinline__ void tile_epilogue(const EpiArgs& e, const f32x16_t (
         dls[r8] = m < M ? e.lse[m] : 0.f;
       }
     }
+    // inputs of the elementwise epilogue for the round's row groups, issued
+    // before the LDS round trip so that their latencies overlap instead of
+    // each group's load, wait and store running in turn: bf16 inputs for all
+    // four groups, fp32 ones for the first EPI_NPRE32 (addresses clamped to
+    // row M-1 and column 0 where the row or the lane's columns lie past the
+    // matrix; those values are not used)
+    constexpr bool PRE = EPI == EPI_RESID || EPI == EPI_ACCUM || EPI == EPI_GELU_BWD;
+    using PreT = std::conditional_t<EPI == EPI_GELU_BWD, TO, float>;
+    constexpr int NPRE = !PRE ? 0 : sizeof(PreT) == 2 ? 4 : EPI_NPRE32;
+    [[maybe_unused]] In8<PreT> pre[4];
+    if constexpr (PRE) {
+#pragma unroll
+      for (int r8 = 0; r8 < NPRE; ++r8) {
+        const long m = mw + sm * 32 + r8 * 8 + (lane >> 3);
+        const long mc = m < M ? m : M - 1;
+        const long nc = ncol ? nl : 0;
+        if constexpr (EPI == EPI_RESID) pre[r8].load(e.resid + mc * e.ldr + nc);
+        else if constexpr (EPI == EPI_ACCUM)
+          pre[r8].load(reinterpret_cast<const float*>(e.out) + mc * e.ldo + nc);
+        else pre[r8].load(reinterpret_cast<const TO*>(e.aux) + mc * e.ldx + nc);
+      }
+    }
     // (1) fragments -> round buffer (row = lane%32, one 16-byte chunk each)
     {
       const int row = lane & 31;
@@ -360,8 +415,12 @@ __device__ __forceinline__ void tile_epilogue(const EpiArgs& e, const f32x16_t (
           st4(reinterpret_cast<TO*>(e.out2) + m * e.ldo + nl + 4, v + 4);
         } else if constexpr (EPI == EPI_RESID) {
           float x[8];
-          ld4(e.resid + m * e.ldr + nl, x);
-          ld4(e.resid + m * e.ldr + nl + 4, x + 4);
+          if (r8 < NPRE) {
+            pre[r8].get(x);
+          } else {
+            ld4(e.resid + m * e.ldr + nl, x);
+            ld4(e.resid + m * e.ldr + nl + 4, x + 4);
+          }
 #pragma unroll
           for (int j = 0; j < 8; ++j) v[j] += x[j];
           st4(reinterpret_cast<float*>(e.out) + m * e.ldo + nl, v);
@@ -369,8 +428,12 @@ __device__ __forceinline__ void tile_epilogue(const EpiArgs& e, const f32x16_t (
         } else if constexpr (EPI == EPI_ACCUM) {
           float* o = reinterpret_cast<float*>(e.out) + m * e.ldo + nl;
           float x[8];
-          ld4(o, x);
-          ld4(o + 4, x + 4);
+          if (r8 < NPRE) {
+            pre[r8].get(x);
+          } else {
+            ld4(o, x);
+            ld4(o + 4, x + 4);
+          }
 #pragma unroll
           for (int j = 0; j < 8; ++j) v[j] += x[j];
           st4(o, v);
@@ -385,8 +448,12 @@ __device__ __forceinline__ void tile_epilogue(const EpiArgs& e, const f32x16_t (
           st4(o + 4, v + 4);
         } else if constexpr (EPI == EPI_GELU_BWD) {
           float dg[8];
-          ld4(reinterpret_cast<const TO*>(e.aux) + m * e.ldx + nl, dg);
-          ld4(reinterpret_cast<const TO*>(e.aux) + m * e.ldx + nl + 4, dg + 4);
+          if (r8 < NPRE) {
+            pre[r8].get(dg);
+          } else {
+            ld4(reinterpret_cast<const TO*>(e.aux) + m * e.ldx + nl, dg);
+            ld4(reinterpret_cast<const TO*>(e.aux) + m * e.ldx + nl + 4, dg + 4);
+          }
 #pragma unroll
           for (int j = 0; j < 8; ++j) {
             v[j] *= dg[j];

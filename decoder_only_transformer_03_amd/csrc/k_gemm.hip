@@ -265,6 +265,108 @@ __global__ __launch_bounds__(256) void splitk_epi_kernel(const float* __restrict
   epi_apply4<EPI, TO>(e, m, n, c, 0);
 }
 
+// Few rows (M <= 16: a decoding step's batch): C = A B^T with A (M x K) and
+// B (N x K) both k-contiguous bf16.  The work is streaming B once, so each
+// workgroup owns 16 output columns and splits K over its 16 wavefronts, each a
+// contiguous range of 32-deep chunks whose loads are all issued before its
+// matrix products (v_mfma_f32_16x16x32_bf16: lane l supplies row l%16 of A
+// and of B at contraction slots 8(l/16) .. +7; rows of A past M are zeros,
+// columns past N read column N-1 and are dropped).  The 16 partial 16 x 16
+// blocks are added in a fixed order through LDS and 64 threads apply the
+// epilogue to four columns each.
+constexpr int SKINNY_M = 16, SKINNY_WAVES = 16, SKINNY_BATCH = 8;
+template <int EPI, typename TO>
+__global__ __launch_bounds__(SKINNY_WAVES * 64) void gemm_skinny_kernel(
+    int M, int N, int K, const bf16_t* __restrict__ A, long lda, const bf16_t* __restrict__ B,
+    long ldb, EpiArgs e) {
+  __shared__ float red[SKINNY_WAVES][SKINNY_M * 16];
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int n0 = blockIdx.x * 16;
+  const int r = lane & 15, kq = 8 * (lane >> 4);
+  const bool arow = r < M;
+  const int bn = n0 + r < N ? n0 + r : N - 1;
+  const bf16_t* ap = A + (long)(arow ? r : 0) * lda + kq;
+  const bf16_t* bp = B + (long)bn * ldb + kq;
+  const int nk = K / 32;
+  const int c0 = (w * nk) / SKINNY_WAVES, c1 = ((w + 1) * nk) / SKINNY_WAVES;
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  for (int cb = c0; cb < c1; cb += SKINNY_BATCH) {
+    bf16x8_t af[SKINNY_BATCH], bfv[SKINNY_BATCH];
+#pragma unroll
+    for (int j = 0; j < SKINNY_BATCH; ++j) {
+      if (cb + j < c1) {
+        const long k = (long)(cb + j) * 32;
+        af[j] = arow ? *reinterpret_cast<const bf16x8_t*>(ap + k) : bf16x8_t{};
+        bfv[j] = *reinterpret_cast<const bf16x8_t*>(bp + k);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < SKINNY_BATCH; ++j)
+      if (cb + j < c1) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[j], bfv[j], acc, 0, 0, 0);
+  }
+  // lane l holds rows 4(l/16) .. +3 of column l%16
+#pragma unroll
+  for (int i = 0; i < 4; ++i) red[w][(4 * (lane >> 4) + i) * 16 + r] = acc[i];
+  __syncthreads();
+  if (tid < SKINNY_M * 4) {
+    const int m = tid >> 2, cl = 4 * (tid & 3);
+    const int n = n0 + cl;
+    if (m < M && n < N) {
+      float c[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        float t = red[0][m * 16 + cl + j];
+        for (int q = 1; q < SKINNY_WAVES; ++q) t += red[q][m * 16 + cl + j];
+        c[j] = t;
+      }
+      epi_apply4<EPI, TO>(e, m, n, c, 0);
+    }
+  }
+}
+
+// Whether the few-rows kernel takes this product (bf16, C = A B^T with both
+// operands k-contiguous, M <= 16, K a multiple of 32, an elementwise epilogue).
+bool skinny_ok(DType in_t, int M, int K, bool a_t, bool b_t, int epi) {
+  return in_t == DT_BF16 && !a_t && !b_t && M >= 1 && M <= SKINNY_M && K % 32 == 0 &&
+         (epi == EPI_STORE || epi == EPI_BIAS || epi == EPI_BIAS_GELU || epi == EPI_RESID ||
+          epi == EPI_ACCUM);
+}
+
+hipError_t launch_gemm_skinny(int M, int N, int K, const bf16_t* A, long lda, const bf16_t* B,
+                              long ldb, int epi, DType out_t, const EpiArgs& e, hipStream_t s) {
+  const unsigned grid = (unsigned)((N + 15) / 16);
+  const int nt = SKINNY_WAVES * 64;
+  switch (epi) {
+    case EPI_STORE:
+      if (out_t == DT_BF16)
+        gemm_skinny_kernel<EPI_STORE, bf16_t><<<grid, nt, 0, s>>>(M, N, K, A, lda, B, ldb, e);
+      else
+        gemm_skinny_kernel<EPI_STORE, float><<<grid, nt, 0, s>>>(M, N, K, A, lda, B, ldb, e);
+      break;
+    case EPI_BIAS:
+      if (out_t == DT_BF16)
+        gemm_skinny_kernel<EPI_BIAS, bf16_t><<<grid, nt, 0, s>>>(M, N, K, A, lda, B, ldb, e);
+      else
+        gemm_skinny_kernel<EPI_BIAS, float><<<grid, nt, 0, s>>>(M, N, K, A, lda, B, ldb, e);
+      break;
+    case EPI_BIAS_GELU:
+      if (out_t == DT_BF16)
+        gemm_skinny_kernel<EPI_BIAS_GELU, bf16_t><<<grid, nt, 0, s>>>(M, N, K, A, lda, B, ldb, e);
+      else
+        gemm_skinny_kernel<EPI_BIAS_GELU, float><<<grid, nt, 0, s>>>(M, N, K, A, lda, B, ldb, e);
+      break;
+    case EPI_RESID:
+      gemm_skinny_kernel<EPI_RESID, float><<<grid, nt, 0, s>>>(M, N, K, A, lda, B, ldb, e);
+      break;
+    case EPI_ACCUM:
+      gemm_skinny_kernel<EPI_ACCUM, float><<<grid, nt, 0, s>>>(M, N, K, A, lda, B, ldb, e);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_gemm_fill(DType in_t, int M, int N, int K, const void* A, long lda, bool a_t,
                             const void* B, long ldb, bool b_t, int epi, DType out_t,
                             const EpiArgs& e, float* part, long part_elems, hipStream_t s) {
@@ -272,6 +374,8 @@ hipError_t launch_gemm_fill(DType in_t, int M, int N, int K, const void* A, long
   // sampling loop's forward passes) and a deep enough contraction: K-slices
   // into fp32 scratch, then the epilogue over their sum.
   const bool kinds = epi == EPI_STORE || epi == EPI_BIAS || epi == EPI_BIAS_GELU || epi == EPI_RESID;
+  if (skinny_ok(in_t, M, K, a_t, b_t, epi))
+    return launch_gemm(in_t, M, N, K, A, lda, a_t, B, ldb, b_t, epi, out_t, e, 1, s);
   if (in_t == DT_BF16 && kinds && part && K % 64 == 0 && N % 4 == 0) {
     const long slots = gemm_slots();
     const long tiles = (long)((M + 255) / 256) * ((N + 255) / 256);
@@ -338,6 +442,9 @@ hipError_t launch_gemm(DType in_t, int M, int N, int K, const void* A, long lda,
   if ((a_t && M % 8) || (b_t && N % 8)) return hipErrorInvalidValue;
   const bf16_t* a = (const bf16_t*)A;
   const bf16_t* b = (const bf16_t*)B;
+  if (skinny_ok(in_t, M, K, a_t, b_t, epi) && (epi != EPI_RESID || out_t == DT_F32) &&
+      (epi != EPI_ACCUM || out_t == DT_F32))
+    return launch_gemm_skinny(M, N, K, a, lda, b, ldb, epi, out_t, e, s);
   if (!a_t && !b_t)
     return gemm_mfma::dispatch<false, false>(M, N, K, a, lda, b, ldb, epi, out_t, e, split_k, s);
   if (!a_t && b_t)

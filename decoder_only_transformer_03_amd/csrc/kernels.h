@@ -174,7 +174,8 @@ hipError_t launch_attn_bwd(DType t, const void* qkv, const void* y, const float*
 hipError_t launch_kv_append(DType t, const void* qkv, void* cache, int B, int Tn, int pos0, int bs,
                             int C, hipStream_t s);
 // attention of one new position p per sequence over the cached positions
-// 0 .. p: q from row b of qkv (B, 3C), output row b of y (B, C)
-constexpr int ATTN_DECODE_MAX_POS = 8192;  // scores of one (b, h) held in LDS (33 KB)
-hipError_t launch_attn_decode(DType t, const void* qkv, const void* cache, void* y, int B, int p,
-                              int bs, int H, int hd, hipStream_t s);
+// 0 .. p: appends position p's key and value (from row b of qkv (B, 3C)) to
+// the cache, then attends with q from that row; output row b of y (B, C)
+constexpr int ATTN_DECODE_MAX_POS = 8192;  // fp32 path: scores of one (b, h) in LDS (33 KB)
+hipError_t launch_attn_decode(DType t, const void* qkv, void* cache, void* y, int B, int p, int bs,
+                              int H, int hd, hipStream_t s);

@@ -59,6 +59,31 @@ gpt2_status gpt2_op_gemm(int dtype, int M, int N, int K, const void* A, long lda
   return r == hipSuccess ? GPT2_OK : GPT2_E_HIP;
 }
 
+gpt2_status gpt2_op_gemm_epi(int M, int N, int K, const void* A, long lda, const void* B, long ldb,
+                             int epi, const float* bias, const float* R, long ldr, void* C,
+                             void* C2, long ldc, int out_dtype, void* hip_stream) {
+  if (!A || !B || !C || M < 0 || N < 0 || K < 0 || epi < 0 || epi > 2) return GPT2_E_ARG;
+  if (out_dtype != (epi == 2 ? GPT2_FP32 : GPT2_BF16)) return GPT2_E_ARG;
+  if (epi == 1 && !C2) return GPT2_E_ARG;
+  if (epi == 2 && (!R || ldr % 4)) return GPT2_E_ARG;
+  if (ldc % 8 || K % 8) return GPT2_E_ARG;
+  EpiArgs e;
+  std::memset(&e, 0, sizeof(e));
+  e.out = C;
+  e.out2 = C2;
+  e.ldo = ldc;
+  e.alpha = 1.f;
+  e.bias = bias;
+  e.resid = R;
+  e.ldr = ldr;
+  const int kind = epi == 0 ? EPI_BIAS : epi == 1 ? EPI_BIAS_GELU : EPI_RESID;
+  hipError_t r = launch_gemm(DT_BF16, M, N, K, A, lda, false, B, ldb, false, kind,
+                             out_dtype == GPT2_BF16 ? DT_BF16 : DT_F32, e, 1,
+                             reinterpret_cast<hipStream_t>(hip_stream));
+  if (r == hipErrorInvalidValue) return GPT2_E_ARG;
+  return r == hipSuccess ? GPT2_OK : GPT2_E_HIP;
+}
+
 gpt2_status gpt2_op_attention_fwd(int dtype, const void* qkv, void* y, float* lse, int B, int T,
                                   int H, int hd, void* hip_stream) {
   if (!qkv || !y || !lse || B < 1 || T < 1 || H < 1) return GPT2_E_ARG;

@@ -86,6 +86,8 @@ def lib():
             "gpt2_wgrad_layout": (i32, [vp, ct.POINTER(i64), ct.POINTER(i64), ct.POINTER(i64)]),
             "gpt2_op_gemm": (i32, [i32, i32, i32, i32, vp, ct.c_long, i32, vp, ct.c_long, i32, vp,
                                    ct.c_long, f32, i32, i32, vp]),
+            "gpt2_op_gemm_epi": (i32, [i32, i32, i32, vp, ct.c_long, vp, ct.c_long, i32, vp, vp,
+                                       ct.c_long, vp, vp, ct.c_long, i32, vp]),
             "gpt2_op_attention_fwd": (i32, [i32, vp, vp, vp, i32, i32, i32, i32, vp]),
             "gpt2_op_attention_bwd": (i32, [i32, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, vp]),
             "gpt2_op_attention_bwd_noalloc": (i32, [i32, vp, vp, vp, vp, vp, i32, i32, i32, i32,
@@ -107,7 +109,7 @@ EXPORTED = ["gpt2_num_params", "gpt2_workspace_bytes", "gpt2_init", "gpt2_lr_at"
             "gpt2_zero_grad", "gpt2_backward", "gpt2_adamw_step", "gpt2_get_grad_norm",
             "gpt2_sync", "gpt2_last_error", "gpt2_destroy", "gpt2_get_activation",
             "gpt2_timing_begin", "gpt2_timing_end", "gpt2_wgrad_layout",
-            "gpt2_op_gemm", "gpt2_op_attention_fwd", "gpt2_op_attention_bwd",
+            "gpt2_op_gemm", "gpt2_op_gemm_epi", "gpt2_op_attention_fwd", "gpt2_op_attention_bwd",
             "gpt2_op_attention_bwd_noalloc"]
 
 
@@ -330,6 +332,14 @@ def gpt2_op_gemm(dtype, M, N, K, A, lda, a_trans, B, ldb, b_trans, C, ldc, alpha
     _st(lib().gpt2_op_gemm(dtype, M, N, K, _ptr(A), lda, int(a_trans), _ptr(B), ldb, int(b_trans),
                            _ptr(C), ldc, alpha, mode, split_k,
                            stream.cuda_stream if stream is not None else None), "gpt2_op_gemm")
+
+
+def gpt2_op_gemm_epi(M, N, K, A, lda, B, ldb, epi, bias, R, ldr, C, C2, ldc, out_dtype,
+                     stream=None):
+    _st(lib().gpt2_op_gemm_epi(M, N, K, _ptr(A), lda, _ptr(B), ldb, epi, _ptr(bias), _ptr(R), ldr,
+                               _ptr(C), _ptr(C2), ldc, out_dtype,
+                               stream.cuda_stream if stream is not None else None),
+        "gpt2_op_gemm_epi")
 
 
 def gpt2_op_attention_fwd(dtype, qkv, y, lse, B, T, H, hd, stream=None):

@@ -34,6 +34,23 @@ gpt2_status gpt2_op_gemm(int dtype, int M, int N, int K, const void* A, long lda
                          const void* B, long ldb, int b_trans, float* C, long ldc, float alpha,
                          int mode, int split_k, void* hip_stream);
 
+/* A linear layer's forward product with its fused epilogue ("GPT-2 from
+ * Scratch": nn.Linear with bias; The MLP and GPT-2's GELU; The Block:
+ * pre-LN and residuals), bf16 operands: h[m][n] = sum_k A[m*lda + k] B[n*ldb
+ * + k] + bias[n] (bias may be NULL), then
+ *   epi 0: C[m][n] = h                                  (bf16)
+ *   epi 1: C[m][n] = gelu'(h), C2[m][n] = gelu(h)       (bf16, tanh form)
+ *   epi 2: C[m][n] = R[m*ldr + n] + h                   (fp32; R may equal C)
+ * out_dtype must name that output type (GPT2_BF16, GPT2_BF16, GPT2_FP32).
+ * C and C2 are row-major with leading dimension ldc.  The same kernels the
+ * model's forward pass runs: the tiled matrix-core GEMM, or for M <= 16 and K
+ * a multiple of 32 the few-rows kernel of a decoding step.  Requires lda,
+ * ldb, ldc multiples of 8, K a multiple of 8, N a multiple of 8 (else
+ * GPT2_E_ARG, nothing enqueued). */
+gpt2_status gpt2_op_gemm_epi(int M, int N, int K, const void* A, long lda, const void* B, long ldb,
+                             int epi, const float* bias, const float* R, long ldr, void* C,
+                             void* C2, long ldc, int out_dtype, void* hip_stream);
+
 /* Causal self-attention forward ("CausalSelfAttention"): qkv is (B*T, 3C) in
  * dtype with [q | k | v] and head h at columns h*hd of each third; writes y
  * (B*T, C) in dtype with heads re-interleaved and lse (B, H, T) fp32, the

@@ -146,6 +146,16 @@ int main() {
                       1.f, 0, 0, nullptr) == GPT2_E_ARG);
   EXPECT(gpt2_op_gemm(7, 4, 4, 4, fake, 4, 0, fake, 4, 0, reinterpret_cast<float*>(fake), 4, 1.f, 0,
                       0, nullptr) == GPT2_E_ARG);
+  EXPECT(gpt2_op_gemm_epi(8, 64, 64, nullptr, 64, fake, 64, 0, nullptr, nullptr, 0, fake, nullptr,
+                          64, GPT2_BF16, nullptr) == GPT2_E_ARG);
+  EXPECT(gpt2_op_gemm_epi(8, 64, 64, fake, 64, fake, 64, 3, nullptr, nullptr, 0, fake, nullptr, 64,
+                          GPT2_BF16, nullptr) == GPT2_E_ARG);
+  EXPECT(gpt2_op_gemm_epi(8, 64, 64, fake, 64, fake, 64, 1, nullptr, nullptr, 0, fake, nullptr, 64,
+                          GPT2_BF16, nullptr) == GPT2_E_ARG);  // GELU needs C2
+  EXPECT(gpt2_op_gemm_epi(8, 64, 64, fake, 64, fake, 64, 2, nullptr, nullptr, 0, fake, nullptr, 64,
+                          GPT2_FP32, nullptr) == GPT2_E_ARG);  // residual needs R
+  EXPECT(gpt2_op_gemm_epi(8, 64, 64, fake, 64, fake, 64, 0, nullptr, nullptr, 0, fake, nullptr, 64,
+                          GPT2_FP32, nullptr) == GPT2_E_ARG);  // bias output is bf16
   EXPECT(gpt2_op_attention_fwd(GPT2_BF16, nullptr, fake, reinterpret_cast<float*>(fake), 1, 1, 1,
                                64, nullptr) == GPT2_E_ARG);
   EXPECT(gpt2_op_attention_bwd(GPT2_BF16, fake, fake, reinterpret_cast<float*>(fake), fake, fake,

@@ -86,6 +86,68 @@ def test_gemm_accumulate(mode, layout):
     assert err < 2e-5
 
 
+# few rows (a decoding step's batch): with both operands k-contiguous, M <= 16
+# and K a multiple of 32 the product runs on the few-rows kernel (16 output
+# columns per workgroup, K split over 16 wavefronts); ragged N and M = 1 included
+SKINNY = [(1, 2304, 768), (16, 3072, 768), (8, 768, 3072), (5, 50304, 768), (3, 776, 64),
+          (12, 8, 32), (16, 136, 96)]
+
+
+@pytest.mark.parametrize("mode", [0, 1])
+@pytest.mark.parametrize("shape", SKINNY)
+def test_gemm_few_rows(shape, mode):
+    M, N, K = shape
+    A, An = bf16_tensor((M, K), seed=31)
+    B, Bn = bf16_tensor((N, K), seed=32)
+    C0, C0n = f32_tensor((M, N), seed=33, scale=3.0)
+    C = C0.clone()
+    G.gpt2_op_gemm(G.GPT2_BF16, M, N, K, A, K, False, B, K, False, C, N, 0.5, mode, 0)
+    torch.cuda.synchronize()
+    ref = 0.5 * (An @ Bn.T) + (C0n if mode == 1 else 0.0)
+    err = maxrel(C.cpu().numpy().astype(np.float64), ref)
+    print(f"gemm few rows {shape} mode {mode}: maxrel {err:.2e}")
+    assert err < 2e-5
+
+
+# the linear layers' fused epilogues (bias; bias + GELU and its derivative;
+# bias + residual), on the few-rows kernel (M <= 16) and on the tiled one
+EPI_SHAPES = [(1, 776, 64), (8, 3072, 768), (16, 768, 3072), (300, 776, 128), (256, 768, 192)]
+
+
+@pytest.mark.parametrize("epi", [0, 1, 2])
+@pytest.mark.parametrize("shape", EPI_SHAPES)
+def test_gemm_fused_epilogues(shape, epi):
+    M, N, K = shape
+    A, An = bf16_tensor((M, K), seed=41)
+    B, Bn = bf16_tensor((N, K), seed=42, scale=0.05)
+    bias, bn = f32_tensor((N,), seed=43, scale=0.5)
+    h = An @ Bn.T + bn
+    if epi == 2:
+        R, Rn = f32_tensor((M, N), seed=44, scale=2.0)
+        C = torch.empty((M, N), dtype=torch.float32, device=DEV)
+        G.gpt2_op_gemm_epi(M, N, K, A, K, B, K, 2, bias, R, N, C, None, N, G.GPT2_FP32)
+        torch.cuda.synchronize()
+        err = maxrel(C.cpu().numpy().astype(np.float64), Rn + h)
+        print(f"gemm epi residual {shape}: maxrel {err:.2e}")
+        assert err < 2e-5
+        return
+    C = torch.empty((M, N), dtype=torch.bfloat16, device=DEV)
+    C2 = torch.empty((M, N), dtype=torch.bfloat16, device=DEV) if epi == 1 else None
+    G.gpt2_op_gemm_epi(M, N, K, A, K, B, K, epi, bias, None, 0, C, C2, N, G.GPT2_BF16)
+    torch.cuda.synchronize()
+    got = C.float().cpu().numpy().astype(np.float64)
+    # bf16 outputs: half-ulp 2^-9 of each value, below 5e-3 of the largest
+    if epi == 0:
+        err = maxrel(got, h)
+        print(f"gemm epi bias {shape}: maxrel {err:.2e}")
+        assert err < 5e-3
+    else:
+        e1 = maxrel(got, O.gelu_tanh_grad(h))
+        e2 = maxrel(C2.float().cpu().numpy().astype(np.float64), O.gelu_tanh(h))
+        print(f"gemm epi bias+gelu {shape}: gelu' maxrel {e1:.2e}, gelu maxrel {e2:.2e}")
+        assert e1 < 5e-3 and e2 < 5e-3
+
+
 def test_gemm_rejects_bad_alignment():
     A, _ = bf16_tensor((64, 60), seed=1)
     B, _ = bf16_tensor((64, 60), seed=2)

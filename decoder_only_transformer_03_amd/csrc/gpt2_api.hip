@@ -862,15 +862,23 @@ gpt2_status run_decode(gpt2* h, const int32_t* d_tok, int B, int p) {
   TIMED(h, GPT2_SITE_EMBED_FWD, launch_embed_fwd(d_tok, h->idx, P + h->lay.wte,
                                                  P + h->lay.wpe + (long)p * C, x, B, 1, C, Vp,
                                                  h->err, s));
+  // bf16 with at most 16 sequences: each LayerNorm runs inside the few-rows
+  // GEMM that reads it (one launch instead of two)
+  const bool ln_fused = at == DT_BF16 && B <= 16 && C % 32 == 0 && C <= LN_SKINNY_MAX_K;
   for (int l = 0; l < c.n_layer; ++l) {
     const LayerOff& o = h->lay.layer[l];
-    TIMED(h, GPT2_SITE_LN_FWD, launch_layernorm_fwd(at, x, P + o.ln1w, P + o.ln1b, a.u1, a.mean1,
-                                                    a.rstd1, B, C, s));
     EpiArgs e = epi(a.qkv, 3 * C);
     e.bias = P + o.attnb;
-    TIMED(h, GPT2_SITE_QKV_FWD, launch_gemm_fill(at, B, 3 * C, C, a.u1, C, false, W(h, o.attnw), C,
-                                                 false, EPI_BIAS, at, e, h->splitk,
-                                                 SPLITK_PART_ELEMS, s));
+    if (ln_fused) {
+      TIMED(h, GPT2_SITE_QKV_FWD, launch_gemm_ln_skinny(B, 3 * C, C, x, P + o.ln1w, P + o.ln1b,
+                                                        W(h, o.attnw), C, EPI_BIAS, at, e, s));
+    } else {
+      TIMED(h, GPT2_SITE_LN_FWD, launch_layernorm_fwd(at, x, P + o.ln1w, P + o.ln1b, a.u1, a.mean1,
+                                                      a.rstd1, B, C, s));
+      TIMED(h, GPT2_SITE_QKV_FWD, launch_gemm_fill(at, B, 3 * C, C, a.u1, C, false, W(h, o.attnw),
+                                                   C, false, EPI_BIAS, at, e, h->splitk,
+                                                   SPLITK_PART_ELEMS, s));
+    }
     // (appends position p's key and value to the cache, then attends)
     TIMED(h, GPT2_SITE_ATTN_FWD, launch_attn_decode(at, a.qkv, kv_slot(h, l), a.y, B, p,
                                                     c.block_size, H, hd, s));
@@ -881,14 +889,19 @@ gpt2_status run_decode(gpt2* h, const int32_t* d_tok, int B, int p) {
     TIMED(h, GPT2_SITE_PROJ_FWD, launch_gemm_fill(at, B, C, C, a.y, C, false, W(h, o.projw), C,
                                                   false, EPI_RESID, DT_F32, e, h->splitk,
                                                   SPLITK_PART_ELEMS, s));
-    TIMED(h, GPT2_SITE_LN_FWD, launch_layernorm_fwd(at, xm, P + o.ln2w, P + o.ln2b, a.u2, a.mean2,
-                                                    a.rstd2, B, C, s));
     e = epi(a.h, 4 * C);
     e.out2 = a.g;
     e.bias = P + o.fcb;
-    TIMED(h, GPT2_SITE_FC_FWD, launch_gemm_fill(at, B, 4 * C, C, a.u2, C, false, W(h, o.fcw), C,
-                                                false, EPI_BIAS_GELU, at, e, h->splitk,
-                                                SPLITK_PART_ELEMS, s));
+    if (ln_fused) {
+      TIMED(h, GPT2_SITE_FC_FWD, launch_gemm_ln_skinny(B, 4 * C, C, xm, P + o.ln2w, P + o.ln2b,
+                                                       W(h, o.fcw), C, EPI_BIAS_GELU, at, e, s));
+    } else {
+      TIMED(h, GPT2_SITE_LN_FWD, launch_layernorm_fwd(at, xm, P + o.ln2w, P + o.ln2b, a.u2, a.mean2,
+                                                      a.rstd2, B, C, s));
+      TIMED(h, GPT2_SITE_FC_FWD, launch_gemm_fill(at, B, 4 * C, C, a.u2, C, false, W(h, o.fcw), C,
+                                                  false, EPI_BIAS_GELU, at, e, h->splitk,
+                                                  SPLITK_PART_ELEMS, s));
+    }
     e = epi(x, C);
     e.bias = P + o.fc2b;
     e.resid = xm;
@@ -897,11 +910,18 @@ gpt2_status run_decode(gpt2* h, const int32_t* d_tok, int B, int p) {
                                                     W(h, o.fc2w), 4 * C, false, EPI_RESID, DT_F32,
                                                     e, h->splitk, SPLITK_PART_ELEMS, s));
   }
-  TIMED(h, GPT2_SITE_LN_FWD, launch_layernorm_fwd(at, x, P + h->lay.lnfw, P + h->lay.lnfb, h->z,
-                                                  h->meanf, h->rstdf, B, C, s));
-  TIMED(h, GPT2_SITE_LMHEAD_FWD, launch_gemm(at, B, Vp, C, h->z, C, false, W(h, h->lay.wte), C,
-                                             false, EPI_STORE, DT_F32, epi(h->gen_logits, Vp), 0,
-                                             s));
+  if (ln_fused) {
+    TIMED(h, GPT2_SITE_LMHEAD_FWD, launch_gemm_ln_skinny(B, Vp, C, x, P + h->lay.lnfw,
+                                                         P + h->lay.lnfb, W(h, h->lay.wte), C,
+                                                         EPI_STORE, DT_F32, epi(h->gen_logits, Vp),
+                                                         s));
+  } else {
+    TIMED(h, GPT2_SITE_LN_FWD, launch_layernorm_fwd(at, x, P + h->lay.lnfw, P + h->lay.lnfb, h->z,
+                                                    h->meanf, h->rstdf, B, C, s));
+    TIMED(h, GPT2_SITE_LMHEAD_FWD, launch_gemm(at, B, Vp, C, h->z, C, false, W(h, h->lay.wte), C,
+                                               false, EPI_STORE, DT_F32, epi(h->gen_logits, Vp), 0,
+                                               s));
+  }
   return GPT2_OK;
 }
 

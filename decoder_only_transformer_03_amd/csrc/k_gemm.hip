@@ -275,17 +275,54 @@ __global__ __launch_bounds__(256) void splitk_epi_kernel(const float* __restrict
 // blocks are added in a fixed order through LDS and 64 threads apply the
 // epilogue to four columns each.
 constexpr int SKINNY_M = 16, SKINNY_WAVES = 16, SKINNY_BATCH = 8;
-template <int EPI, typename TO>
+// LNA: A is LayerNorm(x) of fp32 rows x (M x K, row stride K) with weight
+// lnw and bias lnb ("The Block: pre-LN and residuals"), formed here instead
+// of by a separate pass: wavefront w normalises row w in the same order and
+// arithmetic as layernorm_fwd_kernel (per-lane sums of 4-column chunks, then
+// a wavefront sum; biased variance, eps 1e-5) and writes it as bf16 to LDS,
+// from where the fragments are read.
+template <int EPI, typename TO, bool LNA>
 __global__ __launch_bounds__(SKINNY_WAVES * 64) void gemm_skinny_kernel(
     int M, int N, int K, const bf16_t* __restrict__ A, long lda, const bf16_t* __restrict__ B,
-    long ldb, EpiArgs e) {
+    long ldb, EpiArgs e, const float* __restrict__ x, const float* __restrict__ lnw,
+    const float* __restrict__ lnb) {
   __shared__ float red[SKINNY_WAVES][SKINNY_M * 16];
+  extern __shared__ __attribute__((aligned(16))) bf16_t sA[];  // LNA: M x K
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  if constexpr (LNA) {
+    if (w < M) {
+      const float* xr = x + (long)w * K;
+      float sum = 0.f;
+      for (int c = lane * 4; c < K; c += 256) {
+        const float4 v = *reinterpret_cast<const float4*>(xr + c);
+        sum += (v.x + v.y) + (v.z + v.w);
+      }
+      const float mean = wave_sum(sum) / (float)K;
+      float q = 0.f;
+      for (int c = lane * 4; c < K; c += 256) {
+        const float4 v = *reinterpret_cast<const float4*>(xr + c);
+        const float d[4] = {v.x - mean, v.y - mean, v.z - mean, v.w - mean};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) q += d[j] * d[j];
+      }
+      const float rstd = 1.0f / sqrtf(wave_sum(q) / (float)K + 1e-5f);
+      for (int c = lane * 4; c < K; c += 256) {
+        const float4 v = *reinterpret_cast<const float4*>(xr + c);
+        const float4 g = *reinterpret_cast<const float4*>(lnw + c);
+        const float4 bb = *reinterpret_cast<const float4*>(lnb + c);
+        const float o0 = (v.x - mean) * rstd * g.x + bb.x, o1 = (v.y - mean) * rstd * g.y + bb.y;
+        const float o2 = (v.z - mean) * rstd * g.z + bb.z, o3 = (v.w - mean) * rstd * g.w + bb.w;
+        *reinterpret_cast<uint2*>(sA + (long)w * K + c) = make_uint2(pack_bf2(o0, o1),
+                                                                     pack_bf2(o2, o3));
+      }
+    }
+    __syncthreads();
+  }
   const int n0 = blockIdx.x * 16;
   const int r = lane & 15, kq = 8 * (lane >> 4);
   const bool arow = r < M;
   const int bn = n0 + r < N ? n0 + r : N - 1;
-  const bf16_t* ap = A + (long)(arow ? r : 0) * lda + kq;
+  const bf16_t* ap = LNA ? sA + (long)(arow ? r : 0) * K + kq : A + (long)(arow ? r : 0) * lda + kq;
   const bf16_t* bp = B + (long)bn * ldb + kq;
   const int nk = K / 32;
   const int c0 = (w * nk) / SKINNY_WAVES, c1 = ((w + 1) * nk) / SKINNY_WAVES;
@@ -332,39 +369,54 @@ bool skinny_ok(DType in_t, int M, int K, bool a_t, bool b_t, int epi) {
           epi == EPI_ACCUM);
 }
 
-hipError_t launch_gemm_skinny(int M, int N, int K, const bf16_t* A, long lda, const bf16_t* B,
-                              long ldb, int epi, DType out_t, const EpiArgs& e, hipStream_t s) {
+template <bool LNA>
+static hipError_t skinny_by_epi(int M, int N, int K, const bf16_t* A, long lda, const bf16_t* B,
+                                long ldb, int epi, DType out_t, const EpiArgs& e, const float* x,
+                                const float* lnw, const float* lnb, hipStream_t s) {
   const unsigned grid = (unsigned)((N + 15) / 16);
   const int nt = SKINNY_WAVES * 64;
+  const size_t lds = LNA ? (size_t)M * K * sizeof(bf16_t) : 0;
+#define SKINNY_RUN(E, T) \
+  gemm_skinny_kernel<E, T, LNA><<<grid, nt, lds, s>>>(M, N, K, A, lda, B, ldb, e, x, lnw, lnb)
   switch (epi) {
     case EPI_STORE:
-      if (out_t == DT_BF16)
-        gemm_skinny_kernel<EPI_STORE, bf16_t><<<grid, nt, 0, s>>>(M, N, K, A, lda, B, ldb, e);
-      else
-        gemm_skinny_kernel<EPI_STORE, float><<<grid, nt, 0, s>>>(M, N, K, A, lda, B, ldb, e);
+      if (out_t == DT_BF16) SKINNY_RUN(EPI_STORE, bf16_t);
+      else SKINNY_RUN(EPI_STORE, float);
       break;
     case EPI_BIAS:
-      if (out_t == DT_BF16)
-        gemm_skinny_kernel<EPI_BIAS, bf16_t><<<grid, nt, 0, s>>>(M, N, K, A, lda, B, ldb, e);
-      else
-        gemm_skinny_kernel<EPI_BIAS, float><<<grid, nt, 0, s>>>(M, N, K, A, lda, B, ldb, e);
+      if (out_t == DT_BF16) SKINNY_RUN(EPI_BIAS, bf16_t);
+      else SKINNY_RUN(EPI_BIAS, float);
       break;
     case EPI_BIAS_GELU:
-      if (out_t == DT_BF16)
-        gemm_skinny_kernel<EPI_BIAS_GELU, bf16_t><<<grid, nt, 0, s>>>(M, N, K, A, lda, B, ldb, e);
-      else
-        gemm_skinny_kernel<EPI_BIAS_GELU, float><<<grid, nt, 0, s>>>(M, N, K, A, lda, B, ldb, e);
+      if (out_t == DT_BF16) SKINNY_RUN(EPI_BIAS_GELU, bf16_t);
+      else SKINNY_RUN(EPI_BIAS_GELU, float);
       break;
     case EPI_RESID:
-      gemm_skinny_kernel<EPI_RESID, float><<<grid, nt, 0, s>>>(M, N, K, A, lda, B, ldb, e);
+      SKINNY_RUN(EPI_RESID, float);
       break;
     case EPI_ACCUM:
-      gemm_skinny_kernel<EPI_ACCUM, float><<<grid, nt, 0, s>>>(M, N, K, A, lda, B, ldb, e);
+      SKINNY_RUN(EPI_ACCUM, float);
       break;
     default:
       return hipErrorInvalidValue;
   }
+#undef SKINNY_RUN
   return hipGetLastError();
+}
+
+hipError_t launch_gemm_skinny(int M, int N, int K, const bf16_t* A, long lda, const bf16_t* B,
+                              long ldb, int epi, DType out_t, const EpiArgs& e, hipStream_t s) {
+  return skinny_by_epi<false>(M, N, K, A, lda, B, ldb, epi, out_t, e, nullptr, nullptr, nullptr,
+                              s);
+}
+
+hipError_t launch_gemm_ln_skinny(int M, int N, int K, const float* x, const float* lnw,
+                                 const float* lnb, const void* B, long ldb, int epi, DType out_t,
+                                 const EpiArgs& e, hipStream_t s) {
+  if (M < 1 || M > SKINNY_M || K % 32 || K > LN_SKINNY_MAX_K || ldb % 8 || N % 8)
+    return hipErrorInvalidValue;
+  return skinny_by_epi<true>(M, N, K, nullptr, 0, (const bf16_t*)B, ldb, epi, out_t, e, x, lnw,
+                             lnb, s);
 }
 
 hipError_t launch_gemm_fill(DType in_t, int M, int N, int K, const void* A, long lda, bool a_t,

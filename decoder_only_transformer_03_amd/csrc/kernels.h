@@ -169,6 +169,16 @@ hipError_t launch_attn_bwd(DType t, const void* qkv, const void* y, const float*
                            const void* dy, void* dqkv, float* dbuf, int B, int T, int H, int hd,
                            float* bias_part, hipStream_t s);
 
+// Few rows (M <= 16) of a linear layer whose input is LayerNorm(x) (x fp32,
+// M x K row-major, LayerNorm weight lnw and bias lnb): C = LN(x) B^T with
+// the bf16 rounding of LN(x) that layernorm_fwd + the GEMM would give, in
+// one launch; the epilogue as for launch_gemm (e.out etc.).  K a multiple of
+// 32 and at most LN_SKINNY_MAX_K (the normalised rows are held in LDS).
+constexpr int LN_SKINNY_MAX_K = 2048;
+hipError_t launch_gemm_ln_skinny(int M, int N, int K, const float* x, const float* lnw,
+                                 const float* lnb, const void* B, long ldb, int epi, DType out_t,
+                                 const EpiArgs& e, hipStream_t s);
+
 // Key/value cache of the decoding path: per block (B, bs, 2C) [k | v] rows.
 // kv_append: the k, v parts of qkv rows (B*T, 3C) into positions pos0 .. pos0+T-1.
 hipError_t launch_kv_append(DType t, const void* qkv, void* cache, int B, int Tn, int pos0, int bs,

@@ -266,98 +266,130 @@ __global__ __launch_bounds__(256) void splitk_epi_kernel(const float* __restrict
 }
 
 // Few rows (M <= 16: a decoding step's batch): C = A B^T with A (M x K) and
-// B (N x K) both k-contiguous bf16.  The work is streaming B once, so each
-// workgroup owns 16 output columns and splits K over its 16 wavefronts, each a
-// contiguous range of 32-deep chunks whose loads are all issued before its
-// matrix products (v_mfma_f32_16x16x32_bf16: lane l supplies row l%16 of A
-// and of B at contraction slots 8(l/16) .. +7; rows of A past M are zeros,
-// columns past N read column N-1 and are dropped).  The 16 partial 16 x 16
-// blocks are added in a fixed order through LDS and 64 threads apply the
-// epilogue to four columns each.
+// B (N x K) both k-contiguous bf16.  The work is streaming B once.  A
+// workgroup owns CT tiles of 16 output columns; its 16 wavefronts take tile
+// w % CT and split K into 16/CT contiguous ranges of 32-deep chunks, whose
+// loads are all issued before their matrix products
+// (v_mfma_f32_16x16x32_bf16: lane l supplies row l%16 of A and of B at
+// contraction slots 8(l/16) .. +7; rows of A past M are zeros, columns past N
+// read column N-1 and are dropped).  The partial 16 x 16 blocks of a tile are
+// added in a fixed order through LDS, and 4 threads per row and tile apply
+// the epilogue to four columns each, its inputs (residual, bias) fetched
+// before the products.
 constexpr int SKINNY_M = 16, SKINNY_WAVES = 16, SKINNY_BATCH = 8;
 // LNA: A is LayerNorm(x) of fp32 rows x (M x K, row stride K) with weight
 // lnw and bias lnb ("The Block: pre-LN and residuals"), formed here instead
-// of by a separate pass: wavefront w normalises row w in the same order and
-// arithmetic as layernorm_fwd_kernel (per-lane sums of 4-column chunks, then
-// a wavefront sum; biased variance, eps 1e-5) and writes it as bf16 to LDS,
-// from where the fragments are read.
-template <int EPI, typename TO, bool LNA>
+// of by a separate pass, after the first chunks of B are in flight:
+// wavefront w holds row w in registers and normalises it in the same order
+// and arithmetic as layernorm_fwd_kernel (per-lane sums of 4-column chunks,
+// then a wavefront sum; biased variance, eps 1e-5), writing it as bf16 to
+// LDS, from where the fragments are read.
+template <int EPI, typename TO, bool LNA, int CT>
 __global__ __launch_bounds__(SKINNY_WAVES * 64) void gemm_skinny_kernel(
     int M, int N, int K, const bf16_t* __restrict__ A, long lda, const bf16_t* __restrict__ B,
     long ldb, EpiArgs e, const float* __restrict__ x, const float* __restrict__ lnw,
     const float* __restrict__ lnb) {
+  constexpr int NKS = SKINNY_WAVES / CT;  // K ranges per column tile
   __shared__ float red[SKINNY_WAVES][SKINNY_M * 16];
   extern __shared__ __attribute__((aligned(16))) bf16_t sA[];  // LNA: M x K
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+  const int ct = w % CT, ks = w / CT;
+  const int n0 = (blockIdx.x * CT + ct) * 16;
+  const int r = lane & 15, kq = 8 * (lane >> 4);
+  const bool arow = r < M;
+  const int bn = n0 + r < N ? n0 + r : N - 1;
+  const bf16_t* bp = B + (long)bn * ldb + kq;
+  const int nk = K / 32;
+  const int c0 = (ks * nk) / NKS, c1 = ((ks + 1) * nk) / NKS;
+  // Every batch runs all SKINNY_BATCH products, those of chunks past c1 on
+  // zero operands (adding exactly nothing): a matrix product ignores the
+  // exec mask, so none is placed under a condition.
+  bf16x8_t bfv[SKINNY_BATCH];
+#pragma unroll
+  for (int j = 0; j < SKINNY_BATCH; ++j)
+    bfv[j] = c0 + j < c1 ? *reinterpret_cast<const bf16x8_t*>(bp + (long)(c0 + j) * 32)
+                         : bf16x8_t{};
+
+  // epilogue thread: row em, columns en .. en+3
+  const int em = tid / (4 * CT), en = blockIdx.x * 16 * CT + 4 * (tid % (4 * CT));
+  const bool etd = tid < SKINNY_M * 4 * CT && em < M && en < N;
+  float ein[4] = {0.f, 0.f, 0.f, 0.f}, eb[4];
+  if (etd) {
+    epi_load4<EPI, TO>(e, em, en, ein);
+    epi_load_bias(e, en, eb);
+  }
+
   if constexpr (LNA) {
+    constexpr int NV = LN_SKINNY_MAX_K / 256;
     if (w < M) {
       const float* xr = x + (long)w * K;
+      float4 v[NV];
+#pragma unroll
+      for (int i = 0; i < NV; ++i)
+        if (lane * 4 + 256 * i < K) v[i] = *reinterpret_cast<const float4*>(xr + lane * 4 + 256 * i);
       float sum = 0.f;
-      for (int c = lane * 4; c < K; c += 256) {
-        const float4 v = *reinterpret_cast<const float4*>(xr + c);
-        sum += (v.x + v.y) + (v.z + v.w);
-      }
+#pragma unroll
+      for (int i = 0; i < NV; ++i)
+        if (lane * 4 + 256 * i < K) sum += (v[i].x + v[i].y) + (v[i].z + v[i].w);
       const float mean = wave_sum(sum) / (float)K;
       float q = 0.f;
-      for (int c = lane * 4; c < K; c += 256) {
-        const float4 v = *reinterpret_cast<const float4*>(xr + c);
-        const float d[4] = {v.x - mean, v.y - mean, v.z - mean, v.w - mean};
 #pragma unroll
-        for (int j = 0; j < 4; ++j) q += d[j] * d[j];
-      }
+      for (int i = 0; i < NV; ++i)
+        if (lane * 4 + 256 * i < K) {
+          const float d[4] = {v[i].x - mean, v[i].y - mean, v[i].z - mean, v[i].w - mean};
+#pragma unroll
+          for (int j = 0; j < 4; ++j) q += d[j] * d[j];
+        }
       const float rstd = 1.0f / sqrtf(wave_sum(q) / (float)K + 1e-5f);
-      for (int c = lane * 4; c < K; c += 256) {
-        const float4 v = *reinterpret_cast<const float4*>(xr + c);
-        const float4 g = *reinterpret_cast<const float4*>(lnw + c);
-        const float4 bb = *reinterpret_cast<const float4*>(lnb + c);
-        const float o0 = (v.x - mean) * rstd * g.x + bb.x, o1 = (v.y - mean) * rstd * g.y + bb.y;
-        const float o2 = (v.z - mean) * rstd * g.z + bb.z, o3 = (v.w - mean) * rstd * g.w + bb.w;
-        *reinterpret_cast<uint2*>(sA + (long)w * K + c) = make_uint2(pack_bf2(o0, o1),
-                                                                     pack_bf2(o2, o3));
+#pragma unroll
+      for (int i = 0; i < NV; ++i) {
+        const int c = lane * 4 + 256 * i;
+        if (c < K) {
+          const float4 g = *reinterpret_cast<const float4*>(lnw + c);
+          const float4 bb = *reinterpret_cast<const float4*>(lnb + c);
+          const float o0 = (v[i].x - mean) * rstd * g.x + bb.x;
+          const float o1 = (v[i].y - mean) * rstd * g.y + bb.y;
+          const float o2 = (v[i].z - mean) * rstd * g.z + bb.z;
+          const float o3 = (v[i].w - mean) * rstd * g.w + bb.w;
+          *reinterpret_cast<uint2*>(sA + (long)w * K + c) = make_uint2(pack_bf2(o0, o1),
+                                                                       pack_bf2(o2, o3));
+        }
       }
     }
     __syncthreads();
   }
-  const int n0 = blockIdx.x * 16;
-  const int r = lane & 15, kq = 8 * (lane >> 4);
-  const bool arow = r < M;
-  const int bn = n0 + r < N ? n0 + r : N - 1;
   const bf16_t* ap = LNA ? sA + (long)(arow ? r : 0) * K + kq : A + (long)(arow ? r : 0) * lda + kq;
-  const bf16_t* bp = B + (long)bn * ldb + kq;
-  const int nk = K / 32;
-  const int c0 = (w * nk) / SKINNY_WAVES, c1 = ((w + 1) * nk) / SKINNY_WAVES;
   f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
   for (int cb = c0; cb < c1; cb += SKINNY_BATCH) {
-    bf16x8_t af[SKINNY_BATCH], bfv[SKINNY_BATCH];
-#pragma unroll
-    for (int j = 0; j < SKINNY_BATCH; ++j) {
-      if (cb + j < c1) {
-        const long k = (long)(cb + j) * 32;
-        af[j] = arow ? *reinterpret_cast<const bf16x8_t*>(ap + k) : bf16x8_t{};
-        bfv[j] = *reinterpret_cast<const bf16x8_t*>(bp + k);
-      }
-    }
+    bf16x8_t af[SKINNY_BATCH];
 #pragma unroll
     for (int j = 0; j < SKINNY_BATCH; ++j)
-      if (cb + j < c1) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[j], bfv[j], acc, 0, 0, 0);
+      af[j] = arow && cb + j < c1 ? *reinterpret_cast<const bf16x8_t*>(ap + (long)(cb + j) * 32)
+                                  : bf16x8_t{};
+#pragma unroll
+    for (int j = 0; j < SKINNY_BATCH; ++j)
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[j], bfv[j], acc, 0, 0, 0);
+    // the next batch of B (a contraction of more than 8 chunks per wavefront)
+#pragma unroll
+    for (int j = 0; j < SKINNY_BATCH; ++j)
+      bfv[j] = cb + SKINNY_BATCH + j < c1
+                   ? *reinterpret_cast<const bf16x8_t*>(bp + (long)(cb + SKINNY_BATCH + j) * 32)
+                   : bf16x8_t{};
   }
   // lane l holds rows 4(l/16) .. +3 of column l%16
 #pragma unroll
   for (int i = 0; i < 4; ++i) red[w][(4 * (lane >> 4) + i) * 16 + r] = acc[i];
   __syncthreads();
-  if (tid < SKINNY_M * 4) {
-    const int m = tid >> 2, cl = 4 * (tid & 3);
-    const int n = n0 + cl;
-    if (m < M && n < N) {
-      float c[4];
+  if (etd) {
+    const int cl = en - blockIdx.x * 16 * CT, t = cl >> 4, cc = cl & 15;
+    float c[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        float t = red[0][m * 16 + cl + j];
-        for (int q = 1; q < SKINNY_WAVES; ++q) t += red[q][m * 16 + cl + j];
-        c[j] = t;
-      }
-      epi_apply4<EPI, TO>(e, m, n, c, 0);
+    for (int j = 0; j < 4; ++j) {
+      float a = red[t][em * 16 + cc + j];
+      for (int q = 1; q < NKS; ++q) a += red[q * CT + t][em * 16 + cc + j];
+      c[j] = a;
     }
+    epi_store4<EPI, TO>(e, em, en, c, ein, eb, 0);
   }
 }
 
@@ -369,15 +401,15 @@ bool skinny_ok(DType in_t, int M, int K, bool a_t, bool b_t, int epi) {
           epi == EPI_ACCUM);
 }
 
-template <bool LNA>
+template <bool LNA, int CT>
 static hipError_t skinny_by_epi(int M, int N, int K, const bf16_t* A, long lda, const bf16_t* B,
                                 long ldb, int epi, DType out_t, const EpiArgs& e, const float* x,
                                 const float* lnw, const float* lnb, hipStream_t s) {
-  const unsigned grid = (unsigned)((N + 15) / 16);
+  const unsigned grid = (unsigned)((N + 16 * CT - 1) / (16 * CT));
   const int nt = SKINNY_WAVES * 64;
   const size_t lds = LNA ? (size_t)M * K * sizeof(bf16_t) : 0;
 #define SKINNY_RUN(E, T) \
-  gemm_skinny_kernel<E, T, LNA><<<grid, nt, lds, s>>>(M, N, K, A, lda, B, ldb, e, x, lnw, lnb)
+  gemm_skinny_kernel<E, T, LNA, CT><<<grid, nt, lds, s>>>(M, N, K, A, lda, B, ldb, e, x, lnw, lnb)
   switch (epi) {
     case EPI_STORE:
       if (out_t == DT_BF16) SKINNY_RUN(EPI_STORE, bf16_t);
@@ -404,10 +436,17 @@ static hipError_t skinny_by_epi(int M, int N, int K, const bf16_t* A, long lda, 
   return hipGetLastError();
 }
 
+// Four column tiles per workgroup once there are enough columns for 512 such
+// workgroups (the vocabulary-wide head), one otherwise.
+constexpr int SKINNY_WIDE_N = 16 * 4 * 512;
+
 hipError_t launch_gemm_skinny(int M, int N, int K, const bf16_t* A, long lda, const bf16_t* B,
                               long ldb, int epi, DType out_t, const EpiArgs& e, hipStream_t s) {
-  return skinny_by_epi<false>(M, N, K, A, lda, B, ldb, epi, out_t, e, nullptr, nullptr, nullptr,
-                              s);
+  if (N >= SKINNY_WIDE_N)
+    return skinny_by_epi<false, 4>(M, N, K, A, lda, B, ldb, epi, out_t, e, nullptr, nullptr,
+                                   nullptr, s);
+  return skinny_by_epi<false, 1>(M, N, K, A, lda, B, ldb, epi, out_t, e, nullptr, nullptr,
+                                 nullptr, s);
 }
 
 hipError_t launch_gemm_ln_skinny(int M, int N, int K, const float* x, const float* lnw,
@@ -415,8 +454,11 @@ hipError_t launch_gemm_ln_skinny(int M, int N, int K, const float* x, const floa
                                  const EpiArgs& e, hipStream_t s) {
   if (M < 1 || M > SKINNY_M || K % 32 || K > LN_SKINNY_MAX_K || ldb % 8 || N % 8)
     return hipErrorInvalidValue;
-  return skinny_by_epi<true>(M, N, K, nullptr, 0, (const bf16_t*)B, ldb, epi, out_t, e, x, lnw,
-                             lnb, s);
+  if (N >= SKINNY_WIDE_N)
+    return skinny_by_epi<true, 4>(M, N, K, nullptr, 0, (const bf16_t*)B, ldb, epi, out_t, e, x,
+                                  lnw, lnb, s);
+  return skinny_by_epi<true, 1>(M, N, K, nullptr, 0, (const bf16_t*)B, ldb, epi, out_t, e, x, lnw,
+                                lnb, s);
 }
 
 hipError_t launch_gemm_fill(DType in_t, int M, int N, int K, const void* A, long lda, bool a_t,

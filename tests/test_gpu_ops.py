@@ -89,8 +89,10 @@ def test_gemm_accumulate(mode, layout):
 # few rows (a decoding step's batch): with both operands k-contiguous, M <= 16
 # and K a multiple of 32 the product runs on the few-rows kernel (16 output
 # columns per workgroup, K split over 16 wavefronts); ragged N and M = 1 included
+# (7, 33000, 96): four column tiles per workgroup, a ragged last workgroup, and
+# K ranges that are empty for some wavefronts (3 chunks over 4 ranges)
 SKINNY = [(1, 2304, 768), (16, 3072, 768), (8, 768, 3072), (5, 50304, 768), (3, 776, 64),
-          (12, 8, 32), (16, 136, 96)]
+          (12, 8, 32), (16, 136, 96), (7, 33000, 96)]
 
 
 @pytest.mark.parametrize("mode", [0, 1])
@@ -111,7 +113,8 @@ def test_gemm_few_rows(shape, mode):
 
 # the linear layers' fused epilogues (bias; bias + GELU and its derivative;
 # bias + residual), on the few-rows kernel (M <= 16) and on the tiled one
-EPI_SHAPES = [(1, 776, 64), (8, 3072, 768), (16, 768, 3072), (300, 776, 128), (256, 768, 192)]
+EPI_SHAPES = [(1, 776, 64), (8, 3072, 768), (16, 768, 3072), (4, 33000, 64), (300, 776, 128),
+              (256, 768, 192)]
 
 
 @pytest.mark.parametrize("epi", [0, 1, 2])

@@ -144,6 +144,48 @@ def cpu_baseline(d, wl, seconds_hint=20.0):
             "sample": f"{what} on 1 x {T} tokens of the same workload; {dt:.1f} s"}
 
 
+def library_gemm(torch, BT, d):
+    """The platform's bf16 GEMM (torch.mm, fp32 accumulation, bf16 out, no
+    epilogue) on the matrix products of one step, timed with events over 10
+    calls after 3 warm-up calls; one line per shape on stderr."""
+    C, Vp = d["n_embd"], d["padded_vocab_size"]
+    shapes = [  # (product, M, N, K, layout of C[M,N] = A B): nt = B given as (N, K)
+        ("lm_head forward", BT, Vp, C, "nt"), ("qkv forward", BT, 3 * C, C, "nt"),
+        ("proj forward", BT, C, C, "nt"), ("fc forward", BT, 4 * C, C, "nt"),
+        ("fcproj forward", BT, C, 4 * C, "nt"), ("lm_head dX", BT, C, Vp, "nn"),
+        ("qkv dX", BT, C, 3 * C, "nn"), ("proj dX", BT, C, C, "nn"),
+        ("fc dX", BT, C, 4 * C, "nn"), ("fcproj dX", BT, 4 * C, C, "nn"),
+        ("lm_head dW", Vp, C, BT, "tn"), ("qkv dW", 3 * C, C, BT, "tn"),
+        ("proj dW", C, C, BT, "tn"), ("fc dW", 4 * C, C, BT, "tn"),
+        ("fcproj dW", C, 4 * C, BT, "tn")]
+    dev = "cuda:0"
+    g = torch.Generator(device=dev).manual_seed(0)
+    for name, M, N, K, lay in shapes:
+        def rnd(*shape):
+            return torch.randn(shape, device=dev, dtype=torch.bfloat16, generator=g)
+        if lay == "nt":
+            A, Bm = rnd(M, K), rnd(N, K).t()
+        elif lay == "nn":
+            A, Bm = rnd(M, K), rnd(K, N)
+        else:
+            A, Bm = rnd(K, M).t(), rnd(K, N)
+        for _ in range(3):
+            torch.mm(A, Bm)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(10):
+            torch.mm(A, Bm)
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 100.0
+        tf = 2.0 * M * N * K / (us * 1e-6) / 1e12
+        print(f"library gemm {name}: {M}x{N}x{K} {lay} {us:.1f} us {tf:.1f} TFLOP/s "
+              f"({tf / 2500.0:.3f} of 2.5 PF)", file=sys.stderr, flush=True)
+        del A, Bm
+    torch.cuda.empty_cache()
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -154,6 +196,9 @@ def main():
     ap.add_argument("--breakdown", action="store_true", help="also time every launch site")
     ap.add_argument("--copy-probe", action="store_true",
                     help="first run three 1 GiB device copies (calibrates HBM byte counters)")
+    ap.add_argument("--library-gemm", action="store_true",
+                    help="first time the platform's bf16 GEMM (torch.mm) on the step's GEMM "
+                         "shapes, printed to stderr: a reference point, not part of the step")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
@@ -172,6 +217,8 @@ def main():
     cfg = G.make_config(max_batch=B, precision="bf16", head_chunk=fused, **d)
     model = G.GPT2(cfg, device="cuda:0")
     model.set_params(synthetic.init_params(d, seed=42))
+    if args.library_gemm:
+        library_gemm(torch, B * T, d)
     if args.copy_probe:
         src = torch.ones(1 << 29, dtype=torch.bfloat16, device="cuda:0")
         dst = torch.empty_like(src)

@@ -186,6 +186,48 @@ def library_gemm(torch, BT, d):
     torch.cuda.empty_cache()
 
 
+def library_attention(torch, B, T, d):
+    """The platform's fused causal attention (torch SDPA restricted to its
+    flash and memory-efficient backends; the math path is never used) in
+    bf16 on (B, n_head, T, head width), forward and forward + backward timed
+    with events over 10 calls after 3 warm-up calls; one line per backend on
+    stderr, flops counted as causal (half the score matrix)."""
+    import torch.nn.functional as F
+    from torch.nn.attention import sdpa_kernel, SDPBackend
+    H, D = d["n_head"], d["n_embd"] // d["n_head"]
+    dev = "cuda:0"
+    g = torch.Generator(device=dev).manual_seed(0)
+    fl = 4.0 * B * H * T * T * D / 2
+    for be in (SDPBackend.FLASH_ATTENTION, SDPBackend.EFFICIENT_ATTENTION):
+        try:
+            q, k, v, do = (torch.randn((B, H, T, D), device=dev, dtype=torch.bfloat16,
+                                       generator=g) for _ in range(4))
+            q.requires_grad_(), k.requires_grad_(), v.requires_grad_()
+            with sdpa_kernel([be]):
+                for _ in range(3):
+                    F.scaled_dot_product_attention(q, k, v, is_causal=True).backward(do)
+                torch.cuda.synchronize()
+                e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+                e[0].record()
+                for _ in range(10):
+                    F.scaled_dot_product_attention(q, k, v, is_causal=True)
+                e[1].record()
+                for _ in range(10):
+                    F.scaled_dot_product_attention(q, k, v, is_causal=True).backward(do)
+                e[2].record()
+                torch.cuda.synchronize()
+            fwd = e[0].elapsed_time(e[1]) * 100.0
+            bwd = e[1].elapsed_time(e[2]) * 100.0 - fwd
+            print(f"library attention {be.name}: {B}x{H}x{T}x{D} causal forward {fwd:.1f} us "
+                  f"{fl / fwd / 1e6:.1f} TFLOP/s, backward {bwd:.1f} us "
+                  f"{2.5 * fl / bwd / 1e6:.1f} TFLOP/s", file=sys.stderr, flush=True)
+            del q, k, v, do
+        except RuntimeError as ex:
+            print(f"library attention {be.name}: unavailable ({str(ex)[:120]})", file=sys.stderr,
+                  flush=True)
+    torch.cuda.empty_cache()
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -196,9 +238,11 @@ def main():
     ap.add_argument("--breakdown", action="store_true", help="also time every launch site")
     ap.add_argument("--copy-probe", action="store_true",
                     help="first run three 1 GiB device copies (calibrates HBM byte counters)")
-    ap.add_argument("--library-gemm", action="store_true",
+    ap.add_argument("--library-ref", action="store_true",
                     help="first time the platform's bf16 GEMM (torch.mm) on the step's GEMM "
-                         "shapes, printed to stderr: a reference point, not part of the step")
+                         "shapes and its fused attention (torch SDPA, flash and memory-efficient "
+                         "backends) on the step's attention shape, printed to stderr: reference "
+                         "points, not part of the step")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
@@ -217,8 +261,9 @@ def main():
     cfg = G.make_config(max_batch=B, precision="bf16", head_chunk=fused, **d)
     model = G.GPT2(cfg, device="cuda:0")
     model.set_params(synthetic.init_params(d, seed=42))
-    if args.library_gemm:
+    if args.library_ref:
         library_gemm(torch, B * T, d)
+        library_attention(torch, B, T, d)
     if args.copy_probe:
         src = torch.ones(1 << 29, dtype=torch.bfloat16, device="cuda:0")
         dst = torch.empty_like(src)

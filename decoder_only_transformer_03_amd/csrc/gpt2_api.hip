@@ -204,6 +204,8 @@ struct gpt2 {
   float* gen_logits;      // (max_batch, Vp) last-position logits
   int32_t* gen_idx;       // (max_batch, block_size) cropped context
   void* kv;               // key/value cache: per block (max_batch, block_size, 2C)
+  int kv_len = 0;         // positions 0 .. kv_len-1 of kv_B sequences hold the current
+  int kv_B = 0;           // parameters' keys and values (gpt2_prefill / gpt2_decode)
   // backward scratch
   float* dres;
   void* dres_b;           // bf16 mode: 2L slots of the residual gradient (see run_backward)
@@ -848,9 +850,9 @@ void* kv_slot(const gpt2* h, int l) {
 
 // One decoding step: the blocks for position p of each sequence only, the
 // token ids d_tok (B, device), the keys and values of positions < p read from
-// the cache and those of p appended to it; the last-position logits (B, Vp)
-// fp32 into h->gen_logits.  The activations of layer 0 serve as scratch.
-gpt2_status run_decode(gpt2* h, const int32_t* d_tok, int B, int p) {
+// the cache and those of p appended to it; the logits of position p (B, Vp)
+// fp32 into `logits`.  The activations of layer 0 serve as scratch.
+gpt2_status run_decode(gpt2* h, const int32_t* d_tok, int B, int p, float* logits) {
   const gpt2_config& c = h->cfg;
   const int C = c.n_embd, H = c.n_head, hd = C / H, Vp = c.padded_vocab_size;
   const DType at = h->act;
@@ -913,13 +915,13 @@ gpt2_status run_decode(gpt2* h, const int32_t* d_tok, int B, int p) {
   if (ln_fused) {
     TIMED(h, GPT2_SITE_LMHEAD_FWD, launch_gemm_ln_skinny(B, Vp, C, x, P + h->lay.lnfw,
                                                          P + h->lay.lnfb, W(h, h->lay.wte), C,
-                                                         EPI_STORE, DT_F32, epi(h->gen_logits, Vp),
+                                                         EPI_STORE, DT_F32, epi(logits, Vp),
                                                          s));
   } else {
     TIMED(h, GPT2_SITE_LN_FWD, launch_layernorm_fwd(at, x, P + h->lay.lnfw, P + h->lay.lnfb, h->z,
                                                     h->meanf, h->rstdf, B, C, s));
     TIMED(h, GPT2_SITE_LMHEAD_FWD, launch_gemm(at, B, Vp, C, h->z, C, false, W(h, h->lay.wte), C,
-                                               false, EPI_STORE, DT_F32, epi(h->gen_logits, Vp), 0,
+                                               false, EPI_STORE, DT_F32, epi(logits, Vp), 0,
                                                s));
   }
   return GPT2_OK;
@@ -1004,6 +1006,7 @@ gpt2_status gpt2_init(const gpt2_config* cfg, void* d_workspace, size_t ws_bytes
 gpt2_status gpt2_set_params(gpt2_t* h, const float* src, size_t n, int src_on_device) {
   if (!h || !src) return GPT2_E_ARG;
   if (n != (size_t)h->lay.P) return fail(h, GPT2_E_ARG, "n != gpt2_num_params");
+  h->kv_len = 0;  // cached keys and values belong to the old parameters
   HIPTRY(h, hipMemcpyAsync(h->params, src, n * 4,
                            src_on_device ? hipMemcpyDeviceToDevice : hipMemcpyHostToDevice,
                            h->stream));
@@ -1176,6 +1179,7 @@ gpt2_status gpt2_generate_cached(gpt2_t* h, const int32_t* d_prompt, int B, int 
   hipStream_t s = h->stream;
   h->have_targets = false;
   h->forward_done = false;
+  h->kv_len = 0;  // the loop overwrites the cache
   HIPTRY(h, hipMemcpy2DAsync(d_out, L * 4, d_prompt, (size_t)T0 * 4, (size_t)T0 * 4, B,
                              hipMemcpyDeviceToDevice, s));
   for (int step = 0; step < n_new; ++step) {
@@ -1185,7 +1189,7 @@ gpt2_status gpt2_generate_cached(gpt2_t* h, const int32_t* d_prompt, int B, int 
       // the last drawn token at position cur - 1 against the cached ones
       HIPTRY(h, hipMemcpy2DAsync(h->gen_idx, 4, d_out + (cur - 1), L * 4, 4, B,
                                  hipMemcpyDeviceToDevice, s));
-      st = run_decode(h, h->gen_idx, B, (int)(cur - 1));
+      st = run_decode(h, h->gen_idx, B, (int)(cur - 1), h->gen_logits);
     } else {
       // the prompt (filling the cache), or a window that has shifted: the
       // last block_size tokens at positions 0 .. T-1, recomputed whole
@@ -1202,6 +1206,45 @@ gpt2_status gpt2_generate_cached(gpt2_t* h, const int32_t* d_prompt, int B, int 
     HIPTRY(h, launch_sample(h->gen_logits, Vp, B, Vp, temperature, top_k, d_uniform + step, n_new,
                             d_out + cur, L, s));
   }
+  return GPT2_OK;
+}
+
+gpt2_status gpt2_prefill(gpt2_t* h, const int32_t* d_idx, int B, int T, float* d_logits) {
+  if (!h || !d_idx || !d_logits) return GPT2_E_ARG;
+  if (reinterpret_cast<uintptr_t>(d_logits) % 16)
+    return fail(h, GPT2_E_ARG, "d_logits must be 16-byte aligned");
+  if (B < 1 || B > h->cfg.max_batch || T < 1 || T > h->cfg.block_size)
+    return fail(h, GPT2_E_SHAPE, "need 1 <= B <= max_batch and 1 <= T <= block_size");
+  if (h->cfg.block_size > ATTN_DECODE_MAX_POS)
+    return fail(h, GPT2_E_ARG, "the key/value cache supports block_size <= 8192");
+  h->kv_len = 0;
+  h->have_targets = false;
+  h->forward_done = false;
+  gpt2_status st = run_forward(h, d_idx, nullptr, B, T, false, d_logits);
+  if (st != GPT2_OK) return st;
+  for (int l = 0; l < h->cfg.n_layer; ++l)
+    HIPTRY(h, launch_kv_append(h->act, h->A[l].qkv, kv_slot(h, l), B, T, 0, h->cfg.block_size,
+                               h->cfg.n_embd, h->stream));
+  h->kv_B = B;
+  h->kv_len = T;
+  return GPT2_OK;
+}
+
+gpt2_status gpt2_decode(gpt2_t* h, const int32_t* d_tok, int B, int p, float* d_logits) {
+  if (!h || !d_tok || !d_logits) return GPT2_E_ARG;
+  if (reinterpret_cast<uintptr_t>(d_logits) % 16)
+    return fail(h, GPT2_E_ARG, "d_logits must be 16-byte aligned");
+  if (h->kv_len < 1 || B != h->kv_B || p != h->kv_len)
+    return fail(h, GPT2_E_STATE, "gpt2_decode continues the sequences of the last gpt2_prefill "
+                                 "(same B) at the next position");
+  if (p >= h->cfg.block_size)
+    return fail(h, GPT2_E_SHAPE, "the cache is full (p must be < block_size)");
+  h->have_targets = false;
+  h->forward_done = false;
+  h->kv_len = 0;  // until this step has been issued
+  gpt2_status st = run_decode(h, d_tok, B, p, d_logits);
+  if (st != GPT2_OK) return st;
+  h->kv_len = p + 1;
   return GPT2_OK;
 }
 
@@ -1250,6 +1293,7 @@ gpt2_status gpt2_adamw_step(gpt2_t* h, float lr, float beta1, float beta2, float
     return fail(h, GPT2_E_ARG, "need 0 <= beta < 1 and eps >= 0");
   const gpt2_status st = settle_zero(h);
   if (st != GPT2_OK) return st;
+  h->kv_len = 0;  // cached keys and values belong to the old parameters
   h->step += 1;
   const double t = (double)h->step;
   const double bc1 = 1.0 - std::pow((double)beta1, t);

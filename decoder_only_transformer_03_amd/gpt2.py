@@ -72,6 +72,8 @@ def lib():
             "gpt2_sample": (i32, [vp, vp, ct.c_long, i32, i32, f32, i32, vp, vp]),
             "gpt2_generate": (i32, [vp, vp, i32, i32, i32, f32, i32, vp, vp]),
             "gpt2_generate_cached": (i32, [vp, vp, i32, i32, i32, f32, i32, vp, vp]),
+            "gpt2_prefill": (i32, [vp, vp, i32, i32, vp]),
+            "gpt2_decode": (i32, [vp, vp, i32, i32, vp]),
             "gpt2_get_loss": (i32, [vp, ct.POINTER(f32)]),
             "gpt2_zero_grad": (i32, [vp]),
             "gpt2_backward": (i32, [vp, f32]),
@@ -105,7 +107,7 @@ EXPORTED = ["gpt2_num_params", "gpt2_workspace_bytes", "gpt2_init", "gpt2_lr_at"
             "gpt2_get",
             "gpt2_set_state", "gpt2_get_step", "gpt2_set_step", "gpt2_forward", "gpt2_eval",
             "gpt2_forward_last", "gpt2_sample", "gpt2_generate", "gpt2_generate_cached",
-            "gpt2_get_loss",
+            "gpt2_prefill", "gpt2_decode", "gpt2_get_loss",
             "gpt2_zero_grad", "gpt2_backward", "gpt2_adamw_step", "gpt2_get_grad_norm",
             "gpt2_sync", "gpt2_last_error", "gpt2_destroy", "gpt2_get_activation",
             "gpt2_timing_begin", "gpt2_timing_end", "gpt2_wgrad_layout",
@@ -260,6 +262,16 @@ class GPT2:
         self._check(lib().gpt2_generate_cached(self.h, _ptr(prompt), B, T0, int(n_new),
                                                float(temperature), int(top_k), _ptr(uniforms),
                                                _ptr(out)))
+
+    def prefill(self, idx, logits):
+        """idx int32 (B, T); logits float32 (B, padded vocab), device tensors:
+        the prompt's keys and values kept, the logits of its last position."""
+        B, T = idx.shape
+        self._check(lib().gpt2_prefill(self.h, _ptr(idx), B, T, _ptr(logits)))
+
+    def decode(self, tok, p, logits):
+        """tok int32 (B,), the tokens at position p; logits as in prefill."""
+        self._check(lib().gpt2_decode(self.h, _ptr(tok), tok.shape[0], int(p), _ptr(logits)))
 
     def get_loss(self) -> float:
         loss = ct.c_float(0.0)

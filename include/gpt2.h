@@ -242,6 +242,36 @@ gpt2_status gpt2_generate_cached(gpt2_t* h, const int32_t* d_prompt, int B, int 
                                  float temperature, int top_k, const float* d_uniform,
                                  int32_t* d_out);
 
+/* The key/value-cached decoding of gpt2_generate_cached, one position per
+ * call, for callers that draw the tokens themselves ("GPT-2 from Scratch",
+ * A generation loop: the logits of the last position of each running
+ * sequence are what the loop samples from).
+ *
+ * gpt2_prefill runs the blocks over d_idx (device int32, (B, T) row-major,
+ * 1 <= B <= max_batch, 1 <= T <= block_size), keeps every block's keys and
+ * values of positions 0 .. T-1 in the workspace, and writes the logits of
+ * position T-1 of each sequence to d_logits (device fp32, (B, padded
+ * vocabulary) row-major, 16-byte aligned; entries past vocab_size are the
+ * products with the zero rows of the padded embedding).
+ *
+ * gpt2_decode takes d_tok (device int32, (B)), the token at position p of
+ * each sequence, where p is the number of positions already kept (the T of
+ * the last gpt2_prefill plus the gpt2_decode calls since) and B the batch of
+ * that gpt2_prefill; it runs the blocks for position p only, its attention
+ * reading the kept keys and values of positions 0 .. p-1 and keeping those
+ * of p, and writes the logits of position p to d_logits as above.
+ *
+ * Errors: GPT2_E_ARG for null or misaligned pointers (and block_size >
+ * 8192); GPT2_E_SHAPE for B or T out of range, or p = block_size (the cache
+ * is full); GPT2_E_STATE for a gpt2_decode that does not continue the kept
+ * sequences (no gpt2_prefill yet, another B or p; also after
+ * gpt2_set_params, gpt2_adamw_step or gpt2_generate_cached, which leave the
+ * kept keys and values stale).  Asynchronous: out-of-range token ids are
+ * reported by the next synchronising call.  Saved activations are not
+ * readable afterwards. */
+gpt2_status gpt2_prefill(gpt2_t* h, const int32_t* d_idx, int B, int T, float* d_logits);
+gpt2_status gpt2_decode(gpt2_t* h, const int32_t* d_tok, int B, int p, float* d_logits);
+
 /* Loss of the last forward with targets; waits for the stream. */
 gpt2_status gpt2_get_loss(gpt2_t* h, float* h_loss);
 

@@ -127,6 +127,8 @@ int main() {
   EXPECT(gpt2_sample(nullptr, nullptr, 4, 1, 1, 1.f, 0, nullptr, nullptr) == GPT2_E_ARG);
   EXPECT(gpt2_generate(nullptr, nullptr, 1, 1, 1, 1.f, 0, nullptr, nullptr) == GPT2_E_ARG);
   EXPECT(gpt2_generate_cached(nullptr, nullptr, 1, 1, 1, 1.f, 0, nullptr, nullptr) == GPT2_E_ARG);
+  EXPECT(gpt2_prefill(nullptr, nullptr, 1, 1, nullptr) == GPT2_E_ARG);
+  EXPECT(gpt2_decode(nullptr, nullptr, 1, 1, nullptr) == GPT2_E_ARG);
   EXPECT(gpt2_get_loss(nullptr, &f) == GPT2_E_ARG);
   EXPECT(gpt2_zero_grad(nullptr) == GPT2_E_ARG);
   EXPECT(gpt2_backward(nullptr, 1.f) == GPT2_E_ARG);

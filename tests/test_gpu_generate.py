@@ -294,3 +294,81 @@ def test_generate_cached_bf16_124m():
             assert np.any(top2[:, 1] - top2[:, 0] < 2 * tol), s
             break
     print(f"\nbf16 124M cached greedy: {np.sum(cached == full)} of {cached.size} tokens equal")
+
+
+def maxrel(got, ref):
+    return float(np.max(np.abs(got - ref)) / max(np.max(np.abs(ref)), 1e-30))
+
+
+def test_prefill_decode_fp32(tiny):
+    """gpt2_prefill + gpt2_decode, one position per call up to block_size: the
+    logits of every position within 1e-5 of the oracle's last-position logits
+    of the same context (measured: 5e-7; the tokens fed are fixed, not
+    drawn); the calls that do not continue the kept sequences, or run past
+    block_size, are refused."""
+    d, flat, m = tiny
+    cfg = O.Config(**d)
+    B, T0, Vp = 3, 5, d["padded_vocab_size"]
+    seq = np.random.default_rng(31).integers(0, d["vocab_size"], size=(B, cfg.block_size))
+    seq = seq.astype(np.int32)
+    lg = torch.zeros((B, Vp), dtype=torch.float32, device=DEV)
+    m.prefill(dev(seq[:, :T0], torch.int32), lg)
+    worst = maxrel(lg.cpu().numpy().astype(np.float64), O.last_logits(flat, seq[:, :T0], cfg))
+    for p in range(T0, cfg.block_size):
+        m.decode(dev(seq[:, p], torch.int32), p, lg)
+        ref = O.last_logits(flat, seq[:, :p + 1], cfg)
+        worst = max(worst, maxrel(lg.cpu().numpy().astype(np.float64), ref))
+    print(f"\nfp32 prefill + {cfg.block_size - T0} decode steps: worst maxrel {worst:.2e}")
+    assert worst < 1e-5
+    tok = dev(seq[:, 0], torch.int32)
+    with pytest.raises(G.GPT2Error) as e:  # the cache is full
+        m.decode(tok, cfg.block_size, lg)
+    assert e.value.status == G.GPT2_E_SHAPE
+    m.prefill(dev(seq[:, :T0], torch.int32), lg)
+    for bad_p in (T0 - 1, T0 + 1):
+        with pytest.raises(G.GPT2Error) as e:
+            m.decode(tok, bad_p, lg)
+        assert e.value.status == G.GPT2_E_STATE
+    with pytest.raises(G.GPT2Error) as e:  # another batch
+        m.decode(tok[:2], T0, lg)
+    assert e.value.status == G.GPT2_E_STATE
+    m.set_params(flat)  # the kept keys and values are stale now
+    with pytest.raises(G.GPT2Error) as e:
+        m.decode(tok, T0, lg)
+    assert e.value.status == G.GPT2_E_STATE
+
+
+@pytest.mark.parametrize("B,n_dec", [(2, 8), (16, 2), (17, 2)])
+def test_prefill_decode_bf16_124m(B, n_dec):
+    """GPT-2 124M bf16, the decoding kernels themselves: at B <= 16 each
+    LayerNorm runs inside the few-rows GEMM that reads it (ln_1 -> qkv, ln_2
+    -> fc, ln_f -> lm_head), the projections add the residual in the few-rows
+    kernel and the decode attention appends to the cache; B = 17 takes the
+    separate LayerNorm and the K-split GEMMs.  Every position's logits against
+    the oracle's last-position logits of the same context, within 1.2e-2 of
+    the largest: the bf16 full forward of the prompt (the first position
+    checked) lands at 7.0e-3, the decoded positions at 5.7e-3 to 7.8e-3, and
+    the bound is 1.5 times the largest of these."""
+    d = synthetic.model_dims("gpt2-124m")
+    cfg = O.Config(**d)
+    flat = synthetic.init_params(d, seed=42)
+    T0, Vp = 24, d["padded_vocab_size"]
+    seq, _ = synthetic.zipf_batch(B, T0 + n_dec, seed=90 + B)
+    seq = seq.astype(np.int32)
+    m = G.GPT2(G.make_config(max_batch=B, precision="bf16", **d), device=DEV)
+    try:
+        m.set_params(flat)
+        lg = torch.zeros((B, Vp), dtype=torch.float32, device=DEV)
+        got = []
+        m.prefill(dev(seq[:, :T0], torch.int32), lg)
+        got.append(lg.cpu().numpy().astype(np.float64))
+        for p in range(T0, T0 + n_dec - 1):
+            m.decode(dev(seq[:, p], torch.int32), p, lg)
+            got.append(lg.cpu().numpy().astype(np.float64))
+    finally:
+        m.close()
+    for i, g in enumerate(got):
+        ref = O.last_logits(flat, seq[:, :T0 + i], cfg).astype(np.float64)
+        err = maxrel(g, ref)
+        print(f"\nbf16 124M B={B} position {T0 + i - 1}: maxrel {err:.2e}")
+        assert err < 1.2e-2

@@ -75,7 +75,8 @@ def tiny():
     (512, 512, 1.0, 7, 0.5),                          # ties at the k-th value
     (50304, 50304, 1.0, 50, None), (50304, 50304, 0.8, 0, None),
     (50257, 50304, 1.0, 200, 0.25), (50304, 50304, 1.0, 50304, None),
-    (3, 4, 1.0, 2, None), (53248, 53248, 1.0, 5, None)])
+    (3, 4, 1.0, 2, None), (53248, 53248, 1.0, 5, None),
+    (50304, 50304, 1.0, 2000, None)])                 # k above the 1024 threads' maxima
 def test_sample_matches_oracle(tiny, V, ld, temperature, top_k, grid):
     _, _, m = tiny
     B = 64

@@ -301,13 +301,33 @@ def maxrel(got, ref):
     return float(np.max(np.abs(got - ref)) / max(np.max(np.abs(ref)), 1e-30))
 
 
+def with_vector_noise(d, flat, seed):
+    """The initial parameters with every LayerNorm gain at 1 + 0.1 N(0,1) and
+    every bias (LayerNorm and linear) at 0.1 N(0,1), instead of the init's
+    ones and zeros, so that the kernels' use of them is checked too."""
+    rng = np.random.default_rng(seed)
+    out = flat.copy()
+    off = 0
+    for shape, kind in synthetic._layout(d):
+        n = int(np.prod(shape))
+        if kind == "g":
+            out[off:off + n] = 1.0 + 0.1 * rng.standard_normal(n)
+        elif kind == "b":
+            out[off:off + n] = 0.1 * rng.standard_normal(n)
+        off += n
+    assert off == flat.size
+    return out
+
+
 def test_prefill_decode_fp32(tiny):
     """gpt2_prefill + gpt2_decode, one position per call up to block_size: the
     logits of every position within 1e-5 of the oracle's last-position logits
     of the same context (measured: 5e-7; the tokens fed are fixed, not
     drawn); the calls that do not continue the kept sequences, or run past
     block_size, are refused."""
-    d, flat, m = tiny
+    d, flat0, m = tiny
+    flat = with_vector_noise(d, flat0, seed=5)
+    m.set_params(flat)
     cfg = O.Config(**d)
     B, T0, Vp = 3, 5, d["padded_vocab_size"]
     seq = np.random.default_rng(31).integers(0, d["vocab_size"], size=(B, cfg.block_size))
@@ -333,26 +353,34 @@ def test_prefill_decode_fp32(tiny):
     with pytest.raises(G.GPT2Error) as e:  # another batch
         m.decode(tok[:2], T0, lg)
     assert e.value.status == G.GPT2_E_STATE
-    m.set_params(flat)  # the kept keys and values are stale now
+    m.set_params(flat0)  # the kept keys and values are stale now (and the fixture's again)
     with pytest.raises(G.GPT2Error) as e:
         m.decode(tok, T0, lg)
     assert e.value.status == G.GPT2_E_STATE
 
 
-@pytest.mark.parametrize("B,n_dec", [(2, 8), (16, 2), (17, 2)])
-def test_prefill_decode_bf16_124m(B, n_dec):
-    """GPT-2 124M bf16, the decoding kernels themselves: at B <= 16 each
-    LayerNorm runs inside the few-rows GEMM that reads it (ln_1 -> qkv, ln_2
-    -> fc, ln_f -> lm_head), the projections add the residual in the few-rows
-    kernel and the decode attention appends to the cache; B = 17 takes the
-    separate LayerNorm and the K-split GEMMs.  Every position's logits against
-    the oracle's last-position logits of the same context, within 1.2e-2 of
-    the largest: the bf16 full forward of the prompt (the first position
-    checked) lands at 7.0e-3, the decoded positions at 5.7e-3 to 7.8e-3, and
-    the bound is 1.5 times the largest of these."""
-    d = synthetic.model_dims("gpt2-124m")
+@pytest.mark.parametrize("model,B,n_dec", [("gpt2-124m", 2, 8), ("gpt2-124m", 16, 2),
+                                           ("gpt2-124m", 17, 2), ("xl-width", 3, 4)])
+def test_prefill_decode_bf16(model, B, n_dec):
+    """bf16, the decoding kernels themselves, with LayerNorm gains and all
+    biases away from the init's ones and zeros: at B <= 16 each LayerNorm runs
+    inside the few-rows GEMM that reads it (ln_1 -> qkv, ln_2 -> fc, ln_f ->
+    lm_head), the projections add the residual in the few-rows kernel and
+    the decode attention appends to the cache; B = 17 takes the separate
+    LayerNorm and the K-split GEMMs.  The XL width (2 blocks of C = 1600, 25
+    heads) normalises 1600-wide rows in the fused prologue and runs the
+    fcproj's K = 6400 in two batches of loads per wavefront.  Every
+    position's logits against the oracle's last-position logits of the same
+    context, within 1.2e-2 of the largest.  Measured: 124M 2.8e-3 for the
+    prompt's full forward (the first position checked) and 3.0e-3 to 3.8e-3
+    for the decoded positions (5.7e-3 to 7.8e-3 with the init's vectors);
+    XL width 4.9e-3 to 5.8e-3.  The bound is about twice the largest."""
+    if model == "xl-width":
+        d = dict(synthetic.model_dims("gpt2-xl"), n_layer=2)
+    else:
+        d = synthetic.model_dims(model)
     cfg = O.Config(**d)
-    flat = synthetic.init_params(d, seed=42)
+    flat = with_vector_noise(d, synthetic.init_params(d, seed=42), seed=7)
     T0, Vp = 24, d["padded_vocab_size"]
     seq, _ = synthetic.zipf_batch(B, T0 + n_dec, seed=90 + B)
     seq = seq.astype(np.int32)
@@ -371,5 +399,5 @@ def test_prefill_decode_bf16_124m(B, n_dec):
     for i, g in enumerate(got):
         ref = O.last_logits(flat, seq[:, :T0 + i], cfg).astype(np.float64)
         err = maxrel(g, ref)
-        print(f"\nbf16 124M B={B} position {T0 + i - 1}: maxrel {err:.2e}")
+        print(f"\nbf16 {model} B={B} position {T0 + i - 1}: maxrel {err:.2e}")
         assert err < 1.2e-2

@@ -90,9 +90,11 @@ def test_gemm_accumulate(mode, layout):
 # and K a multiple of 32 the product runs on the few-rows kernel (16 output
 # columns per workgroup, K split over 16 wavefronts); ragged N and M = 1 included
 # (7, 33000, 96): four column tiles per workgroup, a ragged last workgroup, and
-# K ranges that are empty for some wavefronts (3 chunks over 4 ranges)
+# K ranges that are empty for some wavefronts (3 chunks over 4 ranges);
+# (5, 200, 8320) and (3, 32832, 4160): more than 8 chunks per wavefront, so
+# the operands come in several batches of loads (one and four column tiles)
 SKINNY = [(1, 2304, 768), (16, 3072, 768), (8, 768, 3072), (5, 50304, 768), (3, 776, 64),
-          (12, 8, 32), (16, 136, 96), (7, 33000, 96)]
+          (12, 8, 32), (16, 136, 96), (7, 33000, 96), (5, 200, 8320), (3, 32832, 4160)]
 
 
 @pytest.mark.parametrize("mode", [0, 1])

@@ -85,6 +85,25 @@ def init_params(d, seed=42, dtype=np.float32):
     return np.concatenate(parts).astype(dtype, copy=False)
 
 
+def perturb_vectors(d, flat, seed, scale=0.1):
+    """A copy of flat with every LayerNorm gain at 1 + scale N(0,1) and every
+    bias (LayerNorm and linear) at scale N(0,1), in place of the init's ones
+    and zeros: parameters a trained model could hold, on which a wrong use of
+    a gain or a bias shows from the first step."""
+    rng = np.random.default_rng(seed)
+    out = np.array(flat, copy=True)
+    off = 0
+    for shape, kind in _layout(d):
+        n = int(np.prod(shape))
+        if kind == "g":
+            out[off:off + n] = 1.0 + scale * rng.standard_normal(n)
+        elif kind == "b":
+            out[off:off + n] = scale * rng.standard_normal(n)
+        off += n
+    assert off == out.size
+    return out
+
+
 def uniform_batch(B, T, vocab, seed):
     """ids uniform in [0, vocab); returns (idx, targets) int64 (B, T)."""
     rng = np.random.default_rng(seed)

@@ -32,7 +32,15 @@ fixed by a bf16 computation only where |g| clearly exceeds the rounding
 noise, so the elements compared are those with |g_ref| above K_FLOOR times
 the rms over the element's row of g_emul - g_ref.  Over those, parameters
 agree within TOL_PARAM normwise per tensor; the elements below the floor may
-differ by at most 2 lr, and may be at most MAX_BELOW of all elements.
+differ by at most 2 lr, and may be at most MAX_BELOW of all elements.  How
+many fall there depends on the parameters: once the LayerNorm and key biases
+give all keys of a head a large common part, the query and key rows of
+c_attn.weight carry the rounding noise of two sums that are exactly zero
+(each row of dS sums to zero, and so do the key gradients over positions)
+times that common part, above most of their exact gradient.  In a 124M step
+at B=2, T=1024 with gains and biases drawn around the init's ones and zeros
+(0.1 N(0,1) off them) 70-90% of those rows' elements fall under the floor,
+11% of all elements; with the init's own ones and zeros, 5%.
 
 Parameters after a step t >= 2 taken from the same state on both sides
 (the GPU's parameters and moments copied into the oracle): the previous
@@ -74,7 +82,7 @@ ROW_SLACK = 2e-2      # ... plus this times the tensor's median row norm
 F_STEP = 6.0          # t >= 2: parameters and moments within this times the rounded oracle's error
 K_FLOOR = 8.0         # compared parameters at t = 1: |g_ref| above this times the row's noise rms
 TOL_PARAM = 5e-3      # per-tensor normwise parameter error
-MAX_BELOW = 0.1       # largest fraction of elements under the floor at t = 1
+MAX_BELOW = 0.15      # largest fraction of elements under the floor at t = 1
 TOL_MOM = 2e-2        # per-tensor normwise error of m and v at t >= 2
 TOL_NORM = 2e-2       # relative error of the pre-clip gradient norm
 TOL_ADAMW = 1e-5      # the GPU's own gradients through the oracle's AdamW

@@ -97,7 +97,7 @@ def compare(d, flat, g, r, keep, what):
 @pytest.fixture(scope="module")
 def b16():
     d = synthetic.model_dims("gpt2-124m")
-    flat = synthetic.init_params(d, seed=42)
+    flat = synthetic.perturb_vectors(d, synthetic.init_params(d, seed=42), seed=13)
     idx, tgt = synthetic.zipf_batch(16, 1024, seed=1002)
     keep = [0, 15]
     idx, tgt_m = masked_batch(idx, tgt, keep)
@@ -117,7 +117,7 @@ def test_xl_width_b8_backward_matches_oracle():
     partial tiles in the forward products, the input-gradient products and
     the grouped weight gradients; B = 8 as in the XL workload."""
     d = dict(synthetic.model_dims("gpt2-xl"), n_layer=2)
-    flat = synthetic.init_params(d, seed=42)
+    flat = synthetic.perturb_vectors(d, synthetic.init_params(d, seed=42), seed=14)
     idx, tgt = synthetic.zipf_batch(8, 1024, seed=1005)
     keep = [0, 7]
     idx, tgt_m = masked_batch(idx, tgt, keep)

@@ -301,24 +301,6 @@ def maxrel(got, ref):
     return float(np.max(np.abs(got - ref)) / max(np.max(np.abs(ref)), 1e-30))
 
 
-def with_vector_noise(d, flat, seed):
-    """The initial parameters with every LayerNorm gain at 1 + 0.1 N(0,1) and
-    every bias (LayerNorm and linear) at 0.1 N(0,1), instead of the init's
-    ones and zeros, so that the kernels' use of them is checked too."""
-    rng = np.random.default_rng(seed)
-    out = flat.copy()
-    off = 0
-    for shape, kind in synthetic._layout(d):
-        n = int(np.prod(shape))
-        if kind == "g":
-            out[off:off + n] = 1.0 + 0.1 * rng.standard_normal(n)
-        elif kind == "b":
-            out[off:off + n] = 0.1 * rng.standard_normal(n)
-        off += n
-    assert off == flat.size
-    return out
-
-
 def test_prefill_decode_fp32(tiny):
     """gpt2_prefill + gpt2_decode, one position per call up to block_size: the
     logits of every position within 1e-5 of the oracle's last-position logits
@@ -326,7 +308,7 @@ def test_prefill_decode_fp32(tiny):
     drawn); the calls that do not continue the kept sequences, or run past
     block_size, are refused."""
     d, flat0, m = tiny
-    flat = with_vector_noise(d, flat0, seed=5)
+    flat = synthetic.perturb_vectors(d, flat0, seed=5)
     m.set_params(flat)
     cfg = O.Config(**d)
     B, T0, Vp = 3, 5, d["padded_vocab_size"]
@@ -380,7 +362,7 @@ def test_prefill_decode_bf16(model, B, n_dec):
     else:
         d = synthetic.model_dims(model)
     cfg = O.Config(**d)
-    flat = with_vector_noise(d, synthetic.init_params(d, seed=42), seed=7)
+    flat = synthetic.perturb_vectors(d, synthetic.init_params(d, seed=42), seed=7)
     T0, Vp = 24, d["padded_vocab_size"]
     seq, _ = synthetic.zipf_batch(B, T0 + n_dec, seed=90 + B)
     seq = seq.astype(np.int32)

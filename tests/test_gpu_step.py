@@ -122,7 +122,7 @@ def run_oracle_step(d, flat, idx, tgt, lr=LR, wd=WD, dtype=np.float32, emul=Fals
 def test_fp32_tiny_step_matches_oracle(B, T, hc):
     d = synthetic.model_dims("tiny")
     cfg = O.Config(**d)
-    flat = synthetic.init_params(d, seed=42)
+    flat = synthetic.perturb_vectors(d, synthetic.init_params(d, seed=42), seed=11 + T)
     idx, tgt = synthetic.uniform_batch(B, T, 512, seed=1001 + T)
     if B == 2:
         tgt[0, :20] = -1                      # masked positions
@@ -366,7 +366,7 @@ def test_fused_head_edges():
 @pytest.fixture(scope="module")
 def step_124m_b2():
     d = synthetic.model_dims("gpt2-124m")
-    flat = synthetic.init_params(d, seed=42)
+    flat = synthetic.perturb_vectors(d, synthetic.init_params(d, seed=42), seed=12)
     idx, tgt = synthetic.zipf_batch(2, 1024, seed=1002)
     g = run_gpu_step(d, "bf16", flat, idx, tgt)
     r = run_oracle_step(d, flat, idx, tgt, emul=True)

@@ -113,7 +113,7 @@ def gpu_opt_step(model, micro, lr, wd=WD):
 def test_fp32_accumulation_and_schedule_trajectory():
     d = synthetic.model_dims("tiny")
     cfg = O.Config(**d)
-    flat = synthetic.init_params(d, seed=42)
+    flat = synthetic.perturb_vectors(d, synthetic.init_params(d, seed=42), seed=15)
     model = G.GPT2(G.make_config(max_batch=2, precision="fp32", **d), device=DEV)
     model.set_params(flat)
     p, m, v = flat.copy(), np.zeros_like(flat), np.zeros_like(flat)
@@ -179,7 +179,7 @@ def check_fp32_step_state(cfg, model, t, lr, g_gpu, g_ref, pre, p, m, v, kb):
 def test_bf16_124m_accumulation_and_schedule_from_shared_state():
     d = synthetic.model_dims("gpt2-124m")
     cfg = O.Config(**d)
-    flat = synthetic.init_params(d, seed=42)
+    flat = synthetic.perturb_vectors(d, synthetic.init_params(d, seed=42), seed=16)
     model = G.GPT2(G.make_config(max_batch=2, precision="bf16", **d), device=DEV)
     try:
         model.set_params(flat)

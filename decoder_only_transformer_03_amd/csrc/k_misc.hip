@@ -1048,12 +1048,6 @@ __global__ __launch_bounds__(256) void f32_to_bf16_kernel(const float* __restric
   for (; i < n; i += (long)gridDim.x * 256) d[i] = f2bf(s[i]);
 }
 
-__global__ __launch_bounds__(256) void bf16_to_f32_kernel(const bf16_t* __restrict__ s,
-                                                          float* __restrict__ d, long n) {
-  long i = (long)blockIdx.x * 256 + threadIdx.x;
-  for (; i < n; i += (long)gridDim.x * 256) d[i] = bf2f(s[i]);
-}
-
 // ===========================================================================
 // launchers
 // ===========================================================================
@@ -1302,9 +1296,3 @@ hipError_t launch_f32_to_bf16(const float* src, bf16_t* dst, long n, hipStream_t
   return hipGetLastError();
 }
 
-hipError_t launch_bf16_to_f32(const bf16_t* src, float* dst, long n, hipStream_t s) {
-  long blocks = (n + 255) / 256;
-  if (blocks > 16384) blocks = 16384;
-  bf16_to_f32_kernel<<<(unsigned)(blocks < 1 ? 1 : blocks), 256, 0, s>>>(src, dst, n);
-  return hipGetLastError();
-}

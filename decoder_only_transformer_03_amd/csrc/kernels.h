@@ -107,7 +107,6 @@ hipError_t launch_fill(float* p, long n, float val, hipStream_t s);
 // 0 <= i < n (Philox4x32-10 counters, Box-Muller; k_init.hip).
 hipError_t launch_init_normal(float* p, long n, long e0, float std, uint64_t seed, hipStream_t s);
 hipError_t launch_f32_to_bf16(const float* src, bf16_t* dst, long n, hipStream_t s);
-hipError_t launch_bf16_to_f32(const bf16_t* src, float* dst, long n, hipStream_t s);
 
 // C[m][n] = sum_k A(m,k) B(n,k) followed by epilogue `epi`, where
 // A(m,k) = a_t ? A[k*lda + m] : A[m*lda + k] and B(n,k) = b_t ? B[k*ldb + n] : B[n*ldb + k].

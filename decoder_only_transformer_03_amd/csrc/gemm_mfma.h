@@ -299,14 +299,23 @@ template <> struct In8<bf16_t> {
 // each -- 8 lanes cover the 64 columns of a row -- apply the elementwise
 // epilogue and store 16-byte pieces, so one store instruction writes 8
 // complete row segments.
+// Rows per epilogue round: 32, or 16 when the wavefronts' 32-row buffers
+// would not fit one LDS stage (16 wavefronts on a 256 x 256 tile); a round
+// buffer takes ROWS x 64 fp32 = ROWS x 128 bf16 elements of scratch.
+template <int BM, int BN, int WM, int WN>
+constexpr int epi_rows() {
+  return (BM + BN) * BK >= WM * WN * 32 * 128 ? 32 : 16;
+}
+
 template <int BM, int BN, int WM, int WN, int EPI, typename TO, int SN, int SM>
 __device__ __forceinline__ void tile_epilogue(const EpiArgs& e, const f32x16_t (&acc)[SN][SM],
                                               long m0, long n0, int split, int M, int N, int lane,
                                               int wm, int wn, bf16_t* scratch) {
   constexpr int WTM = BM / WM, WTN = BN / WN;
+  constexpr int ROWS = epi_rows<BM, BN, WM, WN>();
   static_assert(WTN == 64, "staged epilogue assumes 64-column wavefront sub-tiles");
-  static_assert((BM + BN) * BK >= WM * WN * 4096, "epilogue scratch must fit one LDS stage");
-  float* sf = reinterpret_cast<float*>(scratch);  // [32 rows][64 fp32]
+  static_assert((BM + BN) * BK >= WM * WN * ROWS * 128, "epilogue scratch must fit one LDS stage");
+  float* sf = reinterpret_cast<float*>(scratch);  // [ROWS rows][64 fp32]
   const long mw = m0 + wm * WTM;                  // first row of the sub-tile
   const long nl = n0 + wn * WTN + (lane & 7) * 8; // this lane's 8 columns in the read phase
   const bool ncol = nl < N;
@@ -365,9 +374,12 @@ __device__ __forceinline__ void tile_epilogue(const EpiArgs& e, const f32x16_t (
         else pre[r8].load(reinterpret_cast<const TO*>(e.aux) + mc * e.ldx + nc);
       }
     }
-    // (1) fragments -> round buffer (row = lane%32, one 16-byte chunk each)
-    {
-      const int row = lane & 31;
+#pragma unroll
+    for (int hr = 0; hr < 32 / ROWS; ++hr) {
+    // (1) fragments -> round buffer (row = lane%32, one 16-byte chunk each;
+    // with 16-row rounds, the lanes whose row lies in this round)
+    if (ROWS == 32 || ((lane & 31) >> 4) == hr) {
+      const int row = (lane & 31) - hr * ROWS;
 #pragma unroll
       for (int sn = 0; sn < SN; ++sn)
 #pragma unroll
@@ -381,11 +393,12 @@ __device__ __forceinline__ void tile_epilogue(const EpiArgs& e, const f32x16_t (
     }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
-    // (2) rows of the round -> global, 8 lanes per row
+    // (2) rows of the round -> global, 8 lanes per row; r8 counts the round's
+    // 8-row groups over the whole 32-row block
 #pragma unroll
-    for (int r8 = 0; r8 < 4; ++r8) {
-      const int row = r8 * 8 + (lane >> 3);
-      const long m = mw + sm * 32 + row;
+    for (int r8 = hr * (ROWS / 8); r8 < (hr + 1) * (ROWS / 8); ++r8) {
+      const int row = r8 * 8 + (lane >> 3) - hr * ROWS;
+      const long m = mw + sm * 32 + hr * ROWS + row;
       const int c0 = (2 * (lane & 7)) ^ (row & 7), c1 = (2 * (lane & 7) + 1) ^ (row & 7);
       const float4 a = *reinterpret_cast<const float4*>(sf + row * 64 + c0 * 4);
       const float4 b = *reinterpret_cast<const float4*>(sf + row * 64 + c1 * 4);
@@ -466,6 +479,7 @@ __device__ __forceinline__ void tile_epilogue(const EpiArgs& e, const f32x16_t (
     }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
+    }
   }
   if constexpr (EPI == EPI_GELU_BWD) {
     if (e.colsum) {
@@ -851,13 +865,15 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(int M, int N, int
       eg.out = P.out;
       eg.ldo = P.ldo;
       eg.alpha = P.scaled ? P.alpha * e.alpha : P.alpha;
-      tile_epilogue<BM, BN, WM, WN, EPI, TO, SN, SM>(eg, acc, em0, en0, esplit, P.M, P.N, lane, wm,
-                                                     wn, smem[cur ^ 1] + wave * 4096);
+      tile_epilogue<BM, BN, WM, WN, EPI, TO, SN, SM>(
+          eg, acc, em0, en0, esplit, P.M, P.N, lane, wm, wn,
+          smem[cur ^ 1] + wave * (epi_rows<BM, BN, WM, WN>() * 128));
     } else if constexpr (EPI == EPI_LSE)
       lse_epilogue<BM, BN, WM, WN, SN, SM>(e, acc, em0, en0, M, N, lane, wm, wn);
     else if constexpr (WTN == 64)
-      tile_epilogue<BM, BN, WM, WN, EPI, TO, SN, SM>(e, acc, em0, en0, esplit, M, N, lane, wm, wn,
-                                                     smem[cur ^ 1] + wave * 4096);
+      tile_epilogue<BM, BN, WM, WN, EPI, TO, SN, SM>(
+          e, acc, em0, en0, esplit, M, N, lane, wm, wn,
+          smem[cur ^ 1] + wave * (epi_rows<BM, BN, WM, WN>() * 128));
     else
       tile_epilogue_w96<BM, BN, WM, WN, EPI, TO, SN, SM>(e, acc, em0, en0, esplit, M, N, lane, wm,
                                                          wn, smem[cur ^ 1] + wave * 3200);
@@ -912,10 +928,10 @@ inline hipError_t run_grouped_accum_tt(const GemmProblem* d_probs, int nprobs, l
   const int nkt = K / BK;
   long grid = total_tiles < persistent_slots() ? total_tiles : persistent_slots();
   if (store)
-    gemm_kernel<256, 256, 2, 4, 3, 3, EPI_STORE, float, true><<<(unsigned)grid, 512, 0, s>>>(
+    gemm_kernel<256, 256, 4, 4, 3, 3, EPI_STORE, float, true><<<(unsigned)grid, 1024, 0, s>>>(
         0, 0, K, nullptr, 0, nullptr, 0, e, (int)total_tiles, 1, nkt, d_probs, nprobs);
   else
-    gemm_kernel<256, 256, 2, 4, 3, 3, EPI_ACCUM, float, true><<<(unsigned)grid, 512, 0, s>>>(
+    gemm_kernel<256, 256, 4, 4, 3, 3, EPI_ACCUM, float, true><<<(unsigned)grid, 1024, 0, s>>>(
         0, 0, K, nullptr, 0, nullptr, 0, e, (int)total_tiles, 1, nkt, d_probs, nprobs);
   return hipGetLastError();
 }

@@ -164,9 +164,13 @@ __global__ __launch_bounds__(SORT_THREADS) void id_sort_kernel(const int32_t* __
 // 16 bits carries the position along.  3-bit digits; 512 threads own 32
 // consecutive elements each, element e at LDS word e + e/32 so that the
 // threads of a wavefront stepping through their own ranges hit different
-// banks.  Per-thread digit counters live in LDS (column t of cnt): outside
-// the scan only thread t touches them, so its atomic adds there are plain
-// in-order counters.  The sorted ids and positions go to (ka, va).
+// banks.  A thread counts the digits of its elements in registers: eight
+// 6-bit fields of one 64-bit word (at most 32 per digit).  The counts go to
+// column t of cnt ([digit][thread]) for the workgroup scan, which turns them
+// into the first output slot of each (digit, thread); the scatter then gives
+// an element that slot plus the number of its digit's elements already
+// placed by the thread, counted again in a packed word, so no step waits on
+// an LDS atomic.  The sorted ids and positions go to (ka, va).
 constexpr int SORT_LDS_N = 16384;
 constexpr int SORT_LDS_THREADS = 512;
 constexpr int SORT_LDS_DIGITS = 8;
@@ -192,15 +196,17 @@ __global__ __launch_bounds__(SORT_LDS_THREADS) void id_sort_lds_kernel(
     const int shift = 16 + 3 * pass;
     const uint32_t* ks = buf[src];
     uint32_t* kd = buf[src ^ 1];
-#pragma unroll
-    for (int d = 0; d < SORT_LDS_DIGITS; ++d) cnt[d * SORT_LDS_THREADS + t] = 0;
+    uint64_t packed = 0;  // 6-bit count of digit d at bits 6d
 #pragma unroll 8
     for (int j = 0; j < PER; ++j) {
       const int i = e0 + j;
       if (i >= e1) break;
       const uint32_t d = (ks[sort_slot(i)] >> shift) & 7u;
-      atomicAdd(&cnt[d * SORT_LDS_THREADS + t], 1u);
+      packed += 1ull << (6 * d);
     }
+#pragma unroll
+    for (int d = 0; d < SORT_LDS_DIGITS; ++d)
+      cnt[d * SORT_LDS_THREADS + t] = (uint32_t)(packed >> (6 * d)) & 63u;
     __syncthreads();
     // exclusive scan over the flattened (digit, thread) counters
     uint32_t loc[SORT_LDS_DIGITS], sum = 0;
@@ -215,12 +221,15 @@ __global__ __launch_bounds__(SORT_LDS_THREADS) void id_sort_lds_kernel(
     for (int j = 0; j < SORT_LDS_DIGITS; ++j) cnt[SORT_LDS_DIGITS * t + j] = base + loc[j];
     __syncthreads();
     // scatter in order: each element takes the next slot of its digit
+    uint64_t placed = 0;
 #pragma unroll 8
     for (int j = 0; j < PER; ++j) {
       const int i = e0 + j;
       if (i >= e1) break;
       const uint32_t k = ks[sort_slot(i)];
-      const uint32_t o = atomicAdd(&cnt[((k >> shift) & 7u) * SORT_LDS_THREADS + t], 1u);
+      const uint32_t d = (k >> shift) & 7u;
+      const uint32_t o = cnt[d * SORT_LDS_THREADS + t] + ((uint32_t)(placed >> (6 * d)) & 63u);
+      placed += 1ull << (6 * d);
       kd[sort_slot((int)o)] = k;
     }
     __syncthreads();

@@ -7,14 +7,18 @@
 // k-contiguous), input gradient dx = dy W (B transposed), weight gradient
 // dW = dy^T x (both transposed).
 //
-// Block tile BM x BN x 64 with 4 wavefronts in a 2 x 2 grid; each wavefront
-// owns a (BM/2) x (BN/2) sub-tile of 32x32 MFMA tiles.  Operand tiles live in
-// LDS as [row][64 k] bf16 with the 16-byte chunk index XOR-swizzled by the row
-// (conflict-free ds_read_b128 of MFMA fragments).  A transposed operand is
-// turned k-contiguous on its way into LDS: each thread loads an 8 (k) x 8 (row)
-// block with eight 16-byte loads and transposes it in registers with
-// v_perm_b32.  Two LDS stages: the global loads of tile k+1 are in flight while
-// the MFMAs of tile k run; one barrier per k-tile.
+// Block tile BM x BN x 64 with WM x WN wavefronts (2 x 4 or 4 x 2, and 4 x 4
+// for the weight gradients); each wavefront owns a (BM/WM) x (BN/WN)
+// sub-tile of 32x32 MFMA tiles.  When K is a multiple of 64 the operand
+// tiles go straight from global memory to LDS (global_load_lds): a
+// k-contiguous operand as [row][64 k] bf16 with the 16-byte chunk index
+// XOR-swizzled by the row (conflict-free ds_read_b128 of MFMA fragments), a
+// transposed one as [64 k][rows], whose fragments are gathered with LDS
+// transpose reads (ds_read_b64_tr_b16).  Otherwise the tiles pass through
+// registers, and a transposed operand is turned k-contiguous on the way: each
+// thread loads an 8 (k) x 8 (row) block and transposes it with v_perm_b32.
+// Two LDS stages: the global loads of tile k+1 are in flight while the MFMAs
+// of tile k run; one barrier per k-tile.
 //
 // MFMA role assignment: the matrix-core "row" operand is the B tile (n) and
 // the "column" operand the A tile (m), so each lane's accumulator holds four
@@ -291,8 +295,8 @@ template <> struct In8<bf16_t> {
 // Epilogue of one output tile, staged through LDS so that global memory sees
 // whole row segments.  acc[sn][sm][4i + j] is C[m][n] with m = sm*32 +
 // lane%32 and n = sn*32 + 8i + 4(lane/32) + j inside the wavefront's
-// (BM/WM) x (BN/WN) sub-tile.  Each wavefront owns 8 KB of scratch LDS and
-// moves its sub-tile in rounds of 32 rows: (1) lanes write alpha * their
+// (BM/WM) x (BN/WN) sub-tile.  Each wavefront owns a round buffer of scratch
+// LDS and moves its sub-tile in rounds of rows: (1) lanes write alpha * their
 // accumulator fragments, fp32, into a row-major round buffer (16-byte chunks
 // XOR-swizzled by row, so both the fragment writes and the row reads are
 // bank-conflict free); (2) lanes read back 8 consecutive columns of one row
@@ -857,8 +861,8 @@ __global__ __launch_bounds__(64 * WM * WN, 1) void gemm_kernel(int M, int N, int
     }
     if constexpr (LA >= 2 || LB >= 2) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();  // the last k-tile's stage is free; the next k-tile is in LDS
-    // the stage not holding the next item's first k-tile is free: 8 KB of
-    // epilogue scratch per wavefront
+    // the stage not holding the next item's first k-tile is free: one
+    // epilogue round buffer per wavefront (epi_rows x 256 bytes)
     if constexpr (GRP) {
       const GemmProblem& P = probs[eprob];
       EpiArgs eg = e;

@@ -161,85 +161,110 @@ __global__ __launch_bounds__(SORT_THREADS) void id_sort_kernel(const int32_t* __
 
 // The same sort held in LDS, for n <= SORT_LDS_N positions and ids below
 // 2^16: each element is packed as id << 16 | position, so sorting by the top
-// 16 bits carries the position along.  3-bit digits; 512 threads own 32
-// consecutive elements each, element e at LDS word e + e/32 so that the
-// threads of a wavefront stepping through their own ranges hit different
-// banks.  A thread counts the digits of its elements in registers: eight
-// 6-bit fields of one 64-bit word (at most 32 per digit).  The counts go to
-// column t of cnt ([digit][thread]) for the workgroup scan, which turns them
-// into the first output slot of each (digit, thread); the scatter then gives
-// an element that slot plus the number of its digit's elements already
-// placed by the thread, counted again in a packed word, so no step waits on
-// an LDS atomic.  The sorted ids and positions go to (ka, va).
+// 16 bits carries the position along.  8-bit digits, so one or two passes.
+// Wavefront w owns the contiguous chunk [w*chunk, (w+1)*chunk) and walks it
+// 64 elements at a time, lane l taking element s0 + l.  The lanes holding
+// the same digit are found with eight ballots (one per digit bit); a lane's
+// rank among them is the number of such lanes below it, and the lowest of
+// them (rank 0) advances the wavefront's running offset for that digit.
+// Counting (LDS atomic adds: the count does not depend on their order) fills
+// cnt[w][digit]; the workgroup turns the counts into output offsets
+// (digits in order, within a digit the wavefronts in order); the scatter
+// walks the chunk again in the same order, so equal ids keep their order.
+// The sorted ids and positions go to (ka, va).
 constexpr int SORT_LDS_N = 16384;
-constexpr int SORT_LDS_THREADS = 512;
-constexpr int SORT_LDS_DIGITS = 8;
-__device__ __forceinline__ int sort_slot(int e) { return e + (e >> 5); }
+constexpr int SORT_LDS_THREADS = 1024;
+constexpr int SORT_LDS_WAVES = SORT_LDS_THREADS / 64;
+
+// Lanes (among the active ones) whose digit equals this lane's.
+__device__ __forceinline__ uint64_t same_digit_lanes(uint32_t d, bool active) {
+  uint64_t m = __ballot(active);
+#pragma unroll
+  for (int b = 0; b < 8; ++b) {
+    const bool bit = (d >> b) & 1u;
+    const uint64_t set = __ballot(bit);
+    m &= bit ? set : ~set;
+  }
+  return m;
+}
+
 __global__ __launch_bounds__(SORT_LDS_THREADS) void id_sort_lds_kernel(
     const int32_t* __restrict__ idx, int n, int npass, uint32_t* __restrict__ ka,
     uint32_t* __restrict__ va) {
-  __shared__ uint32_t buf[2][SORT_LDS_N + SORT_LDS_N / 32];
-  __shared__ uint32_t cnt[SORT_LDS_DIGITS * SORT_LDS_THREADS];  // [digit][thread]
-  __shared__ uint32_t wsum[SORT_LDS_THREADS / 64 + 1];
-  constexpr int PER = SORT_LDS_N / SORT_LDS_THREADS;
-  const int t = threadIdx.x;
-  const int e0 = t * PER, e1 = e0 + PER < n ? e0 + PER : n;  // (empty when e0 >= n)
-  // (fixed trip counts below, so that the loads of a loop are issued together)
-#pragma unroll 16
-  for (int j = 0; j < PER; ++j) {
+  __shared__ uint32_t buf[2][SORT_LDS_N];
+  __shared__ uint32_t cnt[SORT_LDS_WAVES][256];  // per wavefront and digit
+  __shared__ uint32_t dbase[256];                // first output slot of each digit
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const uint64_t below = (1ull << lane) - 1;
+  const int chunk = (n + SORT_LDS_WAVES - 1) / SORT_LDS_WAVES;
+  const int c0 = w * chunk, c1 = c0 + chunk < n ? c0 + chunk : n;  // (empty when c0 >= n)
+  // (fixed trip count, so that the loads are issued together)
+#pragma unroll
+  for (int j = 0; j < SORT_LDS_N / SORT_LDS_THREADS; ++j) {
     const int i = j * SORT_LDS_THREADS + t;
-    if (i < n) buf[0][sort_slot(i)] = ((uint32_t)idx[i] << 16) | (uint32_t)i;
+    if (i < n) buf[0][i] = ((uint32_t)idx[i] << 16) | (uint32_t)i;
   }
   __syncthreads();
   int src = 0;
   for (int pass = 0; pass < npass; ++pass) {
-    const int shift = 16 + 3 * pass;
+    const int shift = 16 + 8 * pass;
     const uint32_t* ks = buf[src];
     uint32_t* kd = buf[src ^ 1];
-    uint64_t packed = 0;  // 6-bit count of digit d at bits 6d
-#pragma unroll 8
-    for (int j = 0; j < PER; ++j) {
-      const int i = e0 + j;
-      if (i >= e1) break;
-      const uint32_t d = (ks[sort_slot(i)] >> shift) & 7u;
-      packed += 1ull << (6 * d);
-    }
-#pragma unroll
-    for (int d = 0; d < SORT_LDS_DIGITS; ++d)
-      cnt[d * SORT_LDS_THREADS + t] = (uint32_t)(packed >> (6 * d)) & 63u;
+    // (this wavefront's own row: its later accesses follow in order)
+    for (int d = lane; d < 256; d += 64) cnt[w][d] = 0;
+    for (int i = c0 + lane; i < c1; i += 64) atomicAdd(&cnt[w][(ks[i] >> shift) & 255u], 1u);
     __syncthreads();
-    // exclusive scan over the flattened (digit, thread) counters
-    uint32_t loc[SORT_LDS_DIGITS], sum = 0;
-#pragma unroll
-    for (int j = 0; j < SORT_LDS_DIGITS; ++j) {
-      loc[j] = sum;
-      sum += cnt[SORT_LDS_DIGITS * t + j];
+    if (t < 256) {  // per digit: exclusive prefix over the wavefronts, and the total
+      uint32_t run = 0;
+      for (int v = 0; v < SORT_LDS_WAVES; ++v) {
+        const uint32_t c = cnt[v][t];
+        cnt[v][t] = run;
+        run += c;
+      }
+      dbase[t] = run;
     }
-    uint32_t total;
-    const uint32_t base = block_exclusive_scan<SORT_LDS_THREADS>(sum, wsum, &total);
-#pragma unroll
-    for (int j = 0; j < SORT_LDS_DIGITS; ++j) cnt[SORT_LDS_DIGITS * t + j] = base + loc[j];
     __syncthreads();
-    // scatter in order: each element takes the next slot of its digit
-    uint64_t placed = 0;
-#pragma unroll 8
-    for (int j = 0; j < PER; ++j) {
-      const int i = e0 + j;
-      if (i >= e1) break;
-      const uint32_t k = ks[sort_slot(i)];
-      const uint32_t d = (k >> shift) & 7u;
-      const uint32_t o = cnt[d * SORT_LDS_THREADS + t] + ((uint32_t)(placed >> (6 * d)) & 63u);
-      placed += 1ull << (6 * d);
-      kd[sort_slot((int)o)] = k;
+    if (w == 0) {  // exclusive prefix of the digit totals, four digits per lane
+      uint32_t v[4], own = 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        v[j] = dbase[4 * lane + j];
+        own += v[j];
+      }
+      uint32_t inc = own;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t u = __shfl_up(inc, o, 64);
+        if (lane >= o) inc += u;
+      }
+      uint32_t run = inc - own;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        dbase[4 * lane + j] = run;
+        run += v[j];
+      }
+    }
+    __syncthreads();
+    for (int s0 = c0; s0 < c1; s0 += 64) {
+      const bool act = s0 + lane < c1;
+      const uint32_t k = act ? ks[s0 + lane] : 0u;
+      const uint32_t d = (k >> shift) & 255u;
+      const uint64_t m = same_digit_lanes(d, act);
+      const uint32_t rank = (uint32_t)__popcll(m & below);
+      // every lane reads its digit's running offset before the lowest lane of
+      // the digit advances it (one wavefront: LDS accesses in program order)
+      const uint32_t o = dbase[d] + cnt[w][d] + rank;
+      if (act) kd[o] = k;
+      if (act && rank == 0) cnt[w][d] += (uint32_t)__popcll(m);
     }
     __syncthreads();
     src ^= 1;
   }
-#pragma unroll 16
-  for (int j = 0; j < PER; ++j) {
+#pragma unroll
+  for (int j = 0; j < SORT_LDS_N / SORT_LDS_THREADS; ++j) {
     const int i = j * SORT_LDS_THREADS + t;
     if (i < n) {
-      const uint32_t k = buf[src][sort_slot(i)];
+      const uint32_t k = buf[src][i];
       ka[i] = k >> 16;
       va[i] = k & 0xffffu;
     }
@@ -1093,7 +1118,7 @@ hipError_t launch_embed_bwd(const int32_t* idx, const float* dx, float* dwte, fl
   int bits = 1;
   while (bits < 31 && (1L << bits) < (long)Vp) ++bits;
   if (rows <= SORT_LDS_N && bits <= 16) {
-    id_sort_lds_kernel<<<1, SORT_LDS_THREADS, 0, s>>>(idx, (int)rows, (bits + 2) / 3, ka, va);
+    id_sort_lds_kernel<<<1, SORT_LDS_THREADS, 0, s>>>(idx, (int)rows, (bits + 7) / 8, ka, va);
   } else {
     int npass = (bits + 3) / 4;
     npass += npass & 1;  // even: the sorted result ends in (ka, va)

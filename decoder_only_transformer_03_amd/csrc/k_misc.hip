@@ -302,34 +302,44 @@ __global__ __launch_bounds__(256) void embed_bwd_chunk_kernel(const uint32_t* __
     const bool one_run = key[0] == key[m - 1];
     hflag[blockIdx.x] = cont_out && !(one_run && cont_in) ? (int)key[m - 1] : -1;
   }
+  // Run ending at position q: it continues a run from the previous chunk when
+  // it is the chunk's first run (keys are sorted, so its key is key[0]) and
+  // cont_in; it goes on into the next chunk when q is the last position and
+  // cont_out; otherwise it lies wholly here and is added into its dwte row.
+  // The runs of a chunk have distinct ids, so a batch's dwte rows are loaded
+  // before any of its stores: one round trip per batch, not one per run.
+  auto run_end = [&](int q) { return q + 1 == m || key[q + 1] != key[q]; };
+  auto from_prev = [&](int q) { return cont_in && key[q] == key[0]; };
+  auto to_next = [&](int q) { return q + 1 == m && cont_out; };
   for (int c = t * 4; c < C; c += 1024) {
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    int qs = 0;  // first position of the current run in this chunk
     for (int q0 = 0; q0 < m; q0 += 8) {
-      float4 v[8];
+      float4 v[8], o[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j)  // issue the batch's loads before using any
         if (q0 + j < m) v[j] = *reinterpret_cast<const float4*>(dx + (long)pos[q0 + j] * C + c);
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const int q = q0 + j;
+        if (q < m && run_end(q) && !from_prev(q) && !to_next(q))
+          o[j] = *reinterpret_cast<const float4*>(dwte + (long)key[q] * C + c);
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int q = q0 + j;
         if (q >= m) break;
         acc.x += v[j].x; acc.y += v[j].y; acc.z += v[j].z; acc.w += v[j].w;
-        if (q + 1 == m || key[q + 1] != key[q]) {
-          const bool from_prev = qs == 0 && cont_in, to_next = q + 1 == m && cont_out;
-          float* d;
-          if (from_prev) d = tail + (long)blockIdx.x * C + c;           // continues a run
-          else if (to_next) d = head + (long)blockIdx.x * C + c;        // run goes on
-          else d = dwte + (long)key[q] * C + c;                         // whole run here
-          if (from_prev || to_next) {
-            *reinterpret_cast<float4*>(d) = acc;
-          } else {
-            float4 o = *reinterpret_cast<const float4*>(d);
-            o.x += acc.x; o.y += acc.y; o.z += acc.z; o.w += acc.w;
-            *reinterpret_cast<float4*>(d) = o;
+        if (run_end(q)) {
+          if (from_prev(q)) {         // continues a run
+            *reinterpret_cast<float4*>(tail + (long)blockIdx.x * C + c) = acc;
+          } else if (to_next(q)) {    // run goes on
+            *reinterpret_cast<float4*>(head + (long)blockIdx.x * C + c) = acc;
+          } else {                    // whole run here
+            float4 r = o[j];
+            r.x += acc.x; r.y += acc.y; r.z += acc.z; r.w += acc.w;
+            *reinterpret_cast<float4*>(dwte + (long)key[q] * C + c) = r;
           }
           acc = make_float4(0.f, 0.f, 0.f, 0.f);
-          qs = q + 1;
         }
       }
     }

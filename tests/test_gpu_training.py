@@ -21,6 +21,10 @@
   a last 256-row tile holding 40 rows): bf16 against the oracle.
 * The seeded initialisation of gpt2_init against the oracle's recipe
   (Philox4x32-10 normal stream).
+* Resuming from saved state: parameters, AdamW moments and the step count
+  read out after two optimizer steps and loaded into a second handle give
+  a third step identical, bit for bit, to the first handle's, and that step
+  matches the oracle's from the same saved state.
 """
 import numpy as np
 import pytest
@@ -328,3 +332,58 @@ def test_seeded_init_matches_oracle(name, prec):
     assert la == lc
     for x in (a, b, c):
         x.close()
+
+
+@pytest.mark.parametrize("name,prec", [("tiny", "fp32"), ("gpt2-124m", "bf16")])
+def test_resume_from_saved_state(name, prec):
+    """Checkpoint and resume through gpt2_get / gpt2_set_params /
+    gpt2_set_state / gpt2_set_step: a second handle, initialised from
+    another seed, is loaded with the first's parameters, moments and step
+    count after two optimizer steps; the third step (t = 3, non-zero
+    moments, bias correction of t = 3, the bf16 weight copies refreshed by
+    gpt2_set_params) is then the same on both handles, bit for bit, and its
+    loss and pre-clip norm are the oracle's from the same saved state."""
+    d = synthetic.model_dims(name)
+    cfg = O.Config(**d)
+    B, T = (2, 64) if name == "tiny" else (1, 128)
+
+    def batches(step):
+        if name == "tiny":
+            return [synthetic.uniform_batch(B, T, 512, seed=5000 + 10 * step + j) for j in range(2)]
+        return [synthetic.zipf_batch(B, T, seed=5000 + 10 * step + j) for j in range(2)]
+
+    gcfg = G.make_config(max_batch=B, precision=prec, **d)
+    a = G.GPT2(gcfg, device=DEV, seed=7)
+    b = G.GPT2(gcfg, device=DEV, seed=8)
+    try:
+        for s in range(2):
+            gpu_opt_step(a, batches(s), G.gpt2_lr_at(s, **SCHED))
+        saved = {k: a.get(k) for k in (G.GPT2_PARAMS, G.GPT2_ADAM_M, G.GPT2_ADAM_V)}
+        assert a.get_step() == 2
+        b.set_params(saved[G.GPT2_PARAMS])
+        b.set_state(G.GPT2_ADAM_M, saved[G.GPT2_ADAM_M])
+        b.set_state(G.GPT2_ADAM_V, saved[G.GPT2_ADAM_V])
+        b.set_step(2)
+        lr = G.gpt2_lr_at(2, **SCHED)
+        micro = batches(2)
+        loss_a, norm_a, g_a = gpu_opt_step(a, micro, lr)
+        loss_b, norm_b, g_b = gpu_opt_step(b, micro, lr)
+        assert b.get_step() == 3
+        assert loss_a == loss_b and norm_a == norm_b
+        assert np.array_equal(g_a, g_b)
+        for k in (G.GPT2_PARAMS, G.GPT2_ADAM_M, G.GPT2_ADAM_V):
+            assert np.array_equal(a.get(k), b.get(k)), k
+        p, m, v = (saved[k].copy() for k in (G.GPT2_PARAMS, G.GPT2_ADAM_M, G.GPT2_ADAM_V))
+        loss_r, norm_r, _ = oracle_opt_step(cfg, p, m, v, 3, micro, lr)
+        print(f"\n{name} {prec} resumed step 3: loss {loss_b:.6f} / {loss_r:.6f}, "
+              f"norm {norm_b:.5f} / {norm_r:.5f}")
+        if prec == "fp32":
+            assert abs(loss_b - loss_r) <= 1e-4 * abs(loss_r)
+            assert abs(norm_b - norm_r) <= 1e-3 * norm_r
+        else:
+            assert abs(loss_b - loss_r) < 5e-3
+            # (measured: 6e-4 of the norm, loss within 3e-4)
+            assert abs(norm_b - norm_r) <= 5e-3 * norm_r
+    finally:
+        a.close()
+        b.close()

@@ -403,8 +403,18 @@ __global__ __launch_bounds__(256) void embed_bwd_wpe_kernel(const float* __restr
                                                             int C, int store) {
   long i = (long)blockIdx.x * 256 + threadIdx.x;
   if (i >= (long)T * C) return;
+  const float* p = dx + i;
+  const long st = (long)T * C;
   float s = 0.f;
-  for (int b = 0; b < B; ++b) s += dx[(long)b * T * C + i];
+  int b = 0;
+  for (; b + 8 <= B; b += 8) {  // eight loads in flight, added in order of b
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = p[(long)(b + u) * st];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) s += v[u];
+  }
+  for (; b < B; ++b) s += p[(long)b * st];
   dwpe[i] = store ? s : dwpe[i] + s;
 }
 
@@ -676,12 +686,16 @@ __global__ __launch_bounds__(1024) void count_valid_kernel(const int32_t* __rest
                                                            int* __restrict__ n_valid, int* err) {
   __shared__ int s[16];
   int cnt = 0, bad = 0;
-  for (long i = threadIdx.x; i < rows; i += 1024) {
-    int t = tgt[i];
-    if (t != -1) {
-      ++cnt;
-      if (t < 0 || t >= Vp) bad = 1;
-    }
+  for (long i0 = threadIdx.x; i0 < rows; i0 += 8 * 1024) {  // eight loads in flight
+    int t[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) t[u] = i0 + 1024L * u < rows ? tgt[i0 + 1024L * u] : -1;
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (t[u] != -1) {
+        ++cnt;
+        if (t[u] < 0 || t[u] >= Vp) bad = 1;
+      }
   }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
@@ -850,7 +864,13 @@ __global__ __launch_bounds__(1024) void loss_reduce_kernel(const float* __restri
                                                            float* __restrict__ loss) {
   __shared__ double s[16];
   double a = 0.0;
-  for (long i = threadIdx.x; i < rows; i += 1024) a += (double)row_loss[i];
+  for (long i0 = threadIdx.x; i0 < rows; i0 += 8 * 1024) {  // eight loads in flight, same order
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = i0 + 1024L * u < rows ? row_loss[i0 + 1024L * u] : 0.f;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) a += (double)v[u];
+  }
   a = wave_sum_d(a);
   if ((threadIdx.x & 63) == 0) s[threadIdx.x >> 6] = a;
   __syncthreads();
